@@ -1,0 +1,189 @@
+"""Python binding of libgdn, the Gated DeltaNet token mixer for MI355X (gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libgdn.so``.  PyTorch supplies device memory and the stream.
+
+Raw C-ABI entry points (same names and arguments as ``include/gdn.h``, with
+pointers passed as integers):
+
+    gdn_chunk_prefill, gdn_chunk_prefill_workspace_size, gdn_decode_step,
+    gdn_status_string, gdn_version
+
+Tensor helpers that allocate outputs with torch and call the above on the
+current stream:
+
+    chunk_prefill(q, k, v, g, beta, initial_state=None, chunk=64) -> (o, final_state)
+    decode_step(q, k, v, g, beta, state) -> o        (state updated in place)
+
+The rule computed (a gated delta rule; the pages describe the GDN layer in
+words only -- kwkr.cn digest of HyLo-Llama-8MLA8GDN-8K-SFT, architecture
+section; we0.ai Priming article, SSM comparison):
+
+    S_t = a_t S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T,  a_t = exp(g_t)
+    o_t = S_t q_t / sqrt(d_k)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libgdn.so")
+
+GDN_F32, GDN_BF16 = 0, 1
+STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_UNSUPPORTED",
+          4: "GDN_ERR_ALIGN", 5: "GDN_ERR_ALIAS", 6: "GDN_ERR_WORKSPACE", 7: "GDN_ERR_HIP"}
+EXPORTS = ("gdn_chunk_prefill", "gdn_chunk_prefill_workspace_size", "gdn_decode_step",
+           "gdn_status_string", "gdn_version")
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {gdn_status_string(status)}")
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libgdn.so; raises if it has not been built (there is no fallback)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libgdn.so is not built ({LIB_PATH}); run "
+                               "`python -m hybrid_linear_attention_gated_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        L.gdn_chunk_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                        i32, vp, sz, vp]
+        L.gdn_chunk_prefill.restype = i32
+        L.gdn_chunk_prefill_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+        L.gdn_chunk_prefill_workspace_size.restype = sz
+        L.gdn_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
+        L.gdn_decode_step.restype = i32
+        L.gdn_status_string.argtypes = [i32]
+        L.gdn_status_string.restype = ctypes.c_char_p
+        L.gdn_version.argtypes = []
+        L.gdn_version.restype = i32
+        _lib = L
+    return _lib
+
+
+# ---- raw C-ABI entry points ----------------------------------------------------------
+
+def gdn_chunk_prefill(q, k, v, g, beta, initial_state, o, final_state, B, T, H, d_k, d_v, chunk,
+                      qkv_dtype, workspace, workspace_bytes, stream) -> int:
+    return lib().gdn_chunk_prefill(q, k, v, g, beta, initial_state, o, final_state, B, T, H, d_k,
+                                   d_v, chunk, qkv_dtype, workspace, workspace_bytes, stream)
+
+
+def gdn_chunk_prefill_workspace_size(B, T, H, d_k, d_v, chunk, qkv_dtype) -> int:
+    return lib().gdn_chunk_prefill_workspace_size(B, T, H, d_k, d_v, chunk, qkv_dtype)
+
+
+def gdn_decode_step(q, k, v, g, beta, state, o, N, H, d_k, d_v, qkv_dtype, stream) -> int:
+    return lib().gdn_decode_step(q, k, v, g, beta, state, o, N, H, d_k, d_v, qkv_dtype, stream)
+
+
+def gdn_status_string(status: int) -> str:
+    return lib().gdn_status_string(status).decode()
+
+
+def gdn_version() -> int:
+    return lib().gdn_version()
+
+
+# ---- torch helpers ------------------------------------------------------------------------
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return GDN_BF16
+    if t.dtype == torch.float32:
+        return GDN_F32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _check(t, name, dtype=None):
+    import torch
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise TypeError(f"{name} must be a tensor on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def workspace_bytes(B, T, H, d_k, d_v, chunk, qkv_dtype) -> int:
+    return int(gdn_chunk_prefill_workspace_size(B, T, H, d_k, d_v, chunk, qkv_dtype))
+
+
+def chunk_prefill(q, k, v, g, beta, initial_state=None, chunk=64, *, out=None, final_state=None,
+                  workspace=None, stream=None):
+    """q, k [B,T,H,d_k]; v [B,T,H,d_v] (bf16 or fp32); g, beta [B,T,H] fp32;
+    initial_state [B,H,d_k,d_v] fp32 or None.  Returns (o fp32 [B,T,H,d_v], final_state).
+    ``final_state`` may be ``initial_state`` itself for in-place chaining."""
+    import torch
+    B, T, H, d_k = q.shape
+    d_v = v.shape[-1]
+    dt = _dtype_code(q)
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, q.dtype)
+    _check(g, "g", torch.float32)
+    _check(beta, "beta", torch.float32)
+    _check(initial_state, "initial_state", torch.float32)
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, T, H, d_v), device=dev, dtype=torch.float32)
+    if final_state is None:
+        final_state = torch.empty((B, H, d_k, d_v), device=dev, dtype=torch.float32)
+    _check(out, "out", torch.float32)
+    _check(final_state, "final_state", torch.float32)
+    need = workspace_bytes(B, T, H, d_k, d_v, chunk, dt)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, device=dev, dtype=torch.uint8)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    st = gdn_chunk_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                           _ptr(out), _ptr(final_state), B, T, H, d_k, d_v, chunk, dt,
+                           _ptr(workspace), ws_bytes, stream)
+    if st != 0:
+        raise GdnError(st, "gdn_chunk_prefill")
+    return out, final_state
+
+
+def decode_step(q, k, v, g, beta, state, *, out=None, stream=None):
+    """q, k [N,H,d_k]; v [N,H,d_v]; g, beta [N,H] fp32; state [N,H,d_k,d_v] fp32
+    (updated in place).  Returns o fp32 [N,H,d_v]."""
+    import torch
+    N, H, d_k = q.shape
+    d_v = v.shape[-1]
+    dt = _dtype_code(q)
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, q.dtype)
+    _check(g, "g", torch.float32)
+    _check(beta, "beta", torch.float32)
+    _check(state, "state", torch.float32)
+    if out is None:
+        out = torch.empty((N, H, d_v), device=q.device, dtype=torch.float32)
+    _check(out, "out", torch.float32)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = gdn_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(out),
+                         N, H, d_k, d_v, dt, stream)
+    if st != 0:
+        raise GdnError(st, "gdn_decode_step")
+    return out
+
+
+__all__ = ["EXPORTS", "GDN_F32", "GDN_BF16", "GdnError", "lib", "gdn_chunk_prefill",
+           "gdn_chunk_prefill_workspace_size", "gdn_decode_step", "gdn_status_string",
+           "gdn_version", "chunk_prefill", "decode_step", "workspace_bytes"]

@@ -1,0 +1,180 @@
+// gdn_api.hip -- the C ABI of libgdn: argument validation and dispatch.
+//
+// Every check runs on the host before anything is queued, so a call that
+// returns an error has no side effect.  The library keeps no state and
+// allocates nothing; scratch memory comes from the caller.
+#include <stdint.h>
+#include <string.h>
+
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+__global__ void state_copy_kernel(const float *__restrict__ src, float *__restrict__ dst, size_t n) {
+    const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
+    for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride)
+        dst[i] = src ? src[i] : 0.f;
+}
+
+bool supported_dim(int d) { return d == 16 || d == 64 || d == 128; }
+bool supported_chunk(int c) { return c == 16 || c == 32 || c == 64; }
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Span {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+Span span(const void *p, size_t bytes) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return {a, a + bytes};
+}
+bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
+
+// element count of a product of non-negative ints, or SIZE_MAX on overflow
+size_t prod(std::initializer_list<long long> xs) {
+    unsigned __int128 acc = 1;
+    for (long long x : xs) {
+        acc *= static_cast<unsigned __int128>(x);
+        if (acc > (static_cast<unsigned __int128>(1) << 60)) return SIZE_MAX;
+    }
+    return static_cast<size_t>(acc);
+}
+
+size_t elem_bytes(gdn_dtype dt) { return dt == GDN_BF16 ? 2 : 4; }
+
+gdn_status check_prefill_shape(int B, int T, int H, int d_k, int d_v, int chunk, gdn_dtype dt) {
+    if (B <= 0 || H <= 0 || T < 0 || d_k <= 0 || d_v <= 0 || chunk <= 0) return GDN_ERR_SHAPE;
+    if (dt != GDN_F32 && dt != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+    if (!supported_dim(d_k) || !supported_dim(d_v) || !supported_chunk(chunk))
+        return GDN_ERR_UNSUPPORTED;
+    if (prod({B, T, H, d_k > d_v ? d_k : d_v}) == SIZE_MAX) return GDN_ERR_SHAPE;
+    if (prod({B, H, 16}) > 0x7fffffffULL) return GDN_ERR_SHAPE;  // grid limits
+    return GDN_OK;
+}
+
+}  // namespace
+
+hipError_t launch_state_copy(const float *s0, float *s_out, size_t n, hipStream_t stream) {
+    if (n == 0 || s0 == s_out) return hipSuccess;
+    size_t blocks = (n + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(state_copy_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+                       s0, s_out, n);
+    return hipGetLastError();
+}
+
+}  // namespace gdn
+
+using namespace gdn;
+
+extern "C" {
+
+int gdn_version(void) { return GDN_ABI_VERSION; }
+
+const char *gdn_status_string(gdn_status status) {
+    switch (status) {
+    case GDN_OK: return "GDN_OK: success";
+    case GDN_ERR_NULL: return "GDN_ERR_NULL: a required pointer is NULL";
+    case GDN_ERR_SHAPE: return "GDN_ERR_SHAPE: invalid or too large size argument";
+    case GDN_ERR_UNSUPPORTED:
+        return "GDN_ERR_UNSUPPORTED: d_k/d_v must be 16, 64 or 128, chunk 16, 32 or 64, dtype F32 or BF16";
+    case GDN_ERR_ALIGN: return "GDN_ERR_ALIGN: a pointer is not 16-byte aligned";
+    case GDN_ERR_ALIAS: return "GDN_ERR_ALIAS: an output buffer overlaps another buffer";
+    case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE: workspace missing or too small";
+    case GDN_ERR_HIP: return "GDN_ERR_HIP: the HIP runtime failed to queue work";
+    }
+    return "unknown gdn_status";
+}
+
+size_t gdn_chunk_prefill_workspace_size(int B, int T, int H, int d_k, int d_v, int chunk,
+                                        gdn_dtype qkv_dtype) {
+    if (check_prefill_shape(B, T, H, d_k, d_v, chunk, qkv_dtype) != GDN_OK || T == 0) return 0;
+    if (qkv_dtype == GDN_BF16) return prefill_bf16_workspace(B, T, H, d_k, d_v, chunk);
+    return 0;  // the fp32 path keeps everything on chip
+}
+
+gdn_status gdn_chunk_prefill(const void *q, const void *k, const void *v, const float *g,
+                             const float *beta, const float *initial_state, float *o,
+                             float *final_state, int B, int T, int H, int d_k, int d_v, int chunk,
+                             gdn_dtype qkv_dtype, void *workspace, size_t workspace_bytes,
+                             void *stream) {
+    gdn_status st = check_prefill_shape(B, T, H, d_k, d_v, chunk, qkv_dtype);
+    if (st != GDN_OK) return st;
+    if (!final_state) return GDN_ERR_NULL;
+    if (T > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL;
+    const void *ptrs[] = {q, k, v, g, beta, initial_state, o, final_state, workspace};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return GDN_ERR_ALIGN;
+
+    const size_t es = elem_bytes(qkv_dtype);
+    const size_t state_bytes = prod({B, H, d_k, d_v}) * 4;
+    const Span s_fin = span(final_state, state_bytes);
+    const Span s_init = initial_state ? span(initial_state, state_bytes) : Span{0, 0};
+    if (initial_state && initial_state != final_state && overlap(s_init, s_fin)) return GDN_ERR_ALIAS;
+
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (T == 0) {
+        if (workspace && overlap(span(workspace, workspace_bytes), s_fin)) return GDN_ERR_ALIAS;
+        return launch_state_copy(initial_state, final_state, state_bytes / 4, hs) == hipSuccess
+                   ? GDN_OK
+                   : GDN_ERR_HIP;
+    }
+
+    const Span s_q = span(q, prod({B, T, H, d_k}) * es), s_k = span(k, prod({B, T, H, d_k}) * es);
+    const Span s_v = span(v, prod({B, T, H, d_v}) * es);
+    const Span s_g = span(g, prod({B, T, H}) * 4), s_b = span(beta, prod({B, T, H}) * 4);
+    const Span s_o = span(o, prod({B, T, H, d_v}) * 4);
+    const Span inputs[] = {s_q, s_k, s_v, s_g, s_b};
+    for (const Span &in : inputs)
+        if (overlap(s_o, in) || overlap(s_fin, in)) return GDN_ERR_ALIAS;
+    if (overlap(s_o, s_init) || overlap(s_o, s_fin)) return GDN_ERR_ALIAS;
+
+    const size_t need = gdn_chunk_prefill_workspace_size(B, T, H, d_k, d_v, chunk, qkv_dtype);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return GDN_ERR_WORKSPACE;
+        const Span s_ws = span(workspace, need);
+        const Span all[] = {s_q, s_k, s_v, s_g, s_b, s_init, s_o, s_fin};
+        for (const Span &x : all)
+            if (overlap(s_ws, x)) return GDN_ERR_ALIAS;
+    }
+
+    hipError_t err;
+    if (qkv_dtype == GDN_BF16)
+        err = launch_prefill_bf16(static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
+                                  static_cast<const uint16_t *>(v), g, beta, initial_state, o,
+                                  final_state, B, T, H, d_k, d_v, chunk, workspace, hs);
+    else
+        err = launch_prefill_valu(q, k, v, g, beta, initial_state, o, final_state, B, T, H, d_k,
+                                  d_v, chunk, GDN_F32, hs);
+    return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+gdn_status gdn_decode_step(const void *q, const void *k, const void *v, const float *g,
+                           const float *beta, float *state, float *o, int N, int H, int d_k,
+                           int d_v, gdn_dtype qkv_dtype, void *stream) {
+    if (N < 0 || H <= 0 || d_k <= 0 || d_v <= 0) return GDN_ERR_SHAPE;
+    if (qkv_dtype != GDN_F32 && qkv_dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+    if (!supported_dim(d_k) || !supported_dim(d_v)) return GDN_ERR_UNSUPPORTED;
+    if (prod({N, H, d_k, d_v}) == SIZE_MAX || prod({N, H, 4}) > 0x7fffffffULL) return GDN_ERR_SHAPE;
+    if (N == 0) return GDN_OK;
+    if (!q || !k || !v || !g || !beta || !state || !o) return GDN_ERR_NULL;
+    const void *ptrs[] = {q, k, v, g, beta, state, o};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return GDN_ERR_ALIGN;
+
+    const size_t es = elem_bytes(qkv_dtype);
+    const Span s_q = span(q, prod({N, H, d_k}) * es), s_k = span(k, prod({N, H, d_k}) * es);
+    const Span s_v = span(v, prod({N, H, d_v}) * es);
+    const Span s_g = span(g, prod({N, H}) * 4), s_b = span(beta, prod({N, H}) * 4);
+    const Span s_s = span(state, prod({N, H, d_k, d_v}) * 4), s_o = span(o, prod({N, H, d_v}) * 4);
+    const Span inputs[] = {s_q, s_k, s_v, s_g, s_b};
+    for (const Span &in : inputs)
+        if (overlap(s_o, in) || overlap(s_s, in)) return GDN_ERR_ALIAS;
+    if (overlap(s_o, s_s)) return GDN_ERR_ALIAS;
+
+    const hipError_t err = launch_decode(q, k, v, g, beta, state, o, N, H, d_k, d_v, qkv_dtype,
+                                         static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,145 @@
+// gdn_decode.hip -- single-token GDN step for a batch of sequences (gfx950).
+//
+// One token of the gated delta rule per (sequence, head), applied to the
+// stored fp32 state in place (the step the HyLo serving runs repeat for every
+// generated token at a cost that does not grow with context: ftxj.github.io
+// digest of arXiv 2604.24715, Figure 5; we0.ai Priming article, SSM
+// comparison: same compute budget per token).  With u = S k and p = S q,
+//
+//     delta = b (v - a u)
+//     S'    = a S + delta k^T                (= a S (I - b k k^T) + b v k^T)
+//     o     = S' q / sqrt(d_k) = (a p + delta (k . q)) / sqrt(d_k)
+//
+// The step is bound by HBM bandwidth: every state byte is read once and
+// written once, ~0.25 FLOP per byte, so there is no MFMA here.  Layout of the
+// work: a wavefront owns a column slice of one (sequence, head) state stored
+// key-major [d_k][d_v]; each lane holds float4 columns of a contiguous block
+// of key rows in registers, so the column sums u, p reduce over key rows with
+// a few cross-lane xor shuffles, and the state is loaded and stored with
+// fully coalesced 16-byte accesses exactly once.
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kWavesPerBlock = 4;
+
+template <int DK, int DV>
+struct DecodeShape {
+    // columns per wavefront: keep at most 64 state floats per lane
+    static constexpr int WC = (DK * DV <= 64 * 64) ? DV : (4096 / DK < DV ? 4096 / DK : DV);
+    static constexpr int SLICES = DV / WC;
+    static constexpr int LPR = WC / 4;       // lanes per key row (one float4 each)
+    static constexpr int RG = kWave / LPR;   // key-row groups per wavefront
+    static constexpr int ROWS = DK / RG;     // key rows per lane
+    static_assert(WC % 4 == 0 && kWave % LPR == 0 && DK % RG == 0, "decode tiling");
+};
+
+template <int DK, int DV, typename TIn>
+__global__ __launch_bounds__(kWave * kWavesPerBlock) void decode_kernel(
+    const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
+    const float *__restrict__ g, const float *__restrict__ beta, float *__restrict__ state,
+    float *__restrict__ o, int items, float scale) {
+    using S = DecodeShape<DK, DV>;
+    const int lane = threadIdx.x % kWave;
+    const int item = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+    if (item >= items) return;  // whole wavefront exits together
+    const int slice = item % S::SLICES;
+    const size_t nh = static_cast<size_t>(item / S::SLICES);  // n * H + h
+
+    const int c = lane % S::LPR;   // float4 column index inside the slice
+    const int rg = lane / S::LPR;  // key-row group
+    const int col = slice * S::WC + 4 * c;
+    const int row0 = rg * S::ROWS;
+
+    const float a = __expf(g[nh]);
+    const float b = beta[nh];
+
+    float *st = state + nh * DK * DV;
+    f32x4 s[S::ROWS];
+#pragma unroll
+    for (int m = 0; m < S::ROWS; ++m)
+        s[m] = *reinterpret_cast<const f32x4 *>(st + static_cast<size_t>(row0 + m) * DV + col);
+
+    float kr[S::ROWS], qr[S::ROWS];
+#pragma unroll
+    for (int m = 0; m < S::ROWS; ++m) {
+        kr[m] = load_in(k, nh * DK + row0 + m);
+        qr[m] = load_in(q, nh * DK + row0 + m);
+    }
+
+    f32x4 u = {0.f, 0.f, 0.f, 0.f}, p = {0.f, 0.f, 0.f, 0.f};
+    float kq = 0.f;
+#pragma unroll
+    for (int m = 0; m < S::ROWS; ++m) {
+        u += s[m] * kr[m];
+        p += s[m] * qr[m];
+        kq += kr[m] * qr[m];
+    }
+    // reduce over the key-row groups (lanes that share a column)
+#pragma unroll
+    for (int off = S::LPR; off < kWave; off <<= 1) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            u[e] += __shfl_xor(u[e], off, kWave);
+            p[e] += __shfl_xor(p[e], off, kWave);
+        }
+        kq += __shfl_xor(kq, off, kWave);
+    }
+
+    f32x4 vv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vv[e] = load_in(v, nh * DV + col + e);
+    const f32x4 delta = b * (vv - a * u);
+
+    if (rg == 0) {
+        const f32x4 out = scale * (a * p + delta * kq);
+        *reinterpret_cast<f32x4 *>(o + nh * DV + col) = out;
+    }
+#pragma unroll
+    for (int m = 0; m < S::ROWS; ++m)
+        *reinterpret_cast<f32x4 *>(st + static_cast<size_t>(row0 + m) * DV + col) =
+            a * s[m] + delta * kr[m];
+}
+
+template <int DK, int DV, typename TIn>
+hipError_t launch_decode_t(const void *q, const void *k, const void *v, const float *g,
+                           const float *beta, float *state, float *o, int N, int H,
+                           hipStream_t stream) {
+    using S = DecodeShape<DK, DV>;
+    const long long items = static_cast<long long>(N) * H * S::SLICES;
+    const int blocks = static_cast<int>((items + kWavesPerBlock - 1) / kWavesPerBlock);
+    const float scale = 1.0f / sqrtf(static_cast<float>(DK));
+    hipLaunchKernelGGL((decode_kernel<DK, DV, TIn>), dim3(blocks), dim3(kWave * kWavesPerBlock), 0,
+                       stream, static_cast<const TIn *>(q), static_cast<const TIn *>(k),
+                       static_cast<const TIn *>(v), g, beta, state, o, static_cast<int>(items),
+                       scale);
+    return hipGetLastError();
+}
+
+template <typename TIn>
+hipError_t dispatch_decode(const void *q, const void *k, const void *v, const float *g,
+                           const float *beta, float *state, float *o, int N, int H, int dk,
+                           int dv, hipStream_t s) {
+#define GDN_DEC(DK_, DV_)                                                                        \
+    if (dk == DK_ && dv == DV_)                                                                  \
+        return launch_decode_t<DK_, DV_, TIn>(q, k, v, g, beta, state, o, N, H, s);
+    GDN_DEC(16, 16) GDN_DEC(16, 64) GDN_DEC(16, 128)
+    GDN_DEC(64, 16) GDN_DEC(64, 64) GDN_DEC(64, 128)
+    GDN_DEC(128, 16) GDN_DEC(128, 64) GDN_DEC(128, 128)
+#undef GDN_DEC
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_decode(const void *q, const void *k, const void *v, const float *g,
+                         const float *beta, float *state, float *o, int N, int H, int dk, int dv,
+                         gdn_dtype dt, hipStream_t stream) {
+    if (dt == GDN_BF16)
+        return dispatch_decode<uint16_t>(q, k, v, g, beta, state, o, N, H, dk, dv, stream);
+    return dispatch_decode<float>(q, k, v, g, beta, state, o, N, H, dk, dv, stream);
+}
+
+}  // namespace gdn

@@ -1,0 +1,62 @@
+// gdn_internal.h -- device helpers and launcher declarations shared by the
+// libgdn translation units (not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "gdn.h"
+
+namespace gdn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ---- scalar conversions --------------------------------------------------
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
+    return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 bits (inputs are finite here).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+// Loads one stored q/k/v element as fp32.
+template <typename T> __device__ __forceinline__ float load_in(const T *p, size_t i);
+template <> __device__ __forceinline__ float load_in<float>(const float *p, size_t i) { return p[i]; }
+template <> __device__ __forceinline__ float load_in<uint16_t>(const uint16_t *p, size_t i) {
+    return bf16_bits_to_f32(p[i]);
+}
+
+// ---- launchers (host side; each returns the launch's hipError_t) ---------
+
+hipError_t launch_decode(const void *q, const void *k, const void *v, const float *g,
+                         const float *beta, float *state, float *o, int N, int H, int dk, int dv,
+                         gdn_dtype dt, hipStream_t stream);
+
+// Chunked prefill with fp32 VALU arithmetic (fp32 inputs, and bf16 inputs at
+// sizes the MFMA path does not tile).  Needs no workspace.
+hipError_t launch_prefill_valu(const void *q, const void *k, const void *v, const float *g,
+                               const float *beta, const float *s0, float *o, float *s_out, int B,
+                               int T, int H, int dk, int dv, int chunk, gdn_dtype dt,
+                               hipStream_t stream);
+
+// bf16 inputs: chunked prefill with bf16 MFMA contractions.
+bool prefill_bf16_uses_mfma(int dk, int dv, int chunk);
+hipError_t launch_prefill_bf16(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                               const float *g, const float *beta, const float *s0, float *o,
+                               float *s_out, int B, int T, int H, int dk, int dv, int chunk,
+                               void *ws, hipStream_t stream);
+size_t prefill_bf16_workspace(int B, int T, int H, int dk, int dv, int chunk);
+
+// Copies (or zero-fills, when s0 == NULL) a start state into s_out.
+hipError_t launch_state_copy(const float *s0, float *s_out, size_t n, hipStream_t stream);
+
+}  // namespace gdn

@@ -1,0 +1,145 @@
+/*
+ * gdn.h -- C ABI of libgdn, the Gated DeltaNet (GDN) token mixer for AMD
+ * MI355X (gfx950).
+ *
+ * The GDN layer is the linear-attention block that HyLo places in half or
+ * more of a Transformer's layers so that those layers keep a fixed-size
+ * recurrent state instead of a KV cache (kwkr.cn digest of
+ * HyLo-Llama-8MLA8GDN-8K-SFT, architecture section on 8 MLA + 8 Gated
+ * DeltaNet layers; ftxj.github.io digest of arXiv 2604.24715, Key Ideas and
+ * Method).  The pages describe its update only in words -- a gated delta rule
+ * that can erase or rewrite the value stored under one key (we0.ai article on
+ * Priming, comparison of Mamba-2, Gated DeltaNet and Gated KalmaNet).  The
+ * library computes the standard form of that rule, per sequence b and head h:
+ *
+ *     S_t = a_t S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T,   a_t = exp(g_t)
+ *     o_t = S_t q_t / sqrt(d_k)
+ *
+ * with the state S in R^{d_v x d_k}.  The readout uses the updated state.
+ *
+ * Conventions shared by every call
+ *   - Every pointer is a device pointer owned by the caller.  The library
+ *     allocates, frees and retains no memory.
+ *   - Tensors are dense, row-major and contiguous, and every pointer must be
+ *     16-byte aligned.
+ *   - q, k, v are stored as qkv_dtype (GDN_F32 or GDN_BF16); g, beta, states
+ *     and outputs are always fp32.
+ *   - States are stored key-major: [.., d_k, d_v], element (j, i) = S[i][j].
+ *   - q and k are used as given (the library does not normalise them);
+ *     scale = 1/sqrt(d_k) is fixed; g is expected finite and <= 0; beta is
+ *     used as given (no clamp).
+ *   - Work is queued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     the call returns at once.  Arguments are validated on the host before
+ *     anything is queued: a call that returns an error has queued nothing and
+ *     written nothing.  Faults inside kernels surface at the caller's next
+ *     synchronisation with the stream.
+ *   - Supported sizes: d_k, d_v in {16, 64, 128}; chunk in {16, 32, 64}.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+#if defined(__GNUC__) || defined(__clang__)
+#define GDN_API __attribute__((visibility("default")))
+#else
+#define GDN_API
+#endif
+
+typedef enum gdn_status {
+    GDN_OK = 0,
+    GDN_ERR_NULL = 1,        /* a required pointer is NULL */
+    GDN_ERR_SHAPE = 2,       /* a size is negative / zero where not allowed, or too large */
+    GDN_ERR_UNSUPPORTED = 3, /* d_k, d_v, chunk or dtype outside the supported set */
+    GDN_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+    GDN_ERR_ALIAS = 5,       /* an output overlaps an input (other than the allowed in-place state) */
+    GDN_ERR_WORKSPACE = 6,   /* workspace missing or smaller than gdn_chunk_prefill_workspace_size() */
+    GDN_ERR_HIP = 7          /* the HIP runtime reported an error while queuing work */
+} gdn_status;
+
+typedef enum gdn_dtype {
+    GDN_F32 = 0,  /* IEEE binary32 */
+    GDN_BF16 = 1  /* bfloat16 (upper half of a binary32) */
+} gdn_dtype;
+
+/*
+ * gdn_chunk_prefill -- run the rule over T tokens of B sequences at once.
+ *
+ * The sequence is processed in chunks of `chunk` tokens (the last chunk may be
+ * partial).  Inside a chunk the per-token updates are folded into dense
+ * products: a cumulative log-gate, the lower-triangular system
+ * (I + tril(diag(b) K K^T * decay)) solved by forward substitution, the
+ * W/U products, a scan of the fp32 state from chunk to chunk, and outputs as
+ * the intra-chunk term plus Q times the chunk's start state.  The result
+ * equals the token-by-token rule up to rounding.
+ *
+ *   q, k           [B, T, H, d_k]  qkv_dtype
+ *   v              [B, T, H, d_v]  qkv_dtype
+ *   g, beta        [B, T, H]       fp32 (log-gate; a_t = exp(g_t))
+ *   initial_state  [B, H, d_k, d_v] fp32, or NULL for a zero start state
+ *   o              [B, T, H, d_v]  fp32, written
+ *   final_state    [B, H, d_k, d_v] fp32, written; may be the same pointer
+ *                  as initial_state (in-place chaining of calls), but may not
+ *                  overlap it otherwise
+ *   workspace      device scratch of at least
+ *                  gdn_chunk_prefill_workspace_size(...) bytes (may be NULL
+ *                  when that size is 0); its contents on entry do not matter
+ *   T may be 0: then nothing is read but the start state, which is copied to
+ *   final_state (zeros when initial_state is NULL).
+ * Errors: GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_UNSUPPORTED, GDN_ERR_ALIGN,
+ * GDN_ERR_ALIAS (o overlapping any input or final_state, final_state
+ * overlapping q/k/v/g/beta, or the workspace overlapping anything),
+ * GDN_ERR_WORKSPACE, GDN_ERR_HIP.
+ */
+GDN_API gdn_status gdn_chunk_prefill(const void *q, const void *k, const void *v,
+                             const float *g, const float *beta,
+                             const float *initial_state,
+                             float *o, float *final_state,
+                             int B, int T, int H, int d_k, int d_v, int chunk,
+                             gdn_dtype qkv_dtype,
+                             void *workspace, size_t workspace_bytes,
+                             void *stream);
+
+/*
+ * Bytes of device scratch gdn_chunk_prefill needs for these sizes (0 if
+ * none).  Returns 0 as well for arguments gdn_chunk_prefill would reject.
+ */
+GDN_API size_t gdn_chunk_prefill_workspace_size(int B, int T, int H, int d_k, int d_v, int chunk,
+                                        gdn_dtype qkv_dtype);
+
+/*
+ * gdn_decode_step -- one token for each of N independent sequences: the rule
+ * with T = 1, applied to a batch of per-sequence states in place.
+ *
+ *   q, k      [N, H, d_k]  qkv_dtype
+ *   v         [N, H, d_v]  qkv_dtype
+ *   g, beta   [N, H]       fp32
+ *   state     [N, H, d_k, d_v] fp32, read and updated in place
+ *   o         [N, H, d_v]  fp32, written
+ * N may be 0 (nothing is done).
+ * Errors: GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_UNSUPPORTED, GDN_ERR_ALIGN,
+ * GDN_ERR_ALIAS (o or state overlapping an input or each other), GDN_ERR_HIP.
+ */
+GDN_API gdn_status gdn_decode_step(const void *q, const void *k, const void *v,
+                           const float *g, const float *beta,
+                           float *state, float *o,
+                           int N, int H, int d_k, int d_v,
+                           gdn_dtype qkv_dtype, void *stream);
+
+/* Static, human-readable text for a status code (never NULL). */
+GDN_API const char *gdn_status_string(gdn_status status);
+
+/* GDN_ABI_VERSION of the built library. */
+GDN_API int gdn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

@@ -1,0 +1,105 @@
+"""The C-ABI library loads, exports what include/gdn.h declares, and rejects bad
+arguments on the host before touching the GPU (CPU only: no kernel runs)."""
+import os
+import re
+
+import pytest
+
+import hybrid_linear_attention_gated_amd as gdn
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "gdn.h")
+OK, NULL, SHAPE, UNSUP, ALIGN, ALIAS, WS = 0, 1, 2, 3, 4, 5, 6
+BF16, F32 = gdn.GDN_BF16, gdn.GDN_F32
+
+
+def declared_functions():
+    with open(HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"GDN_API\s+[\w\s\*]+?\b(gdn_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_abi():
+    assert declared_functions() == sorted(gdn.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = gdn.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert gdn.gdn_version() == 1
+
+
+def test_status_strings():
+    for code in range(8):
+        assert gdn.gdn_status_string(code).startswith(gdn.STATUS[code])
+    assert gdn.gdn_status_string(99) == "unknown gdn_status"
+
+
+# fake, never dereferenced device addresses (validation is host-only)
+A = 1 << 32
+
+
+def addr(i, size=1 << 30):
+    return A + i * size
+
+
+def prefill(**kw):
+    args = dict(q=addr(0), k=addr(1), v=addr(2), g=addr(3), beta=addr(4), s0=None, o=addr(5),
+                sf=addr(6), B=1, T=128, H=2, dk=64, dv=64, chunk=64, dt=BF16, ws=addr(7),
+                ws_bytes=1 << 30, stream=None)
+    args.update(kw)
+    return gdn.gdn_chunk_prefill(args["q"], args["k"], args["v"], args["g"], args["beta"], args["s0"],
+                                 args["o"], args["sf"], args["B"], args["T"], args["H"], args["dk"],
+                                 args["dv"], args["chunk"], args["dt"], args["ws"], args["ws_bytes"],
+                                 args["stream"])
+
+
+def decode(**kw):
+    args = dict(q=addr(0), k=addr(1), v=addr(2), g=addr(3), beta=addr(4), st=addr(5), o=addr(6),
+                N=4, H=2, dk=64, dv=64, dt=BF16, stream=None)
+    args.update(kw)
+    return gdn.gdn_decode_step(args["q"], args["k"], args["v"], args["g"], args["beta"], args["st"],
+                               args["o"], args["N"], args["H"], args["dk"], args["dv"], args["dt"],
+                               args["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(o=None), NULL), (dict(sf=None), NULL), (dict(beta=None), NULL),
+    (dict(B=0), SHAPE), (dict(H=-1), SHAPE), (dict(T=-5), SHAPE), (dict(chunk=0), SHAPE),
+    (dict(dk=32), UNSUP), (dict(dv=96), UNSUP), (dict(chunk=128), UNSUP), (dict(dt=7), UNSUP),
+    (dict(q=addr(0) + 8), ALIGN), (dict(sf=addr(6) + 4), ALIGN), (dict(ws=addr(7) + 2), ALIGN),
+    (dict(o=addr(0)), ALIAS), (dict(o=addr(2) + 64), ALIAS), (dict(sf=addr(1)), ALIAS),
+    (dict(sf=addr(5)), ALIAS), (dict(s0=addr(8), sf=addr(8) + 256), ALIAS),
+    (dict(s0=addr(5)), ALIAS),
+    (dict(ws=None), WS), (dict(ws_bytes=1024), WS), (dict(ws=addr(4)), ALIAS),
+])
+def test_prefill_rejects(kw, code):
+    assert prefill(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(st=None), NULL), (dict(o=None), NULL),
+    (dict(N=-1), SHAPE), (dict(H=0), SHAPE), (dict(dk=8), UNSUP), (dict(dt=3), UNSUP),
+    (dict(st=addr(5) + 4), ALIGN), (dict(o=addr(1)), ALIAS), (dict(st=addr(2)), ALIAS),
+    (dict(o=addr(5) + 1024), ALIAS),
+])
+def test_decode_rejects(kw, code):
+    assert decode(**kw) == code
+
+
+def test_decode_zero_sequences_is_a_no_op():
+    assert decode(N=0, q=None, k=None) == OK
+
+
+def test_workspace_size():
+    # bf16 MFMA shapes need scratch, proportional to the number of chunks
+    w1 = gdn.gdn_chunk_prefill_workspace_size(1, 64, 32, 64, 64, 64, BF16)
+    w2 = gdn.gdn_chunk_prefill_workspace_size(1, 128, 32, 64, 64, 64, BF16)
+    assert w1 > 0 and abs(w2 - 2 * w1) < 4096
+    assert gdn.gdn_chunk_prefill_workspace_size(1, 65, 32, 64, 64, 64, BF16) == w2
+    # fp32 inputs and the VALU shapes keep everything on chip
+    assert gdn.gdn_chunk_prefill_workspace_size(1, 64, 2, 16, 16, 16, F32) == 0
+    assert gdn.gdn_chunk_prefill_workspace_size(1, 64, 2, 64, 64, 16, BF16) == 0
+    # rejected arguments and T = 0 need nothing
+    assert gdn.gdn_chunk_prefill_workspace_size(1, 64, 2, 48, 64, 64, BF16) == 0
+    assert gdn.gdn_chunk_prefill_workspace_size(1, 0, 2, 64, 64, 64, BF16) == 0
