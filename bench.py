@@ -53,6 +53,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=65536,
                     help="tokens of the 64K workload the oracle is timed on")
+    ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all",
+                    help="run one component (for profiling); the JSON line needs 'all'")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only; the GDN path shards over heads and "
@@ -83,10 +85,14 @@ def main():
     dout = torch.empty((dw.B, dw.H, dw.dv), device=dev, dtype=torch.float32)
 
     def prefill():
+        if args.only == "decode":
+            return
         gdn.chunk_prefill(pre["q"], pre["k"], pre["v"], pre["g"], pre["beta"], pre["s0"],
                           chunk=w.chunk, out=out, final_state=fin, workspace=ws)
 
     def decode_chain(ev):
+        if args.only == "prefill":
+            return
         for s, d in enumerate(steps_in):
             ev[s][0].record(stream)
             gdn.decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], state, out=dout)
@@ -111,6 +117,9 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    if args.only != "all":
+        print(json.dumps({"only": args.only, "steps": args.steps, "wall_ms": wall * 1e3}), flush=True)
+        return
     pre_ms = sorted(a.elapsed_time(b) for a, b in pre_ev)
     dec_ms = sorted(a.elapsed_time(b) for step in dec_ev for a, b in step)
     pre_avg = sum(pre_ms) / len(pre_ms)

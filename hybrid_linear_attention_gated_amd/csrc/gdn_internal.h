@@ -56,6 +56,13 @@ hipError_t launch_prefill_bf16(const uint16_t *q, const uint16_t *k, const uint1
                                void *ws, hipStream_t stream);
 size_t prefill_bf16_workspace(int B, int T, int H, int dk, int dv, int chunk);
 
+// bf16 inputs, fused chunk kernel with sequence pieces (gdn_prefill_chunk.hip).
+hipError_t launch_prefill_chunk(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                const float *g, const float *beta, const float *s0, float *o,
+                                float *s_out, int B, int T, int H, int dk, int dv, int chunk,
+                                void *ws, hipStream_t stream);
+size_t prefill_chunk_workspace(int B, int T, int H, int dk, int dv, int chunk);
+
 // Copies (or zero-fills, when s0 == NULL) a start state into s_out.
 hipError_t launch_state_copy(const float *s0, float *s_out, size_t n, hipStream_t stream);
 

@@ -29,24 +29,38 @@ __device__ __forceinline__ float from_bf16(uint16_t h) { return bf16_bits_to_f32
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u16x8 u) { return __builtin_bit_cast(bf16x8, u); }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// Two fp32 -> two bf16 (round to nearest even) in one 32-bit word, element 0
+// in the low half: a single v_cvt_pk_bf16_f32.
+__device__ __forceinline__ unsigned cvt2_bf16(float a, float b) {
+    const f32x2 v = {a, b};
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
+}
+// The two bf16 halves of a packed word, widened back to fp32 (exact).
+__device__ __forceinline__ float lo_half_f32(unsigned w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_half_f32(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
+
 // Eight fp32 values -> one bf16 fragment (round to nearest even).
 __device__ __forceinline__ bf16x8 pack_bf16(const float (&x)[8]) {
-    u16x8 u;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) u[e] = to_bf16(x[e]);
-    return as_bf16x8(u);
+    const u32x4 w = {cvt2_bf16(x[0], x[1]), cvt2_bf16(x[2], x[3]), cvt2_bf16(x[4], x[5]),
+                     cvt2_bf16(x[6], x[7])};
+    return __builtin_bit_cast(bf16x8, w);
 }
 
-// Eight fp32 values -> hi + lo bf16 fragments with hi + lo ~= x to ~16 bits.
+// Eight fp32 values -> hi + lo bf16 fragments: hi = RNE(x), lo = RNE(x - hi),
+// so hi + lo carries about 16 significant bits of x.
 __device__ __forceinline__ void split_bf16(const float (&x)[8], bf16x8 &hi, bf16x8 &lo) {
-    u16x8 h, l;
+    u32x4 h, l;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        h[e] = to_bf16(x[e]);
-        l[e] = to_bf16(x[e] - from_bf16(h[e]));
+    for (int i = 0; i < 4; ++i) {
+        h[i] = cvt2_bf16(x[2 * i], x[2 * i + 1]);
+        l[i] = cvt2_bf16(x[2 * i] - lo_half_f32(h[i]), x[2 * i + 1] - hi_half_f32(h[i]));
     }
-    hi = as_bf16x8(h);
-    lo = as_bf16x8(l);
+    hi = __builtin_bit_cast(bf16x8, h);
+    lo = __builtin_bit_cast(bf16x8, l);
 }
 
 // Two accumulator tiles (consecutive 16-row blocks along k) -> the 8 k-slots of one step.

@@ -1,0 +1,676 @@
+// gdn_prefill_chunk.hip -- fused chunked GDN prefill for bf16 q/k/v (gfx950).
+//
+// Chunk form of the gated delta rule (derived from the rule; the pages give
+// no chunked algorithm).  For a chunk of C tokens with start state
+// St = S0^T (d_k x d_v, fp32) and G_r = sum_{i<=r} g_i within the chunk:
+//   A     = strict_tril(diag(b) (K K^T .* exp(G_r - G_j)))
+//   T     = (I + A)^{-1}
+//   W     = T diag(b exp(G)) K,   U = T diag(b) V
+//   Delta = U - W St                      (row r is b_r (v_r - a_r S_{r-1} k_r))
+//   O     = scale (diag(exp(G)) Q St + (Q K^T .* exp(G_r - G_j) .* tril) Delta)
+//   St'   = exp(G_C) St + K^T diag(exp(G_C - G)) Delta
+//
+// Sequence pieces.  A head's chunks are split into P consecutive pieces so
+// that every compute unit has work even for few heads.  The state after a
+// piece is an affine function of the state before it:
+//   St_out = M_p St_in + N_p
+// where N_p is the piece run from a zero state and M_p (d_k x d_k) is the
+// same chunk recurrence run on the identity with no values.  Three launches:
+//   MAP   (one workgroup per head and piece but the last) runs the recurrence
+//         on [values | identity] columns and stores [N_p | M_p];
+//   chain (one wavefront per head and 16 value columns) composes the maps
+//         serially over pieces and stores every piece's true start state;
+//   OUT   (one workgroup per head and piece) reruns each piece from its
+//         start state and writes the outputs (and the final state).
+// With a single piece only OUT runs, from the caller's start state.
+//
+// Inside a workgroup (4 wavefronts) all per-chunk operands live in LDS:
+// K K^T and A, T by blocked substitution (16x16 diagonal blocks one column
+// per lane, then 16x16 block products on MFMA with hi/lo bf16 splits), the
+// W and K^T fragments of the scan, and P = Q K^T .* decay.  Each wavefront
+// owns whole 16-column slices of the state: it keeps them in registers,
+// computes U, Delta and the state update for them, and (OUT) their outputs,
+// so the serial path never leaves the wavefront.
+//
+// Precision: K K^T and Q K^T are exact bf16 products with fp32 accumulation.
+// W and the state in W St are single bf16; T diag(b) in U, the state in
+// Q St, P and Delta in P Delta, the decayed Delta in the state update and
+// both factors of the inversion's block products are hi + lo bf16 pairs.
+#include "gdn_mfma.h"
+
+namespace gdn {
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kWaves = 4;
+constexpr int kBlock = kWave * kWaves;
+constexpr int kPad = 8;  // bf16 row padding in LDS
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma16(s16x4 a, s16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void split4(f32x4 x, s16x4 &hi, s16x4 &lo) {
+    u32x2 h, l;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        h[i] = cvt2_bf16(x[2 * i], x[2 * i + 1]);
+        l[i] = cvt2_bf16(x[2 * i] - lo_half_f32(h[i]), x[2 * i + 1] - hi_half_f32(h[i]));
+    }
+    hi = __builtin_bit_cast(s16x4, h);
+    lo = __builtin_bit_cast(s16x4, l);
+}
+
+// acc + A B for 16x16 blocks to ~fp32 accuracy: a holds A[i][4 gq + e] of
+// lane (gq, i); b holds B[4 gq + e][n] of lane (gq, n) (accumulator layout).
+__device__ __forceinline__ f32x4 mm16(f32x4 a, f32x4 b, f32x4 acc) {
+    s16x4 ah, al, bh, bl;
+    split4(a, ah, al);
+    split4(b, bh, bl);
+    acc = mfma16(ah, bh, acc);
+    acc = mfma16(ah, bl, acc);
+    acc = mfma16(al, bh, acc);
+    return acc;
+}
+
+template <int DK, int DV, int C, bool MAP>
+struct Cfg {
+    static constexpr int CT = C / 16, CS = C / 32, KT = DK / 16, KS = DK / 32, VT = DV / 16;
+    static constexpr int NB = C / 16;
+    static constexpr int NS = VT + (MAP ? KT : 0);  // 16-column slices of the carried state
+    static constexpr int SPW = NS / kWaves;          // slices per wavefront
+    static constexpr int VPW = (VT + kWaves - 1) / kWaves;
+    static_assert(NS % kWaves == 0, "slices must divide among the wavefronts");
+    static_assert(C == 32 || C == 64, "chunk");
+    static constexpr int MAPW = DV + DK;  // row length of a stored piece map
+};
+
+struct ChunkArgs {
+    const uint16_t *q, *k, *v;
+    const float *g, *beta;
+    const float *s_start;  // OUT: start states, (bh * P + piece) * DK * DV; NULL = zeros
+    float *o;              // OUT: outputs
+    float *s_final;        // OUT: final states [BH][DK][DV], written by the last piece
+    float *maps;           // MAP: [BH][P - 1][DK][DV + DK]
+    int T, H, P, piece_chunks, N;
+    float scale;
+};
+
+// Column fragment of a row-major bf16 LDS matrix M: slots e hold M[kmap(s, gq, e)][col].
+__device__ __forceinline__ bf16x8 lds_colfrag(const uint16_t *m, int stride, int col, int s, int gq) {
+    u16x8 u;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) u[e] = m[kmap(s, gq, e) * stride + col];
+    return as_bf16x8(u);
+}
+
+// Per-thread share of one chunk's rows, loaded from HBM one chunk ahead.
+template <int DK, int DV, int C, bool MAP>
+struct ChunkRegs {
+    static constexpr int NK = C * DK / 8 / kBlock, NV = C * DV / 8 / kBlock;
+    u16x8 k[NK], q[MAP ? 1 : NK], v[NV];
+    float g, beta;
+};
+
+template <int DK, int DV, int C, bool MAP>
+__device__ __forceinline__ void load_chunk(ChunkRegs<DK, DV, C, MAP> &r, const ChunkArgs &a, int b,
+                                           int h, int n, int tid) {
+    using R = ChunkRegs<DK, DV, C, MAP>;
+    const int t0 = n * C;
+    const int L = min(C, a.T - t0);
+    const size_t row0 = (static_cast<size_t>(b) * a.T + t0) * a.H + h;  // token-head row of t0
+    const u16x8 zero = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < R::NK; ++i) {
+        const int e = tid + i * kBlock, rr = e / (DK / 8), c8 = e % (DK / 8);
+        const size_t off = (row0 + static_cast<size_t>(rr) * a.H) * DK + 8 * c8;
+        r.k[i] = rr < L ? *reinterpret_cast<const u16x8 *>(a.k + off) : zero;
+        if (!MAP) r.q[i] = rr < L ? *reinterpret_cast<const u16x8 *>(a.q + off) : zero;
+    }
+#pragma unroll
+    for (int i = 0; i < R::NV; ++i) {
+        const int e = tid + i * kBlock, rr = e / (DV / 8), c8 = e % (DV / 8);
+        r.v[i] = rr < L ? *reinterpret_cast<const u16x8 *>(a.v + (row0 + static_cast<size_t>(rr) * a.H) * DV + 8 * c8)
+                        : zero;
+    }
+    const int lane = tid % kWave;
+    r.g = (tid < kWave && lane < L) ? a.g[row0 + static_cast<size_t>(lane) * a.H] : 0.f;
+    r.beta = (tid < kWave && lane < L) ? a.beta[row0 + static_cast<size_t>(lane) * a.H] : 0.f;
+}
+
+// Two workgroups per compute unit where LDS allows it (64-wide heads), so one
+// workgroup's barrier waits are filled by the other's work.
+template <int DK, int DV>
+constexpr int kBlocksPerCU = (DK == 64 && DV == 64) ? 2 : 1;
+
+template <int DK, int DV, int C, bool MAP>
+__global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(ChunkArgs a) {
+    using G = Cfg<DK, DV, C, MAP>;
+    using R = ChunkRegs<DK, DV, C, MAP>;
+    constexpr int KSTR = DK + kPad;   // K and Q rows
+    constexpr int VSTR = C + kPad;    // V^T rows
+    constexpr int CSTR = C + 4;       // A and T rows (fp32)
+    constexpr int KV_ELEMS = C * KSTR > DV * VSTR ? C * KSTR : DV * VSTR;
+    static_assert(2 * G::CT * G::CS * kWave * 16 <= C * CSTR * 4, "P fragments fit in A's buffer");
+    __shared__ __align__(16) uint16_t kv_s[KV_ELEMS];              // K rows, then V^T
+    __shared__ __align__(16) uint16_t q_s[MAP ? 8 : C * KSTR];     // Q rows
+    __shared__ __align__(16) float a_s[C * CSTR];                  // A, then P fragments
+    __shared__ __align__(16) float t_s[C * CSTR];                  // T = (I + A)^{-1}
+    __shared__ __align__(16) bf16x8 wf_s[G::CT * G::KS * kWave];   // W A-fragments
+    __shared__ __align__(16) bf16x8 kf_s[G::KT * G::CS * kWave];   // K^T A-fragments
+    __shared__ __align__(16) f32x4 x_s[4 * kWave];                 // inversion block scratch
+    __shared__ float g_s[C], b_s[C], bg_s[C], dec_s[C], gam_s[C];
+
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int gq = lane / 16, li = lane % 16;
+    const int pieces = MAP ? a.P - 1 : a.P;
+    const int piece = blockIdx.x % pieces;
+    const size_t bh = blockIdx.x / pieces;
+    const int b = static_cast<int>(bh / a.H), h = static_cast<int>(bh % a.H);
+    const int n0 = piece * a.piece_chunks;
+    const int n1 = min(n0 + a.piece_chunks, a.N);
+
+    // ---- carried state: St[j][mt] holds rows 16 mt + 4 gq + r, column 16 sl + li, sl = wave + 4 j
+    f32x4 St[G::SPW][G::KT];
+#pragma unroll
+    for (int j = 0; j < G::SPW; ++j) {
+        const int sl = wave + kWaves * j;
+#pragma unroll
+        for (int mt = 0; mt < G::KT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * mt + 4 * gq + r;
+                float x = 0.f;
+                if (MAP) {
+                    if (sl >= G::VT) x = (row == 16 * (sl - G::VT) + li) ? 1.f : 0.f;
+                } else if (a.s_start) {
+                    x = a.s_start[((bh * a.P + piece) * DK + row) * DV + 16 * sl + li];
+                }
+                St[j][mt][r] = x;
+            }
+    }
+    // T's blocks above the diagonal stay zero for the whole kernel
+    for (int e = tid; e < C * CSTR; e += kBlock) t_s[e] = 0.f;
+
+    uint16_t(*ks)[KSTR] = reinterpret_cast<uint16_t(*)[KSTR]>(kv_s);
+    uint16_t(*vt)[VSTR] = reinterpret_cast<uint16_t(*)[VSTR]>(kv_s);
+    uint16_t(*qs)[KSTR] = reinterpret_cast<uint16_t(*)[KSTR]>(q_s);
+    float(*as)[CSTR] = reinterpret_cast<float(*)[CSTR]>(a_s);
+    float(*ts)[CSTR] = reinterpret_cast<float(*)[CSTR]>(t_s);
+    bf16x8 *pf_s = reinterpret_cast<bf16x8 *>(a_s);  // P fragments: ((mt * CS + s) * 2 + hi/lo) * 64 + lane
+
+    auto rowfrag = [&](const float(*m)[CSTR], int r0, int c0) {
+        return *reinterpret_cast<const f32x4 *>(&m[r0 + li][c0 + 4 * gq]);
+    };
+    auto accfrag = [&](const float(*m)[CSTR], int r0, int c0) {
+        f32x4 x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = m[r0 + 4 * gq + e][c0 + li];
+        return x;
+    };
+    auto store_acc = [&](float(*m)[CSTR], int r0, int c0, f32x4 x) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) m[r0 + 4 * gq + e][c0 + li] = x[e];
+    };
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+
+    R cur;
+    if (n0 < n1) load_chunk<DK, DV, C, MAP>(cur, a, b, h, n0, tid);
+
+    for (int n = n0; n < n1; ++n) {
+        const int t0 = n * C;
+        const int L = min(C, a.T - t0);
+
+        // ---- A: this chunk's rows into LDS; gates and their decays
+#pragma unroll
+        for (int i = 0; i < R::NK; ++i) {
+            const int e = tid + i * kBlock, rr = e / (DK / 8), c8 = e % (DK / 8);
+            *reinterpret_cast<u16x8 *>(&ks[rr][8 * c8]) = cur.k[i];
+            if (!MAP) *reinterpret_cast<u16x8 *>(&qs[rr][8 * c8]) = cur.q[i];
+        }
+        if (wave == 0) {
+            // inclusive prefix sum of the gates; rows >= L add 0 and repeat G_{L-1}
+            float x = cur.g;
+#pragma unroll
+            for (int off = 1; off < kWave; off <<= 1) {
+                const float y = __shfl_up(x, off, kWave);
+                if (lane >= off) x += y;
+            }
+            const float glast = __shfl(x, C - 1, kWave);
+            if (lane < C) {
+                const float ex = __expf(x);
+                g_s[lane] = x;
+                b_s[lane] = cur.beta;
+                gam_s[lane] = ex;
+                bg_s[lane] = cur.beta * ex;
+                dec_s[lane] = __expf(glast - x);
+            }
+        }
+        __syncthreads();
+
+        // ---- B: A = strict_tril(diag(b) (K K^T .* exp(G_r - G_j))); K^T A-fragments
+        {
+            int idx = 0;
+#pragma unroll
+            for (int mt = 0; mt < G::CT; ++mt)
+#pragma unroll
+                for (int nt = 0; nt <= mt; ++nt, ++idx) {
+                    if (idx % kWaves != wave) continue;
+                    f32x4 acc = zero4;
+#pragma unroll
+                    for (int s = 0; s < G::KS; ++s)
+                        acc = mfma_bf16(lds_frag_bf16(&ks[16 * mt + li][0], s, gq),
+                                        lds_frag_bf16(&ks[16 * nt + li][0], s, gq), acc);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = 16 * mt + 4 * gq + r, col = 16 * nt + li;
+                        as[row][col] = (row > col) ? b_s[row] * acc[r] * __expf(g_s[row] - g_s[col]) : 0.f;
+                    }
+                }
+#pragma unroll
+            for (int f = 0; f < G::KT * G::CS; ++f) {
+                if ((idx + f) % kWaves != wave) continue;
+                const int mt = f / G::CS, s = f % G::CS;
+                kf_s[f * kWave + lane] = lds_colfrag(&ks[0][0], KSTR, 16 * mt + li, s, gq);
+            }
+        }
+        __syncthreads();
+
+        // ---- C: wave 0 inverts the two 32x32 diagonal halves of (I + A): 16x16 diagonal
+        // blocks by forward substitution (one column per lane, one block per 16 lanes), then
+        // T_{c+1,c} = -T_{c+1,c+1} A_{c+1,c} T_cc.  Waves 1..3 form P = Q K^T .* decay as
+        // P^T tiles, whose accumulator layout is P's A-fragment layout, split hi + lo.
+        bf16x8 pfr[MAP ? 1 : 2][2];
+        if (wave == 0) {
+            if (gq < G::NB) {
+                const int blk = gq, j = li;
+                float t[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float acc = 0.f;
+#pragma unroll
+                    for (int m = 0; m < r; ++m) acc += as[16 * blk + r][16 * blk + m] * t[m];
+                    t[r] = (r == j) ? 1.f : -acc;
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) ts[16 * blk + r][16 * blk + j] = t[r];
+            }
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int c = 0; c < G::NB; c += 2) {
+                const f32x4 x = mm16(rowfrag(as, 16 * (c + 1), 16 * c), accfrag(ts, 16 * c, 16 * c), zero4);
+                const f32x4 y = mm16(rowfrag(ts, 16 * (c + 1), 16 * (c + 1)), x, zero4);
+                store_acc(ts, 16 * (c + 1), 16 * c, -y);
+            }
+        } else if (!MAP) {
+            int idx = 0;
+#pragma unroll
+            for (int mt = 0; mt < G::CT; ++mt)
+#pragma unroll
+                for (int s = 0; s < G::CS; ++s) {
+                    if (32 * s > 16 * mt + 15) continue;  // P is lower triangular
+                    const int mine = idx++;
+                    if (mine % (kWaves - 1) != wave - 1) continue;
+                    f32x4 acc[2] = {zero4, zero4};
+#pragma unroll
+                    for (int half = 0; half < 2; ++half) {
+                        const int jt = 2 * s + half;
+                        if (jt > mt) continue;
+#pragma unroll
+                        for (int ss = 0; ss < G::KS; ++ss)
+                            acc[half] = mfma_bf16(lds_frag_bf16(&ks[16 * jt + li][0], ss, gq),
+                                                  lds_frag_bf16(&qs[16 * mt + li][0], ss, gq), acc[half]);
+                    }
+                    // lane holds P[r][j] for r = 16 mt + li and j = kmap(s, gq, e)
+                    const int r = 16 * mt + li;
+                    float x[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int jj = kmap(s, gq, e);
+                        const float qk = acc[e >> 2][e & 3];
+                        x[e] = (jj <= r) ? qk * __expf(g_s[r] - g_s[jj]) : 0.f;
+                    }
+                    split_bf16(x, pfr[mine / (kWaves - 1)][0], pfr[mine / (kWaves - 1)][1]);
+                }
+        }
+        __syncthreads();
+
+        // ---- D (chunk 64): X = A_BL T_TL for the lower-left 32x32 quarter, one tile per wave
+        if constexpr (G::NB == 4) {
+            const int aa = 2 + wave / 2, c = wave % 2;
+            f32x4 x = zero4;
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+                if (m >= c) x = mm16(rowfrag(as, 16 * aa, 16 * m), accfrag(ts, 16 * m, 16 * c), x);
+            x_s[wave * kWave + lane] = x;
+            __syncthreads();
+        }
+
+        // ---- E: T_BL = -T_BR X (chunk 64); P fragments and V^T into LDS (A and K are dead)
+        if constexpr (G::NB == 4) {
+            const int aa = 2 + wave / 2, c = wave % 2;
+            f32x4 y = zero4;
+#pragma unroll
+            for (int m = 2; m < 4; ++m)
+                if (m <= aa) y = mm16(rowfrag(ts, 16 * aa, 16 * m), x_s[((m - 2) * 2 + c) * kWave + lane], y);
+            store_acc(ts, 16 * aa, 16 * c, -y);
+        }
+        if (!MAP && wave > 0) {
+            int idx = 0;
+#pragma unroll
+            for (int mt = 0; mt < G::CT; ++mt)
+#pragma unroll
+                for (int s = 0; s < G::CS; ++s) {
+                    if (32 * s > 16 * mt + 15) continue;
+                    const int mine = idx++;
+                    if (mine % (kWaves - 1) != wave - 1) continue;
+                    pf_s[((mt * G::CS + s) * 2 + 0) * kWave + lane] = pfr[mine / (kWaves - 1)][0];
+                    pf_s[((mt * G::CS + s) * 2 + 1) * kWave + lane] = pfr[mine / (kWaves - 1)][1];
+                }
+        }
+#pragma unroll
+        for (int i = 0; i < R::NV; ++i) {
+            const int e = tid + i * kBlock, rr = e / (DV / 8), c8 = e % (DV / 8);
+#pragma unroll
+            for (int q8 = 0; q8 < 8; ++q8) vt[8 * c8 + q8][rr] = cur.v[i][q8];
+        }
+        __syncthreads();
+
+        // ---- F: W A-fragments = W^T tiles (2 s2, ct) and (2 s2 + 1, ct), W = T diag(b exp G) K
+#pragma unroll
+        for (int p = 0; p < G::CT * G::KS; ++p) {
+            if (p % kWaves != wave) continue;
+            const int ct = p % G::CT, s2 = p / G::CT;
+            f32x4 acc0 = zero4, acc1 = zero4;
+#pragma unroll
+            for (int s = 0; s < G::CS; ++s) {
+                if (32 * s > 16 * ct + 15) continue;  // T is lower triangular
+                float x[8];
+                lds_slots_f32(&ts[16 * ct + li][0], s, gq, x);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] *= bg_s[kmap(s, gq, e)];
+                const bf16x8 bfr = pack_bf16(x);
+                acc0 = mfma_bf16(kf_s[((2 * s2) * G::CS + s) * kWave + lane], bfr, acc0);
+                acc1 = mfma_bf16(kf_s[((2 * s2 + 1) * G::CS + s) * kWave + lane], bfr, acc1);
+            }
+            float x[8];
+            acc_pair_to_slots(acc0, acc1, x);
+            wf_s[(ct * G::KS + s2) * kWave + lane] = pack_bf16(x);
+        }
+        __syncthreads();
+
+        // next chunk's rows: loads in flight while this chunk's slices are computed
+        if (n + 1 < n1) load_chunk<DK, DV, C, MAP>(cur, a, b, h, n + 1, tid);
+
+        // ---- G: per slice: U = (T diag b) V, Delta = U - W St, outputs, state update
+#pragma unroll
+        for (int j = 0; j < G::SPW; ++j) {
+            const int sl = wave + kWaves * j;
+            const bool value_slice = sl < G::VT;
+            f32x4 D[G::CT];
+#pragma unroll
+            for (int ct = 0; ct < G::CT; ++ct) D[ct] = zero4;
+            if (value_slice) {
+#pragma unroll
+                for (int s = 0; s < G::CS; ++s) {
+                    const bf16x8 vb = lds_frag_bf16(&vt[16 * sl + li][0], s, gq);
+#pragma unroll
+                    for (int ct = 0; ct < G::CT; ++ct) {
+                        if (32 * s > 16 * ct + 15) continue;  // T is lower triangular
+                        float x[8];
+                        lds_slots_f32(&ts[16 * ct + li][0], s, gq, x);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) x[e] *= b_s[kmap(s, gq, e)];
+                        bf16x8 th, tl;
+                        split_bf16(x, th, tl);
+                        D[ct] = mfma_bf16(th, vb, D[ct]);
+                        D[ct] = mfma_bf16(tl, vb, D[ct]);
+                    }
+                }
+            }
+            bf16x8 Sb[G::KS];
+#pragma unroll
+            for (int s = 0; s < G::KS; ++s) {
+                float x[8];
+                acc_pair_to_slots(St[j][2 * s], St[j][2 * s + 1], x);
+                Sb[s] = pack_bf16(x);
+            }
+#pragma unroll
+            for (int ct = 0; ct < G::CT; ++ct) {
+                f32x4 acc = zero4;
+#pragma unroll
+                for (int s = 0; s < G::KS; ++s) acc = mfma_bf16(wf_s[(ct * G::KS + s) * kWave + lane], Sb[s], acc);
+                D[ct] -= acc;  // Delta = U - W St
+            }
+
+            if (!MAP && value_slice) {
+                // O = scale (diag(exp G) Q St + P Delta) with the chunk's start state
+                bf16x8 Sh[G::KS], Sl[G::KS], Dh[G::CS], Dl[G::CS];
+#pragma unroll
+                for (int s = 0; s < G::KS; ++s) {
+                    float x[8];
+                    acc_pair_to_slots(St[j][2 * s], St[j][2 * s + 1], x);
+                    split_bf16(x, Sh[s], Sl[s]);
+                }
+#pragma unroll
+                for (int s = 0; s < G::CS; ++s) {
+                    float x[8];
+                    acc_pair_to_slots(D[2 * s], D[2 * s + 1], x);
+                    split_bf16(x, Dh[s], Dl[s]);
+                }
+                float *orow = a.o + ((static_cast<size_t>(b) * a.T + t0) * a.H + h) * DV + 16 * sl + li;
+#pragma unroll
+                for (int mt = 0; mt < G::CT; ++mt) {
+                    f32x4 qsa = zero4, pd = zero4;
+#pragma unroll
+                    for (int s = 0; s < G::KS; ++s) {
+                        const bf16x8 qa = lds_frag_bf16(&qs[16 * mt + li][0], s, gq);
+                        qsa = mfma_bf16(qa, Sh[s], qsa);
+                        qsa = mfma_bf16(qa, Sl[s], qsa);
+                    }
+#pragma unroll
+                    for (int s = 0; s < G::CS; ++s) {
+                        if (32 * s > 16 * mt + 15) continue;
+                        const bf16x8 ph = pf_s[((mt * G::CS + s) * 2 + 0) * kWave + lane];
+                        const bf16x8 pl = pf_s[((mt * G::CS + s) * 2 + 1) * kWave + lane];
+                        pd = mfma_bf16(ph, Dh[s], pd);
+                        pd = mfma_bf16(ph, Dl[s], pd);
+                        pd = mfma_bf16(pl, Dh[s], pd);
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = 16 * mt + 4 * gq + r;
+                        if (row < L) orow[static_cast<size_t>(row) * a.H * DV] = a.scale * (gam_s[row] * qsa[r] + pd[r]);
+                    }
+                }
+            }
+
+            // St' = exp(G_C) St + K^T diag(exp(G_C - G)) Delta
+#pragma unroll
+            for (int ct = 0; ct < G::CT; ++ct) {
+                const f32x4 dec = *reinterpret_cast<const f32x4 *>(&dec_s[16 * ct + 4 * gq]);
+                D[ct] *= dec;
+            }
+            bf16x8 Eh[G::CS], El[G::CS];
+#pragma unroll
+            for (int s = 0; s < G::CS; ++s) {
+                float x[8];
+                acc_pair_to_slots(D[2 * s], D[2 * s + 1], x);
+                split_bf16(x, Eh[s], El[s]);
+            }
+            const float gl = gam_s[C - 1];
+#pragma unroll
+            for (int mt = 0; mt < G::KT; ++mt) {
+                f32x4 acc = gl * St[j][mt];
+#pragma unroll
+                for (int s = 0; s < G::CS; ++s) {
+                    const bf16x8 kfr = kf_s[(mt * G::CS + s) * kWave + lane];
+                    acc = mfma_bf16(kfr, Eh[s], acc);
+                    acc = mfma_bf16(kfr, El[s], acc);
+                }
+                St[j][mt] = acc;
+            }
+        }
+        __syncthreads();
+    }
+
+    // ---- results
+#pragma unroll
+    for (int j = 0; j < G::SPW; ++j) {
+        const int sl = wave + kWaves * j;
+#pragma unroll
+        for (int mt = 0; mt < G::KT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * mt + 4 * gq + r;
+                if (MAP)
+                    a.maps[((bh * (a.P - 1) + piece) * DK + row) * G::MAPW + 16 * sl + li] = St[j][mt][r];
+                else if (piece == a.P - 1)
+                    a.s_final[(bh * DK + row) * DV + 16 * sl + li] = St[j][mt][r];
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// chain: start states of every piece, St_in(p+1) = M_p St_in(p) + N_p, for one
+// 16-column slice of one head (one wavefront; state in registers, M_p rows
+// loaded as A fragments and split hi + lo, the state split hi + lo).
+// ---------------------------------------------------------------------------
+template <int DK, int DV>
+__global__ __launch_bounds__(kWave) void chain_kernel(const float *__restrict__ maps,
+                                                      const float *__restrict__ s0,
+                                                      float *__restrict__ starts, int P) {
+    constexpr int KT = DK / 16, KS = DK / 32, VT = DV / 16, MAPW = DV + DK;
+    const int lane = threadIdx.x, gq = lane / 16, li = lane % 16;
+    const int sl = blockIdx.x % VT;
+    const size_t bh = blockIdx.x / VT;
+    const int col = 16 * sl + li;
+    f32x4 St[KT];
+#pragma unroll
+    for (int mt = 0; mt < KT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) St[mt][r] = s0 ? s0[(bh * DK + 16 * mt + 4 * gq + r) * DV + col] : 0.f;
+    for (int p = 0; p < P; ++p) {
+#pragma unroll
+        for (int mt = 0; mt < KT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                starts[((bh * P + p) * DK + 16 * mt + 4 * gq + r) * DV + col] = St[mt][r];
+        if (p == P - 1) break;
+        const float *mp = maps + (bh * (P - 1) + p) * DK * MAPW;
+        bf16x8 Sh[KS], Sl[KS];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            float x[8];
+            acc_pair_to_slots(St[2 * s], St[2 * s + 1], x);
+            split_bf16(x, Sh[s], Sl[s]);
+        }
+#pragma unroll
+        for (int mt = 0; mt < KT; ++mt) {
+            f32x4 acc;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] = mp[(16 * mt + 4 * gq + r) * MAPW + col];  // N_p
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                float x[8];
+                lds_slots_f32(mp + (16 * mt + li) * MAPW + DV, s, gq, x);  // M_p row
+                bf16x8 mh, ml;
+                split_bf16(x, mh, ml);
+                acc = mfma_bf16(mh, Sh[s], acc);
+                acc = mfma_bf16(mh, Sl[s], acc);
+                acc = mfma_bf16(ml, Sh[s], acc);
+            }
+            St[mt] = acc;
+        }
+    }
+}
+
+// Piece plan: enough workgroups to fill the chip twice over, at least eight
+// chunks per piece, and no empty pieces.
+struct PiecePlan {
+    int P, piece_chunks;
+};
+PiecePlan piece_plan(int BH, int N) {
+    int P = (512 + BH - 1) / BH;
+    P = max(1, min(P, N / 8));
+    const int pc = (N + P - 1) / P;
+    return {(N + pc - 1) / pc, pc};
+}
+
+template <int DK, int DV, int C>
+size_t chunk_ws_bytes(int B, int T, int H) {
+    const int N = (T + C - 1) / C;
+    const int BH = B * H;
+    const int P = piece_plan(BH, N).P;
+    if (P == 1) return 0;
+    const size_t maps = static_cast<size_t>(BH) * (P - 1) * DK * (DV + DK) * 4;
+    const size_t starts = static_cast<size_t>(BH) * P * DK * DV * 4;
+    return ((maps + 255) & ~static_cast<size_t>(255)) + starts;
+}
+
+template <int DK, int DV, int C>
+hipError_t run_chunk(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,
+                     const float *beta, const float *s0, float *o, float *s_out, int B, int T, int H,
+                     void *ws, hipStream_t stream) {
+    const int N = (T + C - 1) / C;
+    const int BH = B * H;
+    const PiecePlan plan = piece_plan(BH, N);
+    const int P = plan.P;
+    ChunkArgs a{};
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.o = o; a.s_final = s_out;
+    a.T = T; a.H = H; a.P = P; a.N = N;
+    a.piece_chunks = plan.piece_chunks;
+    a.scale = 1.0f / sqrtf(static_cast<float>(DK));
+    if (P == 1) {
+        a.s_start = s0;
+        hipLaunchKernelGGL((chunk_kernel<DK, DV, C, false>), dim3(BH), dim3(kBlock), 0, stream, a);
+        return hipGetLastError();
+    }
+    const size_t maps_bytes = static_cast<size_t>(BH) * (P - 1) * DK * (DV + DK) * 4;
+    float *maps = static_cast<float *>(ws);
+    float *starts = reinterpret_cast<float *>(static_cast<char *>(ws) +
+                                              ((maps_bytes + 255) & ~static_cast<size_t>(255)));
+    a.maps = maps;
+    hipLaunchKernelGGL((chunk_kernel<DK, DV, C, true>), dim3(BH * (P - 1)), dim3(kBlock), 0, stream, a);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL((chain_kernel<DK, DV>), dim3(BH * (DV / 16)), dim3(kWave), 0, stream,
+                       static_cast<const float *>(maps), s0, starts, P);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    a.s_start = starts;
+    hipLaunchKernelGGL((chunk_kernel<DK, DV, C, false>), dim3(BH * P), dim3(kBlock), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+#define GDN_CHUNK_CASES(X) \
+    X(64, 64, 32) X(64, 64, 64) X(64, 128, 32) X(64, 128, 64) \
+    X(128, 64, 32) X(128, 64, 64) X(128, 128, 32) X(128, 128, 64)
+
+size_t prefill_chunk_workspace(int B, int T, int H, int dk, int dv, int chunk) {
+#define GDN_WS(DK_, DV_, C_) \
+    if (dk == DK_ && dv == DV_ && chunk == C_) return chunk_ws_bytes<DK_, DV_, C_>(B, T, H);
+    GDN_CHUNK_CASES(GDN_WS)
+#undef GDN_WS
+    return 0;
+}
+
+hipError_t launch_prefill_chunk(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                const float *g, const float *beta, const float *s0, float *o,
+                                float *s_out, int B, int T, int H, int dk, int dv, int chunk,
+                                void *ws, hipStream_t stream) {
+#define GDN_RUN(DK_, DV_, C_)                                                                      \
+    if (dk == DK_ && dv == DV_ && chunk == C_)                                                     \
+        return run_chunk<DK_, DV_, C_>(q, k, v, g, beta, s0, o, s_out, B, T, H, ws, stream);
+    GDN_CHUNK_CASES(GDN_RUN)
+#undef GDN_RUN
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gdn

@@ -45,7 +45,7 @@ def addr(i, size=1 << 30):
 
 def prefill(**kw):
     args = dict(q=addr(0), k=addr(1), v=addr(2), g=addr(3), beta=addr(4), s0=None, o=addr(5),
-                sf=addr(6), B=1, T=128, H=2, dk=64, dv=64, chunk=64, dt=BF16, ws=addr(7),
+                sf=addr(6), B=1, T=65536, H=2, dk=64, dv=64, chunk=64, dt=BF16, ws=addr(7),
                 ws_bytes=1 << 30, stream=None)
     args.update(kw)
     return gdn.gdn_chunk_prefill(args["q"], args["k"], args["v"], args["g"], args["beta"], args["s0"],
@@ -92,14 +92,16 @@ def test_decode_zero_sequences_is_a_no_op():
 
 
 def test_workspace_size():
-    # bf16 MFMA shapes need scratch, proportional to the number of chunks
-    w1 = gdn.gdn_chunk_prefill_workspace_size(1, 64, 32, 64, 64, 64, BF16)
-    w2 = gdn.gdn_chunk_prefill_workspace_size(1, 128, 32, 64, 64, 64, BF16)
-    assert w1 > 0 and abs(w2 - 2 * w1) < 4096
-    assert gdn.gdn_chunk_prefill_workspace_size(1, 65, 32, 64, 64, 64, BF16) == w2
-    # fp32 inputs and the VALU shapes keep everything on chip
+    # one sequence piece: everything stays on chip
+    assert gdn.gdn_chunk_prefill_workspace_size(1, 128, 32, 64, 64, 64, BF16) == 0
+    # long sequences with few heads are split into pieces; scratch holds the piece maps
+    # [DK][DV+DK] and start states [DK][DV], fp32, a few tens of MB at most
+    w = gdn.gdn_chunk_prefill_workspace_size(1, 65536, 32, 64, 64, 64, BF16)
+    assert 0 < w < 64 << 20
+    assert gdn.gdn_chunk_prefill_workspace_size(1, 65536, 24, 128, 128, 64, BF16) < 256 << 20
+    # fp32 inputs and the VALU shapes need none
     assert gdn.gdn_chunk_prefill_workspace_size(1, 64, 2, 16, 16, 16, F32) == 0
-    assert gdn.gdn_chunk_prefill_workspace_size(1, 64, 2, 64, 64, 16, BF16) == 0
+    assert gdn.gdn_chunk_prefill_workspace_size(1, 65536, 2, 64, 64, 16, BF16) == 0
     # rejected arguments and T = 0 need nothing
     assert gdn.gdn_chunk_prefill_workspace_size(1, 64, 2, 48, 64, 64, BF16) == 0
     assert gdn.gdn_chunk_prefill_workspace_size(1, 0, 2, 64, 64, 64, BF16) == 0

@@ -63,6 +63,17 @@ def test_bf16_mfma_path(orc, gate, dk, dv, chunk):
     check(orc, d, chunk, TOL["bf16"], f"bf16 dk={dk} dv={dv} gate={gate}")
 
 
+@pytest.mark.parametrize("gate", ["primary", "literal"])
+@pytest.mark.parametrize("dk,dv,chunk,T,s0", [
+    (64, 64, 64, 2560, True), (64, 64, 64, 2547, False), (128, 128, 64, 2560, True),
+    (64, 128, 32, 2600, True), (128, 64, 64, 4096, True)])
+def test_bf16_sequence_pieces(orc, gate, dk, dv, chunk, T, s0):
+    """Long sequences on few heads are split into pieces (piece maps, then a chained
+    start state per piece): every element, ragged tails included."""
+    d = inputs(1, T, 2, dk, dv, torch.bfloat16, s0=s0, gate=gate)
+    check(orc, d, chunk, TOL["bf16"], f"pieces T={T} dk={dk} dv={dv} gate={gate}")
+
+
 @pytest.mark.parametrize("dk,dv", [(16, 16), (16, 64), (64, 16), (64, 64)])
 def test_bf16_chunk16_and_small_heads(orc, dk, dv):
     d = inputs(1, 70, 2, dk, dv, torch.bfloat16)
@@ -219,12 +230,14 @@ def test_prefill_guard_regions_untouched():
 
 
 def test_prefill_error_has_no_side_effect():
-    d = inputs(1, 128, 2, 64, 64, torch.bfloat16)
-    o = torch.full((1, 128, 2, 64), 5.0, device=DEV)
-    sf = torch.full((1, 2, 64, 64), 6.0, device=DEV)
-    st = gdn.gdn_chunk_prefill(d["q"].data_ptr(), d["k"].data_ptr(), d["v"].data_ptr(),
-                               d["g"].data_ptr(), d["beta"].data_ptr(), d["s0"].data_ptr(),
-                               o.data_ptr(), sf.data_ptr(), 1, 128, 2, 64, 64, 64, gdn.GDN_BF16,
+    B, T, H, d = 1, 2560, 2, 64  # long enough to be split into pieces: needs workspace
+    assert gdn.workspace_bytes(B, T, H, d, d, 64, gdn.GDN_BF16) > 0
+    x = inputs(B, T, H, d, d, torch.bfloat16)
+    o = torch.full((B, T, H, d), 5.0, device=DEV)
+    sf = torch.full((B, H, d, d), 6.0, device=DEV)
+    st = gdn.gdn_chunk_prefill(x["q"].data_ptr(), x["k"].data_ptr(), x["v"].data_ptr(),
+                               x["g"].data_ptr(), x["beta"].data_ptr(), x["s0"].data_ptr(),
+                               o.data_ptr(), sf.data_ptr(), B, T, H, d, d, 64, gdn.GDN_BF16,
                                None, 0, None)
     torch.cuda.synchronize()
     assert st == 6  # workspace missing
