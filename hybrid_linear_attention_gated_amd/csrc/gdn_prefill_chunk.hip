@@ -116,6 +116,8 @@ struct ChunkRegs {
     float g, beta;
 };
 
+// K and V are loaded one chunk row per lane (so their transposed copies can be
+// written to LDS without bank conflicts); Q with consecutive lanes on one row.
 template <int DK, int DV, int C, bool MAP>
 __device__ __forceinline__ void load_chunk(ChunkRegs<DK, DV, C, MAP> &r, const ChunkArgs &a, int b,
                                            int h, int n, int tid) {
@@ -126,14 +128,20 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<DK, DV, C, MAP> &r, const C
     const u16x8 zero = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
     for (int i = 0; i < R::NK; ++i) {
-        const int e = tid + i * kBlock, rr = e / (DK / 8), c8 = e % (DK / 8);
-        const size_t off = (row0 + static_cast<size_t>(rr) * a.H) * DK + 8 * c8;
-        r.k[i] = rr < L ? *reinterpret_cast<const u16x8 *>(a.k + off) : zero;
-        if (!MAP) r.q[i] = rr < L ? *reinterpret_cast<const u16x8 *>(a.q + off) : zero;
+        const int e = tid + i * kBlock;
+        const int rr = e % C, c8 = e / C;
+        r.k[i] = rr < L ? *reinterpret_cast<const u16x8 *>(a.k + (row0 + static_cast<size_t>(rr) * a.H) * DK + 8 * c8)
+                        : zero;
+        if (!MAP) {
+            const int rq = e / (DK / 8), cq = e % (DK / 8);
+            r.q[i] = rq < L ? *reinterpret_cast<const u16x8 *>(a.q + (row0 + static_cast<size_t>(rq) * a.H) * DK + 8 * cq)
+                            : zero;
+        }
     }
 #pragma unroll
     for (int i = 0; i < R::NV; ++i) {
-        const int e = tid + i * kBlock, rr = e / (DV / 8), c8 = e % (DV / 8);
+        const int e = tid + i * kBlock;
+        const int rr = e % C, c8 = e / C;
         r.v[i] = rr < L ? *reinterpret_cast<const u16x8 *>(a.v + (row0 + static_cast<size_t>(rr) * a.H) * DV + 8 * c8)
                         : zero;
     }
@@ -155,13 +163,14 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
     constexpr int VSTR = C + kPad;    // V^T rows
     constexpr int CSTR = C + 4;       // A and T rows (fp32)
     constexpr int KV_ELEMS = C * KSTR > DV * VSTR ? C * KSTR : DV * VSTR;
+    constexpr int KTSTR = C + kPad;   // K^T rows
     static_assert(2 * G::CT * G::CS * kWave * 16 <= C * CSTR * 4, "P fragments fit in A's buffer");
     __shared__ __align__(16) uint16_t kv_s[KV_ELEMS];              // K rows, then V^T
     __shared__ __align__(16) uint16_t q_s[MAP ? 8 : C * KSTR];     // Q rows
     __shared__ __align__(16) float a_s[C * CSTR];                  // A, then P fragments
     __shared__ __align__(16) float t_s[C * CSTR];                  // T = (I + A)^{-1}
     __shared__ __align__(16) bf16x8 wf_s[G::CT * G::KS * kWave];   // W A-fragments
-    __shared__ __align__(16) bf16x8 kf_s[G::KT * G::CS * kWave];   // K^T A-fragments
+    __shared__ __align__(16) uint16_t kt_s[DK * KTSTR];            // K^T
     __shared__ __align__(16) f32x4 x_s[4 * kWave];                 // inversion block scratch
     __shared__ float g_s[C], b_s[C], bg_s[C], dec_s[C], gam_s[C];
 
@@ -199,6 +208,9 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
     uint16_t(*ks)[KSTR] = reinterpret_cast<uint16_t(*)[KSTR]>(kv_s);
     uint16_t(*vt)[VSTR] = reinterpret_cast<uint16_t(*)[VSTR]>(kv_s);
     uint16_t(*qs)[KSTR] = reinterpret_cast<uint16_t(*)[KSTR]>(q_s);
+    uint16_t(*kt)[KTSTR] = reinterpret_cast<uint16_t(*)[KTSTR]>(kt_s);
+    // K^T A-fragment (d tile mt, chunk-row step s): K^T[16 mt + li][kmap(s, gq, e)]
+    auto kfrag = [&](int mt, int s) { return lds_frag_bf16(&kt[16 * mt + li][0], s, gq); };
     float(*as)[CSTR] = reinterpret_cast<float(*)[CSTR]>(a_s);
     float(*ts)[CSTR] = reinterpret_cast<float(*)[CSTR]>(t_s);
     bf16x8 *pf_s = reinterpret_cast<bf16x8 *>(a_s);  // P fragments: ((mt * CS + s) * 2 + hi/lo) * 64 + lane
@@ -225,12 +237,18 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
         const int t0 = n * C;
         const int L = min(C, a.T - t0);
 
-        // ---- A: this chunk's rows into LDS; gates and their decays
+        // ---- A: this chunk's rows into LDS (K both row-major and transposed); gates
 #pragma unroll
         for (int i = 0; i < R::NK; ++i) {
-            const int e = tid + i * kBlock, rr = e / (DK / 8), c8 = e % (DK / 8);
+            const int e = tid + i * kBlock;
+            const int rr = e % C, c8 = e / C;
             *reinterpret_cast<u16x8 *>(&ks[rr][8 * c8]) = cur.k[i];
-            if (!MAP) *reinterpret_cast<u16x8 *>(&qs[rr][8 * c8]) = cur.q[i];
+#pragma unroll
+            for (int q8 = 0; q8 < 8; ++q8) kt[8 * c8 + q8][rr] = cur.k[i][q8];
+            if (!MAP) {
+                const int rq = e / (DK / 8), cq = e % (DK / 8);
+                *reinterpret_cast<u16x8 *>(&qs[rq][8 * cq]) = cur.q[i];
+            }
         }
         if (wave == 0) {
             // inclusive prefix sum of the gates; rows >= L add 0 and repeat G_{L-1}
@@ -252,7 +270,7 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
         }
         __syncthreads();
 
-        // ---- B: A = strict_tril(diag(b) (K K^T .* exp(G_r - G_j))); K^T A-fragments
+        // ---- B: A = strict_tril(diag(b) (K K^T .* exp(G_r - G_j)))
         {
             int idx = 0;
 #pragma unroll
@@ -265,18 +283,15 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
                     for (int s = 0; s < G::KS; ++s)
                         acc = mfma_bf16(lds_frag_bf16(&ks[16 * mt + li][0], s, gq),
                                         lds_frag_bf16(&ks[16 * nt + li][0], s, gq), acc);
+                    const f32x4 grow = *reinterpret_cast<const f32x4 *>(&g_s[16 * mt + 4 * gq]);
+                    const f32x4 brow = *reinterpret_cast<const f32x4 *>(&b_s[16 * mt + 4 * gq]);
+                    const float gcol = g_s[16 * nt + li];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int row = 16 * mt + 4 * gq + r, col = 16 * nt + li;
-                        as[row][col] = (row > col) ? b_s[row] * acc[r] * __expf(g_s[row] - g_s[col]) : 0.f;
+                        as[row][col] = (row > col) ? brow[r] * acc[r] * __expf(grow[r] - gcol) : 0.f;
                     }
                 }
-#pragma unroll
-            for (int f = 0; f < G::KT * G::CS; ++f) {
-                if ((idx + f) % kWaves != wave) continue;
-                const int mt = f / G::CS, s = f % G::CS;
-                kf_s[f * kWave + lane] = lds_colfrag(&ks[0][0], KSTR, 16 * mt + li, s, gq);
-            }
         }
         __syncthreads();
 
@@ -287,14 +302,32 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
         bf16x8 pfr[MAP ? 1 : 2][2];
         if (wave == 0) {
             if (gq < G::NB) {
+                // t[r] = T_aa[r][j]: t[r] = delta_rj - sum_{m<r} A[r][m] t[m]; the sum is
+                // taken as a pairwise tree so each row costs a few dependent adds
                 const int blk = gq, j = li;
                 float t[16];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    float acc = 0.f;
+                    float p[16];
 #pragma unroll
-                    for (int m = 0; m < r; ++m) acc += as[16 * blk + r][16 * blk + m] * t[m];
-                    t[r] = (r == j) ? 1.f : -acc;
+                    for (int m4 = 0; m4 < 4; ++m4) {
+                        if (4 * m4 >= r) break;
+                        const f32x4 av = *reinterpret_cast<const f32x4 *>(&as[16 * blk + r][16 * blk + 4 * m4]);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (4 * m4 + e < r) p[4 * m4 + e] = av[e] * t[4 * m4 + e];
+                    }
+                    int n = r;
+#pragma unroll
+                    for (int lvl = 0; lvl < 4; ++lvl) {
+                        if (n <= 1) break;
+#pragma unroll
+                        for (int i2 = 0; i2 < 8; ++i2)
+                            if (2 * i2 + 1 < n) p[i2] = p[2 * i2] + p[2 * i2 + 1];
+                            else if (2 * i2 < n) p[i2] = p[2 * i2];
+                        n = (n + 1) / 2;
+                    }
+                    t[r] = (r == j) ? 1.f : (r == 0 ? 0.f : -p[0]);
                 }
 #pragma unroll
                 for (int r = 0; r < 16; ++r) ts[16 * blk + r][16 * blk + j] = t[r];
@@ -374,7 +407,7 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
         }
 #pragma unroll
         for (int i = 0; i < R::NV; ++i) {
-            const int e = tid + i * kBlock, rr = e / (DV / 8), c8 = e % (DV / 8);
+            const int e = tid + i * kBlock, rr = e % C, c8 = e / C;
 #pragma unroll
             for (int q8 = 0; q8 < 8; ++q8) vt[8 * c8 + q8][rr] = cur.v[i][q8];
         }
@@ -394,8 +427,8 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
 #pragma unroll
                 for (int e = 0; e < 8; ++e) x[e] *= bg_s[kmap(s, gq, e)];
                 const bf16x8 bfr = pack_bf16(x);
-                acc0 = mfma_bf16(kf_s[((2 * s2) * G::CS + s) * kWave + lane], bfr, acc0);
-                acc1 = mfma_bf16(kf_s[((2 * s2 + 1) * G::CS + s) * kWave + lane], bfr, acc1);
+                acc0 = mfma_bf16(kfrag(2 * s2, s), bfr, acc0);
+                acc1 = mfma_bf16(kfrag(2 * s2 + 1, s), bfr, acc1);
             }
             float x[8];
             acc_pair_to_slots(acc0, acc1, x);
@@ -403,7 +436,7 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
         }
         __syncthreads();
 
-        // next chunk's rows: loads in flight while this chunk's slices are computed
+        // next chunk's rows: loads in flight during this chunk's slice work
         if (n + 1 < n1) load_chunk<DK, DV, C, MAP>(cur, a, b, h, n + 1, tid);
 
         // ---- G: per slice: U = (T diag b) V, Delta = U - W St, outputs, state update
@@ -462,30 +495,31 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
                     acc_pair_to_slots(D[2 * s], D[2 * s + 1], x);
                     split_bf16(x, Dh[s], Dl[s]);
                 }
-                float *orow = a.o + ((static_cast<size_t>(b) * a.T + t0) * a.H + h) * DV + 16 * sl + li;
+                // O^T tiles: with the operands swapped, lane (gq, li) holds O[16 mt + li][16 sl + 4 gq + r]
+                // for r = 0..3, i.e. four consecutive columns of one row -- one 16-byte store
+                float *obase = a.o + ((static_cast<size_t>(b) * a.T + t0) * a.H + h) * DV + 16 * sl + 4 * gq;
 #pragma unroll
                 for (int mt = 0; mt < G::CT; ++mt) {
                     f32x4 qsa = zero4, pd = zero4;
 #pragma unroll
                     for (int s = 0; s < G::KS; ++s) {
                         const bf16x8 qa = lds_frag_bf16(&qs[16 * mt + li][0], s, gq);
-                        qsa = mfma_bf16(qa, Sh[s], qsa);
-                        qsa = mfma_bf16(qa, Sl[s], qsa);
+                        qsa = mfma_bf16(Sh[s], qa, qsa);
+                        qsa = mfma_bf16(Sl[s], qa, qsa);
                     }
 #pragma unroll
                     for (int s = 0; s < G::CS; ++s) {
                         if (32 * s > 16 * mt + 15) continue;
                         const bf16x8 ph = pf_s[((mt * G::CS + s) * 2 + 0) * kWave + lane];
                         const bf16x8 pl = pf_s[((mt * G::CS + s) * 2 + 1) * kWave + lane];
-                        pd = mfma_bf16(ph, Dh[s], pd);
-                        pd = mfma_bf16(ph, Dl[s], pd);
-                        pd = mfma_bf16(pl, Dh[s], pd);
+                        pd = mfma_bf16(Dh[s], ph, pd);
+                        pd = mfma_bf16(Dl[s], ph, pd);
+                        pd = mfma_bf16(Dh[s], pl, pd);
                     }
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int row = 16 * mt + 4 * gq + r;
-                        if (row < L) orow[static_cast<size_t>(row) * a.H * DV] = a.scale * (gam_s[row] * qsa[r] + pd[r]);
-                    }
+                    const int row = 16 * mt + li;
+                    if (row < L)
+                        *reinterpret_cast<f32x4 *>(obase + static_cast<size_t>(row) * a.H * DV) =
+                            a.scale * (gam_s[row] * qsa + pd);
                 }
             }
 
@@ -508,7 +542,7 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
                 f32x4 acc = gl * St[j][mt];
 #pragma unroll
                 for (int s = 0; s < G::CS; ++s) {
-                    const bf16x8 kfr = kf_s[(mt * G::CS + s) * kWave + lane];
+                    const bf16x8 kfr = kfrag(mt, s);
                     acc = mfma_bf16(kfr, Eh[s], acc);
                     acc = mfma_bf16(kfr, El[s], acc);
                 }
