@@ -15,13 +15,18 @@ Each component is timed with HIP events recorded on the stream its kernels
 are launched on (the current torch stream).  `roofline` describes the
 prefill call (HBM-bound: algorithmic bytes / call time vs 8 TB/s), with the
 useful MFMA work (chunk-form FLOPs, no precision splits) as a fraction of the
-2.5 PFLOP/s bf16 dense peak next to it.  `cpu_baseline` is the fp64 oracle
-(tests only, never the product path) timed on the host cores on the same
-64K prefill workload.
+2.5 PFLOP/s bf16 dense peak next to it.  `roofline.traffic` is the HBM byte count of one
+call from the committed FETCH_SIZE/WRITE_SIZE counter summary, reported only
+while the kernel sources still hash to the digest recorded with it (else
+null).  Decode is also timed cold: a 1 GiB buffer is rewritten before every
+step (outside the timed events) so the state cannot come from the 256 MB
+last-level cache.  `cpu_baseline` is the fp64 oracle (tests only, never the
+product path) timed on the host cores on the same 64K prefill workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -43,6 +48,28 @@ FLOPS_PER_TOKEN_HEAD = 64 * (6 * 64 + 4 * 64) + 6 * 64 * 64 + 64 * 64 // 3
 # decode, per (sequence, head) per step: state read + write (2 * 4 * 64 * 64),
 # q, k, v bf16 (3 * 64 * 2), g, beta (8), o fp32 (64 * 4)
 DECODE_BYTES_PER_SEQ_HEAD = 2 * 4 * 64 * 64 + 3 * 64 * 2 + 8 + 64 * 4
+COPY_BYTES = 4 << 30  # far larger than the 256 MB last-level cache
+FLUSH_BYTES = 1 << 30
+CSRC = os.path.join(ROOT, "hybrid_linear_attention_gated_amd", "csrc")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_prefill_1b_64k_decode_n256_h32.md")
+
+
+def recorded_traffic(kind):
+    """Counter-measured HBM bytes for `kind` ('prefill' per call, 'decode' per step) from the
+    committed summary, or None when the kernel sources no longer match the recorded digest."""
+    try:
+        with open(TRAFFIC_SUMMARY) as f:
+            fields = dict(line.strip().split(": ", 1) for line in f if line.strip().startswith(kind + "-"))
+        d = hashlib.sha256()
+        for name in fields[kind + "-sources"].split():
+            with open(os.path.join(CSRC, name), "rb") as src:
+                d.update(src.read())
+        if d.hexdigest() != fields[kind + "-source-sha256"]:
+            return None
+        unit = "call" if kind == "prefill" else "step"
+        return int(fields[f"{kind}-traffic-bytes-per-{unit}"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def main():
@@ -53,8 +80,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=65536,
                     help="tokens of the 64K workload the oracle is timed on")
-    ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all",
-                    help="run one component (for profiling); the JSON line needs 'all'")
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "copy"], default="all",
+                    help="run one component (for profiling); 'copy' runs a plain 4 GiB device copy "
+                         "used to calibrate the HBM byte counters; the JSON line needs 'all'")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only; the GDN path shards over heads and "
@@ -69,6 +97,16 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
+
+    if args.only == "copy":
+        # counter calibration: each copy reads and writes exactly COPY_BYTES
+        src = torch.ones(COPY_BYTES // 4, device=dev, dtype=torch.float32)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"only": "copy", "bytes_per_copy": COPY_BYTES, "copies": args.warmup + args.steps}))
+        return
 
     # ---- inputs (resident before timing) ----
     w = gi.WORKLOADS["1b_64k"]
@@ -120,6 +158,20 @@ def main():
     if args.only != "all":
         print(json.dumps({"only": args.only, "steps": args.steps, "wall_ms": wall * 1e3}), flush=True)
         return
+
+    # decode with a cold last-level cache: rewrite a 1 GiB buffer before each step, outside the events
+    flush = torch.empty(FLUSH_BYTES // 4, device=dev, dtype=torch.float32)
+    cold_ev = [[(mk(), mk()) for _ in steps_in] for _ in range(max(1, args.steps // 4))]
+    for chain in cold_ev:
+        state.copy_(state0)
+        for s, d in enumerate(steps_in):
+            flush.fill_(float(s))
+            chain[s][0].record(stream)
+            gdn.decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], state, out=dout)
+            chain[s][1].record(stream)
+    torch.cuda.synchronize()
+    cold_ms = sorted(a.elapsed_time(b) for chain in cold_ev for a, b in chain)
+    cold_avg = sum(cold_ms) / len(cold_ms)
     pre_ms = sorted(a.elapsed_time(b) for a, b in pre_ev)
     dec_ms = sorted(a.elapsed_time(b) for step in dec_ev for a, b in step)
     pre_avg = sum(pre_ms) / len(pre_ms)
@@ -135,6 +187,7 @@ def main():
     tokens_per_s = w.B * w.T / (pre_avg * 1e-3)
     dec_bytes = dw.B * dw.H * DECODE_BYTES_PER_SEQ_HEAD
     dec_gbps = dec_bytes / (dec_avg * 1e-3) / 1e9
+    cold_gbps = dec_bytes / (cold_avg * 1e-3) / 1e9
 
     result = {
         "metric": "GDN prefill tokens/s at 64K (% bf16 MFMA peak); decode GB/s (% HBM peak)",
@@ -165,12 +218,16 @@ def main():
             "us_per_step_avg": round(dec_avg * 1e3, 2), "us_per_step_median": round(med(dec_ms) * 1e3, 2),
             "GBps": round(dec_gbps, 1), "hbm_frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
             "bytes_per_step": dec_bytes,
-            "note": "16 back-to-back steps; the 128 MiB state can stay in the 256 MB last-level cache",
+            "cold_us_per_step_avg": round(cold_avg * 1e3, 2), "cold_GBps": round(cold_gbps, 1),
+            "cold_hbm_frac": round(cold_gbps / HBM_PEAK_GBPS, 4),
+            "traffic_bytes_per_step": recorded_traffic("decode"),
+            "note": "warm: 16 back-to-back steps, the 128 MiB state can stay in the 256 MB last-level "
+                    "cache; cold: a 1 GiB buffer is rewritten before every step",
         },
         "roofline": {
-            "kernel": "gdn_chunk_prefill (prep + scan + output kernels of one call)",
+            "kernel": "one gdn_chunk_prefill call: chunk_kernel MAP + chain_kernel + chunk_kernel OUT",
             "bound": "hbm", "achieved": round(pre_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": round(pre_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+            "frac": round(pre_gbps / HBM_PEAK_GBPS, 4), "traffic": recorded_traffic("prefill"),
         },
     }
 

@@ -1,0 +1,40 @@
+"""Host-side logic of bench.py (CPU only): the recorded HBM traffic is reported only for the
+kernel sources it was measured on."""
+import os
+import shutil
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_traffic_is_none_once_a_source_changes(tmp_path, monkeypatch):
+    csrc = tmp_path / "csrc"
+    shutil.copytree(bench.CSRC, csrc)
+    monkeypatch.setattr(bench, "CSRC", str(csrc))
+    before = {k: bench.recorded_traffic(k) for k in ("prefill", "decode")}
+    with open(csrc / "gdn_internal.h", "a") as f:
+        f.write("\n// edited\n")
+    assert bench.recorded_traffic("prefill") is None
+    assert bench.recorded_traffic("decode") is None
+    # unchanged sources give either the recorded figure or None (stale summary), never an error
+    for v in before.values():
+        assert v is None or v > 0
+
+
+def test_traffic_summary_missing_gives_none(monkeypatch):
+    monkeypatch.setattr(bench, "TRAFFIC_SUMMARY", "/nonexistent/summary.md")
+    assert bench.recorded_traffic("prefill") is None
+
+
+def test_multi_gpu_request_exits_with_message(monkeypatch, capsys):
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--gpus", "2"])
+    try:
+        bench.main()
+    except SystemExit as e:
+        assert e.code == 2
+    else:
+        raise AssertionError("bench.py --gpus 2 must exit")
+    assert "one GPU" in capsys.readouterr().err
