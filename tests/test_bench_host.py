@@ -38,3 +38,10 @@ def test_multi_gpu_request_exits_with_message(monkeypatch, capsys):
     else:
         raise AssertionError("bench.py --gpus 2 must exit")
     assert "one GPU" in capsys.readouterr().err
+
+
+def test_build_entry_resolves_both_builders():
+    # __graft_entry__.build() calls these two; a name clash once made it fail before compiling
+    import oracle
+    from hybrid_linear_attention_gated_amd import build as gdn_build
+    assert callable(oracle.build) and callable(gdn_build.build)
