@@ -44,7 +44,9 @@ namespace {
 constexpr int kWave = 64;
 constexpr int kWaves = 4;
 constexpr int kBlock = kWave * kWaves;
-constexpr int kPad = 8;  // bf16 row padding in LDS
+// bf16 row padding in LDS: row strides of 2 * odd dwords, so the 8-byte fragment
+// reads of 16 consecutive rows (one per lane) cover all 32 banks once
+constexpr int kPad = 4;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
@@ -100,12 +102,10 @@ struct ChunkArgs {
     float scale;
 };
 
-// Column fragment of a row-major bf16 LDS matrix M: slots e hold M[kmap(s, gq, e)][col].
-__device__ __forceinline__ bf16x8 lds_colfrag(const uint16_t *m, int stride, int col, int s, int gq) {
-    u16x8 u;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) u[e] = m[kmap(s, gq, e) * stride + col];
-    return as_bf16x8(u);
+// Eight bf16 to an 8-byte aligned LDS address (padded rows are not 16-byte aligned).
+__device__ __forceinline__ void lds_store8(uint16_t *p, u16x8 x) {
+    reinterpret_cast<u16x4 *>(p)[0] = u16x4{x[0], x[1], x[2], x[3]};
+    reinterpret_cast<u16x4 *>(p)[1] = u16x4{x[4], x[5], x[6], x[7]};
 }
 
 // Per-thread share of one chunk's rows, loaded from HBM one chunk ahead.
@@ -118,36 +118,44 @@ struct ChunkRegs {
 
 // K and V are loaded one chunk row per lane (so their transposed copies can be
 // written to LDS without bank conflicts); Q with consecutive lanes on one row.
+// Addresses are a per-chunk base (uniform) plus a 32-bit lane offset.
 template <int DK, int DV, int C, bool MAP>
 __device__ __forceinline__ void load_chunk(ChunkRegs<DK, DV, C, MAP> &r, const ChunkArgs &a, int b,
                                            int h, int n, int tid) {
     using R = ChunkRegs<DK, DV, C, MAP>;
+    // the lane offsets below are cheap to rebuild per chunk; hoisted out of the chunk loop
+    // they would hold a dozen registers for its whole length
+    __asm__ __volatile__("" : "+v"(tid));
     const int t0 = n * C;
     const int L = min(C, a.T - t0);
     const size_t row0 = (static_cast<size_t>(b) * a.T + t0) * a.H + h;  // token-head row of t0
+    const uint16_t *kb = a.k + row0 * DK;
+    const uint16_t *qb = a.q + row0 * DK;
+    const uint16_t *vb = a.v + row0 * DV;
     const u16x8 zero = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
     for (int i = 0; i < R::NK; ++i) {
         const int e = tid + i * kBlock;
         const int rr = e % C, c8 = e / C;
-        r.k[i] = rr < L ? *reinterpret_cast<const u16x8 *>(a.k + (row0 + static_cast<size_t>(rr) * a.H) * DK + 8 * c8)
-                        : zero;
+        const unsigned off = static_cast<unsigned>(rr * a.H * DK + 8 * c8);
+        r.k[i] = rr < L ? *reinterpret_cast<const u16x8 *>(kb + off) : zero;
         if (!MAP) {
             const int rq = e / (DK / 8), cq = e % (DK / 8);
-            r.q[i] = rq < L ? *reinterpret_cast<const u16x8 *>(a.q + (row0 + static_cast<size_t>(rq) * a.H) * DK + 8 * cq)
-                            : zero;
+            const unsigned offq = static_cast<unsigned>(rq * a.H * DK + 8 * cq);
+            r.q[i] = rq < L ? *reinterpret_cast<const u16x8 *>(qb + offq) : zero;
         }
     }
 #pragma unroll
     for (int i = 0; i < R::NV; ++i) {
         const int e = tid + i * kBlock;
         const int rr = e % C, c8 = e / C;
-        r.v[i] = rr < L ? *reinterpret_cast<const u16x8 *>(a.v + (row0 + static_cast<size_t>(rr) * a.H) * DV + 8 * c8)
-                        : zero;
+        const unsigned off = static_cast<unsigned>(rr * a.H * DV + 8 * c8);
+        r.v[i] = rr < L ? *reinterpret_cast<const u16x8 *>(vb + off) : zero;
     }
     const int lane = tid % kWave;
-    r.g = (tid < kWave && lane < L) ? a.g[row0 + static_cast<size_t>(lane) * a.H] : 0.f;
-    r.beta = (tid < kWave && lane < L) ? a.beta[row0 + static_cast<size_t>(lane) * a.H] : 0.f;
+    const unsigned offg = static_cast<unsigned>(lane * a.H);
+    r.g = (tid < kWave && lane < L) ? a.g[row0 + offg] : 0.f;
+    r.beta = (tid < kWave && lane < L) ? a.beta[row0 + offg] : 0.f;
 }
 
 // Two workgroups per compute unit where LDS allows it (64-wide heads), so one
@@ -165,6 +173,10 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
     constexpr int KV_ELEMS = C * KSTR > DV * VSTR ? C * KSTR : DV * VSTR;
     constexpr int KTSTR = C + kPad;   // K^T rows
     static_assert(2 * G::CT * G::CS * kWave * 16 <= C * CSTR * 4, "P fragments fit in A's buffer");
+    // With one 16-row tile of T per wavefront (chunk 64), F builds the hi/lo fragments of
+    // T diag(b) once and parks them over that wavefront's own (then dead) T rows.
+    constexpr bool kTbFrags = G::CT == kWaves;
+    static_assert(!kTbFrags || 2 * G::CS * kWave * 16 <= 16 * CSTR * 4, "T diag(b) fragments fit in 16 T rows");
     __shared__ __align__(16) uint16_t kv_s[KV_ELEMS];              // K rows, then V^T
     __shared__ __align__(16) uint16_t q_s[MAP ? 8 : C * KSTR];     // Q rows
     __shared__ __align__(16) float a_s[C * CSTR];                  // A, then P fragments
@@ -174,7 +186,8 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
     __shared__ __align__(16) f32x4 x_s[4 * kWave];                 // inversion block scratch
     __shared__ float g_s[C], b_s[C], bg_s[C], dec_s[C], gam_s[C];
 
-    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform
+    const int tid = threadIdx.x, lane = tid % kWave;
     const int gq = lane / 16, li = lane % 16;
     const int pieces = MAP ? a.P - 1 : a.P;
     const int piece = blockIdx.x % pieces;
@@ -242,12 +255,12 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
         for (int i = 0; i < R::NK; ++i) {
             const int e = tid + i * kBlock;
             const int rr = e % C, c8 = e / C;
-            *reinterpret_cast<u16x8 *>(&ks[rr][8 * c8]) = cur.k[i];
+            lds_store8(&ks[rr][8 * c8], cur.k[i]);
 #pragma unroll
             for (int q8 = 0; q8 < 8; ++q8) kt[8 * c8 + q8][rr] = cur.k[i][q8];
             if (!MAP) {
                 const int rq = e / (DK / 8), cq = e % (DK / 8);
-                *reinterpret_cast<u16x8 *>(&qs[rq][8 * cq]) = cur.q[i];
+                lds_store8(&qs[rq][8 * cq], cur.q[i]);
             }
         }
         if (wave == 0) {
@@ -270,28 +283,56 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
         }
         __syncthreads();
 
-        // ---- B: A = strict_tril(diag(b) (K K^T .* exp(G_r - G_j)))
+        // ---- B: A = strict_tril(diag(b) (K K^T .* exp(G_r - G_j))).  The CT (CT + 1) / 2 lower
+        // tiles go round-robin to the wavefronts; each wavefront issues all its fragment loads
+        // and products before the exps (a surplus slot computes tile 0 and stores nothing).
         {
-            int idx = 0;
+            constexpr int NTL = G::CT * (G::CT + 1) / 2, PER = (NTL + kWaves - 1) / kWaves;
+            int mts[PER], nts[PER];
+            bool ok[PER];
 #pragma unroll
-            for (int mt = 0; mt < G::CT; ++mt)
+            for (int i = 0; i < PER; ++i) {
+                const int idx = wave + kWaves * i;
+                ok[i] = idx < NTL;
+                const int id = ok[i] ? idx : 0;
+                int mt = 0;
 #pragma unroll
-                for (int nt = 0; nt <= mt; ++nt, ++idx) {
-                    if (idx % kWaves != wave) continue;
-                    f32x4 acc = zero4;
+                for (int m = 1; m < G::CT; ++m) mt += (id >= m * (m + 1) / 2) ? 1 : 0;
+                mts[i] = mt;
+                nts[i] = id - mt * (mt + 1) / 2;
+            }
+            f32x4 acc[PER];
 #pragma unroll
-                    for (int s = 0; s < G::KS; ++s)
-                        acc = mfma_bf16(lds_frag_bf16(&ks[16 * mt + li][0], s, gq),
-                                        lds_frag_bf16(&ks[16 * nt + li][0], s, gq), acc);
-                    const f32x4 grow = *reinterpret_cast<const f32x4 *>(&g_s[16 * mt + 4 * gq]);
-                    const f32x4 brow = *reinterpret_cast<const f32x4 *>(&b_s[16 * mt + 4 * gq]);
-                    const float gcol = g_s[16 * nt + li];
+            for (int i = 0; i < PER; ++i) {
+                acc[i] = zero4;
+#pragma unroll
+                for (int s = 0; s < G::KS; ++s)
+                    acc[i] = mfma_bf16(lds_frag_bf16(&ks[16 * mts[i] + li][0], s, gq),
+                                       lds_frag_bf16(&ks[16 * nts[i] + li][0], s, gq), acc[i]);
+            }
+#pragma unroll
+            for (int i = 0; i < PER; ++i) {
+                const f32x4 grow = *reinterpret_cast<const f32x4 *>(&g_s[16 * mts[i] + 4 * gq]);
+                const f32x4 brow = *reinterpret_cast<const f32x4 *>(&b_s[16 * mts[i] + 4 * gq]);
+                const int col = 16 * nts[i] + li;
+                const float gcol = g_s[col];
+                if (ok[i]) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const int row = 16 * mt + 4 * gq + r, col = 16 * nt + li;
-                        as[row][col] = (row > col) ? brow[r] * acc[r] * __expf(grow[r] - gcol) : 0.f;
+                        const int row = 16 * mts[i] + 4 * gq + r;
+                        // exp of a clamped exponent times a 0/1 mask: no divergent branch
+                        const float ex = __expf(fminf(grow[r] - gcol, 0.f));
+                        as[row][col] = ((row > col) ? 1.f : 0.f) * (brow[r] * acc[i][r] * ex);
                     }
                 }
+            }
+            if constexpr (kTbFrags) {
+                // T's blocks (0,1) and (2,3) are read as zeros by F; last chunk's T diag(b)
+                // fragments (written over T's rows) are dead, so clear them again
+                const int r = tid / 16, c = 16 + tid % 16;
+                ts[r][c] = 0.f;
+                ts[32 + r][32 + c] = 0.f;
+            }
         }
         __syncthreads();
 
@@ -365,7 +406,8 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
                     for (int e = 0; e < 8; ++e) {
                         const int jj = kmap(s, gq, e);
                         const float qk = acc[e >> 2][e & 3];
-                        x[e] = (jj <= r) ? qk * __expf(g_s[r] - g_s[jj]) : 0.f;
+                        const float ex = __expf(fminf(g_s[r] - g_s[jj], 0.f));
+                        x[e] = ((jj <= r) ? 1.f : 0.f) * (qk * ex);
                     }
                     split_bf16(x, pfr[mine / (kWaves - 1)][0], pfr[mine / (kWaves - 1)][1]);
                 }
@@ -414,25 +456,74 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
         __syncthreads();
 
         // ---- F: W A-fragments = W^T tiles (2 s2, ct) and (2 s2 + 1, ct), W = T diag(b exp G) K
+        auto tb_frag = [&](int ct, int s, int hl) -> bf16x8 * {
+            return reinterpret_cast<bf16x8 *>(&ts[16 * ct][0]) + (s * 2 + hl) * kWave + lane;
+        };
+        if constexpr (kTbFrags) {
+            // wavefront ct owns T's row tile ct: one pass over it gives T diag(b exp G) for
+            // every W tile of that row and the T diag(b) fragments of U
+            const int ct = wave;
+            f32x4 accw[G::KT];
 #pragma unroll
-        for (int p = 0; p < G::CT * G::KS; ++p) {
-            if (p % kWaves != wave) continue;
-            const int ct = p % G::CT, s2 = p / G::CT;
-            f32x4 acc0 = zero4, acc1 = zero4;
+            for (int mt = 0; mt < G::KT; ++mt) accw[mt] = zero4;
+            bf16x8 tbh[G::CS], tbl[G::CS];
 #pragma unroll
             for (int s = 0; s < G::CS; ++s) {
                 if (32 * s > 16 * ct + 15) continue;  // T is lower triangular
-                float x[8];
+                float x[8], xg[8], xb[8];
                 lds_slots_f32(&ts[16 * ct + li][0], s, gq, x);
+                const f32x4 bg0 = *reinterpret_cast<const f32x4 *>(&bg_s[32 * s + 4 * gq]);
+                const f32x4 bg1 = *reinterpret_cast<const f32x4 *>(&bg_s[32 * s + 16 + 4 * gq]);
+                const f32x4 b0 = *reinterpret_cast<const f32x4 *>(&b_s[32 * s + 4 * gq]);
+                const f32x4 b1 = *reinterpret_cast<const f32x4 *>(&b_s[32 * s + 16 + 4 * gq]);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] *= bg_s[kmap(s, gq, e)];
-                const bf16x8 bfr = pack_bf16(x);
-                acc0 = mfma_bf16(kfrag(2 * s2, s), bfr, acc0);
-                acc1 = mfma_bf16(kfrag(2 * s2 + 1, s), bfr, acc1);
+                for (int e = 0; e < 4; ++e) {
+                    xg[e] = x[e] * bg0[e];
+                    xg[4 + e] = x[4 + e] * bg1[e];
+                    xb[e] = x[e] * b0[e];
+                    xb[4 + e] = x[4 + e] * b1[e];
+                }
+                const bf16x8 bfr = pack_bf16(xg);
+                split_bf16(xb, tbh[s], tbl[s]);
+#pragma unroll
+                for (int mt = 0; mt < G::KT; ++mt) accw[mt] = mfma_bf16(kfrag(mt, s), bfr, accw[mt]);
             }
-            float x[8];
-            acc_pair_to_slots(acc0, acc1, x);
-            wf_s[(ct * G::KS + s2) * kWave + lane] = pack_bf16(x);
+#pragma unroll
+            for (int s2 = 0; s2 < G::KS; ++s2) {
+                float x[8];
+                acc_pair_to_slots(accw[2 * s2], accw[2 * s2 + 1], x);
+                wf_s[(ct * G::KS + s2) * kWave + lane] = pack_bf16(x);
+            }
+            // this wavefront's T rows have all been read (LDS keeps a wavefront's accesses in
+            // order); keep the compiler from moving the stores above the loads
+            __asm__ __volatile__("" ::: "memory");
+#pragma unroll
+            for (int s = 0; s < G::CS; ++s) {
+                if (32 * s > 16 * ct + 15) continue;
+                *tb_frag(ct, s, 0) = tbh[s];
+                *tb_frag(ct, s, 1) = tbl[s];
+            }
+        } else {
+#pragma unroll
+            for (int p = 0; p < G::CT * G::KS; ++p) {
+                if (p % kWaves != wave) continue;
+                const int ct = p % G::CT, s2 = p / G::CT;
+                f32x4 acc0 = zero4, acc1 = zero4;
+#pragma unroll
+                for (int s = 0; s < G::CS; ++s) {
+                    if (32 * s > 16 * ct + 15) continue;  // T is lower triangular
+                    float x[8];
+                    lds_slots_f32(&ts[16 * ct + li][0], s, gq, x);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) x[e] *= bg_s[kmap(s, gq, e)];
+                    const bf16x8 bfr = pack_bf16(x);
+                    acc0 = mfma_bf16(kfrag(2 * s2, s), bfr, acc0);
+                    acc1 = mfma_bf16(kfrag(2 * s2 + 1, s), bfr, acc1);
+                }
+                float x[8];
+                acc_pair_to_slots(acc0, acc1, x);
+                wf_s[(ct * G::KS + s2) * kWave + lane] = pack_bf16(x);
+            }
         }
         __syncthreads();
 
@@ -454,12 +545,17 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
 #pragma unroll
                     for (int ct = 0; ct < G::CT; ++ct) {
                         if (32 * s > 16 * ct + 15) continue;  // T is lower triangular
-                        float x[8];
-                        lds_slots_f32(&ts[16 * ct + li][0], s, gq, x);
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) x[e] *= b_s[kmap(s, gq, e)];
                         bf16x8 th, tl;
-                        split_bf16(x, th, tl);
+                        if constexpr (kTbFrags) {
+                            th = *tb_frag(ct, s, 0);
+                            tl = *tb_frag(ct, s, 1);
+                        } else {
+                            float x[8];
+                            lds_slots_f32(&ts[16 * ct + li][0], s, gq, x);
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) x[e] *= b_s[kmap(s, gq, e)];
+                            split_bf16(x, th, tl);
+                        }
                         D[ct] = mfma_bf16(th, vb, D[ct]);
                         D[ct] = mfma_bf16(tl, vb, D[ct]);
                     }
@@ -497,7 +593,7 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
                 }
                 // O^T tiles: with the operands swapped, lane (gq, li) holds O[16 mt + li][16 sl + 4 gq + r]
                 // for r = 0..3, i.e. four consecutive columns of one row -- one 16-byte store
-                float *obase = a.o + ((static_cast<size_t>(b) * a.T + t0) * a.H + h) * DV + 16 * sl + 4 * gq;
+                float *obase = a.o + ((static_cast<size_t>(b) * a.T + t0) * a.H + h) * DV;  // uniform
 #pragma unroll
                 for (int mt = 0; mt < G::CT; ++mt) {
                     f32x4 qsa = zero4, pd = zero4;
@@ -518,7 +614,7 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
                     }
                     const int row = 16 * mt + li;
                     if (row < L)
-                        *reinterpret_cast<f32x4 *>(obase + static_cast<size_t>(row) * a.H * DV) =
+                        *reinterpret_cast<f32x4 *>(obase + static_cast<unsigned>(row * a.H * DV + 16 * sl + 4 * gq)) =
                             a.scale * (gam_s[row] * qsa + pd);
                 }
             }
