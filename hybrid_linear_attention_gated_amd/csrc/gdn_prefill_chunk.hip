@@ -36,6 +36,8 @@
 // W and the state in W St are single bf16; T diag(b) in U, the state in
 // Q St, P and Delta in P Delta, the decayed Delta in the state update and
 // both factors of the inversion's block products are hi + lo bf16 pairs.
+#include <type_traits>
+
 #include "gdn_mfma.h"
 
 namespace gdn {
@@ -55,6 +57,21 @@ __device__ __forceinline__ f32x4 mfma16(s16x4 a, s16x4 b, f32x4 c) {
 }
 
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+struct FragPair {
+    bf16x8 h, l;  // hi and lo bf16 parts of one MFMA operand fragment
+};
+
+template <int N>
+using IC = std::integral_constant<int, N>;
+
+// x from the lane whose index differs in bit 0 (resp. bit 1): DPP quad permutations
+__device__ __forceinline__ float quad_xor1(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float quad_xor2(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
+}
 
 __device__ __forceinline__ void split4(f32x4 x, s16x4 &hi, s16x4 &lo) {
     u32x2 h, l;
@@ -172,6 +189,7 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
     constexpr int CSTR = C + 4;       // A and T rows (fp32)
     constexpr int KV_ELEMS = C * KSTR > DV * VSTR ? C * KSTR : DV * VSTR;
     constexpr int KTSTR = C + kPad;   // K^T rows
+    constexpr int CSTR16 = 20;        // rows of the 16x16 scratch tile (conflict-free f32x4 reads)
     static_assert(2 * G::CT * G::CS * kWave * 16 <= C * CSTR * 4, "P fragments fit in A's buffer");
     // With one 16-row tile of T per wavefront (chunk 64), F builds the hi/lo fragments of
     // T diag(b) once and parks them over that wavefront's own (then dead) T rows.
@@ -183,7 +201,7 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
     __shared__ __align__(16) float t_s[C * CSTR];                  // T = (I + A)^{-1}
     __shared__ __align__(16) bf16x8 wf_s[G::CT * G::KS * kWave];   // W A-fragments
     __shared__ __align__(16) uint16_t kt_s[DK * KTSTR];            // K^T
-    __shared__ __align__(16) f32x4 x_s[4 * kWave];                 // inversion block scratch
+    __shared__ __align__(16) float x_s[16 * CSTR16];              // one 16x16 fp32 tile (C)
     __shared__ float g_s[C], b_s[C], bg_s[C], dec_s[C], gam_s[C];
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform
@@ -228,16 +246,18 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
     float(*ts)[CSTR] = reinterpret_cast<float(*)[CSTR]>(t_s);
     bf16x8 *pf_s = reinterpret_cast<bf16x8 *>(a_s);  // P fragments: ((mt * CS + s) * 2 + hi/lo) * 64 + lane
 
-    auto rowfrag = [&](const float(*m)[CSTR], int r0, int c0) {
+    float(*xs)[CSTR16] = reinterpret_cast<float(*)[CSTR16]>(x_s);
+    // 16x16 fp32 blocks of a row-major LDS matrix as MFMA operands
+    auto rowfrag = [&](auto m, int r0, int c0) {
         return *reinterpret_cast<const f32x4 *>(&m[r0 + li][c0 + 4 * gq]);
     };
-    auto accfrag = [&](const float(*m)[CSTR], int r0, int c0) {
+    auto accfrag = [&](auto m, int r0, int c0) {
         f32x4 x;
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[e] = m[r0 + 4 * gq + e][c0 + li];
         return x;
     };
-    auto store_acc = [&](float(*m)[CSTR], int r0, int c0, f32x4 x) {
+    auto store_acc = [&](auto m, int r0, int c0, f32x4 x) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) m[r0 + 4 * gq + e][c0 + li] = x[e];
     };
@@ -283,169 +303,222 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
         }
         __syncthreads();
 
-        // ---- B: A = strict_tril(diag(b) (K K^T .* exp(G_r - G_j))).  The CT (CT + 1) / 2 lower
-        // tiles go round-robin to the wavefronts; each wavefront issues all its fragment loads
-        // and products before the exps (a surplus slot computes tile 0 and stores nothing).
-        {
-            constexpr int NTL = G::CT * (G::CT + 1) / 2, PER = (NTL + kWaves - 1) / kWaves;
-            int mts[PER], nts[PER];
-            bool ok[PER];
+        // ---- B: A = strict_tril(diag(b) (K K^T .* exp(G_r - G_j))) tile by tile, then each
+        // wavefront inverts the diagonal block of (I + A) whose A tile it computed itself, so no
+        // barrier separates the two.  Tiles (C = 64): w0 (0,0) (1,0) (2,0); w1 (1,1) (2,1) (3,0);
+        // w2 (2,2) (3,1); w3 (3,3) (3,2); w2 and w3 also form the two single-product P tiles.
+        auto a_tile = [&](auto mt_c, auto nt_c) {
+            constexpr int mt = decltype(mt_c)::value, nt = decltype(nt_c)::value;
+            f32x4 acc = zero4;
 #pragma unroll
-            for (int i = 0; i < PER; ++i) {
-                const int idx = wave + kWaves * i;
-                ok[i] = idx < NTL;
-                const int id = ok[i] ? idx : 0;
-                int mt = 0;
+            for (int s = 0; s < G::KS; ++s)
+                acc = mfma_bf16(lds_frag_bf16(&ks[16 * mt + li][0], s, gq), lds_frag_bf16(&ks[16 * nt + li][0], s, gq),
+                                acc);
+            const f32x4 grow = *reinterpret_cast<const f32x4 *>(&g_s[16 * mt + 4 * gq]);
+            const f32x4 brow = *reinterpret_cast<const f32x4 *>(&b_s[16 * mt + 4 * gq]);
+            const int col = 16 * nt + li;
+            const float gcol = g_s[col];
 #pragma unroll
-                for (int m = 1; m < G::CT; ++m) mt += (id >= m * (m + 1) / 2) ? 1 : 0;
-                mts[i] = mt;
-                nts[i] = id - mt * (mt + 1) / 2;
-            }
-            f32x4 acc[PER];
-#pragma unroll
-            for (int i = 0; i < PER; ++i) {
-                acc[i] = zero4;
-#pragma unroll
-                for (int s = 0; s < G::KS; ++s)
-                    acc[i] = mfma_bf16(lds_frag_bf16(&ks[16 * mts[i] + li][0], s, gq),
-                                       lds_frag_bf16(&ks[16 * nts[i] + li][0], s, gq), acc[i]);
-            }
-#pragma unroll
-            for (int i = 0; i < PER; ++i) {
-                const f32x4 grow = *reinterpret_cast<const f32x4 *>(&g_s[16 * mts[i] + 4 * gq]);
-                const f32x4 brow = *reinterpret_cast<const f32x4 *>(&b_s[16 * mts[i] + 4 * gq]);
-                const int col = 16 * nts[i] + li;
-                const float gcol = g_s[col];
-                if (ok[i]) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int row = 16 * mts[i] + 4 * gq + r;
-                        // exp of a clamped exponent times a 0/1 mask: no divergent branch
-                        const float ex = __expf(fminf(grow[r] - gcol, 0.f));
-                        as[row][col] = ((row > col) ? 1.f : 0.f) * (brow[r] * acc[i][r] * ex);
-                    }
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * mt + 4 * gq + r;
+                if constexpr (mt > nt) {
+                    as[row][col] = brow[r] * acc[r] * __expf(grow[r] - gcol);
+                } else {
+                    // diagonal tile: exp of a clamped exponent times a 0/1 mask (no branch)
+                    const float ex = __expf(fminf(grow[r] - gcol, 0.f));
+                    as[row][col] = ((row > col) ? 1.f : 0.f) * (brow[r] * acc[r] * ex);
                 }
             }
+        };
+        // Diagonal block w of T = (I + A)^{-1} by forward substitution, t_r = delta_rj -
+        // sum_{m<r} A[r][m] t_m down column j.  Lane (j, q) = (lane / 4, lane % 4) sums the terms
+        // m in [4q, 4q + 4); two quad-lane adds complete each row.  A is strictly lower and t_m
+        // is zero until its row is reached, so nothing needs masking.  Reads only this
+        // wavefront's own A tile (LDS keeps a wavefront's accesses in order).
+        auto inv_diag = [&]() {
+            const int bb = 16 * wave, j = lane >> 2, q = lane & 3;
+            f32x4 arow[16];
+#pragma unroll
+            for (int r = 1; r < 16; ++r) arow[r] = *reinterpret_cast<const f32x4 *>(&as[bb + r][bb + 4 * q]);
+            float tq[4] = {0.f, 0.f, 0.f, 0.f};  // t_m for m = 4q + i
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float t;
+                if (r == 0) {
+                    t = (j == 0) ? 1.f : 0.f;
+                } else {
+                    const int k = (r - 1) & 3;  // slot of the newest t (added last)
+                    float p = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (i != k) p = fmaf(arow[r][i], tq[i], p);
+                    p = fmaf(arow[r][k], tq[k], p);
+                    p += quad_xor1(p);
+                    p += quad_xor2(p);
+                    t = (r == j) ? 1.f : -p;
+                }
+                tq[r & 3] = (q == (r >> 2)) ? t : tq[r & 3];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ts[bb + 4 * q + i][bb + j] = tq[i];
+        };
+        // P tiles (mt, s): formed into registers (P^T accumulator tiles are P's A-fragment
+        // layout, split hi + lo), stored in F once A's buffer is free.  Per wavefront (chunk 64):
+        // B: w2 (0,0), w3 (2,1) (single products); C: w0 (3,0), w1 (1,0) (2,0), w2 (3,1).
+        auto p_pair = [&](auto mt_c, auto s_c) {
+            constexpr int mt = decltype(mt_c)::value, s = decltype(s_c)::value;
+            f32x4 acc[2] = {zero4, zero4};
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int jt = 2 * s + half;
+                if (jt > mt) continue;
+#pragma unroll
+                for (int ss = 0; ss < G::KS; ++ss)
+                    acc[half] = mfma_bf16(lds_frag_bf16(&ks[16 * jt + li][0], ss, gq),
+                                          lds_frag_bf16(&qs[16 * mt + li][0], ss, gq), acc[half]);
+            }
+            // lane holds P[r][j] for r = 16 mt + li and j = kmap(s, gq, e)
+            const int r = 16 * mt + li;
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int jj = kmap(s, gq, e);
+                const float qk = acc[e >> 2][e & 3];
+                const float ex = __expf(fminf(g_s[r] - g_s[jj], 0.f));
+                x[e] = ((jj <= r) ? 1.f : 0.f) * (qk * ex);
+            }
+            FragPair f;
+            split_bf16(x, f.h, f.l);
+            return f;
+        };
+        auto p_store = [&](auto mt_c, auto s_c, FragPair f) {
+            constexpr int mt = decltype(mt_c)::value, s = decltype(s_c)::value;
+            pf_s[((mt * G::CS + s) * 2 + 0) * kWave + lane] = f.h;
+            pf_s[((mt * G::CS + s) * 2 + 1) * kWave + lane] = f.l;
+        };
+        FragPair pa{}, pb{};
+        {
+            using I0 = IC<0>;
+            using I1 = IC<1>;
+            if constexpr (G::CT == 4) {
+                if (wave == 0) {
+                    a_tile(I0{}, I0{});
+                    a_tile(I1{}, I0{});
+                    a_tile(IC<2>{}, I0{});
+                } else if (wave == 1) {
+                    a_tile(I1{}, I1{});
+                    a_tile(IC<2>{}, I1{});
+                    a_tile(IC<3>{}, I0{});
+                } else if (wave == 2) {
+                    a_tile(IC<2>{}, IC<2>{});
+                    a_tile(IC<3>{}, I1{});
+                } else {
+                    a_tile(IC<3>{}, IC<3>{});
+                    a_tile(IC<3>{}, IC<2>{});
+                }
+            } else {
+                if (wave == 0) {
+                    a_tile(I0{}, I0{});
+                    a_tile(I1{}, I0{});
+                } else if (wave == 1) {
+                    a_tile(I1{}, I1{});
+                }
+            }
+            if constexpr (!MAP) {
+                if constexpr (G::CT == 4) {
+                    if (wave == 2) pa = p_pair(IC<0>{}, IC<0>{});
+                    else if (wave == 3) pa = p_pair(IC<2>{}, IC<1>{});
+                } else {
+                    if (wave == 2) pa = p_pair(IC<0>{}, IC<0>{});
+                    else if (wave == 3) pa = p_pair(IC<1>{}, IC<0>{});
+                }
+            }
+            if (wave < G::NB) inv_diag();
             if constexpr (kTbFrags) {
                 // T's blocks (0,1) and (2,3) are read as zeros by F; last chunk's T diag(b)
                 // fragments (written over T's rows) are dead, so clear them again
-                const int r = tid / 16, c = 16 + tid % 16;
-                ts[r][c] = 0.f;
-                ts[32 + r][32 + c] = 0.f;
+                if (wave == 0 || wave == 2) {
+                    const int r = 16 * wave + lane / 4, c = 16 * wave + 16 + 4 * (lane % 4);
+                    *reinterpret_cast<f32x4 *>(&ts[r][c]) = zero4;
+                }
             }
         }
         __syncthreads();
 
-        // ---- C: wave 0 inverts the two 32x32 diagonal halves of (I + A): 16x16 diagonal
-        // blocks by forward substitution (one column per lane, one block per 16 lanes), then
-        // T_{c+1,c} = -T_{c+1,c+1} A_{c+1,c} T_cc.  Waves 1..3 form P = Q K^T .* decay as
-        // P^T tiles, whose accumulator layout is P's A-fragment layout, split hi + lo.
-        bf16x8 pfr[MAP ? 1 : 2][2];
-        if (wave == 0) {
-            if (gq < G::NB) {
-                // t[r] = T_aa[r][j]: t[r] = delta_rj - sum_{m<r} A[r][m] t[m]; the sum is
-                // taken as a pairwise tree so each row costs a few dependent adds
-                const int blk = gq, j = li;
-                float t[16];
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float p[16];
-#pragma unroll
-                    for (int m4 = 0; m4 < 4; ++m4) {
-                        if (4 * m4 >= r) break;
-                        const f32x4 av = *reinterpret_cast<const f32x4 *>(&as[16 * blk + r][16 * blk + 4 * m4]);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (4 * m4 + e < r) p[4 * m4 + e] = av[e] * t[4 * m4 + e];
-                    }
-                    int n = r;
-#pragma unroll
-                    for (int lvl = 0; lvl < 4; ++lvl) {
-                        if (n <= 1) break;
-#pragma unroll
-                        for (int i2 = 0; i2 < 8; ++i2)
-                            if (2 * i2 + 1 < n) p[i2] = p[2 * i2] + p[2 * i2 + 1];
-                            else if (2 * i2 < n) p[i2] = p[2 * i2];
-                        n = (n + 1) / 2;
-                    }
-                    t[r] = (r == j) ? 1.f : (r == 0 ? 0.f : -p[0]);
-                }
-#pragma unroll
-                for (int r = 0; r < 16; ++r) ts[16 * blk + r][16 * blk + j] = t[r];
+        // ---- C: the blocks of T below the diagonal (chunk 64: T10, T32 and the lower-left
+        // quarter T_BL = -T_BR A_BL T_TL), one output tile per wavefront:
+        //   T10 = -T11 A10 T00, T32 = -T33 A32 T22, X = A_BL T_TL, T_BL = -T_BR X.
+        // A wavefront recomputes the level-1 block it needs rather than waiting for it;
+        // the remaining P tiles fill the shorter chains.
+        if constexpr (G::NB == 4) {
+            if (wave == 0) {
+                const f32x4 t10 = -mm16(rowfrag(ts, 16, 16), mm16(rowfrag(as, 16, 0), accfrag(ts, 0, 0), zero4), zero4);
+                store_acc(ts, 16, 0, t10);
+                f32x4 x = mm16(rowfrag(as, 32, 0), accfrag(ts, 0, 0), zero4);
+                x = mm16(rowfrag(as, 32, 16), t10, x);
+                store_acc(ts, 32, 0, -mm16(rowfrag(ts, 32, 32), x, zero4));
+            } else if (wave == 1) {
+                const f32x4 x = mm16(rowfrag(as, 32, 16), accfrag(ts, 16, 16), zero4);
+                store_acc(ts, 32, 16, -mm16(rowfrag(ts, 32, 32), x, zero4));
+            } else if (wave == 2) {
+                const f32x4 t32 =
+                    -mm16(rowfrag(ts, 48, 48), mm16(rowfrag(as, 48, 32), accfrag(ts, 32, 32), zero4), zero4);
+                store_acc(ts, 48, 32, t32);
+                const f32x4 x21 = mm16(rowfrag(as, 32, 16), accfrag(ts, 16, 16), zero4);
+                const f32x4 x31 = mm16(rowfrag(as, 48, 16), accfrag(ts, 16, 16), zero4);
+                f32x4 y = mm16(rowfrag(ts, 48, 48), x31, zero4);
+                y = mm16(rowfrag(ts, 48, 32), x21, y);  // T32 row fragments: this wavefront's store
+                store_acc(ts, 48, 16, -y);
+            } else {
+                const f32x4 t10 = -mm16(rowfrag(ts, 16, 16), mm16(rowfrag(as, 16, 0), accfrag(ts, 0, 0), zero4), zero4);
+                const f32x4 t32 =
+                    -mm16(rowfrag(ts, 48, 48), mm16(rowfrag(as, 48, 32), accfrag(ts, 32, 32), zero4), zero4);
+                store_acc(xs, 0, 0, t32);  // private copy, read back as row fragments
+                f32x4 x20 = mm16(rowfrag(as, 32, 0), accfrag(ts, 0, 0), zero4);
+                x20 = mm16(rowfrag(as, 32, 16), t10, x20);
+                f32x4 x30 = mm16(rowfrag(as, 48, 0), accfrag(ts, 0, 0), zero4);
+                x30 = mm16(rowfrag(as, 48, 16), t10, x30);
+                f32x4 y = mm16(rowfrag(ts, 48, 48), x30, zero4);
+                y = mm16(rowfrag(xs, 0, 0), x20, y);
+                store_acc(ts, 48, 0, -y);
             }
-            __builtin_amdgcn_wave_barrier();
-#pragma unroll
-            for (int c = 0; c < G::NB; c += 2) {
-                const f32x4 x = mm16(rowfrag(as, 16 * (c + 1), 16 * c), accfrag(ts, 16 * c, 16 * c), zero4);
-                const f32x4 y = mm16(rowfrag(ts, 16 * (c + 1), 16 * (c + 1)), x, zero4);
-                store_acc(ts, 16 * (c + 1), 16 * c, -y);
+        } else {
+            if (wave == 0) {
+                const f32x4 t10 = -mm16(rowfrag(ts, 16, 16), mm16(rowfrag(as, 16, 0), accfrag(ts, 0, 0), zero4), zero4);
+                store_acc(ts, 16, 0, t10);
             }
-        } else if (!MAP) {
-            int idx = 0;
-#pragma unroll
-            for (int mt = 0; mt < G::CT; ++mt)
-#pragma unroll
-                for (int s = 0; s < G::CS; ++s) {
-                    if (32 * s > 16 * mt + 15) continue;  // P is lower triangular
-                    const int mine = idx++;
-                    if (mine % (kWaves - 1) != wave - 1) continue;
-                    f32x4 acc[2] = {zero4, zero4};
-#pragma unroll
-                    for (int half = 0; half < 2; ++half) {
-                        const int jt = 2 * s + half;
-                        if (jt > mt) continue;
-#pragma unroll
-                        for (int ss = 0; ss < G::KS; ++ss)
-                            acc[half] = mfma_bf16(lds_frag_bf16(&ks[16 * jt + li][0], ss, gq),
-                                                  lds_frag_bf16(&qs[16 * mt + li][0], ss, gq), acc[half]);
-                    }
-                    // lane holds P[r][j] for r = 16 mt + li and j = kmap(s, gq, e)
-                    const int r = 16 * mt + li;
-                    float x[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int jj = kmap(s, gq, e);
-                        const float qk = acc[e >> 2][e & 3];
-                        const float ex = __expf(fminf(g_s[r] - g_s[jj], 0.f));
-                        x[e] = ((jj <= r) ? 1.f : 0.f) * (qk * ex);
-                    }
-                    split_bf16(x, pfr[mine / (kWaves - 1)][0], pfr[mine / (kWaves - 1)][1]);
-                }
+        }
+        if constexpr (!MAP && G::CT == 4) {
+            if (wave == 0) {
+                pb = p_pair(IC<3>{}, IC<0>{});
+            } else if (wave == 1) {
+                pa = p_pair(IC<1>{}, IC<0>{});
+                pb = p_pair(IC<2>{}, IC<0>{});
+            } else if (wave == 2) {
+                pb = p_pair(IC<3>{}, IC<1>{});
+            }
         }
         __syncthreads();
 
-        // ---- D (chunk 64): X = A_BL T_TL for the lower-left 32x32 quarter, one tile per wave
-        if constexpr (G::NB == 4) {
-            const int aa = 2 + wave / 2, c = wave % 2;
-            f32x4 x = zero4;
-#pragma unroll
-            for (int m = 0; m < 2; ++m)
-                if (m >= c) x = mm16(rowfrag(as, 16 * aa, 16 * m), accfrag(ts, 16 * m, 16 * c), x);
-            x_s[wave * kWave + lane] = x;
-            __syncthreads();
-        }
-
-        // ---- E: T_BL = -T_BR X (chunk 64); P fragments and V^T into LDS (A and K are dead)
-        if constexpr (G::NB == 4) {
-            const int aa = 2 + wave / 2, c = wave % 2;
-            f32x4 y = zero4;
-#pragma unroll
-            for (int m = 2; m < 4; ++m)
-                if (m <= aa) y = mm16(rowfrag(ts, 16 * aa, 16 * m), x_s[((m - 2) * 2 + c) * kWave + lane], y);
-            store_acc(ts, 16 * aa, 16 * c, -y);
-        }
-        if (!MAP && wave > 0) {
-            int idx = 0;
-#pragma unroll
-            for (int mt = 0; mt < G::CT; ++mt)
-#pragma unroll
-                for (int s = 0; s < G::CS; ++s) {
-                    if (32 * s > 16 * mt + 15) continue;
-                    const int mine = idx++;
-                    if (mine % (kWaves - 1) != wave - 1) continue;
-                    pf_s[((mt * G::CS + s) * 2 + 0) * kWave + lane] = pfr[mine / (kWaves - 1)][0];
-                    pf_s[((mt * G::CS + s) * 2 + 1) * kWave + lane] = pfr[mine / (kWaves - 1)][1];
+        // ---- F: P fragments and V^T into LDS (A and K are dead); W A-fragments = W^T tiles
+        // (2 s2, ct) and (2 s2 + 1, ct), W = T diag(b exp G) K
+        if constexpr (!MAP) {
+            if constexpr (G::CT == 4) {
+                if (wave == 0) {
+                    p_store(IC<3>{}, IC<0>{}, pb);
+                } else if (wave == 1) {
+                    p_store(IC<1>{}, IC<0>{}, pa);
+                    p_store(IC<2>{}, IC<0>{}, pb);
+                } else if (wave == 2) {
+                    p_store(IC<0>{}, IC<0>{}, pa);
+                    p_store(IC<3>{}, IC<1>{}, pb);
+                } else {
+                    p_store(IC<2>{}, IC<1>{}, pa);
                 }
+            } else {
+                if (wave == 2) p_store(IC<0>{}, IC<0>{}, pa);
+                else if (wave == 3) p_store(IC<1>{}, IC<0>{}, pa);
+            }
         }
 #pragma unroll
         for (int i = 0; i < R::NV; ++i) {
@@ -453,9 +526,6 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
 #pragma unroll
             for (int q8 = 0; q8 < 8; ++q8) vt[8 * c8 + q8][rr] = cur.v[i][q8];
         }
-        __syncthreads();
-
-        // ---- F: W A-fragments = W^T tiles (2 s2, ct) and (2 s2 + 1, ct), W = T diag(b exp G) K
         auto tb_frag = [&](int ct, int s, int hl) -> bf16x8 * {
             return reinterpret_cast<bf16x8 *>(&ts[16 * ct][0]) + (s * 2 + hl) * kWave + lane;
         };
