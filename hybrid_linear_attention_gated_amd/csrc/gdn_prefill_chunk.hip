@@ -65,12 +65,36 @@ struct FragPair {
 template <int N>
 using IC = std::integral_constant<int, N>;
 
+constexpr float kLog2e = 1.4426950408889634f;
+// 2^x by the hardware instruction (the decays here are 2^(non-positive) in log2 units)
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // x from the lane whose index differs in bit 0 (resp. bit 1): DPP quad permutations
 __device__ __forceinline__ float quad_xor1(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
 }
 __device__ __forceinline__ float quad_xor2(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
+}
+
+// x + (x of the lane selected by a DPP control); lanes without a source, or outside the
+// enabled rows, add zero
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_add(float x) {
+    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xF, false));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wavefront, all in DPP: shifts by 1, 2, 4, 8
+// within each 16-lane row, then row 0's total broadcast into row 1 (and row 2's into row 3),
+// then rows 0-1's total into rows 2 and 3.
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+    x = dpp_add<0x111>(x);        // row_shr:1
+    x = dpp_add<0x112>(x);        // row_shr:2
+    x = dpp_add<0x114>(x);        // row_shr:4
+    x = dpp_add<0x118>(x);        // row_shr:8
+    x = dpp_add<0x142, 0xA>(x);   // row_bcast:15 into rows 1 and 3
+    x = dpp_add<0x143, 0xC>(x);   // row_bcast:31 into rows 2 and 3
+    return x;
 }
 
 __device__ __forceinline__ void split4(f32x4 x, s16x4 &hi, s16x4 &lo) {
@@ -128,14 +152,32 @@ __device__ __forceinline__ void lds_store8(uint16_t *p, u16x8 x) {
 // Per-thread share of one chunk's rows, loaded from HBM one chunk ahead.
 template <int DK, int DV, int C, bool MAP>
 struct ChunkRegs {
-    static constexpr int NK = C * DK / 8 / kBlock, NV = C * DV / 8 / kBlock;
+    // V is loaded (and transposed into LDS in F) by the first VTHREADS threads only: with
+    // 64-wide values that is wavefronts 0 and 1, whose share of F is otherwise the smaller
+    static constexpr int VTHREADS = DV == 64 ? kBlock / 2 : kBlock;
+    static constexpr int NK = C * DK / 8 / kBlock, NV = C * DV / 8 / VTHREADS;
     u16x8 k[NK], q[MAP ? 1 : NK], v[NV];
     float g, beta;
 };
 
 // K and V are loaded one chunk row per lane (so their transposed copies can be
 // written to LDS without bank conflicts); Q with consecutive lanes on one row.
-// Addresses are a per-chunk base (uniform) plus a 32-bit lane offset.
+// Buffer loads: each tensor's resource starts at the chunk's first row of this
+// head and ends after its last valid row, so rows past the sequence end read as
+// zeros (the hardware's range check) with no branch, and the lane offsets are 32-bit.
+constexpr int kBufWord3 = 0x00020000;  // raw buffer, default data format (gfx9 family)
+
+template <typename T>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(const T *base, unsigned bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(base), 0, static_cast<int>(bytes), kBufWord3);
+}
+__device__ __forceinline__ u16x8 buf_load16(__amdgpu_buffer_rsrc_t r, unsigned byte_off) {
+    return __builtin_bit_cast(u16x8, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(byte_off), 0, 0));
+}
+__device__ __forceinline__ float buf_load4(__amdgpu_buffer_rsrc_t r, unsigned byte_off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(byte_off), 0, 0));
+}
+
 template <int DK, int DV, int C, bool MAP>
 __device__ __forceinline__ void load_chunk(ChunkRegs<DK, DV, C, MAP> &r, const ChunkArgs &a, int b,
                                            int h, int n, int tid) {
@@ -144,35 +186,37 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<DK, DV, C, MAP> &r, const C
     // they would hold a dozen registers for its whole length
     __asm__ __volatile__("" : "+v"(tid));
     const int t0 = n * C;
-    const int L = min(C, a.T - t0);
+    const int L = min(C, a.T - t0);  // >= 1
     const size_t row0 = (static_cast<size_t>(b) * a.T + t0) * a.H + h;  // token-head row of t0
-    const uint16_t *kb = a.k + row0 * DK;
-    const uint16_t *qb = a.q + row0 * DK;
-    const uint16_t *vb = a.v + row0 * DV;
-    const u16x8 zero = {0, 0, 0, 0, 0, 0, 0, 0};
+    const unsigned rows_k = static_cast<unsigned>((L - 1) * a.H * DK + DK) * 2u;
+    const unsigned rows_v = static_cast<unsigned>((L - 1) * a.H * DV + DV) * 2u;
+    const auto rk = chunk_rsrc(a.k + row0 * DK, rows_k);
+    const auto rv = chunk_rsrc(a.v + row0 * DV, rows_v);
 #pragma unroll
     for (int i = 0; i < R::NK; ++i) {
         const int e = tid + i * kBlock;
         const int rr = e % C, c8 = e / C;
-        const unsigned off = static_cast<unsigned>(rr * a.H * DK + 8 * c8);
-        r.k[i] = rr < L ? *reinterpret_cast<const u16x8 *>(kb + off) : zero;
+        r.k[i] = buf_load16(rk, static_cast<unsigned>(rr * a.H * DK + 8 * c8) * 2u);
         if (!MAP) {
-            const int rq = e / (DK / 8), cq = e % (DK / 8);
-            const unsigned offq = static_cast<unsigned>(rq * a.H * DK + 8 * cq);
-            r.q[i] = rq < L ? *reinterpret_cast<const u16x8 *>(qb + offq) : zero;
+            const auto rq = chunk_rsrc(a.q + row0 * DK, rows_k);
+            const int qr = e / (DK / 8), qc = e % (DK / 8);
+            r.q[i] = buf_load16(rq, static_cast<unsigned>(qr * a.H * DK + 8 * qc) * 2u);
         }
     }
+    if (tid < R::VTHREADS) {
 #pragma unroll
-    for (int i = 0; i < R::NV; ++i) {
-        const int e = tid + i * kBlock;
-        const int rr = e % C, c8 = e / C;
-        const unsigned off = static_cast<unsigned>(rr * a.H * DV + 8 * c8);
-        r.v[i] = rr < L ? *reinterpret_cast<const u16x8 *>(vb + off) : zero;
+        for (int i = 0; i < R::NV; ++i) {
+            const int e = tid + i * R::VTHREADS;
+            const int rr = e % C, c8 = e / C;
+            r.v[i] = buf_load16(rv, static_cast<unsigned>(rr * a.H * DV + 8 * c8) * 2u);
+        }
     }
-    const int lane = tid % kWave;
-    const unsigned offg = static_cast<unsigned>(lane * a.H);
-    r.g = (tid < kWave && lane < L) ? a.g[row0 + offg] : 0.f;
-    r.beta = (tid < kWave && lane < L) ? a.beta[row0 + offg] : 0.f;
+    if (tid < kWave) {
+        const unsigned rows_g = static_cast<unsigned>((L - 1) * a.H + 1) * 4u;
+        const unsigned off = static_cast<unsigned>(tid * a.H) * 4u;
+        r.g = buf_load4(chunk_rsrc(a.g + row0, rows_g), off);
+        r.beta = buf_load4(chunk_rsrc(a.beta + row0, rows_g), off);
+    }
 }
 
 // Two workgroups per compute unit where LDS allows it (64-wide heads), so one
@@ -202,7 +246,7 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
     __shared__ __align__(16) bf16x8 wf_s[G::CT * G::KS * kWave];   // W A-fragments
     __shared__ __align__(16) uint16_t kt_s[DK * KTSTR];            // K^T
     __shared__ __align__(16) float x_s[16 * CSTR16];              // one 16x16 fp32 tile (C)
-    __shared__ float g_s[C], b_s[C], bg_s[C], dec_s[C], gam_s[C];
+    __shared__ float g_s[C], b_s[C], bg_s[C], dec_s[C], gam_s[C];  // g_s: G * log2(e)
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform
     const int tid = threadIdx.x, lane = tid % kWave;
@@ -285,20 +329,16 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
         }
         if (wave == 0) {
             // inclusive prefix sum of the gates; rows >= L add 0 and repeat G_{L-1}
-            float x = cur.g;
-#pragma unroll
-            for (int off = 1; off < kWave; off <<= 1) {
-                const float y = __shfl_up(x, off, kWave);
-                if (lane >= off) x += y;
-            }
-            const float glast = __shfl(x, C - 1, kWave);
+            // G in log2 units: every decay below is then one v_exp_f32 (2^x)
+            const float x = wave_prefix_sum(cur.g) * kLog2e;
+            const float glast = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), C - 1));
             if (lane < C) {
-                const float ex = __expf(x);
+                const float ex = exp2_fast(x);
                 g_s[lane] = x;
                 b_s[lane] = cur.beta;
                 gam_s[lane] = ex;
                 bg_s[lane] = cur.beta * ex;
-                dec_s[lane] = __expf(glast - x);
+                dec_s[lane] = exp2_fast(glast - x);
             }
         }
         __syncthreads();
@@ -306,7 +346,8 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
         // ---- B: A = strict_tril(diag(b) (K K^T .* exp(G_r - G_j))) tile by tile, then each
         // wavefront inverts the diagonal block of (I + A) whose A tile it computed itself, so no
         // barrier separates the two.  Tiles (C = 64): w0 (0,0) (1,0) (2,0); w1 (1,1) (2,1) (3,0);
-        // w2 (2,2) (3,1); w3 (3,3) (3,2); w2 and w3 also form the two single-product P tiles.
+        // w2 (2,2); w3 (3,3) (3,2); (3,1) on w0 (OUT) or w2 (MAP); w2 and w3 also form the
+        // two single-product P tiles (OUT).
         auto a_tile = [&](auto mt_c, auto nt_c) {
             constexpr int mt = decltype(mt_c)::value, nt = decltype(nt_c)::value;
             f32x4 acc = zero4;
@@ -322,10 +363,10 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
             for (int r = 0; r < 4; ++r) {
                 const int row = 16 * mt + 4 * gq + r;
                 if constexpr (mt > nt) {
-                    as[row][col] = brow[r] * acc[r] * __expf(grow[r] - gcol);
+                    as[row][col] = brow[r] * acc[r] * exp2_fast(grow[r] - gcol);
                 } else {
                     // diagonal tile: exp of a clamped exponent times a 0/1 mask (no branch)
-                    const float ex = __expf(fminf(grow[r] - gcol, 0.f));
+                    const float ex = exp2_fast(fminf(grow[r] - gcol, 0.f));
                     as[row][col] = ((row > col) ? 1.f : 0.f) * (brow[r] * acc[r] * ex);
                 }
             }
@@ -384,7 +425,7 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
             for (int e = 0; e < 8; ++e) {
                 const int jj = kmap(s, gq, e);
                 const float qk = acc[e >> 2][e & 3];
-                const float ex = __expf(fminf(g_s[r] - g_s[jj], 0.f));
+                const float ex = exp2_fast(fminf(g_s[r] - g_s[jj], 0.f));
                 x[e] = ((jj <= r) ? 1.f : 0.f) * (qk * ex);
             }
             FragPair f;
@@ -401,17 +442,19 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
             using I0 = IC<0>;
             using I1 = IC<1>;
             if constexpr (G::CT == 4) {
+                // (3,1) goes to wavefront 0 where wavefront 2 also forms a P tile
                 if (wave == 0) {
                     a_tile(I0{}, I0{});
                     a_tile(I1{}, I0{});
                     a_tile(IC<2>{}, I0{});
+                    if constexpr (!MAP) a_tile(IC<3>{}, I1{});
                 } else if (wave == 1) {
                     a_tile(I1{}, I1{});
                     a_tile(IC<2>{}, I1{});
                     a_tile(IC<3>{}, I0{});
                 } else if (wave == 2) {
                     a_tile(IC<2>{}, IC<2>{});
-                    a_tile(IC<3>{}, I1{});
+                    if constexpr (MAP) a_tile(IC<3>{}, I1{});
                 } else {
                     a_tile(IC<3>{}, IC<3>{});
                     a_tile(IC<3>{}, IC<2>{});
@@ -520,11 +563,13 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
                 else if (wave == 3) p_store(IC<1>{}, IC<0>{}, pa);
             }
         }
+        if (tid < R::VTHREADS) {
 #pragma unroll
-        for (int i = 0; i < R::NV; ++i) {
-            const int e = tid + i * kBlock, rr = e % C, c8 = e / C;
+            for (int i = 0; i < R::NV; ++i) {
+                const int e = tid + i * R::VTHREADS, rr = e % C, c8 = e / C;
 #pragma unroll
-            for (int q8 = 0; q8 < 8; ++q8) vt[8 * c8 + q8][rr] = cur.v[i][q8];
+                for (int q8 = 0; q8 < 8; ++q8) vt[8 * c8 + q8][rr] = cur.v[i][q8];
+            }
         }
         auto tb_frag = [&](int ct, int s, int hl) -> bf16x8 * {
             return reinterpret_cast<bf16x8 *>(&ts[16 * ct][0]) + (s * 2 + hl) * kWave + lane;
@@ -738,53 +783,107 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
 // ---------------------------------------------------------------------------
 // chain: start states of every piece, St_in(p+1) = M_p St_in(p) + N_p, for one
 // 16-column slice of one head (one wavefront; state in registers, M_p rows
-// loaded as A fragments and split hi + lo, the state split hi + lo).
+// loaded as A fragments and split hi + lo, the state split hi + lo).  The maps do
+// not depend on the state, so (64-wide keys) piece p + 1's are loaded while piece p's
+// product runs.
 // ---------------------------------------------------------------------------
+template <int DK, int DV>
+struct ChainMap {
+    static constexpr int KT = DK / 16, KS = DK / 32;
+    float n[KT][4];     // N_p rows 16 mt + 4 gq + r, this lane's column
+    float m[KT][KS][8];  // M_p row 16 mt + li, k-slots of step s
+};
+
+template <int DK, int DV>
+__device__ __forceinline__ void chain_load(ChainMap<DK, DV> &c, const float *mp, int gq, int li, int col) {
+    constexpr int KT = DK / 16, KS = DK / 32, MAPW = DV + DK;
+#pragma unroll
+    for (int mt = 0; mt < KT; ++mt) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) c.n[mt][r] = mp[(16 * mt + 4 * gq + r) * MAPW + col];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) lds_slots_f32(mp + (16 * mt + li) * MAPW + DV, s, gq, c.m[mt][s]);
+    }
+}
+
+template <int DK, int DV>
+__device__ __forceinline__ void chain_step(f32x4 (&St)[DK / 16], const ChainMap<DK, DV> &c) {
+    constexpr int KT = DK / 16, KS = DK / 32;
+    bf16x8 Sh[KS], Sl[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        float x[8];
+        acc_pair_to_slots(St[2 * s], St[2 * s + 1], x);
+        split_bf16(x, Sh[s], Sl[s]);
+    }
+#pragma unroll
+    for (int mt = 0; mt < KT; ++mt) {
+        f32x4 acc = {c.n[mt][0], c.n[mt][1], c.n[mt][2], c.n[mt][3]};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            bf16x8 mh, ml;
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = c.m[mt][s][e];
+            split_bf16(x, mh, ml);
+            acc = mfma_bf16(mh, Sh[s], acc);
+            acc = mfma_bf16(mh, Sl[s], acc);
+            acc = mfma_bf16(ml, Sh[s], acc);
+        }
+        St[mt] = acc;
+    }
+}
+
 template <int DK, int DV>
 __global__ __launch_bounds__(kWave) void chain_kernel(const float *__restrict__ maps,
                                                       const float *__restrict__ s0,
                                                       float *__restrict__ starts, int P) {
-    constexpr int KT = DK / 16, KS = DK / 32, VT = DV / 16, MAPW = DV + DK;
+    constexpr int KT = DK / 16, VT = DV / 16, MAPW = DV + DK;
     const int lane = threadIdx.x, gq = lane / 16, li = lane % 16;
     const int sl = blockIdx.x % VT;
     const size_t bh = blockIdx.x / VT;
     const int col = 16 * sl + li;
-    f32x4 St[KT];
-#pragma unroll
-    for (int mt = 0; mt < KT; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) St[mt][r] = s0 ? s0[(bh * DK + 16 * mt + 4 * gq + r) * DV + col] : 0.f;
-    for (int p = 0; p < P; ++p) {
+    const float *mbase = maps + bh * (P - 1) * DK * MAPW;
+    auto piece_map = [&](int p) { return mbase + static_cast<size_t>(p) * DK * MAPW; };
+    auto store_start = [&](const f32x4 (&St)[KT], int p) {
 #pragma unroll
         for (int mt = 0; mt < KT; ++mt)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 starts[((bh * P + p) * DK + 16 * mt + 4 * gq + r) * DV + col] = St[mt][r];
-        if (p == P - 1) break;
-        const float *mp = maps + (bh * (P - 1) + p) * DK * MAPW;
-        bf16x8 Sh[KS], Sl[KS];
+    };
+    f32x4 St[KT];
+    if (s0) {
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            float x[8];
-            acc_pair_to_slots(St[2 * s], St[2 * s + 1], x);
-            split_bf16(x, Sh[s], Sl[s]);
+        for (int mt = 0; mt < KT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) St[mt][r] = s0[(bh * DK + 16 * mt + 4 * gq + r) * DV + col];
+    } else {
+#pragma unroll
+        for (int mt = 0; mt < KT; ++mt) St[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    if constexpr (DK == 64) {
+        // two map buffers used in turn, so piece p + 1's loads overlap piece p's product
+        ChainMap<DK, DV> ma, mb;
+        if (P > 1) chain_load<DK, DV>(ma, piece_map(0), gq, li, col);
+        for (int p = 0; p < P; p += 2) {
+            store_start(St, p);
+            if (p + 1 >= P) break;
+            if (p + 1 < P - 1) chain_load<DK, DV>(mb, piece_map(p + 1), gq, li, col);
+            chain_step<DK, DV>(St, ma);
+            store_start(St, p + 1);
+            if (p + 2 >= P) break;
+            if (p + 2 < P - 1) chain_load<DK, DV>(ma, piece_map(p + 2), gq, li, col);
+            chain_step<DK, DV>(St, mb);
         }
-#pragma unroll
-        for (int mt = 0; mt < KT; ++mt) {
-            f32x4 acc;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] = mp[(16 * mt + 4 * gq + r) * MAPW + col];  // N_p
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                float x[8];
-                lds_slots_f32(mp + (16 * mt + li) * MAPW + DV, s, gq, x);  // M_p row
-                bf16x8 mh, ml;
-                split_bf16(x, mh, ml);
-                acc = mfma_bf16(mh, Sh[s], acc);
-                acc = mfma_bf16(mh, Sl[s], acc);
-                acc = mfma_bf16(ml, Sh[s], acc);
-            }
-            St[mt] = acc;
+    } else {
+        // 128-wide maps would not fit twice in registers: load each in place
+        for (int p = 0; p < P; ++p) {
+            store_start(St, p);
+            if (p == P - 1) break;
+            ChainMap<DK, DV> mc;
+            chain_load<DK, DV>(mc, piece_map(p), gq, li, col);
+            chain_step<DK, DV>(St, mc);
         }
     }
 }
