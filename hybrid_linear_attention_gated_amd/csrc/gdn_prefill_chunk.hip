@@ -49,6 +49,7 @@ constexpr int kBlock = kWave * kWaves;
 // bf16 row padding in LDS: row strides of 2 * odd dwords, so the 8-byte fragment
 // reads of 16 consecutive rows (one per lane) cover all 32 banks once
 constexpr int kPad = 4;
+constexpr int kXcds = 8;  // accelerator dies (each with its own L2) of an MI355X
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
@@ -139,7 +140,7 @@ struct ChunkArgs {
     float *o;              // OUT: outputs
     float *s_final;        // OUT: final states [BH][DK][DV], written by the last piece
     float *maps;           // MAP: [BH][P - 1][DK][DV + DK]
-    int T, H, P, piece_chunks, N;
+    int T, H, BH, P, piece_chunks, N;
     float scale;
 };
 
@@ -251,9 +252,16 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform
     const int tid = threadIdx.x, lane = tid % kWave;
     const int gq = lane / 16, li = lane % 16;
+    // Work item w = piece * BH + bh.  Workgroups go to the eight XCDs round-robin by index,
+    // so consecutive work items (one piece, consecutive heads: they share every g and beta
+    // cache line) are given to indices that land on the same XCD and its L2.  The grid is a
+    // multiple of 8; surplus workgroups leave at once.
     const int pieces = MAP ? a.P - 1 : a.P;
-    const int piece = blockIdx.x % pieces;
-    const size_t bh = blockIdx.x / pieces;
+    const int per_xcd = gridDim.x / kXcds;
+    const int w = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+    if (w >= a.BH * pieces) return;
+    const int piece = w / a.BH;
+    const size_t bh = w % a.BH;
     const int b = static_cast<int>(bh / a.H), h = static_cast<int>(bh % a.H);
     const int n0 = piece * a.piece_chunks;
     const int n1 = min(n0 + a.piece_chunks, a.N);
@@ -921,12 +929,13 @@ hipError_t run_chunk(const uint16_t *q, const uint16_t *k, const uint16_t *v, co
     const int P = plan.P;
     ChunkArgs a{};
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.o = o; a.s_final = s_out;
-    a.T = T; a.H = H; a.P = P; a.N = N;
+    a.T = T; a.H = H; a.BH = BH; a.P = P; a.N = N;
+    auto grid = [](int items) { return dim3((items + kXcds - 1) / kXcds * kXcds); };
     a.piece_chunks = plan.piece_chunks;
     a.scale = 1.0f / sqrtf(static_cast<float>(DK));
     if (P == 1) {
         a.s_start = s0;
-        hipLaunchKernelGGL((chunk_kernel<DK, DV, C, false>), dim3(BH), dim3(kBlock), 0, stream, a);
+        hipLaunchKernelGGL((chunk_kernel<DK, DV, C, false>), grid(BH), dim3(kBlock), 0, stream, a);
         return hipGetLastError();
     }
     const size_t maps_bytes = static_cast<size_t>(BH) * (P - 1) * DK * (DV + DK) * 4;
@@ -934,7 +943,7 @@ hipError_t run_chunk(const uint16_t *q, const uint16_t *k, const uint16_t *v, co
     float *starts = reinterpret_cast<float *>(static_cast<char *>(ws) +
                                               ((maps_bytes + 255) & ~static_cast<size_t>(255)));
     a.maps = maps;
-    hipLaunchKernelGGL((chunk_kernel<DK, DV, C, true>), dim3(BH * (P - 1)), dim3(kBlock), 0, stream, a);
+    hipLaunchKernelGGL((chunk_kernel<DK, DV, C, true>), grid(BH * (P - 1)), dim3(kBlock), 0, stream, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL((chain_kernel<DK, DV>), dim3(BH * (DV / 16)), dim3(kWave), 0, stream,
@@ -942,7 +951,7 @@ hipError_t run_chunk(const uint16_t *q, const uint16_t *k, const uint16_t *v, co
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     a.s_start = starts;
-    hipLaunchKernelGGL((chunk_kernel<DK, DV, C, false>), dim3(BH * P), dim3(kBlock), 0, stream, a);
+    hipLaunchKernelGGL((chunk_kernel<DK, DV, C, false>), grid(BH * P), dim3(kBlock), 0, stream, a);
     return hipGetLastError();
 }
 
