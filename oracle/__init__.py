@@ -20,6 +20,10 @@ under a key):
     S_t = a_t S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T,   a_t = exp(g_t)
     o_t = S_t q_t / sqrt(d_k)
 
+A second rule, ``rule=GATED_DECAY``, drops the erase term: S_t = a_t S_{t-1} + b_t v_t k_t^T
+(the uniform decay the Priming article attributes to Mamba-2).  ``closed_form_decay``
+(``oracle.brute``) evaluates it as explicit decayed sums, independently of the recurrence.
+
 States are stored key-major, ``[..., d_k, d_v]`` (element (j, i) = S[i][j]).
 """
 from __future__ import annotations
@@ -29,10 +33,11 @@ import os
 
 import numpy as np
 
-from .brute import brute_force
+from .brute import brute_force, closed_form_decay
 from .build import LIB, build
 
 F64, F32, BF16 = 0, 1, 2
+GATED_DELTA, GATED_DECAY = 0, 1  # the rules the oracle evaluates
 
 
 def _as_array(x):
@@ -72,21 +77,23 @@ class Oracle:
     def __init__(self, path: str = LIB):
         lib = ctypes.CDLL(path)
         vp, dp, lg, i32 = ctypes.c_void_p, ctypes.POINTER(ctypes.c_double), ctypes.c_long, ctypes.c_int
-        lib.gdn_oracle_prefill.argtypes = [vp, vp, vp, i32, vp, vp, i32, vp, i32, dp, dp,
-                                           lg, lg, lg, lg, lg, ctypes.POINTER(ctypes.c_int), lg]
-        lib.gdn_oracle_prefill.restype = i32
-        lib.gdn_oracle_decode_step.argtypes = [vp, vp, vp, i32, vp, vp, i32, dp, dp, lg, lg, lg, lg]
-        lib.gdn_oracle_decode_step.restype = i32
+        lib.gdn_oracle_prefill_rule.argtypes = [i32, vp, vp, vp, i32, vp, vp, i32, vp, i32, dp, dp,
+                                                lg, lg, lg, lg, lg, ctypes.POINTER(ctypes.c_int), lg]
+        lib.gdn_oracle_prefill_rule.restype = i32
+        lib.gdn_oracle_decode_step_rule.argtypes = [i32, vp, vp, vp, i32, vp, vp, i32, dp, dp,
+                                                    lg, lg, lg, lg]
+        lib.gdn_oracle_decode_step_rule.restype = i32
         lib.gdn_oracle_num_threads.argtypes = []
         lib.gdn_oracle_num_threads.restype = i32
         self.lib = lib
         self.brute_force = brute_force
+        self.closed_form_decay = closed_form_decay
 
     def num_threads(self) -> int:
         return int(self.lib.gdn_oracle_num_threads())
 
-    def prefill(self, q, k, v, g, beta, s0=None, rows=None):
-        """Token-by-token fp64 evaluation.
+    def prefill(self, q, k, v, g, beta, s0=None, rows=None, rule=GATED_DELTA):
+        """Token-by-token fp64 evaluation of ``rule`` (GATED_DELTA or GATED_DECAY).
 
         q, k: [B,T,H,d_k]; v: [B,T,H,d_v]; g, beta: [B,T,H]; s0: [B,H,d_k,d_v] or None (zeros).
         rows: optional list of value rows to evaluate (others are left NaN).
@@ -118,15 +125,15 @@ class Oracle:
         else:
             rows_arr, rp, nr = None, None, 0
         dp = ctypes.POINTER(ctypes.c_double)
-        rc = self.lib.gdn_oracle_prefill(_ptr(qa), _ptr(ka), _ptr(va), qd, _ptr(ga), _ptr(ba), gd,
-                                         _ptr(sa), sd, o.ctypes.data_as(dp), sf.ctypes.data_as(dp),
-                                         B, T, H, dk, dv, rp, nr)
+        rc = self.lib.gdn_oracle_prefill_rule(rule, _ptr(qa), _ptr(ka), _ptr(va), qd, _ptr(ga), _ptr(ba),
+                                              gd, _ptr(sa), sd, o.ctypes.data_as(dp),
+                                              sf.ctypes.data_as(dp), B, T, H, dk, dv, rp, nr)
         if rc != 0:
             raise ValueError("oracle: gdn_oracle_prefill rejected its arguments")
         return o, sf
 
-    def decode_step(self, q, k, v, g, beta, state):
-        """One single-token step for N sequences.
+    def decode_step(self, q, k, v, g, beta, state, rule=GATED_DELTA):
+        """One single-token step of ``rule`` for N sequences.
 
         q, k: [N,H,d_k]; v: [N,H,d_v]; g, beta: [N,H]; state: [N,H,d_k,d_v] fp64 numpy,
         updated in place.  Returns o [N,H,d_v] fp64.
@@ -145,9 +152,9 @@ class Oracle:
             raise ValueError("oracle: state shape mismatch")
         o = np.full((N, H, dv), np.nan)
         dp = ctypes.POINTER(ctypes.c_double)
-        rc = self.lib.gdn_oracle_decode_step(_ptr(qa), _ptr(ka), _ptr(va), qd, _ptr(ga), _ptr(ba),
-                                             gd, state.ctypes.data_as(dp), o.ctypes.data_as(dp),
-                                             N, H, dk, dv)
+        rc = self.lib.gdn_oracle_decode_step_rule(rule, _ptr(qa), _ptr(ka), _ptr(va), qd, _ptr(ga),
+                                                  _ptr(ba), gd, state.ctypes.data_as(dp),
+                                                  o.ctypes.data_as(dp), N, H, dk, dv)
         if rc != 0:
             raise ValueError("oracle: gdn_oracle_decode_step rejected its arguments")
         return o
@@ -177,4 +184,5 @@ def num_threads() -> int:
     return default().num_threads()
 
 
-__all__ = ["Oracle", "default", "prefill", "decode_step", "brute_force", "num_threads", "build"]
+__all__ = ["Oracle", "default", "prefill", "decode_step", "brute_force", "closed_form_decay",
+           "num_threads", "build", "GATED_DELTA", "GATED_DECAY"]

@@ -62,3 +62,30 @@ def brute_force(q, k, v, g, beta, s0=None):
                 o[b, t - 1, h] = S @ q[b, t - 1, h] / np.sqrt(dk)
             sf[b, h] = S.T
     return o, sf
+
+
+def closed_form_decay(q, k, v, g, beta, s0=None):
+    """The gated-decay rule S_t = a_t S_{t-1} + b_t v_t k_t^T written out as sums.
+
+    Unrolled, S_t = exp(G_t) S_0 + sum_{j<=t} exp(G_t - G_j) b_j v_j k_j^T with
+    G_t = g_1 + ... + g_t, and o_t = S_t q_t / sqrt(d_k).  Every S_t is summed
+    from scratch (no carried state).  Same argument conventions as brute_force.
+    """
+    q, k, v, g, beta = (_f64(x) for x in (q, k, v, g, beta))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    s0 = np.zeros((B, H, dk, dv)) if s0 is None else _f64(s0)
+    o = np.zeros((B, T, H, dv))
+    sf = np.zeros((B, H, dk, dv))
+    for b in range(B):
+        for h in range(H):
+            G = np.cumsum(g[b, :, h])
+            S = s0[b, h].T
+            for t in range(T):
+                St = np.exp(G[t]) * s0[b, h].T
+                for j in range(t + 1):
+                    St = St + np.exp(G[t] - G[j]) * beta[b, j, h] * np.outer(v[b, j, h], k[b, j, h])
+                o[b, t, h] = St @ q[b, t, h] / np.sqrt(dk)
+                S = St
+            sf[b, h] = S.T
+    return o, sf

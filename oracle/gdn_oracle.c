@@ -22,6 +22,16 @@
  *
  * with S in R^{d_v x d_k}.  Readout uses the updated state S_t.
  *
+ * Second rule (ORC_RULE_GATED_DECAY): the same gated recurrence without the
+ * erase term,
+ *
+ *     S_t = a_t * S_{t-1} + b_t v_t k_t^T
+ *
+ * i.e. the uniform decay the Priming article attributes to Mamba-2 (we0.ai
+ * article, comparison of Mamba-2, Gated DeltaNet and Gated KalmaNet: the
+ * state decays as a whole while new information is added), with b_t as the
+ * write strength.  Readout and layouts are as above.
+ *
  * Because (I - b k k^T) acts on the key side only, row i of S (value dim i)
  * evolves on its own:
  *     S_t[i,:] = a_t * (S_{t-1}[i,:] - b_t * (S_{t-1}[i,:] . k_t) * k_t)
@@ -47,6 +57,7 @@
 #include <string.h>
 
 enum { ORC_F64 = 0, ORC_F32 = 1, ORC_BF16 = 2 };
+enum { ORC_RULE_GATED_DELTA = 0, ORC_RULE_GATED_DECAY = 1 };
 
 static double orc_load(const void *p, int dtype, long idx)
 {
@@ -63,6 +74,7 @@ static double orc_load(const void *p, int dtype, long idx)
 
 /*
  * Token-by-token prefill.
+ *   rule:      ORC_RULE_GATED_DELTA or ORC_RULE_GATED_DECAY
  *   qkv_dtype: storage type of q, k, v (ORC_F64 / ORC_F32 / ORC_BF16)
  *   gb_dtype:  storage type of g and beta
  *   s0_dtype:  storage type of s0 (ignored when s0 == NULL, which means zeros)
@@ -70,13 +82,15 @@ static double orc_load(const void *p, int dtype, long idx)
  *               entries of o and s_out are written.
  * Returns 0, or -1 on a bad argument.
  */
-int gdn_oracle_prefill(const void *q, const void *k, const void *v, int qkv_dtype,
-                       const void *g, const void *beta, int gb_dtype,
-                       const void *s0, int s0_dtype,
-                       double *o, double *s_out,
-                       long B, long T, long H, long dk, long dv,
-                       const int *rows, long nrows)
+int gdn_oracle_prefill_rule(int rule, const void *q, const void *k, const void *v, int qkv_dtype,
+                            const void *g, const void *beta, int gb_dtype,
+                            const void *s0, int s0_dtype,
+                            double *o, double *s_out,
+                            long B, long T, long H, long dk, long dv,
+                            const int *rows, long nrows)
 {
+    if (rule != ORC_RULE_GATED_DELTA && rule != ORC_RULE_GATED_DECAY)
+        return -1;
     if (!q || !k || !v || !g || !beta || !o || !s_out)
         return -1;
     if (B <= 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0)
@@ -112,15 +126,21 @@ int gdn_oracle_prefill(const void *q, const void *k, const void *v, int qkv_dtyp
                 const double bt = orc_load(beta, gb_dtype, bth);
                 const double vi = orc_load(v, qkv_dtype, bth * dv + i);
 
-                /* w = S_{t-1}[i,:] . k_t */
-                double w = 0.0;
-                for (long j = 0; j < dk; ++j)
-                    w += srow[j] * orc_load(k, qkv_dtype, bth * dk + j);
+                if (rule == ORC_RULE_GATED_DECAY) {
+                    /* S_t[i,:] = a S_{t-1}[i,:] + b v_i k_t */
+                    for (long j = 0; j < dk; ++j)
+                        srow[j] = a * srow[j] + bt * vi * orc_load(k, qkv_dtype, bth * dk + j);
+                } else {
+                    /* w = S_{t-1}[i,:] . k_t */
+                    double w = 0.0;
+                    for (long j = 0; j < dk; ++j)
+                        w += srow[j] * orc_load(k, qkv_dtype, bth * dk + j);
 
-                /* S_t[i,:] = a (S_{t-1}[i,:] - b w k_t) + b v_i k_t */
-                for (long j = 0; j < dk; ++j) {
-                    const double kj = orc_load(k, qkv_dtype, bth * dk + j);
-                    srow[j] = a * (srow[j] - bt * w * kj) + bt * vi * kj;
+                    /* S_t[i,:] = a (S_{t-1}[i,:] - b w k_t) + b v_i k_t */
+                    for (long j = 0; j < dk; ++j) {
+                        const double kj = orc_load(k, qkv_dtype, bth * dk + j);
+                        srow[j] = a * (srow[j] - bt * w * kj) + bt * vi * kj;
+                    }
                 }
 
                 /* o_t[i] = S_t[i,:] . q_t / sqrt(d_k) */
@@ -138,17 +158,37 @@ int gdn_oracle_prefill(const void *q, const void *k, const void *v, int qkv_dtyp
     return 0;
 }
 
+/* The gated delta rule (the library's default). */
+int gdn_oracle_prefill(const void *q, const void *k, const void *v, int qkv_dtype,
+                       const void *g, const void *beta, int gb_dtype,
+                       const void *s0, int s0_dtype,
+                       double *o, double *s_out,
+                       long B, long T, long H, long dk, long dv,
+                       const int *rows, long nrows)
+{
+    return gdn_oracle_prefill_rule(ORC_RULE_GATED_DELTA, q, k, v, qkv_dtype, g, beta, gb_dtype,
+                                   s0, s0_dtype, o, s_out, B, T, H, dk, dv, rows, nrows);
+}
+
 /*
  * One decode step for N independent sequences: the prefill recurrence with
  * T = 1.  q, k, v: [N, H, d]; g, beta: [N, H]; state: [N, H, d_k, d_v]
  * (key-major, fp64, updated in place); o: [N, H, d_v].
  */
+int gdn_oracle_decode_step_rule(int rule, const void *q, const void *k, const void *v, int qkv_dtype,
+                                const void *g, const void *beta, int gb_dtype,
+                                double *state, double *o, long N, long H, long dk, long dv)
+{
+    return gdn_oracle_prefill_rule(rule, q, k, v, qkv_dtype, g, beta, gb_dtype, state, ORC_F64,
+                                   o, state, N, 1, H, dk, dv, NULL, 0);
+}
+
 int gdn_oracle_decode_step(const void *q, const void *k, const void *v, int qkv_dtype,
                            const void *g, const void *beta, int gb_dtype,
                            double *state, double *o, long N, long H, long dk, long dv)
 {
-    return gdn_oracle_prefill(q, k, v, qkv_dtype, g, beta, gb_dtype, state, ORC_F64,
-                              o, state, N, 1, H, dk, dv, NULL, 0);
+    return gdn_oracle_decode_step_rule(ORC_RULE_GATED_DELTA, q, k, v, qkv_dtype, g, beta, gb_dtype,
+                                       state, o, N, H, dk, dv);
 }
 
 /* Threads an OpenMP parallel region of this library uses (for reporting). */

@@ -13,6 +13,7 @@ import pytest
 import oracle
 from oracle.build import SRC
 import test_oracle_pins as pins
+import test_oracle_pins_decay as dpins
 
 PINS = [
     pins.test_hand_worked_example,
@@ -70,3 +71,41 @@ def test_pins_catch_planted_mistake(mutant_dir, name, orig, bad):
         except AssertionError:
             failed.append(getattr(pin, "__name__", "lambda"))
     assert failed, f"no pin detects the planted mistake {name!r}"
+
+
+# the second rule (no erase), caught by its own pins
+PINS_DECAY = [
+    dpins.test_decay_hand_worked_example,
+    lambda o: dpins.test_decay_matches_explicit_decayed_sums(o, 1, 1, 9, 2, 4, 3, "primary"),
+    dpins.test_decay_pure_decay_and_single_token,
+    dpins.test_decay_accumulates_where_the_delta_rule_overwrites,
+]
+MUTANTS_DECAY = [
+    ("decay_write_decayed", "srow[j] = a * srow[j] + bt * vi * orc_load(k, qkv_dtype, bth * dk + j);",
+     "srow[j] = a * (srow[j] + bt * vi * orc_load(k, qkv_dtype, bth * dk + j));"),
+    ("decay_write_without_beta", "a * srow[j] + bt * vi * orc_load(", "a * srow[j] + vi * orc_load("),
+    ("decay_not_applied", "srow[j] = a * srow[j] + bt", "srow[j] = srow[j] + bt"),
+    ("decay_rule_erases", "if (rule == ORC_RULE_GATED_DECAY) {", "if (0) {"),
+]
+
+
+@pytest.mark.parametrize("name,orig,bad", MUTANTS_DECAY, ids=[m[0] for m in MUTANTS_DECAY])
+def test_decay_pins_catch_planted_mistake(mutant_dir, name, orig, bad):
+    with open(SRC) as f:
+        src = f.read()
+    assert src.count(orig) == 1, f"mutation site for {name} not unique"
+    src = src.replace(orig, bad)
+    csrc = os.path.join(mutant_dir, f"{name}.c")
+    lib = os.path.join(mutant_dir, f"lib{name}.so")
+    with open(csrc, "w") as f:
+        f.write(src)
+    subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-o", lib, csrc, "-lm"],
+                   check=True)
+    mutant = oracle.Oracle(lib)
+    failed = []
+    for pin in PINS_DECAY:
+        try:
+            pin(mutant)
+        except AssertionError:
+            failed.append(getattr(pin, "__name__", "lambda"))
+    assert failed, f"no decay pin detects the planted mistake {name!r}"
