@@ -167,6 +167,29 @@ def main():
         print(json.dumps({"only": args.only, "steps": args.steps, "wall_ms": wall * 1e3}), flush=True)
         return
 
+    # the second rule (no erase term) on the same inputs, timed the same way; reported beside
+    # the main figures, not part of `value`
+    def decay_prefill():
+        gdn.chunk_prefill(pre["q"], pre["k"], pre["v"], pre["g"], pre["beta"], pre["s0"], chunk=w.chunk,
+                          out=out, final_state=fin, workspace=ws, rule=gdn.GDN_RULE_GATED_DECAY)
+    for _ in range(args.warmup):
+        decay_prefill()
+    dp_ev = [(mk(), mk()) for _ in range(args.steps)]
+    for a, b in dp_ev:
+        a.record(stream)
+        decay_prefill()
+        b.record(stream)
+    state.copy_(state0)
+    dd_ev = [(mk(), mk()) for _ in steps_in]
+    for s, d in enumerate(steps_in):
+        dd_ev[s][0].record(stream)
+        gdn.decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], state, out=dout,
+                        rule=gdn.GDN_RULE_GATED_DECAY)
+        dd_ev[s][1].record(stream)
+    torch.cuda.synchronize()
+    decay_pre_ms = sum(a.elapsed_time(b) for a, b in dp_ev) / len(dp_ev)
+    decay_dec_ms = sum(a.elapsed_time(b) for a, b in dd_ev) / len(dd_ev)
+
     # decode with a cold last-level cache: read a 1 GiB buffer before each step, outside the
     # events (a read leaves only clean lines behind, so no write-back competes with the step)
     flush = torch.ones(FLUSH_BYTES // 4, device=dev, dtype=torch.float32)
@@ -233,6 +256,14 @@ def main():
             "traffic_bytes_per_step": recorded_traffic("decode"),
             "note": "warm: 16 back-to-back steps, the 128 MiB state can stay in the 256 MB last-level "
                     "cache; cold: a 1 GiB buffer is read before every step",
+        },
+        "gated_decay_rule": {
+            "prefill_ms_avg": round(decay_pre_ms, 4),
+            "prefill_tokens_per_s": round(w.B * w.T / (decay_pre_ms * 1e-3), 1),
+            "prefill_GBps_algorithmic": round(pre_bytes / (decay_pre_ms * 1e-3) / 1e9, 1),
+            "decode_us_per_step_avg": round(decay_dec_ms * 1e3, 2),
+            "decode_GBps": round(dec_bytes / (decay_dec_ms * 1e-3) / 1e9, 1),
+            "note": "S_t = a_t S_{t-1} + b_t v_t k_t^T (no erase term) on the same 64K and decode inputs",
         },
         "roofline": {
             "kernel": "one gdn_chunk_prefill call: chunk_kernel MAP + chain_kernel + chunk_kernel OUT",

@@ -31,10 +31,11 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libgdn.so")
 
 GDN_F32, GDN_BF16 = 0, 1
+GDN_RULE_GATED_DELTA, GDN_RULE_GATED_DECAY = 0, 1
 STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_UNSUPPORTED",
           4: "GDN_ERR_ALIGN", 5: "GDN_ERR_ALIAS", 6: "GDN_ERR_WORKSPACE", 7: "GDN_ERR_HIP"}
-EXPORTS = ("gdn_chunk_prefill", "gdn_chunk_prefill_workspace_size", "gdn_decode_step",
-           "gdn_status_string", "gdn_version")
+EXPORTS = ("gdn_chunk_prefill", "gdn_chunk_prefill_rule", "gdn_chunk_prefill_workspace_size",
+           "gdn_decode_step", "gdn_decode_step_rule", "gdn_status_string", "gdn_version")
 
 
 class GdnError(RuntimeError):
@@ -58,10 +59,14 @@ def lib():
         L.gdn_chunk_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                         i32, vp, sz, vp]
         L.gdn_chunk_prefill.restype = i32
+        L.gdn_chunk_prefill_rule.argtypes = [i32] + L.gdn_chunk_prefill.argtypes
+        L.gdn_chunk_prefill_rule.restype = i32
         L.gdn_chunk_prefill_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
         L.gdn_chunk_prefill_workspace_size.restype = sz
         L.gdn_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
         L.gdn_decode_step.restype = i32
+        L.gdn_decode_step_rule.argtypes = [i32] + L.gdn_decode_step.argtypes
+        L.gdn_decode_step_rule.restype = i32
         L.gdn_status_string.argtypes = [i32]
         L.gdn_status_string.restype = ctypes.c_char_p
         L.gdn_version.argtypes = []
@@ -78,12 +83,23 @@ def gdn_chunk_prefill(q, k, v, g, beta, initial_state, o, final_state, B, T, H, 
                                    d_v, chunk, qkv_dtype, workspace, workspace_bytes, stream)
 
 
+def gdn_chunk_prefill_rule(rule, q, k, v, g, beta, initial_state, o, final_state, B, T, H, d_k, d_v,
+                           chunk, qkv_dtype, workspace, workspace_bytes, stream) -> int:
+    return lib().gdn_chunk_prefill_rule(rule, q, k, v, g, beta, initial_state, o, final_state, B, T, H,
+                                        d_k, d_v, chunk, qkv_dtype, workspace, workspace_bytes, stream)
+
+
 def gdn_chunk_prefill_workspace_size(B, T, H, d_k, d_v, chunk, qkv_dtype) -> int:
     return lib().gdn_chunk_prefill_workspace_size(B, T, H, d_k, d_v, chunk, qkv_dtype)
 
 
 def gdn_decode_step(q, k, v, g, beta, state, o, N, H, d_k, d_v, qkv_dtype, stream) -> int:
     return lib().gdn_decode_step(q, k, v, g, beta, state, o, N, H, d_k, d_v, qkv_dtype, stream)
+
+
+def gdn_decode_step_rule(rule, q, k, v, g, beta, state, o, N, H, d_k, d_v, qkv_dtype, stream) -> int:
+    return lib().gdn_decode_step_rule(rule, q, k, v, g, beta, state, o, N, H, d_k, d_v, qkv_dtype,
+                                      stream)
 
 
 def gdn_status_string(status: int) -> str:
@@ -126,10 +142,11 @@ def workspace_bytes(B, T, H, d_k, d_v, chunk, qkv_dtype) -> int:
 
 
 def chunk_prefill(q, k, v, g, beta, initial_state=None, chunk=64, *, out=None, final_state=None,
-                  workspace=None, stream=None):
+                  workspace=None, stream=None, rule=GDN_RULE_GATED_DELTA):
     """q, k [B,T,H,d_k]; v [B,T,H,d_v] (bf16 or fp32); g, beta [B,T,H] fp32;
     initial_state [B,H,d_k,d_v] fp32 or None.  Returns (o fp32 [B,T,H,d_v], final_state).
-    ``final_state`` may be ``initial_state`` itself for in-place chaining."""
+    ``final_state`` may be ``initial_state`` itself for in-place chaining.  ``rule`` is
+    GDN_RULE_GATED_DELTA (default) or GDN_RULE_GATED_DECAY (no erase term)."""
     import torch
     B, T, H, d_k = q.shape
     d_v = v.shape[-1]
@@ -152,17 +169,17 @@ def chunk_prefill(q, k, v, g, beta, initial_state=None, chunk=64, *, out=None, f
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
-    st = gdn_chunk_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
-                           _ptr(out), _ptr(final_state), B, T, H, d_k, d_v, chunk, dt,
-                           _ptr(workspace), ws_bytes, stream)
+    st = gdn_chunk_prefill_rule(rule, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                _ptr(initial_state), _ptr(out), _ptr(final_state), B, T, H, d_k, d_v,
+                                chunk, dt, _ptr(workspace), ws_bytes, stream)
     if st != 0:
-        raise GdnError(st, "gdn_chunk_prefill")
+        raise GdnError(st, "gdn_chunk_prefill_rule")
     return out, final_state
 
 
-def decode_step(q, k, v, g, beta, state, *, out=None, stream=None):
+def decode_step(q, k, v, g, beta, state, *, out=None, stream=None, rule=GDN_RULE_GATED_DELTA):
     """q, k [N,H,d_k]; v [N,H,d_v]; g, beta [N,H] fp32; state [N,H,d_k,d_v] fp32
-    (updated in place).  Returns o fp32 [N,H,d_v]."""
+    (updated in place).  Returns o fp32 [N,H,d_v].  ``rule`` as for chunk_prefill."""
     import torch
     N, H, d_k = q.shape
     d_v = v.shape[-1]
@@ -177,13 +194,14 @@ def decode_step(q, k, v, g, beta, state, *, out=None, stream=None):
     _check(out, "out", torch.float32)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
-    st = gdn_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(out),
-                         N, H, d_k, d_v, dt, stream)
+    st = gdn_decode_step_rule(rule, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
+                              _ptr(out), N, H, d_k, d_v, dt, stream)
     if st != 0:
-        raise GdnError(st, "gdn_decode_step")
+        raise GdnError(st, "gdn_decode_step_rule")
     return out
 
 
-__all__ = ["EXPORTS", "GDN_F32", "GDN_BF16", "GdnError", "lib", "gdn_chunk_prefill",
-           "gdn_chunk_prefill_workspace_size", "gdn_decode_step", "gdn_status_string",
-           "gdn_version", "chunk_prefill", "decode_step", "workspace_bytes"]
+__all__ = ["EXPORTS", "GDN_F32", "GDN_BF16", "GDN_RULE_GATED_DELTA", "GDN_RULE_GATED_DECAY", "GdnError",
+           "lib", "gdn_chunk_prefill", "gdn_chunk_prefill_rule", "gdn_chunk_prefill_workspace_size",
+           "gdn_decode_step", "gdn_decode_step_rule", "gdn_status_string", "gdn_version",
+           "chunk_prefill", "decode_step", "workspace_bytes"]

@@ -77,7 +77,8 @@ const char *gdn_status_string(gdn_status status) {
     case GDN_ERR_NULL: return "GDN_ERR_NULL: a required pointer is NULL";
     case GDN_ERR_SHAPE: return "GDN_ERR_SHAPE: invalid or too large size argument";
     case GDN_ERR_UNSUPPORTED:
-        return "GDN_ERR_UNSUPPORTED: d_k/d_v must be 16, 64 or 128, chunk 16, 32 or 64, dtype F32 or BF16";
+        return "GDN_ERR_UNSUPPORTED: d_k/d_v must be 16, 64 or 128, chunk 16, 32 or 64, dtype F32 or BF16, "
+               "rule GATED_DELTA or GATED_DECAY";
     case GDN_ERR_ALIGN: return "GDN_ERR_ALIGN: a pointer is not 16-byte aligned";
     case GDN_ERR_ALIAS: return "GDN_ERR_ALIAS: an output buffer overlaps another buffer";
     case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE: workspace missing or too small";
@@ -93,11 +94,13 @@ size_t gdn_chunk_prefill_workspace_size(int B, int T, int H, int d_k, int d_v, i
     return 0;  // the fp32 path keeps everything on chip
 }
 
-gdn_status gdn_chunk_prefill(const void *q, const void *k, const void *v, const float *g,
-                             const float *beta, const float *initial_state, float *o,
-                             float *final_state, int B, int T, int H, int d_k, int d_v, int chunk,
-                             gdn_dtype qkv_dtype, void *workspace, size_t workspace_bytes,
-                             void *stream) {
+gdn_status gdn_chunk_prefill_rule(gdn_rule rule, const void *q, const void *k, const void *v,
+                                  const float *g, const float *beta, const float *initial_state,
+                                  float *o, float *final_state, int B, int T, int H, int d_k,
+                                  int d_v, int chunk, gdn_dtype qkv_dtype, void *workspace,
+                                  size_t workspace_bytes, void *stream) {
+    if (rule != GDN_RULE_GATED_DELTA && rule != GDN_RULE_GATED_DECAY) return GDN_ERR_UNSUPPORTED;
+    const bool delta = rule == GDN_RULE_GATED_DELTA;
     gdn_status st = check_prefill_shape(B, T, H, d_k, d_v, chunk, qkv_dtype);
     if (st != GDN_OK) return st;
     if (!final_state) return GDN_ERR_NULL;
@@ -142,16 +145,27 @@ gdn_status gdn_chunk_prefill(const void *q, const void *k, const void *v, const 
     if (qkv_dtype == GDN_BF16)
         err = launch_prefill_bf16(static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
                                   static_cast<const uint16_t *>(v), g, beta, initial_state, o,
-                                  final_state, B, T, H, d_k, d_v, chunk, workspace, hs);
+                                  final_state, B, T, H, d_k, d_v, chunk, delta, workspace, hs);
     else
         err = launch_prefill_valu(q, k, v, g, beta, initial_state, o, final_state, B, T, H, d_k,
-                                  d_v, chunk, GDN_F32, hs);
+                                  d_v, chunk, GDN_F32, delta, hs);
     return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
-gdn_status gdn_decode_step(const void *q, const void *k, const void *v, const float *g,
-                           const float *beta, float *state, float *o, int N, int H, int d_k,
-                           int d_v, gdn_dtype qkv_dtype, void *stream) {
+gdn_status gdn_chunk_prefill(const void *q, const void *k, const void *v, const float *g,
+                             const float *beta, const float *initial_state, float *o,
+                             float *final_state, int B, int T, int H, int d_k, int d_v, int chunk,
+                             gdn_dtype qkv_dtype, void *workspace, size_t workspace_bytes,
+                             void *stream) {
+    return gdn_chunk_prefill_rule(GDN_RULE_GATED_DELTA, q, k, v, g, beta, initial_state, o,
+                                  final_state, B, T, H, d_k, d_v, chunk, qkv_dtype, workspace,
+                                  workspace_bytes, stream);
+}
+
+gdn_status gdn_decode_step_rule(gdn_rule rule, const void *q, const void *k, const void *v,
+                                const float *g, const float *beta, float *state, float *o, int N,
+                                int H, int d_k, int d_v, gdn_dtype qkv_dtype, void *stream) {
+    if (rule != GDN_RULE_GATED_DELTA && rule != GDN_RULE_GATED_DECAY) return GDN_ERR_UNSUPPORTED;
     if (N < 0 || H <= 0 || d_k <= 0 || d_v <= 0) return GDN_ERR_SHAPE;
     if (qkv_dtype != GDN_F32 && qkv_dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
     if (!supported_dim(d_k) || !supported_dim(d_v)) return GDN_ERR_UNSUPPORTED;
@@ -173,8 +187,15 @@ gdn_status gdn_decode_step(const void *q, const void *k, const void *v, const fl
     if (overlap(s_o, s_s)) return GDN_ERR_ALIAS;
 
     const hipError_t err = launch_decode(q, k, v, g, beta, state, o, N, H, d_k, d_v, qkv_dtype,
-                                         static_cast<hipStream_t>(stream));
+                                         rule == GDN_RULE_GATED_DELTA, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+gdn_status gdn_decode_step(const void *q, const void *k, const void *v, const float *g,
+                           const float *beta, float *state, float *o, int N, int H, int d_k,
+                           int d_v, gdn_dtype qkv_dtype, void *stream) {
+    return gdn_decode_step_rule(GDN_RULE_GATED_DELTA, q, k, v, g, beta, state, o, N, H, d_k, d_v,
+                                qkv_dtype, stream);
 }
 
 }  // extern "C"

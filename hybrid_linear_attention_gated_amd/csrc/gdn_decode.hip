@@ -10,6 +10,9 @@
 //     S'    = a S + delta k^T                (= a S (I - b k k^T) + b v k^T)
 //     o     = S' q / sqrt(d_k) = (a p + delta (k . q)) / sqrt(d_k)
 //
+// Without the erase term (DELTA = false, S' = a S + b v k^T) delta = b v and
+// u is not needed; the readout and update formulas are unchanged.
+//
 // The step is bound by HBM bandwidth: every state byte is read once and
 // written once, ~0.25 FLOP per byte, so there is no MFMA here.  Layout of the
 // work: a wavefront owns a column slice of one (sequence, head) state stored
@@ -36,7 +39,7 @@ struct DecodeShape {
     static_assert(WC % 4 == 0 && kWave % LPR == 0 && DK % RG == 0, "decode tiling");
 };
 
-template <int DK, int DV, typename TIn>
+template <int DK, int DV, typename TIn, bool DELTA>
 __global__ __launch_bounds__(kWave * kWavesPerBlock) void decode_kernel(
     const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, float *__restrict__ state,
@@ -91,7 +94,7 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void decode_kernel(
     f32x4 vv;
 #pragma unroll
     for (int e = 0; e < 4; ++e) vv[e] = load_in(v, nh * DV + col + e);
-    const f32x4 delta = b * (vv - a * u);
+    const f32x4 delta = DELTA ? b * (vv - a * u) : b * vv;
 
     if (rg == 0) {
         const f32x4 out = scale * (a * p + delta * kq);
@@ -105,26 +108,32 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void decode_kernel(
 
 template <int DK, int DV, typename TIn>
 hipError_t launch_decode_t(const void *q, const void *k, const void *v, const float *g,
-                           const float *beta, float *state, float *o, int N, int H,
+                           const float *beta, float *state, float *o, int N, int H, bool delta,
                            hipStream_t stream) {
     using S = DecodeShape<DK, DV>;
     const long long items = static_cast<long long>(N) * H * S::SLICES;
     const int blocks = static_cast<int>((items + kWavesPerBlock - 1) / kWavesPerBlock);
     const float scale = 1.0f / sqrtf(static_cast<float>(DK));
-    hipLaunchKernelGGL((decode_kernel<DK, DV, TIn>), dim3(blocks), dim3(kWave * kWavesPerBlock), 0,
-                       stream, static_cast<const TIn *>(q), static_cast<const TIn *>(k),
-                       static_cast<const TIn *>(v), g, beta, state, o, static_cast<int>(items),
-                       scale);
+    if (delta)
+        hipLaunchKernelGGL((decode_kernel<DK, DV, TIn, true>), dim3(blocks), dim3(kWave * kWavesPerBlock),
+                           0, stream, static_cast<const TIn *>(q), static_cast<const TIn *>(k),
+                           static_cast<const TIn *>(v), g, beta, state, o, static_cast<int>(items),
+                           scale);
+    else
+        hipLaunchKernelGGL((decode_kernel<DK, DV, TIn, false>), dim3(blocks), dim3(kWave * kWavesPerBlock),
+                           0, stream, static_cast<const TIn *>(q), static_cast<const TIn *>(k),
+                           static_cast<const TIn *>(v), g, beta, state, o, static_cast<int>(items),
+                           scale);
     return hipGetLastError();
 }
 
 template <typename TIn>
 hipError_t dispatch_decode(const void *q, const void *k, const void *v, const float *g,
                            const float *beta, float *state, float *o, int N, int H, int dk,
-                           int dv, hipStream_t s) {
+                           int dv, bool delta, hipStream_t s) {
 #define GDN_DEC(DK_, DV_)                                                                        \
     if (dk == DK_ && dv == DV_)                                                                  \
-        return launch_decode_t<DK_, DV_, TIn>(q, k, v, g, beta, state, o, N, H, s);
+        return launch_decode_t<DK_, DV_, TIn>(q, k, v, g, beta, state, o, N, H, delta, s);
     GDN_DEC(16, 16) GDN_DEC(16, 64) GDN_DEC(16, 128)
     GDN_DEC(64, 16) GDN_DEC(64, 64) GDN_DEC(64, 128)
     GDN_DEC(128, 16) GDN_DEC(128, 64) GDN_DEC(128, 128)
@@ -136,10 +145,10 @@ hipError_t dispatch_decode(const void *q, const void *k, const void *v, const fl
 
 hipError_t launch_decode(const void *q, const void *k, const void *v, const float *g,
                          const float *beta, float *state, float *o, int N, int H, int dk, int dv,
-                         gdn_dtype dt, hipStream_t stream) {
+                         gdn_dtype dt, bool delta, hipStream_t stream) {
     if (dt == GDN_BF16)
-        return dispatch_decode<uint16_t>(q, k, v, g, beta, state, o, N, H, dk, dv, stream);
-    return dispatch_decode<float>(q, k, v, g, beta, state, o, N, H, dk, dv, stream);
+        return dispatch_decode<uint16_t>(q, k, v, g, beta, state, o, N, H, dk, dv, delta, stream);
+    return dispatch_decode<float>(q, k, v, g, beta, state, o, N, H, dk, dv, delta, stream);
 }
 
 }  // namespace gdn

@@ -37,30 +37,31 @@ template <> __device__ __forceinline__ float load_in<uint16_t>(const uint16_t *p
 
 // ---- launchers (host side; each returns the launch's hipError_t) ---------
 
+// `delta` selects the rule everywhere: true = gated delta rule, false = no erase term.
 hipError_t launch_decode(const void *q, const void *k, const void *v, const float *g,
                          const float *beta, float *state, float *o, int N, int H, int dk, int dv,
-                         gdn_dtype dt, hipStream_t stream);
+                         gdn_dtype dt, bool delta, hipStream_t stream);
 
 // Chunked prefill with fp32 VALU arithmetic (fp32 inputs, and bf16 inputs at
 // sizes the MFMA path does not tile).  Needs no workspace.
 hipError_t launch_prefill_valu(const void *q, const void *k, const void *v, const float *g,
                                const float *beta, const float *s0, float *o, float *s_out, int B,
                                int T, int H, int dk, int dv, int chunk, gdn_dtype dt,
-                               hipStream_t stream);
+                               bool delta, hipStream_t stream);
 
 // bf16 inputs: chunked prefill with bf16 MFMA contractions.
 bool prefill_bf16_uses_mfma(int dk, int dv, int chunk);
 hipError_t launch_prefill_bf16(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                const float *g, const float *beta, const float *s0, float *o,
                                float *s_out, int B, int T, int H, int dk, int dv, int chunk,
-                               void *ws, hipStream_t stream);
+                               bool delta, void *ws, hipStream_t stream);
 size_t prefill_bf16_workspace(int B, int T, int H, int dk, int dv, int chunk);
 
 // bf16 inputs, fused chunk kernel with sequence pieces (gdn_prefill_chunk.hip).
 hipError_t launch_prefill_chunk(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                 const float *g, const float *beta, const float *s0, float *o,
                                 float *s_out, int B, int T, int H, int dk, int dv, int chunk,
-                                void *ws, hipStream_t stream);
+                                bool delta, void *ws, hipStream_t stream);
 size_t prefill_chunk_workspace(int B, int T, int H, int dk, int dv, int chunk);
 
 // Copies (or zero-fills, when s0 == NULL) a start state into s_out.

@@ -20,11 +20,12 @@ size_t prefill_bf16_workspace(int B, int T, int H, int dk, int dv, int chunk) {
 hipError_t launch_prefill_bf16(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                const float *g, const float *beta, const float *s0, float *o,
                                float *s_out, int B, int T, int H, int dk, int dv, int chunk,
-                               void *ws, hipStream_t stream) {
+                               bool delta, void *ws, hipStream_t stream) {
     if (!prefill_bf16_uses_mfma(dk, dv, chunk))
         return launch_prefill_valu(q, k, v, g, beta, s0, o, s_out, B, T, H, dk, dv, chunk, GDN_BF16,
-                                   stream);
-    return launch_prefill_chunk(q, k, v, g, beta, s0, o, s_out, B, T, H, dk, dv, chunk, ws, stream);
+                                   delta, stream);
+    return launch_prefill_chunk(q, k, v, g, beta, s0, o, s_out, B, T, H, dk, dv, chunk, delta, ws,
+                                stream);
 }
 
 }  // namespace gdn

@@ -225,7 +225,10 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<DK, DV, C, MAP> &r, const C
 template <int DK, int DV>
 constexpr int kBlocksPerCU = (DK == 64 && DV == 64) ? 2 : 1;
 
-template <int DK, int DV, int C, bool MAP>
+// DELTA selects the rule: the gated delta rule (true) or the same recurrence without the
+// erase term (false), S_t = a_t S_{t-1} + b_t v_t k_t^T, whose chunk form has A = 0 and T = I:
+// Delta = diag(b) V with no W St term, and a piece map M_p that is a multiple of I.
+template <int DK, int DV, int C, bool MAP, bool DELTA>
 __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(ChunkArgs a) {
     using G = Cfg<DK, DV, C, MAP>;
     using R = ChunkRegs<DK, DV, C, MAP>;
@@ -243,10 +246,12 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
     __shared__ __align__(16) uint16_t kv_s[KV_ELEMS];              // K rows, then V^T
     __shared__ __align__(16) uint16_t q_s[MAP ? 8 : C * KSTR];     // Q rows
     __shared__ __align__(16) float a_s[C * CSTR];                  // A, then P fragments
-    __shared__ __align__(16) float t_s[C * CSTR];                  // T = (I + A)^{-1}
-    __shared__ __align__(16) bf16x8 wf_s[G::CT * G::KS * kWave];   // W A-fragments
+    // T = (I + A)^{-1}; without the erase term (no T) the same buffer holds V^T
+    constexpr int TS_FLOATS = (DELTA || C * CSTR * 2 >= DV * VSTR) ? C * CSTR : (DV * VSTR + 1) / 2;
+    __shared__ __align__(16) float t_s[TS_FLOATS];
+    __shared__ __align__(16) bf16x8 wf_s[DELTA ? G::CT * G::KS * kWave : 1];   // W A-fragments
     __shared__ __align__(16) uint16_t kt_s[DK * KTSTR];            // K^T
-    __shared__ __align__(16) float x_s[16 * CSTR16];              // one 16x16 fp32 tile (C)
+    __shared__ __align__(16) float x_s[DELTA ? 16 * CSTR16 : 4];   // one 16x16 fp32 tile (C)
     __shared__ float g_s[C], b_s[C], bg_s[C], dec_s[C], gam_s[C];  // g_s: G * log2(e)
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform
@@ -286,10 +291,11 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
             }
     }
     // T's blocks above the diagonal stay zero for the whole kernel
-    for (int e = tid; e < C * CSTR; e += kBlock) t_s[e] = 0.f;
+    for (int e = tid; e < TS_FLOATS; e += kBlock) t_s[e] = 0.f;
 
     uint16_t(*ks)[KSTR] = reinterpret_cast<uint16_t(*)[KSTR]>(kv_s);
-    uint16_t(*vt)[VSTR] = reinterpret_cast<uint16_t(*)[VSTR]>(kv_s);
+    uint16_t(*vt)[VSTR] = reinterpret_cast<uint16_t(*)[VSTR]>(DELTA ? static_cast<void *>(kv_s)
+                                                                     : static_cast<void *>(t_s));
     uint16_t(*qs)[KSTR] = reinterpret_cast<uint16_t(*)[KSTR]>(q_s);
     uint16_t(*kt)[KTSTR] = reinterpret_cast<uint16_t(*)[KTSTR]>(kt_s);
     // K^T A-fragment (d tile mt, chunk-row step s): K^T[16 mt + li][kmap(s, gq, e)]
@@ -347,6 +353,17 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
                 gam_s[lane] = ex;
                 bg_s[lane] = cur.beta * ex;
                 dec_s[lane] = exp2_fast(glast - x);
+            }
+        }
+        if constexpr (!DELTA) {
+            // V^T goes to its own buffer at once: without the inversion no later phase frees one
+            if (tid < R::VTHREADS) {
+#pragma unroll
+                for (int i = 0; i < R::NV; ++i) {
+                    const int e = tid + i * R::VTHREADS, rr = e % C, c8 = e / C;
+#pragma unroll
+                    for (int q8 = 0; q8 < 8; ++q8) vt[8 * c8 + q8][rr] = cur.v[i][q8];
+                }
             }
         }
         __syncthreads();
@@ -446,7 +463,7 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
             pf_s[((mt * G::CS + s) * 2 + 1) * kWave + lane] = f.l;
         };
         FragPair pa{}, pb{};
-        {
+        if constexpr (DELTA) {
             using I0 = IC<0>;
             using I1 = IC<1>;
             if constexpr (G::CT == 4) {
@@ -493,162 +510,184 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
                     *reinterpret_cast<f32x4 *>(&ts[r][c]) = zero4;
                 }
             }
-        }
-        __syncthreads();
-
-        // ---- C: the blocks of T below the diagonal (chunk 64: T10, T32 and the lower-left
-        // quarter T_BL = -T_BR A_BL T_TL), one output tile per wavefront:
-        //   T10 = -T11 A10 T00, T32 = -T33 A32 T22, X = A_BL T_TL, T_BL = -T_BR X.
-        // A wavefront recomputes the level-1 block it needs rather than waiting for it;
-        // the remaining P tiles fill the shorter chains.
-        if constexpr (G::NB == 4) {
-            if (wave == 0) {
-                const f32x4 t10 = -mm16(rowfrag(ts, 16, 16), mm16(rowfrag(as, 16, 0), accfrag(ts, 0, 0), zero4), zero4);
-                store_acc(ts, 16, 0, t10);
-                f32x4 x = mm16(rowfrag(as, 32, 0), accfrag(ts, 0, 0), zero4);
-                x = mm16(rowfrag(as, 32, 16), t10, x);
-                store_acc(ts, 32, 0, -mm16(rowfrag(ts, 32, 32), x, zero4));
-            } else if (wave == 1) {
-                const f32x4 x = mm16(rowfrag(as, 32, 16), accfrag(ts, 16, 16), zero4);
-                store_acc(ts, 32, 16, -mm16(rowfrag(ts, 32, 32), x, zero4));
-            } else if (wave == 2) {
-                const f32x4 t32 =
-                    -mm16(rowfrag(ts, 48, 48), mm16(rowfrag(as, 48, 32), accfrag(ts, 32, 32), zero4), zero4);
-                store_acc(ts, 48, 32, t32);
-                const f32x4 x21 = mm16(rowfrag(as, 32, 16), accfrag(ts, 16, 16), zero4);
-                const f32x4 x31 = mm16(rowfrag(as, 48, 16), accfrag(ts, 16, 16), zero4);
-                f32x4 y = mm16(rowfrag(ts, 48, 48), x31, zero4);
-                y = mm16(rowfrag(ts, 48, 32), x21, y);  // T32 row fragments: this wavefront's store
-                store_acc(ts, 48, 16, -y);
-            } else {
-                const f32x4 t10 = -mm16(rowfrag(ts, 16, 16), mm16(rowfrag(as, 16, 0), accfrag(ts, 0, 0), zero4), zero4);
-                const f32x4 t32 =
-                    -mm16(rowfrag(ts, 48, 48), mm16(rowfrag(as, 48, 32), accfrag(ts, 32, 32), zero4), zero4);
-                store_acc(xs, 0, 0, t32);  // private copy, read back as row fragments
-                f32x4 x20 = mm16(rowfrag(as, 32, 0), accfrag(ts, 0, 0), zero4);
-                x20 = mm16(rowfrag(as, 32, 16), t10, x20);
-                f32x4 x30 = mm16(rowfrag(as, 48, 0), accfrag(ts, 0, 0), zero4);
-                x30 = mm16(rowfrag(as, 48, 16), t10, x30);
-                f32x4 y = mm16(rowfrag(ts, 48, 48), x30, zero4);
-                y = mm16(rowfrag(xs, 0, 0), x20, y);
-                store_acc(ts, 48, 0, -y);
-            }
-        } else {
-            if (wave == 0) {
-                const f32x4 t10 = -mm16(rowfrag(ts, 16, 16), mm16(rowfrag(as, 16, 0), accfrag(ts, 0, 0), zero4), zero4);
-                store_acc(ts, 16, 0, t10);
-            }
-        }
-        if constexpr (!MAP && G::CT == 4) {
-            if (wave == 0) {
-                pb = p_pair(IC<3>{}, IC<0>{});
-            } else if (wave == 1) {
-                pa = p_pair(IC<1>{}, IC<0>{});
-                pb = p_pair(IC<2>{}, IC<0>{});
-            } else if (wave == 2) {
-                pb = p_pair(IC<3>{}, IC<1>{});
-            }
-        }
-        __syncthreads();
-
-        // ---- F: P fragments and V^T into LDS (A and K are dead); W A-fragments = W^T tiles
-        // (2 s2, ct) and (2 s2 + 1, ct), W = T diag(b exp G) K
-        if constexpr (!MAP) {
+        } else if constexpr (!MAP) {
+            // no erase term: only P is needed, and its tiles go straight to LDS (A's buffer is unused)
             if constexpr (G::CT == 4) {
                 if (wave == 0) {
-                    p_store(IC<3>{}, IC<0>{}, pb);
+                    p_store(IC<1>{}, IC<0>{}, p_pair(IC<1>{}, IC<0>{}));
+                    p_store(IC<0>{}, IC<0>{}, p_pair(IC<0>{}, IC<0>{}));
                 } else if (wave == 1) {
-                    p_store(IC<1>{}, IC<0>{}, pa);
-                    p_store(IC<2>{}, IC<0>{}, pb);
+                    p_store(IC<2>{}, IC<0>{}, p_pair(IC<2>{}, IC<0>{}));
+                    p_store(IC<2>{}, IC<1>{}, p_pair(IC<2>{}, IC<1>{}));
                 } else if (wave == 2) {
-                    p_store(IC<0>{}, IC<0>{}, pa);
-                    p_store(IC<3>{}, IC<1>{}, pb);
+                    p_store(IC<3>{}, IC<0>{}, p_pair(IC<3>{}, IC<0>{}));
                 } else {
-                    p_store(IC<2>{}, IC<1>{}, pa);
+                    p_store(IC<3>{}, IC<1>{}, p_pair(IC<3>{}, IC<1>{}));
                 }
             } else {
-                if (wave == 2) p_store(IC<0>{}, IC<0>{}, pa);
-                else if (wave == 3) p_store(IC<1>{}, IC<0>{}, pa);
+                if (wave == 0) p_store(IC<0>{}, IC<0>{}, p_pair(IC<0>{}, IC<0>{}));
+                else if (wave == 1) p_store(IC<1>{}, IC<0>{}, p_pair(IC<1>{}, IC<0>{}));
             }
         }
-        if (tid < R::VTHREADS) {
-#pragma unroll
-            for (int i = 0; i < R::NV; ++i) {
-                const int e = tid + i * R::VTHREADS, rr = e % C, c8 = e / C;
-#pragma unroll
-                for (int q8 = 0; q8 < 8; ++q8) vt[8 * c8 + q8][rr] = cur.v[i][q8];
+        if constexpr (DELTA || !MAP) __syncthreads();
+
+        if constexpr (DELTA) {
+            // ---- C: the blocks of T below the diagonal (chunk 64: T10, T32 and the lower-left
+            // quarter T_BL = -T_BR A_BL T_TL), one output tile per wavefront:
+            //   T10 = -T11 A10 T00, T32 = -T33 A32 T22, X = A_BL T_TL, T_BL = -T_BR X.
+            // A wavefront recomputes the level-1 block it needs rather than waiting for it;
+            // the remaining P tiles fill the shorter chains.
+            if constexpr (G::NB == 4) {
+                if (wave == 0) {
+                    const f32x4 t10 = -mm16(rowfrag(ts, 16, 16), mm16(rowfrag(as, 16, 0), accfrag(ts, 0, 0), zero4), zero4);
+                    store_acc(ts, 16, 0, t10);
+                    f32x4 x = mm16(rowfrag(as, 32, 0), accfrag(ts, 0, 0), zero4);
+                    x = mm16(rowfrag(as, 32, 16), t10, x);
+                    store_acc(ts, 32, 0, -mm16(rowfrag(ts, 32, 32), x, zero4));
+                } else if (wave == 1) {
+                    const f32x4 x = mm16(rowfrag(as, 32, 16), accfrag(ts, 16, 16), zero4);
+                    store_acc(ts, 32, 16, -mm16(rowfrag(ts, 32, 32), x, zero4));
+                } else if (wave == 2) {
+                    const f32x4 t32 =
+                        -mm16(rowfrag(ts, 48, 48), mm16(rowfrag(as, 48, 32), accfrag(ts, 32, 32), zero4), zero4);
+                    store_acc(ts, 48, 32, t32);
+                    const f32x4 x21 = mm16(rowfrag(as, 32, 16), accfrag(ts, 16, 16), zero4);
+                    const f32x4 x31 = mm16(rowfrag(as, 48, 16), accfrag(ts, 16, 16), zero4);
+                    f32x4 y = mm16(rowfrag(ts, 48, 48), x31, zero4);
+                    y = mm16(rowfrag(ts, 48, 32), x21, y);  // T32 row fragments: this wavefront's store
+                    store_acc(ts, 48, 16, -y);
+                } else {
+                    const f32x4 t10 = -mm16(rowfrag(ts, 16, 16), mm16(rowfrag(as, 16, 0), accfrag(ts, 0, 0), zero4), zero4);
+                    const f32x4 t32 =
+                        -mm16(rowfrag(ts, 48, 48), mm16(rowfrag(as, 48, 32), accfrag(ts, 32, 32), zero4), zero4);
+                    store_acc(xs, 0, 0, t32);  // private copy, read back as row fragments
+                    f32x4 x20 = mm16(rowfrag(as, 32, 0), accfrag(ts, 0, 0), zero4);
+                    x20 = mm16(rowfrag(as, 32, 16), t10, x20);
+                    f32x4 x30 = mm16(rowfrag(as, 48, 0), accfrag(ts, 0, 0), zero4);
+                    x30 = mm16(rowfrag(as, 48, 16), t10, x30);
+                    f32x4 y = mm16(rowfrag(ts, 48, 48), x30, zero4);
+                    y = mm16(rowfrag(xs, 0, 0), x20, y);
+                    store_acc(ts, 48, 0, -y);
+                }
+            } else {
+                if (wave == 0) {
+                    const f32x4 t10 = -mm16(rowfrag(ts, 16, 16), mm16(rowfrag(as, 16, 0), accfrag(ts, 0, 0), zero4), zero4);
+                    store_acc(ts, 16, 0, t10);
+                }
             }
+            if constexpr (!MAP && G::CT == 4) {
+                if (wave == 0) {
+                    pb = p_pair(IC<3>{}, IC<0>{});
+                } else if (wave == 1) {
+                    pa = p_pair(IC<1>{}, IC<0>{});
+                    pb = p_pair(IC<2>{}, IC<0>{});
+                } else if (wave == 2) {
+                    pb = p_pair(IC<3>{}, IC<1>{});
+                }
+            }
+            __syncthreads();
         }
+
         auto tb_frag = [&](int ct, int s, int hl) -> bf16x8 * {
             return reinterpret_cast<bf16x8 *>(&ts[16 * ct][0]) + (s * 2 + hl) * kWave + lane;
         };
-        if constexpr (kTbFrags) {
-            // wavefront ct owns T's row tile ct: one pass over it gives T diag(b exp G) for
-            // every W tile of that row and the T diag(b) fragments of U
-            const int ct = wave;
-            f32x4 accw[G::KT];
-#pragma unroll
-            for (int mt = 0; mt < G::KT; ++mt) accw[mt] = zero4;
-            bf16x8 tbh[G::CS], tbl[G::CS];
-#pragma unroll
-            for (int s = 0; s < G::CS; ++s) {
-                if (32 * s > 16 * ct + 15) continue;  // T is lower triangular
-                float x[8], xg[8], xb[8];
-                lds_slots_f32(&ts[16 * ct + li][0], s, gq, x);
-                const f32x4 bg0 = *reinterpret_cast<const f32x4 *>(&bg_s[32 * s + 4 * gq]);
-                const f32x4 bg1 = *reinterpret_cast<const f32x4 *>(&bg_s[32 * s + 16 + 4 * gq]);
-                const f32x4 b0 = *reinterpret_cast<const f32x4 *>(&b_s[32 * s + 4 * gq]);
-                const f32x4 b1 = *reinterpret_cast<const f32x4 *>(&b_s[32 * s + 16 + 4 * gq]);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    xg[e] = x[e] * bg0[e];
-                    xg[4 + e] = x[4 + e] * bg1[e];
-                    xb[e] = x[e] * b0[e];
-                    xb[4 + e] = x[4 + e] * b1[e];
+        if constexpr (DELTA) {
+            // ---- F: P fragments and V^T into LDS (A and K are dead); W A-fragments = W^T tiles
+            // (2 s2, ct) and (2 s2 + 1, ct), W = T diag(b exp G) K
+            if constexpr (!MAP) {
+                if constexpr (G::CT == 4) {
+                    if (wave == 0) {
+                        p_store(IC<3>{}, IC<0>{}, pb);
+                    } else if (wave == 1) {
+                        p_store(IC<1>{}, IC<0>{}, pa);
+                        p_store(IC<2>{}, IC<0>{}, pb);
+                    } else if (wave == 2) {
+                        p_store(IC<0>{}, IC<0>{}, pa);
+                        p_store(IC<3>{}, IC<1>{}, pb);
+                    } else {
+                        p_store(IC<2>{}, IC<1>{}, pa);
+                    }
+                } else {
+                    if (wave == 2) p_store(IC<0>{}, IC<0>{}, pa);
+                    else if (wave == 3) p_store(IC<1>{}, IC<0>{}, pa);
                 }
-                const bf16x8 bfr = pack_bf16(xg);
-                split_bf16(xb, tbh[s], tbl[s]);
-#pragma unroll
-                for (int mt = 0; mt < G::KT; ++mt) accw[mt] = mfma_bf16(kfrag(mt, s), bfr, accw[mt]);
             }
-#pragma unroll
-            for (int s2 = 0; s2 < G::KS; ++s2) {
-                float x[8];
-                acc_pair_to_slots(accw[2 * s2], accw[2 * s2 + 1], x);
-                wf_s[(ct * G::KS + s2) * kWave + lane] = pack_bf16(x);
+            if (tid < R::VTHREADS) {
+    #pragma unroll
+                for (int i = 0; i < R::NV; ++i) {
+                    const int e = tid + i * R::VTHREADS, rr = e % C, c8 = e / C;
+    #pragma unroll
+                    for (int q8 = 0; q8 < 8; ++q8) vt[8 * c8 + q8][rr] = cur.v[i][q8];
+                }
             }
-            // this wavefront's T rows have all been read (LDS keeps a wavefront's accesses in
-            // order); keep the compiler from moving the stores above the loads
-            __asm__ __volatile__("" ::: "memory");
-#pragma unroll
-            for (int s = 0; s < G::CS; ++s) {
-                if (32 * s > 16 * ct + 15) continue;
-                *tb_frag(ct, s, 0) = tbh[s];
-                *tb_frag(ct, s, 1) = tbl[s];
-            }
-        } else {
-#pragma unroll
-            for (int p = 0; p < G::CT * G::KS; ++p) {
-                if (p % kWaves != wave) continue;
-                const int ct = p % G::CT, s2 = p / G::CT;
-                f32x4 acc0 = zero4, acc1 = zero4;
-#pragma unroll
+            if constexpr (kTbFrags) {
+                // wavefront ct owns T's row tile ct: one pass over it gives T diag(b exp G) for
+                // every W tile of that row and the T diag(b) fragments of U
+                const int ct = wave;
+                f32x4 accw[G::KT];
+    #pragma unroll
+                for (int mt = 0; mt < G::KT; ++mt) accw[mt] = zero4;
+                bf16x8 tbh[G::CS], tbl[G::CS];
+    #pragma unroll
                 for (int s = 0; s < G::CS; ++s) {
                     if (32 * s > 16 * ct + 15) continue;  // T is lower triangular
-                    float x[8];
+                    float x[8], xg[8], xb[8];
                     lds_slots_f32(&ts[16 * ct + li][0], s, gq, x);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) x[e] *= bg_s[kmap(s, gq, e)];
-                    const bf16x8 bfr = pack_bf16(x);
-                    acc0 = mfma_bf16(kfrag(2 * s2, s), bfr, acc0);
-                    acc1 = mfma_bf16(kfrag(2 * s2 + 1, s), bfr, acc1);
+                    const f32x4 bg0 = *reinterpret_cast<const f32x4 *>(&bg_s[32 * s + 4 * gq]);
+                    const f32x4 bg1 = *reinterpret_cast<const f32x4 *>(&bg_s[32 * s + 16 + 4 * gq]);
+                    const f32x4 b0 = *reinterpret_cast<const f32x4 *>(&b_s[32 * s + 4 * gq]);
+                    const f32x4 b1 = *reinterpret_cast<const f32x4 *>(&b_s[32 * s + 16 + 4 * gq]);
+    #pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        xg[e] = x[e] * bg0[e];
+                        xg[4 + e] = x[4 + e] * bg1[e];
+                        xb[e] = x[e] * b0[e];
+                        xb[4 + e] = x[4 + e] * b1[e];
+                    }
+                    const bf16x8 bfr = pack_bf16(xg);
+                    split_bf16(xb, tbh[s], tbl[s]);
+    #pragma unroll
+                    for (int mt = 0; mt < G::KT; ++mt) accw[mt] = mfma_bf16(kfrag(mt, s), bfr, accw[mt]);
                 }
-                float x[8];
-                acc_pair_to_slots(acc0, acc1, x);
-                wf_s[(ct * G::KS + s2) * kWave + lane] = pack_bf16(x);
+    #pragma unroll
+                for (int s2 = 0; s2 < G::KS; ++s2) {
+                    float x[8];
+                    acc_pair_to_slots(accw[2 * s2], accw[2 * s2 + 1], x);
+                    wf_s[(ct * G::KS + s2) * kWave + lane] = pack_bf16(x);
+                }
+                // this wavefront's T rows have all been read (LDS keeps a wavefront's accesses in
+                // order); keep the compiler from moving the stores above the loads
+                __asm__ __volatile__("" ::: "memory");
+    #pragma unroll
+                for (int s = 0; s < G::CS; ++s) {
+                    if (32 * s > 16 * ct + 15) continue;
+                    *tb_frag(ct, s, 0) = tbh[s];
+                    *tb_frag(ct, s, 1) = tbl[s];
+                }
+            } else {
+    #pragma unroll
+                for (int p = 0; p < G::CT * G::KS; ++p) {
+                    if (p % kWaves != wave) continue;
+                    const int ct = p % G::CT, s2 = p / G::CT;
+                    f32x4 acc0 = zero4, acc1 = zero4;
+    #pragma unroll
+                    for (int s = 0; s < G::CS; ++s) {
+                        if (32 * s > 16 * ct + 15) continue;  // T is lower triangular
+                        float x[8];
+                        lds_slots_f32(&ts[16 * ct + li][0], s, gq, x);
+    #pragma unroll
+                        for (int e = 0; e < 8; ++e) x[e] *= bg_s[kmap(s, gq, e)];
+                        const bf16x8 bfr = pack_bf16(x);
+                        acc0 = mfma_bf16(kfrag(2 * s2, s), bfr, acc0);
+                        acc1 = mfma_bf16(kfrag(2 * s2 + 1, s), bfr, acc1);
+                    }
+                    float x[8];
+                    acc_pair_to_slots(acc0, acc1, x);
+                    wf_s[(ct * G::KS + s2) * kWave + lane] = pack_bf16(x);
+                }
             }
+            __syncthreads();
         }
-        __syncthreads();
 
         // next chunk's rows: loads in flight during this chunk's slice work
         if (n + 1 < n1) load_chunk<DK, DV, C, MAP>(cur, a, b, h, n + 1, tid);
@@ -658,10 +697,28 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
         for (int j = 0; j < G::SPW; ++j) {
             const int sl = wave + kWaves * j;
             const bool value_slice = sl < G::VT;
+            if constexpr (!DELTA) {
+                if (!value_slice) {
+                    // identity columns of a piece map: with no erase term only the decay acts
+                    const float gl = gam_s[C - 1];
+#pragma unroll
+                    for (int mt = 0; mt < G::KT; ++mt) St[j][mt] = gl * St[j][mt];
+                    continue;
+                }
+            }
             f32x4 D[G::CT];
 #pragma unroll
             for (int ct = 0; ct < G::CT; ++ct) D[ct] = zero4;
-            if (value_slice) {
+            if (!DELTA) {
+                // no erase term: Delta = diag(b) V, four consecutive chunk rows per lane from V^T
+#pragma unroll
+                for (int ct = 0; ct < G::CT; ++ct) {
+                    const u16x4 v4 = *reinterpret_cast<const u16x4 *>(&vt[16 * sl + li][16 * ct + 4 * gq]);
+                    const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&b_s[16 * ct + 4 * gq]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) D[ct][r] = b4[r] * from_bf16(v4[r]);
+                }
+            } else if (value_slice) {
 #pragma unroll
                 for (int s = 0; s < G::CS; ++s) {
                     const bf16x8 vb = lds_frag_bf16(&vt[16 * sl + li][0], s, gq);
@@ -684,19 +741,22 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
                     }
                 }
             }
-            bf16x8 Sb[G::KS];
+            if constexpr (DELTA) {
+                bf16x8 Sb[G::KS];
 #pragma unroll
-            for (int s = 0; s < G::KS; ++s) {
-                float x[8];
-                acc_pair_to_slots(St[j][2 * s], St[j][2 * s + 1], x);
-                Sb[s] = pack_bf16(x);
-            }
+                for (int s = 0; s < G::KS; ++s) {
+                    float x[8];
+                    acc_pair_to_slots(St[j][2 * s], St[j][2 * s + 1], x);
+                    Sb[s] = pack_bf16(x);
+                }
 #pragma unroll
-            for (int ct = 0; ct < G::CT; ++ct) {
-                f32x4 acc = zero4;
+                for (int ct = 0; ct < G::CT; ++ct) {
+                    f32x4 acc = zero4;
 #pragma unroll
-                for (int s = 0; s < G::KS; ++s) acc = mfma_bf16(wf_s[(ct * G::KS + s) * kWave + lane], Sb[s], acc);
-                D[ct] -= acc;  // Delta = U - W St
+                    for (int s = 0; s < G::KS; ++s)
+                        acc = mfma_bf16(wf_s[(ct * G::KS + s) * kWave + lane], Sb[s], acc);
+                    D[ct] -= acc;  // Delta = U - W St
+                }
             }
 
             if (!MAP && value_slice) {
@@ -919,7 +979,7 @@ size_t chunk_ws_bytes(int B, int T, int H) {
     return ((maps + 255) & ~static_cast<size_t>(255)) + starts;
 }
 
-template <int DK, int DV, int C>
+template <int DK, int DV, int C, bool DELTA>
 hipError_t run_chunk(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,
                      const float *beta, const float *s0, float *o, float *s_out, int B, int T, int H,
                      void *ws, hipStream_t stream) {
@@ -935,7 +995,7 @@ hipError_t run_chunk(const uint16_t *q, const uint16_t *k, const uint16_t *v, co
     a.scale = 1.0f / sqrtf(static_cast<float>(DK));
     if (P == 1) {
         a.s_start = s0;
-        hipLaunchKernelGGL((chunk_kernel<DK, DV, C, false>), grid(BH), dim3(kBlock), 0, stream, a);
+        hipLaunchKernelGGL((chunk_kernel<DK, DV, C, false, DELTA>), grid(BH), dim3(kBlock), 0, stream, a);
         return hipGetLastError();
     }
     const size_t maps_bytes = static_cast<size_t>(BH) * (P - 1) * DK * (DV + DK) * 4;
@@ -943,7 +1003,7 @@ hipError_t run_chunk(const uint16_t *q, const uint16_t *k, const uint16_t *v, co
     float *starts = reinterpret_cast<float *>(static_cast<char *>(ws) +
                                               ((maps_bytes + 255) & ~static_cast<size_t>(255)));
     a.maps = maps;
-    hipLaunchKernelGGL((chunk_kernel<DK, DV, C, true>), grid(BH * (P - 1)), dim3(kBlock), 0, stream, a);
+    hipLaunchKernelGGL((chunk_kernel<DK, DV, C, true, DELTA>), grid(BH * (P - 1)), dim3(kBlock), 0, stream, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL((chain_kernel<DK, DV>), dim3(BH * (DV / 16)), dim3(kWave), 0, stream,
@@ -951,7 +1011,7 @@ hipError_t run_chunk(const uint16_t *q, const uint16_t *k, const uint16_t *v, co
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     a.s_start = starts;
-    hipLaunchKernelGGL((chunk_kernel<DK, DV, C, false>), grid(BH * P), dim3(kBlock), 0, stream, a);
+    hipLaunchKernelGGL((chunk_kernel<DK, DV, C, false, DELTA>), grid(BH * P), dim3(kBlock), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -972,10 +1032,11 @@ size_t prefill_chunk_workspace(int B, int T, int H, int dk, int dv, int chunk) {
 hipError_t launch_prefill_chunk(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                 const float *g, const float *beta, const float *s0, float *o,
                                 float *s_out, int B, int T, int H, int dk, int dv, int chunk,
-                                void *ws, hipStream_t stream) {
+                                bool delta, void *ws, hipStream_t stream) {
 #define GDN_RUN(DK_, DV_, C_)                                                                      \
     if (dk == DK_ && dv == DV_ && chunk == C_)                                                     \
-        return run_chunk<DK_, DV_, C_>(q, k, v, g, beta, s0, o, s_out, B, T, H, ws, stream);
+        return delta ? run_chunk<DK_, DV_, C_, true>(q, k, v, g, beta, s0, o, s_out, B, T, H, ws, stream) \
+                     : run_chunk<DK_, DV_, C_, false>(q, k, v, g, beta, s0, o, s_out, B, T, H, ws, stream);
     GDN_CHUNK_CASES(GDN_RUN)
 #undef GDN_RUN
     return hipErrorInvalidValue;

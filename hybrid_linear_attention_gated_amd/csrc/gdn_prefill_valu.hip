@@ -19,6 +19,9 @@
 // arithmetic.  Decays are always formed as exp of a non-positive difference
 // of cumulative gates (never as a ratio of two exponentials).
 //
+// Without the erase term (DELTA = false: S_t = a_t S_{t-1} + b_t v_t k_t^T) the
+// same chunk form holds with A = 0, T = I and no W St term: Delta = diag(b) V.
+//
 // Work layout: one workgroup per (sequence, head, 16-wide value slice);
 // value columns of the state evolve independently, so slices never talk.
 // Chunks run in order inside the workgroup with the state slice in LDS.
@@ -30,7 +33,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kSW = 16;  // value columns per workgroup
 
-template <int DK, int C, typename TIn>
+template <int DK, int C, typename TIn, bool DELTA>
 __global__ __launch_bounds__(kThreads) void prefill_valu_kernel(
     const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, const float *__restrict__ s0,
@@ -76,7 +79,7 @@ __global__ __launch_bounds__(kThreads) void prefill_valu_kernel(
         for (int e = tid; e < L * L; e += kThreads) {
             const int r = e / L, j = e % L;
             float val = 0.f;
-            if (j < r) {
+            if (DELTA && j < r) {
                 float dot = 0.f;
                 for (int m = 0; m < DK; ++m) dot += load_in(k, row(r) * DK + m) * load_in(k, row(j) * DK + m);
                 val = bet[r] * dot * expf(Gc[r] - Gc[j]);
@@ -87,7 +90,7 @@ __global__ __launch_bounds__(kThreads) void prefill_valu_kernel(
         __syncthreads();
 
         // forward substitution, one row at a time: T[r][j] = -(A[r][j] + sum_{j<m<r} A[r][m] T[m][j])
-        for (int r = 1; r < L; ++r) {
+        for (int r = 1; DELTA && r < L; ++r) {
             if (tid < r) {
                 const int j = tid;
                 float acc = A[r][j];
@@ -104,7 +107,8 @@ __global__ __launch_bounds__(kThreads) void prefill_valu_kernel(
             for (int j = 0; j <= r; ++j) u += Tm[r][j] * bet[j] * load_in(v, row(j) * DV + col0 + c);
             U[r][c] = u;
             float y = 0.f;
-            for (int m = 0; m < DK; ++m) y += load_in(k, row(r) * DK + m) * St[m][c];
+            if (DELTA)
+                for (int m = 0; m < DK; ++m) y += load_in(k, row(r) * DK + m) * St[m][c];
             Y[r][c] = y;
         }
         __syncthreads();
@@ -113,7 +117,8 @@ __global__ __launch_bounds__(kThreads) void prefill_valu_kernel(
         for (int e = tid; e < L * kSW; e += kThreads) {
             const int r = e / kSW, c = e % kSW;
             float w = 0.f;
-            for (int j = 0; j <= r; ++j) w += Tm[r][j] * bet[j] * gam[j] * Y[j][c];
+            if (DELTA)
+                for (int j = 0; j <= r; ++j) w += Tm[r][j] * bet[j] * gam[j] * Y[j][c];
             D[r][c] = U[r][c] - w;
         }
         // P = Q K^T .* exp(G_r - G_j) .* tril (inclusive), reusing A
@@ -160,22 +165,27 @@ __global__ __launch_bounds__(kThreads) void prefill_valu_kernel(
 template <int DK, int C, typename TIn>
 hipError_t launch_valu_t(const void *q, const void *k, const void *v, const float *g,
                          const float *beta, const float *s0, float *o, float *s_out, int B, int T,
-                         int H, int dv, hipStream_t stream) {
+                         int H, int dv, bool delta, hipStream_t stream) {
     const int blocks = B * H * (dv / kSW);
     const float scale = 1.0f / sqrtf(static_cast<float>(DK));
-    hipLaunchKernelGGL((prefill_valu_kernel<DK, C, TIn>), dim3(blocks), dim3(kThreads), 0, stream,
-                       static_cast<const TIn *>(q), static_cast<const TIn *>(k),
-                       static_cast<const TIn *>(v), g, beta, s0, o, s_out, T, H, dv, scale);
+    if (delta)
+        hipLaunchKernelGGL((prefill_valu_kernel<DK, C, TIn, true>), dim3(blocks), dim3(kThreads), 0,
+                           stream, static_cast<const TIn *>(q), static_cast<const TIn *>(k),
+                           static_cast<const TIn *>(v), g, beta, s0, o, s_out, T, H, dv, scale);
+    else
+        hipLaunchKernelGGL((prefill_valu_kernel<DK, C, TIn, false>), dim3(blocks), dim3(kThreads), 0,
+                           stream, static_cast<const TIn *>(q), static_cast<const TIn *>(k),
+                           static_cast<const TIn *>(v), g, beta, s0, o, s_out, T, H, dv, scale);
     return hipGetLastError();
 }
 
 template <typename TIn>
 hipError_t dispatch_valu(const void *q, const void *k, const void *v, const float *g,
                          const float *beta, const float *s0, float *o, float *s_out, int B, int T,
-                         int H, int dk, int dv, int chunk, hipStream_t stream) {
+                         int H, int dk, int dv, int chunk, bool delta, hipStream_t stream) {
 #define GDN_VALU(DK_, C_)                                                                         \
     if (dk == DK_ && chunk == C_)                                                                 \
-        return launch_valu_t<DK_, C_, TIn>(q, k, v, g, beta, s0, o, s_out, B, T, H, dv, stream);
+        return launch_valu_t<DK_, C_, TIn>(q, k, v, g, beta, s0, o, s_out, B, T, H, dv, delta, stream);
     GDN_VALU(16, 16) GDN_VALU(16, 32) GDN_VALU(16, 64)
     GDN_VALU(64, 16) GDN_VALU(64, 32) GDN_VALU(64, 64)
     GDN_VALU(128, 16) GDN_VALU(128, 32) GDN_VALU(128, 64)
@@ -188,10 +198,11 @@ hipError_t dispatch_valu(const void *q, const void *k, const void *v, const floa
 hipError_t launch_prefill_valu(const void *q, const void *k, const void *v, const float *g,
                                const float *beta, const float *s0, float *o, float *s_out, int B,
                                int T, int H, int dk, int dv, int chunk, gdn_dtype dt,
-                               hipStream_t stream) {
+                               bool delta, hipStream_t stream) {
     if (dt == GDN_BF16)
-        return dispatch_valu<uint16_t>(q, k, v, g, beta, s0, o, s_out, B, T, H, dk, dv, chunk, stream);
-    return dispatch_valu<float>(q, k, v, g, beta, s0, o, s_out, B, T, H, dk, dv, chunk, stream);
+        return dispatch_valu<uint16_t>(q, k, v, g, beta, s0, o, s_out, B, T, H, dk, dv, chunk, delta,
+                                       stream);
+    return dispatch_valu<float>(q, k, v, g, beta, s0, o, s_out, B, T, H, dk, dv, chunk, delta, stream);
 }
 
 }  // namespace gdn

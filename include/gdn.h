@@ -34,6 +34,17 @@
  *     written nothing.  Faults inside kernels surface at the caller's next
  *     synchronisation with the stream.
  *   - Supported sizes: d_k, d_v in {16, 64, 128}; chunk in {16, 32, 64}.
+ *
+ * A second rule (gdn_rule, the *_rule entry points) drops the erase term:
+ *
+ *     S_t = a_t S_{t-1} + b_t v_t k_t^T
+ *
+ * the uniform decay the Priming article attributes to Mamba-2, which the
+ * HyLo hybrids use as the other linear block (aiexpert.news article on HyLo:
+ * selected attention layers become Mamba2 or Gated DeltaNet blocks; we0.ai
+ * Priming article: Mamba-2 lets the whole state fade while new information is
+ * added).  Everything else -- layouts, readout, scale, chunking, workspace --
+ * is shared by both rules.
  */
 #ifndef GDN_H
 #define GDN_H
@@ -44,7 +55,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 #if defined(__GNUC__) || defined(__clang__)
 #define GDN_API __attribute__((visibility("default")))
@@ -67,6 +78,11 @@ typedef enum gdn_dtype {
     GDN_F32 = 0,  /* IEEE binary32 */
     GDN_BF16 = 1  /* bfloat16 (upper half of a binary32) */
 } gdn_dtype;
+
+typedef enum gdn_rule {
+    GDN_RULE_GATED_DELTA = 0, /* S_t = a_t S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T */
+    GDN_RULE_GATED_DECAY = 1  /* S_t = a_t S_{t-1} + b_t v_t k_t^T (no erase term) */
+} gdn_rule;
 
 /*
  * gdn_chunk_prefill -- run the rule over T tokens of B sequences at once.
@@ -107,8 +123,25 @@ GDN_API gdn_status gdn_chunk_prefill(const void *q, const void *k, const void *v
                              void *stream);
 
 /*
+ * gdn_chunk_prefill_rule -- gdn_chunk_prefill for either rule.  Identical
+ * arguments, layouts, workspace and errors; an unknown `rule` returns
+ * GDN_ERR_UNSUPPORTED.  gdn_chunk_prefill(...) is
+ * gdn_chunk_prefill_rule(GDN_RULE_GATED_DELTA, ...).
+ */
+GDN_API gdn_status gdn_chunk_prefill_rule(gdn_rule rule,
+                             const void *q, const void *k, const void *v,
+                             const float *g, const float *beta,
+                             const float *initial_state,
+                             float *o, float *final_state,
+                             int B, int T, int H, int d_k, int d_v, int chunk,
+                             gdn_dtype qkv_dtype,
+                             void *workspace, size_t workspace_bytes,
+                             void *stream);
+
+/*
  * Bytes of device scratch gdn_chunk_prefill needs for these sizes (0 if
- * none).  Returns 0 as well for arguments gdn_chunk_prefill would reject.
+ * none); the same size serves gdn_chunk_prefill_rule with either rule.
+ * Returns 0 as well for arguments gdn_chunk_prefill would reject.
  */
 GDN_API size_t gdn_chunk_prefill_workspace_size(int B, int T, int H, int d_k, int d_v, int chunk,
                                         gdn_dtype qkv_dtype);
@@ -127,6 +160,17 @@ GDN_API size_t gdn_chunk_prefill_workspace_size(int B, int T, int H, int d_k, in
  * GDN_ERR_ALIAS (o or state overlapping an input or each other), GDN_ERR_HIP.
  */
 GDN_API gdn_status gdn_decode_step(const void *q, const void *k, const void *v,
+                           const float *g, const float *beta,
+                           float *state, float *o,
+                           int N, int H, int d_k, int d_v,
+                           gdn_dtype qkv_dtype, void *stream);
+
+/*
+ * gdn_decode_step_rule -- gdn_decode_step for either rule (same arguments and
+ * errors; an unknown `rule` returns GDN_ERR_UNSUPPORTED).
+ */
+GDN_API gdn_status gdn_decode_step_rule(gdn_rule rule,
+                           const void *q, const void *k, const void *v,
                            const float *g, const float *beta,
                            float *state, float *o,
                            int N, int H, int d_k, int d_v,

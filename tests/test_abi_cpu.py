@@ -26,12 +26,13 @@ def test_library_exports_every_declared_symbol():
     L = gdn.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert gdn.gdn_version() == 1
+    assert gdn.gdn_version() == 2
 
 
 def test_status_strings():
     for code in range(8):
         assert gdn.gdn_status_string(code).startswith(gdn.STATUS[code])
+    assert "rule" in gdn.gdn_status_string(3)
     assert gdn.gdn_status_string(99) == "unknown gdn_status"
 
 
@@ -105,3 +106,23 @@ def test_workspace_size():
     # rejected arguments and T = 0 need nothing
     assert gdn.gdn_chunk_prefill_workspace_size(1, 64, 2, 48, 64, 64, BF16) == 0
     assert gdn.gdn_chunk_prefill_workspace_size(1, 0, 2, 64, 64, 64, BF16) == 0
+
+
+def test_rule_entry_points_validate_the_rule():
+    args = dict(q=addr(0), k=addr(1), v=addr(2), g=addr(3), beta=addr(4), s0=None, o=addr(5),
+                sf=addr(6), B=1, T=65536, H=2, dk=64, dv=64, chunk=64, dt=BF16, ws=addr(7),
+                ws_bytes=1 << 30, stream=None)
+    pre = lambda rule, **kw: gdn.gdn_chunk_prefill_rule(
+        rule, *[dict(args, **kw)[n] for n in ("q", "k", "v", "g", "beta", "s0", "o", "sf", "B", "T", "H",
+                                              "dk", "dv", "chunk", "dt", "ws", "ws_bytes", "stream")])
+    assert pre(2) == UNSUP and pre(-1) == UNSUP
+    # the rule is checked first, then the same argument checks as gdn_chunk_prefill
+    for rule in (gdn.GDN_RULE_GATED_DELTA, gdn.GDN_RULE_GATED_DECAY):
+        assert pre(rule, q=None) == NULL and pre(rule, dk=32) == UNSUP and pre(rule, o=addr(0)) == ALIAS
+    dec = lambda rule, **kw: gdn.gdn_decode_step_rule(
+        rule, *[dict(dict(q=addr(0), k=addr(1), v=addr(2), g=addr(3), beta=addr(4), st=addr(5), o=addr(6),
+                          N=4, H=2, dk=64, dv=64, dt=BF16, stream=None), **kw)[n]
+                for n in ("q", "k", "v", "g", "beta", "st", "o", "N", "H", "dk", "dv", "dt", "stream")])
+    assert dec(5) == UNSUP
+    assert dec(gdn.GDN_RULE_GATED_DECAY, st=addr(2)) == ALIAS
+    assert dec(gdn.GDN_RULE_GATED_DECAY, N=0, q=None) == OK
