@@ -35,7 +35,8 @@ GDN_RULE_GATED_DELTA, GDN_RULE_GATED_DECAY = 0, 1
 STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_UNSUPPORTED",
           4: "GDN_ERR_ALIGN", 5: "GDN_ERR_ALIAS", 6: "GDN_ERR_WORKSPACE", 7: "GDN_ERR_HIP"}
 EXPORTS = ("gdn_chunk_prefill", "gdn_chunk_prefill_rule", "gdn_chunk_prefill_workspace_size",
-           "gdn_decode_step", "gdn_decode_step_rule", "gdn_status_string", "gdn_version")
+           "gdn_decode_step", "gdn_decode_step_rule", "gdn_decode_step_slots", "gdn_status_string",
+           "gdn_version")
 
 
 class GdnError(RuntimeError):
@@ -67,6 +68,9 @@ def lib():
         L.gdn_decode_step.restype = i32
         L.gdn_decode_step_rule.argtypes = [i32] + L.gdn_decode_step.argtypes
         L.gdn_decode_step_rule.restype = i32
+        L.gdn_decode_step_slots.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32,
+                                            i32, vp]
+        L.gdn_decode_step_slots.restype = i32
         L.gdn_status_string.argtypes = [i32]
         L.gdn_status_string.restype = ctypes.c_char_p
         L.gdn_version.argtypes = []
@@ -100,6 +104,12 @@ def gdn_decode_step(q, k, v, g, beta, state, o, N, H, d_k, d_v, qkv_dtype, strea
 def gdn_decode_step_rule(rule, q, k, v, g, beta, state, o, N, H, d_k, d_v, qkv_dtype, stream) -> int:
     return lib().gdn_decode_step_rule(rule, q, k, v, g, beta, state, o, N, H, d_k, d_v, qkv_dtype,
                                       stream)
+
+
+def gdn_decode_step_slots(rule, q, k, v, g, beta, state_pool, slots, pool_size, o, N, H, d_k, d_v,
+                          qkv_dtype, stream) -> int:
+    return lib().gdn_decode_step_slots(rule, q, k, v, g, beta, state_pool, slots, pool_size, o, N, H,
+                                       d_k, d_v, qkv_dtype, stream)
 
 
 def gdn_status_string(status: int) -> str:
@@ -201,7 +211,35 @@ def decode_step(q, k, v, g, beta, state, *, out=None, stream=None, rule=GDN_RULE
     return out
 
 
+def decode_step_slots(q, k, v, g, beta, state_pool, slots, *, out=None, stream=None,
+                      rule=GDN_RULE_GATED_DELTA):
+    """q, k [N,H,d_k]; v [N,H,d_v]; g, beta [N,H] fp32; state_pool [P,H,d_k,d_v] fp32;
+    slots [N] int32 on the GPU: sequence n updates state_pool[slots[n]] in place; a slot
+    outside [0, P) is padding (zero output, no state touched).  Returns o fp32 [N,H,d_v]."""
+    import torch
+    N, H, d_k = q.shape
+    d_v = v.shape[-1]
+    dt = _dtype_code(q)
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, q.dtype)
+    _check(g, "g", torch.float32)
+    _check(beta, "beta", torch.float32)
+    _check(state_pool, "state_pool", torch.float32)
+    _check(slots, "slots", torch.int32)
+    if out is None:
+        out = torch.empty((N, H, d_v), device=q.device, dtype=torch.float32)
+    _check(out, "out", torch.float32)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = gdn_decode_step_slots(rule, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool),
+                               _ptr(slots), state_pool.shape[0], _ptr(out), N, H, d_k, d_v, dt, stream)
+    if st != 0:
+        raise GdnError(st, "gdn_decode_step_slots")
+    return out
+
+
 __all__ = ["EXPORTS", "GDN_F32", "GDN_BF16", "GDN_RULE_GATED_DELTA", "GDN_RULE_GATED_DECAY", "GdnError",
            "lib", "gdn_chunk_prefill", "gdn_chunk_prefill_rule", "gdn_chunk_prefill_workspace_size",
            "gdn_decode_step", "gdn_decode_step_rule", "gdn_status_string", "gdn_version",
-           "chunk_prefill", "decode_step", "workspace_bytes"]
+           "gdn_decode_step_slots", "chunk_prefill", "decode_step", "decode_step_slots",
+           "workspace_bytes"]

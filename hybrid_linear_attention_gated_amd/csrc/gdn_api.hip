@@ -162,33 +162,59 @@ gdn_status gdn_chunk_prefill(const void *q, const void *k, const void *v, const 
                                   workspace_bytes, stream);
 }
 
-gdn_status gdn_decode_step_rule(gdn_rule rule, const void *q, const void *k, const void *v,
-                                const float *g, const float *beta, float *state, float *o, int N,
-                                int H, int d_k, int d_v, gdn_dtype qkv_dtype, void *stream) {
+namespace {
+
+// shared by the decode entry points: slots == NULL means sequence n owns state n (pool = N)
+gdn_status decode_impl(gdn_rule rule, const void *q, const void *k, const void *v, const float *g,
+                       const float *beta, float *state, const int32_t *slots, int pool, float *o,
+                       int N, int H, int d_k, int d_v, gdn_dtype qkv_dtype, void *stream) {
     if (rule != GDN_RULE_GATED_DELTA && rule != GDN_RULE_GATED_DECAY) return GDN_ERR_UNSUPPORTED;
-    if (N < 0 || H <= 0 || d_k <= 0 || d_v <= 0) return GDN_ERR_SHAPE;
+    if (N < 0 || H <= 0 || d_k <= 0 || d_v <= 0 || pool < 0) return GDN_ERR_SHAPE;
     if (qkv_dtype != GDN_F32 && qkv_dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
     if (!supported_dim(d_k) || !supported_dim(d_v)) return GDN_ERR_UNSUPPORTED;
-    if (prod({N, H, d_k, d_v}) == SIZE_MAX || prod({N, H, 4}) > 0x7fffffffULL) return GDN_ERR_SHAPE;
+    if (prod({N, H, d_k, d_v}) == SIZE_MAX || prod({pool, H, d_k, d_v}) == SIZE_MAX ||
+        prod({N, H, 4}) > 0x7fffffffULL)
+        return GDN_ERR_SHAPE;
     if (N == 0) return GDN_OK;
-    if (!q || !k || !v || !g || !beta || !state || !o) return GDN_ERR_NULL;
-    const void *ptrs[] = {q, k, v, g, beta, state, o};
+    if (!q || !k || !v || !g || !beta || !o) return GDN_ERR_NULL;
+    if ((!state && pool > 0) || (slots == nullptr && !state)) return GDN_ERR_NULL;
+    const void *ptrs[] = {q, k, v, g, beta, state, o, slots};
     for (const void *p : ptrs)
-        if (!aligned16(p)) return GDN_ERR_ALIGN;
+        if (p && !aligned16(p)) return GDN_ERR_ALIGN;
 
     const size_t es = elem_bytes(qkv_dtype);
     const Span s_q = span(q, prod({N, H, d_k}) * es), s_k = span(k, prod({N, H, d_k}) * es);
     const Span s_v = span(v, prod({N, H, d_v}) * es);
     const Span s_g = span(g, prod({N, H}) * 4), s_b = span(beta, prod({N, H}) * 4);
-    const Span s_s = span(state, prod({N, H, d_k, d_v}) * 4), s_o = span(o, prod({N, H, d_v}) * 4);
-    const Span inputs[] = {s_q, s_k, s_v, s_g, s_b};
+    const Span s_s = state ? span(state, prod({pool, H, d_k, d_v}) * 4) : Span{0, 0};
+    const Span s_o = span(o, prod({N, H, d_v}) * 4);
+    const Span s_slot = slots ? span(slots, static_cast<size_t>(N) * 4) : Span{0, 0};
+    const Span inputs[] = {s_q, s_k, s_v, s_g, s_b, s_slot};
     for (const Span &in : inputs)
         if (overlap(s_o, in) || overlap(s_s, in)) return GDN_ERR_ALIAS;
     if (overlap(s_o, s_s)) return GDN_ERR_ALIAS;
 
     const hipError_t err = launch_decode(q, k, v, g, beta, state, o, N, H, d_k, d_v, qkv_dtype,
-                                         rule == GDN_RULE_GATED_DELTA, static_cast<hipStream_t>(stream));
+                                         rule == GDN_RULE_GATED_DELTA, slots, pool,
+                                         static_cast<hipStream_t>(stream));
     return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+}  // namespace
+
+gdn_status gdn_decode_step_rule(gdn_rule rule, const void *q, const void *k, const void *v,
+                                const float *g, const float *beta, float *state, float *o, int N,
+                                int H, int d_k, int d_v, gdn_dtype qkv_dtype, void *stream) {
+    return decode_impl(rule, q, k, v, g, beta, state, nullptr, N, o, N, H, d_k, d_v, qkv_dtype, stream);
+}
+
+gdn_status gdn_decode_step_slots(gdn_rule rule, const void *q, const void *k, const void *v,
+                                 const float *g, const float *beta, float *state_pool,
+                                 const int32_t *slots, int pool_size, float *o, int N, int H,
+                                 int d_k, int d_v, gdn_dtype qkv_dtype, void *stream) {
+    if (N > 0 && !slots) return GDN_ERR_NULL;
+    return decode_impl(rule, q, k, v, g, beta, state_pool, slots, pool_size, o, N, H, d_k, d_v,
+                       qkv_dtype, stream);
 }
 
 gdn_status gdn_decode_step(const void *q, const void *k, const void *v, const float *g,

@@ -13,6 +13,12 @@
 // Without the erase term (DELTA = false, S' = a S + b v k^T) delta = b v and
 // u is not needed; the readout and update formulas are unchanged.
 //
+// States may live in a pool indexed by a per-sequence slot (continuous
+// batching: a serving engine keeps one fixed-size state per live request and
+// batches whichever requests are decoding; the Priming article lists
+// continuous batching among its serving plugin's features).  A slot outside
+// [0, pool_size) marks a padding entry: its output is zero, no state is touched.
+//
 // The step is bound by HBM bandwidth: every state byte is read once and
 // written once, ~0.25 FLOP per byte, so there is no MFMA here.  Layout of the
 // work: a wavefront owns a column slice of one (sequence, head) state stored
@@ -43,7 +49,7 @@ template <int DK, int DV, typename TIn, bool DELTA>
 __global__ __launch_bounds__(kWave * kWavesPerBlock) void decode_kernel(
     const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, float *__restrict__ state,
-    float *__restrict__ o, int items, float scale) {
+    float *__restrict__ o, int items, float scale, const int *__restrict__ slots, int H, int pool) {
     using S = DecodeShape<DK, DV>;
     const int lane = threadIdx.x % kWave;
     const int item = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
@@ -56,10 +62,21 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void decode_kernel(
     const int col = slice * S::WC + 4 * c;
     const int row0 = rg * S::ROWS;
 
+    size_t sh = nh;  // state index: (slot * H + h) when states live in a pool
+    if (slots) {
+        const int n = static_cast<int>(nh / H), h = static_cast<int>(nh % H);
+        const int slot = slots[n];  // the same for the whole wavefront
+        if (slot < 0 || slot >= pool) {
+            if (rg == 0) *reinterpret_cast<f32x4 *>(o + nh * DV + col) = f32x4{0.f, 0.f, 0.f, 0.f};
+            return;
+        }
+        sh = static_cast<size_t>(slot) * H + h;
+    }
+
     const float a = __expf(g[nh]);
     const float b = beta[nh];
 
-    float *st = state + nh * DK * DV;
+    float *st = state + sh * DK * DV;
     f32x4 s[S::ROWS];
 #pragma unroll
     for (int m = 0; m < S::ROWS; ++m)
@@ -109,7 +126,7 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void decode_kernel(
 template <int DK, int DV, typename TIn>
 hipError_t launch_decode_t(const void *q, const void *k, const void *v, const float *g,
                            const float *beta, float *state, float *o, int N, int H, bool delta,
-                           hipStream_t stream) {
+                           const int *slots, int pool, hipStream_t stream) {
     using S = DecodeShape<DK, DV>;
     const long long items = static_cast<long long>(N) * H * S::SLICES;
     const int blocks = static_cast<int>((items + kWavesPerBlock - 1) / kWavesPerBlock);
@@ -118,22 +135,22 @@ hipError_t launch_decode_t(const void *q, const void *k, const void *v, const fl
         hipLaunchKernelGGL((decode_kernel<DK, DV, TIn, true>), dim3(blocks), dim3(kWave * kWavesPerBlock),
                            0, stream, static_cast<const TIn *>(q), static_cast<const TIn *>(k),
                            static_cast<const TIn *>(v), g, beta, state, o, static_cast<int>(items),
-                           scale);
+                           scale, slots, H, pool);
     else
         hipLaunchKernelGGL((decode_kernel<DK, DV, TIn, false>), dim3(blocks), dim3(kWave * kWavesPerBlock),
                            0, stream, static_cast<const TIn *>(q), static_cast<const TIn *>(k),
                            static_cast<const TIn *>(v), g, beta, state, o, static_cast<int>(items),
-                           scale);
+                           scale, slots, H, pool);
     return hipGetLastError();
 }
 
 template <typename TIn>
 hipError_t dispatch_decode(const void *q, const void *k, const void *v, const float *g,
                            const float *beta, float *state, float *o, int N, int H, int dk,
-                           int dv, bool delta, hipStream_t s) {
+                           int dv, bool delta, const int *slots, int pool, hipStream_t s) {
 #define GDN_DEC(DK_, DV_)                                                                        \
     if (dk == DK_ && dv == DV_)                                                                  \
-        return launch_decode_t<DK_, DV_, TIn>(q, k, v, g, beta, state, o, N, H, delta, s);
+        return launch_decode_t<DK_, DV_, TIn>(q, k, v, g, beta, state, o, N, H, delta, slots, pool, s);
     GDN_DEC(16, 16) GDN_DEC(16, 64) GDN_DEC(16, 128)
     GDN_DEC(64, 16) GDN_DEC(64, 64) GDN_DEC(64, 128)
     GDN_DEC(128, 16) GDN_DEC(128, 64) GDN_DEC(128, 128)
@@ -145,10 +162,11 @@ hipError_t dispatch_decode(const void *q, const void *k, const void *v, const fl
 
 hipError_t launch_decode(const void *q, const void *k, const void *v, const float *g,
                          const float *beta, float *state, float *o, int N, int H, int dk, int dv,
-                         gdn_dtype dt, bool delta, hipStream_t stream) {
+                         gdn_dtype dt, bool delta, const int *slots, int pool, hipStream_t stream) {
     if (dt == GDN_BF16)
-        return dispatch_decode<uint16_t>(q, k, v, g, beta, state, o, N, H, dk, dv, delta, stream);
-    return dispatch_decode<float>(q, k, v, g, beta, state, o, N, H, dk, dv, delta, stream);
+        return dispatch_decode<uint16_t>(q, k, v, g, beta, state, o, N, H, dk, dv, delta, slots, pool,
+                                         stream);
+    return dispatch_decode<float>(q, k, v, g, beta, state, o, N, H, dk, dv, delta, slots, pool, stream);
 }
 
 }  // namespace gdn

@@ -38,9 +38,11 @@ template <> __device__ __forceinline__ float load_in<uint16_t>(const uint16_t *p
 // ---- launchers (host side; each returns the launch's hipError_t) ---------
 
 // `delta` selects the rule everywhere: true = gated delta rule, false = no erase term.
+// slots == NULL: sequence n uses state n; else state slots[n] of a pool of `pool` states
+// (slots outside [0, pool) are padding: zero output, no state touched).
 hipError_t launch_decode(const void *q, const void *k, const void *v, const float *g,
                          const float *beta, float *state, float *o, int N, int H, int dk, int dv,
-                         gdn_dtype dt, bool delta, hipStream_t stream);
+                         gdn_dtype dt, bool delta, const int *slots, int pool, hipStream_t stream);
 
 // Chunked prefill with fp32 VALU arithmetic (fp32 inputs, and bf16 inputs at
 // sizes the MFMA path does not tile).  Needs no workspace.

@@ -50,6 +50,7 @@
 #define GDN_H
 
 #include <stddef.h>
+#include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -173,6 +174,31 @@ GDN_API gdn_status gdn_decode_step_rule(gdn_rule rule,
                            const void *q, const void *k, const void *v,
                            const float *g, const float *beta,
                            float *state, float *o,
+                           int N, int H, int d_k, int d_v,
+                           gdn_dtype qkv_dtype, void *stream);
+
+/*
+ * gdn_decode_step_slots -- gdn_decode_step_rule with states kept in a pool
+ * (continuous batching: one fixed-size state per live request; the Priming
+ * article lists continuous batching among its serving plugin's features).
+ *
+ *   state_pool  [pool_size, H, d_k, d_v] fp32: sequence n reads and updates
+ *               state_pool[slots[n]] in place
+ *   slots       [N] int32, device memory.  A slot outside [0, pool_size)
+ *               marks a padding entry: o[n] is written as zeros and no state
+ *               is read or written.  Valid slots must be distinct (two
+ *               sequences updating one slot race).
+ * Other arguments as for gdn_decode_step.  Slot values are device data and
+ * are not validated on the host beyond the rule above.
+ * Errors: as gdn_decode_step_rule, plus GDN_ERR_NULL for slots == NULL
+ * (N > 0) and GDN_ERR_SHAPE for pool_size < 0; GDN_ERR_ALIAS also covers o
+ * or state_pool overlapping slots.
+ */
+GDN_API gdn_status gdn_decode_step_slots(gdn_rule rule,
+                           const void *q, const void *k, const void *v,
+                           const float *g, const float *beta,
+                           float *state_pool, const int32_t *slots, int pool_size,
+                           float *o,
                            int N, int H, int d_k, int d_v,
                            gdn_dtype qkv_dtype, void *stream);
 

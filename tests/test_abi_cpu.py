@@ -126,3 +126,22 @@ def test_rule_entry_points_validate_the_rule():
     assert dec(5) == UNSUP
     assert dec(gdn.GDN_RULE_GATED_DECAY, st=addr(2)) == ALIAS
     assert dec(gdn.GDN_RULE_GATED_DECAY, N=0, q=None) == OK
+
+
+def test_decode_slots_validation():
+    base = dict(q=addr(0), k=addr(1), v=addr(2), g=addr(3), beta=addr(4), pool=addr(5), slots=addr(6),
+                P=10, o=addr(7), N=4, H=2, dk=64, dv=64, dt=BF16, stream=None)
+
+    def call(rule=gdn.GDN_RULE_GATED_DELTA, **kw):
+        a = dict(base, **kw)
+        return gdn.gdn_decode_step_slots(rule, a["q"], a["k"], a["v"], a["g"], a["beta"], a["pool"],
+                                         a["slots"], a["P"], a["o"], a["N"], a["H"], a["dk"], a["dv"],
+                                         a["dt"], a["stream"])
+    assert call(slots=None) == NULL
+    assert call(pool=None) == NULL
+    assert call(P=-1) == SHAPE
+    assert call(rule=3) == UNSUP
+    assert call(slots=addr(6) + 4) == ALIGN
+    assert call(o=addr(6)) == ALIAS            # output over the slot table
+    assert call(pool=addr(6) - 1024) == ALIAS  # pool running into the slot table
+    assert call(N=0, slots=None, q=None) == OK

@@ -86,3 +86,39 @@ def test_decode_error_leaves_buffers_untouched():
     torch.cuda.synchronize()
     assert st == 5  # o aliases q
     assert torch.equal(state, before)
+
+
+@pytest.mark.parametrize("rule", [gdn.GDN_RULE_GATED_DELTA, gdn.GDN_RULE_GATED_DECAY])
+def test_decode_with_state_slots(orc, rule):
+    """States in a pool of 10 slots; six sequences use slots 3, 7, 0, 9 and two padding entries
+    (-1 and 12, out of range): valid slots follow the oracle, padding outputs are zero, every
+    other slot is left bit for bit as it was."""
+    import oracle
+    N, H, dk, dv, P = 6, 4, 64, 64, 10
+    slots = torch.tensor([3, 7, -1, 0, 12, 9], dtype=torch.int32, device=DEV)
+    pool = gi.decode_state(P, H, dk, dv, device=DEV)
+    pool0 = pool.clone()
+    ref = pool.cpu().double().numpy().copy()
+    orule = oracle.GATED_DELTA if rule == gdn.GDN_RULE_GATED_DELTA else oracle.GATED_DECAY
+    outs, refs = [], []
+    for s in range(3):
+        d = gi.decode_inputs(N, H, dk, dv, s, device=DEV)
+        outs.append(gdn.decode_step_slots(d["q"], d["k"], d["v"], d["g"], d["beta"], pool, slots,
+                                          rule=rule).cpu().numpy())
+        valid = [n for n, sl in enumerate(slots.tolist()) if 0 <= sl < P]
+        sel = [slots[n].item() for n in valid]
+        st = np.ascontiguousarray(ref[sel])
+        ro = orc.decode_step(d["q"][valid], d["k"][valid], d["v"][valid], d["g"][valid], d["beta"][valid],
+                             st, rule=orule)
+        ref[sel] = st
+        full = np.zeros((N, H, dv))
+        full[valid] = ro
+        refs.append(full)
+    torch.cuda.synchronize()
+    got = np.stack(outs)
+    assert np.all(got[:, [2, 4]] == 0.0), "padding entries must output zeros"
+    assert_parity(got[:, [0, 1, 3, 5]], np.stack(refs)[:, [0, 1, 3, 5]], TOL["bf16"], "slot decode outputs")
+    used = [3, 7, 0, 9]
+    assert_parity(pool.cpu().numpy()[used], ref[used], TOL["bf16"], "slot decode states")
+    untouched = [i for i in range(P) if i not in used]
+    assert torch.equal(pool[untouched], pool0[untouched]), "unused slots must not change"
