@@ -35,6 +35,7 @@ GDN_RULE_GATED_DELTA, GDN_RULE_GATED_DECAY = 0, 1
 STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_UNSUPPORTED",
           4: "GDN_ERR_ALIGN", 5: "GDN_ERR_ALIAS", 6: "GDN_ERR_WORKSPACE", 7: "GDN_ERR_HIP"}
 EXPORTS = ("gdn_chunk_prefill", "gdn_chunk_prefill_rule", "gdn_chunk_prefill_workspace_size",
+           "gdn_chunk_prefill_varlen", "gdn_chunk_prefill_varlen_workspace_size",
            "gdn_decode_step", "gdn_decode_step_rule", "gdn_decode_step_slots", "gdn_status_string",
            "gdn_version")
 
@@ -71,6 +72,11 @@ def lib():
         L.gdn_decode_step_slots.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32,
                                             i32, vp]
         L.gdn_decode_step_slots.restype = i32
+        L.gdn_chunk_prefill_varlen.argtypes = [i32, vp, vp, vp, vp, vp, vp, i32, i32, vp, i32, vp, vp, vp,
+                                               i32, i32, i32, i32, i32, vp, sz, vp]
+        L.gdn_chunk_prefill_varlen.restype = i32
+        L.gdn_chunk_prefill_varlen_workspace_size.argtypes = [vp, i32, i32, i32, i32, i32, i32]
+        L.gdn_chunk_prefill_varlen_workspace_size.restype = sz
         L.gdn_status_string.argtypes = [i32]
         L.gdn_status_string.restype = ctypes.c_char_p
         L.gdn_version.argtypes = []
@@ -110,6 +116,18 @@ def gdn_decode_step_slots(rule, q, k, v, g, beta, state_pool, slots, pool_size, 
                           qkv_dtype, stream) -> int:
     return lib().gdn_decode_step_slots(rule, q, k, v, g, beta, state_pool, slots, pool_size, o, N, H,
                                        d_k, d_v, qkv_dtype, stream)
+
+
+def gdn_chunk_prefill_varlen(rule, q, k, v, g, beta, cu_seqlens, S, T_total, state_pool, pool_size, slots,
+                             has_initial, o, H, d_k, d_v, chunk, qkv_dtype, workspace, workspace_bytes,
+                             stream) -> int:
+    return lib().gdn_chunk_prefill_varlen(rule, q, k, v, g, beta, cu_seqlens, S, T_total, state_pool,
+                                          pool_size, slots, has_initial, o, H, d_k, d_v, chunk, qkv_dtype,
+                                          workspace, workspace_bytes, stream)
+
+
+def gdn_chunk_prefill_varlen_workspace_size(cu_seqlens, S, H, d_k, d_v, chunk, qkv_dtype) -> int:
+    return lib().gdn_chunk_prefill_varlen_workspace_size(cu_seqlens, S, H, d_k, d_v, chunk, qkv_dtype)
 
 
 def gdn_status_string(status: int) -> str:
@@ -238,8 +256,70 @@ def decode_step_slots(q, k, v, g, beta, state_pool, slots, *, out=None, stream=N
     return out
 
 
+def _host_i32(x):
+    """A host int32 array (numpy) from a list, numpy array or CPU tensor, or None."""
+    import numpy as np
+    if x is None:
+        return None
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            if x.device.type != "cpu":
+                raise TypeError("cu_seqlens, slots and has_initial are host arrays")
+            x = x.numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+
+
+def _np_ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def varlen_workspace_bytes(cu_seqlens, H, d_k, d_v, chunk, qkv_dtype) -> int:
+    cu = _host_i32(cu_seqlens)
+    return int(gdn_chunk_prefill_varlen_workspace_size(_np_ptr(cu), len(cu) - 1, H, d_k, d_v, chunk,
+                                                       qkv_dtype))
+
+
+def chunk_prefill_varlen(q, k, v, g, beta, cu_seqlens, state_pool, slots=None, has_initial=None, chunk=64,
+                         *, out=None, workspace=None, stream=None, rule=GDN_RULE_GATED_DELTA):
+    """Packed sequences: q, k [T,H,d_k]; v [T,H,d_v] bf16; g, beta [T,H] fp32; cu_seqlens host int32
+    [S+1]; state_pool [P,H,d_k,d_v] fp32 (sequence s starts from and ends in slot slots[s], slot s when
+    slots is None; -1 = from zeros, final state dropped); has_initial host [S] (0 = start from zeros).
+    Returns o fp32 [T,H,d_v]; final states are written into the pool."""
+    import torch
+    T, H, d_k = q.shape
+    d_v = v.shape[-1]
+    dt = _dtype_code(q)
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, q.dtype)
+    _check(g, "g", torch.float32)
+    _check(beta, "beta", torch.float32)
+    _check(state_pool, "state_pool", torch.float32)
+    cu, sl, hi = _host_i32(cu_seqlens), _host_i32(slots), _host_i32(has_initial)
+    S = len(cu) - 1
+    if out is None:
+        out = torch.empty((T, H, d_v), device=q.device, dtype=torch.float32)
+    _check(out, "out", torch.float32)
+    need = int(gdn_chunk_prefill_varlen_workspace_size(_np_ptr(cu), S, H, d_k, d_v, chunk, dt))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    pool_size = 0 if state_pool is None else state_pool.shape[0]
+    st = gdn_chunk_prefill_varlen(rule, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _np_ptr(cu), S, T,
+                                  _ptr(state_pool), pool_size, _np_ptr(sl), _np_ptr(hi), _ptr(out), H, d_k, d_v,
+                                  chunk, dt, _ptr(workspace), ws_bytes, stream)
+    if st != 0:
+        raise GdnError(st, "gdn_chunk_prefill_varlen")
+    return out
+
+
 __all__ = ["EXPORTS", "GDN_F32", "GDN_BF16", "GDN_RULE_GATED_DELTA", "GDN_RULE_GATED_DECAY", "GdnError",
            "lib", "gdn_chunk_prefill", "gdn_chunk_prefill_rule", "gdn_chunk_prefill_workspace_size",
            "gdn_decode_step", "gdn_decode_step_rule", "gdn_status_string", "gdn_version",
-           "gdn_decode_step_slots", "chunk_prefill", "decode_step", "decode_step_slots",
-           "workspace_bytes"]
+           "gdn_decode_step_slots", "gdn_chunk_prefill_varlen", "gdn_chunk_prefill_varlen_workspace_size",
+           "chunk_prefill", "chunk_prefill_varlen", "decode_step", "decode_step_slots", "workspace_bytes",
+           "varlen_workspace_bytes"]

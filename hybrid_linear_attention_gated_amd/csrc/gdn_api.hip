@@ -6,6 +6,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <vector>
+
 #include "gdn_internal.h"
 
 namespace gdn {
@@ -160,6 +162,93 @@ gdn_status gdn_chunk_prefill(const void *q, const void *k, const void *v, const 
     return gdn_chunk_prefill_rule(GDN_RULE_GATED_DELTA, q, k, v, g, beta, initial_state, o,
                                   final_state, B, T, H, d_k, d_v, chunk, qkv_dtype, workspace,
                                   workspace_bytes, stream);
+}
+
+namespace {
+
+// Host checks of a packed batch: offsets from 0 to T_total, never decreasing; slots in
+// [-1, pool) and the valid ones distinct.  Returns GDN_OK or the error to report.
+gdn_status check_varlen_batch(const int32_t *cu, int S, int T_total, const int32_t *slots, int pool) {
+    if (S < 0 || T_total < 0 || pool < 0) return GDN_ERR_SHAPE;
+    if (S == 0) return T_total == 0 ? GDN_OK : GDN_ERR_SHAPE;
+    if (!cu) return GDN_ERR_NULL;
+    if (cu[0] != 0 || cu[S] != T_total) return GDN_ERR_SHAPE;
+    for (int s = 0; s < S; ++s)
+        if (cu[s + 1] < cu[s]) return GDN_ERR_SHAPE;
+    if (!slots) return pool >= S ? GDN_OK : GDN_ERR_SHAPE;
+    std::vector<unsigned char> used(static_cast<size_t>(pool), 0);
+    for (int s = 0; s < S; ++s) {
+        const int32_t sl = slots[s];
+        if (sl < -1 || sl >= pool) return GDN_ERR_SHAPE;
+        if (sl >= 0) {
+            if (used[sl]) return GDN_ERR_ALIAS;  // two sequences would write one state
+            used[sl] = 1;
+        }
+    }
+    return GDN_OK;
+}
+
+bool varlen_supported(int d_k, int d_v, int chunk, gdn_dtype dt) {
+    return dt == GDN_BF16 && prefill_bf16_uses_mfma(d_k, d_v, chunk);
+}
+
+}  // namespace
+
+size_t gdn_chunk_prefill_varlen_workspace_size(const int32_t *cu_seqlens, int S, int H, int d_k, int d_v,
+                                               int chunk, gdn_dtype qkv_dtype) {
+    if (S <= 0 || H <= 0 || !cu_seqlens || !varlen_supported(d_k, d_v, chunk, qkv_dtype)) return 0;
+    if (check_varlen_batch(cu_seqlens, S, cu_seqlens[S], nullptr, S) != GDN_OK) return 0;
+    VarlenLayout L;
+    if (!varlen_layout(cu_seqlens, S, H, d_k, d_v, chunk, &L)) return 0;
+    return L.bytes;
+}
+
+gdn_status gdn_chunk_prefill_varlen(gdn_rule rule, const void *q, const void *k, const void *v,
+                                    const float *g, const float *beta, const int32_t *cu_seqlens, int S,
+                                    int T_total, float *state_pool, int pool_size, const int32_t *slots,
+                                    const int32_t *has_initial, float *o, int H, int d_k, int d_v,
+                                    int chunk, gdn_dtype qkv_dtype, void *workspace,
+                                    size_t workspace_bytes, void *stream) {
+    if (rule != GDN_RULE_GATED_DELTA && rule != GDN_RULE_GATED_DECAY) return GDN_ERR_UNSUPPORTED;
+    if (H <= 0 || d_k <= 0 || d_v <= 0 || chunk <= 0) return GDN_ERR_SHAPE;
+    if (!varlen_supported(d_k, d_v, chunk, qkv_dtype)) return GDN_ERR_UNSUPPORTED;
+    gdn_status st = check_varlen_batch(cu_seqlens, S, T_total, slots, pool_size);
+    if (st != GDN_OK) return st;
+    if (prod({T_total, H, d_k > d_v ? d_k : d_v}) == SIZE_MAX || prod({pool_size, H, d_k, d_v}) == SIZE_MAX)
+        return GDN_ERR_SHAPE;
+    if (S == 0) return GDN_OK;
+    if (T_total > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL;
+    bool any_slot = !slots;
+    for (int s = 0; slots && s < S; ++s) any_slot = any_slot || slots[s] >= 0;
+    if (any_slot && !state_pool) return GDN_ERR_NULL;
+    const void *ptrs[] = {q, k, v, g, beta, state_pool, o, workspace};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return GDN_ERR_ALIGN;
+
+    const size_t es = elem_bytes(qkv_dtype);
+    const Span s_q = span(q, prod({T_total, H, d_k}) * es), s_k = span(k, prod({T_total, H, d_k}) * es);
+    const Span s_v = span(v, prod({T_total, H, d_v}) * es);
+    const Span s_g = span(g, prod({T_total, H}) * 4), s_b = span(beta, prod({T_total, H}) * 4);
+    const Span s_o = span(o, prod({T_total, H, d_v}) * 4);
+    const Span s_p = state_pool ? span(state_pool, prod({pool_size, H, d_k, d_v}) * 4) : Span{0, 0};
+    const Span inputs[] = {s_q, s_k, s_v, s_g, s_b};
+    for (const Span &in : inputs)
+        if (overlap(s_o, in) || overlap(s_p, in)) return GDN_ERR_ALIAS;
+    if (overlap(s_o, s_p)) return GDN_ERR_ALIAS;
+
+    VarlenLayout L;
+    if (!varlen_layout(cu_seqlens, S, H, d_k, d_v, chunk, &L)) return GDN_ERR_SHAPE;
+    if (!workspace || workspace_bytes < L.bytes) return GDN_ERR_WORKSPACE;
+    const Span s_ws = span(workspace, L.bytes);
+    const Span all[] = {s_q, s_k, s_v, s_g, s_b, s_o, s_p};
+    for (const Span &x : all)
+        if (overlap(s_ws, x)) return GDN_ERR_ALIAS;
+
+    const hipError_t err = launch_prefill_chunk_varlen(
+        static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k), static_cast<const uint16_t *>(v), g,
+        beta, cu_seqlens, S, slots, has_initial, state_pool, o, H, d_k, d_v, chunk,
+        rule == GDN_RULE_GATED_DELTA, workspace, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
 namespace {

@@ -66,6 +66,21 @@ hipError_t launch_prefill_chunk(const uint16_t *q, const uint16_t *k, const uint
                                 bool delta, void *ws, hipStream_t stream);
 size_t prefill_chunk_workspace(int B, int T, int H, int dk, int dv, int chunk);
 
+// Packed variable-length sequences (bf16, MFMA shapes).  cu, slots and init are host
+// arrays (cu[S + 1] token offsets; slots[S] pool slots, NULL = slot s, -1 = none;
+// init[S] start-from-stored-state flags, NULL = all).  The workspace holds a table
+// built from them, the piece maps and the piece start states.
+struct VarlenLayout {
+    int pc, NP, NM, chunk;   // chunks per piece, global pieces, global maps, chunk size
+    size_t table_ints, maps_off, starts_off, bytes;
+};
+bool varlen_layout(const int *cu, int S, int H, int dk, int dv, int chunk, VarlenLayout *L);
+hipError_t launch_prefill_chunk_varlen(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                       const float *g, const float *beta, const int *cu, int S,
+                                       const int *slots, const int *init, float *pool, float *o,
+                                       int H, int dk, int dv, int chunk, bool delta, void *ws,
+                                       hipStream_t stream);
+
 // Copies (or zero-fills, when s0 == NULL) a start state into s_out.
 hipError_t launch_state_copy(const float *s0, float *s_out, size_t n, hipStream_t stream);
 

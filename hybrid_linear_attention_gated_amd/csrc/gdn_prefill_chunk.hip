@@ -37,10 +37,16 @@
 // Q St, P and Delta in P Delta, the decayed Delta in the state update and
 // both factors of the inversion's block products are hi + lo bf16 pairs.
 #include <type_traits>
+#include <vector>
 
 #include "gdn_mfma.h"
 
 namespace gdn {
+
+#define GDN_CHUNK_CASES(X) \
+    X(64, 64, 32) X(64, 64, 64) X(64, 128, 32) X(64, 128, 64) \
+    X(128, 64, 32) X(128, 64, 64) X(128, 128, 32) X(128, 128, 64)
+
 namespace {
 
 constexpr int kWave = 64;
@@ -133,15 +139,29 @@ struct Cfg {
     static constexpr int MAPW = DV + DK;  // row length of a stored piece map
 };
 
+// Packed variable-length sequences: a table built on the host and copied to the
+// device.  Global piece gp (all sequences' pieces in order) belongs to sequence
+// piece_seq[gp], global map gm (every piece but a sequence's last) to map_seq[gm];
+// per sequence: first token, length, first global piece, first global map, state
+// slot in the pool (-1: start from zeros, final state dropped) and whether to start
+// from the slot's stored state.
+struct SeqTable {
+    const int *piece_seq, *map_seq;
+    const int *tok0, *len, *pstart, *mstart, *slot, *init;
+};
+
 struct ChunkArgs {
     const uint16_t *q, *k, *v;
     const float *g, *beta;
-    const float *s_start;  // OUT: start states, (bh * P + piece) * DK * DV; NULL = zeros
+    const float *s_start;  // OUT: start states, dense (bh * P + piece) or packed (gp * H + h) * DK * DV; NULL = zeros
     float *o;              // OUT: outputs
-    float *s_final;        // OUT: final states [BH][DK][DV], written by the last piece
-    float *maps;           // MAP: [BH][P - 1][DK][DV + DK]
+    float *s_final;        // OUT, dense: final states [BH][DK][DV], written by the last piece
+    float *maps;           // MAP: dense [BH][P - 1] or packed [gm][H], each [DK][DV + DK]
     int T, H, BH, P, piece_chunks, N;
     float scale;
+    SeqTable sq;           // packed sequences when sq.tok0 != NULL (then work items = pieces * H)
+    float *pool;           // packed: state pool [slot][H][DK][DV] receiving final states
+    int items;             // work items of this launch
 };
 
 // Eight bf16 to an 8-byte aligned LDS address (padded rows are not 16-byte aligned).
@@ -180,15 +200,15 @@ __device__ __forceinline__ float buf_load4(__amdgpu_buffer_rsrc_t r, unsigned by
 }
 
 template <int DK, int DV, int C, bool MAP>
-__device__ __forceinline__ void load_chunk(ChunkRegs<DK, DV, C, MAP> &r, const ChunkArgs &a, int b,
-                                           int h, int n, int tid) {
+__device__ __forceinline__ void load_chunk(ChunkRegs<DK, DV, C, MAP> &r, const ChunkArgs &a, size_t tok_base,
+                                           int seq_len, int h, int n, int tid) {
     using R = ChunkRegs<DK, DV, C, MAP>;
     // the lane offsets below are cheap to rebuild per chunk; hoisted out of the chunk loop
     // they would hold a dozen registers for its whole length
     __asm__ __volatile__("" : "+v"(tid));
     const int t0 = n * C;
-    const int L = min(C, a.T - t0);  // >= 1
-    const size_t row0 = (static_cast<size_t>(b) * a.T + t0) * a.H + h;  // token-head row of t0
+    const int L = min(C, seq_len - t0);  // >= 1
+    const size_t row0 = (tok_base + t0) * a.H + h;  // token-head row of t0
     const unsigned rows_k = static_cast<unsigned>((L - 1) * a.H * DK + DK) * 2u;
     const unsigned rows_v = static_cast<unsigned>((L - 1) * a.H * DV + DV) * 2u;
     const auto rk = chunk_rsrc(a.k + row0 * DK, rows_k);
@@ -261,15 +281,45 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
     // so consecutive work items (one piece, consecutive heads: they share every g and beta
     // cache line) are given to indices that land on the same XCD and its L2.  The grid is a
     // multiple of 8; surplus workgroups leave at once.
-    const int pieces = MAP ? a.P - 1 : a.P;
     const int per_xcd = gridDim.x / kXcds;
     const int w = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-    if (w >= a.BH * pieces) return;
-    const int piece = w / a.BH;
-    const size_t bh = w % a.BH;
-    const int b = static_cast<int>(bh / a.H), h = static_cast<int>(bh % a.H);
-    const int n0 = piece * a.piece_chunks;
-    const int n1 = min(n0 + a.piece_chunks, a.N);
+    if (w >= a.items) return;
+    // this work item: one head of one piece of one sequence
+    int h, n0, n1, seq_len;
+    size_t tok_base;                  // first token of the sequence in the [tokens, H, d] layout
+    const float *start = nullptr;     // OUT: start state [DK][DV] (NULL = zeros)
+    float *map_out = nullptr;         // MAP: piece map [DK][DV + DK]
+    float *final_out = nullptr;       // OUT: final state [DK][DV] of the sequence's last piece
+    if (a.sq.tok0 == nullptr) {
+        const int piece = w / a.BH;
+        const size_t bh = w % a.BH;
+        const int b = static_cast<int>(bh / a.H);
+        h = static_cast<int>(bh % a.H);
+        tok_base = static_cast<size_t>(b) * a.T;
+        seq_len = a.T;
+        n0 = piece * a.piece_chunks;
+        n1 = min(n0 + a.piece_chunks, a.N);
+        if (MAP) map_out = a.maps + (bh * (a.P - 1) + piece) * DK * G::MAPW;
+        else if (a.s_start) start = a.s_start + (bh * a.P + piece) * DK * DV;
+        if (!MAP && piece == a.P - 1) final_out = a.s_final + bh * DK * DV;
+    } else {
+        const int gp = w / a.H;  // global piece (OUT) or global map (MAP)
+        h = w % a.H;
+        const int s = MAP ? a.sq.map_seq[gp] : a.sq.piece_seq[gp];
+        const int piece = gp - (MAP ? a.sq.mstart[s] : a.sq.pstart[s]);
+        tok_base = static_cast<size_t>(a.sq.tok0[s]);
+        seq_len = a.sq.len[s];
+        const int nchunks = (seq_len + C - 1) / C;
+        n0 = piece * a.piece_chunks;
+        n1 = min(n0 + a.piece_chunks, nchunks);
+        if (MAP) {
+            map_out = a.maps + (static_cast<size_t>(gp) * a.H + h) * DK * G::MAPW;
+        } else {
+            start = a.s_start + (static_cast<size_t>(gp) * a.H + h) * DK * DV;
+            const int slot = a.sq.slot[s];
+            if (n1 == nchunks && slot >= 0) final_out = a.pool + (static_cast<size_t>(slot) * a.H + h) * DK * DV;
+        }
+    }
 
     // ---- carried state: St[j][mt] holds rows 16 mt + 4 gq + r, column 16 sl + li, sl = wave + 4 j
     f32x4 St[G::SPW][G::KT];
@@ -284,8 +334,8 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
                 float x = 0.f;
                 if (MAP) {
                     if (sl >= G::VT) x = (row == 16 * (sl - G::VT) + li) ? 1.f : 0.f;
-                } else if (a.s_start) {
-                    x = a.s_start[((bh * a.P + piece) * DK + row) * DV + 16 * sl + li];
+                } else if (start) {
+                    x = start[row * DV + 16 * sl + li];
                 }
                 St[j][mt][r] = x;
             }
@@ -322,11 +372,11 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
     R cur;
-    if (n0 < n1) load_chunk<DK, DV, C, MAP>(cur, a, b, h, n0, tid);
+    if (n0 < n1) load_chunk<DK, DV, C, MAP>(cur, a, tok_base, seq_len, h, n0, tid);
 
     for (int n = n0; n < n1; ++n) {
         const int t0 = n * C;
-        const int L = min(C, a.T - t0);
+        const int L = min(C, seq_len - t0);
 
         // ---- A: this chunk's rows into LDS (K both row-major and transposed); gates
 #pragma unroll
@@ -690,7 +740,7 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
         }
 
         // next chunk's rows: loads in flight during this chunk's slice work
-        if (n + 1 < n1) load_chunk<DK, DV, C, MAP>(cur, a, b, h, n + 1, tid);
+        if (n + 1 < n1) load_chunk<DK, DV, C, MAP>(cur, a, tok_base, seq_len, h, n + 1, tid);
 
         // ---- G: per slice: U = (T diag b) V, Delta = U - W St, outputs, state update
 #pragma unroll
@@ -776,7 +826,7 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
                 }
                 // O^T tiles: with the operands swapped, lane (gq, li) holds O[16 mt + li][16 sl + 4 gq + r]
                 // for r = 0..3, i.e. four consecutive columns of one row -- one 16-byte store
-                float *obase = a.o + ((static_cast<size_t>(b) * a.T + t0) * a.H + h) * DV;  // uniform
+                float *obase = a.o + ((tok_base + t0) * a.H + h) * DV;  // uniform
 #pragma unroll
                 for (int mt = 0; mt < G::CT; ++mt) {
                     f32x4 qsa = zero4, pd = zero4;
@@ -841,9 +891,9 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
             for (int r = 0; r < 4; ++r) {
                 const int row = 16 * mt + 4 * gq + r;
                 if (MAP)
-                    a.maps[((bh * (a.P - 1) + piece) * DK + row) * G::MAPW + 16 * sl + li] = St[j][mt][r];
-                else if (piece == a.P - 1)
-                    a.s_final[(bh * DK + row) * DV + 16 * sl + li] = St[j][mt][r];
+                    map_out[row * G::MAPW + 16 * sl + li] = St[j][mt][r];
+                else if (final_out)
+                    final_out[row * DV + 16 * sl + li] = St[j][mt][r];
             }
     }
 }
@@ -902,6 +952,38 @@ __device__ __forceinline__ void chain_step(f32x4 (&St)[DK / 16], const ChainMap<
     }
 }
 
+// The serial part shared by both layouts: start states of P pieces from St (the first
+// piece's), St <- M_p St + N_p.  map_at(p) points at piece p's map [DK][DV + DK];
+// store_at(St, p) records piece p's start state.
+template <int DK, int DV, typename MapAt, typename StoreAt>
+__device__ __forceinline__ void chain_run(f32x4 (&St)[DK / 16], int P, MapAt map_at, StoreAt store_at,
+                                          int gq, int li, int col) {
+    if constexpr (DK == 64) {
+        // two map buffers used in turn, so piece p + 1's loads overlap piece p's product
+        ChainMap<DK, DV> ma, mb;
+        if (P > 1) chain_load<DK, DV>(ma, map_at(0), gq, li, col);
+        for (int p = 0; p < P; p += 2) {
+            store_at(St, p);
+            if (p + 1 >= P) break;
+            if (p + 1 < P - 1) chain_load<DK, DV>(mb, map_at(p + 1), gq, li, col);
+            chain_step<DK, DV>(St, ma);
+            store_at(St, p + 1);
+            if (p + 2 >= P) break;
+            if (p + 2 < P - 1) chain_load<DK, DV>(ma, map_at(p + 2), gq, li, col);
+            chain_step<DK, DV>(St, mb);
+        }
+    } else {
+        // 128-wide maps would not fit twice in registers: load each in place
+        for (int p = 0; p < P; ++p) {
+            store_at(St, p);
+            if (p == P - 1) break;
+            ChainMap<DK, DV> mc;
+            chain_load<DK, DV>(mc, map_at(p), gq, li, col);
+            chain_step<DK, DV>(St, mc);
+        }
+    }
+}
+
 template <int DK, int DV>
 __global__ __launch_bounds__(kWave) void chain_kernel(const float *__restrict__ maps,
                                                       const float *__restrict__ s0,
@@ -912,14 +994,6 @@ __global__ __launch_bounds__(kWave) void chain_kernel(const float *__restrict__ 
     const size_t bh = blockIdx.x / VT;
     const int col = 16 * sl + li;
     const float *mbase = maps + bh * (P - 1) * DK * MAPW;
-    auto piece_map = [&](int p) { return mbase + static_cast<size_t>(p) * DK * MAPW; };
-    auto store_start = [&](const f32x4 (&St)[KT], int p) {
-#pragma unroll
-        for (int mt = 0; mt < KT; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                starts[((bh * P + p) * DK + 16 * mt + 4 * gq + r) * DV + col] = St[mt][r];
-    };
     f32x4 St[KT];
     if (s0) {
 #pragma unroll
@@ -930,30 +1004,65 @@ __global__ __launch_bounds__(kWave) void chain_kernel(const float *__restrict__ 
 #pragma unroll
         for (int mt = 0; mt < KT; ++mt) St[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    if constexpr (DK == 64) {
-        // two map buffers used in turn, so piece p + 1's loads overlap piece p's product
-        ChainMap<DK, DV> ma, mb;
-        if (P > 1) chain_load<DK, DV>(ma, piece_map(0), gq, li, col);
-        for (int p = 0; p < P; p += 2) {
-            store_start(St, p);
-            if (p + 1 >= P) break;
-            if (p + 1 < P - 1) chain_load<DK, DV>(mb, piece_map(p + 1), gq, li, col);
-            chain_step<DK, DV>(St, ma);
-            store_start(St, p + 1);
-            if (p + 2 >= P) break;
-            if (p + 2 < P - 1) chain_load<DK, DV>(ma, piece_map(p + 2), gq, li, col);
-            chain_step<DK, DV>(St, mb);
-        }
+    chain_run<DK, DV>(
+        St, P, [&](int p) { return mbase + static_cast<size_t>(p) * DK * MAPW; },
+        [&](const f32x4 (&S)[KT], int p) {
+#pragma unroll
+            for (int mt = 0; mt < KT; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    starts[((bh * P + p) * DK + 16 * mt + 4 * gq + r) * DV + col] = S[mt][r];
+        },
+        gq, li, col);
+}
+
+// Packed sequences: one wavefront per (sequence, head, 16 value columns).  The first
+// piece starts from the sequence's pool slot (or zeros); an empty sequence that is to
+// start from zeros gets a zero final state in its slot.
+template <int DK, int DV>
+__global__ __launch_bounds__(kWave) void chain_varlen_kernel(SeqTable sq, const float *__restrict__ maps,
+                                                             float *__restrict__ starts,
+                                                             float *__restrict__ pool, int H) {
+    constexpr int KT = DK / 16, VT = DV / 16, MAPW = DV + DK;
+    const int lane = threadIdx.x, gq = lane / 16, li = lane % 16;
+    const int sl = blockIdx.x % VT;
+    const int h = (blockIdx.x / VT) % H;
+    const int s = blockIdx.x / (VT * H);
+    const int col = 16 * sl + li;
+    const int P = sq.pstart[s + 1] - sq.pstart[s];
+    const int slot = sq.slot[s];
+    float *st = slot >= 0 ? pool + (static_cast<size_t>(slot) * H + h) * DK * DV : nullptr;
+    f32x4 St[KT];
+    if (st && sq.init[s]) {
+#pragma unroll
+        for (int mt = 0; mt < KT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) St[mt][r] = st[(16 * mt + 4 * gq + r) * DV + col];
     } else {
-        // 128-wide maps would not fit twice in registers: load each in place
-        for (int p = 0; p < P; ++p) {
-            store_start(St, p);
-            if (p == P - 1) break;
-            ChainMap<DK, DV> mc;
-            chain_load<DK, DV>(mc, piece_map(p), gq, li, col);
-            chain_step<DK, DV>(St, mc);
-        }
+#pragma unroll
+        for (int mt = 0; mt < KT; ++mt) St[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    if (P == 0) {
+        if (st && !sq.init[s]) {
+#pragma unroll
+            for (int mt = 0; mt < KT; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) st[(16 * mt + 4 * gq + r) * DV + col] = 0.f;
+        }
+        return;
+    }
+    const int p0 = sq.pstart[s], m0 = sq.mstart[s];
+    chain_run<DK, DV>(
+        St, P, [&](int p) { return maps + (static_cast<size_t>(m0 + p) * H + h) * DK * MAPW; },
+        [&](const f32x4 (&S)[KT], int p) {
+#pragma unroll
+            for (int mt = 0; mt < KT; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    starts[((static_cast<size_t>(p0 + p) * H + h) * DK + 16 * mt + 4 * gq + r) * DV + col] =
+                        S[mt][r];
+        },
+        gq, li, col);
 }
 
 // Piece plan: enough workgroups to fill the chip twice over, at least eight
@@ -990,11 +1099,13 @@ hipError_t run_chunk(const uint16_t *q, const uint16_t *k, const uint16_t *v, co
     ChunkArgs a{};
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.o = o; a.s_final = s_out;
     a.T = T; a.H = H; a.BH = BH; a.P = P; a.N = N;
+    a.sq = SeqTable{};
     auto grid = [](int items) { return dim3((items + kXcds - 1) / kXcds * kXcds); };
     a.piece_chunks = plan.piece_chunks;
     a.scale = 1.0f / sqrtf(static_cast<float>(DK));
     if (P == 1) {
         a.s_start = s0;
+        a.items = BH;
         hipLaunchKernelGGL((chunk_kernel<DK, DV, C, false, DELTA>), grid(BH), dim3(kBlock), 0, stream, a);
         return hipGetLastError();
     }
@@ -1003,6 +1114,7 @@ hipError_t run_chunk(const uint16_t *q, const uint16_t *k, const uint16_t *v, co
     float *starts = reinterpret_cast<float *>(static_cast<char *>(ws) +
                                               ((maps_bytes + 255) & ~static_cast<size_t>(255)));
     a.maps = maps;
+    a.items = BH * (P - 1);
     hipLaunchKernelGGL((chunk_kernel<DK, DV, C, true, DELTA>), grid(BH * (P - 1)), dim3(kBlock), 0, stream, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
@@ -1011,15 +1123,126 @@ hipError_t run_chunk(const uint16_t *q, const uint16_t *k, const uint16_t *v, co
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     a.s_start = starts;
+    a.items = BH * P;
     hipLaunchKernelGGL((chunk_kernel<DK, DV, C, false, DELTA>), grid(BH * P), dim3(kBlock), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int DK, int DV, int C, bool DELTA>
+hipError_t run_chunk_varlen(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,
+                            const float *beta, const VarlenLayout &L, const int *table_dev, float *pool,
+                            float *o, int S, int H, void *ws, hipStream_t stream) {
+    const int *t = table_dev;
+    SeqTable sq;
+    sq.piece_seq = t;
+    sq.map_seq = t + L.NP;
+    sq.tok0 = t + L.NP + L.NM;
+    sq.len = sq.tok0 + S;
+    sq.pstart = sq.len + S;
+    sq.mstart = sq.pstart + S + 1;
+    sq.slot = sq.mstart + S + 1;
+    sq.init = sq.slot + S;
+    float *maps = reinterpret_cast<float *>(static_cast<char *>(ws) + L.maps_off);
+    float *starts = reinterpret_cast<float *>(static_cast<char *>(ws) + L.starts_off);
+    ChunkArgs a{};
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.o = o;
+    a.H = H; a.piece_chunks = L.pc;
+    a.scale = 1.0f / sqrtf(static_cast<float>(DK));
+    a.sq = sq;
+    a.pool = pool;
+    auto grid = [](int items) { return dim3((items + kXcds - 1) / kXcds * kXcds); };
+    if (L.NM > 0) {
+        a.maps = maps;
+        a.items = L.NM * H;
+        hipLaunchKernelGGL((chunk_kernel<DK, DV, C, true, DELTA>), grid(a.items), dim3(kBlock), 0, stream, a);
+        const hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    hipLaunchKernelGGL((chain_varlen_kernel<DK, DV>), dim3(S * H * (DV / 16)), dim3(kWave), 0, stream, sq,
+                       static_cast<const float *>(maps), starts, pool, H);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || L.NP == 0) return err;
+    a.s_start = starts;
+    a.items = L.NP * H;
+    hipLaunchKernelGGL((chunk_kernel<DK, DV, C, false, DELTA>), grid(a.items), dim3(kBlock), 0, stream, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
-#define GDN_CHUNK_CASES(X) \
-    X(64, 64, 32) X(64, 64, 64) X(64, 128, 32) X(64, 128, 64) \
-    X(128, 64, 32) X(128, 64, 64) X(128, 128, 32) X(128, 128, 64)
+// Plan for packed sequences: pieces of pc chunks (at least 8, and enough to give about
+// two workgroups per compute unit over all heads), the host table and the workspace layout.
+bool varlen_layout(const int *cu, int S, int H, int dk, int dv, int chunk, VarlenLayout *L) {
+    long long chunk_heads = 0;
+    for (int s = 0; s < S; ++s) chunk_heads += static_cast<long long>((cu[s + 1] - cu[s] + chunk - 1) / chunk) * H;
+    long long pc = (chunk_heads + 511) / 512;
+    if (pc < 8) pc = 8;
+    long long NP = 0, NM = 0;
+    for (int s = 0; s < S; ++s) {
+        const long long n = (cu[s + 1] - cu[s] + chunk - 1) / chunk;
+        const long long P = (n + pc - 1) / pc;
+        NP += P;
+        NM += P > 1 ? P - 1 : 0;
+    }
+    if (NP * H > 0x7fffffffLL || static_cast<long long>(S) * H * (dv / 16) > 0x7fffffffLL) return false;
+    L->chunk = chunk;
+    L->pc = static_cast<int>(pc);
+    L->NP = static_cast<int>(NP);
+    L->NM = static_cast<int>(NM);
+    L->table_ints = static_cast<size_t>(NP + NM) + 6 * static_cast<size_t>(S) + 2;
+    auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+    L->maps_off = up(L->table_ints * 4);
+    L->starts_off = L->maps_off + up(static_cast<size_t>(NM) * H * dk * (dv + dk) * 4);
+    L->bytes = L->starts_off + static_cast<size_t>(NP) * H * dk * dv * 4;
+    return true;
+}
+
+void varlen_table(const int *cu, int S, const int *slots, const int *init, const VarlenLayout &L, int *t) {
+    int *piece_seq = t, *map_seq = t + L.NP, *tok0 = t + L.NP + L.NM, *len = tok0 + S;
+    int *pstart = len + S, *mstart = pstart + S + 1, *slot = mstart + S + 1, *ini = slot + S;
+    int gp = 0, gm = 0;
+    for (int s = 0; s < S; ++s) {
+        const int n = cu[s + 1] - cu[s];  // tokens
+        tok0[s] = cu[s];
+        len[s] = n;
+        pstart[s] = gp;
+        mstart[s] = gm;
+        slot[s] = slots ? slots[s] : s;
+        ini[s] = init ? (init[s] != 0) : 1;
+        const int nchunks = (n + L.chunk - 1) / L.chunk;
+        const int P = (nchunks + L.pc - 1) / L.pc;
+        for (int p = 0; p < P; ++p) piece_seq[gp++] = s;
+        for (int p = 0; p + 1 < P; ++p) map_seq[gm++] = s;
+    }
+    pstart[S] = gp;
+    mstart[S] = gm;
+}
+
+hipError_t launch_prefill_chunk_varlen(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                       const float *g, const float *beta, const int *cu, int S,
+                                       const int *slots, const int *init, float *pool, float *o,
+                                       int H, int dk, int dv, int chunk, bool delta, void *ws,
+                                       hipStream_t stream) {
+    VarlenLayout L;
+    if (!varlen_layout(cu, S, H, dk, dv, chunk, &L)) return hipErrorInvalidValue;
+    std::vector<int> table(L.table_ints);
+    varlen_table(cu, S, slots, init, L, table.data());
+    // the table is pageable host memory: the copy has read it by the time the call returns
+    hipError_t err = hipMemcpyAsync(ws, table.data(), L.table_ints * 4, hipMemcpyHostToDevice, stream);
+    if (err != hipSuccess) return err;
+    const int *tdev = static_cast<const int *>(ws);
+#define GDN_RUNV(DK_, DV_, C_)                                                                           \
+    if (dk == DK_ && dv == DV_ && chunk == C_)                                                           \
+        return delta ? run_chunk_varlen<DK_, DV_, C_, true>(q, k, v, g, beta, L, tdev, pool, o, S, H, ws, stream) \
+                     : run_chunk_varlen<DK_, DV_, C_, false>(q, k, v, g, beta, L, tdev, pool, o, S, H, ws, stream);
+    GDN_CHUNK_CASES(GDN_RUNV)
+#undef GDN_RUNV
+    return hipErrorInvalidValue;
+}
+
+namespace {
+}  // namespace
+
 
 size_t prefill_chunk_workspace(int B, int T, int H, int dk, int dv, int chunk) {
 #define GDN_WS(DK_, DV_, C_) \

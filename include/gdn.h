@@ -202,6 +202,53 @@ GDN_API gdn_status gdn_decode_step_slots(gdn_rule rule,
                            int N, int H, int d_k, int d_v,
                            gdn_dtype qkv_dtype, void *stream);
 
+/*
+ * gdn_chunk_prefill_varlen -- prefill of S packed sequences of different
+ * lengths in one call, states in a pool (continuous batching: the serving
+ * runs batch whole prompts of any length next to each other; HyLo's vLLM
+ * runtime keeps a fixed-size state per request, ftxj.github.io digest of
+ * arXiv 2604.24715, Key Ideas).
+ *
+ *   q, k           [T_total, H, d_k] bf16 (sequence s = tokens cu_seqlens[s] ..
+ *                  cu_seqlens[s+1]-1)
+ *   v              [T_total, H, d_v] bf16
+ *   g, beta        [T_total, H] fp32
+ *   cu_seqlens     HOST array [S + 1]: 0 = cu[0] <= cu[1] <= ... <= cu[S] = T_total
+ *                  (empty sequences allowed)
+ *   state_pool     [pool_size, H, d_k, d_v] fp32: sequence s starts from
+ *                  state_pool[slot(s)] (or zeros, see has_initial) and its final
+ *                  state is written back to the same slot
+ *   slots          HOST array [S], or NULL for slot(s) = s (then pool_size >= S).
+ *                  Slot -1: the sequence starts from zeros and its final state is
+ *                  dropped; other slots must lie in [0, pool_size) and be distinct
+ *   has_initial    HOST array [S], or NULL (all start from their stored state);
+ *                  0 = start from zeros (a new request)
+ *   o              [T_total, H, d_v] fp32, written
+ *   workspace      at least gdn_chunk_prefill_varlen_workspace_size(...) bytes
+ * Supported: qkv_dtype GDN_BF16, d_k and d_v in {64, 128}, chunk in {32, 64};
+ * both rules.  The host arrays are read during the call only.
+ * Errors: GDN_ERR_UNSUPPORTED (rule, dtype or sizes), GDN_ERR_SHAPE (bad
+ * offsets, slots out of range, pool_size < S without slots), GDN_ERR_NULL,
+ * GDN_ERR_ALIGN, GDN_ERR_ALIAS (repeated slot, overlapping buffers),
+ * GDN_ERR_WORKSPACE, GDN_ERR_HIP.
+ */
+GDN_API gdn_status gdn_chunk_prefill_varlen(gdn_rule rule,
+                             const void *q, const void *k, const void *v,
+                             const float *g, const float *beta,
+                             const int32_t *cu_seqlens, int S, int T_total,
+                             float *state_pool, int pool_size,
+                             const int32_t *slots, const int32_t *has_initial,
+                             float *o,
+                             int H, int d_k, int d_v, int chunk,
+                             gdn_dtype qkv_dtype,
+                             void *workspace, size_t workspace_bytes,
+                             void *stream);
+
+/* Workspace bytes gdn_chunk_prefill_varlen needs for this batch (0 when the
+ * arguments would be rejected). */
+GDN_API size_t gdn_chunk_prefill_varlen_workspace_size(const int32_t *cu_seqlens, int S, int H,
+                                               int d_k, int d_v, int chunk, gdn_dtype qkv_dtype);
+
 /* Static, human-readable text for a status code (never NULL). */
 GDN_API const char *gdn_status_string(gdn_status status);
 

@@ -145,3 +145,33 @@ def test_decode_slots_validation():
     assert call(o=addr(6)) == ALIAS            # output over the slot table
     assert call(pool=addr(6) - 1024) == ALIAS  # pool running into the slot table
     assert call(N=0, slots=None, q=None) == OK
+
+
+def test_varlen_validation():
+    import numpy as np
+    cu = np.array([0, 100, 100, 350], dtype=np.int32)
+
+    def call(cu=cu, slots=None, init=None, P=8, dt=BF16, dk=64, dv=64, chunk=64, T=350, ws_bytes=1 << 30,
+             rule=gdn.GDN_RULE_GATED_DELTA, o=addr(5), pool=addr(6), ws=addr(7)):
+        S = len(cu) - 1
+        return gdn.gdn_chunk_prefill_varlen(rule, addr(0), addr(1), addr(2), addr(3), addr(4),
+                                            None if cu is None else cu.ctypes.data, S, T, pool, P,
+                                            None if slots is None else slots.ctypes.data,
+                                            None if init is None else init.ctypes.data, o, 2, dk, dv, chunk, dt,
+                                            ws, ws_bytes, None)
+    assert call(rule=4) == UNSUP
+    assert call(dt=F32) == UNSUP and call(dk=16) == UNSUP and call(chunk=16) == UNSUP
+    assert call(T=351) == SHAPE                                   # offsets must end at T_total
+    assert call(cu=np.array([0, 100, 90, 350], dtype=np.int32)) == SHAPE  # decreasing offsets
+    assert call(cu=np.array([5, 100, 350], dtype=np.int32)) == SHAPE      # must start at 0
+    assert call(P=2) == SHAPE                                     # slot s = s needs pool_size >= S
+    assert call(slots=np.array([1, 8, 0], dtype=np.int32)) == SHAPE       # slot out of range
+    assert call(slots=np.array([1, -2, 0], dtype=np.int32)) == SHAPE
+    assert call(slots=np.array([3, 5, 3], dtype=np.int32)) == ALIAS       # one state, two sequences
+    assert call(pool=None) == NULL
+    assert call(ws_bytes=16) == WS and call(ws=None) == WS
+    assert call(o=addr(0)) == ALIAS and call(pool=addr(4)) == ALIAS
+    need = gdn.gdn_chunk_prefill_varlen_workspace_size(cu.ctypes.data, 3, 2, 64, 64, 64, BF16)
+    assert 0 < need < 1 << 20
+    assert gdn.gdn_chunk_prefill_varlen_workspace_size(cu.ctypes.data, 3, 2, 16, 64, 64, BF16) == 0
+    assert call(cu=np.array([0], dtype=np.int32), T=0) == OK      # no sequences: nothing to do
