@@ -34,6 +34,7 @@ import os
 import numpy as np
 
 from .brute import brute_force, closed_form_decay
+from . import prep
 from .build import LIB, build
 
 F64, F32, BF16 = 0, 1, 2
@@ -184,5 +185,5 @@ def num_threads() -> int:
     return default().num_threads()
 
 
-__all__ = ["Oracle", "default", "prefill", "decode_step", "brute_force", "closed_form_decay",
+__all__ = ["Oracle", "default", "prefill", "decode_step", "brute_force", "closed_form_decay", "prep",
            "num_threads", "build", "GATED_DELTA", "GATED_DECAY"]
