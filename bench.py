@@ -48,6 +48,11 @@ FLOPS_PER_TOKEN_HEAD = 64 * (6 * 64 + 4 * 64) + 6 * 64 * 64 + 64 * 64 // 3
 # decode, per (sequence, head) per step: state read + write (2 * 4 * 64 * 64),
 # q, k, v bf16 (3 * 64 * 2), g, beta (8), o fp32 (64 * 4)
 DECODE_BYTES_PER_SEQ_HEAD = 2 * 4 * 64 * 64 + 3 * 64 * 2 + 8 + 64 * 4
+# preparation ahead of the mixer, per token-head: raw q/k/v projections read and q/k/v written, bf16
+# (2 * 3 * 64 * 2), gate and write-strength logits read and g, beta written, fp32 (4 * 4) = 784; per
+# channel once per call: convolution weights (4 * 4) and, per sequence, the carried state read and
+# written (2 * 3 * 4)
+PREP_BYTES_PER_TOKEN_HEAD = 2 * 3 * 64 * 2 + 4 * 4
 COPY_BYTES = 4 << 30  # far larger than the 256 MB last-level cache
 FLUSH_BYTES = 1 << 30
 CSRC = os.path.join(ROOT, "hybrid_linear_attention_gated_amd", "csrc")
@@ -80,7 +85,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=65536,
                     help="tokens of the 64K workload the oracle is timed on")
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "copy"], default="all",
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "copy", "prepare"], default="all",
                     help="run one component (for profiling); 'copy' runs a plain 4 GiB device copy "
                          "used to calibrate the HBM byte counters; the JSON line needs 'all'")
     args = ap.parse_args()
@@ -129,6 +134,40 @@ def main():
     state0 = gi.decode_state(dw.B, dw.H, dw.dk, dw.dv, device=dev)
     state = state0.clone()
     dout = torch.empty((dw.B, dw.H, dw.dv), device=dev, dtype=torch.float32)
+
+    # input preparation ahead of the mixer (short convolution, SiLU, q/k norm, gates) on the same
+    # 64K shape and on the decode batch (one token per sequence, convolution state carried in place)
+    pin = gi.prep_inputs(w.B, w.T, w.H, w.dk, w.dv, wid=200, device=dev)
+    pouts = (torch.empty_like(pin["xq"]), torch.empty_like(pin["xk"]), torch.empty_like(pin["xv"]),
+             torch.empty((w.B, w.T, w.H), device=dev, dtype=torch.float32),
+             torch.empty((w.B, w.T, w.H), device=dev, dtype=torch.float32))
+    pstate = torch.empty_like(pin["conv_state"])
+    din = gi.prep_inputs(dw.B, 1, dw.H, dw.dk, dw.dv, wid=201, device=dev)
+    dstate0 = din["conv_state"].clone()
+
+    def prepare():
+        gdn.prepare(pin["xq"], pin["xk"], pin["xv"], pin["conv_weight"], pin["a_raw"], pin["b_raw"],
+                    decay_rate=pin["decay_rate"], gate_bias=pin["gate_bias"], conv_state=pin["conv_state"],
+                    conv_state_out=pstate, outs=pouts)
+
+    def prepare_decode():
+        gdn.prepare(din["xq"], din["xk"], din["xv"], din["conv_weight"], din["a_raw"], din["b_raw"],
+                    decay_rate=din["decay_rate"], gate_bias=din["gate_bias"], conv_state=din["conv_state"],
+                    conv_state_out=din["conv_state"])
+
+    if args.only == "prepare":
+        for _ in range(args.warmup):
+            prepare()
+            prepare_decode()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            prepare()
+            prepare_decode()
+        torch.cuda.synchronize()
+        print(json.dumps({"only": "prepare", "steps": args.steps,
+                          "wall_ms": (time.perf_counter() - t0) * 1e3}), flush=True)
+        return
 
     def prefill():
         if args.only == "decode":
@@ -218,6 +257,35 @@ def main():
     torch.cuda.synchronize()
     varlen_ms = sum(a.elapsed_time(b) for a, b in vl_ev) / len(vl_ev)
 
+    # preparation: alone (64K shape and decode batch), and followed by the 64K prefill
+    for _ in range(args.warmup):
+        prepare()
+        prepare_decode()
+    pp_ev = [(mk(), mk()) for _ in range(args.steps)]
+    pd_ev = [(mk(), mk()) for _ in range(args.steps)]
+    pc_ev = [(mk(), mk()) for _ in range(args.steps)]
+    for i in range(args.steps):
+        pp_ev[i][0].record(stream)
+        prepare()
+        pp_ev[i][1].record(stream)
+        pd_ev[i][0].record(stream)
+        prepare_decode()
+        pd_ev[i][1].record(stream)
+    for i in range(args.steps):
+        pc_ev[i][0].record(stream)
+        prepare()
+        gdn.chunk_prefill(pouts[0], pouts[1], pouts[2], pouts[3], pouts[4], pre["s0"], chunk=w.chunk,
+                          out=out, final_state=fin, workspace=ws)
+        pc_ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    din["conv_state"].copy_(dstate0)
+    prep_ms = sum(a.elapsed_time(b) for a, b in pp_ev) / len(pp_ev)
+    prep_dec_ms = sum(a.elapsed_time(b) for a, b in pd_ev) / len(pd_ev)
+    prep_chain_ms = sum(a.elapsed_time(b) for a, b in pc_ev) / len(pc_ev)
+    conv_ch = w.H * (2 * w.dk + w.dv)
+    prep_bytes = w.B * w.T * w.H * PREP_BYTES_PER_TOKEN_HEAD + conv_ch * (16 + 24 * w.B)
+    prep_dec_bytes = dw.B * dw.H * PREP_BYTES_PER_TOKEN_HEAD + conv_ch * (16 + 24 * dw.B)
+
     # decode with a cold last-level cache: read a 1 GiB buffer before each step, outside the
     # events (a read leaves only clean lines behind, so no write-back competes with the step)
     flush = torch.ones(FLUSH_BYTES // 4, device=dev, dtype=torch.float32)
@@ -291,6 +359,16 @@ def main():
             "GBps_algorithmic": round(Tv * w.H * BYTES_PER_TOKEN_HEAD / (varlen_ms * 1e-3) / 1e9, 1),
             "note": "64 packed prompts of seeded lengths 1..2047, H=32 d=64 chunk 64, zero start states "
                     "written to a 64-slot pool",
+        },
+        "prepare": {
+            "ms_avg": round(prep_ms, 4), "GBps_algorithmic": round(prep_bytes / (prep_ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(prep_bytes / (prep_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "bytes_per_call": prep_bytes,
+            "decode_us_avg": round(prep_dec_ms * 1e3, 2),
+            "decode_GBps_algorithmic": round(prep_dec_bytes / (prep_dec_ms * 1e-3) / 1e9, 1),
+            "prepare_then_prefill_ms_avg": round(prep_chain_ms, 4),
+            "prepare_then_prefill_tokens_per_s": round(w.B * w.T / (prep_chain_ms * 1e-3), 1),
+            "note": "short causal convolution + SiLU + q/k L2 norm + gate activations on the 64K shape "
+                    "(bf16 in and out) and on the 256-sequence decode batch (state in place)",
         },
         "gated_decay_rule": {
             "prefill_ms_avg": round(decay_pre_ms, 4),

@@ -33,7 +33,8 @@ from dataclasses import dataclass
 
 import torch
 
-TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "beta": 3, "g": 4, "s0": 5}
+TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "beta": 3, "g": 4, "s0": 5, "xq": 6, "xk": 7, "xv": 8, "conv_w": 9,
+              "a_raw": 10, "b_raw": 11, "rate": 12, "dt": 13, "conv_state": 14}
 
 
 @dataclass(frozen=True)
@@ -139,3 +140,38 @@ def decode_inputs(N, H, dk, dv, step, *, wid=5, qkv_dtype=torch.bfloat16, gate_s
 
 def decode_state(N, H, dk, dv, *, wid=5, device="cpu"):
     return draw_state((N, H, dk, dv), seed_of(wid, 0, "s0"), device)
+
+
+def _uniform(shape, seed, lo, hi, device):
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    return lo + (hi - lo) * torch.rand(shape, generator=gen, device=device, dtype=torch.float32)
+
+
+def prep_inputs(B, T, H, dk, dv, *, wid=0, call=0, x_dtype=torch.bfloat16, state=True, rate=True,
+                device="cpu"):
+    """Raw inputs of the preparation ahead of the mixer (the projections' outputs and the block's
+    own parameters), as a randomly initialised converted block would hold them:
+
+    xq, xk [B,T,H,dk], xv [B,T,H,dv] ~ N(0,1) in x_dtype; conv_weight [H*(2dk+dv), 4] ~ U(-1/2, 1/2)
+    (fan-in 4); a_raw, b_raw [B,T,H] ~ N(0,1); decay_rate [H] ~ U(1, 16); gate_bias [H] = the inverse
+    softplus of dt ~ exp(U(log 1e-3, log 1e-1)); conv_state [B, H*(2dk+dv), 3] ~ N(0,1) rounded
+    through x_dtype (it holds earlier raw inputs).  ``state=False`` / ``rate=False`` give None for
+    the state / for decay_rate and gate_bias."""
+    C = H * (2 * dk + dv)
+    d = {
+        "xq": _normal((B, T, H, dk), seed_of(wid, call, "xq"), device).to(x_dtype),
+        "xk": _normal((B, T, H, dk), seed_of(wid, call, "xk"), device).to(x_dtype),
+        "xv": _normal((B, T, H, dv), seed_of(wid, call, "xv"), device).to(x_dtype),
+        "conv_weight": _uniform((C, 4), seed_of(wid, 0, "conv_w"), -0.5, 0.5, device),
+        "a_raw": _normal((B, T, H), seed_of(wid, call, "a_raw"), device),
+        "b_raw": _normal((B, T, H), seed_of(wid, call, "b_raw"), device),
+        "decay_rate": None, "gate_bias": None, "conv_state": None,
+    }
+    if rate:
+        d["decay_rate"] = _uniform((H,), seed_of(wid, 0, "rate"), 1.0, 16.0, device)
+        dt = torch.exp(_uniform((H,), seed_of(wid, 0, "dt"), -6.907755, -2.302585, device))
+        d["gate_bias"] = dt + torch.log(-torch.expm1(-dt))
+    if state:
+        d["conv_state"] = _normal((B, C, 3), seed_of(wid, call, "conv_state"), device).to(x_dtype).float()
+    return d

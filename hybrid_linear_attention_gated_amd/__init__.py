@@ -6,14 +6,17 @@ kernels of ``libgdn.so``.  PyTorch supplies device memory and the stream.
 Raw C-ABI entry points (same names and arguments as ``include/gdn.h``, with
 pointers passed as integers):
 
-    gdn_chunk_prefill, gdn_chunk_prefill_workspace_size, gdn_decode_step,
-    gdn_status_string, gdn_version
+    gdn_chunk_prefill, gdn_chunk_prefill_rule, gdn_chunk_prefill_workspace_size,
+    gdn_chunk_prefill_varlen, gdn_chunk_prefill_varlen_workspace_size, gdn_decode_step,
+    gdn_decode_step_rule, gdn_decode_step_slots, gdn_prepare, gdn_status_string, gdn_version
 
 Tensor helpers that allocate outputs with torch and call the above on the
 current stream:
 
     chunk_prefill(q, k, v, g, beta, initial_state=None, chunk=64) -> (o, final_state)
     decode_step(q, k, v, g, beta, state) -> o        (state updated in place)
+    decode_step_slots / chunk_prefill_varlen          (states in a pool, packed sequences)
+    prepare(xq, xk, xv, conv_weight, a_raw, b_raw) -> (q, k, v, g, beta)
 
 The rule computed (a gated delta rule; the pages describe the GDN layer in
 words only -- kwkr.cn digest of HyLo-Llama-8MLA8GDN-8K-SFT, architecture
@@ -36,8 +39,8 @@ STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_UNSUPP
           4: "GDN_ERR_ALIGN", 5: "GDN_ERR_ALIAS", 6: "GDN_ERR_WORKSPACE", 7: "GDN_ERR_HIP"}
 EXPORTS = ("gdn_chunk_prefill", "gdn_chunk_prefill_rule", "gdn_chunk_prefill_workspace_size",
            "gdn_chunk_prefill_varlen", "gdn_chunk_prefill_varlen_workspace_size",
-           "gdn_decode_step", "gdn_decode_step_rule", "gdn_decode_step_slots", "gdn_status_string",
-           "gdn_version")
+           "gdn_decode_step", "gdn_decode_step_rule", "gdn_decode_step_slots", "gdn_prepare",
+           "gdn_status_string", "gdn_version")
 
 
 class GdnError(RuntimeError):
@@ -77,6 +80,8 @@ def lib():
         L.gdn_chunk_prefill_varlen.restype = i32
         L.gdn_chunk_prefill_varlen_workspace_size.argtypes = [vp, i32, i32, i32, i32, i32, i32]
         L.gdn_chunk_prefill_varlen_workspace_size.restype = sz
+        L.gdn_prepare.argtypes = [vp] * 15 + [i32] * 6 + [vp]
+        L.gdn_prepare.restype = i32
         L.gdn_status_string.argtypes = [i32]
         L.gdn_status_string.restype = ctypes.c_char_p
         L.gdn_version.argtypes = []
@@ -128,6 +133,12 @@ def gdn_chunk_prefill_varlen(rule, q, k, v, g, beta, cu_seqlens, S, T_total, sta
 
 def gdn_chunk_prefill_varlen_workspace_size(cu_seqlens, S, H, d_k, d_v, chunk, qkv_dtype) -> int:
     return lib().gdn_chunk_prefill_varlen_workspace_size(cu_seqlens, S, H, d_k, d_v, chunk, qkv_dtype)
+
+
+def gdn_prepare(xq, xk, xv, conv_weight, a_raw, b_raw, decay_rate, gate_bias, conv_state_in,
+                conv_state_out, q, k, v, g, beta, B, T, H, d_k, d_v, x_dtype, stream) -> int:
+    return lib().gdn_prepare(xq, xk, xv, conv_weight, a_raw, b_raw, decay_rate, gate_bias, conv_state_in,
+                             conv_state_out, q, k, v, g, beta, B, T, H, d_k, d_v, x_dtype, stream)
 
 
 def gdn_status_string(status: int) -> str:
@@ -256,6 +267,42 @@ def decode_step_slots(q, k, v, g, beta, state_pool, slots, *, out=None, stream=N
     return out
 
 
+def prepare(xq, xk, xv, conv_weight, a_raw, b_raw, *, decay_rate=None, gate_bias=None, conv_state=None,
+            conv_state_out=None, outs=None, stream=None):
+    """Input preparation ahead of the mixer.  xq, xk [B,T,H,d_k]; xv [B,T,H,d_v] (bf16 or fp32);
+    conv_weight [H*(2 d_k + d_v), 4] fp32; a_raw, b_raw [B,T,H] fp32; decay_rate, gate_bias [H] fp32
+    or None; conv_state [B, H*(2 d_k + d_v), 3] fp32 or None (zeros).  conv_state_out receives the
+    carried state (pass conv_state itself to update it in place; None = not kept).
+    Returns (q, k, v, g, beta) ready for chunk_prefill / decode_step."""
+    import torch
+    B, T, H, d_k = xq.shape
+    d_v = xv.shape[-1]
+    dt = _dtype_code(xq)
+    for t, n in ((xq, "xq"), (xk, "xk"), (xv, "xv")):
+        _check(t, n, xq.dtype)
+    for t, n in ((conv_weight, "conv_weight"), (a_raw, "a_raw"), (b_raw, "b_raw"), (decay_rate, "decay_rate"),
+                 (gate_bias, "gate_bias"), (conv_state, "conv_state"), (conv_state_out, "conv_state_out")):
+        _check(t, n, torch.float32)
+    dev = xq.device
+    if outs is None:
+        outs = (torch.empty_like(xq), torch.empty_like(xk), torch.empty_like(xv),
+                torch.empty((B, T, H), device=dev, dtype=torch.float32),
+                torch.empty((B, T, H), device=dev, dtype=torch.float32))
+    q, k, v, g, beta = outs
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, xq.dtype)
+    _check(g, "g", torch.float32)
+    _check(beta, "beta", torch.float32)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    st = gdn_prepare(_ptr(xq), _ptr(xk), _ptr(xv), _ptr(conv_weight), _ptr(a_raw), _ptr(b_raw), _ptr(decay_rate),
+                     _ptr(gate_bias), _ptr(conv_state), _ptr(conv_state_out), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                     _ptr(beta), B, T, H, d_k, d_v, dt, stream)
+    if st != 0:
+        raise GdnError(st, "gdn_prepare")
+    return q, k, v, g, beta
+
+
 def _host_i32(x):
     """A host int32 array (numpy) from a list, numpy array or CPU tensor, or None."""
     import numpy as np
@@ -322,4 +369,4 @@ __all__ = ["EXPORTS", "GDN_F32", "GDN_BF16", "GDN_RULE_GATED_DELTA", "GDN_RULE_G
            "gdn_decode_step", "gdn_decode_step_rule", "gdn_status_string", "gdn_version",
            "gdn_decode_step_slots", "gdn_chunk_prefill_varlen", "gdn_chunk_prefill_varlen_workspace_size",
            "chunk_prefill", "chunk_prefill_varlen", "decode_step", "decode_step_slots", "workspace_bytes",
-           "varlen_workspace_bytes"]
+           "varlen_workspace_bytes", "gdn_prepare", "prepare"]

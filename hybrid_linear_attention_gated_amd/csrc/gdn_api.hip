@@ -313,4 +313,57 @@ gdn_status gdn_decode_step(const void *q, const void *k, const void *v, const fl
                                 qkv_dtype, stream);
 }
 
+gdn_status gdn_prepare(const void *xq, const void *xk, const void *xv, const float *conv_weight,
+                       const float *a_raw, const float *b_raw, const float *decay_rate,
+                       const float *gate_bias, const float *conv_state_in, float *conv_state_out,
+                       void *q, void *k, void *v, float *g, float *beta, int B, int T, int H,
+                       int d_k, int d_v, gdn_dtype x_dtype, void *stream) {
+    if (B <= 0 || H <= 0 || T < 0 || d_k <= 0 || d_v <= 0) return GDN_ERR_SHAPE;
+    if (x_dtype != GDN_F32 && x_dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+    if (!supported_dim(d_k) || !supported_dim(d_v)) return GDN_ERR_UNSUPPORTED;
+    const long long C = static_cast<long long>(H) * (2 * d_k + d_v);
+    if (prod({B, T, C}) == SIZE_MAX || C > (1LL << 28)) return GDN_ERR_SHAPE;
+    // workgroups: 256 channel columns x 64 tokens each, plus 1024 gate elements each
+    const long long slabs = (C / 4 + 255) / 256, tiles = T > 0 ? (T + 63) / 64 : 1;
+    const unsigned __int128 blocks = static_cast<unsigned __int128>(slabs) * B * tiles +
+                                     (static_cast<unsigned __int128>(B) * T * H + 1023) / 1024;
+    if (blocks > 0x7fffff00ULL) return GDN_ERR_SHAPE;
+    if (!conv_weight) return GDN_ERR_NULL;
+    if (T > 0 && (!xq || !xk || !xv || !a_raw || !b_raw || !q || !k || !v || !g || !beta))
+        return GDN_ERR_NULL;
+    const void *ptrs[] = {xq, xk, xv, conv_weight, a_raw, b_raw, decay_rate, gate_bias,
+                          conv_state_in, conv_state_out, q, k, v, g, beta};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return GDN_ERR_ALIGN;
+
+    const size_t es = elem_bytes(x_dtype);
+    const size_t nk = prod({B, T, H, d_k}) * es, nv = prod({B, T, H, d_v}) * es;
+    const size_t ngate = prod({B, T, H}) * 4, nstate = prod({B, C, 3}) * 4;
+    const Span in[] = {span(xq, xq ? nk : 0), span(xk, xk ? nk : 0), span(xv, xv ? nv : 0),
+                       span(conv_weight, static_cast<size_t>(C) * 16), span(a_raw, a_raw ? ngate : 0),
+                       span(b_raw, b_raw ? ngate : 0),
+                       span(decay_rate, decay_rate ? static_cast<size_t>(H) * 4 : 0),
+                       span(gate_bias, gate_bias ? static_cast<size_t>(H) * 4 : 0),
+                       span(conv_state_in, conv_state_in ? nstate : 0)};
+    const Span out[] = {span(q, q ? nk : 0), span(k, k ? nk : 0), span(v, v ? nv : 0),
+                        span(g, g ? ngate : 0), span(beta, beta ? ngate : 0),
+                        span(conv_state_out, conv_state_out ? nstate : 0)};
+    const int n_out = sizeof(out) / sizeof(out[0]);
+    for (int i = 0; i < n_out; ++i) {
+        for (int j = i + 1; j < n_out; ++j)
+            if (overlap(out[i], out[j])) return GDN_ERR_ALIAS;
+        for (const Span &x : in) {
+            const bool same_state = i == n_out - 1 && x.lo == out[i].lo && x.hi == out[i].hi &&
+                                    conv_state_in == conv_state_out;
+            if (!same_state && overlap(out[i], x)) return GDN_ERR_ALIAS;
+        }
+    }
+    if (T == 0 && !conv_state_out) return GDN_OK;
+    const hipError_t err =
+        launch_prepare(xq, xk, xv, conv_weight, a_raw, b_raw, decay_rate, gate_bias, conv_state_in,
+                       conv_state_out, q, k, v, g, beta, B, T, H, d_k, d_v, x_dtype,
+                       static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
 }  // extern "C"

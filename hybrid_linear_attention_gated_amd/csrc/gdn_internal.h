@@ -81,6 +81,13 @@ hipError_t launch_prefill_chunk_varlen(const uint16_t *q, const uint16_t *k, con
                                        int H, int dk, int dv, int chunk, bool delta, void *ws,
                                        hipStream_t stream);
 
+// Input preparation ahead of the mixer (gdn_prepare.hip): convolution, SiLU, q/k norm, gates.
+hipError_t launch_prepare(const void *xq, const void *xk, const void *xv, const float *w,
+                          const float *a_raw, const float *b_raw, const float *rate,
+                          const float *bias, const float *state_in, float *state_out, void *q,
+                          void *k, void *v, float *g, float *beta, int B, int T, int H, int dk,
+                          int dv, gdn_dtype dt, hipStream_t stream);
+
 // Copies (or zero-fills, when s0 == NULL) a start state into s_out.
 hipError_t launch_state_copy(const float *s0, float *s_out, size_t n, hipStream_t stream);
 

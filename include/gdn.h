@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 2
+#define GDN_ABI_VERSION 3
 
 #if defined(__GNUC__) || defined(__clang__)
 #define GDN_API __attribute__((visibility("default")))
@@ -248,6 +248,60 @@ GDN_API gdn_status gdn_chunk_prefill_varlen(gdn_rule rule,
  * arguments would be rejected). */
 GDN_API size_t gdn_chunk_prefill_varlen_workspace_size(const int32_t *cu_seqlens, int S, int H,
                                                int d_k, int d_v, int chunk, gdn_dtype qkv_dtype);
+
+/*
+ * gdn_prepare -- the input preparation that feeds the mixer, fused into one
+ * pass over the raw projections.  The GDN block carries a short convolution
+ * and gate/decay parameters of its own (ftxj.github.io digest of arXiv
+ * 2604.24715, Method: these start from random values when an attention layer
+ * is converted); the pages give no formulas, and the library computes the
+ * usual GDN input path.  Per token t, head h and channel c:
+ *
+ *   conv   c_t = w[c,0] x_{t-3} + w[c,1] x_{t-2} + w[c,2] x_{t-1} + w[c,3] x_t
+ *          (causal, depthwise, width 4; inputs before t = 0 come from
+ *          conv_state_in, or are zero)
+ *   q, k   y = silu(c) = c sigmoid(c), then y / sqrt(sum_c y^2 + 1e-6) over
+ *          the head's d_k channels
+ *   v      silu(c)
+ *   g      -A_h softplus(a_t + bias_h)   (A_h = 1, bias_h = 0 when absent)
+ *   beta   sigmoid(b_t)
+ *
+ * so that q, k, v, g, beta go straight into gdn_chunk_prefill or
+ * gdn_decode_step (decode = T = 1 with the carried convolution state).
+ *
+ *   xq, xk          [B, T, H, d_k] x_dtype (raw projections)
+ *   xv              [B, T, H, d_v] x_dtype
+ *   conv_weight     [H*(2 d_k + d_v), 4] fp32: rows are the q channels
+ *                   (head-major), then k, then v; column 3 weighs the current
+ *                   token
+ *   a_raw, b_raw    [B, T, H] fp32 gate and write-strength logits
+ *   decay_rate      [H] fp32 (A_h > 0) or NULL;  gate_bias [H] fp32 or NULL
+ *   conv_state_in   [B, H*(2 d_k + d_v), 3] fp32, the three raw inputs before
+ *                   t = 0 (oldest first, channels ordered as conv_weight), or
+ *                   NULL for zeros
+ *   conv_state_out  same shape, written with the last three raw inputs of
+ *                   [conv_state_in, x] (so calls chain exactly), or NULL; may
+ *                   be the same pointer as conv_state_in, not overlap it
+ *                   otherwise
+ *   q, k            [B, T, H, d_k] x_dtype, written (rounded once to bf16 for
+ *                   GDN_BF16)
+ *   v               [B, T, H, d_v] x_dtype, written
+ *   g, beta         [B, T, H] fp32, written
+ * T may be 0: only conv_state_out is written (a copy of the start state).
+ * conv_weight is required even then.
+ * Errors: GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_UNSUPPORTED (d_k, d_v not in
+ * {16, 64, 128}, or dtype), GDN_ERR_ALIGN, GDN_ERR_ALIAS (an output
+ * overlapping an input or another output, other than conv_state_out ==
+ * conv_state_in), GDN_ERR_HIP.
+ */
+GDN_API gdn_status gdn_prepare(const void *xq, const void *xk, const void *xv,
+                               const float *conv_weight,
+                               const float *a_raw, const float *b_raw,
+                               const float *decay_rate, const float *gate_bias,
+                               const float *conv_state_in, float *conv_state_out,
+                               void *q, void *k, void *v, float *g, float *beta,
+                               int B, int T, int H, int d_k, int d_v,
+                               gdn_dtype x_dtype, void *stream);
 
 /* Static, human-readable text for a status code (never NULL). */
 GDN_API const char *gdn_status_string(gdn_status status);

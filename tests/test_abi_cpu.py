@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     L = gdn.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert gdn.gdn_version() == 2
+    assert gdn.gdn_version() == 3
 
 
 def test_status_strings():
@@ -175,3 +175,32 @@ def test_varlen_validation():
     assert 0 < need < 1 << 20
     assert gdn.gdn_chunk_prefill_varlen_workspace_size(cu.ctypes.data, 3, 2, 16, 64, 64, BF16) == 0
     assert call(cu=np.array([0], dtype=np.int32), T=0) == OK      # no sequences: nothing to do
+
+
+def prepare_call(**kw):
+    args = dict(xq=addr(0), xk=addr(1), xv=addr(2), w=addr(3), a=addr(4), b=addr(5), rate=None, bias=None,
+                s_in=None, s_out=None, q=addr(6), k=addr(7), v=addr(8), g=addr(9), beta=addr(10),
+                B=1, T=65536, H=32, dk=64, dv=64, dt=BF16, stream=None)
+    args.update(kw)
+    return gdn.gdn_prepare(*[args[n] for n in ("xq", "xk", "xv", "w", "a", "b", "rate", "bias", "s_in", "s_out",
+                                                "q", "k", "v", "g", "beta", "B", "T", "H", "dk", "dv", "dt",
+                                                "stream")])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(w=None), NULL), (dict(xq=None), NULL), (dict(beta=None), NULL), (dict(v=None), NULL),
+    (dict(B=0), SHAPE), (dict(T=-1), SHAPE), (dict(H=0), SHAPE), (dict(T=1 << 30, H=1 << 12), SHAPE),
+    (dict(dk=32), UNSUP), (dict(dv=96), UNSUP), (dict(dt=5), UNSUP),
+    (dict(xk=addr(1) + 8), ALIGN), (dict(s_out=addr(11) + 4), ALIGN), (dict(rate=addr(12) + 2), ALIGN),
+    (dict(q=addr(0)), ALIAS), (dict(v=addr(6) + 1024), ALIAS), (dict(g=addr(4)), ALIAS),
+    (dict(beta=addr(9)), ALIAS), (dict(s_out=addr(3)), ALIAS), (dict(s_in=addr(11), s_out=addr(11) + 16), ALIAS),
+    (dict(k=addr(12), rate=addr(12)), ALIAS), (dict(s_in=addr(11), q=addr(11)), ALIAS),
+])
+def test_prepare_rejects(kw, code):
+    assert prepare_call(**kw) == code
+
+
+def test_prepare_nothing_to_do_is_a_no_op():
+    # T = 0 with no state to carry: validated, nothing queued (no GPU needed)
+    assert prepare_call(T=0, xq=None, xk=None, xv=None, a=None, b=None, q=None, k=None, v=None, g=None,
+                        beta=None) == OK
