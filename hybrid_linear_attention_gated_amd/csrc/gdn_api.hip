@@ -323,11 +323,7 @@ gdn_status gdn_prepare(const void *xq, const void *xk, const void *xv, const flo
     if (!supported_dim(d_k) || !supported_dim(d_v)) return GDN_ERR_UNSUPPORTED;
     const long long C = static_cast<long long>(H) * (2 * d_k + d_v);
     if (prod({B, T, C}) == SIZE_MAX || C > (1LL << 28)) return GDN_ERR_SHAPE;
-    // workgroups: 256 channel columns x 64 tokens each, plus 1024 gate elements each
-    const long long slabs = (C / 4 + 255) / 256, tiles = T > 0 ? (T + 63) / 64 : 1;
-    const unsigned __int128 blocks = static_cast<unsigned __int128>(slabs) * B * tiles +
-                                     (static_cast<unsigned __int128>(B) * T * H + 1023) / 1024;
-    if (blocks > 0x7fffff00ULL) return GDN_ERR_SHAPE;
+    if (prepare_grid_blocks(B, T, H, d_k, d_v) > kMaxPrepareBlocks) return GDN_ERR_SHAPE;
     if (!conv_weight) return GDN_ERR_NULL;
     if (T > 0 && (!xq || !xk || !xv || !a_raw || !b_raw || !q || !k || !v || !g || !beta))
         return GDN_ERR_NULL;

@@ -82,6 +82,9 @@ hipError_t launch_prefill_chunk_varlen(const uint16_t *q, const uint16_t *k, con
                                        hipStream_t stream);
 
 // Input preparation ahead of the mixer (gdn_prepare.hip): convolution, SiLU, q/k norm, gates.
+// prepare_grid_blocks: workgroups one call launches (at most kMaxPrepareBlocks is accepted).
+constexpr size_t kMaxPrepareBlocks = 0x7fffff00u;
+size_t prepare_grid_blocks(int B, int T, int H, int dk, int dv);
 hipError_t launch_prepare(const void *xq, const void *xk, const void *xv, const float *w,
                           const float *a_raw, const float *b_raw, const float *rate,
                           const float *bias, const float *state_in, float *state_out, void *q,

@@ -25,13 +25,26 @@
 namespace gdn {
 namespace {
 
-constexpr int kTile = 64;    // tokens per convolution workgroup
-constexpr int kCols = 256;   // channel columns (4 channels each) per workgroup
-constexpr int kGateEl = 4;   // gate elements per thread
-constexpr int kUnroll = 8;   // tokens whose loads are issued together
+#ifndef GDN_PREP_CPT
+#define GDN_PREP_CPT 4
+#endif
+#ifndef GDN_PREP_UNROLL
+#define GDN_PREP_UNROLL 8
+#endif
+#ifndef GDN_PREP_TILE
+#define GDN_PREP_TILE 32
+#endif
+
+constexpr int kCpt = GDN_PREP_CPT;        // adjacent channels per thread
+constexpr int kTile = GDN_PREP_TILE;      // tokens per convolution workgroup
+constexpr int kUnroll = GDN_PREP_UNROLL;  // tokens whose loads are issued together
+constexpr int kCols = 256;                // threads (channel columns) per workgroup
+constexpr int kGateEl = 4;                // gate elements per thread
 constexpr int kXcd = 8;
 constexpr float kEps = 1e-6f;
 constexpr float kLog2e = 1.4426950408889634f;
+static_assert(kCpt == 4 || kCpt == 8, "channels per thread");
+static_assert(kTile % kUnroll == 0 && kTile >= 3, "tile");
 
 struct PrepArgs {
     const void *xq, *xk, *xv;
@@ -42,20 +55,51 @@ struct PrepArgs {
     void *q, *k, *v;
     float *g, *beta;
     int B, T, H, dv;
-    int ncol;                 // C / 4
+    int C, ncol;              // channels, C / kCpt
     int slabs, tiles;         // convolution workgroups = slabs * B * tiles
     int conv_blocks, gate_blocks, per_xcd;
     int state_in_kernel;      // 1: the last tile writes state_out
 };
 
-__device__ __forceinline__ float4 load4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
-__device__ __forceinline__ float4 load4(const uint16_t *p) {
-    const uint2 u = *reinterpret_cast<const uint2 *>(p);
-    return make_float4(lo_half_f32(u.x), hi_half_f32(u.x), lo_half_f32(u.y), hi_half_f32(u.y));
+// kCpt stored values as raw 32-bit words (bf16 pairs or fp32), and their fp32 widening
+template <typename TIn> struct Raw {
+    static constexpr int kWords = kCpt * static_cast<int>(sizeof(TIn)) / 4;
+    uint32_t w[kWords];
+};
+template <typename TIn> __device__ __forceinline__ Raw<TIn> load_raw(const TIn *p) {
+    Raw<TIn> r;
+    if constexpr (Raw<TIn>::kWords == 2) {
+        const uint2 u = *reinterpret_cast<const uint2 *>(p);
+        r.w[0] = u.x; r.w[1] = u.y;
+    } else {
+#pragma unroll
+        for (int i = 0; i < Raw<TIn>::kWords / 4; ++i) {
+            const uint4 u = reinterpret_cast<const uint4 *>(p)[i];
+            r.w[4 * i] = u.x; r.w[4 * i + 1] = u.y; r.w[4 * i + 2] = u.z; r.w[4 * i + 3] = u.w;
+        }
+    }
+    return r;
 }
-__device__ __forceinline__ void store4(float *p, float4 x) { *reinterpret_cast<float4 *>(p) = x; }
-__device__ __forceinline__ void store4(uint16_t *p, float4 x) {
-    *reinterpret_cast<uint2 *>(p) = make_uint2(cvt2_bf16(x.x, x.y), cvt2_bf16(x.z, x.w));
+__device__ __forceinline__ void widen(const Raw<uint16_t> &r, float (&x)[kCpt]) {
+#pragma unroll
+    for (int i = 0; i < kCpt / 2; ++i) { x[2 * i] = lo_half_f32(r.w[i]); x[2 * i + 1] = hi_half_f32(r.w[i]); }
+}
+__device__ __forceinline__ void widen(const Raw<float> &r, float (&x)[kCpt]) {
+#pragma unroll
+    for (int i = 0; i < kCpt; ++i) x[i] = __uint_as_float(r.w[i]);
+}
+__device__ __forceinline__ void store_out(float *p, const float (&x)[kCpt]) {
+#pragma unroll
+    for (int i = 0; i < kCpt / 4; ++i)
+        reinterpret_cast<float4 *>(p)[i] = make_float4(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
+}
+__device__ __forceinline__ void store_out(uint16_t *p, const float (&x)[kCpt]) {
+    if constexpr (kCpt == 4) {
+        *reinterpret_cast<uint2 *>(p) = make_uint2(cvt2_bf16(x[0], x[1]), cvt2_bf16(x[2], x[3]));
+    } else {
+        *reinterpret_cast<uint4 *>(p) = make_uint4(cvt2_bf16(x[0], x[1]), cvt2_bf16(x[2], x[3]),
+                                                   cvt2_bf16(x[4], x[5]), cvt2_bf16(x[6], x[7]));
+    }
 }
 
 __device__ __forceinline__ float silu(float c) {
@@ -63,10 +107,35 @@ __device__ __forceinline__ float silu(float c) {
     return c * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-c * kLog2e));
 }
 
+// v plus the value of another lane, picked by a DPP lane pattern (all lanes active)
+template <int CTRL> __device__ __forceinline__ float dpp_plus(float v) {
+    return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+// sum over aligned groups of G adjacent lanes, left in every lane of the group
 template <int G> __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-    for (int m = 1; m < G; m <<= 1) v += __shfl_xor(v, m);
+    if constexpr (G >= 2) v = dpp_plus<0xB1>(v);    // quad_perm [1,0,3,2]: lane ^ 1
+    if constexpr (G >= 4) v = dpp_plus<0x4E>(v);    // quad_perm [2,3,0,1]: lane ^ 2
+    if constexpr (G >= 8) v = dpp_plus<0x141>(v);   // row_half_mirror: the other quad of the 8
+    if constexpr (G >= 16) v = dpp_plus<0x140>(v);  // row_mirror: the other 8 of the row
+    if constexpr (G >= 32) v += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));  // lane ^ 16
+    static_assert(G <= 32, "group");
     return v;
+}
+
+// this thread's tensor, position and row stride, from its first channel in the q|k|v space
+template <typename TIn> struct Route {
+    const TIn *x;
+    TIn *y;
+    int rs;
+    bool norm;
+};
+template <int DK, typename TIn> __device__ __forceinline__ Route<TIn> route(const PrepArgs &a, int ch) {
+    const int HK = a.H * DK;
+    if (ch < HK) return {static_cast<const TIn *>(a.xq) + ch, static_cast<TIn *>(a.q) + ch, HK, true};
+    if (ch < 2 * HK)
+        return {static_cast<const TIn *>(a.xk) + (ch - HK), static_cast<TIn *>(a.k) + (ch - HK), HK, true};
+    return {static_cast<const TIn *>(a.xv) + (ch - 2 * HK), static_cast<TIn *>(a.v) + (ch - 2 * HK), a.H * a.dv,
+            false};
 }
 
 template <int DK, typename TIn>
@@ -97,100 +166,103 @@ __global__ __launch_bounds__(kCols) void prepare_kernel(PrepArgs a) {
     const int slab = w / (a.tiles * a.B);
     const int col = slab * kCols + tid;
     if (col >= a.ncol) return;  // whole cross-lane groups drop out together
-    const int ch = 4 * col;
-    const int HK = a.H * DK;
-
-    const TIn *x;
-    TIn *y;
-    int rs;       // row stride (elements) of this thread's tensor
-    bool norm;
-    if (ch < HK) {
-        x = static_cast<const TIn *>(a.xq) + ch; y = static_cast<TIn *>(a.q) + ch; rs = HK; norm = true;
-    } else if (ch < 2 * HK) {
-        x = static_cast<const TIn *>(a.xk) + (ch - HK); y = static_cast<TIn *>(a.k) + (ch - HK); rs = HK; norm = true;
-    } else {
-        x = static_cast<const TIn *>(a.xv) + (ch - 2 * HK); y = static_cast<TIn *>(a.v) + (ch - 2 * HK);
-        rs = a.H * a.dv; norm = false;
-    }
+    const int ch = kCpt * col;
+    Route<TIn> r = route<DK, TIn>(a, ch);
     const size_t row0 = static_cast<size_t>(b) * a.T;
-    x += row0 * rs;
-    y += row0 * rs;
+    r.x += row0 * r.rs;
+    r.y += row0 * r.rs;
 
-    float4 wt[4];  // wt[j] = taps of channel ch + j
+    float wt[4][kCpt];  // wt[i][j]: tap i of channel ch + j
 #pragma unroll
-    for (int j = 0; j < 4; ++j) wt[j] = load4(a.w + static_cast<size_t>(ch + j) * 4);
+    for (int j = 0; j < kCpt; ++j) {
+        const float4 u = *reinterpret_cast<const float4 *>(a.w + static_cast<size_t>(ch + j) * 4);
+        wt[0][j] = u.x; wt[1][j] = u.y; wt[2][j] = u.z; wt[3][j] = u.w;
+    }
 
     const int t0 = tile * kTile;
     const int t1 = min(t0 + kTile, a.T);
-    float4 x3, x2, x1;  // inputs at t-3, t-2, t-1
+    float x3[kCpt], x2[kCpt], x1[kCpt];  // inputs at t-3, t-2, t-1
     if (t0 == 0) {
         if (a.state_in) {
-            const float *s = a.state_in + (static_cast<size_t>(b) * a.ncol * 4 + ch) * 3;
-            const float4 p = load4(s), q = load4(s + 4), r = load4(s + 8);  // 4 channels x 3 taps
-            x3 = make_float4(p.x, p.w, q.z, r.y);
-            x2 = make_float4(p.y, q.x, q.w, r.z);
-            x1 = make_float4(p.z, q.y, r.x, r.w);
+            float s[3 * kCpt];  // kCpt channels x 3 taps, channel-major
+            const float *sp = a.state_in + (static_cast<size_t>(b) * a.C + ch) * 3;
+#pragma unroll
+            for (int i = 0; i < 3 * kCpt / 4; ++i) {
+                const float4 u = reinterpret_cast<const float4 *>(sp)[i];
+                s[4 * i] = u.x; s[4 * i + 1] = u.y; s[4 * i + 2] = u.z; s[4 * i + 3] = u.w;
+            }
+#pragma unroll
+            for (int j = 0; j < kCpt; ++j) { x3[j] = s[3 * j]; x2[j] = s[3 * j + 1]; x1[j] = s[3 * j + 2]; }
         } else {
-            x3 = x2 = x1 = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int j = 0; j < kCpt; ++j) x3[j] = x2[j] = x1[j] = 0.f;
         }
     } else {
-        x3 = load4(x + static_cast<size_t>(t0 - 3) * rs);
-        x2 = load4(x + static_cast<size_t>(t0 - 2) * rs);
-        x1 = load4(x + static_cast<size_t>(t0 - 1) * rs);
+        widen(load_raw(r.x + static_cast<size_t>(t0 - 3) * r.rs), x3);
+        widen(load_raw(r.x + static_cast<size_t>(t0 - 2) * r.rs), x2);
+        widen(load_raw(r.x + static_cast<size_t>(t0 - 1) * r.rs), x1);
     }
 
     for (int tb = t0; tb < t1; tb += kUnroll) {
-        float4 xs[kUnroll];
+        Raw<TIn> raw[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u)
-            xs[u] = tb + u < t1 ? load4(x + static_cast<size_t>(tb + u) * rs) : make_float4(0.f, 0.f, 0.f, 0.f);
+            if (tb + u < t1) raw[u] = load_raw(r.x + static_cast<size_t>(tb + u) * r.rs);
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             if (tb + u >= t1) break;  // uniform across the workgroup
-            const float4 xt = xs[u];
-            float4 c;
-            c.x = fmaf(wt[0].w, xt.x, fmaf(wt[0].z, x1.x, fmaf(wt[0].y, x2.x, wt[0].x * x3.x)));
-            c.y = fmaf(wt[1].w, xt.y, fmaf(wt[1].z, x1.y, fmaf(wt[1].y, x2.y, wt[1].x * x3.y)));
-            c.z = fmaf(wt[2].w, xt.z, fmaf(wt[2].z, x1.z, fmaf(wt[2].y, x2.z, wt[2].x * x3.z)));
-            c.w = fmaf(wt[3].w, xt.w, fmaf(wt[3].z, x1.w, fmaf(wt[3].y, x2.w, wt[3].x * x3.w)));
-            float4 s = make_float4(silu(c.x), silu(c.y), silu(c.z), silu(c.w));
-            const float ss = group_sum<DK / 4>(s.x * s.x + s.y * s.y + s.z * s.z + s.w * s.w);
-            const float r = norm ? __builtin_amdgcn_rsqf(ss + kEps) : 1.f;
-            s.x *= r; s.y *= r; s.z *= r; s.w *= r;
-            store4(y + static_cast<size_t>(tb + u) * rs, s);
-            x3 = x2; x2 = x1; x1 = xt;
+            float xt[kCpt], y[kCpt];
+            widen(raw[u], xt);
+            float ss = 0.f;
+#pragma unroll
+            for (int j = 0; j < kCpt; ++j) {
+                const float c = fmaf(wt[3][j], xt[j], fmaf(wt[2][j], x1[j], fmaf(wt[1][j], x2[j], wt[0][j] * x3[j])));
+                y[j] = silu(c);
+                ss = fmaf(y[j], y[j], ss);
+            }
+            ss = group_sum<DK / kCpt>(ss);
+            const float rn = r.norm ? __builtin_amdgcn_rsqf(ss + kEps) : 1.f;
+#pragma unroll
+            for (int j = 0; j < kCpt; ++j) {
+                y[j] *= rn;
+                x3[j] = x2[j]; x2[j] = x1[j]; x1[j] = xt[j];
+            }
+            store_out(r.y + static_cast<size_t>(tb + u) * r.rs, y);
         }
     }
 
     if (a.state_in_kernel && t1 == a.T && a.state_out) {  // last tile: the window is the new state
-        float *s = a.state_out + (static_cast<size_t>(b) * a.ncol * 4 + ch) * 3;
-        store4(s, make_float4(x3.x, x2.x, x1.x, x3.y));
-        store4(s + 4, make_float4(x2.y, x1.y, x3.z, x2.z));
-        store4(s + 8, make_float4(x1.z, x3.w, x2.w, x1.w));
+        float s[3 * kCpt];
+#pragma unroll
+        for (int j = 0; j < kCpt; ++j) { s[3 * j] = x3[j]; s[3 * j + 1] = x2[j]; s[3 * j + 2] = x1[j]; }
+        float *sp = a.state_out + (static_cast<size_t>(b) * a.C + ch) * 3;
+#pragma unroll
+        for (int i = 0; i < 3 * kCpt / 4; ++i)
+            reinterpret_cast<float4 *>(sp)[i] = make_float4(s[4 * i], s[4 * i + 1], s[4 * i + 2], s[4 * i + 3]);
     }
 }
 
 // New convolution state from the last three tokens (T >= 3), for calls whose
 // state is updated in place and spans several tiles: run after prepare_kernel,
 // which has then finished reading the old state.
-template <typename TIn>
-__global__ __launch_bounds__(kCols) void conv_state_tail_kernel(PrepArgs a, int DK) {
+template <int DK, typename TIn>
+__global__ __launch_bounds__(kCols) void conv_state_tail_kernel(PrepArgs a) {
     const int col = static_cast<int>(blockIdx.x % a.slabs) * kCols + threadIdx.x;
     const int b = static_cast<int>(blockIdx.x / a.slabs);
     if (col >= a.ncol) return;
-    const int ch = 4 * col;
-    const int HK = a.H * DK;
-    const TIn *x;
-    int rs;
-    if (ch < HK) { x = static_cast<const TIn *>(a.xq) + ch; rs = HK; }
-    else if (ch < 2 * HK) { x = static_cast<const TIn *>(a.xk) + (ch - HK); rs = HK; }
-    else { x = static_cast<const TIn *>(a.xv) + (ch - 2 * HK); rs = a.H * a.dv; }
-    x += (static_cast<size_t>(b) * a.T + a.T - 3) * rs;
-    const float4 x3 = load4(x), x2 = load4(x + rs), x1 = load4(x + 2 * static_cast<size_t>(rs));
-    float *s = a.state_out + (static_cast<size_t>(b) * a.ncol * 4 + ch) * 3;
-    store4(s, make_float4(x3.x, x2.x, x1.x, x3.y));
-    store4(s + 4, make_float4(x2.y, x1.y, x3.z, x2.z));
-    store4(s + 8, make_float4(x1.z, x3.w, x2.w, x1.w));
+    const int ch = kCpt * col;
+    Route<TIn> r = route<DK, TIn>(a, ch);
+    const TIn *x = r.x + (static_cast<size_t>(b) * a.T + a.T - 3) * r.rs;
+    float x3[kCpt], x2[kCpt], x1[kCpt], s[3 * kCpt];
+    widen(load_raw(x), x3);
+    widen(load_raw(x + r.rs), x2);
+    widen(load_raw(x + 2 * static_cast<size_t>(r.rs)), x1);
+#pragma unroll
+    for (int j = 0; j < kCpt; ++j) { s[3 * j] = x3[j]; s[3 * j + 1] = x2[j]; s[3 * j + 2] = x1[j]; }
+    float *sp = a.state_out + (static_cast<size_t>(b) * a.C + ch) * 3;
+#pragma unroll
+    for (int i = 0; i < 3 * kCpt / 4; ++i)
+        reinterpret_cast<float4 *>(sp)[i] = make_float4(s[4 * i], s[4 * i + 1], s[4 * i + 2], s[4 * i + 3]);
 }
 
 template <int DK, typename TIn> hipError_t run(PrepArgs &a, hipStream_t stream) {
@@ -198,11 +270,19 @@ template <int DK, typename TIn> hipError_t run(PrepArgs &a, hipStream_t stream) 
     hipLaunchKernelGGL((prepare_kernel<DK, TIn>), dim3(grid), dim3(kCols), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.state_in_kernel || !a.state_out) return e;
-    hipLaunchKernelGGL((conv_state_tail_kernel<TIn>), dim3(a.slabs * a.B), dim3(kCols), 0, stream, a, DK);
+    hipLaunchKernelGGL((conv_state_tail_kernel<DK, TIn>), dim3(a.slabs * a.B), dim3(kCols), 0, stream, a);
     return hipGetLastError();
 }
 
 }  // namespace
+
+size_t prepare_grid_blocks(int B, int T, int H, int dk, int dv) {
+    const size_t ncol = static_cast<size_t>(H) * (2 * dk + dv) / kCpt;
+    const size_t slabs = (ncol + kCols - 1) / kCols;
+    const size_t tiles = T > 0 ? (static_cast<size_t>(T) + kTile - 1) / kTile : 1;
+    const size_t gates = (static_cast<size_t>(B) * T * H + kCols * kGateEl - 1) / (kCols * kGateEl);
+    return slabs * B * tiles + gates;
+}
 
 hipError_t launch_prepare(const void *xq, const void *xk, const void *xv, const float *w,
                           const float *a_raw, const float *b_raw, const float *rate,
@@ -215,12 +295,13 @@ hipError_t launch_prepare(const void *xq, const void *xk, const void *xv, const 
     a.state_in = state_in; a.state_out = state_out;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
     a.B = B; a.T = T; a.H = H; a.dv = dv;
-    a.ncol = H * (2 * dk + dv) / 4;
+    a.C = H * (2 * dk + dv);
+    a.ncol = a.C / kCpt;
     a.slabs = (a.ncol + kCols - 1) / kCols;
     a.tiles = T > 0 ? (T + kTile - 1) / kTile : 1;  // T = 0: one empty tile carries the state over
     const size_t conv = static_cast<size_t>(a.slabs) * B * a.tiles;
-    const size_t gates = (static_cast<size_t>(B) * T * H + kCols * kGateEl - 1) / (kCols * kGateEl);
-    if (conv + gates > 0x7fffffffULL - kXcd) return hipErrorInvalidValue;
+    const size_t gates = prepare_grid_blocks(B, T, H, dk, dv) - conv;
+    if (conv + gates > kMaxPrepareBlocks) return hipErrorInvalidValue;
     a.conv_blocks = static_cast<int>(conv);
     a.gate_blocks = static_cast<int>(gates);
     a.per_xcd = static_cast<int>((conv + gates + kXcd - 1) / kXcd);
