@@ -60,8 +60,9 @@ TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_prefill_1b_64k_dec
 
 
 def recorded_traffic(kind):
-    """Counter-measured HBM bytes for `kind` ('prefill' per call, 'decode' per step) from the
-    committed summary, or None when the kernel sources no longer match the recorded digest."""
+    """Counter-measured HBM bytes for `kind` ('prefill' and 'prepare' per 64K call, 'decode' per
+    step) from the committed summary, or None when the kernel sources no longer match the recorded
+    digest."""
     try:
         with open(TRAFFIC_SUMMARY) as f:
             fields = dict(line.strip().split(": ", 1) for line in f if line.strip().startswith(kind + "-"))
@@ -71,7 +72,7 @@ def recorded_traffic(kind):
                 d.update(src.read())
         if d.hexdigest() != fields[kind + "-source-sha256"]:
             return None
-        unit = "call" if kind == "prefill" else "step"
+        unit = "step" if kind == "decode" else "call"
         return int(fields[f"{kind}-traffic-bytes-per-{unit}"])
     except (OSError, KeyError, ValueError):
         return None
@@ -365,6 +366,7 @@ def main():
             "hbm_frac": round(prep_bytes / (prep_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "bytes_per_call": prep_bytes,
             "decode_us_avg": round(prep_dec_ms * 1e3, 2),
             "decode_GBps_algorithmic": round(prep_dec_bytes / (prep_dec_ms * 1e-3) / 1e9, 1),
+            "traffic_bytes_per_call": recorded_traffic("prepare"),
             "prepare_then_prefill_ms_avg": round(prep_chain_ms, 4),
             "prepare_then_prefill_tokens_per_s": round(w.B * w.T / (prep_chain_ms * 1e-3), 1),
             "note": "short causal convolution + SiLU + q/k L2 norm + gate activations on the 64K shape "
