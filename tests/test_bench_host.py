@@ -14,7 +14,11 @@ def test_traffic_is_none_once_a_source_changes(tmp_path, monkeypatch):
     csrc = tmp_path / "csrc"
     shutil.copytree(bench.CSRC, csrc)
     monkeypatch.setattr(bench, "CSRC", str(csrc))
-    before = {k: bench.recorded_traffic(k) for k in ("prefill", "decode")}
+    before = {k: bench.recorded_traffic(k) for k in ("prefill", "decode", "prepare")}
+    with open(csrc / "gdn_prepare.hip", "a") as f:
+        f.write("\n// edited\n")
+    assert bench.recorded_traffic("prepare") is None
+    assert before["prefill"] is None or bench.recorded_traffic("prefill") == before["prefill"]
     with open(csrc / "gdn_internal.h", "a") as f:
         f.write("\n// edited\n")
     assert bench.recorded_traffic("prefill") is None
