@@ -24,6 +24,9 @@ A second rule, ``rule=GATED_DECAY``, drops the erase term: S_t = a_t S_{t-1} + b
 (the uniform decay the Priming article attributes to Mamba-2).  ``closed_form_decay``
 (``oracle.brute``) evaluates it as explicit decayed sums, independently of the recurrence.
 
+``backward`` gives the gradients of L = sum_t <d_o_t, o_t> + <dS_T, S_T> by the token-by-token
+adjoint of the recurrence (C, fp64).
+
 States are stored key-major, ``[..., d_k, d_v]`` (element (j, i) = S[i][j]).
 """
 from __future__ import annotations
@@ -84,6 +87,9 @@ class Oracle:
         lib.gdn_oracle_decode_step_rule.argtypes = [i32, vp, vp, vp, i32, vp, vp, i32, dp, dp,
                                                     lg, lg, lg, lg]
         lib.gdn_oracle_decode_step_rule.restype = i32
+        lib.gdn_oracle_backward_rule.argtypes = [i32, vp, vp, vp, i32, vp, vp, i32, vp, i32, vp, vp, i32,
+                                                 dp, dp, dp, dp, dp, dp, lg, lg, lg, lg, lg]
+        lib.gdn_oracle_backward_rule.restype = i32
         lib.gdn_oracle_num_threads.argtypes = []
         lib.gdn_oracle_num_threads.restype = i32
         self.lib = lib
@@ -161,6 +167,48 @@ class Oracle:
         return o
 
 
+    def backward(self, q, k, v, g, beta, s0, d_o, ds_final=None, rule=GATED_DELTA):
+        """Gradients of L = sum_t <d_o_t, o_t> + <ds_final, S_T> for ``rule``, fp64, by the
+        token-by-token adjoint of the recurrence (states recomputed from checkpoints).
+
+        Shapes as ``prefill``; d_o [B,T,H,d_v]; ds_final [B,H,d_k,d_v] or None (zero), d_o and
+        ds_final in one storage type.  Returns a dict of fp64 arrays dq, dk [B,T,H,d_k],
+        dv [B,T,H,d_v], dg, dbeta [B,T,H], ds0 [B,H,d_k,d_v].
+        """
+        qa, qd = _as_array(q)
+        ka, kd = _as_array(k)
+        va, vd = _as_array(v)
+        if not (qd == kd == vd):
+            raise TypeError("oracle: q, k, v must share one storage type")
+        ga, gd = _as_array(g)
+        ba, bd = _as_array(beta)
+        if gd != bd:
+            raise TypeError("oracle: g and beta must share one storage type")
+        sa, sd = _as_array(s0)
+        oa, od = _as_array(d_o)
+        fa, fd = _as_array(ds_final)
+        if fa is not None and fd != od:
+            raise TypeError("oracle: d_o and ds_final must share one storage type")
+        B, T, H, dk = qa.shape
+        dv = va.shape[-1]
+        if oa.shape != (B, T, H, dv) or (fa is not None and fa.shape != (B, H, dk, dv)):
+            raise ValueError("oracle: gradient shape mismatch")
+        if sa is not None and sa.shape != (B, H, dk, dv):
+            raise ValueError("oracle: s0 shape mismatch")
+        out = {"dq": np.full((B, T, H, dk), np.nan), "dk": np.full((B, T, H, dk), np.nan),
+               "dv": np.full((B, T, H, dv), np.nan), "dg": np.full((B, T, H), np.nan),
+               "dbeta": np.full((B, T, H), np.nan), "ds0": np.full((B, H, dk, dv), np.nan)}
+        dp = ctypes.POINTER(ctypes.c_double)
+        rc = self.lib.gdn_oracle_backward_rule(rule, _ptr(qa), _ptr(ka), _ptr(va), qd, _ptr(ga), _ptr(ba), gd,
+                                               _ptr(sa), sd, _ptr(oa), _ptr(fa), od,
+                                               *[out[n].ctypes.data_as(dp) for n in ("dq", "dk", "dv", "dg",
+                                                                                     "dbeta", "ds0")],
+                                               B, T, H, dk, dv)
+        if rc != 0:
+            raise ValueError("oracle: gdn_oracle_backward rejected its arguments")
+        return out
+
+
 _default = None
 
 
@@ -181,9 +229,13 @@ def decode_step(*args, **kw):
     return default().decode_step(*args, **kw)
 
 
+def backward(*args, **kw):
+    return default().backward(*args, **kw)
+
+
 def num_threads() -> int:
     return default().num_threads()
 
 
-__all__ = ["Oracle", "default", "prefill", "decode_step", "brute_force", "closed_form_decay", "prep",
+__all__ = ["Oracle", "default", "prefill", "decode_step", "backward", "brute_force", "closed_form_decay", "prep",
            "num_threads", "build", "GATED_DELTA", "GATED_DECAY"]
