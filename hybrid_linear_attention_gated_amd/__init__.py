@@ -8,7 +8,8 @@ pointers passed as integers):
 
     gdn_chunk_prefill, gdn_chunk_prefill_rule, gdn_chunk_prefill_workspace_size,
     gdn_chunk_prefill_varlen, gdn_chunk_prefill_varlen_workspace_size, gdn_decode_step,
-    gdn_decode_step_rule, gdn_decode_step_slots, gdn_prepare, gdn_status_string, gdn_version
+    gdn_decode_step_rule, gdn_decode_step_slots, gdn_prepare, gdn_chunk_backward,
+    gdn_chunk_backward_workspace_size, gdn_status_string, gdn_version
 
 Tensor helpers that allocate outputs with torch and call the above on the
 current stream:
@@ -17,6 +18,7 @@ current stream:
     decode_step(q, k, v, g, beta, state) -> o        (state updated in place)
     decode_step_slots / chunk_prefill_varlen          (states in a pool, packed sequences)
     prepare(xq, xk, xv, conv_weight, a_raw, b_raw) -> (q, k, v, g, beta)
+    chunk_backward(q, k, v, g, beta, d_o, ...) -> (dq, dk, dv, dg, dbeta, d_initial_state)
 
 The rule computed (a gated delta rule; the pages describe the GDN layer in
 words only -- kwkr.cn digest of HyLo-Llama-8MLA8GDN-8K-SFT, architecture
@@ -40,7 +42,7 @@ STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_UNSUPP
 EXPORTS = ("gdn_chunk_prefill", "gdn_chunk_prefill_rule", "gdn_chunk_prefill_workspace_size",
            "gdn_chunk_prefill_varlen", "gdn_chunk_prefill_varlen_workspace_size",
            "gdn_decode_step", "gdn_decode_step_rule", "gdn_decode_step_slots", "gdn_prepare",
-           "gdn_status_string", "gdn_version")
+           "gdn_chunk_backward", "gdn_chunk_backward_workspace_size", "gdn_status_string", "gdn_version")
 
 
 class GdnError(RuntimeError):
@@ -82,6 +84,10 @@ def lib():
         L.gdn_chunk_prefill_varlen_workspace_size.restype = sz
         L.gdn_prepare.argtypes = [vp] * 15 + [i32] * 6 + [vp]
         L.gdn_prepare.restype = i32
+        L.gdn_chunk_backward.argtypes = [i32] + [vp] * 14 + [i32] * 6 + [vp, sz, vp]
+        L.gdn_chunk_backward.restype = i32
+        L.gdn_chunk_backward_workspace_size.argtypes = [i32] * 6
+        L.gdn_chunk_backward_workspace_size.restype = sz
         L.gdn_status_string.argtypes = [i32]
         L.gdn_status_string.restype = ctypes.c_char_p
         L.gdn_version.argtypes = []
@@ -139,6 +145,17 @@ def gdn_prepare(xq, xk, xv, conv_weight, a_raw, b_raw, decay_rate, gate_bias, co
                 conv_state_out, q, k, v, g, beta, B, T, H, d_k, d_v, x_dtype, stream) -> int:
     return lib().gdn_prepare(xq, xk, xv, conv_weight, a_raw, b_raw, decay_rate, gate_bias, conv_state_in,
                              conv_state_out, q, k, v, g, beta, B, T, H, d_k, d_v, x_dtype, stream)
+
+
+def gdn_chunk_backward(rule, q, k, v, g, beta, initial_state, d_o, d_final_state, dq, dk, dv, dg, dbeta,
+                       d_initial_state, B, T, H, d_k, d_v, qkv_dtype, workspace, workspace_bytes, stream) -> int:
+    return lib().gdn_chunk_backward(rule, q, k, v, g, beta, initial_state, d_o, d_final_state, dq, dk, dv, dg,
+                                    dbeta, d_initial_state, B, T, H, d_k, d_v, qkv_dtype, workspace,
+                                    workspace_bytes, stream)
+
+
+def gdn_chunk_backward_workspace_size(B, T, H, d_k, d_v, qkv_dtype) -> int:
+    return lib().gdn_chunk_backward_workspace_size(B, T, H, d_k, d_v, qkv_dtype)
 
 
 def gdn_status_string(status: int) -> str:
@@ -303,6 +320,46 @@ def prepare(xq, xk, xv, conv_weight, a_raw, b_raw, *, decay_rate=None, gate_bias
     return q, k, v, g, beta
 
 
+def chunk_backward(q, k, v, g, beta, d_o, initial_state=None, d_final_state=None, *, want_d_initial=True,
+                   outs=None, workspace=None, stream=None, rule=GDN_RULE_GATED_DELTA):
+    """Gradients of one prefill call for L = <d_o, o> + <d_final_state, S_T>.  Inputs as for
+    chunk_prefill (bf16 q/k/v, d_k = d_v = 64); d_o [B,T,H,d_v] fp32; d_final_state [B,H,d_k,d_v]
+    fp32 or None.  Returns (dq, dk, dv, dg, dbeta, d_initial_state or None), all fp32."""
+    import torch
+    B, T, H, d_k = q.shape
+    d_v = v.shape[-1]
+    dt = _dtype_code(q)
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, q.dtype)
+    for t, n in ((g, "g"), (beta, "beta"), (d_o, "d_o"), (initial_state, "initial_state"),
+                 (d_final_state, "d_final_state")):
+        _check(t, n, torch.float32)
+    dev = q.device
+    if outs is None:
+        f32 = dict(device=dev, dtype=torch.float32)
+        outs = (torch.empty((B, T, H, d_k), **f32), torch.empty((B, T, H, d_k), **f32),
+                torch.empty((B, T, H, d_v), **f32), torch.empty((B, T, H), **f32), torch.empty((B, T, H), **f32),
+                torch.empty((B, H, d_k, d_v), **f32) if want_d_initial else None)
+    for t, n in zip(outs, ("dq", "dk", "dv", "dg", "dbeta", "d_initial_state")):
+        _check(t, n, torch.float32)
+    need = int(gdn_chunk_backward_workspace_size(B, T, H, d_k, d_v, dt))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, device=dev, dtype=torch.uint8)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    st = gdn_chunk_backward(rule, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(d_o),
+                            _ptr(d_final_state), *[_ptr(t) for t in outs], B, T, H, d_k, d_v, dt,
+                            _ptr(workspace), ws_bytes, stream)
+    if st != 0:
+        raise GdnError(st, "gdn_chunk_backward")
+    return outs
+
+
+def backward_workspace_bytes(B, T, H, d_k, d_v, qkv_dtype) -> int:
+    return int(gdn_chunk_backward_workspace_size(B, T, H, d_k, d_v, qkv_dtype))
+
+
 def _host_i32(x):
     """A host int32 array (numpy) from a list, numpy array or CPU tensor, or None."""
     import numpy as np
@@ -369,4 +426,5 @@ __all__ = ["EXPORTS", "GDN_F32", "GDN_BF16", "GDN_RULE_GATED_DELTA", "GDN_RULE_G
            "gdn_decode_step", "gdn_decode_step_rule", "gdn_status_string", "gdn_version",
            "gdn_decode_step_slots", "gdn_chunk_prefill_varlen", "gdn_chunk_prefill_varlen_workspace_size",
            "chunk_prefill", "chunk_prefill_varlen", "decode_step", "decode_step_slots", "workspace_bytes",
-           "varlen_workspace_bytes", "gdn_prepare", "prepare"]
+           "varlen_workspace_bytes", "gdn_prepare", "prepare", "gdn_chunk_backward",
+           "gdn_chunk_backward_workspace_size", "chunk_backward", "backward_workspace_bytes"]

@@ -362,4 +362,58 @@ gdn_status gdn_prepare(const void *xq, const void *xk, const void *xv, const flo
     return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
+size_t gdn_chunk_backward_workspace_size(int B, int T, int H, int d_k, int d_v, gdn_dtype qkv_dtype) {
+    if (B <= 0 || H <= 0 || T < 0 || !backward_supported(d_k, d_v, qkv_dtype)) return 0;
+    if (prod({B, T, H, d_k}) == SIZE_MAX) return 0;
+    return backward_workspace(B, T, H, d_k, d_v);
+}
+
+gdn_status gdn_chunk_backward(gdn_rule rule, const void *q, const void *k, const void *v,
+                              const float *g, const float *beta, const float *initial_state,
+                              const float *d_o, const float *d_final_state, float *dq, float *dk,
+                              float *dv, float *dg, float *dbeta, float *d_initial_state, int B,
+                              int T, int H, int d_k, int d_v, gdn_dtype qkv_dtype, void *workspace,
+                              size_t workspace_bytes, void *stream) {
+    if (rule != GDN_RULE_GATED_DELTA && rule != GDN_RULE_GATED_DECAY) return GDN_ERR_UNSUPPORTED;
+    if (B <= 0 || H <= 0 || T < 0 || d_k <= 0 || d_v <= 0) return GDN_ERR_SHAPE;
+    if (qkv_dtype != GDN_F32 && qkv_dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+    if (!backward_supported(d_k, d_v, qkv_dtype)) return GDN_ERR_UNSUPPORTED;
+    if (prod({B, T, H, d_k}) == SIZE_MAX) return GDN_ERR_SHAPE;
+    const long long chunks = (static_cast<long long>(T) + backward_chunk() - 1) / backward_chunk();
+    if (static_cast<long long>(B) * H * (chunks > 0 ? chunks : 1) > 0x7fffff00LL) return GDN_ERR_SHAPE;
+    if (T > 0 && (!q || !k || !v || !g || !beta || !d_o || !dq || !dk || !dv || !dg || !dbeta))
+        return GDN_ERR_NULL;
+    const void *ptrs[] = {q, k, v, g, beta, initial_state, d_o, d_final_state, dq, dk, dv, dg, dbeta,
+                          d_initial_state, workspace};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return GDN_ERR_ALIGN;
+    const size_t need = backward_workspace(B, T, H, d_k, d_v);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return GDN_ERR_WORKSPACE;
+
+    const size_t es = elem_bytes(qkv_dtype);
+    const size_t nk = prod({B, T, H, d_k}), nv = prod({B, T, H, d_v}), ng = prod({B, T, H});
+    const size_t ns = prod({B, H, d_k, d_v}) * 4;
+    const Span in[] = {span(q, q ? nk * es : 0), span(k, k ? nk * es : 0), span(v, v ? nv * es : 0),
+                       span(g, g ? ng * 4 : 0), span(beta, beta ? ng * 4 : 0),
+                       span(initial_state, initial_state ? ns : 0), span(d_o, d_o ? nv * 4 : 0),
+                       span(d_final_state, d_final_state ? ns : 0)};
+    const Span out[] = {span(dq, dq ? nk * 4 : 0), span(dk, dk ? nk * 4 : 0), span(dv, dv ? nv * 4 : 0),
+                        span(dg, dg ? ng * 4 : 0), span(dbeta, dbeta ? ng * 4 : 0),
+                        span(d_initial_state, d_initial_state ? ns : 0),
+                        span(workspace, workspace ? need : 0)};
+    const int n_out = sizeof(out) / sizeof(out[0]);
+    for (int i = 0; i < n_out; ++i) {
+        for (int j = i + 1; j < n_out; ++j)
+            if (overlap(out[i], out[j])) return GDN_ERR_ALIAS;
+        for (const Span &x : in)
+            if (overlap(out[i], x)) return GDN_ERR_ALIAS;
+    }
+    if (T == 0 && !d_initial_state) return GDN_OK;
+    const hipError_t err = launch_backward(q, k, v, g, beta, initial_state, d_o, d_final_state, dq, dk, dv, dg,
+                                           dbeta, d_initial_state, B, T, H, d_k, d_v, qkv_dtype,
+                                           rule == GDN_RULE_GATED_DELTA, workspace,
+                                           static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
 }  // extern "C"

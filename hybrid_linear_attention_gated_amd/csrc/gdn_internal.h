@@ -60,10 +60,12 @@ hipError_t launch_prefill_bf16(const uint16_t *q, const uint16_t *k, const uint1
 size_t prefill_bf16_workspace(int B, int T, int H, int dk, int dv, int chunk);
 
 // bf16 inputs, fused chunk kernel with sequence pieces (gdn_prefill_chunk.hip).
+// chunk_states (optional): receives the state every chunk starts from, [B*H][N][dk][dv].
 hipError_t launch_prefill_chunk(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                 const float *g, const float *beta, const float *s0, float *o,
                                 float *s_out, int B, int T, int H, int dk, int dv, int chunk,
-                                bool delta, void *ws, hipStream_t stream);
+                                bool delta, void *ws, hipStream_t stream,
+                                float *chunk_states = nullptr);
 size_t prefill_chunk_workspace(int B, int T, int H, int dk, int dv, int chunk);
 
 // Packed variable-length sequences (bf16, MFMA shapes).  cu, slots and init are host
@@ -90,6 +92,17 @@ hipError_t launch_prepare(const void *xq, const void *xk, const void *xv, const 
                           const float *bias, const float *state_in, float *state_out, void *q,
                           void *k, void *v, float *g, float *beta, int B, int T, int H, int dk,
                           int dv, gdn_dtype dt, hipStream_t stream);
+
+// Gradients of the chunked prefill (gdn_backward.hip): a forward pass keeping chunk start
+// states, then per-chunk maps, a reverse scan of the state gradient and per-chunk gradients.
+bool backward_supported(int dk, int dv, gdn_dtype dt);
+int backward_chunk();
+size_t backward_workspace(int B, int T, int H, int dk, int dv);
+hipError_t launch_backward(const void *q, const void *k, const void *v, const float *g,
+                           const float *beta, const float *s0, const float *d_o,
+                           const float *ds_final, float *dq, float *dk, float *dv, float *dg,
+                           float *dbeta, float *ds0, int B, int T, int H, int d_k, int d_v,
+                           gdn_dtype dt, bool delta, void *ws, hipStream_t stream);
 
 // Copies (or zero-fills, when s0 == NULL) a start state into s_out.
 hipError_t launch_state_copy(const float *s0, float *s_out, size_t n, hipStream_t stream);

@@ -157,6 +157,7 @@ struct ChunkArgs {
     float *o;              // OUT: outputs
     float *s_final;        // OUT, dense: final states [BH][DK][DV], written by the last piece
     float *maps;           // MAP: dense [BH][P - 1] or packed [gm][H], each [DK][DV + DK]
+    float *chunk_states;   // OUT, dense: start state of every chunk [BH][N][DK][DV], or NULL
     int T, H, BH, P, piece_chunks, N;
     float scale;
     SeqTable sq;           // packed sequences when sq.tok0 != NULL (then work items = pieces * H)
@@ -290,6 +291,7 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
     const float *start = nullptr;     // OUT: start state [DK][DV] (NULL = zeros)
     float *map_out = nullptr;         // MAP: piece map [DK][DV + DK]
     float *final_out = nullptr;       // OUT: final state [DK][DV] of the sequence's last piece
+    float *states_out = nullptr;      // OUT, dense: this head's chunk start states [N][DK][DV]
     if (a.sq.tok0 == nullptr) {
         const int piece = w / a.BH;
         const size_t bh = w % a.BH;
@@ -302,6 +304,7 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
         if (MAP) map_out = a.maps + (bh * (a.P - 1) + piece) * DK * G::MAPW;
         else if (a.s_start) start = a.s_start + (bh * a.P + piece) * DK * DV;
         if (!MAP && piece == a.P - 1) final_out = a.s_final + bh * DK * DV;
+        if (!MAP && a.chunk_states) states_out = a.chunk_states + bh * a.N * DK * DV;
     } else {
         const int gp = w / a.H;  // global piece (OUT) or global map (MAP)
         h = w % a.H;
@@ -377,6 +380,16 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
     for (int n = n0; n < n1; ++n) {
         const int t0 = n * C;
         const int L = min(C, seq_len - t0);
+        if (!MAP && states_out) {  // the state this chunk starts from, kept for the gradients
+            float *cs = states_out + static_cast<size_t>(n) * DK * DV;
+#pragma unroll
+            for (int j = 0; j < G::SPW; ++j)
+#pragma unroll
+                for (int mt = 0; mt < G::KT; ++mt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        cs[(16 * mt + 4 * gq + r) * DV + 16 * (wave + kWaves * j) + li] = St[j][mt][r];
+        }
 
         // ---- A: this chunk's rows into LDS (K both row-major and transposed); gates
 #pragma unroll
@@ -1091,13 +1104,14 @@ size_t chunk_ws_bytes(int B, int T, int H) {
 template <int DK, int DV, int C, bool DELTA>
 hipError_t run_chunk(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,
                      const float *beta, const float *s0, float *o, float *s_out, int B, int T, int H,
-                     void *ws, hipStream_t stream) {
+                     void *ws, hipStream_t stream, float *chunk_states = nullptr) {
     const int N = (T + C - 1) / C;
     const int BH = B * H;
     const PiecePlan plan = piece_plan(BH, N);
     const int P = plan.P;
     ChunkArgs a{};
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.o = o; a.s_final = s_out;
+    a.chunk_states = chunk_states;
     a.T = T; a.H = H; a.BH = BH; a.P = P; a.N = N;
     a.sq = SeqTable{};
     auto grid = [](int items) { return dim3((items + kXcds - 1) / kXcds * kXcds); };
@@ -1255,11 +1269,13 @@ size_t prefill_chunk_workspace(int B, int T, int H, int dk, int dv, int chunk) {
 hipError_t launch_prefill_chunk(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                 const float *g, const float *beta, const float *s0, float *o,
                                 float *s_out, int B, int T, int H, int dk, int dv, int chunk,
-                                bool delta, void *ws, hipStream_t stream) {
+                                bool delta, void *ws, hipStream_t stream, float *chunk_states) {
 #define GDN_RUN(DK_, DV_, C_)                                                                      \
     if (dk == DK_ && dv == DV_ && chunk == C_)                                                     \
-        return delta ? run_chunk<DK_, DV_, C_, true>(q, k, v, g, beta, s0, o, s_out, B, T, H, ws, stream) \
-                     : run_chunk<DK_, DV_, C_, false>(q, k, v, g, beta, s0, o, s_out, B, T, H, ws, stream);
+        return delta ? run_chunk<DK_, DV_, C_, true>(q, k, v, g, beta, s0, o, s_out, B, T, H, ws, stream,  \
+                                                     chunk_states)                                         \
+                     : run_chunk<DK_, DV_, C_, false>(q, k, v, g, beta, s0, o, s_out, B, T, H, ws, stream, \
+                                                      chunk_states);
     GDN_CHUNK_CASES(GDN_RUN)
 #undef GDN_RUN
     return hipErrorInvalidValue;

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 3
+#define GDN_ABI_VERSION 4
 
 #if defined(__GNUC__) || defined(__clang__)
 #define GDN_API __attribute__((visibility("default")))
@@ -302,6 +302,49 @@ GDN_API gdn_status gdn_prepare(const void *xq, const void *xk, const void *xv,
                                void *q, void *k, void *v, float *g, float *beta,
                                int B, int T, int H, int d_k, int d_v,
                                gdn_dtype x_dtype, void *stream);
+
+/*
+ * gdn_chunk_backward -- gradients of gdn_chunk_prefill_rule (training of the GDN
+ * layers: the converted blocks are trained by layer-wise distillation and then
+ * end to end, ftxj.github.io digest of arXiv 2604.24715, Method; kwkr.cn digest
+ * of HyLo-Llama-8MLA8GDN-8K-SFT, training stages).
+ *
+ * For the loss L = sum_t <d_o_t, o_t> + <d_final_state, S_T> of one prefill
+ * call with the same inputs, writes dL/dq, dL/dk, dL/dv, dL/dg, dL/dbeta and
+ * dL/dS_0.  The forward pass is recomputed inside the call (nothing has to be
+ * kept from it), in chunks of 32 tokens.
+ *
+ *   q, k, v, g, beta, initial_state   as for gdn_chunk_prefill (initial_state
+ *                    NULL = zeros)
+ *   d_o              [B, T, H, d_v] fp32
+ *   d_final_state    [B, H, d_k, d_v] fp32, or NULL for zero
+ *   dq, dk           [B, T, H, d_k] fp32, written
+ *   dv               [B, T, H, d_v] fp32, written
+ *   dg, dbeta        [B, T, H] fp32, written
+ *   d_initial_state  [B, H, d_k, d_v] fp32, written, or NULL (not computed)
+ *   workspace        at least gdn_chunk_backward_workspace_size(...) bytes
+ * Supported: qkv_dtype GDN_BF16, d_k = d_v = 64; both rules.  T may be 0
+ * (then d_initial_state = d_final_state, or zeros).
+ * Errors: GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_UNSUPPORTED, GDN_ERR_ALIGN,
+ * GDN_ERR_ALIAS (an output overlapping an input, another output or the
+ * workspace), GDN_ERR_WORKSPACE, GDN_ERR_HIP.
+ */
+GDN_API gdn_status gdn_chunk_backward(gdn_rule rule,
+                             const void *q, const void *k, const void *v,
+                             const float *g, const float *beta,
+                             const float *initial_state,
+                             const float *d_o, const float *d_final_state,
+                             float *dq, float *dk, float *dv, float *dg, float *dbeta,
+                             float *d_initial_state,
+                             int B, int T, int H, int d_k, int d_v,
+                             gdn_dtype qkv_dtype,
+                             void *workspace, size_t workspace_bytes,
+                             void *stream);
+
+/* Workspace bytes gdn_chunk_backward needs (0 when the arguments would be
+ * rejected). */
+GDN_API size_t gdn_chunk_backward_workspace_size(int B, int T, int H, int d_k, int d_v,
+                                                 gdn_dtype qkv_dtype);
 
 /* Static, human-readable text for a status code (never NULL). */
 GDN_API const char *gdn_status_string(gdn_status status);

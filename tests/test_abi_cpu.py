@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     L = gdn.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert gdn.gdn_version() == 3
+    assert gdn.gdn_version() == 4
 
 
 def test_status_strings():
@@ -204,3 +204,33 @@ def test_prepare_nothing_to_do_is_a_no_op():
     # T = 0 with no state to carry: validated, nothing queued (no GPU needed)
     assert prepare_call(T=0, xq=None, xk=None, xv=None, a=None, b=None, q=None, k=None, v=None, g=None,
                         beta=None) == OK
+
+
+def backward_call(**kw):
+    args = dict(rule=0, q=addr(0), k=addr(1), v=addr(2), g=addr(3), beta=addr(4), s0=None, do=addr(5), dsf=None,
+                dq=addr(6), dk=addr(7), dv=addr(8), dg=addr(9), db=addr(10), ds0=None, B=1, T=8192, H=4, dk_=64,
+                dv_=64, dt=BF16, ws=addr(11, 1 << 34), ws_bytes=1 << 33, stream=None)
+    args.update(kw)
+    return gdn.gdn_chunk_backward(*[args[n] for n in ("rule", "q", "k", "v", "g", "beta", "s0", "do", "dsf", "dq",
+                                                      "dk", "dv", "dg", "db", "ds0", "B", "T", "H", "dk_", "dv_",
+                                                      "dt", "ws", "ws_bytes", "stream")])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(do=None), NULL), (dict(dbeta=None) if False else dict(db=None), NULL),
+    (dict(B=0), SHAPE), (dict(T=-1), SHAPE), (dict(rule=3), UNSUP), (dict(dk_=128), UNSUP), (dict(dt=F32), UNSUP),
+    (dict(dq=addr(6) + 4), ALIGN), (dict(ws=addr(11, 1 << 34) + 8), ALIGN),
+    (dict(dq=addr(0)), ALIAS), (dict(dk=addr(6) + 256), ALIAS), (dict(ds0=addr(3)), ALIAS),
+    (dict(dv=addr(11, 1 << 34)), ALIAS), (dict(ws=None), WS), (dict(ws_bytes=1024), WS),
+])
+def test_backward_rejects(kw, code):
+    assert backward_call(**kw) == code
+
+
+def test_backward_workspace_size():
+    assert gdn.gdn_chunk_backward_workspace_size(1, 8192, 4, 64, 64, BF16) > 4 * 256 * 64 * 64 * 4 * 4
+    assert gdn.gdn_chunk_backward_workspace_size(1, 8192, 4, 128, 128, BF16) == 0
+    assert gdn.gdn_chunk_backward_workspace_size(0, 8192, 4, 64, 64, BF16) == 0
+    # nothing to compute: T = 0 without an initial-state gradient is accepted without a GPU
+    assert backward_call(T=0, q=None, k=None, v=None, g=None, beta=None, do=None, dq=None, dk=None, dv=None,
+                         dg=None, db=None) == OK
