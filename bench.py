@@ -53,6 +53,12 @@ DECODE_BYTES_PER_SEQ_HEAD = 2 * 4 * 64 * 64 + 3 * 64 * 2 + 8 + 64 * 4
 # channel once per call: convolution weights (4 * 4) and, per sequence, the carried state read and
 # written (2 * 3 * 4)
 PREP_BYTES_PER_TOKEN_HEAD = 2 * 3 * 64 * 2 + 4 * 4
+# gradients (d_k = d_v = 64, chunks of 32 tokens), multiply-adds per chunk and head of the kernels'
+# products: keyside twice (P, K K^T, W: 3 C^2 d + C^3/6 = 202,411), map (X, R, F: C^2 d + 2 C d^2 =
+# 327,680), scan (d^3 = 262,144), gradients (Delta, K Y, dDelta, dP, dQ, dq, dW, T^T dW, T^T dDelta, dT,
+# dA, dK: 10 C^2 d + 5 C d^2 + 2 C^3 = 1,441,792); 2 FLOPs each, per token-head = / 32
+BWD_FLOPS_PER_TOKEN_HEAD = 2 * (2 * 202411 + 327680 + 262144 + 1441792) // 32
+FP32_VALU_PEAK_TFLOPS = 157.3
 COPY_BYTES = 4 << 30  # far larger than the 256 MB last-level cache
 FLUSH_BYTES = 1 << 30
 CSRC = os.path.join(ROOT, "hybrid_linear_attention_gated_amd", "csrc")
@@ -86,7 +92,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=65536,
                     help="tokens of the 64K workload the oracle is timed on")
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "copy", "prepare"], default="all",
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "copy", "prepare", "backward"], default="all",
                     help="run one component (for profiling); 'copy' runs a plain 4 GiB device copy "
                          "used to calibrate the HBM byte counters; the JSON line needs 'all'")
     args = ap.parse_args()
@@ -155,6 +161,33 @@ def main():
         gdn.prepare(din["xq"], din["xk"], din["xv"], din["conv_weight"], din["a_raw"], din["b_raw"],
                     decay_rate=din["decay_rate"], gate_bias=din["gate_bias"], conv_state=din["conv_state"],
                     conv_state_out=din["conv_state"])
+
+    # gradients of one prefill call on the training shape 1b_8k (B=4 H=32 T=8192 d=64)
+    bw = gi.WORKLOADS["1b_8k"]
+    bin_ = gi.workload_inputs("1b_8k", device=dev)
+    bdo = gi.draw_v((bw.B, bw.T, bw.H, bw.dv), gi.seed_of(bw.wid, 1, "v"), torch.float32, dev)
+    f32 = dict(device=dev, dtype=torch.float32)
+    bouts = (torch.empty((bw.B, bw.T, bw.H, bw.dk), **f32), torch.empty((bw.B, bw.T, bw.H, bw.dk), **f32),
+             torch.empty((bw.B, bw.T, bw.H, bw.dv), **f32), torch.empty((bw.B, bw.T, bw.H), **f32),
+             torch.empty((bw.B, bw.T, bw.H), **f32), torch.empty((bw.B, bw.H, bw.dk, bw.dv), **f32))
+    bws = torch.empty(max(gdn.backward_workspace_bytes(bw.B, bw.T, bw.H, bw.dk, bw.dv, gdn.GDN_BF16), 1),
+                      device=dev, dtype=torch.uint8)
+
+    def backward():
+        gdn.chunk_backward(bin_["q"], bin_["k"], bin_["v"], bin_["g"], bin_["beta"], bdo, None, None, outs=bouts,
+                           workspace=bws)
+
+    if args.only == "backward":
+        for _ in range(args.warmup):
+            backward()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            backward()
+        torch.cuda.synchronize()
+        print(json.dumps({"only": "backward", "steps": args.steps,
+                          "wall_ms": (time.perf_counter() - t0) * 1e3}), flush=True)
+        return
 
     if args.only == "prepare":
         for _ in range(args.warmup):
@@ -287,6 +320,18 @@ def main():
     prep_bytes = w.B * w.T * w.H * PREP_BYTES_PER_TOKEN_HEAD + conv_ch * (16 + 24 * w.B)
     prep_dec_bytes = dw.B * dw.H * PREP_BYTES_PER_TOKEN_HEAD + conv_ch * (16 + 24 * dw.B)
 
+    # backward on the training shape
+    for _ in range(args.warmup):
+        backward()
+    bw_ev = [(mk(), mk()) for _ in range(max(2, args.steps // 2))]
+    for a, b in bw_ev:
+        a.record(stream)
+        backward()
+        b.record(stream)
+    torch.cuda.synchronize()
+    bwd_ms = sum(a.elapsed_time(b) for a, b in bw_ev) / len(bw_ev)
+    bwd_flops = bw.B * bw.T * bw.H * BWD_FLOPS_PER_TOKEN_HEAD
+
     # decode with a cold last-level cache: read a 1 GiB buffer before each step, outside the
     # events (a read leaves only clean lines behind, so no write-back competes with the step)
     flush = torch.ones(FLUSH_BYTES // 4, device=dev, dtype=torch.float32)
@@ -371,6 +416,15 @@ def main():
             "prepare_then_prefill_tokens_per_s": round(w.B * w.T / (prep_chain_ms * 1e-3), 1),
             "note": "short causal convolution + SiLU + q/k L2 norm + gate activations on the 64K shape "
                     "(bf16 in and out) and on the 256-sequence decode batch (state in place)",
+        },
+        "backward": {
+            "workload": "1b_8k: B=4 H=32 T=8192 d_k=d_v=64, bf16 q/k/v, gated delta rule, zero start state",
+            "ms_avg": round(bwd_ms, 4), "tokens_per_s": round(bw.B * bw.T / (bwd_ms * 1e-3), 1),
+            "TFLOPs_fp32": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 2),
+            "alu_frac": round(bwd_flops / (bwd_ms * 1e-3) / 1e12 / FP32_VALU_PEAK_TFLOPS, 4),
+            "flops_per_call": bwd_flops,
+            "note": "forward recompute (keeps chunk start states) + per-chunk maps + reverse scan + per-chunk "
+                    "gradients, fp32 VALU; FLOPs are the gradient kernels' multiply-adds x 2",
         },
         "gated_decay_rule": {
             "prefill_ms_avg": round(decay_pre_ms, 4),

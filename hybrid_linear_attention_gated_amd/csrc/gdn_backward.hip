@@ -25,18 +25,28 @@
 //
 // Three launches after a forward pass that keeps every chunk's start state
 // (gdn_prefill_chunk.hip): bwd_map_kernel (F and R of every chunk, chunks in
-// parallel), bwd_scan_kernel (Y of every chunk, chunks in reverse order, 16
-// state columns per workgroup) and bwd_grad_kernel (all gradients, chunks in
-// parallel).  fp32 VALU arithmetic on LDS-resident chunk matrices.
+// parallel), bwd_scan_kernel (Y of every chunk, chunks in reverse order, one
+// workgroup per head) and bwd_grad_kernel (all gradients, chunks in
+// parallel).  fp32 arithmetic (matrix cores for the products) on LDS-resident chunk matrices.
 #include "gdn_internal.h"
 
 namespace gdn {
 namespace {
 
-constexpr int kBT = 256;          // threads per workgroup
+#ifndef GDN_BWD_THREADS
+#define GDN_BWD_THREADS 512
+#endif
+constexpr int kBT = 256;          // threads per workgroup (map, scan)
+constexpr int kBTG = GDN_BWD_THREADS;  // threads per gradient workgroup
 constexpr int kC = 32;            // tokens per chunk
-constexpr int kCP = kC + 1;       // padded C x C row
-constexpr int kSl = 16;           // state columns per scan workgroup
+#ifndef GDN_BWD_PAD_D
+#define GDN_BWD_PAD_D 1
+#endif
+#ifndef GDN_BWD_PAD_C
+#define GDN_BWD_PAD_C 1
+#endif
+constexpr int kPD = GDN_BWD_PAD_D;  // row padding of d-wide LDS matrices (floats)
+constexpr int kCP = kC + GDN_BWD_PAD_C;  // padded C x C row
 
 struct BwdArgs {
     const void *q, *k, *v;
@@ -50,36 +60,43 @@ struct BwdArgs {
     float scale;
 };
 
-// out(i, j) = sum_kk A(i, kk) B(kk, j) for i < M, j < N: thread (ti, tj) owns
-// column tj and rows ti + (kBT / N) x.
+// out(i, j) = sum_kk A(i, kk) B(kk, j) for i < M, j < N, on the fp32 matrix cores:
+// 16 x 16 output tiles dealt round-robin to the four wavefronts, each accumulated by
+// v_mfma_f32_16x16x4_f32 over K in steps of 4.  Lane l feeds A(i0 + l % 16, k0 + l / 16)
+// and B(k0 + l / 16, j0 + l % 16) and receives out(i0 + 4 (l / 16) + r, j0 + l % 16), r < 4.
 template <int M, int N, int K, class FA, class FB, class FS>
 __device__ __forceinline__ void mm(FA A, FB Bm, FS store) {
-    constexpr int NI = kBT / N;
-    constexpr int RI = M / NI;
-    static_assert(kBT % N == 0 && M % NI == 0, "tile");
-    const int tj = threadIdx.x % N, ti = threadIdx.x / N;
-    float acc[RI];
-#pragma unroll
-    for (int x = 0; x < RI; ++x) acc[x] = 0.f;
+    static_assert(M % 16 == 0 && N % 16 == 0 && K % 4 == 0, "tile");
+    constexpr int TN = N / 16, TILES = (M / 16) * TN;
+    const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+    const int li = lane % 16, lk = lane / 16;
+    const int waves = static_cast<int>(blockDim.x) / 64;
+    for (int t = wave; t < TILES; t += waves) {
+        const int i0 = (t / TN) * 16, j0 = (t % TN) * 16;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
-    for (int kk = 0; kk < K; ++kk) {
-        const float bv = Bm(kk, tj);
+        for (int k0 = 0; k0 < K; k0 += 4)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A(i0 + li, k0 + lk), Bm(k0 + lk, j0 + li), acc, 0, 0, 0);
 #pragma unroll
-        for (int x = 0; x < RI; ++x) acc[x] = fmaf(A(ti + NI * x, kk), bv, acc[x]);
+        for (int r = 0; r < 4; ++r) store(i0 + 4 * lk + r, j0 + li, acc[r]);
     }
-#pragma unroll
-    for (int x = 0; x < RI; ++x) store(ti + NI * x, tj, acc[x]);
+}
+
+// sum_kk A(i, kk) for i < M, by a product with a block of ones; store(i, x).
+template <int M, int K, class FA, class FS>
+__device__ __forceinline__ void rowsum(FA A, FS store) {
+    mm<M, 16, K>(A, [](int, int) { return 1.f; }, [&](int i, int j, float x) { if (j == 0) store(i, x); });
 }
 
 // One chunk's rows and its keyside matrices (shared by the map and gradient kernels).
 template <int DK, int DV> struct ChunkLds {
-    float q[kC][DK + 1], k[kC][DK + 1];
-    float dO[kC][DV + 1];
+    float q[kC][DK + kPD], k[kC][DK + kPD];
+    float dO[kC][DV + kPD];
     float T[kC][kCP];    // (I + A)^-1 (gated delta)
     float KG[kC][kCP];   // (k_r . k_j) Gam_rj, j < r
     float P[kC][kCP];    // (q_r . k_j) Gam_rj, j <= r
-    float W[kC][DK + 1];
-    float G[kC], gam[kC], eps[kC], b[kC];
+    float W[kC][DK + kPD];
+    float graw[kC], G[kC], gam[kC], eps[kC], b[kC];
 };
 
 // Loads q, k, dO, g, beta of chunk n of head bh (rows past the end read as zeros) and
@@ -92,26 +109,26 @@ __device__ void chunk_keyside(const BwdArgs &a, ChunkLds<DK, DV> &s, int bh, int
     L = min(kC, a.T - t0);
     tok = static_cast<size_t>(bb) * a.T + t0;
     const TIn *q = static_cast<const TIn *>(a.q), *k = static_cast<const TIn *>(a.k);
-    for (int e = tid; e < kC * DK; e += kBT) {
+    const int nt = blockDim.x;
+    for (int e = tid; e < kC * DK; e += nt) {
         const int r = e / DK, c = e % DK;
         const size_t i = ((tok + r) * a.H + h) * DK + c;
         s.q[r][c] = r < L ? load_in(q, i) : 0.f;
         s.k[r][c] = r < L ? load_in(k, i) : 0.f;
     }
-    for (int e = tid; e < kC * DV; e += kBT) {
+    for (int e = tid; e < kC * DV; e += nt) {
         const int r = e / DV, c = e % DV;
         s.dO[r][c] = r < L ? a.d_o[((tok + r) * a.H + h) * DV + c] : 0.f;
     }
     if (tid < kC) {
         const size_t i = (tok + tid) * a.H + h;
-        s.G[tid] = tid < L ? a.g[i] : 0.f;
+        s.graw[tid] = tid < L ? a.g[i] : 0.f;
         s.b[tid] = tid < L ? a.beta[i] : 0.f;
     }
     __syncthreads();
-    if (tid == 0) {
-        float acc = 0.f;
-        for (int r = 0; r < kC; ++r) { acc += s.G[r]; s.G[r] = acc; }
-    }
+    // G = (lower-triangular ones) g
+    mm<kC, 16, kC>([](int i, int j) { return j <= i ? 1.f : 0.f; }, [&](int j, int) { return s.graw[j]; },
+                   [&](int i, int c, float x) { if (c == 0) s.G[i] = x; });
     __syncthreads();
     if (tid < kC) {
         s.gam[tid] = expf(s.G[tid]);
@@ -151,7 +168,7 @@ __device__ void chunk_keyside(const BwdArgs &a, ChunkLds<DK, DV> &s, int bh, int
 template <int DK, int DV, typename TIn, bool DELTA>
 __global__ __launch_bounds__(kBT) void bwd_map_kernel(BwdArgs a) {
     __shared__ ChunkLds<DK, DV> s;
-    __shared__ float X[kC][DK + 1];  // diag(gam) Q - P W
+    __shared__ float X[kC][DK + kPD];  // diag(gam) Q - P W
     const int bh = blockIdx.x / a.N, n = blockIdx.x % a.N;
     size_t tok;
     int L;
@@ -177,85 +194,101 @@ __global__ __launch_bounds__(kBT) void bwd_map_kernel(BwdArgs a) {
     }
 }
 
-// ---- reverse scan: Y of every chunk, 16 state columns per workgroup --------------------
+// ---- reverse scan: Y of every chunk, one workgroup per head -------------------------
+// Y_{n-1} = F_n Y_n + R_n on the matrix cores: wavefront w owns rows 16 w .. 16 w + 15 of Y
+// (four 16 x 16 tiles).  Its rows of F_n and R_n are loaded into registers one chunk
+// ahead; within a block of 16 keys, lane group lk takes keys 4 lk .. 4 lk + 3 (a float4
+// of F) and Y is read from LDS with the same key order.
 template <int DK, int DV>
 __global__ __launch_bounds__(kBT) void bwd_scan_kernel(BwdArgs a) {
-    constexpr int RJ = DK * kSl / kBT;  // rows per thread
-    static_assert(RJ >= 1 && DK * kSl % kBT == 0, "scan tile");
-    __shared__ float Fb[2][DK][DK + 1];
-    __shared__ float Yb[2][DK][kSl + 1];
-    const int slices = DV / kSl;
-    const int bh = blockIdx.x / slices, c0 = (blockIdx.x % slices) * kSl;
-    const int tid = threadIdx.x, c = tid % kSl, j0 = tid / kSl;
-    constexpr int JS = kBT / kSl;  // row stride between a thread's rows
+    static_assert(DK == 64 && DV == 64, "one 16-row tile of Y per wavefront");
+    constexpr int YP = DV + 4;
+    __shared__ float Yb[2][DK][YP];
+    const int bh = blockIdx.x, tid = threadIdx.x;
+    const int lane = tid % 64, wave = tid / 64, li = lane % 16, lk = lane / 16, i0 = 16 * wave;
     const size_t head = static_cast<size_t>(bh) * a.N;
-
-    for (int x = 0; x < RJ; ++x) {
-        const int j = j0 + JS * x;
-        Yb[0][j][c] = a.ds_final ? a.ds_final[(static_cast<size_t>(bh) * DK + j) * DV + c0 + c] : 0.f;
-    }
+    for (int e = tid; e < DK * DV; e += kBT)
+        Yb[0][e / DV][e % DV] = a.ds_final ? a.ds_final[static_cast<size_t>(bh) * DK * DV + e] : 0.f;
+    float4 Fc[DK / 16], Fn[DK / 16];
+    f32x4 Rc[DV / 16], Rn[DV / 16];
+    auto load_f = [&](int n, float4 (&f)[DK / 16]) {
+        const float *F = a.F + (head + n) * DK * DK + (i0 + li) * DK + 4 * lk;
+#pragma unroll
+        for (int blk = 0; blk < DK / 16; ++blk) f[blk] = *reinterpret_cast<const float4 *>(F + 16 * blk);
+    };
+    auto load_r = [&](int n, f32x4 (&r)[DV / 16]) {
+        const float *R = a.R + (head + n) * DK * DV;
+#pragma unroll
+        for (int t = 0; t < DV / 16; ++t)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) r[t][q] = R[(i0 + 4 * lk + q) * DV + 16 * t + li];
+    };
     if (a.N > 0) {
-        const float *F = a.F + (head + a.N - 1) * DK * DK;
-        for (int e = tid; e < DK * DK; e += kBT) Fb[0][e / DK][e % DK] = F[e];
+        load_f(a.N - 1, Fc);
+        load_r(a.N - 1, Rc);
     }
     __syncthreads();
     for (int s = 0; s < a.N; ++s) {
         const int n = a.N - 1 - s, cur = s & 1;
-        constexpr int FPT = DK * DK / kBT;
-        float fn[FPT];
         if (n > 0) {
-            const float *F = a.F + (head + n - 1) * DK * DK;
-#pragma unroll
-            for (int i = 0; i < FPT; ++i) fn[i] = F[tid + kBT * i];
+            load_f(n - 1, Fn);
+            load_r(n - 1, Rn);
         }
-        const float *R = a.R + (head + n) * DK * DV;
-        float *Yo = a.Y + (head + n) * DK * DV;
-#pragma unroll
-        for (int x = 0; x < RJ; ++x) {
-            const int j = j0 + JS * x;
-            Yo[j * DV + c0 + c] = Yb[cur][j][c];
-            float acc = R[j * DV + c0 + c];
-#pragma unroll 8
-            for (int m = 0; m < DK; ++m) acc = fmaf(Fb[cur][j][m], Yb[cur][m][c], acc);
-            Yb[cur ^ 1][j][c] = acc;
+        float *Yo = a.Y + (head + n) * DK * DV;  // this chunk's Y, before the update
+        for (int e = lane; e < 16 * DV / 4; e += 64) {
+            const int row = i0 + e / (DV / 4), c4 = e % (DV / 4);
+            *reinterpret_cast<float4 *>(Yo + row * DV + 4 * c4) = *reinterpret_cast<const float4 *>(&Yb[cur][row][4 * c4]);
         }
-        if (n > 0) {
+        f32x4 acc[DV / 16];
 #pragma unroll
-            for (int i = 0; i < FPT; ++i) {
-                const int e = tid + kBT * i;
-                Fb[cur ^ 1][e / DK][e % DK] = fn[i];
-            }
+        for (int t = 0; t < DV / 16; ++t) acc[t] = Rc[t];
+#pragma unroll
+        for (int blk = 0; blk < DK / 16; ++blk) {
+            const float fa[4] = {Fc[blk].x, Fc[blk].y, Fc[blk].z, Fc[blk].w};
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int t = 0; t < DV / 16; ++t)
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[m], Yb[cur][16 * blk + 4 * lk + m][16 * t + li],
+                                                                  acc[t], 0, 0, 0);
         }
+#pragma unroll
+        for (int t = 0; t < DV / 16; ++t)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) Yb[cur ^ 1][i0 + 4 * lk + q][16 * t + li] = acc[t][q];
+#pragma unroll
+        for (int blk = 0; blk < DK / 16; ++blk) Fc[blk] = Fn[blk];
+#pragma unroll
+        for (int t = 0; t < DV / 16; ++t) Rc[t] = Rn[t];
         __syncthreads();
     }
     if (a.ds0) {
         const int fin = a.N & 1;
-        for (int x = 0; x < RJ; ++x) {
-            const int j = j0 + JS * x;
-            a.ds0[(static_cast<size_t>(bh) * DK + j) * DV + c0 + c] = Yb[fin][j][c];
-        }
+        for (int e = tid; e < DK * DV; e += kBT)
+            a.ds0[static_cast<size_t>(bh) * DK * DV + e] = Yb[fin][e / DV][e % DV];
     }
 }
 
 // ---- all gradients of one chunk -----------------------------------------------
 template <int DK, int DV> struct GradLds {
-    float v[kC][DV + 1];
-    float S[DK][DV + 1], Yv[DK][DV + 1];
-    float D[kC][DV + 1];     // Delta
-    float dD[kC][DV + 1];    // dDelta
-    float KY[kC][DV + 1];    // K Y, later dW (DV == DK)
-    float TdW[kC][DK + 1];   // T^T dW
-    float TdU[kC][DV + 1];   // T^T dDelta
+    float v[kC][DV + kPD];
+    float S[DK][DV + kPD], Yv[DK][DV + kPD];
+    float D[kC][DV + kPD];     // Delta
+    float dD[kC][DV + kPD];    // dDelta
+    float KY[kC][DV + kPD];    // K Y, later dW (DV == DK)
+    float TdW[kC][DK + kPD];   // T^T dW
+    float TdU[kC][DV + kPD];   // T^T dDelta
     float dPg[kC][kCP];      // dP .* Gam
     float X1[kC][kCP];       // dP .* P, later dA .* A
     float dT[kC][kCP];       // dT, later dA
     float Z[kC][kCP];        // dT T^T
-    float dG[kC], dbv[kC];   // dG[r]: written by thread r only
-    float dlast;             // gate terms of the chunk's last position, from many threads
+    float red[9][kC];        // per-row reductions, combined into dG and db
+    float red64[DK];         // row sums of Y .* S
+    float dG[kC], dbv[kC];
 };
 
 template <int DK, int DV, typename TIn, bool DELTA>
-__global__ __launch_bounds__(kBT) void bwd_grad_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kBTG) void bwd_grad_kernel(BwdArgs a) {
     static_assert(DK == DV, "the dW buffer reuses K Y's");
     __shared__ ChunkLds<DK, DV> s;
     __shared__ GradLds<DK, DV> u;
@@ -267,16 +300,16 @@ __global__ __launch_bounds__(kBT) void bwd_grad_kernel(BwdArgs a) {
     chunk_keyside<DK, DV, TIn, DELTA>(a, s, bh, n, tok, L);
     const size_t base = static_cast<size_t>(bh) * a.N + n;
     const TIn *vin = static_cast<const TIn *>(a.v);
-    for (int e = tid; e < kC * DV; e += kBT) {
+    for (int e = tid; e < kC * DV; e += kBTG) {
         const int r = e / DV, c = e % DV;
         u.v[r][c] = r < L ? load_in(vin, ((tok + r) * a.H + h) * DV + c) : 0.f;
     }
-    for (int e = tid; e < DK * DV; e += kBT) {
+    for (int e = tid; e < DK * DV; e += kBTG) {
         u.S[e / DV][e % DV] = a.states[base * DK * DV + e];
         u.Yv[e / DV][e % DV] = a.Y[base * DK * DV + e];
     }
-    if (tid < kC) { u.dG[tid] = 0.f; u.dbv[tid] = 0.f; }
-    if (tid == 0) u.dlast = 0.f;
+    if (tid < kC)
+        for (int m = 0; m < 9; ++m) u.red[m][tid] = 0.f;
     __syncthreads();
 
     // Delta = T diag(b) V - W S  (decay rule: diag(b) V);  K Y
@@ -284,7 +317,7 @@ __global__ __launch_bounds__(kBT) void bwd_grad_kernel(BwdArgs a) {
         mm<kC, DV, kC>([&](int i, int j) { return s.T[i][j]; }, [&](int j, int c) { return s.b[j] * u.v[j][c]; },
                        [&](int i, int c, float x) { u.D[i][c] = x; });
     } else {
-        for (int e = tid; e < kC * DV; e += kBT) u.D[e / DV][e % DV] = s.b[e / DV] * u.v[e / DV][e % DV];
+        for (int e = tid; e < kC * DV; e += kBTG) u.D[e / DV][e % DV] = s.b[e / DV] * u.v[e / DV][e % DV];
     }
     mm<kC, DV, DK>([&](int i, int j) { return s.k[i][j]; }, [&](int j, int c) { return u.Yv[j][c]; },
                    [&](int i, int c, float x) { u.KY[i][c] = x; });
@@ -304,31 +337,16 @@ __global__ __launch_bounds__(kBT) void bwd_grad_kernel(BwdArgs a) {
                        u.X1[r][j] = dp * s.P[r][j];
                    });
     __syncthreads();
-    // gate terms: readout decay, P, the end-state decay (eps and gam_last)
-    if (tid < kC) {
-        const int r = tid;
-        float rs = 0.f, cs = 0.f, e = 0.f;
-        for (int j = 0; j < kC; ++j) { rs += u.X1[r][j]; cs += u.X1[j][r]; }
-        for (int c = 0; c < DV; ++c) e = fmaf(u.KY[r][c], u.D[r][c], e);
-        e *= s.eps[r];
-        u.dG[r] += rs - cs - e;
-        atomicAdd(&u.dlast, e);
-    }
-    if (tid >= 64 && tid < 128) {  // gam_last <Y, S>: one wavefront
-        float x = 0.f;
-        for (int e = tid - 64; e < DK * DV; e += 64) x = fmaf(u.Yv[e / DV][e % DV], u.S[e / DV][e % DV], x);
-        for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
-        if (tid == 64) atomicAdd(&u.dlast, s.gam[kC - 1] * x);
-    }
+    // row reductions for the gate and write-strength gradients: P, the end-state decay
+    rowsum<kC, kC>([&](int i, int k) { return u.X1[i][k]; }, [&](int i, float x) { u.red[0][i] = x; });
+    rowsum<kC, kC>([&](int i, int k) { return u.X1[k][i]; }, [&](int i, float x) { u.red[1][i] = x; });
+    rowsum<kC, DV>([&](int i, int c) { return u.KY[i][c] * u.D[i][c]; }, [&](int i, float x) { u.red[2][i] = x; });
+    rowsum<DK, DV>([&](int j, int i) { return u.Yv[j][i] * u.S[j][i]; }, [&](int j, float x) { u.red64[j] = x; });
     // dQ = scale diag(gam) dO S^T (+ its gate term) + (dP .* Gam) K, into W's buffer
     mm<kC, DK, DV>([&](int r, int i) { return s.dO[r][i]; }, [&](int i, int c) { return u.S[c][i]; },
                    [&](int r, int c, float x) { s.W[r][c] = a.scale * s.gam[r] * x; });
     __syncthreads();
-    if (tid < kC) {
-        float x = 0.f;
-        for (int c = 0; c < DK; ++c) x = fmaf(s.q[tid][c], s.W[tid][c], x);
-        u.dG[tid] += x;
-    }
+    rowsum<kC, DK>([&](int i, int c) { return s.q[i][c] * s.W[i][c]; }, [&](int i, float x) { u.red[3][i] = x; });
     mm<kC, DK, kC>([&](int r, int j) { return u.dPg[r][j]; }, [&](int j, int c) { return s.k[j][c]; },
                    [&](int r, int c, float x) {
                        if (r < L) a.dq[((tok + r) * a.H + h) * DK + c] = s.W[r][c] + x;
@@ -350,6 +368,8 @@ __global__ __launch_bounds__(kBT) void bwd_grad_kernel(BwdArgs a) {
         __syncthreads();
         mm<kC, kC, DV>([&](int i, int c) { return u.dD[i][c]; }, [&](int c, int j) { return s.b[j] * u.v[j][c]; },
                        [&](int i, int j, float x) { u.dT[i][j] += x; });
+        rowsum<kC, DK>([&](int i, int c) { return u.TdW[i][c] * s.k[i][c]; }, [&](int i, float x) { u.red[7][i] = x; });
+        rowsum<kC, DV>([&](int i, int c) { return u.TdU[i][c] * u.v[i][c]; }, [&](int i, float x) { u.red[8][i] = x; });
         __syncthreads();
         // dA = -T^T (dT T^T), strictly lower
         mm<kC, kC, kC>([&](int i, int l) { return u.dT[i][l]; }, [&](int l, int j) { return s.T[j][l]; },
@@ -362,35 +382,39 @@ __global__ __launch_bounds__(kBT) void bwd_grad_kernel(BwdArgs a) {
                            u.X1[i][j] = da * s.b[i] * s.KG[i][j];  // dA .* A
                        });
         __syncthreads();
-        if (tid < kC) {
-            const int r = tid;
-            float rs = 0.f, cs = 0.f, dbA = 0.f, wk = 0.f, uv = 0.f;
-            for (int j = 0; j < kC; ++j) {
-                rs += u.X1[r][j];
-                cs += u.X1[j][r];
-                dbA = fmaf(u.dT[r][j], s.KG[r][j], dbA);
-            }
-            for (int c = 0; c < DK; ++c) wk = fmaf(u.TdW[r][c], s.k[r][c], wk);
-            for (int c = 0; c < DV; ++c) uv = fmaf(u.TdU[r][c], u.v[r][c], uv);
-            u.dG[r] += rs - cs + s.b[r] * s.gam[r] * wk;
-            u.dbv[r] = uv + s.gam[r] * wk + dbA;
-        }
+        rowsum<kC, kC>([&](int i, int k) { return u.X1[i][k]; }, [&](int i, float x) { u.red[4][i] = x; });
+        rowsum<kC, kC>([&](int i, int k) { return u.X1[k][i]; }, [&](int i, float x) { u.red[5][i] = x; });
+        rowsum<kC, kC>([&](int i, int k) { return u.dT[i][k] * s.KG[i][k]; }, [&](int i, float x) { u.red[6][i] = x; });
         // E = diag(b) dA .* Gam, kept in Z
-        for (int e = tid; e < kC * kC; e += kBT) {
+        for (int e = tid; e < kC * kC; e += kBTG) {
             const int i = e / kC, j = e % kC;
             u.Z[i][j] = j < i ? s.b[i] * u.dT[i][j] * expf(s.G[i] - s.G[j]) : 0.f;
         }
-        __syncthreads();
     } else {
+        rowsum<kC, DV>([&](int i, int c) { return u.dD[i][c] * u.v[i][c]; }, [&](int i, float x) { u.red[8][i] = x; });
+    }
+    __syncthreads();
+    // combine: dG per position, db, and the last position's end-state terms (one wavefront)
+    if (tid < 64) {
+        float last = s.gam[kC - 1] * u.red64[tid];
         if (tid < kC) {
-            float uv = 0.f;
-            for (int c = 0; c < DV; ++c) uv = fmaf(u.dD[tid][c], u.v[tid][c], uv);
-            u.dbv[tid] = uv;
+            const int r = tid;
+            const float e = s.eps[r] * u.red[2][r];
+            float dg = u.red[0][r] - u.red[1][r] - e + u.red[3][r];
+            float db = u.red[8][r];
+            if (DELTA) {
+                dg += u.red[4][r] - u.red[5][r] + s.b[r] * s.gam[r] * u.red[7][r];
+                db += s.gam[r] * u.red[7][r] + u.red[6][r];
+            }
+            u.dG[r] = dg;
+            u.dbv[r] = db;
+            last += e;
         }
-        __syncthreads();
+        for (int m = 32; m >= 1; m >>= 1) last += __shfl_xor(last, m);
+        if (tid == kC - 1) u.dG[kC - 1] += last;
     }
     // dV = diag(b) T^T dDelta (decay rule: diag(b) dDelta)
-    for (int e = tid; e < kC * DV; e += kBT) {
+    for (int e = tid; e < kC * DV; e += kBTG) {
         const int r = e / DV, c = e % DV;
         if (r < L) a.dv[((tok + r) * a.H + h) * DV + c] = s.b[r] * (DELTA ? u.TdU[r][c] : u.dD[r][c]);
     }
@@ -398,6 +422,10 @@ __global__ __launch_bounds__(kBT) void bwd_grad_kernel(BwdArgs a) {
     mm<kC, DK, kC>([&](int j, int r) { return u.dPg[r][j]; }, [&](int r, int c) { return s.q[r][c]; },
                    [&](int j, int c, float x) { s.W[j][c] = x; });
     __syncthreads();
+    // dg: reverse cumulative sum of dG inside the chunk (upper-triangular ones); dbeta
+    mm<kC, 16, kC>([](int i, int j) { return j >= i ? 1.f : 0.f; }, [&](int j, int) { return u.dG[j]; },
+                   [&](int i, int c, float x) { if (c == 0 && i < L) a.dg[(tok + i) * a.H + h] = x; });
+    if (tid < L) a.dbeta[(tok + tid) * a.H + h] = u.dbv[tid];
     mm<kC, DK, DV>([&](int j, int i) { return u.D[j][i]; }, [&](int i, int c) { return u.Yv[c][i]; },
                    [&](int j, int c, float x) { s.W[j][c] += s.eps[j] * x; });
     __syncthreads();
@@ -406,19 +434,10 @@ __global__ __launch_bounds__(kBT) void bwd_grad_kernel(BwdArgs a) {
                        [&](int i, int c, float x) { s.W[i][c] += x + s.b[i] * s.gam[i] * u.TdW[i][c]; });
         __syncthreads();
     }
-    for (int e = tid; e < kC * DK; e += kBT) {
+    for (int e = tid; e < kC * DK; e += kBTG) {
         const int r = e / DK, c = e % DK;
         if (r < L) a.dk[((tok + r) * a.H + h) * DK + c] = s.W[r][c];
     }
-    // dg: reverse cumulative sum of dG inside the chunk; dbeta
-    if (tid == 0) {
-        float acc = u.dlast;
-        for (int r = kC - 1; r >= 0; --r) {
-            acc += u.dG[r];
-            if (r < L) a.dg[(tok + r) * a.H + h] = acc;
-        }
-    }
-    if (tid < L) a.dbeta[(tok + tid) * a.H + h] = u.dbv[tid];
 }
 
 template <int DK, int DV, bool DELTA>
@@ -431,11 +450,11 @@ hipError_t run_backward(BwdArgs &a, gdn_dtype dt, hipStream_t stream) {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((bwd_scan_kernel<DK, DV>), dim3(a.BH * (DV / kSl)), dim3(kBT), 0, stream, a);
+    hipLaunchKernelGGL((bwd_scan_kernel<DK, DV>), dim3(a.BH), dim3(kBT), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || items == 0) return e;
-    if (bf) hipLaunchKernelGGL((bwd_grad_kernel<DK, DV, uint16_t, DELTA>), dim3(items), dim3(kBT), 0, stream, a);
-    else hipLaunchKernelGGL((bwd_grad_kernel<DK, DV, float, DELTA>), dim3(items), dim3(kBT), 0, stream, a);
+    if (bf) hipLaunchKernelGGL((bwd_grad_kernel<DK, DV, uint16_t, DELTA>), dim3(items), dim3(kBTG), 0, stream, a);
+    else hipLaunchKernelGGL((bwd_grad_kernel<DK, DV, float, DELTA>), dim3(items), dim3(kBTG), 0, stream, a);
     return hipGetLastError();
 }
 
