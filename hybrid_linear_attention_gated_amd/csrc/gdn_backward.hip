@@ -34,16 +34,24 @@ namespace gdn {
 namespace {
 
 #ifndef GDN_BWD_THREADS
-#define GDN_BWD_THREADS 512
+#define GDN_BWD_THREADS 1024
 #endif
-constexpr int kBT = 256;          // threads per workgroup (map, scan)
-constexpr int kBTG = GDN_BWD_THREADS;  // threads per gradient workgroup
+#ifndef GDN_BWD_MAP_THREADS
+#define GDN_BWD_MAP_THREADS 512
+#endif
+#ifndef GDN_BWD_SCAN_SLICES
+#define GDN_BWD_SCAN_SLICES 4
+#endif
+constexpr int kBT = 256;                   // threads per scan workgroup
+constexpr int kBTM = GDN_BWD_MAP_THREADS;  // threads per map workgroup
+constexpr int kBTG = GDN_BWD_THREADS;      // threads per gradient workgroup
+constexpr int kScanSlices = GDN_BWD_SCAN_SLICES;  // scan workgroups per head (column slices of Y)
 constexpr int kC = 32;            // tokens per chunk
 #ifndef GDN_BWD_PAD_D
-#define GDN_BWD_PAD_D 1
+#define GDN_BWD_PAD_D 2
 #endif
 #ifndef GDN_BWD_PAD_C
-#define GDN_BWD_PAD_C 1
+#define GDN_BWD_PAD_C 2
 #endif
 constexpr int kPD = GDN_BWD_PAD_D;  // row padding of d-wide LDS matrices (floats)
 constexpr int kCP = kC + GDN_BWD_PAD_C;  // padded C x C row
@@ -73,10 +81,15 @@ __device__ __forceinline__ void mm(FA A, FB Bm, FS store) {
     const int waves = static_cast<int>(blockDim.x) / 64;
     for (int t = wave; t < TILES; t += waves) {
         const int i0 = (t / TN) * 16, j0 = (t % TN) * 16;
+        float av[K / 4], bv[K / 4];  // the tile's operands, read before the first product
+#pragma unroll
+        for (int s = 0; s < K / 4; ++s) {
+            av[s] = A(i0 + li, 4 * s + lk);
+            bv[s] = Bm(4 * s + lk, j0 + li);
+        }
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-        for (int k0 = 0; k0 < K; k0 += 4)
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A(i0 + li, k0 + lk), Bm(k0 + lk, j0 + li), acc, 0, 0, 0);
+#pragma unroll
+        for (int s = 0; s < K / 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s], bv[s], acc, 0, 0, 0);
 #pragma unroll
         for (int r = 0; r < 4; ++r) store(i0 + 4 * lk + r, j0 + li, acc[r]);
     }
@@ -166,7 +179,7 @@ __device__ void chunk_keyside(const BwdArgs &a, ChunkLds<DK, DV> &s, int bh, int
 
 // ---- F and R of every chunk ---------------------------------------------------
 template <int DK, int DV, typename TIn, bool DELTA>
-__global__ __launch_bounds__(kBT) void bwd_map_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kBTM) void bwd_map_kernel(BwdArgs a) {
     __shared__ ChunkLds<DK, DV> s;
     __shared__ float X[kC][DK + kPD];  // diag(gam) Q - P W
     const int bh = blockIdx.x / a.N, n = blockIdx.x % a.N;
@@ -177,7 +190,7 @@ __global__ __launch_bounds__(kBT) void bwd_map_kernel(BwdArgs a) {
         mm<kC, DK, kC>([&](int i, int j) { return s.P[i][j]; }, [&](int j, int c) { return s.W[j][c]; },
                        [&](int i, int c, float x) { X[i][c] = s.gam[i] * s.q[i][c] - x; });
     } else {
-        for (int e = threadIdx.x; e < kC * DK; e += kBT) X[e / DK][e % DK] = s.gam[e / DK] * s.q[e / DK][e % DK];
+        for (int e = threadIdx.x; e < kC * DK; e += kBTM) X[e / DK][e % DK] = s.gam[e / DK] * s.q[e / DK][e % DK];
     }
     __syncthreads();
     const size_t base = static_cast<size_t>(bh) * a.N + n;
@@ -190,36 +203,38 @@ __global__ __launch_bounds__(kBT) void bwd_map_kernel(BwdArgs a) {
         mm<DK, DK, kC>([&](int j, int r) { return s.W[r][j]; }, [&](int r, int m) { return s.eps[r] * s.k[r][m]; },
                        [&](int j, int m, float x) { F[j * DK + m] = (j == m ? gl : 0.f) - x; });
     } else {
-        for (int e = threadIdx.x; e < DK * DK; e += kBT) F[e] = (e / DK == e % DK) ? gl : 0.f;
+        for (int e = threadIdx.x; e < DK * DK; e += kBTM) F[e] = (e / DK == e % DK) ? gl : 0.f;
     }
 }
 
 // ---- reverse scan: Y of every chunk, one workgroup per head -------------------------
-// Y_{n-1} = F_n Y_n + R_n on the matrix cores: wavefront w owns rows 16 w .. 16 w + 15 of Y
-// (four 16 x 16 tiles).  Its rows of F_n and R_n are loaded into registers one chunk
+// Y_{n-1} = F_n Y_n + R_n on the matrix cores, a head's columns of Y split over kScanSlices
+// workgroups: wavefront w owns rows 16 w .. 16 w + 15 of the workgroup's columns.  Its rows of F_n and R_n are loaded into registers one chunk
 // ahead; within a block of 16 keys, lane group lk takes keys 4 lk .. 4 lk + 3 (a float4
 // of F) and Y is read from LDS with the same key order.
 template <int DK, int DV>
 __global__ __launch_bounds__(kBT) void bwd_scan_kernel(BwdArgs a) {
-    static_assert(DK == 64 && DV == 64, "one 16-row tile of Y per wavefront");
-    constexpr int YP = DV + 4;
+    static_assert(DK == 64 && DV % (16 * kScanSlices) == 0, "one 16-row tile of Y per wavefront");
+    constexpr int SW = DV / kScanSlices;  // columns of Y this workgroup owns
+    constexpr int YP = SW + 4;
     __shared__ float Yb[2][DK][YP];
-    const int bh = blockIdx.x, tid = threadIdx.x;
+    const int bh = blockIdx.x / kScanSlices, c0 = (blockIdx.x % kScanSlices) * SW, tid = threadIdx.x;
     const int lane = tid % 64, wave = tid / 64, li = lane % 16, lk = lane / 16, i0 = 16 * wave;
     const size_t head = static_cast<size_t>(bh) * a.N;
-    for (int e = tid; e < DK * DV; e += kBT)
-        Yb[0][e / DV][e % DV] = a.ds_final ? a.ds_final[static_cast<size_t>(bh) * DK * DV + e] : 0.f;
+    for (int e = tid; e < DK * SW; e += kBT)
+        Yb[0][e / SW][e % SW] =
+            a.ds_final ? a.ds_final[static_cast<size_t>(bh) * DK * DV + (e / SW) * DV + c0 + e % SW] : 0.f;
     float4 Fc[DK / 16], Fn[DK / 16];
-    f32x4 Rc[DV / 16], Rn[DV / 16];
+    f32x4 Rc[SW / 16], Rn[SW / 16];
     auto load_f = [&](int n, float4 (&f)[DK / 16]) {
         const float *F = a.F + (head + n) * DK * DK + (i0 + li) * DK + 4 * lk;
 #pragma unroll
         for (int blk = 0; blk < DK / 16; ++blk) f[blk] = *reinterpret_cast<const float4 *>(F + 16 * blk);
     };
-    auto load_r = [&](int n, f32x4 (&r)[DV / 16]) {
-        const float *R = a.R + (head + n) * DK * DV;
+    auto load_r = [&](int n, f32x4 (&r)[SW / 16]) {
+        const float *R = a.R + (head + n) * DK * DV + c0;
 #pragma unroll
-        for (int t = 0; t < DV / 16; ++t)
+        for (int t = 0; t < SW / 16; ++t)
 #pragma unroll
             for (int q = 0; q < 4; ++q) r[t][q] = R[(i0 + 4 * lk + q) * DV + 16 * t + li];
     };
@@ -234,38 +249,38 @@ __global__ __launch_bounds__(kBT) void bwd_scan_kernel(BwdArgs a) {
             load_f(n - 1, Fn);
             load_r(n - 1, Rn);
         }
-        float *Yo = a.Y + (head + n) * DK * DV;  // this chunk's Y, before the update
-        for (int e = lane; e < 16 * DV / 4; e += 64) {
-            const int row = i0 + e / (DV / 4), c4 = e % (DV / 4);
+        float *Yo = a.Y + (head + n) * DK * DV + c0;  // this chunk's Y, before the update
+        for (int e = lane; e < 16 * SW / 4; e += 64) {
+            const int row = i0 + e / (SW / 4), c4 = e % (SW / 4);
             *reinterpret_cast<float4 *>(Yo + row * DV + 4 * c4) = *reinterpret_cast<const float4 *>(&Yb[cur][row][4 * c4]);
         }
-        f32x4 acc[DV / 16];
+        f32x4 acc[SW / 16];
 #pragma unroll
-        for (int t = 0; t < DV / 16; ++t) acc[t] = Rc[t];
+        for (int t = 0; t < SW / 16; ++t) acc[t] = Rc[t];
 #pragma unroll
         for (int blk = 0; blk < DK / 16; ++blk) {
             const float fa[4] = {Fc[blk].x, Fc[blk].y, Fc[blk].z, Fc[blk].w};
 #pragma unroll
             for (int m = 0; m < 4; ++m)
 #pragma unroll
-                for (int t = 0; t < DV / 16; ++t)
+                for (int t = 0; t < SW / 16; ++t)
                     acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[m], Yb[cur][16 * blk + 4 * lk + m][16 * t + li],
                                                                   acc[t], 0, 0, 0);
         }
 #pragma unroll
-        for (int t = 0; t < DV / 16; ++t)
+        for (int t = 0; t < SW / 16; ++t)
 #pragma unroll
             for (int q = 0; q < 4; ++q) Yb[cur ^ 1][i0 + 4 * lk + q][16 * t + li] = acc[t][q];
 #pragma unroll
         for (int blk = 0; blk < DK / 16; ++blk) Fc[blk] = Fn[blk];
 #pragma unroll
-        for (int t = 0; t < DV / 16; ++t) Rc[t] = Rn[t];
+        for (int t = 0; t < SW / 16; ++t) Rc[t] = Rn[t];
         __syncthreads();
     }
     if (a.ds0) {
         const int fin = a.N & 1;
-        for (int e = tid; e < DK * DV; e += kBT)
-            a.ds0[static_cast<size_t>(bh) * DK * DV + e] = Yb[fin][e / DV][e % DV];
+        for (int e = tid; e < DK * SW; e += kBT)
+            a.ds0[static_cast<size_t>(bh) * DK * DV + (e / SW) * DV + c0 + e % SW] = Yb[fin][e / SW][e % SW];
     }
 }
 
@@ -445,12 +460,12 @@ hipError_t run_backward(BwdArgs &a, gdn_dtype dt, hipStream_t stream) {
     const int items = a.BH * a.N;
     const bool bf = dt == GDN_BF16;
     if (items > 0) {
-        if (bf) hipLaunchKernelGGL((bwd_map_kernel<DK, DV, uint16_t, DELTA>), dim3(items), dim3(kBT), 0, stream, a);
-        else hipLaunchKernelGGL((bwd_map_kernel<DK, DV, float, DELTA>), dim3(items), dim3(kBT), 0, stream, a);
+        if (bf) hipLaunchKernelGGL((bwd_map_kernel<DK, DV, uint16_t, DELTA>), dim3(items), dim3(kBTM), 0, stream, a);
+        else hipLaunchKernelGGL((bwd_map_kernel<DK, DV, float, DELTA>), dim3(items), dim3(kBTM), 0, stream, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((bwd_scan_kernel<DK, DV>), dim3(a.BH), dim3(kBT), 0, stream, a);
+    hipLaunchKernelGGL((bwd_scan_kernel<DK, DV>), dim3(a.BH * kScanSlices), dim3(kBT), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || items == 0) return e;
     if (bf) hipLaunchKernelGGL((bwd_grad_kernel<DK, DV, uint16_t, DELTA>), dim3(items), dim3(kBTG), 0, stream, a);
