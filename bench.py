@@ -424,7 +424,8 @@ def main():
             "alu_frac": round(bwd_flops / (bwd_ms * 1e-3) / 1e12 / FP32_VALU_PEAK_TFLOPS, 4),
             "flops_per_call": bwd_flops,
             "note": "forward recompute (keeps chunk start states) + per-chunk maps + reverse scan + per-chunk "
-                    "gradients, fp32 VALU; FLOPs are the gradient kernels' multiply-adds x 2",
+                    "gradients, fp32 on the matrix cores; FLOPs are the gradient kernels' multiply-adds x 2, "
+                    "alu_frac against the fp32 peak",
         },
         "gated_decay_rule": {
             "prefill_ms_avg": round(decay_pre_ms, 4),

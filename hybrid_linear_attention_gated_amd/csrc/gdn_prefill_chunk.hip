@@ -249,7 +249,8 @@ constexpr int kBlocksPerCU = (DK == 64 && DV == 64) ? 2 : 1;
 // DELTA selects the rule: the gated delta rule (true) or the same recurrence without the
 // erase term (false), S_t = a_t S_{t-1} + b_t v_t k_t^T, whose chunk form has A = 0 and T = I:
 // Delta = diag(b) V with no W St term, and a piece map M_p that is a multiple of I.
-template <int DK, int DV, int C, bool MAP, bool DELTA>
+// STATES (OUT only): also write the state every chunk starts from (for the gradients).
+template <int DK, int DV, int C, bool MAP, bool DELTA, bool STATES = false>
 __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(ChunkArgs a) {
     using G = Cfg<DK, DV, C, MAP>;
     using R = ChunkRegs<DK, DV, C, MAP>;
@@ -304,7 +305,7 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
         if (MAP) map_out = a.maps + (bh * (a.P - 1) + piece) * DK * G::MAPW;
         else if (a.s_start) start = a.s_start + (bh * a.P + piece) * DK * DV;
         if (!MAP && piece == a.P - 1) final_out = a.s_final + bh * DK * DV;
-        if (!MAP && a.chunk_states) states_out = a.chunk_states + bh * a.N * DK * DV;
+        if (!MAP && STATES) states_out = a.chunk_states + bh * a.N * DK * DV;
     } else {
         const int gp = w / a.H;  // global piece (OUT) or global map (MAP)
         h = w % a.H;
@@ -380,7 +381,7 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
     for (int n = n0; n < n1; ++n) {
         const int t0 = n * C;
         const int L = min(C, seq_len - t0);
-        if (!MAP && states_out) {  // the state this chunk starts from, kept for the gradients
+        if (!MAP && STATES) {  // the state this chunk starts from, kept for the gradients
             float *cs = states_out + static_cast<size_t>(n) * DK * DV;
 #pragma unroll
             for (int j = 0; j < G::SPW; ++j)
@@ -1117,11 +1118,22 @@ hipError_t run_chunk(const uint16_t *q, const uint16_t *k, const uint16_t *v, co
     auto grid = [](int items) { return dim3((items + kXcds - 1) / kXcds * kXcds); };
     a.piece_chunks = plan.piece_chunks;
     a.scale = 1.0f / sqrtf(static_cast<float>(DK));
+    // the OUT pass, with chunk start states written only where the gradients need them
+    auto launch_out = [&](int items) {
+        if constexpr (DK == 64 && DV == 64 && C == 32) {
+            if (chunk_states) {
+                hipLaunchKernelGGL((chunk_kernel<DK, DV, C, false, DELTA, true>), grid(items), dim3(kBlock), 0, stream, a);
+                return hipGetLastError();
+            }
+        }
+        if (chunk_states) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((chunk_kernel<DK, DV, C, false, DELTA>), grid(items), dim3(kBlock), 0, stream, a);
+        return hipGetLastError();
+    };
     if (P == 1) {
         a.s_start = s0;
         a.items = BH;
-        hipLaunchKernelGGL((chunk_kernel<DK, DV, C, false, DELTA>), grid(BH), dim3(kBlock), 0, stream, a);
-        return hipGetLastError();
+        return launch_out(BH);
     }
     const size_t maps_bytes = static_cast<size_t>(BH) * (P - 1) * DK * (DV + DK) * 4;
     float *maps = static_cast<float *>(ws);
@@ -1138,8 +1150,7 @@ hipError_t run_chunk(const uint16_t *q, const uint16_t *k, const uint16_t *v, co
     if (err != hipSuccess) return err;
     a.s_start = starts;
     a.items = BH * P;
-    hipLaunchKernelGGL((chunk_kernel<DK, DV, C, false, DELTA>), grid(BH * P), dim3(kBlock), 0, stream, a);
-    return hipGetLastError();
+    return launch_out(BH * P);
 }
 
 template <int DK, int DV, int C, bool DELTA>
