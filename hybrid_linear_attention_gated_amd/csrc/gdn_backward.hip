@@ -69,16 +69,18 @@ struct BwdArgs {
 };
 
 // out(i, j) = sum_kk A(i, kk) B(kk, j) for i < M, j < N, on the fp32 matrix cores:
-// 16 x 16 output tiles dealt round-robin to the four wavefronts, each accumulated by
+// 16 x 16 output tiles dealt round-robin to wavefronts w0 .. w0 + nw - 1 (nw = 0: all of
+// the workgroup's), so independent products can run side by side; each tile accumulated by
 // v_mfma_f32_16x16x4_f32 over K in steps of 4.  Lane l feeds A(i0 + l % 16, k0 + l / 16)
 // and B(k0 + l / 16, j0 + l % 16) and receives out(i0 + 4 (l / 16) + r, j0 + l % 16), r < 4.
 template <int M, int N, int K, class FA, class FB, class FS>
-__device__ __forceinline__ void mm(FA A, FB Bm, FS store) {
+__device__ __forceinline__ void mm(FA A, FB Bm, FS store, int w0 = 0, int nw = 0) {
     static_assert(M % 16 == 0 && N % 16 == 0 && K % 4 == 0, "tile");
     constexpr int TN = N / 16, TILES = (M / 16) * TN;
-    const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+    const int lane = threadIdx.x % 64, wave = static_cast<int>(threadIdx.x / 64) - w0;
     const int li = lane % 16, lk = lane / 16;
-    const int waves = static_cast<int>(blockDim.x) / 64;
+    const int waves = nw > 0 ? nw : static_cast<int>(blockDim.x) / 64;
+    if (wave < 0 || wave >= waves) return;
     for (int t = wave; t < TILES; t += waves) {
         const int i0 = (t / TN) * 16, j0 = (t % TN) * 16;
         float av[K / 4], bv[K / 4];  // the tile's operands, read before the first product
@@ -97,8 +99,8 @@ __device__ __forceinline__ void mm(FA A, FB Bm, FS store) {
 
 // sum_kk A(i, kk) for i < M, by a product with a block of ones; store(i, x).
 template <int M, int K, class FA, class FS>
-__device__ __forceinline__ void rowsum(FA A, FS store) {
-    mm<M, 16, K>(A, [](int, int) { return 1.f; }, [&](int i, int j, float x) { if (j == 0) store(i, x); });
+__device__ __forceinline__ void rowsum(FA A, FS store, int w0 = 0, int nw = 0) {
+    mm<M, 16, K>(A, [](int, int) { return 1.f; }, [&](int i, int j, float x) { if (j == 0) store(i, x); }, w0, nw);
 }
 
 // One chunk's rows and its keyside matrices (shared by the map and gradient kernels).
@@ -148,11 +150,13 @@ __device__ void chunk_keyside(const BwdArgs &a, ChunkLds<DK, DV> &s, int bh, int
         s.eps[tid] = expf(s.G[kC - 1] - s.G[tid]);
     }
     // P and K K^T with the decay of every pair (exponents are <= 0 below the diagonal)
+    const int half = static_cast<int>(blockDim.x) / 128;  // wavefronts in each half of the workgroup
     mm<kC, kC, DK>([&](int i, int kk) { return s.q[i][kk]; }, [&](int kk, int j) { return s.k[j][kk]; },
-                   [&](int i, int j, float x) { s.P[i][j] = j <= i ? x * expf(s.G[i] - s.G[j]) : 0.f; });
+                   [&](int i, int j, float x) { s.P[i][j] = j <= i ? x * expf(s.G[i] - s.G[j]) : 0.f; }, 0, half);
     if (DELTA)
         mm<kC, kC, DK>([&](int i, int kk) { return s.k[i][kk]; }, [&](int kk, int j) { return s.k[j][kk]; },
-                       [&](int i, int j, float x) { s.KG[i][j] = j < i ? x * expf(s.G[i] - s.G[j]) : 0.f; });
+                       [&](int i, int j, float x) { s.KG[i][j] = j < i ? x * expf(s.G[i] - s.G[j]) : 0.f; },
+                       half, half);
     __syncthreads();
     if (!DELTA) return;
     // T = (I + diag(b) KG)^-1 by forward substitution, one column per thread
@@ -195,13 +199,14 @@ __global__ __launch_bounds__(kBTM) void bwd_map_kernel(BwdArgs a) {
     __syncthreads();
     const size_t base = static_cast<size_t>(bh) * a.N + n;
     float *R = a.R + base * DK * DV;
+    const int half = static_cast<int>(blockDim.x) / 128;
     mm<DK, DV, kC>([&](int j, int r) { return X[r][j]; }, [&](int r, int i) { return s.dO[r][i]; },
-                   [&](int j, int i, float x) { R[j * DV + i] = a.scale * x; });
+                   [&](int j, int i, float x) { R[j * DV + i] = a.scale * x; }, 0, half);
     float *F = a.F + base * DK * DK;
     const float gl = s.gam[kC - 1];
     if (DELTA) {
         mm<DK, DK, kC>([&](int j, int r) { return s.W[r][j]; }, [&](int r, int m) { return s.eps[r] * s.k[r][m]; },
-                       [&](int j, int m, float x) { F[j * DK + m] = (j == m ? gl : 0.f) - x; });
+                       [&](int j, int m, float x) { F[j * DK + m] = (j == m ? gl : 0.f) - x; }, half, half);
     } else {
         for (int e = threadIdx.x; e < DK * DK; e += kBTM) F[e] = (e / DK == e % DK) ? gl : 0.f;
     }
@@ -302,9 +307,12 @@ template <int DK, int DV> struct GradLds {
     float dG[kC], dbv[kC];
 };
 
+// Independent products of a phase run side by side on disjoint wavefronts of the 16
+// (ranges in the calls' last two arguments).
 template <int DK, int DV, typename TIn, bool DELTA>
 __global__ __launch_bounds__(kBTG) void bwd_grad_kernel(BwdArgs a) {
     static_assert(DK == DV, "the dW buffer reuses K Y's");
+    static_assert(kBTG == 1024, "the phases below are laid out for 16 wavefronts");
     __shared__ ChunkLds<DK, DV> s;
     __shared__ GradLds<DK, DV> u;
     const int tid = threadIdx.x;
@@ -330,12 +338,12 @@ __global__ __launch_bounds__(kBTG) void bwd_grad_kernel(BwdArgs a) {
     // Delta = T diag(b) V - W S  (decay rule: diag(b) V);  K Y
     if (DELTA) {
         mm<kC, DV, kC>([&](int i, int j) { return s.T[i][j]; }, [&](int j, int c) { return s.b[j] * u.v[j][c]; },
-                       [&](int i, int c, float x) { u.D[i][c] = x; });
+                       [&](int i, int c, float x) { u.D[i][c] = x; }, 0, 8);
     } else {
         for (int e = tid; e < kC * DV; e += kBTG) u.D[e / DV][e % DV] = s.b[e / DV] * u.v[e / DV][e % DV];
     }
     mm<kC, DV, DK>([&](int i, int j) { return s.k[i][j]; }, [&](int j, int c) { return u.Yv[j][c]; },
-                   [&](int i, int c, float x) { u.KY[i][c] = x; });
+                   [&](int i, int c, float x) { u.KY[i][c] = x; }, 8, 8);
     __syncthreads();
     if (DELTA) {
         mm<kC, DV, DK>([&](int i, int j) { return s.W[i][j]; }, [&](int j, int c) { return u.S[j][c]; },
@@ -344,47 +352,49 @@ __global__ __launch_bounds__(kBTG) void bwd_grad_kernel(BwdArgs a) {
     }
     // dDelta = scale P^T dO + diag(eps) K Y;  dP = scale tril(dO Delta^T)
     mm<kC, DV, kC>([&](int i, int r) { return s.P[r][i]; }, [&](int r, int c) { return s.dO[r][c]; },
-                   [&](int i, int c, float x) { u.dD[i][c] = a.scale * x + s.eps[i] * u.KY[i][c]; });
+                   [&](int i, int c, float x) { u.dD[i][c] = a.scale * x + s.eps[i] * u.KY[i][c]; }, 0, 8);
     mm<kC, kC, DV>([&](int r, int c) { return s.dO[r][c]; }, [&](int c, int j) { return u.D[j][c]; },
                    [&](int r, int j, float x) {
                        const float dp = j <= r ? a.scale * x : 0.f;
                        u.dPg[r][j] = dp * (j <= r ? expf(s.G[r] - s.G[j]) : 0.f);
                        u.X1[r][j] = dp * s.P[r][j];
-                   });
+                   },
+                   8, 8);
     __syncthreads();
     // row reductions for the gate and write-strength gradients: P, the end-state decay
-    rowsum<kC, kC>([&](int i, int k) { return u.X1[i][k]; }, [&](int i, float x) { u.red[0][i] = x; });
-    rowsum<kC, kC>([&](int i, int k) { return u.X1[k][i]; }, [&](int i, float x) { u.red[1][i] = x; });
-    rowsum<kC, DV>([&](int i, int c) { return u.KY[i][c] * u.D[i][c]; }, [&](int i, float x) { u.red[2][i] = x; });
-    rowsum<DK, DV>([&](int j, int i) { return u.Yv[j][i] * u.S[j][i]; }, [&](int j, float x) { u.red64[j] = x; });
+    rowsum<kC, kC>([&](int i, int k) { return u.X1[i][k]; }, [&](int i, float x) { u.red[0][i] = x; }, 8, 2);
+    rowsum<kC, kC>([&](int i, int k) { return u.X1[k][i]; }, [&](int i, float x) { u.red[1][i] = x; }, 10, 2);
+    rowsum<kC, DV>([&](int i, int c) { return u.KY[i][c] * u.D[i][c]; }, [&](int i, float x) { u.red[2][i] = x; }, 12, 2);
+    rowsum<DK, DV>([&](int j, int i) { return u.Yv[j][i] * u.S[j][i]; }, [&](int j, float x) { u.red64[j] = x; }, 14, 2);
     // dQ = scale diag(gam) dO S^T (+ its gate term) + (dP .* Gam) K, into W's buffer
     mm<kC, DK, DV>([&](int r, int i) { return s.dO[r][i]; }, [&](int i, int c) { return u.S[c][i]; },
-                   [&](int r, int c, float x) { s.W[r][c] = a.scale * s.gam[r] * x; });
+                   [&](int r, int c, float x) { s.W[r][c] = a.scale * s.gam[r] * x; }, 0, 8);
     __syncthreads();
-    rowsum<kC, DK>([&](int i, int c) { return s.q[i][c] * s.W[i][c]; }, [&](int i, float x) { u.red[3][i] = x; });
+    rowsum<kC, DK>([&](int i, int c) { return s.q[i][c] * s.W[i][c]; }, [&](int i, float x) { u.red[3][i] = x; }, 8, 2);
     mm<kC, DK, kC>([&](int r, int j) { return u.dPg[r][j]; }, [&](int j, int c) { return s.k[j][c]; },
                    [&](int r, int c, float x) {
                        if (r < L) a.dq[((tok + r) * a.H + h) * DK + c] = s.W[r][c] + x;
-                   });
+                   },
+                   0, 8);
     // dW = -dDelta S^T (into K Y's buffer), T^T dDelta
     __syncthreads();
     if (DELTA) {
         mm<kC, DK, DV>([&](int i, int l) { return u.dD[i][l]; }, [&](int l, int c) { return u.S[c][l]; },
-                       [&](int i, int c, float x) { u.KY[i][c] = -x; });
+                       [&](int i, int c, float x) { u.KY[i][c] = -x; }, 0, 8);
         mm<kC, DV, kC>([&](int j, int i) { return s.T[i][j]; }, [&](int i, int c) { return u.dD[i][c]; },
-                       [&](int j, int c, float x) { u.TdU[j][c] = x; });
+                       [&](int j, int c, float x) { u.TdU[j][c] = x; }, 8, 8);
         __syncthreads();
         mm<kC, DK, kC>([&](int j, int i) { return s.T[i][j]; }, [&](int i, int c) { return u.KY[i][c]; },
-                       [&](int j, int c, float x) { u.TdW[j][c] = x; });
+                       [&](int j, int c, float x) { u.TdW[j][c] = x; }, 0, 8);
         // dT = dW (diag(b gam) K)^T + dDelta (diag(b) V)^T
         mm<kC, kC, DK>([&](int i, int c) { return u.KY[i][c]; },
                        [&](int c, int j) { return s.b[j] * s.gam[j] * s.k[j][c]; },
-                       [&](int i, int j, float x) { u.dT[i][j] = x; });
+                       [&](int i, int j, float x) { u.dT[i][j] = x; }, 8, 4);
         __syncthreads();
         mm<kC, kC, DV>([&](int i, int c) { return u.dD[i][c]; }, [&](int c, int j) { return s.b[j] * u.v[j][c]; },
-                       [&](int i, int j, float x) { u.dT[i][j] += x; });
-        rowsum<kC, DK>([&](int i, int c) { return u.TdW[i][c] * s.k[i][c]; }, [&](int i, float x) { u.red[7][i] = x; });
-        rowsum<kC, DV>([&](int i, int c) { return u.TdU[i][c] * u.v[i][c]; }, [&](int i, float x) { u.red[8][i] = x; });
+                       [&](int i, int j, float x) { u.dT[i][j] += x; }, 0, 4);
+        rowsum<kC, DK>([&](int i, int c) { return u.TdW[i][c] * s.k[i][c]; }, [&](int i, float x) { u.red[7][i] = x; }, 4, 2);
+        rowsum<kC, DV>([&](int i, int c) { return u.TdU[i][c] * u.v[i][c]; }, [&](int i, float x) { u.red[8][i] = x; }, 6, 2);
         __syncthreads();
         // dA = -T^T (dT T^T), strictly lower
         mm<kC, kC, kC>([&](int i, int l) { return u.dT[i][l]; }, [&](int l, int j) { return s.T[j][l]; },
@@ -397,16 +407,16 @@ __global__ __launch_bounds__(kBTG) void bwd_grad_kernel(BwdArgs a) {
                            u.X1[i][j] = da * s.b[i] * s.KG[i][j];  // dA .* A
                        });
         __syncthreads();
-        rowsum<kC, kC>([&](int i, int k) { return u.X1[i][k]; }, [&](int i, float x) { u.red[4][i] = x; });
-        rowsum<kC, kC>([&](int i, int k) { return u.X1[k][i]; }, [&](int i, float x) { u.red[5][i] = x; });
-        rowsum<kC, kC>([&](int i, int k) { return u.dT[i][k] * s.KG[i][k]; }, [&](int i, float x) { u.red[6][i] = x; });
+        rowsum<kC, kC>([&](int i, int k) { return u.X1[i][k]; }, [&](int i, float x) { u.red[4][i] = x; }, 0, 2);
+        rowsum<kC, kC>([&](int i, int k) { return u.X1[k][i]; }, [&](int i, float x) { u.red[5][i] = x; }, 2, 2);
+        rowsum<kC, kC>([&](int i, int k) { return u.dT[i][k] * s.KG[i][k]; }, [&](int i, float x) { u.red[6][i] = x; }, 4, 2);
         // E = diag(b) dA .* Gam, kept in Z
         for (int e = tid; e < kC * kC; e += kBTG) {
             const int i = e / kC, j = e % kC;
             u.Z[i][j] = j < i ? s.b[i] * u.dT[i][j] * expf(s.G[i] - s.G[j]) : 0.f;
         }
     } else {
-        rowsum<kC, DV>([&](int i, int c) { return u.dD[i][c] * u.v[i][c]; }, [&](int i, float x) { u.red[8][i] = x; });
+        rowsum<kC, DV>([&](int i, int c) { return u.dD[i][c] * u.v[i][c]; }, [&](int i, float x) { u.red[8][i] = x; }, 6, 2);
     }
     __syncthreads();
     // combine: dG per position, db, and the last position's end-state terms (one wavefront)
@@ -435,18 +445,18 @@ __global__ __launch_bounds__(kBTG) void bwd_grad_kernel(BwdArgs a) {
     }
     // dK = (dP .* Gam)^T Q + diag(eps) Delta Y^T [+ diag(b gam) T^T dW + E K + E^T K]
     mm<kC, DK, kC>([&](int j, int r) { return u.dPg[r][j]; }, [&](int r, int c) { return s.q[r][c]; },
-                   [&](int j, int c, float x) { s.W[j][c] = x; });
+                   [&](int j, int c, float x) { s.W[j][c] = x; }, 8, 8);
     __syncthreads();
     // dg: reverse cumulative sum of dG inside the chunk (upper-triangular ones); dbeta
     mm<kC, 16, kC>([](int i, int j) { return j >= i ? 1.f : 0.f; }, [&](int j, int) { return u.dG[j]; },
-                   [&](int i, int c, float x) { if (c == 0 && i < L) a.dg[(tok + i) * a.H + h] = x; });
+                   [&](int i, int c, float x) { if (c == 0 && i < L) a.dg[(tok + i) * a.H + h] = x; }, 0, 2);
     if (tid < L) a.dbeta[(tok + tid) * a.H + h] = u.dbv[tid];
     mm<kC, DK, DV>([&](int j, int i) { return u.D[j][i]; }, [&](int i, int c) { return u.Yv[c][i]; },
-                   [&](int j, int c, float x) { s.W[j][c] += s.eps[j] * x; });
+                   [&](int j, int c, float x) { s.W[j][c] += s.eps[j] * x; }, 8, 8);
     __syncthreads();
     if (DELTA) {
         mm<kC, DK, kC>([&](int i, int j) { return u.Z[i][j] + u.Z[j][i]; }, [&](int j, int c) { return s.k[j][c]; },
-                       [&](int i, int c, float x) { s.W[i][c] += x + s.b[i] * s.gam[i] * u.TdW[i][c]; });
+                       [&](int i, int c, float x) { s.W[i][c] += x + s.b[i] * s.gam[i] * u.TdW[i][c]; }, 8, 8);
         __syncthreads();
     }
     for (int e = tid; e < kC * DK; e += kBTG) {
