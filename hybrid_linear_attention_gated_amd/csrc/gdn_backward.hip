@@ -505,7 +505,9 @@ BwdLayout bwd_layout(int B, int T, int H, int dk, int dv) {
 
 }  // namespace
 
-bool backward_supported(int dk, int dv, gdn_dtype dt) { return dk == 64 && dv == 64 && dt == GDN_BF16; }
+bool backward_supported(int dk, int dv, gdn_dtype dt) {
+    return dk == 64 && dv == 64 && (dt == GDN_BF16 || dt == GDN_F32);
+}
 
 int backward_chunk() { return kC; }
 
@@ -528,7 +530,13 @@ hipError_t launch_backward(const void *q, const void *k, const void *v, const fl
     a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.ds0 = ds0;
     a.T = T; a.H = H; a.BH = B * H; a.N = (T + kC - 1) / kC;
     a.scale = 1.0f / sqrtf(static_cast<float>(d_k));
-    if (T > 0) {
+    if (T > 0 && dt == GDN_F32) {
+        // fp32 q/k/v: the fp32 chunk kernel, again keeping every chunk's start state
+        hipError_t e = launch_prefill_valu(q, k, v, g, beta, s0, reinterpret_cast<float *>(w + L.o),
+                                           reinterpret_cast<float *>(w + L.sfin), B, T, H, d_k, d_v, kC, dt, delta,
+                                           stream, reinterpret_cast<float *>(w + L.states));
+        if (e != hipSuccess) return e;
+    } else if (T > 0) {
         // forward pass again, keeping the state every chunk starts from
         hipError_t e = launch_prefill_chunk(static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
                                             static_cast<const uint16_t *>(v), g, beta, s0,

@@ -46,10 +46,11 @@ hipError_t launch_decode(const void *q, const void *k, const void *v, const floa
 
 // Chunked prefill with fp32 VALU arithmetic (fp32 inputs, and bf16 inputs at
 // sizes the MFMA path does not tile).  Needs no workspace.
+// chunk_states (optional): receives the state every chunk starts from, [B*H][N][dk][dv].
 hipError_t launch_prefill_valu(const void *q, const void *k, const void *v, const float *g,
                                const float *beta, const float *s0, float *o, float *s_out, int B,
                                int T, int H, int dk, int dv, int chunk, gdn_dtype dt,
-                               bool delta, hipStream_t stream);
+                               bool delta, hipStream_t stream, float *chunk_states = nullptr);
 
 // bf16 inputs: chunked prefill with bf16 MFMA contractions.
 bool prefill_bf16_uses_mfma(int dk, int dv, int chunk);

@@ -37,7 +37,8 @@ template <int DK, int C, typename TIn, bool DELTA>
 __global__ __launch_bounds__(kThreads) void prefill_valu_kernel(
     const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, const float *__restrict__ s0,
-    float *__restrict__ o, float *__restrict__ s_out, int T, int H, int DV, float scale) {
+    float *__restrict__ o, float *__restrict__ s_out, float *__restrict__ chunk_states, int T, int H,
+    int DV, float scale) {
     __shared__ float A[C][C + 1];   // A, then the intra-chunk output weights P
     __shared__ float Tm[C][C + 1];  // (I + A)^{-1}
     __shared__ float St[DK][kSW];
@@ -61,6 +62,10 @@ __global__ __launch_bounds__(kThreads) void prefill_valu_kernel(
 
     for (int t0 = 0; t0 < T; t0 += C) {
         const int L = min(C, T - t0);
+        if (chunk_states) {  // the state this chunk starts from, kept for the gradients
+            float *cs = chunk_states + (bh * ((T + C - 1) / C) + t0 / C) * DK * DV;
+            for (int e = tid; e < DK * kSW; e += kThreads) cs[(e / kSW) * DV + col0 + e % kSW] = St[e / kSW][e % kSW];
+        }
         // rows of token t of this (b, h): index (b*T + t)*H + h
         auto row = [&](int r) { return (static_cast<size_t>(b) * T + t0 + r) * H + h; };
 
@@ -164,28 +169,29 @@ __global__ __launch_bounds__(kThreads) void prefill_valu_kernel(
 
 template <int DK, int C, typename TIn>
 hipError_t launch_valu_t(const void *q, const void *k, const void *v, const float *g,
-                         const float *beta, const float *s0, float *o, float *s_out, int B, int T,
-                         int H, int dv, bool delta, hipStream_t stream) {
+                         const float *beta, const float *s0, float *o, float *s_out, float *chunk_states,
+                         int B, int T, int H, int dv, bool delta, hipStream_t stream) {
     const int blocks = B * H * (dv / kSW);
     const float scale = 1.0f / sqrtf(static_cast<float>(DK));
     if (delta)
         hipLaunchKernelGGL((prefill_valu_kernel<DK, C, TIn, true>), dim3(blocks), dim3(kThreads), 0,
                            stream, static_cast<const TIn *>(q), static_cast<const TIn *>(k),
-                           static_cast<const TIn *>(v), g, beta, s0, o, s_out, T, H, dv, scale);
+                           static_cast<const TIn *>(v), g, beta, s0, o, s_out, chunk_states, T, H, dv, scale);
     else
         hipLaunchKernelGGL((prefill_valu_kernel<DK, C, TIn, false>), dim3(blocks), dim3(kThreads), 0,
                            stream, static_cast<const TIn *>(q), static_cast<const TIn *>(k),
-                           static_cast<const TIn *>(v), g, beta, s0, o, s_out, T, H, dv, scale);
+                           static_cast<const TIn *>(v), g, beta, s0, o, s_out, chunk_states, T, H, dv, scale);
     return hipGetLastError();
 }
 
 template <typename TIn>
 hipError_t dispatch_valu(const void *q, const void *k, const void *v, const float *g,
-                         const float *beta, const float *s0, float *o, float *s_out, int B, int T,
-                         int H, int dk, int dv, int chunk, bool delta, hipStream_t stream) {
+                         const float *beta, const float *s0, float *o, float *s_out, float *chunk_states,
+                         int B, int T, int H, int dk, int dv, int chunk, bool delta, hipStream_t stream) {
 #define GDN_VALU(DK_, C_)                                                                         \
     if (dk == DK_ && chunk == C_)                                                                 \
-        return launch_valu_t<DK_, C_, TIn>(q, k, v, g, beta, s0, o, s_out, B, T, H, dv, delta, stream);
+        return launch_valu_t<DK_, C_, TIn>(q, k, v, g, beta, s0, o, s_out, chunk_states, B, T, H, dv, delta, \
+                                           stream);
     GDN_VALU(16, 16) GDN_VALU(16, 32) GDN_VALU(16, 64)
     GDN_VALU(64, 16) GDN_VALU(64, 32) GDN_VALU(64, 64)
     GDN_VALU(128, 16) GDN_VALU(128, 32) GDN_VALU(128, 64)
@@ -198,11 +204,12 @@ hipError_t dispatch_valu(const void *q, const void *k, const void *v, const floa
 hipError_t launch_prefill_valu(const void *q, const void *k, const void *v, const float *g,
                                const float *beta, const float *s0, float *o, float *s_out, int B,
                                int T, int H, int dk, int dv, int chunk, gdn_dtype dt,
-                               bool delta, hipStream_t stream) {
+                               bool delta, hipStream_t stream, float *chunk_states) {
     if (dt == GDN_BF16)
-        return dispatch_valu<uint16_t>(q, k, v, g, beta, s0, o, s_out, B, T, H, dk, dv, chunk, delta,
-                                       stream);
-    return dispatch_valu<float>(q, k, v, g, beta, s0, o, s_out, B, T, H, dk, dv, chunk, delta, stream);
+        return dispatch_valu<uint16_t>(q, k, v, g, beta, s0, o, s_out, chunk_states, B, T, H, dk, dv, chunk,
+                                       delta, stream);
+    return dispatch_valu<float>(q, k, v, g, beta, s0, o, s_out, chunk_states, B, T, H, dk, dv, chunk, delta,
+                                stream);
 }
 
 }  // namespace gdn

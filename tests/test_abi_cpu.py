@@ -218,7 +218,7 @@ def backward_call(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), NULL), (dict(do=None), NULL), (dict(dbeta=None) if False else dict(db=None), NULL),
-    (dict(B=0), SHAPE), (dict(T=-1), SHAPE), (dict(rule=3), UNSUP), (dict(dk_=128), UNSUP), (dict(dt=F32), UNSUP),
+    (dict(B=0), SHAPE), (dict(T=-1), SHAPE), (dict(rule=3), UNSUP), (dict(dk_=128), UNSUP), (dict(dt=5), UNSUP),
     (dict(dq=addr(6) + 4), ALIGN), (dict(ws=addr(11, 1 << 34) + 8), ALIGN),
     (dict(dq=addr(0)), ALIAS), (dict(dk=addr(6) + 256), ALIAS), (dict(ds0=addr(3)), ALIAS),
     (dict(dv=addr(11, 1 << 34)), ALIAS), (dict(ws=None), WS), (dict(ws_bytes=1024), WS),

@@ -3,7 +3,7 @@
 Every gradient (dq, dk, dv, dg, dbeta, d_initial_state) of the HIP path is compared element by
 element with the fp64 token-by-token adjoint of the oracle on the same seeded inputs (q, k, v
 stored as bf16, so both sides see the same values), within the bf16-input tolerance of the
-forward (max |err| <= 2e-2 RMS of the oracle's tensor).  Cases: ragged lengths, several forward
+forward (max |err| <= 2e-2 RMS of the oracle's tensor; 1e-4 for fp32 q/k/v).  Cases: ragged lengths, several forward
 pieces, both rules, with and without start state and final-state gradient, T = 0 and 1, and the
 full 1b_8k training shape."""
 import numpy as np
@@ -20,16 +20,16 @@ DEV = "cuda:0"
 ORULE = {gdn.GDN_RULE_GATED_DELTA: oracle.GATED_DELTA, gdn.GDN_RULE_GATED_DECAY: oracle.GATED_DECAY}
 
 
-def grad_inputs(B, T, H, d, wid, s0=True, dsf=True):
-    x = gi.prefill_inputs(B, T, H, d, d, wid=wid, qkv_dtype=torch.bfloat16, s0=s0, device=DEV)
+def grad_inputs(B, T, H, d, wid, s0=True, dsf=True, dtype=torch.bfloat16):
+    x = gi.prefill_inputs(B, T, H, d, d, wid=wid, qkv_dtype=dtype, s0=s0, device=DEV)
     d_o = gi.draw_v((B, T, H, d), gi.seed_of(wid, 1, "v"), torch.float32, DEV)
     ds = gi.draw_state((B, H, d, d), gi.seed_of(wid, 1, "s0"), DEV) if dsf else None
     return x, d_o, ds
 
 
-def run_case(B, T, H, rule, wid, s0=True, dsf=True, want_d_initial=True):
-    print(f"[case] backward B={B} T={T} H={H} rule={rule} s0={s0} dsf={dsf}", flush=True)
-    x, d_o, ds = grad_inputs(B, T, H, 64, wid, s0, dsf)
+def run_case(B, T, H, rule, wid, s0=True, dsf=True, want_d_initial=True, dtype=torch.bfloat16):
+    print(f"[case] backward B={B} T={T} H={H} rule={rule} s0={s0} dsf={dsf} {dtype}", flush=True)
+    x, d_o, ds = grad_inputs(B, T, H, 64, wid, s0, dsf, dtype)
     got = gdn.chunk_backward(x["q"], x["k"], x["v"], x["g"], x["beta"], d_o, x["s0"], ds,
                              want_d_initial=want_d_initial, rule=rule)
     torch.cuda.synchronize()
@@ -42,7 +42,8 @@ def run_case(B, T, H, rule, wid, s0=True, dsf=True, want_d_initial=True):
             continue
         if T == 0 and name != "ds0":
             continue
-        assert_parity(t.cpu().numpy(), ref[name], TOL["bf16"], f"{name} T={T} rule={rule}")
+        tol = TOL["bf16"] if dtype == torch.bfloat16 else TOL["f32"]
+        assert_parity(t.cpu().numpy(), ref[name], tol, f"{name} T={T} rule={rule} {dtype}")
     return got, ref
 
 
@@ -75,3 +76,9 @@ def test_backward_full_1b_8k():
     # the training shape B=4, H=32, T=8192, d=64 (the 1b_8k workload), every gradient element
     w = gi.WORKLOADS["1b_8k"]
     run_case(w.B, w.T, w.H, gdn.GDN_RULE_GATED_DELTA, w.wid, s0=True, dsf=True)
+
+
+@pytest.mark.parametrize("rule", [gdn.GDN_RULE_GATED_DELTA, gdn.GDN_RULE_GATED_DECAY])
+def test_backward_fp32_inputs(rule):
+    # fp32 q/k/v: the forward recompute runs the fp32 chunk kernel; fp32 tolerance (1e-4 RMS)
+    run_case(2, 100, 2, rule, 220, dtype=torch.float32)
