@@ -42,7 +42,8 @@ STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_UNSUPP
 EXPORTS = ("gdn_chunk_prefill", "gdn_chunk_prefill_rule", "gdn_chunk_prefill_workspace_size",
            "gdn_chunk_prefill_varlen", "gdn_chunk_prefill_varlen_workspace_size",
            "gdn_decode_step", "gdn_decode_step_rule", "gdn_decode_step_slots", "gdn_prepare",
-           "gdn_chunk_backward", "gdn_chunk_backward_workspace_size", "gdn_status_string", "gdn_version")
+           "gdn_chunk_backward", "gdn_chunk_backward_workspace_size", "gdn_prepare_varlen",
+           "gdn_prepare_varlen_workspace_size", "gdn_status_string", "gdn_version")
 
 
 class GdnError(RuntimeError):
@@ -88,6 +89,10 @@ def lib():
         L.gdn_chunk_backward.restype = i32
         L.gdn_chunk_backward_workspace_size.argtypes = [i32] * 6
         L.gdn_chunk_backward_workspace_size.restype = sz
+        L.gdn_prepare_varlen.argtypes = [vp] * 9 + [i32, i32, vp, i32, vp, vp] + [vp] * 5 + [i32] * 4 + [vp, sz, vp]
+        L.gdn_prepare_varlen.restype = i32
+        L.gdn_prepare_varlen_workspace_size.argtypes = [i32]
+        L.gdn_prepare_varlen_workspace_size.restype = sz
         L.gdn_status_string.argtypes = [i32]
         L.gdn_status_string.restype = ctypes.c_char_p
         L.gdn_version.argtypes = []
@@ -156,6 +161,18 @@ def gdn_chunk_backward(rule, q, k, v, g, beta, initial_state, d_o, d_final_state
 
 def gdn_chunk_backward_workspace_size(B, T, H, d_k, d_v, qkv_dtype) -> int:
     return lib().gdn_chunk_backward_workspace_size(B, T, H, d_k, d_v, qkv_dtype)
+
+
+def gdn_prepare_varlen(xq, xk, xv, conv_weight, a_raw, b_raw, decay_rate, gate_bias, cu_seqlens, S, T_total,
+                       conv_pool, pool_size, slots, has_initial, q, k, v, g, beta, H, d_k, d_v, x_dtype, workspace,
+                       workspace_bytes, stream) -> int:
+    return lib().gdn_prepare_varlen(xq, xk, xv, conv_weight, a_raw, b_raw, decay_rate, gate_bias, cu_seqlens, S,
+                                    T_total, conv_pool, pool_size, slots, has_initial, q, k, v, g, beta, H, d_k, d_v,
+                                    x_dtype, workspace, workspace_bytes, stream)
+
+
+def gdn_prepare_varlen_workspace_size(S) -> int:
+    return lib().gdn_prepare_varlen_workspace_size(S)
 
 
 def gdn_status_string(status: int) -> str:
@@ -386,6 +403,43 @@ def varlen_workspace_bytes(cu_seqlens, H, d_k, d_v, chunk, qkv_dtype) -> int:
                                                        qkv_dtype))
 
 
+def prepare_varlen(xq, xk, xv, conv_weight, a_raw, b_raw, cu_seqlens, conv_pool, slots=None, has_initial=None, *,
+                   decay_rate=None, gate_bias=None, outs=None, workspace=None, stream=None):
+    """Input preparation of packed sequences: xq, xk [T,H,d_k]; xv [T,H,d_v]; a_raw, b_raw [T,H] fp32;
+    cu_seqlens host int32 [S+1]; conv_pool [P, H*(2 d_k + d_v), 3] fp32 (sequence s starts from and ends in
+    slot slots[s], slot s when slots is None; -1 = from zeros, state dropped); has_initial host [S].
+    Returns (q, k, v, g, beta) packed like the inputs."""
+    import torch
+    T, H, d_k = xq.shape
+    d_v = xv.shape[-1]
+    dt = _dtype_code(xq)
+    for t, n in ((xq, "xq"), (xk, "xk"), (xv, "xv")):
+        _check(t, n, xq.dtype)
+    for t, n in ((conv_weight, "conv_weight"), (a_raw, "a_raw"), (b_raw, "b_raw"), (decay_rate, "decay_rate"),
+                 (gate_bias, "gate_bias"), (conv_pool, "conv_pool")):
+        _check(t, n, torch.float32)
+    cu, sl, hi = _host_i32(cu_seqlens), _host_i32(slots), _host_i32(has_initial)
+    S = len(cu) - 1
+    dev = xq.device
+    if outs is None:
+        outs = (torch.empty_like(xq), torch.empty_like(xk), torch.empty_like(xv),
+                torch.empty((T, H), device=dev, dtype=torch.float32), torch.empty((T, H), device=dev, dtype=torch.float32))
+    need = int(gdn_prepare_varlen_workspace_size(S))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, device=dev, dtype=torch.uint8)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    pool_size = 0 if conv_pool is None else conv_pool.shape[0]
+    st = gdn_prepare_varlen(_ptr(xq), _ptr(xk), _ptr(xv), _ptr(conv_weight), _ptr(a_raw), _ptr(b_raw),
+                            _ptr(decay_rate), _ptr(gate_bias), _np_ptr(cu), S, T, _ptr(conv_pool), pool_size,
+                            _np_ptr(sl), _np_ptr(hi), *[_ptr(t) for t in outs], H, d_k, d_v, dt, _ptr(workspace),
+                            ws_bytes, stream)
+    if st != 0:
+        raise GdnError(st, "gdn_prepare_varlen")
+    return outs
+
+
 def chunk_prefill_varlen(q, k, v, g, beta, cu_seqlens, state_pool, slots=None, has_initial=None, chunk=64,
                          *, out=None, workspace=None, stream=None, rule=GDN_RULE_GATED_DELTA):
     """Packed sequences: q, k [T,H,d_k]; v [T,H,d_v] bf16; g, beta [T,H] fp32; cu_seqlens host int32
@@ -427,4 +481,5 @@ __all__ = ["EXPORTS", "GDN_F32", "GDN_BF16", "GDN_RULE_GATED_DELTA", "GDN_RULE_G
            "gdn_decode_step_slots", "gdn_chunk_prefill_varlen", "gdn_chunk_prefill_varlen_workspace_size",
            "chunk_prefill", "chunk_prefill_varlen", "decode_step", "decode_step_slots", "workspace_bytes",
            "varlen_workspace_bytes", "gdn_prepare", "prepare", "gdn_chunk_backward",
-           "gdn_chunk_backward_workspace_size", "chunk_backward", "backward_workspace_bytes"]
+           "gdn_chunk_backward_workspace_size", "chunk_backward", "backward_workspace_bytes", "gdn_prepare_varlen",
+           "gdn_prepare_varlen_workspace_size", "prepare_varlen"]

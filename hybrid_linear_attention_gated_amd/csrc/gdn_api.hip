@@ -416,4 +416,76 @@ gdn_status gdn_chunk_backward(gdn_rule rule, const void *q, const void *k, const
     return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
+size_t gdn_prepare_varlen_workspace_size(int S) {
+    return S > 0 ? ((static_cast<size_t>(3) * S + 1) * 4 + 255) & ~static_cast<size_t>(255) : 0;
+}
+
+gdn_status gdn_prepare_varlen(const void *xq, const void *xk, const void *xv, const float *conv_weight,
+                              const float *a_raw, const float *b_raw, const float *decay_rate,
+                              const float *gate_bias, const int32_t *cu_seqlens, int S, int T_total,
+                              float *conv_pool, int pool_size, const int32_t *slots,
+                              const int32_t *has_initial, void *q, void *k, void *v, float *g, float *beta,
+                              int H, int d_k, int d_v, gdn_dtype x_dtype, void *workspace,
+                              size_t workspace_bytes, void *stream) {
+    if (H <= 0 || d_k <= 0 || d_v <= 0) return GDN_ERR_SHAPE;
+    if (x_dtype != GDN_F32 && x_dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+    if (!supported_dim(d_k) || !supported_dim(d_v)) return GDN_ERR_UNSUPPORTED;
+    gdn_status st = check_varlen_batch(cu_seqlens, S, T_total, slots, pool_size);
+    if (st != GDN_OK) return st;
+    const long long C = static_cast<long long>(H) * (2 * d_k + d_v);
+    if (C > (1LL << 28) || prod({T_total, C}) == SIZE_MAX || prod({pool_size, C, 3}) == SIZE_MAX)
+        return GDN_ERR_SHAPE;
+    if (prepare_grid_blocks(1, T_total, H, d_k, d_v) > kMaxPrepareBlocks ||
+        static_cast<unsigned long long>((C / 4 + 255) / 256) * S > kMaxPrepareBlocks)
+        return GDN_ERR_SHAPE;
+    if (S == 0) return GDN_OK;
+    if (!conv_weight) return GDN_ERR_NULL;
+    if (T_total > 0 && (!xq || !xk || !xv || !a_raw || !b_raw || !q || !k || !v || !g || !beta))
+        return GDN_ERR_NULL;
+    bool any_slot = !slots;
+    for (int s = 0; slots && s < S; ++s) any_slot = any_slot || slots[s] >= 0;
+    if (any_slot && !conv_pool) return GDN_ERR_NULL;
+    const void *ptrs[] = {xq, xk, xv, conv_weight, a_raw, b_raw, decay_rate, gate_bias, conv_pool,
+                          q, k, v, g, beta, workspace};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return GDN_ERR_ALIGN;
+    const size_t need = gdn_prepare_varlen_workspace_size(S);
+    if (!workspace || workspace_bytes < need) return GDN_ERR_WORKSPACE;
+
+    const size_t es = elem_bytes(x_dtype);
+    const size_t nk = prod({T_total, H, d_k}) * es, nv = prod({T_total, H, d_v}) * es;
+    const size_t ngate = prod({T_total, H}) * 4, npool = prod({pool_size, C, 3}) * 4;
+    const Span in[] = {span(xq, xq ? nk : 0), span(xk, xk ? nk : 0), span(xv, xv ? nv : 0),
+                       span(conv_weight, static_cast<size_t>(C) * 16), span(a_raw, a_raw ? ngate : 0),
+                       span(b_raw, b_raw ? ngate : 0),
+                       span(decay_rate, decay_rate ? static_cast<size_t>(H) * 4 : 0),
+                       span(gate_bias, gate_bias ? static_cast<size_t>(H) * 4 : 0)};
+    const Span out[] = {span(q, q ? nk : 0), span(k, k ? nk : 0), span(v, v ? nv : 0),
+                        span(g, g ? ngate : 0), span(beta, beta ? ngate : 0),
+                        span(conv_pool, conv_pool ? npool : 0), span(workspace, need)};
+    const int n_out = sizeof(out) / sizeof(out[0]);
+    for (int i = 0; i < n_out; ++i) {
+        for (int j = i + 1; j < n_out; ++j)
+            if (overlap(out[i], out[j])) return GDN_ERR_ALIAS;
+        for (const Span &x : in)
+            if (overlap(out[i], x)) return GDN_ERR_ALIAS;
+    }
+
+    // the batch table (offsets, slots, start flags) into the workspace, then the kernels
+    std::vector<int32_t> table(static_cast<size_t>(3) * S + 1);
+    for (int s = 0; s <= S; ++s) table[s] = cu_seqlens[s];
+    for (int s = 0; s < S; ++s) {
+        table[S + 1 + s] = slots ? slots[s] : s;
+        table[2 * S + 1 + s] = has_initial ? (has_initial[s] != 0) : 1;
+    }
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    int32_t *dt = static_cast<int32_t *>(workspace);
+    if (hipMemcpyAsync(dt, table.data(), table.size() * 4, hipMemcpyHostToDevice, hs) != hipSuccess)
+        return GDN_ERR_HIP;
+    const hipError_t err = launch_prepare_varlen(xq, xk, xv, conv_weight, a_raw, b_raw, decay_rate, gate_bias,
+                                                 dt, dt + S + 1, dt + 2 * S + 1, S, T_total, conv_pool, q, k,
+                                                 v, g, beta, H, d_k, d_v, x_dtype, hs);
+    return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
 }  // extern "C"

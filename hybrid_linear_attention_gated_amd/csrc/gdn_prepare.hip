@@ -59,7 +59,51 @@ struct PrepArgs {
     int slabs, tiles;         // convolution workgroups = slabs * B * tiles
     int conv_blocks, gate_blocks, per_xcd;
     int state_in_kernel;      // 1: the last tile writes state_out
+    // packed sequences (B = 1, T = all tokens): sequence s is tokens cu[s] .. cu[s+1]-1 and
+    // starts from pool[slot[s]] when init[s] != 0 and slot[s] >= 0, else from zeros
+    const int *cu, *slot, *init;
+    int S;
+    float *pool;              // [pool][C][3]
 };
+
+// The three raw inputs before a position (oldest first) of kCpt channels, from a state row
+// [C][3] at channel ch; zeros for a NULL row.
+__device__ __forceinline__ void read_window(const float *sp, float (&x3)[kCpt], float (&x2)[kCpt],
+                                            float (&x1)[kCpt]) {
+    float st[3 * kCpt];  // kCpt channels x 3 taps, channel-major
+#pragma unroll
+    for (int i = 0; i < 3 * kCpt / 4; ++i) {
+        const float4 u = sp ? reinterpret_cast<const float4 *>(sp)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+        st[4 * i] = u.x; st[4 * i + 1] = u.y; st[4 * i + 2] = u.z; st[4 * i + 3] = u.w;
+    }
+#pragma unroll
+    for (int j = 0; j < kCpt; ++j) { x3[j] = st[3 * j]; x2[j] = st[3 * j + 1]; x1[j] = st[3 * j + 2]; }
+}
+__device__ __forceinline__ void write_window(float *sp, const float (&x3)[kCpt], const float (&x2)[kCpt],
+                                             const float (&x1)[kCpt]) {
+    float st[3 * kCpt];
+#pragma unroll
+    for (int j = 0; j < kCpt; ++j) { st[3 * j] = x3[j]; st[3 * j + 1] = x2[j]; st[3 * j + 2] = x1[j]; }
+#pragma unroll
+    for (int i = 0; i < 3 * kCpt / 4; ++i)
+        reinterpret_cast<float4 *>(sp)[i] = make_float4(st[4 * i], st[4 * i + 1], st[4 * i + 2], st[4 * i + 3]);
+}
+
+// Packed sequences: the sequence holding token t (the last s with cu[s] <= t), and its start
+// state row at channel ch (NULL = zeros).
+__device__ __forceinline__ int seq_of(const PrepArgs &a, int t) {
+    int lo = 0, hi = a.S;  // cu[lo] <= t < cu[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) / 2;
+        if (a.cu[mid] <= t) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+__device__ __forceinline__ const float *start_row(const PrepArgs &a, int s, int ch) {
+    const int sl = a.slot[s];
+    return (sl >= 0 && a.init[s]) ? a.pool + (static_cast<size_t>(sl) * a.C + ch) * 3 : nullptr;
+}
 
 // kCpt stored values as raw 32-bit words (bf16 pairs or fp32), and their fp32 widening
 template <typename TIn> struct Raw {
@@ -138,7 +182,9 @@ template <int DK, typename TIn> __device__ __forceinline__ Route<TIn> route(cons
             false};
 }
 
-template <int DK, typename TIn>
+// VL: packed sequences (the window restarts at every sequence start; states are written by
+// a second launch).
+template <int DK, typename TIn, bool VL>
 __global__ __launch_bounds__(kCols) void prepare_kernel(PrepArgs a) {
     const int w = static_cast<int>(blockIdx.x % kXcd) * a.per_xcd + static_cast<int>(blockIdx.x / kXcd);
     if (w >= a.conv_blocks + a.gate_blocks) return;
@@ -182,17 +228,39 @@ __global__ __launch_bounds__(kCols) void prepare_kernel(PrepArgs a) {
     const int t0 = tile * kTile;
     const int t1 = min(t0 + kTile, a.T);
     float x3[kCpt], x2[kCpt], x1[kCpt];  // inputs at t-3, t-2, t-1
-    if (t0 == 0) {
+    int sq = 0, seq_end = a.T;           // packed: the current sequence and its end
+    if (VL) {
+        sq = seq_of(a, t0);
+        const int cs = a.cu[sq];
+        seq_end = a.cu[sq + 1];
+        // the window before t0: earlier tokens of the sequence, else entries of its start state
+        // (position p < cs is entry 3 - (cs - p), oldest first)
+        const int back = t0 - cs;  // tokens of the sequence before t0 (0, 1, 2 or >= 3)
+        if (back < 3) {
+            read_window(start_row(a, sq, ch), x3, x2, x1);  // the start state ...
+            // ... shifted by the sequence's own tokens before t0
+            for (int p = cs; p < t0; ++p) {
+                float xp[kCpt];
+                widen(load_raw(r.x + static_cast<size_t>(p) * r.rs), xp);
+#pragma unroll
+                for (int j = 0; j < kCpt; ++j) { x3[j] = x2[j]; x2[j] = x1[j]; x1[j] = xp[j]; }
+            }
+        } else {
+            widen(load_raw(r.x + static_cast<size_t>(t0 - 3) * r.rs), x3);
+            widen(load_raw(r.x + static_cast<size_t>(t0 - 2) * r.rs), x2);
+            widen(load_raw(r.x + static_cast<size_t>(t0 - 1) * r.rs), x1);
+        }
+    } else if (t0 == 0) {
         if (a.state_in) {
-            float s[3 * kCpt];  // kCpt channels x 3 taps, channel-major
+            float st[3 * kCpt];  // kCpt channels x 3 taps, channel-major
             const float *sp = a.state_in + (static_cast<size_t>(b) * a.C + ch) * 3;
 #pragma unroll
             for (int i = 0; i < 3 * kCpt / 4; ++i) {
                 const float4 u = reinterpret_cast<const float4 *>(sp)[i];
-                s[4 * i] = u.x; s[4 * i + 1] = u.y; s[4 * i + 2] = u.z; s[4 * i + 3] = u.w;
+                st[4 * i] = u.x; st[4 * i + 1] = u.y; st[4 * i + 2] = u.z; st[4 * i + 3] = u.w;
             }
 #pragma unroll
-            for (int j = 0; j < kCpt; ++j) { x3[j] = s[3 * j]; x2[j] = s[3 * j + 1]; x1[j] = s[3 * j + 2]; }
+            for (int j = 0; j < kCpt; ++j) { x3[j] = st[3 * j]; x2[j] = st[3 * j + 1]; x1[j] = st[3 * j + 2]; }
         } else {
 #pragma unroll
             for (int j = 0; j < kCpt; ++j) x3[j] = x2[j] = x1[j] = 0.f;
@@ -211,6 +279,13 @@ __global__ __launch_bounds__(kCols) void prepare_kernel(PrepArgs a) {
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             if (tb + u >= t1) break;  // uniform across the workgroup
+            if (VL && tb + u == seq_end) {  // a new sequence starts: its start state (uniform)
+                do {
+                    ++sq;
+                } while (a.cu[sq + 1] <= tb + u);  // past empty sequences (cu[S] = T ends it)
+                seq_end = a.cu[sq + 1];
+                read_window(start_row(a, sq, ch), x3, x2, x1);
+            }
             float xt[kCpt], y[kCpt];
             widen(raw[u], xt);
             float ss = 0.f;
@@ -231,15 +306,37 @@ __global__ __launch_bounds__(kCols) void prepare_kernel(PrepArgs a) {
         }
     }
 
-    if (a.state_in_kernel && t1 == a.T && a.state_out) {  // last tile: the window is the new state
-        float s[3 * kCpt];
+    if (!VL && a.state_in_kernel && t1 == a.T && a.state_out) {  // last tile: the window is the new state
+        float st[3 * kCpt];
 #pragma unroll
-        for (int j = 0; j < kCpt; ++j) { s[3 * j] = x3[j]; s[3 * j + 1] = x2[j]; s[3 * j + 2] = x1[j]; }
+        for (int j = 0; j < kCpt; ++j) { st[3 * j] = x3[j]; st[3 * j + 1] = x2[j]; st[3 * j + 2] = x1[j]; }
         float *sp = a.state_out + (static_cast<size_t>(b) * a.C + ch) * 3;
 #pragma unroll
         for (int i = 0; i < 3 * kCpt / 4; ++i)
-            reinterpret_cast<float4 *>(sp)[i] = make_float4(s[4 * i], s[4 * i + 1], s[4 * i + 2], s[4 * i + 3]);
+            reinterpret_cast<float4 *>(sp)[i] = make_float4(st[4 * i], st[4 * i + 1], st[4 * i + 2], st[4 * i + 3]);
     }
+}
+
+// Packed sequences: every sequence's new state (the last three raw inputs of [start state,
+// its tokens]) into its pool slot, after prepare_kernel has read the start states.
+template <int DK, typename TIn>
+__global__ __launch_bounds__(kCols) void conv_state_varlen_kernel(PrepArgs a) {
+    const int s = static_cast<int>(blockIdx.x / a.slabs);
+    const int col = static_cast<int>(blockIdx.x % a.slabs) * kCols + threadIdx.x;
+    if (col >= a.ncol || a.slot[s] < 0) return;
+    const int ch = kCpt * col;
+    const Route<TIn> r = route<DK, TIn>(a, ch);
+    const int cs = a.cu[s], ce = a.cu[s + 1];
+    float x3[kCpt], x2[kCpt], x1[kCpt];
+    const int p0 = ce - cs < 3 ? cs : ce - 3;  // first token in the final window
+    if (ce - cs < 3) read_window(start_row(a, s, ch), x3, x2, x1);
+    for (int p = p0; p < ce; ++p) {  // shift in the sequence's last (up to) three tokens
+        float xp[kCpt];
+        widen(load_raw(r.x + static_cast<size_t>(p) * r.rs), xp);
+#pragma unroll
+        for (int j = 0; j < kCpt; ++j) { x3[j] = x2[j]; x2[j] = x1[j]; x1[j] = xp[j]; }
+    }
+    write_window(a.pool + (static_cast<size_t>(a.slot[s]) * a.C + ch) * 3, x3, x2, x1);
 }
 
 // New convolution state from the last three tokens (T >= 3), for calls whose
@@ -253,25 +350,38 @@ __global__ __launch_bounds__(kCols) void conv_state_tail_kernel(PrepArgs a) {
     const int ch = kCpt * col;
     Route<TIn> r = route<DK, TIn>(a, ch);
     const TIn *x = r.x + (static_cast<size_t>(b) * a.T + a.T - 3) * r.rs;
-    float x3[kCpt], x2[kCpt], x1[kCpt], s[3 * kCpt];
+    float x3[kCpt], x2[kCpt], x1[kCpt];
     widen(load_raw(x), x3);
     widen(load_raw(x + r.rs), x2);
     widen(load_raw(x + 2 * static_cast<size_t>(r.rs)), x1);
-#pragma unroll
-    for (int j = 0; j < kCpt; ++j) { s[3 * j] = x3[j]; s[3 * j + 1] = x2[j]; s[3 * j + 2] = x1[j]; }
-    float *sp = a.state_out + (static_cast<size_t>(b) * a.C + ch) * 3;
-#pragma unroll
-    for (int i = 0; i < 3 * kCpt / 4; ++i)
-        reinterpret_cast<float4 *>(sp)[i] = make_float4(s[4 * i], s[4 * i + 1], s[4 * i + 2], s[4 * i + 3]);
+    write_window(a.state_out + (static_cast<size_t>(b) * a.C + ch) * 3, x3, x2, x1);
 }
 
 template <int DK, typename TIn> hipError_t run(PrepArgs &a, hipStream_t stream) {
     const int grid = a.per_xcd * kXcd;
-    hipLaunchKernelGGL((prepare_kernel<DK, TIn>), dim3(grid), dim3(kCols), 0, stream, a);
+    if (a.cu) {
+        if (a.conv_blocks + a.gate_blocks > 0)
+            hipLaunchKernelGGL((prepare_kernel<DK, TIn, true>), dim3(grid), dim3(kCols), 0, stream, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess || !a.pool || a.S == 0) return e;
+        hipLaunchKernelGGL((conv_state_varlen_kernel<DK, TIn>), dim3(a.slabs * a.S), dim3(kCols), 0, stream, a);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL((prepare_kernel<DK, TIn, false>), dim3(grid), dim3(kCols), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.state_in_kernel || !a.state_out) return e;
     hipLaunchKernelGGL((conv_state_tail_kernel<DK, TIn>), dim3(a.slabs * a.B), dim3(kCols), 0, stream, a);
     return hipGetLastError();
+}
+
+template <typename F> hipError_t dispatch(int dk, gdn_dtype dt, PrepArgs &a, hipStream_t stream) {
+    const bool bf = dt == GDN_BF16;
+    switch (dk) {
+    case 16: return bf ? run<16, uint16_t>(a, stream) : run<16, float>(a, stream);
+    case 64: return bf ? run<64, uint16_t>(a, stream) : run<64, float>(a, stream);
+    case 128: return bf ? run<128, uint16_t>(a, stream) : run<128, float>(a, stream);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -308,13 +418,32 @@ hipError_t launch_prepare(const void *xq, const void *xk, const void *xv, const 
     // in place over several tiles: the first tile still reads the old state, so a second
     // launch writes the new one
     a.state_in_kernel = !(state_in && state_in == state_out && a.tiles > 1);
-    const bool bf = dt == GDN_BF16;
-    switch (dk) {
-    case 16: return bf ? run<16, uint16_t>(a, stream) : run<16, float>(a, stream);
-    case 64: return bf ? run<64, uint16_t>(a, stream) : run<64, float>(a, stream);
-    case 128: return bf ? run<128, uint16_t>(a, stream) : run<128, float>(a, stream);
-    }
-    return hipErrorInvalidValue;
+    return dispatch<void>(dk, dt, a, stream);
+}
+
+hipError_t launch_prepare_varlen(const void *xq, const void *xk, const void *xv, const float *w,
+                                 const float *a_raw, const float *b_raw, const float *rate,
+                                 const float *bias, const int *cu, const int *slot, const int *init, int S,
+                                 int T_total, float *pool, void *q, void *k, void *v, float *g,
+                                 float *beta, int H, int dk, int dv, gdn_dtype dt, hipStream_t stream) {
+    PrepArgs a{};
+    a.xq = xq; a.xk = xk; a.xv = xv; a.w = w;
+    a.a_raw = a_raw; a.b_raw = b_raw; a.rate = rate; a.bias = bias;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+    a.cu = cu; a.slot = slot; a.init = init; a.S = S; a.pool = pool;
+    a.B = 1; a.T = T_total; a.H = H; a.dv = dv;
+    a.C = H * (2 * dk + dv);
+    a.ncol = a.C / kCpt;
+    a.slabs = (a.ncol + kCols - 1) / kCols;
+    a.tiles = (T_total + kTile - 1) / kTile;  // no empty tile: states are written by the second launch
+    const size_t conv = static_cast<size_t>(a.slabs) * a.tiles;
+    const size_t gates = (static_cast<size_t>(T_total) * H + kCols * kGateEl - 1) / (kCols * kGateEl);
+    if (conv + gates > kMaxPrepareBlocks || static_cast<size_t>(a.slabs) * S > kMaxPrepareBlocks)
+        return hipErrorInvalidValue;
+    a.conv_blocks = static_cast<int>(conv);
+    a.gate_blocks = static_cast<int>(gates);
+    a.per_xcd = static_cast<int>((conv + gates + kXcd - 1) / kXcd);
+    return dispatch<void>(dk, dt, a, stream);
 }
 
 }  // namespace gdn

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 4
+#define GDN_ABI_VERSION 5
 
 #if defined(__GNUC__) || defined(__clang__)
 #define GDN_API __attribute__((visibility("default")))
@@ -302,6 +302,45 @@ GDN_API gdn_status gdn_prepare(const void *xq, const void *xk, const void *xv,
                                void *q, void *k, void *v, float *g, float *beta,
                                int B, int T, int H, int d_k, int d_v,
                                gdn_dtype x_dtype, void *stream);
+
+/*
+ * gdn_prepare_varlen -- gdn_prepare over S packed sequences of different
+ * lengths, convolution states in a pool (continuous batching; a decode step
+ * is the case of S sequences of one token each).  The convolution restarts at
+ * every sequence: the three inputs before a sequence's first token come from
+ * conv_pool[slot(s)], or are zero.
+ *
+ *   xq, xk         [T_total, H, d_k] x_dtype;  xv [T_total, H, d_v]
+ *   a_raw, b_raw   [T_total, H] fp32
+ *   cu_seqlens     HOST array [S + 1], 0 = cu[0] <= ... <= cu[S] = T_total
+ *   conv_pool      [pool_size, H*(2 d_k + d_v), 3] fp32: sequence s starts
+ *                  from conv_pool[slot(s)] (zeros when has_initial[s] == 0) and
+ *                  its new state (the last three raw inputs of [start state,
+ *                  its tokens]) is written back to the same slot
+ *   slots          HOST array [S] or NULL for slot(s) = s (then pool_size >=
+ *                  S); -1 = start from zeros, new state dropped; other slots
+ *                  distinct and in [0, pool_size)
+ *   has_initial    HOST array [S] or NULL (all start from their slot)
+ *   q, k, v, g, beta   written, packed like the inputs
+ *   workspace      device scratch of gdn_prepare_varlen_workspace_size(S) bytes
+ * Other arguments and the computation as gdn_prepare.  The host arrays are
+ * read during the call only.
+ * Errors: as gdn_prepare, plus GDN_ERR_SHAPE (bad offsets or slots),
+ * GDN_ERR_ALIAS (a repeated slot), GDN_ERR_WORKSPACE.
+ */
+GDN_API gdn_status gdn_prepare_varlen(const void *xq, const void *xk, const void *xv,
+                               const float *conv_weight,
+                               const float *a_raw, const float *b_raw,
+                               const float *decay_rate, const float *gate_bias,
+                               const int32_t *cu_seqlens, int S, int T_total,
+                               float *conv_pool, int pool_size,
+                               const int32_t *slots, const int32_t *has_initial,
+                               void *q, void *k, void *v, float *g, float *beta,
+                               int H, int d_k, int d_v, gdn_dtype x_dtype,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes gdn_prepare_varlen needs for S sequences. */
+GDN_API size_t gdn_prepare_varlen_workspace_size(int S);
 
 /*
  * gdn_chunk_backward -- gradients of gdn_chunk_prefill_rule (training of the GDN

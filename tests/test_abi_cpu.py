@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     L = gdn.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert gdn.gdn_version() == 4
+    assert gdn.gdn_version() == 5
 
 
 def test_status_strings():
@@ -234,3 +234,46 @@ def test_backward_workspace_size():
     # nothing to compute: T = 0 without an initial-state gradient is accepted without a GPU
     assert backward_call(T=0, q=None, k=None, v=None, g=None, beta=None, do=None, dq=None, dk=None, dv=None,
                          dg=None, db=None) == OK
+
+
+def prepare_varlen_call(**kw):
+    import numpy as np
+    cu = kw.pop("cu", np.array([0, 5, 5, 12], dtype=np.int32))
+    slots = kw.pop("slots", None)
+    S = kw.pop("S", len(cu) - 1)
+    args = dict(xq=addr(0), xk=addr(1), xv=addr(2), w=addr(3), a=addr(4), b=addr(5), rate=None, bias=None,
+                T=int(cu[-1]) if len(cu) else 0, pool=addr(6), pool_size=4, init=None, q=addr(7), k=addr(8),
+                v=addr(9), g=addr(10), beta=addr(11), H=2, dk=64, dv=64, dt=BF16, ws=addr(12), ws_bytes=4096,
+                stream=None)
+    args.update(kw)
+    cup = cu.ctypes.data if len(cu) else None
+    slp = None if slots is None else slots.ctypes.data
+    return gdn.gdn_prepare_varlen(args["xq"], args["xk"], args["xv"], args["w"], args["a"], args["b"], args["rate"],
+                                  args["bias"], cup, S, args["T"], args["pool"], args["pool_size"], slp, args["init"],
+                                  args["q"], args["k"], args["v"], args["g"], args["beta"], args["H"], args["dk"],
+                                  args["dv"], args["dt"], args["ws"], args["ws_bytes"], args["stream"])
+
+
+def test_prepare_varlen_validation():
+    import numpy as np
+    assert prepare_varlen_call(ws=None) == WS
+    assert prepare_varlen_call(ws_bytes=8) == WS
+    assert prepare_varlen_call(cu=np.array([0, 5, 4, 12], dtype=np.int32)) == SHAPE      # decreasing offsets
+    assert prepare_varlen_call(cu=np.array([1, 5, 5, 12], dtype=np.int32)) == SHAPE      # not from 0
+    assert prepare_varlen_call(T=13) == SHAPE                                             # cu[S] != T_total
+    assert prepare_varlen_call(pool_size=2) == SHAPE                                      # default slots need S slots
+    assert prepare_varlen_call(slots=np.array([0, 4, 1], dtype=np.int32)) == SHAPE        # slot out of range
+    assert prepare_varlen_call(slots=np.array([1, 1, -1], dtype=np.int32)) == ALIAS       # repeated slot
+    assert prepare_varlen_call(pool=None) == NULL
+    # no slot in use: the pool may be NULL (validation then stops at the missing workspace, no launch)
+    assert prepare_varlen_call(pool=None, slots=np.array([-1, -1, -1], dtype=np.int32), ws=None) == WS
+    assert prepare_varlen_call(w=None) == NULL
+    assert prepare_varlen_call(dk=32) == UNSUP
+    assert prepare_varlen_call(q=addr(0)) == ALIAS
+    assert prepare_varlen_call(pool=addr(3)) == ALIAS
+    assert prepare_varlen_call(ws=addr(6)) == ALIAS
+    assert prepare_varlen_call(xk=addr(1) + 4) == ALIGN
+    assert gdn.gdn_prepare_varlen_workspace_size(0) == 0
+    assert gdn.gdn_prepare_varlen_workspace_size(3) >= 40
+    # no sequences: nothing to do
+    assert prepare_varlen_call(cu=np.array([0], dtype=np.int32), S=0, T=0) == OK

@@ -197,3 +197,75 @@ def test_prepared_inputs_drive_the_mixer():
     ro, _ = oracle.prefill(as_bf16["q"], as_bf16["k"], as_bf16["v"], torch.from_numpy(ref["g"]).float(),
                            torch.from_numpy(ref["beta"]).float(), None)
     assert_parity(o.cpu().numpy(), ro, TOL["bf16"], "prepare -> prefill outputs")
+
+
+# ---- packed sequences with a pool of convolution states -------------------------------------------------
+
+def varlen_case(lens, H, dk, dv, pool_size, slots, init, dtype=torch.bfloat16, wid=300):
+    S, T = len(lens), int(sum(lens))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    d = gi.prep_inputs(1, T, H, dk, dv, wid=wid, x_dtype=dtype, state=False, device=DEV)
+    x = {kk: (t[0] if kk in ("xq", "xk", "xv", "a_raw", "b_raw") else t) for kk, t in d.items()}
+    C = H * (2 * dk + dv)
+    pool = gi._normal((pool_size, C, 3), gi.seed_of(wid, 7, "conv_state"), DEV).to(dtype).float()
+    pool0 = pool.clone()
+    print(f"[case] prepare_varlen S={S} T={T} H={H} dk={dk} dv={dv} pool={pool_size} {dtype}", flush=True)
+    q, k, v, g, beta = gdn.prepare_varlen(x["xq"], x["xk"], x["xv"], x["conv_weight"], x["a_raw"], x["b_raw"], cu,
+                                          pool, slots=slots, has_initial=init, decay_rate=x["decay_rate"],
+                                          gate_bias=x["gate_bias"])
+    torch.cuda.synchronize()
+    rel, floor = bounds(dtype)
+    p0 = np64(pool0)
+    expect = p0.copy()
+    used = []
+    for s in range(S):
+        a, b = cu[s], cu[s + 1]
+        sl = slots[s] if slots is not None else s
+        start = p0[sl][None] if (sl >= 0 and (init is None or init[s])) else None
+        seq = {kk: (x[kk][a:b][None] if kk in ("xq", "xk", "xv", "a_raw", "b_raw") else t) for kk, t in d.items()}
+        ref = reference({kk: (t.cpu() if isinstance(t, torch.Tensor) else t) for kk, t in seq.items()},
+                        conv_state=None if start is None else torch.from_numpy(start))
+        if b > a:
+            for name, got in (("q", q), ("k", k), ("v", v)):
+                assert_elementwise(got[a:b][None], ref[name], rel, floor, f"seq {s} {name}")
+            assert_elementwise(g[a:b][None], ref["g"], 1e-5, 1e-7, f"seq {s} g")
+            assert_elementwise(beta[a:b][None], ref["beta"], 1e-5, 1e-7, f"seq {s} beta")
+        if sl >= 0:
+            expect[sl] = ref["conv_state"][0]
+            used.append(sl)
+    got_pool = np64(pool)
+    assert np.array_equal(got_pool[used], expect[used]), "new convolution states"
+    untouched = [i for i in range(pool_size) if i not in used]
+    assert np.array_equal(got_pool[untouched], p0[untouched]), "slots no sequence uses must not change"
+
+
+def test_prepare_varlen_mixed_lengths_slots_and_starts():
+    lens = [5, 0, 70, 1, 2, 33, 40, 3]
+    slots = [4, 0, 7, -1, 2, 9, 1, 5]
+    init = [1, 1, 0, 1, 1, 1, 0, 1]
+    varlen_case(lens, 3, 64, 64, 10, slots, init)
+
+
+def test_prepare_varlen_fp32_default_slots():
+    varlen_case([31, 1, 64, 2, 0, 7], 2, 16, 64, 6, None, None, dtype=torch.float32, wid=301)
+
+
+def test_prepare_varlen_decode_batch():
+    # a serving decode step: 64 sequences of one token, states in a 100-slot pool
+    rng = np.random.default_rng(9)
+    slots = rng.permutation(100)[:64].astype(np.int32).tolist()
+    varlen_case([1] * 64, 4, 64, 64, 100, slots, None, wid=302)
+
+
+def test_prepare_varlen_single_sequence_equals_dense():
+    d = gi.prep_inputs(1, 150, 2, 64, 64, wid=303, device=DEV)
+    dense_state = torch.empty_like(d["conv_state"])
+    dense = run(d, state_out=dense_state)
+    pool = d["conv_state"].clone()
+    x = {kk: (t[0] if kk in ("xq", "xk", "xv", "a_raw", "b_raw") else t) for kk, t in d.items()}
+    packed = gdn.prepare_varlen(x["xq"], x["xk"], x["xv"], x["conv_weight"], x["a_raw"], x["b_raw"], [0, 150], pool,
+                                decay_rate=x["decay_rate"], gate_bias=x["gate_bias"])
+    torch.cuda.synchronize()
+    for i, name in enumerate(("q", "k", "v", "g", "beta")):
+        assert torch.equal(packed[i], dense[i][0]), name
+    assert torch.equal(pool, dense_state)
