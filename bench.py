@@ -151,6 +151,19 @@ def main():
     pstate = torch.empty_like(pin["conv_state"])
     din = gi.prep_inputs(dw.B, 1, dw.H, dw.dk, dw.dv, wid=201, device=dev)
     dstate0 = din["conv_state"].clone()
+    # the same decode step through the serving pool: 256 one-token sequences, states in a 512-slot pool
+    import numpy as np
+    pcu = np.arange(dw.B + 1, dtype=np.int32)
+    pslots = np.random.default_rng(12).permutation(2 * dw.B)[:dw.B].astype(np.int32)
+    ppool = torch.zeros((2 * dw.B, din["conv_state"].shape[1], 3), device=dev, dtype=torch.float32)
+    pflat = {kk: din[kk][:, 0].contiguous() for kk in ("xq", "xk", "xv", "a_raw", "b_raw")}
+    pouts = tuple(torch.empty_like(t) for t in (pflat["xq"], pflat["xk"], pflat["xv"], pflat["a_raw"], pflat["b_raw"]))
+    pws = torch.empty(max(gdn.gdn_prepare_varlen_workspace_size(dw.B), 1), device=dev, dtype=torch.uint8)
+
+    def prepare_decode_pool():
+        gdn.prepare_varlen(pflat["xq"], pflat["xk"], pflat["xv"], din["conv_weight"], pflat["a_raw"], pflat["b_raw"],
+                           pcu, ppool, slots=pslots, decay_rate=din["decay_rate"], gate_bias=din["gate_bias"],
+                           outs=pouts, workspace=pws)
 
     def prepare():
         gdn.prepare(pin["xq"], pin["xk"], pin["xv"], pin["conv_weight"], pin["a_raw"], pin["b_raw"],
@@ -295,8 +308,10 @@ def main():
     for _ in range(args.warmup):
         prepare()
         prepare_decode()
+        prepare_decode_pool()
     pp_ev = [(mk(), mk()) for _ in range(args.steps)]
     pd_ev = [(mk(), mk()) for _ in range(args.steps)]
+    pv_ev = [(mk(), mk()) for _ in range(args.steps)]
     pc_ev = [(mk(), mk()) for _ in range(args.steps)]
     for i in range(args.steps):
         pp_ev[i][0].record(stream)
@@ -305,6 +320,9 @@ def main():
         pd_ev[i][0].record(stream)
         prepare_decode()
         pd_ev[i][1].record(stream)
+        pv_ev[i][0].record(stream)
+        prepare_decode_pool()
+        pv_ev[i][1].record(stream)
     for i in range(args.steps):
         pc_ev[i][0].record(stream)
         prepare()
@@ -315,6 +333,7 @@ def main():
     din["conv_state"].copy_(dstate0)
     prep_ms = sum(a.elapsed_time(b) for a, b in pp_ev) / len(pp_ev)
     prep_dec_ms = sum(a.elapsed_time(b) for a, b in pd_ev) / len(pd_ev)
+    prep_pool_ms = sum(a.elapsed_time(b) for a, b in pv_ev) / len(pv_ev)
     prep_chain_ms = sum(a.elapsed_time(b) for a, b in pc_ev) / len(pc_ev)
     conv_ch = w.H * (2 * w.dk + w.dv)
     prep_bytes = w.B * w.T * w.H * PREP_BYTES_PER_TOKEN_HEAD + conv_ch * (16 + 24 * w.B)
@@ -411,11 +430,13 @@ def main():
             "hbm_frac": round(prep_bytes / (prep_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "bytes_per_call": prep_bytes,
             "decode_us_avg": round(prep_dec_ms * 1e3, 2),
             "decode_GBps_algorithmic": round(prep_dec_bytes / (prep_dec_ms * 1e-3) / 1e9, 1),
+            "decode_pool_us_avg": round(prep_pool_ms * 1e3, 2),
             "traffic_bytes_per_call": recorded_traffic("prepare"),
             "prepare_then_prefill_ms_avg": round(prep_chain_ms, 4),
             "prepare_then_prefill_tokens_per_s": round(w.B * w.T / (prep_chain_ms * 1e-3), 1),
             "note": "short causal convolution + SiLU + q/k L2 norm + gate activations on the 64K shape "
-                    "(bf16 in and out) and on the 256-sequence decode batch (state in place)",
+                    "(bf16 in and out) and on the 256-sequence decode batch (state in place; decode_pool: the "
+                    "same step as 256 one-token packed sequences with states in a 512-slot pool)",
         },
         "backward": {
             "workload": "1b_8k: B=4 H=32 T=8192 d_k=d_v=64, bf16 q/k/v, gated delta rule, zero start state",
