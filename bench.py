@@ -92,6 +92,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=65536,
                     help="tokens of the 64K workload the oracle is timed on")
+    ap.add_argument("--backward-workload", choices=["1b_8k", "1b_64k"], default="1b_8k",
+                    help="workload of the backward leg (the JSON line reports 1b_8k)")
     ap.add_argument("--only", choices=["all", "prefill", "decode", "copy", "prepare", "backward"], default="all",
                     help="run one component (for profiling); 'copy' runs a plain 4 GiB device copy "
                          "used to calibrate the HBM byte counters; the JSON line needs 'all'")
@@ -176,8 +178,8 @@ def main():
                     conv_state_out=din["conv_state"])
 
     # gradients of one prefill call on the training shape 1b_8k (B=4 H=32 T=8192 d=64)
-    bw = gi.WORKLOADS["1b_8k"]
-    bin_ = gi.workload_inputs("1b_8k", device=dev)
+    bw = gi.WORKLOADS[args.backward_workload]
+    bin_ = gi.workload_inputs(args.backward_workload, device=dev)
     bdo = gi.draw_v((bw.B, bw.T, bw.H, bw.dv), gi.seed_of(bw.wid, 1, "v"), torch.float32, dev)
     f32 = dict(device=dev, dtype=torch.float32)
     bouts = (torch.empty((bw.B, bw.T, bw.H, bw.dk), **f32), torch.empty((bw.B, bw.T, bw.H, bw.dk), **f32),

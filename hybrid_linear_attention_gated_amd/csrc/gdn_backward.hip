@@ -25,8 +25,8 @@
 //
 // Three launches after a forward pass that keeps every chunk's start state
 // (gdn_prefill_chunk.hip): bwd_map_kernel (F and R of every chunk, chunks in
-// parallel), bwd_scan_kernel (Y of every chunk, chunks in reverse order, one
-// workgroup per head) and bwd_grad_kernel (all gradients, chunks in
+// parallel), bwd_scan_kernel (Y of every chunk, chunks in reverse order; long
+// sequences in two levels of pieces) and bwd_grad_kernel (all gradients, chunks in
 // parallel).  fp32 arithmetic (matrix cores for the products) on LDS-resident chunk matrices.
 #include "gdn_internal.h"
 
@@ -39,13 +39,9 @@ namespace {
 #ifndef GDN_BWD_MAP_THREADS
 #define GDN_BWD_MAP_THREADS 512
 #endif
-#ifndef GDN_BWD_SCAN_SLICES
-#define GDN_BWD_SCAN_SLICES 4
-#endif
 constexpr int kBT = 256;                   // threads per scan workgroup
 constexpr int kBTM = GDN_BWD_MAP_THREADS;  // threads per map workgroup
 constexpr int kBTG = GDN_BWD_THREADS;      // threads per gradient workgroup
-constexpr int kScanSlices = GDN_BWD_SCAN_SLICES;  // scan workgroups per head (column slices of Y)
 constexpr int kC = 32;            // tokens per chunk
 #ifndef GDN_BWD_PAD_D
 #define GDN_BWD_PAD_D 2
@@ -212,23 +208,62 @@ __global__ __launch_bounds__(kBTM) void bwd_map_kernel(BwdArgs a) {
     }
 }
 
-// ---- reverse scan: Y of every chunk, one workgroup per head -------------------------
-// Y_{n-1} = F_n Y_n + R_n on the matrix cores, a head's columns of Y split over kScanSlices
-// workgroups: wavefront w owns rows 16 w .. 16 w + 15 of the workgroup's columns.  Its rows of F_n and R_n are loaded into registers one chunk
-// ahead; within a block of 16 keys, lane group lk takes keys 4 lk .. 4 lk + 3 (a float4
-// of F) and Y is read from LDS with the same key order.
-template <int DK, int DV>
-__global__ __launch_bounds__(kBT) void bwd_scan_kernel(BwdArgs a) {
-    static_assert(DK == 64 && DV % (16 * kScanSlices) == 0, "one 16-row tile of Y per wavefront");
-    constexpr int SW = DV / kScanSlices;  // columns of Y this workgroup owns
-    constexpr int YP = SW + 4;
+// ---- reverse scan of the state gradient ------------------------------------------
+// Y_{n-1} = F_n Y_n + R_n over the chunks [n0, n1) of one head, on the matrix cores, the
+// columns of Y split over workgroups of kSW columns: wavefront w owns rows 16 w .. 16 w + 15.
+// Its rows of F_n and R_n are loaded into registers one chunk ahead; within a block of 16
+// keys, lane group lk takes keys 4 lk .. 4 lk + 3 (a float4 of F) and Y is read from LDS
+// with the same key order.  Modes:
+//   kScanAll   one range per head (all chunks, or all pieces when F and R are piece maps):
+//              starts from the final-state gradient, stores Y at the end of every step's
+//              chunk, writes the start-state gradient;
+//   kScanMap   one range per piece: the piece's own map, on [constant | identity] columns
+//              (the constant part starts at 0 and adds R, the identity part starts at I):
+//              the result is the piece's affine map (G_p, c_p) with Y_start = G_p Y_end + c_p;
+//   kScanPiece one range per piece: starts from the piece's end value and stores every
+//              chunk's Y.
+constexpr int kSW = 16;
+enum { kScanAll = 0, kScanMap = 1, kScanPiece = 2 };
+
+struct ScanArgs {
+    const float *F, *R;      // [BH][steps][DK][DK], [BH][steps][DK][DV]
+    float *Y;                // kScanAll / kScanPiece: [BH][steps][DK][DV], Y at the end of each step
+    const float *y_end;      // kScanAll: final gradient [BH][DK][DV] (NULL = 0); kScanPiece: [BH][P][DK][DV]
+    float *y_start;          // kScanAll: start gradient [BH][DK][DV] (NULL = not kept)
+    float *Gp, *cp;          // kScanMap: piece maps [BH][P][DK][DK], [BH][P][DK][DV]
+    int steps, m, P;         // steps per head, steps per piece, pieces per head
+    int items;               // workgroups with work (the grid is rounded up to a multiple of 8)
+};
+
+template <int DK, int DV, int MODE>
+__global__ __launch_bounds__(kBT) void bwd_scan_kernel(ScanArgs a) {
+    static_assert(DK == 64 && DV % kSW == 0, "one 16-row tile of Y per wavefront");
+    constexpr int SW = kSW, YP = SW + 4, NCOL = MODE == kScanMap ? DV + DK : DV;
+    constexpr int SLICES = NCOL / SW;
     __shared__ float Yb[2][DK][YP];
-    const int bh = blockIdx.x / kScanSlices, c0 = (blockIdx.x % kScanSlices) * SW, tid = threadIdx.x;
+    // work items round-robin over the 8 XCDs so that the slices of one head and piece, which read
+    // the same maps, run on one XCD at the same time and share its L2
+    const int per_xcd = static_cast<int>(gridDim.x) / 8;
+    const int w = static_cast<int>(blockIdx.x % 8) * per_xcd + static_cast<int>(blockIdx.x / 8);
+    if (w >= a.items) return;
+    const int slice = w % SLICES, rest = w / SLICES;
+    const int piece = MODE == kScanAll ? 0 : rest % a.P;
+    const int bh = MODE == kScanAll ? rest : rest / a.P;
+    const int c0 = slice * SW, tid = threadIdx.x;
+    const bool has_r = c0 < DV;  // constant columns take R; the identity part of a map does not
     const int lane = tid % 64, wave = tid / 64, li = lane % 16, lk = lane / 16, i0 = 16 * wave;
-    const size_t head = static_cast<size_t>(bh) * a.N;
-    for (int e = tid; e < DK * SW; e += kBT)
-        Yb[0][e / SW][e % SW] =
-            a.ds_final ? a.ds_final[static_cast<size_t>(bh) * DK * DV + (e / SW) * DV + c0 + e % SW] : 0.f;
+    const int n0 = MODE == kScanAll ? 0 : piece * a.m;
+    const int n1 = MODE == kScanAll ? a.steps : min(n0 + a.m, a.steps);
+    const size_t head = static_cast<size_t>(bh) * a.steps;
+    const size_t hp = static_cast<size_t>(bh) * a.P + piece;
+    for (int e = tid; e < DK * SW; e += kBT) {
+        const int j = e / SW, c = e % SW;
+        float y = 0.f;
+        if (MODE == kScanAll) y = a.y_end ? a.y_end[static_cast<size_t>(bh) * DK * DV + j * DV + c0 + c] : 0.f;
+        if (MODE == kScanPiece) y = a.y_end[hp * DK * DV + j * DV + c0 + c];
+        if (MODE == kScanMap && !has_r) y = (j == c0 - DV + c) ? 1.f : 0.f;
+        Yb[0][j][c] = y;
+    }
     float4 Fc[DK / 16], Fn[DK / 16];
     f32x4 Rc[SW / 16], Rn[SW / 16];
     auto load_f = [&](int n, float4 (&f)[DK / 16]) {
@@ -241,23 +276,26 @@ __global__ __launch_bounds__(kBT) void bwd_scan_kernel(BwdArgs a) {
 #pragma unroll
         for (int t = 0; t < SW / 16; ++t)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) r[t][q] = R[(i0 + 4 * lk + q) * DV + 16 * t + li];
+            for (int q = 0; q < 4; ++q) r[t][q] = has_r ? R[(i0 + 4 * lk + q) * DV + 16 * t + li] : 0.f;
     };
-    if (a.N > 0) {
-        load_f(a.N - 1, Fc);
-        load_r(a.N - 1, Rc);
+    if (n1 > n0) {
+        load_f(n1 - 1, Fc);
+        load_r(n1 - 1, Rc);
     }
     __syncthreads();
-    for (int s = 0; s < a.N; ++s) {
-        const int n = a.N - 1 - s, cur = s & 1;
-        if (n > 0) {
+    for (int s = 0; s < n1 - n0; ++s) {
+        const int n = n1 - 1 - s, cur = s & 1;
+        if (n > n0) {
             load_f(n - 1, Fn);
             load_r(n - 1, Rn);
         }
-        float *Yo = a.Y + (head + n) * DK * DV + c0;  // this chunk's Y, before the update
-        for (int e = lane; e < 16 * SW / 4; e += 64) {
-            const int row = i0 + e / (SW / 4), c4 = e % (SW / 4);
-            *reinterpret_cast<float4 *>(Yo + row * DV + 4 * c4) = *reinterpret_cast<const float4 *>(&Yb[cur][row][4 * c4]);
+        if (MODE != kScanMap) {  // this step's Y, before the update
+            float *Yo = a.Y + (head + n) * DK * DV + c0;
+            for (int e = lane; e < 16 * SW / 4; e += 64) {
+                const int row = i0 + e / (SW / 4), c4 = e % (SW / 4);
+                *reinterpret_cast<float4 *>(Yo + row * DV + 4 * c4) =
+                    *reinterpret_cast<const float4 *>(&Yb[cur][row][4 * c4]);
+            }
         }
         f32x4 acc[SW / 16];
 #pragma unroll
@@ -266,10 +304,10 @@ __global__ __launch_bounds__(kBT) void bwd_scan_kernel(BwdArgs a) {
         for (int blk = 0; blk < DK / 16; ++blk) {
             const float fa[4] = {Fc[blk].x, Fc[blk].y, Fc[blk].z, Fc[blk].w};
 #pragma unroll
-            for (int m = 0; m < 4; ++m)
+            for (int mm = 0; mm < 4; ++mm)
 #pragma unroll
                 for (int t = 0; t < SW / 16; ++t)
-                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[m], Yb[cur][16 * blk + 4 * lk + m][16 * t + li],
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[mm], Yb[cur][16 * blk + 4 * lk + mm][16 * t + li],
                                                                   acc[t], 0, 0, 0);
         }
 #pragma unroll
@@ -282,10 +320,17 @@ __global__ __launch_bounds__(kBT) void bwd_scan_kernel(BwdArgs a) {
         for (int t = 0; t < SW / 16; ++t) Rc[t] = Rn[t];
         __syncthreads();
     }
-    if (a.ds0) {
-        const int fin = a.N & 1;
+    const int fin = (n1 - n0) & 1;
+    if (MODE == kScanAll && a.y_start) {
         for (int e = tid; e < DK * SW; e += kBT)
-            a.ds0[static_cast<size_t>(bh) * DK * DV + (e / SW) * DV + c0 + e % SW] = Yb[fin][e / SW][e % SW];
+            a.y_start[static_cast<size_t>(bh) * DK * DV + (e / SW) * DV + c0 + e % SW] = Yb[fin][e / SW][e % SW];
+    }
+    if (MODE == kScanMap) {
+        for (int e = tid; e < DK * SW; e += kBT) {
+            const int j = e / SW, c = e % SW;
+            if (has_r) a.cp[hp * DK * DV + j * DV + c0 + c] = Yb[fin][j][c];
+            else a.Gp[hp * DK * DK + j * DK + c0 - DV + c] = Yb[fin][j][c];
+        }
     }
 }
 
@@ -465,8 +510,22 @@ __global__ __launch_bounds__(kBTG) void bwd_grad_kernel(BwdArgs a) {
     }
 }
 
+// Pieces for the reverse scan: none when the heads alone give enough workgroups or the
+// sequence is short (the pieces triple the work: their maps run on twice the columns); else
+// about sqrt(N) chunks per piece (three short sequential passes).
+struct ScanPlan {
+    int m, P;  // chunks per piece, pieces per head (P = 1: one range per head)
+};
+ScanPlan scan_plan(int BH, int N) {
+    if (N < 128 || BH * (64 / kSW) >= 256) return {N, 1};  // heads alone fill the 256 CUs
+    int m = 16;
+    while (m * m < N) m *= 2;
+    return {m, (N + m - 1) / m};
+}
+
 template <int DK, int DV, bool DELTA>
-hipError_t run_backward(BwdArgs &a, gdn_dtype dt, hipStream_t stream) {
+hipError_t run_backward(BwdArgs &a, gdn_dtype dt, const ScanPlan &plan, float *Gp, float *cp, float *yend,
+                        hipStream_t stream) {
     const int items = a.BH * a.N;
     const bool bf = dt == GDN_BF16;
     if (items > 0) {
@@ -475,7 +534,28 @@ hipError_t run_backward(BwdArgs &a, gdn_dtype dt, hipStream_t stream) {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((bwd_scan_kernel<DK, DV>), dim3(a.BH * kScanSlices), dim3(kBT), 0, stream, a);
+    auto grid8 = [](int items) { return dim3((items + 7) / 8 * 8); };
+    ScanArgs sa{};
+    sa.F = a.F; sa.R = a.R; sa.Y = a.Y; sa.steps = a.N;
+    if (plan.P == 1) {
+        sa.y_end = a.ds_final; sa.y_start = a.ds0; sa.m = a.N; sa.P = 1;
+        sa.items = a.BH * (DV / kSW);
+        hipLaunchKernelGGL((bwd_scan_kernel<DK, DV, kScanAll>), grid8(sa.items), dim3(kBT), 0, stream, sa);
+    } else {
+        // piece maps, then the chain over pieces (the same scan with piece maps as its steps), then
+        // every chunk's Y inside each piece from the piece's end value
+        sa.m = plan.m; sa.P = plan.P; sa.Gp = Gp; sa.cp = cp;
+        sa.items = a.BH * plan.P * ((DV + DK) / kSW);
+        hipLaunchKernelGGL((bwd_scan_kernel<DK, DV, kScanMap>), grid8(sa.items), dim3(kBT), 0, stream, sa);
+        ScanArgs ch{};
+        ch.F = Gp; ch.R = cp; ch.Y = yend; ch.y_end = a.ds_final; ch.y_start = a.ds0;
+        ch.steps = plan.P; ch.m = plan.P; ch.P = 1;
+        ch.items = a.BH * (DV / kSW);
+        hipLaunchKernelGGL((bwd_scan_kernel<DK, DV, kScanAll>), grid8(ch.items), dim3(kBT), 0, stream, ch);
+        sa.y_end = yend;
+        sa.items = a.BH * plan.P * (DV / kSW);
+        hipLaunchKernelGGL((bwd_scan_kernel<DK, DV, kScanPiece>), grid8(sa.items), dim3(kBT), 0, stream, sa);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || items == 0) return e;
     if (bf) hipLaunchKernelGGL((bwd_grad_kernel<DK, DV, uint16_t, DELTA>), dim3(items), dim3(kBTG), 0, stream, a);
@@ -486,7 +566,7 @@ hipError_t run_backward(BwdArgs &a, gdn_dtype dt, hipStream_t stream) {
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 struct BwdLayout {
-    size_t fwd, o, sfin, states, F, R, Y, total;
+    size_t fwd, o, sfin, states, F, R, Y, Gp, cp, yend, total;
 };
 BwdLayout bwd_layout(int B, int T, int H, int dk, int dv) {
     const size_t BH = static_cast<size_t>(B) * H, N = (static_cast<size_t>(T) + kC - 1) / kC;
@@ -499,6 +579,11 @@ BwdLayout bwd_layout(int B, int T, int H, int dk, int dv) {
     L.F = off; off += align256(BH * N * dk * dk * 4);
     L.R = off; off += align256(BH * N * dk * dv * 4);
     L.Y = off; off += align256(BH * N * dk * dv * 4);
+    const ScanPlan plan = scan_plan(static_cast<int>(BH), static_cast<int>(N));
+    const size_t PP = plan.P > 1 ? static_cast<size_t>(plan.P) : 0;
+    L.Gp = off; off += align256(BH * PP * dk * dk * 4);
+    L.cp = off; off += align256(BH * PP * dk * dv * 4);
+    L.yend = off; off += align256(BH * PP * dk * dv * 4);
     L.total = off;
     return L;
 }
@@ -545,7 +630,11 @@ hipError_t launch_backward(const void *q, const void *k, const void *v, const fl
                                             reinterpret_cast<float *>(w + L.states));
         if (e != hipSuccess) return e;
     }
-    return delta ? run_backward<64, 64, true>(a, dt, stream) : run_backward<64, 64, false>(a, dt, stream);
+    const ScanPlan plan = scan_plan(a.BH, a.N);
+    float *Gp = reinterpret_cast<float *>(w + L.Gp), *cp = reinterpret_cast<float *>(w + L.cp);
+    float *yend = reinterpret_cast<float *>(w + L.yend);
+    return delta ? run_backward<64, 64, true>(a, dt, plan, Gp, cp, yend, stream)
+                 : run_backward<64, 64, false>(a, dt, plan, Gp, cp, yend, stream);
 }
 
 }  // namespace gdn

@@ -82,3 +82,26 @@ def test_backward_full_1b_8k():
 def test_backward_fp32_inputs(rule):
     # fp32 q/k/v: the forward recompute runs the fp32 chunk kernel; fp32 tolerance (1e-4 RMS)
     run_case(2, 100, 2, rule, 220, dtype=torch.float32)
+
+
+@pytest.mark.parametrize("rule", [gdn.GDN_RULE_GATED_DELTA, gdn.GDN_RULE_GATED_DECAY])
+def test_backward_two_level_scan(rule):
+    # 150 chunks of 32 tokens on 2 heads: the reverse scan runs in pieces of 16 chunks (the last one
+    # ragged: 6 chunks, its last chunk 4 tokens short)
+    run_case(1, 150 * 32 - 4, 2, rule, 230)
+
+
+def test_backward_two_level_scan_1b_64k_sampled():
+    # the single 64K sequence (B=1 H=32 T=65536): pieces of 64 chunks.  The oracle runs on 2 of the
+    # 32 heads (heads are independent: the same inputs restricted to those heads)
+    B, T, H = 1, 65536, 32
+    print(f"[case] backward 1b_64k T={T} H={H}", flush=True)
+    x, d_o, ds = grad_inputs(B, T, H, 64, 3)
+    got = gdn.chunk_backward(x["q"], x["k"], x["v"], x["g"], x["beta"], d_o, x["s0"], ds)
+    torch.cuda.synchronize()
+    heads = [0, 21]
+    sub = lambda t: t[:, :, heads].contiguous().cpu() if t.dim() >= 3 and t.shape[1] == T else t[:, heads].contiguous().cpu()
+    ref = oracle.backward(sub(x["q"]), sub(x["k"]), sub(x["v"]), sub(x["g"]), sub(x["beta"]), sub(x["s0"]),
+                          sub(d_o), sub(ds))
+    for name, t in zip(("dq", "dk", "dv", "dg", "dbeta", "ds0"), got):
+        assert_parity(sub(t).numpy(), ref[name], TOL["bf16"], f"{name} 1b_64k heads {heads}")
