@@ -61,6 +61,7 @@ struct BwdArgs {
     float *Y;             // [BH][N][DK][DV] gradient with respect to each chunk's end state
     float *dq, *dk, *dv, *dg, *dbeta, *ds0;
     int T, H, N, BH;
+    int items;            // chunks of all heads (BH * N)
     float scale;
 };
 
@@ -110,33 +111,96 @@ template <int DK, int DV> struct ChunkLds {
     float graw[kC], G[kC], gam[kC], eps[kC], b[kC];
 };
 
-// Loads q, k, dO, g, beta of chunk n of head bh (rows past the end read as zeros) and
-// builds G, gam, eps, KG, P and, for the delta rule, T and W.
-template <int DK, int DV, typename TIn, bool DELTA>
-__device__ void chunk_keyside(const BwdArgs &a, ChunkLds<DK, DV> &s, int bh, int n, size_t &tok, int &L) {
+// One chunk's rows in registers (NT threads, element e = tid + NT i), loaded from HBM ahead of
+// their use; rows past the end of the sequence are zeros.  GRAD also takes v and the chunk's
+// start state and end-state gradient.
+template <int NT, int DK, int DV, bool GRAD> struct ChunkRows {
+    static constexpr int NQ = kC * DK / NT, NV = kC * DV / NT, NS = GRAD ? DK * DV / NT : 1;
+    float q[NQ], k[NQ], dO[NV], v[GRAD ? NV : 1], S[NS], Y[NS], g, b;
+};
+
+struct ChunkPos {
+    size_t tok;  // row of the chunk's first token in [B*T]
+    int h, L;    // head, valid tokens
+};
+__device__ __forceinline__ ChunkPos chunk_pos(const BwdArgs &a, int w) {
+    const int bh = w / a.N, n = w % a.N;
+    ChunkPos p;
+    p.h = bh % a.H;
+    p.L = min(kC, a.T - n * kC);
+    p.tok = static_cast<size_t>(bh / a.H) * a.T + static_cast<size_t>(n) * kC;
+    return p;
+}
+
+template <int NT, int DK, int DV, typename TIn, bool GRAD>
+__device__ __forceinline__ void chunk_load(const BwdArgs &a, int w, ChunkRows<NT, DK, DV, GRAD> &R) {
+    using CR = ChunkRows<NT, DK, DV, GRAD>;
     const int tid = threadIdx.x;
-    const int bb = bh / a.H, h = bh % a.H;
-    const int t0 = n * kC;
-    L = min(kC, a.T - t0);
-    tok = static_cast<size_t>(bb) * a.T + t0;
+    const ChunkPos p = chunk_pos(a, w);
     const TIn *q = static_cast<const TIn *>(a.q), *k = static_cast<const TIn *>(a.k);
-    const int nt = blockDim.x;
-    for (int e = tid; e < kC * DK; e += nt) {
-        const int r = e / DK, c = e % DK;
-        const size_t i = ((tok + r) * a.H + h) * DK + c;
-        s.q[r][c] = r < L ? load_in(q, i) : 0.f;
-        s.k[r][c] = r < L ? load_in(k, i) : 0.f;
+#pragma unroll
+    for (int i = 0; i < CR::NQ; ++i) {
+        const int e = tid + NT * i, r = e / DK, c = e % DK;
+        const size_t x = ((p.tok + r) * a.H + p.h) * DK + c;
+        R.q[i] = r < p.L ? load_in(q, x) : 0.f;
+        R.k[i] = r < p.L ? load_in(k, x) : 0.f;
     }
-    for (int e = tid; e < kC * DV; e += nt) {
-        const int r = e / DV, c = e % DV;
-        s.dO[r][c] = r < L ? a.d_o[((tok + r) * a.H + h) * DV + c] : 0.f;
+#pragma unroll
+    for (int i = 0; i < CR::NV; ++i) {
+        const int e = tid + NT * i, r = e / DV, c = e % DV;
+        const size_t x = ((p.tok + r) * a.H + p.h) * DV + c;
+        R.dO[i] = r < p.L ? a.d_o[x] : 0.f;
+        if (GRAD) R.v[i] = r < p.L ? load_in(static_cast<const TIn *>(a.v), x) : 0.f;
+    }
+    if (GRAD) {
+        const size_t base = static_cast<size_t>(w) * DK * DV;
+#pragma unroll
+        for (int i = 0; i < CR::NS; ++i) {
+            R.S[i] = a.states[base + tid + NT * i];
+            R.Y[i] = a.Y[base + tid + NT * i];
+        }
+    }
+    const size_t x = (p.tok + tid) * a.H + p.h;
+    R.g = tid < p.L ? a.g[x] : 0.f;
+    R.b = tid < p.L ? a.beta[x] : 0.f;
+}
+
+template <int NT, int DK, int DV, bool GRAD>
+__device__ __forceinline__ void chunk_stage(const ChunkRows<NT, DK, DV, GRAD> &R, ChunkLds<DK, DV> &s,
+                                            float (*v)[DV + kPD], float (*S)[DV + kPD], float (*Y)[DV + kPD]) {
+    using CR = ChunkRows<NT, DK, DV, GRAD>;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < CR::NQ; ++i) {
+        const int e = tid + NT * i;
+        s.q[e / DK][e % DK] = R.q[i];
+        s.k[e / DK][e % DK] = R.k[i];
+    }
+#pragma unroll
+    for (int i = 0; i < CR::NV; ++i) {
+        const int e = tid + NT * i;
+        s.dO[e / DV][e % DV] = R.dO[i];
+        if (GRAD) v[e / DV][e % DV] = R.v[i];
+    }
+    if (GRAD) {
+#pragma unroll
+        for (int i = 0; i < CR::NS; ++i) {
+            const int e = tid + NT * i;
+            S[e / DV][e % DV] = R.S[i];
+            Y[e / DV][e % DV] = R.Y[i];
+        }
     }
     if (tid < kC) {
-        const size_t i = (tok + tid) * a.H + h;
-        s.graw[tid] = tid < L ? a.g[i] : 0.f;
-        s.b[tid] = tid < L ? a.beta[i] : 0.f;
+        s.graw[tid] = R.g;
+        s.b[tid] = R.b;
     }
-    __syncthreads();
+}
+
+// The chunk's keyside from its staged rows (the caller has synchronised after staging):
+// G, gam, eps, P, KG and, for the delta rule, T and W.
+template <int DK, int DV, bool DELTA>
+__device__ void chunk_keyside(ChunkLds<DK, DV> &s) {
+    const int tid = threadIdx.x;
     // G = (lower-triangular ones) g
     mm<kC, 16, kC>([](int i, int j) { return j <= i ? 1.f : 0.f; }, [&](int j, int) { return s.graw[j]; },
                    [&](int i, int c, float x) { if (c == 0) s.G[i] = x; });
@@ -182,10 +246,14 @@ template <int DK, int DV, typename TIn, bool DELTA>
 __global__ __launch_bounds__(kBTM) void bwd_map_kernel(BwdArgs a) {
     __shared__ ChunkLds<DK, DV> s;
     __shared__ float X[kC][DK + kPD];  // diag(gam) Q - P W
-    const int bh = blockIdx.x / a.N, n = blockIdx.x % a.N;
-    size_t tok;
-    int L;
-    chunk_keyside<DK, DV, TIn, DELTA>(a, s, bh, n, tok, L);
+    const int w = blockIdx.x;
+    {
+        ChunkRows<kBTM, DK, DV, false> rows;
+        chunk_load<kBTM, DK, DV, TIn, false>(a, w, rows);
+        chunk_stage<kBTM, DK, DV, false>(rows, s, nullptr, nullptr, nullptr);
+    }
+    __syncthreads();
+    chunk_keyside<DK, DV, DELTA>(s);
     if (DELTA) {
         mm<kC, DK, kC>([&](int i, int j) { return s.P[i][j]; }, [&](int j, int c) { return s.W[j][c]; },
                        [&](int i, int c, float x) { X[i][c] = s.gam[i] * s.q[i][c] - x; });
@@ -193,7 +261,7 @@ __global__ __launch_bounds__(kBTM) void bwd_map_kernel(BwdArgs a) {
         for (int e = threadIdx.x; e < kC * DK; e += kBTM) X[e / DK][e % DK] = s.gam[e / DK] * s.q[e / DK][e % DK];
     }
     __syncthreads();
-    const size_t base = static_cast<size_t>(bh) * a.N + n;
+    const size_t base = static_cast<size_t>(w);
     float *R = a.R + base * DK * DV;
     const int half = static_cast<int>(blockDim.x) / 128;
     mm<DK, DV, kC>([&](int j, int r) { return X[r][j]; }, [&](int r, int i) { return s.dO[r][i]; },
@@ -361,24 +429,19 @@ __global__ __launch_bounds__(kBTG) void bwd_grad_kernel(BwdArgs a) {
     __shared__ ChunkLds<DK, DV> s;
     __shared__ GradLds<DK, DV> u;
     const int tid = threadIdx.x;
-    const int bh = blockIdx.x / a.N, n = blockIdx.x % a.N;
-    const int h = bh % a.H;
-    size_t tok;
-    int L;
-    chunk_keyside<DK, DV, TIn, DELTA>(a, s, bh, n, tok, L);
-    const size_t base = static_cast<size_t>(bh) * a.N + n;
-    const TIn *vin = static_cast<const TIn *>(a.v);
-    for (int e = tid; e < kC * DV; e += kBTG) {
-        const int r = e / DV, c = e % DV;
-        u.v[r][c] = r < L ? load_in(vin, ((tok + r) * a.H + h) * DV + c) : 0.f;
-    }
-    for (int e = tid; e < DK * DV; e += kBTG) {
-        u.S[e / DV][e % DV] = a.states[base * DK * DV + e];
-        u.Yv[e / DV][e % DV] = a.Y[base * DK * DV + e];
+    const int w = blockIdx.x;
+    const ChunkPos pos = chunk_pos(a, w);
+    const size_t tok = pos.tok;
+    const int h = pos.h, L = pos.L;
+    {
+        ChunkRows<kBTG, DK, DV, true> rows;
+        chunk_load<kBTG, DK, DV, TIn, true>(a, w, rows);
+        chunk_stage<kBTG, DK, DV, true>(rows, s, u.v, u.S, u.Yv);
     }
     if (tid < kC)
         for (int m = 0; m < 9; ++m) u.red[m][tid] = 0.f;
     __syncthreads();
+    chunk_keyside<DK, DV, DELTA>(s);
 
     // Delta = T diag(b) V - W S  (decay rule: diag(b) V);  K Y
     if (DELTA) {
@@ -614,6 +677,7 @@ hipError_t launch_backward(const void *q, const void *k, const void *v, const fl
     a.Y = reinterpret_cast<float *>(w + L.Y);
     a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.ds0 = ds0;
     a.T = T; a.H = H; a.BH = B * H; a.N = (T + kC - 1) / kC;
+    a.items = a.BH * a.N;
     a.scale = 1.0f / sqrtf(static_cast<float>(d_k));
     if (T > 0 && dt == GDN_F32) {
         // fp32 q/k/v: the fp32 chunk kernel, again keeping every chunk's start state
