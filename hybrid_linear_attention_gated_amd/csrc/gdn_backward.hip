@@ -23,7 +23,7 @@
 //   dA = -T^T (dW (diag(b gam) K)^T + dDelta (diag(b) V)^T) T^T,  E = diag(b) dA .* Gam
 //   db, dG from the same terms; dg = reverse cumulative sum of dG over the chunk.
 //
-// Three launches after a forward pass that keeps every chunk's start state
+// Three passes after a forward pass that keeps every chunk's start state
 // (gdn_prefill_chunk.hip): bwd_map_kernel (F and R of every chunk, chunks in
 // parallel), bwd_scan_kernel (Y of every chunk, chunks in reverse order; long
 // sequences in two levels of pieces) and bwd_grad_kernel (all gradients, chunks in
@@ -33,24 +33,25 @@
 namespace gdn {
 namespace {
 
+// Launch shapes and LDS padding (overridable at build time for tuning sweeps).
 #ifndef GDN_BWD_THREADS
 #define GDN_BWD_THREADS 1024
 #endif
 #ifndef GDN_BWD_MAP_THREADS
 #define GDN_BWD_MAP_THREADS 512
 #endif
-constexpr int kBT = 256;                   // threads per scan workgroup
-constexpr int kBTM = GDN_BWD_MAP_THREADS;  // threads per map workgroup
-constexpr int kBTG = GDN_BWD_THREADS;      // threads per gradient workgroup
-constexpr int kC = 32;            // tokens per chunk
 #ifndef GDN_BWD_PAD_D
 #define GDN_BWD_PAD_D 2
 #endif
 #ifndef GDN_BWD_PAD_C
 #define GDN_BWD_PAD_C 2
 #endif
-constexpr int kPD = GDN_BWD_PAD_D;  // row padding of d-wide LDS matrices (floats)
-constexpr int kCP = kC + GDN_BWD_PAD_C;  // padded C x C row
+constexpr int kC = 32;                     // tokens per chunk
+constexpr int kBT = 256;                   // threads per scan workgroup
+constexpr int kBTM = GDN_BWD_MAP_THREADS;  // threads per map workgroup
+constexpr int kBTG = GDN_BWD_THREADS;      // threads per gradient workgroup
+constexpr int kPD = GDN_BWD_PAD_D;         // row padding of d-wide LDS matrices (floats)
+constexpr int kCP = kC + GDN_BWD_PAD_C;    // padded C x C row
 
 struct BwdArgs {
     const void *q, *k, *v;
@@ -61,7 +62,6 @@ struct BwdArgs {
     float *Y;             // [BH][N][DK][DV] gradient with respect to each chunk's end state
     float *dq, *dk, *dv, *dg, *dbeta, *ds0;
     int T, H, N, BH;
-    int items;            // chunks of all heads (BH * N)
     float scale;
 };
 
@@ -677,7 +677,6 @@ hipError_t launch_backward(const void *q, const void *k, const void *v, const fl
     a.Y = reinterpret_cast<float *>(w + L.Y);
     a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.ds0 = ds0;
     a.T = T; a.H = H; a.BH = B * H; a.N = (T + kC - 1) / kC;
-    a.items = a.BH * a.N;
     a.scale = 1.0f / sqrtf(static_cast<float>(d_k));
     if (T > 0 && dt == GDN_F32) {
         // fp32 q/k/v: the fp32 chunk kernel, again keeping every chunk's start state
