@@ -44,14 +44,15 @@ namespace {
 #define GDN_BWD_PAD_D 2
 #endif
 #ifndef GDN_BWD_PAD_C
-#define GDN_BWD_PAD_C 2
+#define GDN_BWD_PAD_C 4
 #endif
 constexpr int kC = 32;                     // tokens per chunk
 constexpr int kBT = 256;                   // threads per scan workgroup
 constexpr int kBTM = GDN_BWD_MAP_THREADS;  // threads per map workgroup
 constexpr int kBTG = GDN_BWD_THREADS;      // threads per gradient workgroup
 constexpr int kPD = GDN_BWD_PAD_D;         // row padding of d-wide LDS matrices (floats)
-constexpr int kCP = kC + GDN_BWD_PAD_C;    // padded C x C row
+constexpr int kCP = kC + GDN_BWD_PAD_C;    // padded C x C row (a multiple of 4: float4 row reads)
+static_assert(kCP % 4 == 0, "C x C rows read as float4");
 
 struct BwdArgs {
     const void *q, *k, *v;
@@ -101,7 +102,7 @@ __device__ __forceinline__ void rowsum(FA A, FS store, int w0 = 0, int nw = 0) {
 }
 
 // One chunk's rows and its keyside matrices (shared by the map and gradient kernels).
-template <int DK, int DV> struct ChunkLds {
+template <int DK, int DV> struct alignas(16) ChunkLds {
     float q[kC][DK + kPD], k[kC][DK + kPD];
     float dO[kC][DV + kPD];
     float T[kC][kCP];    // (I + A)^-1 (gated delta)
@@ -111,11 +112,13 @@ template <int DK, int DV> struct ChunkLds {
     float graw[kC], G[kC], gam[kC], eps[kC], b[kC];
 };
 
-// One chunk's rows in registers (NT threads, element e = tid + NT i), loaded from HBM ahead of
-// their use; rows past the end of the sequence are zeros.  GRAD also takes v and the chunk's
-// start state and end-state gradient.
+// One chunk's rows in registers, loaded from HBM ahead of their use; rows past the end of the
+// sequence are zeros.  Thread tid holds a contiguous run of each tensor (elements
+// tid * n .. tid * n + n - 1, inside one row), read with one 4-, 8- or 16-byte load.  GRAD also
+// takes v and the chunk's start state and end-state gradient.
 template <int NT, int DK, int DV, bool GRAD> struct ChunkRows {
     static constexpr int NQ = kC * DK / NT, NV = kC * DV / NT, NS = GRAD ? DK * DV / NT : 1;
+    static_assert(NQ >= 2 && NQ <= 4 && NV >= 2 && NV <= 4 && (!GRAD || NS == 4 || NS == 8), "runs per thread");
     float q[NQ], k[NQ], dO[NV], v[GRAD ? NV : 1], S[NS], Y[NS], g, b;
 };
 
@@ -132,33 +135,56 @@ __device__ __forceinline__ ChunkPos chunk_pos(const BwdArgs &a, int w) {
     return p;
 }
 
+// n consecutive stored values (n = 2 or 4) widened to fp32, or zeros
+template <int n> __device__ __forceinline__ void load_run(const uint16_t *p, bool in, float (&x)[n]) {
+    uint32_t u[n / 2];
+    if (n == 2) u[0] = in ? *reinterpret_cast<const uint32_t *>(p) : 0u;
+    else {
+        const uint2 w = in ? *reinterpret_cast<const uint2 *>(p) : make_uint2(0u, 0u);
+        u[0] = w.x;
+        u[n / 2 - 1] = w.y;
+    }
+#pragma unroll
+    for (int i = 0; i < n / 2; ++i) {
+        x[2 * i] = bf16_bits_to_f32(static_cast<uint16_t>(u[i] & 0xffffu));
+        x[2 * i + 1] = bf16_bits_to_f32(static_cast<uint16_t>(u[i] >> 16));
+    }
+}
+template <int n> __device__ __forceinline__ void load_run(const float *p, bool in, float (&x)[n]) {
+    if (n == 2) {
+        const float2 w = in ? *reinterpret_cast<const float2 *>(p) : make_float2(0.f, 0.f);
+        x[0] = w.x;
+        x[n - 1] = w.y;
+    } else {
+#pragma unroll
+        for (int i = 0; i < n / 4; ++i) {
+            const float4 w = in ? reinterpret_cast<const float4 *>(p)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+            x[4 * i] = w.x; x[4 * i + 1] = w.y; x[4 * i + 2] = w.z; x[4 * i + 3] = w.w;
+        }
+    }
+}
+
 template <int NT, int DK, int DV, typename TIn, bool GRAD>
 __device__ __forceinline__ void chunk_load(const BwdArgs &a, int w, ChunkRows<NT, DK, DV, GRAD> &R) {
     using CR = ChunkRows<NT, DK, DV, GRAD>;
     const int tid = threadIdx.x;
     const ChunkPos p = chunk_pos(a, w);
-    const TIn *q = static_cast<const TIn *>(a.q), *k = static_cast<const TIn *>(a.k);
-#pragma unroll
-    for (int i = 0; i < CR::NQ; ++i) {
-        const int e = tid + NT * i, r = e / DK, c = e % DK;
+    {
+        const int e = tid * CR::NQ, r = e / DK, c = e % DK;
         const size_t x = ((p.tok + r) * a.H + p.h) * DK + c;
-        R.q[i] = r < p.L ? load_in(q, x) : 0.f;
-        R.k[i] = r < p.L ? load_in(k, x) : 0.f;
+        load_run<CR::NQ>(static_cast<const TIn *>(a.q) + x, r < p.L, R.q);
+        load_run<CR::NQ>(static_cast<const TIn *>(a.k) + x, r < p.L, R.k);
     }
-#pragma unroll
-    for (int i = 0; i < CR::NV; ++i) {
-        const int e = tid + NT * i, r = e / DV, c = e % DV;
+    {
+        const int e = tid * CR::NV, r = e / DV, c = e % DV;
         const size_t x = ((p.tok + r) * a.H + p.h) * DV + c;
-        R.dO[i] = r < p.L ? a.d_o[x] : 0.f;
-        if (GRAD) R.v[i] = r < p.L ? load_in(static_cast<const TIn *>(a.v), x) : 0.f;
+        load_run<CR::NV>(a.d_o + x, r < p.L, R.dO);
+        if constexpr (GRAD) load_run<CR::NV>(static_cast<const TIn *>(a.v) + x, r < p.L, R.v);
     }
-    if (GRAD) {
-        const size_t base = static_cast<size_t>(w) * DK * DV;
-#pragma unroll
-        for (int i = 0; i < CR::NS; ++i) {
-            R.S[i] = a.states[base + tid + NT * i];
-            R.Y[i] = a.Y[base + tid + NT * i];
-        }
+    if constexpr (GRAD) {
+        const size_t x = static_cast<size_t>(w) * DK * DV + static_cast<size_t>(tid) * CR::NS;
+        load_run<CR::NS>(a.states + x, true, R.S);
+        load_run<CR::NS>(a.Y + x, true, R.Y);
     }
     const size_t x = (p.tok + tid) * a.H + p.h;
     R.g = tid < p.L ? a.g[x] : 0.f;
@@ -172,20 +198,20 @@ __device__ __forceinline__ void chunk_stage(const ChunkRows<NT, DK, DV, GRAD> &R
     const int tid = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < CR::NQ; ++i) {
-        const int e = tid + NT * i;
+        const int e = tid * CR::NQ + i;
         s.q[e / DK][e % DK] = R.q[i];
         s.k[e / DK][e % DK] = R.k[i];
     }
 #pragma unroll
     for (int i = 0; i < CR::NV; ++i) {
-        const int e = tid + NT * i;
+        const int e = tid * CR::NV + i;
         s.dO[e / DV][e % DV] = R.dO[i];
         if (GRAD) v[e / DV][e % DV] = R.v[i];
     }
     if (GRAD) {
 #pragma unroll
         for (int i = 0; i < CR::NS; ++i) {
-            const int e = tid + NT * i;
+            const int e = tid * CR::NS + i;
             S[e / DV][e % DV] = R.S[i];
             Y[e / DV][e % DV] = R.Y[i];
         }
@@ -224,10 +250,19 @@ __device__ void chunk_keyside(ChunkLds<DK, DV> &s) {
         const int c = tid;
         float t[kC];
 #pragma unroll
+        for (int r = 0; r < kC; ++r) t[r] = 0.f;
+#pragma unroll
         for (int r = 0; r < kC; ++r) {
+            // row r of KG four at a time (KG[r][j] = 0 for j >= r, and t[j] = 0 there still)
             float acc = 0.f;
 #pragma unroll
-            for (int j = 0; j < r; ++j) acc = fmaf(s.KG[r][j], t[j], acc);
+            for (int j = 0; j < r; j += 4) {
+                const float4 kg = *reinterpret_cast<const float4 *>(&s.KG[r][j]);
+                acc = fmaf(kg.x, t[j], acc);
+                acc = fmaf(kg.y, t[j + 1], acc);
+                acc = fmaf(kg.z, t[j + 2], acc);
+                acc = fmaf(kg.w, t[j + 3], acc);
+            }
             t[r] = (r == c ? 1.f : 0.f) - s.b[r] * acc;
         }
 #pragma unroll
@@ -403,7 +438,7 @@ __global__ __launch_bounds__(kBT) void bwd_scan_kernel(ScanArgs a) {
 }
 
 // ---- all gradients of one chunk -----------------------------------------------
-template <int DK, int DV> struct GradLds {
+template <int DK, int DV> struct alignas(16) GradLds {
     float v[kC][DV + kPD];
     float S[DK][DV + kPD], Yv[DK][DV + kPD];
     float D[kC][DV + kPD];     // Delta
@@ -455,7 +490,9 @@ __global__ __launch_bounds__(kBTG) void bwd_grad_kernel(BwdArgs a) {
     __syncthreads();
     if (DELTA) {
         mm<kC, DV, DK>([&](int i, int j) { return s.W[i][j]; }, [&](int j, int c) { return u.S[j][c]; },
-                       [&](int i, int c, float x) { u.D[i][c] -= x; });
+                       [&](int i, int c, float x) { u.D[i][c] -= x; }, 0, 8);
+        rowsum<DK, DV>([&](int j, int i) { return u.Yv[j][i] * u.S[j][i]; }, [&](int j, float x) { u.red64[j] = x; },
+                       8, 4);
         __syncthreads();
     }
     // dDelta = scale P^T dO + diag(eps) K Y;  dP = scale tril(dO Delta^T)
@@ -467,13 +504,16 @@ __global__ __launch_bounds__(kBTG) void bwd_grad_kernel(BwdArgs a) {
                        u.dPg[r][j] = dp * (j <= r ? expf(s.G[r] - s.G[j]) : 0.f);
                        u.X1[r][j] = dp * s.P[r][j];
                    },
-                   8, 8);
+                   8, 4);
+    if (!DELTA)
+        rowsum<DK, DV>([&](int j, int i) { return u.Yv[j][i] * u.S[j][i]; }, [&](int j, float x) { u.red64[j] = x; },
+                       12, 4);
     __syncthreads();
     // row reductions for the gate and write-strength gradients: P, the end-state decay
     rowsum<kC, kC>([&](int i, int k) { return u.X1[i][k]; }, [&](int i, float x) { u.red[0][i] = x; }, 8, 2);
     rowsum<kC, kC>([&](int i, int k) { return u.X1[k][i]; }, [&](int i, float x) { u.red[1][i] = x; }, 10, 2);
     rowsum<kC, DV>([&](int i, int c) { return u.KY[i][c] * u.D[i][c]; }, [&](int i, float x) { u.red[2][i] = x; }, 12, 2);
-    rowsum<DK, DV>([&](int j, int i) { return u.Yv[j][i] * u.S[j][i]; }, [&](int j, float x) { u.red64[j] = x; }, 14, 2);
+
     // dQ = scale diag(gam) dO S^T (+ its gate term) + (dP .* Gam) K, into W's buffer
     mm<kC, DK, DV>([&](int r, int i) { return s.dO[r][i]; }, [&](int i, int c) { return u.S[c][i]; },
                    [&](int r, int c, float x) { s.W[r][c] = a.scale * s.gam[r] * x; }, 0, 8);
