@@ -245,29 +245,47 @@ __device__ void chunk_keyside(ChunkLds<DK, DV> &s) {
                        half, half);
     __syncthreads();
     if (!DELTA) return;
-    // T = (I + diag(b) KG)^-1 by forward substitution, one column per thread
-    if (tid < kC) {
-        const int c = tid;
-        float t[kC];
+    // T = (I + diag(b) KG)^-1.  Its two diagonal 16 x 16 blocks by forward substitution, one
+    // column per lane (the first block on wavefront 0, the second on wavefront 1, so the two run
+    // at once); the upper-right block is zero; the lower-left one is T21 = -T22 (A21 T11), with
+    // A21 = diag(b) KG restricted to those rows and columns, by two 16 x 16 products.
+    static_assert(kC == 32, "two diagonal blocks of 16");
+    {
+        const int wave = tid / 64, c = tid % 64;
+        if (wave < 2 && c < 16) {
+            const int o = 16 * wave;
+            float t[16];
 #pragma unroll
-        for (int r = 0; r < kC; ++r) t[r] = 0.f;
+            for (int r = 0; r < 16; ++r) t[r] = 0.f;
 #pragma unroll
-        for (int r = 0; r < kC; ++r) {
-            // row r of KG four at a time (KG[r][j] = 0 for j >= r, and t[j] = 0 there still)
-            float acc = 0.f;
+            for (int r = 0; r < 16; ++r) {
+                // row r of the block four at a time (KG is zero on and above the diagonal, and
+                // t[j] is still zero for j >= r)
+                float acc = 0.f;
 #pragma unroll
-            for (int j = 0; j < r; j += 4) {
-                const float4 kg = *reinterpret_cast<const float4 *>(&s.KG[r][j]);
-                acc = fmaf(kg.x, t[j], acc);
-                acc = fmaf(kg.y, t[j + 1], acc);
-                acc = fmaf(kg.z, t[j + 2], acc);
-                acc = fmaf(kg.w, t[j + 3], acc);
+                for (int j = 0; j < r; j += 4) {
+                    const float4 kg = *reinterpret_cast<const float4 *>(&s.KG[o + r][o + j]);
+                    acc = fmaf(kg.x, t[j], acc);
+                    acc = fmaf(kg.y, t[j + 1], acc);
+                    acc = fmaf(kg.z, t[j + 2], acc);
+                    acc = fmaf(kg.w, t[j + 3], acc);
+                }
+                t[r] = (r == c ? 1.f : 0.f) - s.b[o + r] * acc;
             }
-            t[r] = (r == c ? 1.f : 0.f) - s.b[r] * acc;
-        }
 #pragma unroll
-        for (int r = 0; r < kC; ++r) s.T[r][c] = t[r];
+            for (int r = 0; r < 16; ++r) s.T[o + r][o + c] = t[r];
+        } else if (wave == 2) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s.T[4 * r + c / 16][16 + c % 16] = 0.f;
+        }
     }
+    __syncthreads();
+    // A21 T11, parked in W's rows (W is written after T)
+    mm<16, 16, 16>([&](int i, int j) { return s.b[16 + i] * s.KG[16 + i][j]; }, [&](int j, int c) { return s.T[j][c]; },
+                   [&](int i, int c, float x) { s.W[i][c] = x; }, 0, 1);
+    __syncthreads();
+    mm<16, 16, 16>([&](int i, int j) { return s.T[16 + i][16 + j]; }, [&](int j, int c) { return s.W[j][c]; },
+                   [&](int i, int c, float x) { s.T[16 + i][c] = -x; }, 0, 1);
     __syncthreads();
     // W = T diag(b gam) K
     mm<kC, DK, kC>([&](int i, int j) { return s.T[i][j]; },
