@@ -101,6 +101,11 @@ __device__ __forceinline__ void rowsum(FA A, FS store, int w0 = 0, int nw = 0) {
     mm<M, 16, K>(A, [](int, int) { return 1.f; }, [&](int i, int j, float x) { if (j == 0) store(i, x); }, w0, nw);
 }
 
+// x as held by lane l of the wavefront (l a constant; a uniform value)
+__device__ __forceinline__ float lane_value(float x, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+
 // One chunk's rows and its keyside matrices (shared by the map and gradient kernels).
 template <int DK, int DV> struct alignas(16) ChunkLds {
     float q[kC][DK + kPD], k[kC][DK + kPD];
@@ -253,24 +258,23 @@ __device__ void chunk_keyside(ChunkLds<DK, DV> &s) {
     {
         const int wave = tid / 64, c = tid % 64;
         if (wave < 2 && c < 16) {
+            // lane c holds row c of the block and b of that row; row r reaches every lane by a
+            // read of lane r, so the substitution waits on no LDS access
             const int o = 16 * wave;
+            float kr[16];
+#pragma unroll
+            for (int j = 0; j < 16; j += 4) {
+                const float4 x = *reinterpret_cast<const float4 *>(&s.KG[o + c][o + j]);
+                kr[j] = x.x; kr[j + 1] = x.y; kr[j + 2] = x.z; kr[j + 3] = x.w;
+            }
+            const float br = s.b[o + c];
             float t[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) t[r] = 0.f;
-#pragma unroll
             for (int r = 0; r < 16; ++r) {
-                // row r of the block four at a time (KG is zero on and above the diagonal, and
-                // t[j] is still zero for j >= r)
                 float acc = 0.f;
 #pragma unroll
-                for (int j = 0; j < r; j += 4) {
-                    const float4 kg = *reinterpret_cast<const float4 *>(&s.KG[o + r][o + j]);
-                    acc = fmaf(kg.x, t[j], acc);
-                    acc = fmaf(kg.y, t[j + 1], acc);
-                    acc = fmaf(kg.z, t[j + 2], acc);
-                    acc = fmaf(kg.w, t[j + 3], acc);
-                }
-                t[r] = (r == c ? 1.f : 0.f) - s.b[o + r] * acc;
+                for (int j = 0; j < r; ++j) acc = fmaf(lane_value(kr[j], r), t[j], acc);
+                t[r] = fmaf(-lane_value(br, r), acc, r == c ? 1.f : 0.f);
             }
 #pragma unroll
             for (int r = 0; r < 16; ++r) s.T[o + r][o + c] = t[r];
