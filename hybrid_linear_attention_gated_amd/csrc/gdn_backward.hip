@@ -53,6 +53,8 @@ constexpr int kBTG = GDN_BWD_THREADS;      // threads per gradient workgroup
 constexpr int kPD = GDN_BWD_PAD_D;         // row padding of d-wide LDS matrices (floats)
 constexpr int kCP = kC + GDN_BWD_PAD_C;    // padded C x C row (a multiple of 4: float4 row reads)
 static_assert(kCP % 4 == 0, "C x C rows read as float4");
+// A chunk's stored keyside, in floats: T, KG, P (C x C each), W (C x DK), G, gam, eps (C each)
+template <int DK> constexpr int ks_floats() { return 3 * kC * kC + kC * DK + 3 * kC; }
 
 struct BwdArgs {
     const void *q, *k, *v;
@@ -61,6 +63,7 @@ struct BwdArgs {
     float *F;             // [BH][N][DK][DK] backward map of each chunk
     float *R;             // [BH][N][DK][DV] its constant term
     float *Y;             // [BH][N][DK][DV] gradient with respect to each chunk's end state
+    float *KS;            // [BH][N] keyside of each chunk: T, KG, P, W, G, gam, eps (ks_floats)
     float *dq, *dk, *dv, *dg, *dbeta, *ds0;
     int T, H, N, BH;
     float scale;
@@ -298,6 +301,43 @@ __device__ void chunk_keyside(ChunkLds<DK, DV> &s) {
     __syncthreads();
 }
 
+// The keyside the map kernel stored, in registers (1,024 threads, d_k = 64): thread tid holds
+// float4 number tid of T | KG | P | W rows 0-15 (4,096 floats), float tid of W rows 16-31, and for
+// tid < 96 one of G | gam | eps.  The decay rule reads only P and the gates.
+struct KsRows {
+    float4 m;
+    float w, gate;
+};
+template <int DK, bool DELTA>
+__device__ __forceinline__ void keyside_load(const BwdArgs &a, int w, KsRows &R) {
+    static_assert(kBTG == 1024 && DK == 64 && kC == 32, "laid out for 1,024 threads and d_k = 64");
+    const int tid = threadIdx.x;
+    const float *ks = a.KS + static_cast<size_t>(w) * ks_floats<DK>();
+    // (the decay rule: every wavefront reads a float4 of P, and only P's own ones stage theirs;
+    // an unconditional load keeps R in registers)
+    R.m = reinterpret_cast<const float4 *>(ks)[DELTA ? tid : kC * kC / 2 + tid % (kC * kC / 4)];
+    if (DELTA) R.w = ks[4 * kBTG + tid];
+    if (tid < 3 * kC) R.gate = ks[3 * kC * kC + kC * DK + tid];
+}
+template <int DK, int DV, bool DELTA>
+__device__ __forceinline__ void keyside_stage(const KsRows &R, ChunkLds<DK, DV> &s) {
+    const int tid = threadIdx.x, e = 4 * tid, m = e / (kC * kC), i = e % (kC * kC);
+    if (m < 3) {
+        // (m is uniform over each wavefront)
+        if (m == 2) *reinterpret_cast<float4 *>(&s.P[i / kC][i % kC]) = R.m;
+        else if (DELTA && m == 1) *reinterpret_cast<float4 *>(&s.KG[i / kC][i % kC]) = R.m;
+        else if (DELTA) *reinterpret_cast<float4 *>(&s.T[i / kC][i % kC]) = R.m;
+    } else if (DELTA) {
+        float *row = &s.W[i / DK][i % DK];
+        *reinterpret_cast<float2 *>(row) = make_float2(R.m.x, R.m.y);
+        *reinterpret_cast<float2 *>(row + 2) = make_float2(R.m.z, R.m.w);
+    }
+    if (DELTA) s.W[(kC * kC + tid) / DK][(kC * kC + tid) % DK] = R.w;
+    if (tid < kC) s.G[tid] = R.gate;
+    else if (tid < 2 * kC) s.gam[tid - kC] = R.gate;
+    else if (tid < 3 * kC) s.eps[tid - 2 * kC] = R.gate;
+}
+
 // ---- F and R of every chunk ---------------------------------------------------
 template <int DK, int DV, typename TIn, bool DELTA>
 __global__ __launch_bounds__(kBTM) void bwd_map_kernel(BwdArgs a) {
@@ -311,6 +351,25 @@ __global__ __launch_bounds__(kBTM) void bwd_map_kernel(BwdArgs a) {
     }
     __syncthreads();
     chunk_keyside<DK, DV, DELTA>(s);
+    {
+        // the keyside, for the gradient kernel
+        float *ks = a.KS + static_cast<size_t>(w) * ks_floats<DK>();
+        for (int e = threadIdx.x; e < 3 * kC * kC / 4; e += kBTM) {
+            const int m = e / (kC * kC / 4), r = (e / (kC / 4)) % kC, c = 4 * (e % (kC / 4));
+            float4 *out = reinterpret_cast<float4 *>(ks) + e;
+            if (m == 2) *out = *reinterpret_cast<const float4 *>(&s.P[r][c]);
+            else if (DELTA && m == 1) *out = *reinterpret_cast<const float4 *>(&s.KG[r][c]);
+            else if (DELTA) *out = *reinterpret_cast<const float4 *>(&s.T[r][c]);
+        }
+        if (DELTA)
+            for (int e = threadIdx.x; e < kC * DK / 2; e += kBTM)
+                reinterpret_cast<float2 *>(ks + 3 * kC * kC)[e] =
+                    *reinterpret_cast<const float2 *>(&s.W[e / (DK / 2)][2 * (e % (DK / 2))]);
+        if (threadIdx.x < 3 * kC) {
+            const int r = threadIdx.x % kC, m = threadIdx.x / kC;
+            ks[3 * kC * kC + kC * DK + threadIdx.x] = m == 0 ? s.G[r] : m == 1 ? s.gam[r] : s.eps[r];
+        }
+    }
     if (DELTA) {
         mm<kC, DK, kC>([&](int i, int j) { return s.P[i][j]; }, [&](int j, int c) { return s.W[j][c]; },
                        [&](int i, int c, float x) { X[i][c] = s.gam[i] * s.q[i][c] - x; });
@@ -491,14 +550,17 @@ __global__ __launch_bounds__(kBTG) void bwd_grad_kernel(BwdArgs a) {
     const size_t tok = pos.tok;
     const int h = pos.h, L = pos.L;
     {
+        // the chunk's rows and the keyside its map pass stored
         ChunkRows<kBTG, DK, DV, true> rows;
+        KsRows ks{};
         chunk_load<kBTG, DK, DV, TIn, true>(a, w, rows);
+        keyside_load<DK, DELTA>(a, w, ks);
         chunk_stage<kBTG, DK, DV, true>(rows, s, u.v, u.S, u.Yv);
+        keyside_stage<DK, DV, DELTA>(ks, s);
     }
     if (tid < kC)
         for (int m = 0; m < 9; ++m) u.red[m][tid] = 0.f;
     __syncthreads();
-    chunk_keyside<DK, DV, DELTA>(s);
 
     // Delta = T diag(b) V - W S  (decay rule: diag(b) V);  K Y
     if (DELTA) {
@@ -691,7 +753,7 @@ hipError_t run_backward(BwdArgs &a, gdn_dtype dt, const ScanPlan &plan, float *G
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 struct BwdLayout {
-    size_t fwd, o, sfin, states, F, R, Y, Gp, cp, yend, total;
+    size_t fwd, o, sfin, states, F, R, Y, KS, Gp, cp, yend, total;
 };
 BwdLayout bwd_layout(int B, int T, int H, int dk, int dv) {
     const size_t BH = static_cast<size_t>(B) * H, N = (static_cast<size_t>(T) + kC - 1) / kC;
@@ -704,6 +766,7 @@ BwdLayout bwd_layout(int B, int T, int H, int dk, int dv) {
     L.F = off; off += align256(BH * N * dk * dk * 4);
     L.R = off; off += align256(BH * N * dk * dv * 4);
     L.Y = off; off += align256(BH * N * dk * dv * 4);
+    L.KS = off; off += align256(BH * N * ks_floats<64>() * 4);
     const ScanPlan plan = scan_plan(static_cast<int>(BH), static_cast<int>(N));
     const size_t PP = plan.P > 1 ? static_cast<size_t>(plan.P) : 0;
     L.Gp = off; off += align256(BH * PP * dk * dk * 4);
@@ -737,6 +800,7 @@ hipError_t launch_backward(const void *q, const void *k, const void *v, const fl
     a.F = reinterpret_cast<float *>(w + L.F);
     a.R = reinterpret_cast<float *>(w + L.R);
     a.Y = reinterpret_cast<float *>(w + L.Y);
+    a.KS = reinterpret_cast<float *>(w + L.KS);
     a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.ds0 = ds0;
     a.T = T; a.H = H; a.BH = B * H; a.N = (T + kC - 1) / kC;
     a.scale = 1.0f / sqrtf(static_cast<float>(d_k));
