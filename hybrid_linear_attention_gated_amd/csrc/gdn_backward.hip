@@ -341,8 +341,7 @@ __device__ __forceinline__ void keyside_stage(const KsRows &R, ChunkLds<DK, DV> 
 // ---- F and R of every chunk ---------------------------------------------------
 template <int DK, int DV, typename TIn, bool DELTA>
 __global__ __launch_bounds__(kBTM) void bwd_map_kernel(BwdArgs a) {
-    __shared__ ChunkLds<DK, DV> s;
-    __shared__ float X[kC][DK + kPD];  // diag(gam) Q - P W
+    __shared__ ChunkLds<DK, DV> s;  // (its q rows become diag(gam) Q - P W)
     const int w = blockIdx.x;
     {
         ChunkRows<kBTM, DK, DV, false> rows;
@@ -371,16 +370,18 @@ __global__ __launch_bounds__(kBTM) void bwd_map_kernel(BwdArgs a) {
         }
     }
     if (DELTA) {
+        // in place: each element is read and rewritten by the thread that computes it, and the
+        // product reads P and W only
         mm<kC, DK, kC>([&](int i, int j) { return s.P[i][j]; }, [&](int j, int c) { return s.W[j][c]; },
-                       [&](int i, int c, float x) { X[i][c] = s.gam[i] * s.q[i][c] - x; });
+                       [&](int i, int c, float x) { s.q[i][c] = s.gam[i] * s.q[i][c] - x; });
     } else {
-        for (int e = threadIdx.x; e < kC * DK; e += kBTM) X[e / DK][e % DK] = s.gam[e / DK] * s.q[e / DK][e % DK];
+        for (int e = threadIdx.x; e < kC * DK; e += kBTM) s.q[e / DK][e % DK] *= s.gam[e / DK];
     }
     __syncthreads();
     const size_t base = static_cast<size_t>(w);
     float *R = a.R + base * DK * DV;
     const int half = static_cast<int>(blockDim.x) / 128;
-    mm<DK, DV, kC>([&](int j, int r) { return X[r][j]; }, [&](int r, int i) { return s.dO[r][i]; },
+    mm<DK, DV, kC>([&](int j, int r) { return s.q[r][j]; }, [&](int r, int i) { return s.dO[r][i]; },
                    [&](int j, int i, float x) { R[j * DV + i] = a.scale * x; }, 0, half);
     float *F = a.F + base * DK * DK;
     const float gl = s.gam[kC - 1];
