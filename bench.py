@@ -159,13 +159,13 @@ def main():
     pslots = np.random.default_rng(12).permutation(2 * dw.B)[:dw.B].astype(np.int32)
     ppool = torch.zeros((2 * dw.B, din["conv_state"].shape[1], 3), device=dev, dtype=torch.float32)
     pflat = {kk: din[kk][:, 0].contiguous() for kk in ("xq", "xk", "xv", "a_raw", "b_raw")}
-    pouts = tuple(torch.empty_like(t) for t in (pflat["xq"], pflat["xk"], pflat["xv"], pflat["a_raw"], pflat["b_raw"]))
+    pool_outs = tuple(torch.empty_like(pflat[kk]) for kk in ("xq", "xk", "xv", "a_raw", "b_raw"))
     pws = torch.empty(max(gdn.gdn_prepare_varlen_workspace_size(dw.B), 1), device=dev, dtype=torch.uint8)
 
     def prepare_decode_pool():
         gdn.prepare_varlen(pflat["xq"], pflat["xk"], pflat["xv"], din["conv_weight"], pflat["a_raw"], pflat["b_raw"],
                            pcu, ppool, slots=pslots, decay_rate=din["decay_rate"], gate_bias=din["gate_bias"],
-                           outs=pouts, workspace=pws)
+                           outs=pool_outs, workspace=pws)
 
     def prepare():
         gdn.prepare(pin["xq"], pin["xk"], pin["xv"], pin["conv_weight"], pin["a_raw"], pin["b_raw"],

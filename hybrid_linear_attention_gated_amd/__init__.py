@@ -198,7 +198,9 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
-def _check(t, name, dtype=None):
+def _check(t, name, dtype=None, shape=None):
+    """A GPU tensor (or None) of the given dtype and shape: the C ABI takes bare pointers, so a
+    buffer of the wrong size would be read or written out of bounds."""
     import torch
     if t is None:
         return
@@ -208,6 +210,8 @@ def _check(t, name, dtype=None):
         raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
 
 
 def workspace_bytes(B, T, H, d_k, d_v, chunk, qkv_dtype) -> int:
@@ -224,18 +228,19 @@ def chunk_prefill(q, k, v, g, beta, initial_state=None, chunk=64, *, out=None, f
     B, T, H, d_k = q.shape
     d_v = v.shape[-1]
     dt = _dtype_code(q)
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _check(t, n, q.dtype)
-    _check(g, "g", torch.float32)
-    _check(beta, "beta", torch.float32)
-    _check(initial_state, "initial_state", torch.float32)
+    _check(q, "q", q.dtype)
+    _check(k, "k", q.dtype, (B, T, H, d_k))
+    _check(v, "v", q.dtype, (B, T, H, d_v))
+    _check(g, "g", torch.float32, (B, T, H))
+    _check(beta, "beta", torch.float32, (B, T, H))
+    _check(initial_state, "initial_state", torch.float32, (B, H, d_k, d_v))
     dev = q.device
     if out is None:
         out = torch.empty((B, T, H, d_v), device=dev, dtype=torch.float32)
     if final_state is None:
         final_state = torch.empty((B, H, d_k, d_v), device=dev, dtype=torch.float32)
-    _check(out, "out", torch.float32)
-    _check(final_state, "final_state", torch.float32)
+    _check(out, "out", torch.float32, (B, T, H, d_v))
+    _check(final_state, "final_state", torch.float32, (B, H, d_k, d_v))
     need = workspace_bytes(B, T, H, d_k, d_v, chunk, dt)
     if workspace is None and need > 0:
         workspace = torch.empty(need, device=dev, dtype=torch.uint8)
@@ -257,14 +262,15 @@ def decode_step(q, k, v, g, beta, state, *, out=None, stream=None, rule=GDN_RULE
     N, H, d_k = q.shape
     d_v = v.shape[-1]
     dt = _dtype_code(q)
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _check(t, n, q.dtype)
-    _check(g, "g", torch.float32)
-    _check(beta, "beta", torch.float32)
-    _check(state, "state", torch.float32)
+    _check(q, "q", q.dtype)
+    _check(k, "k", q.dtype, (N, H, d_k))
+    _check(v, "v", q.dtype, (N, H, d_v))
+    _check(g, "g", torch.float32, (N, H))
+    _check(beta, "beta", torch.float32, (N, H))
+    _check(state, "state", torch.float32, (N, H, d_k, d_v))
     if out is None:
         out = torch.empty((N, H, d_v), device=q.device, dtype=torch.float32)
-    _check(out, "out", torch.float32)
+    _check(out, "out", torch.float32, (N, H, d_v))
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     st = gdn_decode_step_rule(rule, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
@@ -283,15 +289,18 @@ def decode_step_slots(q, k, v, g, beta, state_pool, slots, *, out=None, stream=N
     N, H, d_k = q.shape
     d_v = v.shape[-1]
     dt = _dtype_code(q)
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _check(t, n, q.dtype)
-    _check(g, "g", torch.float32)
-    _check(beta, "beta", torch.float32)
+    _check(q, "q", q.dtype)
+    _check(k, "k", q.dtype, (N, H, d_k))
+    _check(v, "v", q.dtype, (N, H, d_v))
+    _check(g, "g", torch.float32, (N, H))
+    _check(beta, "beta", torch.float32, (N, H))
     _check(state_pool, "state_pool", torch.float32)
-    _check(slots, "slots", torch.int32)
+    if state_pool is not None:
+        _check(state_pool, "state_pool", torch.float32, (state_pool.shape[0], H, d_k, d_v))
+    _check(slots, "slots", torch.int32, (N,))
     if out is None:
         out = torch.empty((N, H, d_v), device=q.device, dtype=torch.float32)
-    _check(out, "out", torch.float32)
+    _check(out, "out", torch.float32, (N, H, d_v))
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     st = gdn_decode_step_slots(rule, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool),
@@ -312,21 +321,25 @@ def prepare(xq, xk, xv, conv_weight, a_raw, b_raw, *, decay_rate=None, gate_bias
     B, T, H, d_k = xq.shape
     d_v = xv.shape[-1]
     dt = _dtype_code(xq)
-    for t, n in ((xq, "xq"), (xk, "xk"), (xv, "xv")):
-        _check(t, n, xq.dtype)
-    for t, n in ((conv_weight, "conv_weight"), (a_raw, "a_raw"), (b_raw, "b_raw"), (decay_rate, "decay_rate"),
-                 (gate_bias, "gate_bias"), (conv_state, "conv_state"), (conv_state_out, "conv_state_out")):
-        _check(t, n, torch.float32)
+    C = H * (2 * d_k + d_v)
+    _check(xq, "xq", xq.dtype)
+    _check(xk, "xk", xq.dtype, (B, T, H, d_k))
+    _check(xv, "xv", xq.dtype, (B, T, H, d_v))
+    for t, n, shp in ((conv_weight, "conv_weight", (C, 4)), (a_raw, "a_raw", (B, T, H)), (b_raw, "b_raw", (B, T, H)),
+                      (decay_rate, "decay_rate", (H,)), (gate_bias, "gate_bias", (H,)),
+                      (conv_state, "conv_state", (B, C, 3)), (conv_state_out, "conv_state_out", (B, C, 3))):
+        _check(t, n, torch.float32, shp)
     dev = xq.device
     if outs is None:
         outs = (torch.empty_like(xq), torch.empty_like(xk), torch.empty_like(xv),
                 torch.empty((B, T, H), device=dev, dtype=torch.float32),
                 torch.empty((B, T, H), device=dev, dtype=torch.float32))
     q, k, v, g, beta = outs
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _check(t, n, xq.dtype)
-    _check(g, "g", torch.float32)
-    _check(beta, "beta", torch.float32)
+    _check(q, "q", xq.dtype, (B, T, H, d_k))
+    _check(k, "k", xq.dtype, (B, T, H, d_k))
+    _check(v, "v", xq.dtype, (B, T, H, d_v))
+    _check(g, "g", torch.float32, (B, T, H))
+    _check(beta, "beta", torch.float32, (B, T, H))
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
     st = gdn_prepare(_ptr(xq), _ptr(xk), _ptr(xv), _ptr(conv_weight), _ptr(a_raw), _ptr(b_raw), _ptr(decay_rate),
@@ -346,19 +359,22 @@ def chunk_backward(q, k, v, g, beta, d_o, initial_state=None, d_final_state=None
     B, T, H, d_k = q.shape
     d_v = v.shape[-1]
     dt = _dtype_code(q)
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _check(t, n, q.dtype)
-    for t, n in ((g, "g"), (beta, "beta"), (d_o, "d_o"), (initial_state, "initial_state"),
-                 (d_final_state, "d_final_state")):
-        _check(t, n, torch.float32)
+    _check(q, "q", q.dtype)
+    _check(k, "k", q.dtype, (B, T, H, d_k))
+    _check(v, "v", q.dtype, (B, T, H, d_v))
+    for t, n, shp in ((g, "g", (B, T, H)), (beta, "beta", (B, T, H)), (d_o, "d_o", (B, T, H, d_v)),
+                      (initial_state, "initial_state", (B, H, d_k, d_v)),
+                      (d_final_state, "d_final_state", (B, H, d_k, d_v))):
+        _check(t, n, torch.float32, shp)
     dev = q.device
     if outs is None:
         f32 = dict(device=dev, dtype=torch.float32)
         outs = (torch.empty((B, T, H, d_k), **f32), torch.empty((B, T, H, d_k), **f32),
                 torch.empty((B, T, H, d_v), **f32), torch.empty((B, T, H), **f32), torch.empty((B, T, H), **f32),
                 torch.empty((B, H, d_k, d_v), **f32) if want_d_initial else None)
-    for t, n in zip(outs, ("dq", "dk", "dv", "dg", "dbeta", "d_initial_state")):
-        _check(t, n, torch.float32)
+    shapes = ((B, T, H, d_k), (B, T, H, d_k), (B, T, H, d_v), (B, T, H), (B, T, H), (B, H, d_k, d_v))
+    for t, n, shp in zip(outs, ("dq", "dk", "dv", "dg", "dbeta", "d_initial_state"), shapes):
+        _check(t, n, torch.float32, shp)
     need = int(gdn_chunk_backward_workspace_size(B, T, H, d_k, d_v, dt))
     if workspace is None and need > 0:
         workspace = torch.empty(need, device=dev, dtype=torch.uint8)
@@ -413,17 +429,26 @@ def prepare_varlen(xq, xk, xv, conv_weight, a_raw, b_raw, cu_seqlens, conv_pool,
     T, H, d_k = xq.shape
     d_v = xv.shape[-1]
     dt = _dtype_code(xq)
-    for t, n in ((xq, "xq"), (xk, "xk"), (xv, "xv")):
-        _check(t, n, xq.dtype)
-    for t, n in ((conv_weight, "conv_weight"), (a_raw, "a_raw"), (b_raw, "b_raw"), (decay_rate, "decay_rate"),
-                 (gate_bias, "gate_bias"), (conv_pool, "conv_pool")):
-        _check(t, n, torch.float32)
+    C = H * (2 * d_k + d_v)
+    _check(xq, "xq", xq.dtype)
+    _check(xk, "xk", xq.dtype, (T, H, d_k))
+    _check(xv, "xv", xq.dtype, (T, H, d_v))
+    for t, n, shp in ((conv_weight, "conv_weight", (C, 4)), (a_raw, "a_raw", (T, H)), (b_raw, "b_raw", (T, H)),
+                      (decay_rate, "decay_rate", (H,)), (gate_bias, "gate_bias", (H,))):
+        _check(t, n, torch.float32, shp)
+    _check(conv_pool, "conv_pool", torch.float32)
+    if conv_pool is not None:
+        _check(conv_pool, "conv_pool", torch.float32, (conv_pool.shape[0], C, 3))
     cu, sl, hi = _host_i32(cu_seqlens), _host_i32(slots), _host_i32(has_initial)
     S = len(cu) - 1
     dev = xq.device
     if outs is None:
         outs = (torch.empty_like(xq), torch.empty_like(xk), torch.empty_like(xv),
                 torch.empty((T, H), device=dev, dtype=torch.float32), torch.empty((T, H), device=dev, dtype=torch.float32))
+    for t, n, dtp, shp in zip(outs, ("q", "k", "v", "g", "beta"), (xq.dtype, xq.dtype, xq.dtype, torch.float32,
+                                                                  torch.float32),
+                              ((T, H, d_k), (T, H, d_k), (T, H, d_v), (T, H), (T, H))):
+        _check(t, n, dtp, shp)
     need = int(gdn_prepare_varlen_workspace_size(S))
     if workspace is None and need > 0:
         workspace = torch.empty(need, device=dev, dtype=torch.uint8)
@@ -450,16 +475,19 @@ def chunk_prefill_varlen(q, k, v, g, beta, cu_seqlens, state_pool, slots=None, h
     T, H, d_k = q.shape
     d_v = v.shape[-1]
     dt = _dtype_code(q)
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _check(t, n, q.dtype)
-    _check(g, "g", torch.float32)
-    _check(beta, "beta", torch.float32)
+    _check(q, "q", q.dtype)
+    _check(k, "k", q.dtype, (T, H, d_k))
+    _check(v, "v", q.dtype, (T, H, d_v))
+    _check(g, "g", torch.float32, (T, H))
+    _check(beta, "beta", torch.float32, (T, H))
     _check(state_pool, "state_pool", torch.float32)
+    if state_pool is not None:
+        _check(state_pool, "state_pool", torch.float32, (state_pool.shape[0], H, d_k, d_v))
     cu, sl, hi = _host_i32(cu_seqlens), _host_i32(slots), _host_i32(has_initial)
     S = len(cu) - 1
     if out is None:
         out = torch.empty((T, H, d_v), device=q.device, dtype=torch.float32)
-    _check(out, "out", torch.float32)
+    _check(out, "out", torch.float32, (T, H, d_v))
     need = int(gdn_chunk_prefill_varlen_workspace_size(_np_ptr(cu), S, H, d_k, d_v, chunk, dt))
     if workspace is None and need > 0:
         workspace = torch.empty(need, device=q.device, dtype=torch.uint8)

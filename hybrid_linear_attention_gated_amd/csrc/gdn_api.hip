@@ -484,7 +484,8 @@ gdn_status gdn_prepare_varlen(const void *xq, const void *xk, const void *xv, co
         return GDN_ERR_HIP;
     const hipError_t err = launch_prepare_varlen(xq, xk, xv, conv_weight, a_raw, b_raw, decay_rate, gate_bias,
                                                  dt, dt + S + 1, dt + 2 * S + 1, S, T_total, conv_pool, q, k,
-                                                 v, g, beta, H, d_k, d_v, x_dtype, hs);
+                                                 v, g, beta, H, d_k, d_v, x_dtype, hs, table.data(),
+                                                 table.data() + S + 1);
     return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 

@@ -96,12 +96,14 @@ hipError_t launch_prepare(const void *xq, const void *xk, const void *xv, const 
 
 // Packed sequences: cu [S+1], slot [S], init [S] are device arrays (validated on the host);
 // each sequence's convolution starts from pool[slot] (init != 0, slot >= 0) or zeros and its
-// new state is written back to pool[slot] by a second launch.
+// new state is written back to pool[slot], by the same launch for a sequence that lies in one
+// tile and by a second launch otherwise.  cu_host and slot_host: host copies of cu and slot.
 hipError_t launch_prepare_varlen(const void *xq, const void *xk, const void *xv, const float *w,
                                  const float *a_raw, const float *b_raw, const float *rate,
                                  const float *bias, const int *cu, const int *slot, const int *init, int S,
                                  int T_total, float *pool, void *q, void *k, void *v, float *g,
-                                 float *beta, int H, int dk, int dv, gdn_dtype dt, hipStream_t stream);
+                                 float *beta, int H, int dk, int dv, gdn_dtype dt, hipStream_t stream,
+                                 const int *cu_host, const int *slot_host);
 
 // Gradients of the chunked prefill (gdn_backward.hip): a forward pass keeping chunk start
 // states, then per-chunk maps, a reverse scan of the state gradient and per-chunk gradients.

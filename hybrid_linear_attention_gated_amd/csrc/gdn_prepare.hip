@@ -57,6 +57,7 @@ struct PrepArgs {
     int B, T, H, dv;
     int C, ncol;              // channels, C / kCpt
     int slabs, tiles;         // convolution workgroups = slabs * B * tiles
+    int tile_len;             // packed sequences: tokens per convolution workgroup (dense: kTile)
     int conv_blocks, gate_blocks, per_xcd;
     int state_in_kernel;      // 1: the last tile writes state_out
     // packed sequences (B = 1, T = all tokens): sequence s is tokens cu[s] .. cu[s+1]-1 and
@@ -64,6 +65,7 @@ struct PrepArgs {
     const int *cu, *slot, *init;
     int S;
     float *pool;              // [pool][C][3]
+    int spanning;             // host: some sequence with a slot spans tiles or is empty
 };
 
 // The three raw inputs before a position (oldest first) of kCpt channels, from a state row
@@ -99,6 +101,10 @@ __device__ __forceinline__ int seq_of(const PrepArgs &a, int t) {
         else hi = mid;
     }
     return lo;
+}
+// A non-empty packed sequence [cs, ce) inside one tile (prepare_kernel writes its new state)
+__host__ __device__ __forceinline__ bool single_tile(const PrepArgs &a, int cs, int ce) {
+    return ce > cs && cs / a.tile_len == (ce - 1) / a.tile_len;
 }
 __device__ __forceinline__ const float *start_row(const PrepArgs &a, int s, int ch) {
     const int sl = a.slot[s];
@@ -182,8 +188,8 @@ template <int DK, typename TIn> __device__ __forceinline__ Route<TIn> route(cons
             false};
 }
 
-// VL: packed sequences (the window restarts at every sequence start; states are written by
-// a second launch).
+// VL: packed sequences (the window restarts at every sequence start; the new state of a
+// sequence inside one tile is written here, that of any other by a second launch).
 template <int DK, typename TIn, bool VL>
 __global__ __launch_bounds__(kCols) void prepare_kernel(PrepArgs a) {
     const int w = static_cast<int>(blockIdx.x % kXcd) * a.per_xcd + static_cast<int>(blockIdx.x / kXcd);
@@ -225,8 +231,9 @@ __global__ __launch_bounds__(kCols) void prepare_kernel(PrepArgs a) {
         wt[0][j] = u.x; wt[1][j] = u.y; wt[2][j] = u.z; wt[3][j] = u.w;
     }
 
-    const int t0 = tile * kTile;
-    const int t1 = min(t0 + kTile, a.T);
+    const int len = VL ? a.tile_len : kTile;
+    const int t0 = tile * len;
+    const int t1 = min(t0 + len, a.T);
     float x3[kCpt], x2[kCpt], x1[kCpt];  // inputs at t-3, t-2, t-1
     int sq = 0, seq_end = a.T;           // packed: the current sequence and its end
     if (VL) {
@@ -303,6 +310,10 @@ __global__ __launch_bounds__(kCols) void prepare_kernel(PrepArgs a) {
                 x3[j] = x2[j]; x2[j] = x1[j]; x1[j] = xt[j];
             }
             store_out(r.y + static_cast<size_t>(tb + u) * r.rs, y);
+            // a sequence that lies wholly in this tile: its new state, the window after its last
+            // token (no other workgroup reads its start state)
+            if (VL && tb + u + 1 == seq_end && a.cu[sq] >= t0 && a.slot[sq] >= 0)
+                write_window(a.pool + (static_cast<size_t>(a.slot[sq]) * a.C + ch) * 3, x3, x2, x1);
         }
     }
 
@@ -317,16 +328,17 @@ __global__ __launch_bounds__(kCols) void prepare_kernel(PrepArgs a) {
     }
 }
 
-// Packed sequences: every sequence's new state (the last three raw inputs of [start state,
-// its tokens]) into its pool slot, after prepare_kernel has read the start states.
+// Packed sequences that span tiles, or are empty: the new state (the last three raw inputs of
+// [start state, its tokens]) into the sequence's pool slot, after prepare_kernel has read the
+// start states.
 template <int DK, typename TIn>
 __global__ __launch_bounds__(kCols) void conv_state_varlen_kernel(PrepArgs a) {
     const int s = static_cast<int>(blockIdx.x / a.slabs);
     const int col = static_cast<int>(blockIdx.x % a.slabs) * kCols + threadIdx.x;
-    if (col >= a.ncol || a.slot[s] < 0) return;
+    const int cs = a.cu[s], ce = a.cu[s + 1];
+    if (col >= a.ncol || a.slot[s] < 0 || single_tile(a, cs, ce)) return;
     const int ch = kCpt * col;
     const Route<TIn> r = route<DK, TIn>(a, ch);
-    const int cs = a.cu[s], ce = a.cu[s + 1];
     float x3[kCpt], x2[kCpt], x1[kCpt];
     const int p0 = ce - cs < 3 ? cs : ce - 3;  // first token in the final window
     if (ce - cs < 3) read_window(start_row(a, s, ch), x3, x2, x1);
@@ -363,7 +375,7 @@ template <int DK, typename TIn> hipError_t run(PrepArgs &a, hipStream_t stream) 
         if (a.conv_blocks + a.gate_blocks > 0)
             hipLaunchKernelGGL((prepare_kernel<DK, TIn, true>), dim3(grid), dim3(kCols), 0, stream, a);
         hipError_t e = hipGetLastError();
-        if (e != hipSuccess || !a.pool || a.S == 0) return e;
+        if (e != hipSuccess || !a.pool || a.S == 0 || !a.spanning) return e;
         hipLaunchKernelGGL((conv_state_varlen_kernel<DK, TIn>), dim3(a.slabs * a.S), dim3(kCols), 0, stream, a);
         return hipGetLastError();
     }
@@ -425,7 +437,8 @@ hipError_t launch_prepare_varlen(const void *xq, const void *xk, const void *xv,
                                  const float *a_raw, const float *b_raw, const float *rate,
                                  const float *bias, const int *cu, const int *slot, const int *init, int S,
                                  int T_total, float *pool, void *q, void *k, void *v, float *g,
-                                 float *beta, int H, int dk, int dv, gdn_dtype dt, hipStream_t stream) {
+                                 float *beta, int H, int dk, int dv, gdn_dtype dt, hipStream_t stream,
+                                 const int *cu_host, const int *slot_host) {
     PrepArgs a{};
     a.xq = xq; a.xk = xk; a.xv = xv; a.w = w;
     a.a_raw = a_raw; a.b_raw = b_raw; a.rate = rate; a.bias = bias;
@@ -435,7 +448,14 @@ hipError_t launch_prepare_varlen(const void *xq, const void *xk, const void *xv,
     a.C = H * (2 * dk + dv);
     a.ncol = a.C / kCpt;
     a.slabs = (a.ncol + kCols - 1) / kCols;
-    a.tiles = (T_total + kTile - 1) / kTile;  // no empty tile: states are written by the second launch
+    // Tiles as long as the mean sequence (a power of two up to kTile): a batch of one-token
+    // decode sequences gets one workgroup per token and channel slab rather than one per 32
+    // tokens.  No empty tile: an empty sequence's state is written by the second launch.
+    a.tile_len = kTile;
+    while (a.tile_len > 1 && S > 0 && static_cast<long long>(a.tile_len / 2) * S >= T_total) a.tile_len /= 2;
+    a.tiles = (T_total + a.tile_len - 1) / a.tile_len;
+    for (int s = 0; s < S && !a.spanning; ++s)
+        a.spanning = slot_host[s] >= 0 && !single_tile(a, cu_host[s], cu_host[s + 1]);
     const size_t conv = static_cast<size_t>(a.slabs) * a.tiles;
     const size_t gates = (static_cast<size_t>(T_total) * H + kCols * kGateEl - 1) / (kCols * kGateEl);
     if (conv + gates > kMaxPrepareBlocks || static_cast<size_t>(a.slabs) * S > kMaxPrepareBlocks)

@@ -257,6 +257,17 @@ def test_prepare_varlen_decode_batch():
     varlen_case([1] * 64, 4, 64, 64, 100, slots, None, wid=302)
 
 
+@pytest.mark.parametrize("hi", [3, 9], ids=["tile2or4", "tile8"])
+def test_prepare_varlen_short_sequences(hi):
+    # short prompts: tiles shrink to the mean length (a power of two below 32), so sequence starts
+    # fall inside tiles and sequences run across tile edges
+    rng = np.random.default_rng(hi)
+    lens = rng.integers(0, hi + 1, size=40).tolist()
+    slots = rng.permutation(48)[:40].astype(np.int32).tolist()
+    init = rng.integers(0, 2, size=40).tolist()
+    varlen_case(lens, 2, 64, 64, 48, slots, init, wid=306 + hi)
+
+
 def test_prepare_varlen_single_sequence_equals_dense():
     d = gi.prep_inputs(1, 150, 2, 64, 64, wid=303, device=DEV)
     dense_state = torch.empty_like(d["conv_state"])
@@ -269,3 +280,23 @@ def test_prepare_varlen_single_sequence_equals_dense():
     for i, name in enumerate(("q", "k", "v", "g", "beta")):
         assert torch.equal(packed[i], dense[i][0]), name
     assert torch.equal(pool, dense_state)
+
+
+def test_wrong_sized_buffers_are_refused_before_any_launch():
+    # the C ABI takes bare pointers; the binding checks every shape so that a buffer of another call's
+    # size is never read or written past its end
+    print("[case] wrong-sized buffers", flush=True)
+    d = gi.prep_inputs(1, 40, 2, 64, 64, wid=304, device=DEV)
+    small = gi.prep_inputs(1, 8, 2, 64, 64, wid=305, device=DEV)
+    outs = tuple(torch.empty_like(small[kk]) for kk in ("xq", "xk", "xv", "a_raw", "b_raw"))
+    with pytest.raises(ValueError, match="shape"):
+        gdn.prepare(d["xq"], d["xk"], d["xv"], d["conv_weight"], d["a_raw"], d["b_raw"], outs=outs)
+    with pytest.raises(ValueError, match="shape"):
+        gdn.prepare(d["xq"], d["xk"], small["xv"], d["conv_weight"], d["a_raw"], d["b_raw"])
+    q, k, v = (d["xq"], d["xk"], d["xv"])
+    g = torch.zeros(d["a_raw"].shape, device=DEV)
+    with pytest.raises(ValueError, match="shape"):
+        gdn.chunk_prefill(q, k, v, g, g, out=torch.empty((1, 8, 2, 64), device=DEV))
+    with pytest.raises(ValueError, match="shape"):
+        gdn.chunk_backward(q, k, v, g, g, torch.zeros((1, 40, 2, 64), device=DEV),
+                           outs=tuple(torch.empty((1, 8, 2, 64), device=DEV) for _ in range(6)))
