@@ -54,10 +54,11 @@ DECODE_BYTES_PER_SEQ_HEAD = 2 * 4 * 64 * 64 + 3 * 64 * 2 + 8 + 64 * 4
 # written (2 * 3 * 4)
 PREP_BYTES_PER_TOKEN_HEAD = 2 * 3 * 64 * 2 + 4 * 4
 # gradients (d_k = d_v = 64, chunks of 32 tokens), multiply-adds per chunk and head of the kernels'
-# products: keyside twice (P, K K^T, W: 3 C^2 d + C^3/6 = 202,411), map (X, R, F: C^2 d + 2 C d^2 =
-# 327,680), scan (d^3 = 262,144), gradients (Delta, K Y, dDelta, dP, dQ, dq, dW, T^T dW, T^T dDelta, dT,
-# dA, dK: 10 C^2 d + 5 C d^2 + 2 C^3 = 1,441,792); 2 FLOPs each, per token-head = / 32
-BWD_FLOPS_PER_TOKEN_HEAD = 2 * (2 * 202411 + 327680 + 262144 + 1441792) // 32
+# products: keyside once, in the map pass, which stores it for the gradient pass (P, K K^T, W:
+# 3 C^2 d + C^3/6 = 202,411), map (X, R, F: C^2 d + 2 C d^2 = 327,680), scan (d^3 = 262,144), gradients
+# (Delta, K Y, dDelta, dP, dQ, dq, dW, T^T dW, T^T dDelta, dT, dA, dK: 10 C^2 d + 5 C d^2 + 2 C^3 =
+# 1,441,792); 2 FLOPs each, per token-head = / 32
+BWD_FLOPS_PER_TOKEN_HEAD = 2 * (202411 + 327680 + 262144 + 1441792) // 32
 FP32_VALU_PEAK_TFLOPS = 157.3
 COPY_BYTES = 4 << 30  # far larger than the 256 MB last-level cache
 FLUSH_BYTES = 1 << 30
