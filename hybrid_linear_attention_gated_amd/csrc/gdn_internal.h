@@ -61,7 +61,8 @@ hipError_t launch_prefill_bf16(const uint16_t *q, const uint16_t *k, const uint1
 size_t prefill_bf16_workspace(int B, int T, int H, int dk, int dv, int chunk);
 
 // bf16 inputs, fused chunk kernel with sequence pieces (gdn_prefill_chunk.hip).
-// chunk_states (optional): receives the state every chunk starts from, [B*H][N][dk][dv].
+// chunk_states (optional): receives the state every chunk starts from, [B*H][N][dk][dv]; o is
+// then not written (the gradients need the states, not the outputs).
 hipError_t launch_prefill_chunk(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                 const float *g, const float *beta, const float *s0, float *o,
                                 float *s_out, int B, int T, int H, int dk, int dv, int chunk,

@@ -249,7 +249,8 @@ constexpr int kBlocksPerCU = (DK == 64 && DV == 64) ? 2 : 1;
 // DELTA selects the rule: the gated delta rule (true) or the same recurrence without the
 // erase term (false), S_t = a_t S_{t-1} + b_t v_t k_t^T, whose chunk form has A = 0 and T = I:
 // Delta = diag(b) V with no W St term, and a piece map M_p that is a multiple of I.
-// STATES (OUT only): also write the state every chunk starts from (for the gradients).
+// STATES (OUT only): write the state every chunk starts from (for the gradients) instead of the
+// outputs, which the gradients do not use.
 template <int DK, int DV, int C, bool MAP, bool DELTA, bool STATES = false>
 __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(ChunkArgs a) {
     using G = Cfg<DK, DV, C, MAP>;
@@ -823,7 +824,7 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
                 }
             }
 
-            if (!MAP && value_slice) {
+            if (!MAP && !STATES && value_slice) {
                 // O = scale (diag(exp G) Q St + P Delta) with the chunk's start state
                 bf16x8 Sh[G::KS], Sl[G::KS], Dh[G::CS], Dl[G::CS];
 #pragma unroll
