@@ -425,6 +425,7 @@ def main():
             "sequences": 64, "tokens": Tv, "ms_avg": round(varlen_ms, 4),
             "tokens_per_s": round(Tv / (varlen_ms * 1e-3), 1),
             "GBps_algorithmic": round(Tv * w.H * BYTES_PER_TOKEN_HEAD / (varlen_ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(Tv * w.H * BYTES_PER_TOKEN_HEAD / (varlen_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
             "note": "64 packed prompts of seeded lengths 1..2047, H=32 d=64 chunk 64, zero start states "
                     "written to a 64-slot pool",
         },
@@ -455,8 +456,10 @@ def main():
             "prefill_ms_avg": round(decay_pre_ms, 4),
             "prefill_tokens_per_s": round(w.B * w.T / (decay_pre_ms * 1e-3), 1),
             "prefill_GBps_algorithmic": round(pre_bytes / (decay_pre_ms * 1e-3) / 1e9, 1),
+            "prefill_hbm_frac": round(pre_bytes / (decay_pre_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
             "decode_us_per_step_avg": round(decay_dec_ms * 1e3, 2),
             "decode_GBps": round(dec_bytes / (decay_dec_ms * 1e-3) / 1e9, 1),
+            "decode_hbm_frac": round(dec_bytes / (decay_dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
             "note": "S_t = a_t S_{t-1} + b_t v_t k_t^T (no erase term) on the same 64K and decode inputs",
         },
         "roofline": {
