@@ -268,6 +268,15 @@ def test_prepare_varlen_short_sequences(hi):
     varlen_case(lens, 2, 64, 64, 48, slots, init, wid=306 + hi)
 
 
+def test_prepare_varlen_empty_sequences_and_one_token_tiles():
+    # mostly empty sequences pull the mean length below 1: one-token tiles, so the 3- and 5-token
+    # sequences run across tiles (their windows and new states come from the tokens before each tile)
+    lens = [0, 0, 3, 0, 0, 0, 1, 0, 0, 5, 0, 0]
+    slots = [0, 1, 2, 3, 4, -1, 6, 7, 8, 9, 10, 11]
+    init = [1, 0, 1, 1, 0, 1, 1, 1, 1, 0, 1, 1]
+    varlen_case(lens, 2, 64, 64, 12, slots, init, wid=320)
+
+
 def test_prepare_varlen_single_sequence_equals_dense():
     d = gi.prep_inputs(1, 150, 2, 64, 64, wid=303, device=DEV)
     dense_state = torch.empty_like(d["conv_state"])
