@@ -45,6 +45,10 @@ BF16_PEAK_TFLOPS = 2500.0
 #   forward substitution)
 BYTES_PER_TOKEN_HEAD = 648
 FLOPS_PER_TOKEN_HEAD = 64 * (6 * 64 + 4 * 64) + 6 * 64 * 64 + 64 * 64 // 3
+# the same at d_k = d_v = 128 (one 64K call of the 3B-shaped chain): 3 * 128 * 2 + 8 + 128 * 4 bytes,
+# C (6 d_k + 4 d_v) + 6 d_k d_v + C^2 / 3 FLOPs
+BYTES_PER_TOKEN_HEAD_128 = 3 * 128 * 2 + 8 + 128 * 4
+FLOPS_PER_TOKEN_HEAD_128 = 64 * (6 * 128 + 4 * 128) + 6 * 128 * 128 + 64 * 64 // 3
 # decode, per (sequence, head) per step: state read + write (2 * 4 * 64 * 64),
 # q, k, v bf16 (3 * 64 * 2), g, beta (8), o fp32 (64 * 4)
 DECODE_BYTES_PER_SEQ_HEAD = 2 * 4 * 64 * 64 + 3 * 64 * 2 + 8 + 64 * 4
@@ -307,6 +311,32 @@ def main():
     torch.cuda.synchronize()
     varlen_ms = sum(a.elapsed_time(b) for a, b in vl_ev) / len(vl_ev)
 
+    # one 64K call of the 3B-shaped chain (B=1 H=24 T=65536 d=128), state carried in and out;
+    # reported beside the main figures
+    w3 = gi.WORKLOADS["3b_2m"]
+    p3 = gi.workload_inputs("3b_2m", call=1, device=dev)
+    s3 = gi.draw_state((w3.B, w3.H, w3.dk, w3.dv), gi.seed_of(w3.wid, 1, "s0"), dev)
+    o3 = torch.empty((w3.B, w3.T, w3.H, w3.dv), device=dev, dtype=torch.float32)
+    f3 = torch.empty_like(s3)
+    ws3 = torch.empty(max(gdn.workspace_bytes(w3.B, w3.T, w3.H, w3.dk, w3.dv, w3.chunk, gdn.GDN_BF16), 1),
+                      device=dev, dtype=torch.uint8)
+
+    def prefill_3b():
+        gdn.chunk_prefill(p3["q"], p3["k"], p3["v"], p3["g"], p3["beta"], s3, chunk=w3.chunk, out=o3,
+                          final_state=f3, workspace=ws3)
+    for _ in range(args.warmup):
+        prefill_3b()
+    p3_ev = [(mk(), mk()) for _ in range(args.steps)]
+    for a, b in p3_ev:
+        a.record(stream)
+        prefill_3b()
+        b.record(stream)
+    torch.cuda.synchronize()
+    p3_ms = sum(a.elapsed_time(b) for a, b in p3_ev) / len(p3_ev)
+    p3_th = w3.B * w3.T * w3.H
+    p3_bytes = p3_th * BYTES_PER_TOKEN_HEAD_128 + 2 * w3.B * w3.H * w3.dk * w3.dv * 4
+    del p3, o3, ws3
+
     # preparation: alone (64K shape and decode batch), and followed by the 64K prefill
     for _ in range(args.warmup):
         prepare()
@@ -451,6 +481,14 @@ def main():
             "note": "forward recompute (keeps chunk start states) + per-chunk maps + reverse scan + per-chunk "
                     "gradients, fp32 on the matrix cores; FLOPs are the gradient kernels' multiply-adds x 2, "
                     "alu_frac against the fp32 peak",
+        },
+        "prefill_3b_64k": {
+            "workload": "one 64K call of the 3B-shaped chain: B=1 H=24 T=65536 d_k=d_v=128 chunk 64, bf16 q/k/v, "
+                        "state carried in and out",
+            "ms_avg": round(p3_ms, 4), "tokens_per_s": round(w3.B * w3.T / (p3_ms * 1e-3), 1),
+            "GBps_algorithmic": round(p3_bytes / (p3_ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(p3_bytes / (p3_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "useful_TFLOPs": round(p3_th * FLOPS_PER_TOKEN_HEAD_128 / (p3_ms * 1e-3) / 1e12, 2),
         },
         "gated_decay_rule": {
             "prefill_ms_avg": round(decay_pre_ms, 4),
