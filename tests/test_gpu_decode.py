@@ -59,6 +59,38 @@ def test_decode_is_deterministic_and_in_place():
     assert not torch.equal(s1, s0)
 
 
+def test_decode_graph_replays_match_eager():
+    """Steps captured in a HIP graph (as a serving loop issues them) give, on every replay, the
+    same outputs and state as the eager calls; the state is reset and read back between replays
+    by ordinary eager work."""
+    N, H, d, steps = 32, 8, 64, 4
+    print(f"[case] decode graph N={N} H={H} d={d} steps={steps}", flush=True)
+    s0 = gi.decode_state(N, H, d, d, device=DEV)
+    inp = [gi.decode_inputs(N, H, d, d, t, device=DEV) for t in range(steps)]
+    state = s0.clone()
+    outs = [torch.empty((N, H, d), device=DEV, dtype=torch.float32) for _ in range(steps)]
+    for x, o in zip(inp, outs):
+        gdn.decode_step(x["q"], x["k"], x["v"], x["g"], x["beta"], state, out=o)
+    torch.cuda.synchronize()
+    ref_o, ref_s = [o.clone() for o in outs], state.clone()
+
+    graph = torch.cuda.CUDAGraph()
+    state.copy_(s0)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        for x, o in zip(inp, outs):
+            gdn.decode_step(x["q"], x["k"], x["v"], x["g"], x["beta"], state, out=o)
+    for rep in range(3):
+        state.copy_(s0)
+        for o in outs:
+            o.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(state, ref_s), f"replay {rep}: state"
+        for t, (o, r) in enumerate(zip(outs, ref_o)):
+            assert torch.equal(o, r), f"replay {rep}: step {t} outputs"
+
+
 def test_decode_guard_regions_untouched():
     """Canary words around the state and output stay intact."""
     N, H, d = 33, 5, 64
