@@ -1080,13 +1080,16 @@ __global__ __launch_bounds__(kWave) void chain_varlen_kernel(SeqTable sq, const 
         gq, li, col);
 }
 
-// Piece plan: enough workgroups to fill the chip twice over, at least eight
-// chunks per piece, and no empty pieces.
+// Piece plan: at most 512 workgroups (two per compute unit), at least eight
+// chunks per piece, and no empty pieces.  Rounding the piece count down keeps
+// the grid within 512: one workgroup over it would run alone in a further round
+// (64-wide heads run two workgroups per compute unit, so 512 is one round;
+// 128-wide heads run one, so 512 is two full rounds).
 struct PiecePlan {
     int P, piece_chunks;
 };
 PiecePlan piece_plan(int BH, int N) {
-    int P = (512 + BH - 1) / BH;
+    int P = 512 / BH;
     P = max(1, min(P, N / 8));
     const int pc = (N + P - 1) / P;
     return {(N + pc - 1) / pc, pc};
