@@ -50,8 +50,13 @@ namespace gdn {
 namespace {
 
 constexpr int kWave = 64;
-constexpr int kWaves = 4;
-constexpr int kBlock = kWave * kWaves;
+// Wavefronts per workgroup.  The chunk's keyside (K K^T, T, W, P) is dealt over four
+// wavefronts; the state's 16-column slices over all of them.  128 x 128 heads use eight,
+// so each wavefront carries half the slices it would with four (two wavefronts per SIMD
+// instead of one register-bound wavefront).
+template <int DK, int DV>
+constexpr int kWavesOf = (DK == 128 && DV == 128) ? 8 : 4;
+constexpr int kKeyWaves = 4;  // wavefronts that build the keyside
 // bf16 row padding in LDS: row strides of 2 * odd dwords, so the 8-byte fragment
 // reads of 16 consecutive rows (one per lane) cover all 32 banks once
 constexpr int kPad = 4;
@@ -131,10 +136,10 @@ template <int DK, int DV, int C, bool MAP>
 struct Cfg {
     static constexpr int CT = C / 16, CS = C / 32, KT = DK / 16, KS = DK / 32, VT = DV / 16;
     static constexpr int NB = C / 16;
+    static constexpr int WAVES = kWavesOf<DK, DV>, BLOCK = WAVES * kWave;
     static constexpr int NS = VT + (MAP ? KT : 0);  // 16-column slices of the carried state
-    static constexpr int SPW = NS / kWaves;          // slices per wavefront
-    static constexpr int VPW = (VT + kWaves - 1) / kWaves;
-    static_assert(NS % kWaves == 0, "slices must divide among the wavefronts");
+    static constexpr int SPW = NS / WAVES;           // slices per wavefront
+    static_assert(NS % WAVES == 0, "slices must divide among the wavefronts");
     static_assert(C == 32 || C == 64, "chunk");
     static constexpr int MAPW = DV + DK;  // row length of a stored piece map
 };
@@ -176,8 +181,10 @@ template <int DK, int DV, int C, bool MAP>
 struct ChunkRegs {
     // V is loaded (and transposed into LDS in F) by the first VTHREADS threads only: with
     // 64-wide values that is wavefronts 0 and 1, whose share of F is otherwise the smaller
-    static constexpr int VTHREADS = DV == 64 ? kBlock / 2 : kBlock;
-    static constexpr int NK = C * DK / 8 / kBlock, NV = C * DV / 8 / VTHREADS;
+    static constexpr int BLOCK = kWave * kWavesOf<DK, DV>;
+    static constexpr int VTHREADS = DV == 64 ? BLOCK / 2 : BLOCK;
+    static constexpr int NK = C * DK / 8 / BLOCK, NV = C * DV / 8 / VTHREADS;
+    static_assert(C * DK % (8 * BLOCK) == 0 && C * DV % (8 * VTHREADS) == 0, "rows divide among threads");
     u16x8 k[NK], q[MAP ? 1 : NK], v[NV];
     float g, beta;
 };
@@ -216,7 +223,7 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<DK, DV, C, MAP> &r, const C
     const auto rv = chunk_rsrc(a.v + row0 * DV, rows_v);
 #pragma unroll
     for (int i = 0; i < R::NK; ++i) {
-        const int e = tid + i * kBlock;
+        const int e = tid + i * R::BLOCK;
         const int rr = e % C, c8 = e / C;
         r.k[i] = buf_load16(rk, static_cast<unsigned>(rr * a.H * DK + 8 * c8) * 2u);
         if (!MAP) {
@@ -252,7 +259,7 @@ constexpr int kBlocksPerCU = (DK == 64 && DV == 64) ? 2 : 1;
 // STATES (OUT only): write the state every chunk starts from (for the gradients) instead of the
 // outputs, which the gradients do not use.
 template <int DK, int DV, int C, bool MAP, bool DELTA, bool STATES = false>
-__global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(ChunkArgs a) {
+__global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV>)) void chunk_kernel(ChunkArgs a) {
     using G = Cfg<DK, DV, C, MAP>;
     using R = ChunkRegs<DK, DV, C, MAP>;
     constexpr int KSTR = DK + kPad;   // K and Q rows
@@ -264,7 +271,7 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
     static_assert(2 * G::CT * G::CS * kWave * 16 <= C * CSTR * 4, "P fragments fit in A's buffer");
     // With one 16-row tile of T per wavefront (chunk 64), F builds the hi/lo fragments of
     // T diag(b) once and parks them over that wavefront's own (then dead) T rows.
-    constexpr bool kTbFrags = G::CT == kWaves;
+    constexpr bool kTbFrags = G::CT == kKeyWaves;
     static_assert(!kTbFrags || 2 * G::CS * kWave * 16 <= 16 * CSTR * 4, "T diag(b) fragments fit in 16 T rows");
     __shared__ __align__(16) uint16_t kv_s[KV_ELEMS];              // K rows, then V^T
     __shared__ __align__(16) uint16_t q_s[MAP ? 8 : C * KSTR];     // Q rows
@@ -330,7 +337,7 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
     f32x4 St[G::SPW][G::KT];
 #pragma unroll
     for (int j = 0; j < G::SPW; ++j) {
-        const int sl = wave + kWaves * j;
+        const int sl = wave + G::WAVES * j;
 #pragma unroll
         for (int mt = 0; mt < G::KT; ++mt)
 #pragma unroll
@@ -346,7 +353,7 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
             }
     }
     // T's blocks above the diagonal stay zero for the whole kernel
-    for (int e = tid; e < TS_FLOATS; e += kBlock) t_s[e] = 0.f;
+    for (int e = tid; e < TS_FLOATS; e += G::BLOCK) t_s[e] = 0.f;
 
     uint16_t(*ks)[KSTR] = reinterpret_cast<uint16_t(*)[KSTR]>(kv_s);
     uint16_t(*vt)[VSTR] = reinterpret_cast<uint16_t(*)[VSTR]>(DELTA ? static_cast<void *>(kv_s)
@@ -390,13 +397,13 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
                 for (int mt = 0; mt < G::KT; ++mt)
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        cs[(16 * mt + 4 * gq + r) * DV + 16 * (wave + kWaves * j) + li] = St[j][mt][r];
+                        cs[(16 * mt + 4 * gq + r) * DV + 16 * (wave + G::WAVES * j) + li] = St[j][mt][r];
         }
 
         // ---- A: this chunk's rows into LDS (K both row-major and transposed); gates
 #pragma unroll
         for (int i = 0; i < R::NK; ++i) {
-            const int e = tid + i * kBlock;
+            const int e = tid + i * G::BLOCK;
             const int rr = e % C, c8 = e / C;
             lds_store8(&ks[rr][8 * c8], cur.k[i]);
 #pragma unroll
@@ -545,7 +552,7 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
                 } else if (wave == 2) {
                     a_tile(IC<2>{}, IC<2>{});
                     if constexpr (MAP) a_tile(IC<3>{}, I1{});
-                } else {
+                } else if (wave == 3) {
                     a_tile(IC<3>{}, IC<3>{});
                     a_tile(IC<3>{}, IC<2>{});
                 }
@@ -586,7 +593,7 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
                     p_store(IC<2>{}, IC<1>{}, p_pair(IC<2>{}, IC<1>{}));
                 } else if (wave == 2) {
                     p_store(IC<3>{}, IC<0>{}, p_pair(IC<3>{}, IC<0>{}));
-                } else {
+                } else if (wave == 3) {
                     p_store(IC<3>{}, IC<1>{}, p_pair(IC<3>{}, IC<1>{}));
                 }
             } else {
@@ -621,7 +628,7 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
                     f32x4 y = mm16(rowfrag(ts, 48, 48), x31, zero4);
                     y = mm16(rowfrag(ts, 48, 32), x21, y);  // T32 row fragments: this wavefront's store
                     store_acc(ts, 48, 16, -y);
-                } else {
+                } else if (wave == 3) {
                     const f32x4 t10 = -mm16(rowfrag(ts, 16, 16), mm16(rowfrag(as, 16, 0), accfrag(ts, 0, 0), zero4), zero4);
                     const f32x4 t32 =
                         -mm16(rowfrag(ts, 48, 48), mm16(rowfrag(as, 48, 32), accfrag(ts, 32, 32), zero4), zero4);
@@ -669,7 +676,7 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
                     } else if (wave == 2) {
                         p_store(IC<0>{}, IC<0>{}, pa);
                         p_store(IC<3>{}, IC<1>{}, pb);
-                    } else {
+                    } else if (wave == 3) {
                         p_store(IC<2>{}, IC<1>{}, pa);
                     }
                 } else {
@@ -685,7 +692,7 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
                     for (int q8 = 0; q8 < 8; ++q8) vt[8 * c8 + q8][rr] = cur.v[i][q8];
                 }
             }
-            if constexpr (kTbFrags) {
+            if (kTbFrags && wave < G::CT) {
                 // wavefront ct owns T's row tile ct: one pass over it gives T diag(b exp G) for
                 // every W tile of that row and the T diag(b) fragments of U
                 const int ct = wave;
@@ -729,10 +736,10 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
                     *tb_frag(ct, s, 0) = tbh[s];
                     *tb_frag(ct, s, 1) = tbl[s];
                 }
-            } else {
+            } else if (!kTbFrags) {
     #pragma unroll
                 for (int p = 0; p < G::CT * G::KS; ++p) {
-                    if (p % kWaves != wave) continue;
+                    if (p % G::WAVES != wave) continue;
                     const int ct = p % G::CT, s2 = p / G::CT;
                     f32x4 acc0 = zero4, acc1 = zero4;
     #pragma unroll
@@ -760,7 +767,7 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
         // ---- G: per slice: U = (T diag b) V, Delta = U - W St, outputs, state update
 #pragma unroll
         for (int j = 0; j < G::SPW; ++j) {
-            const int sl = wave + kWaves * j;
+            const int sl = wave + G::WAVES * j;
             const bool value_slice = sl < G::VT;
             if constexpr (!DELTA) {
                 if (!value_slice) {
@@ -899,7 +906,7 @@ __global__ __launch_bounds__(kBlock, (kBlocksPerCU<DK, DV>)) void chunk_kernel(C
     // ---- results
 #pragma unroll
     for (int j = 0; j < G::SPW; ++j) {
-        const int sl = wave + kWaves * j;
+        const int sl = wave + G::WAVES * j;
 #pragma unroll
         for (int mt = 0; mt < G::KT; ++mt)
 #pragma unroll
@@ -1126,12 +1133,12 @@ hipError_t run_chunk(const uint16_t *q, const uint16_t *k, const uint16_t *v, co
     auto launch_out = [&](int items) {
         if constexpr (DK == 64 && DV == 64 && C == 32) {
             if (chunk_states) {
-                hipLaunchKernelGGL((chunk_kernel<DK, DV, C, false, DELTA, true>), grid(items), dim3(kBlock), 0, stream, a);
+                hipLaunchKernelGGL((chunk_kernel<DK, DV, C, false, DELTA, true>), grid(items), dim3(kWave * kWavesOf<DK, DV>), 0, stream, a);
                 return hipGetLastError();
             }
         }
         if (chunk_states) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((chunk_kernel<DK, DV, C, false, DELTA>), grid(items), dim3(kBlock), 0, stream, a);
+        hipLaunchKernelGGL((chunk_kernel<DK, DV, C, false, DELTA>), grid(items), dim3(kWave * kWavesOf<DK, DV>), 0, stream, a);
         return hipGetLastError();
     };
     if (P == 1) {
@@ -1145,7 +1152,7 @@ hipError_t run_chunk(const uint16_t *q, const uint16_t *k, const uint16_t *v, co
                                               ((maps_bytes + 255) & ~static_cast<size_t>(255)));
     a.maps = maps;
     a.items = BH * (P - 1);
-    hipLaunchKernelGGL((chunk_kernel<DK, DV, C, true, DELTA>), grid(BH * (P - 1)), dim3(kBlock), 0, stream, a);
+    hipLaunchKernelGGL((chunk_kernel<DK, DV, C, true, DELTA>), grid(BH * (P - 1)), dim3(kWave * kWavesOf<DK, DV>), 0, stream, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL((chain_kernel<DK, DV>), dim3(BH * (DV / 16)), dim3(kWave), 0, stream,
@@ -1183,7 +1190,7 @@ hipError_t run_chunk_varlen(const uint16_t *q, const uint16_t *k, const uint16_t
     if (L.NM > 0) {
         a.maps = maps;
         a.items = L.NM * H;
-        hipLaunchKernelGGL((chunk_kernel<DK, DV, C, true, DELTA>), grid(a.items), dim3(kBlock), 0, stream, a);
+        hipLaunchKernelGGL((chunk_kernel<DK, DV, C, true, DELTA>), grid(a.items), dim3(kWave * kWavesOf<DK, DV>), 0, stream, a);
         const hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
@@ -1193,7 +1200,7 @@ hipError_t run_chunk_varlen(const uint16_t *q, const uint16_t *k, const uint16_t
     if (err != hipSuccess || L.NP == 0) return err;
     a.s_start = starts;
     a.items = L.NP * H;
-    hipLaunchKernelGGL((chunk_kernel<DK, DV, C, false, DELTA>), grid(a.items), dim3(kBlock), 0, stream, a);
+    hipLaunchKernelGGL((chunk_kernel<DK, DV, C, false, DELTA>), grid(a.items), dim3(kWave * kWavesOf<DK, DV>), 0, stream, a);
     return hipGetLastError();
 }
 
