@@ -899,6 +899,11 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV>))
                 }
                 St[j][mt] = acc;
             }
+            // 128 x 128 maps: two slices per wavefront, one after the other.  Interleaved, their
+            // products need twice the temporaries and spill (85 registers; MAP 0.90 -> 0.68 ms on
+            // a 24-head 64K call with this barrier).  The 64 x 64 maps interleave them in
+            // registers they have, and are faster that way (0.36 vs 0.38 ms).
+            if constexpr (G::SPW > 1 && G::WAVES == 8) __builtin_amdgcn_sched_barrier(0);
         }
         __syncthreads();
     }
