@@ -282,6 +282,10 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV>))
     __shared__ __align__(16) bf16x8 wf_s[DELTA ? G::CT * G::KS * kWave : 1];   // W A-fragments
     __shared__ __align__(16) uint16_t kt_s[DK * KTSTR];            // K^T
     __shared__ __align__(16) float x_s[DELTA ? 16 * CSTR16 : 4];   // one 16x16 fp32 tile (C)
+    // Eight wavefronts: two per T row tile build W in F (each half of its tiles), so the
+    // T diag(b) fragments get a buffer of their own instead of the T rows both still read.
+    constexpr bool kSplitF = kTbFrags && DELTA && G::WAVES == 2 * G::CT;
+    __shared__ __align__(16) bf16x8 tbf_s[kSplitF ? G::CT * G::CS * 2 * kWave : 1];
     __shared__ float g_s[C], b_s[C], bg_s[C], dec_s[C], gam_s[C];  // g_s: G * log2(e)
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform
@@ -661,6 +665,7 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV>))
         }
 
         auto tb_frag = [&](int ct, int s, int hl) -> bf16x8 * {
+            if constexpr (kSplitF) return &tbf_s[((ct * G::CS + s) * 2 + hl) * kWave + lane];
             return reinterpret_cast<bf16x8 *>(&ts[16 * ct][0]) + (s * 2 + hl) * kWave + lane;
         };
         if constexpr (DELTA) {
@@ -692,13 +697,16 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV>))
                     for (int q8 = 0; q8 < 8; ++q8) vt[8 * c8 + q8][rr] = cur.v[i][q8];
                 }
             }
-            if (kTbFrags && wave < G::CT) {
+            if (kTbFrags && (kSplitF || wave < G::CT)) {
                 // wavefront ct owns T's row tile ct: one pass over it gives T diag(b exp G) for
-                // every W tile of that row and the T diag(b) fragments of U
-                const int ct = wave;
-                f32x4 accw[G::KT];
+                // every W tile of that row and the T diag(b) fragments of U.  With eight
+                // wavefronts, wavefronts ct and ct + 4 each build half of the row's W tiles.
+                constexpr int MTN = kSplitF ? G::KT / 2 : G::KT;  // W tiles of this wavefront
+                const int ct = kSplitF ? wave % G::CT : wave;
+                const int half = kSplitF ? wave / G::CT : 0;
+                f32x4 accw[MTN];
     #pragma unroll
-                for (int mt = 0; mt < G::KT; ++mt) accw[mt] = zero4;
+                for (int mt = 0; mt < MTN; ++mt) accw[mt] = zero4;
                 bf16x8 tbh[G::CS], tbl[G::CS];
     #pragma unroll
                 for (int s = 0; s < G::CS; ++s) {
@@ -719,22 +727,25 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV>))
                     const bf16x8 bfr = pack_bf16(xg);
                     split_bf16(xb, tbh[s], tbl[s]);
     #pragma unroll
-                    for (int mt = 0; mt < G::KT; ++mt) accw[mt] = mfma_bf16(kfrag(mt, s), bfr, accw[mt]);
+                    for (int mt = 0; mt < MTN; ++mt)
+                        accw[mt] = mfma_bf16(kfrag(half * MTN + mt, s), bfr, accw[mt]);
                 }
     #pragma unroll
-                for (int s2 = 0; s2 < G::KS; ++s2) {
+                for (int s2 = 0; s2 < MTN / 2; ++s2) {
                     float x[8];
                     acc_pair_to_slots(accw[2 * s2], accw[2 * s2 + 1], x);
-                    wf_s[(ct * G::KS + s2) * kWave + lane] = pack_bf16(x);
+                    wf_s[(ct * G::KS + half * (MTN / 2) + s2) * kWave + lane] = pack_bf16(x);
                 }
                 // this wavefront's T rows have all been read (LDS keeps a wavefront's accesses in
                 // order); keep the compiler from moving the stores above the loads
                 __asm__ __volatile__("" ::: "memory");
+                if (half == 0) {
     #pragma unroll
-                for (int s = 0; s < G::CS; ++s) {
-                    if (32 * s > 16 * ct + 15) continue;
-                    *tb_frag(ct, s, 0) = tbh[s];
-                    *tb_frag(ct, s, 1) = tbl[s];
+                    for (int s = 0; s < G::CS; ++s) {
+                        if (32 * s > 16 * ct + 15) continue;
+                        *tb_frag(ct, s, 0) = tbh[s];
+                        *tb_frag(ct, s, 1) = tbl[s];
+                    }
                 }
             } else if (!kTbFrags) {
     #pragma unroll

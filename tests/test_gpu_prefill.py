@@ -66,7 +66,9 @@ def test_bf16_mfma_path(orc, gate, dk, dv, chunk):
 @pytest.mark.parametrize("gate", ["primary", "literal"])
 @pytest.mark.parametrize("dk,dv,chunk,T,s0", [
     (64, 64, 64, 2560, True), (64, 64, 64, 2547, False), (128, 128, 64, 2560, True),
-    (64, 128, 32, 2600, True), (128, 64, 64, 4096, True)])
+    (64, 128, 32, 2600, True), (128, 64, 64, 4096, True),
+    # two and three pieces: the shortest chains (one and two map steps)
+    (64, 64, 64, 1100, True), (128, 128, 64, 1600, True), (64, 64, 64, 1536, False)])
 def test_bf16_sequence_pieces(orc, gate, dk, dv, chunk, T, s0):
     """Long sequences on few heads are split into pieces (piece maps, then a chained
     start state per piece): every element, ragged tails included."""
