@@ -285,6 +285,10 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV>))
     // Eight wavefronts: two per T row tile build W in F (each half of its tiles), so the
     // T diag(b) fragments get a buffer of their own instead of the T rows both still read.
     constexpr bool kSplitF = kTbFrags && DELTA && G::WAVES == 2 * G::CT;
+    // Eight wavefronts, chunk 64: B's tiles below the diagonal and every P tile go to
+    // wavefronts 4-7, so 0-3 compute only their diagonal tile and its inverse in B, and the
+    // blocks of T in C.
+    constexpr bool kSplitKey = kSplitF;
     __shared__ __align__(16) bf16x8 tbf_s[kSplitF ? G::CT * G::CS * 2 * kWave : 1];
     __shared__ float g_s[C], b_s[C], bg_s[C], dec_s[C], gam_s[C];  // g_s: G * log2(e)
 
@@ -542,7 +546,29 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV>))
         if constexpr (DELTA) {
             using I0 = IC<0>;
             using I1 = IC<1>;
-            if constexpr (G::CT == 4) {
+            if constexpr (kSplitKey) {
+                // eight wavefronts: 0-3 their diagonal tile, then its inverse; 4-6 the tiles below
+                // the diagonal; 7 the two single-product P tiles
+                if (wave == 0) a_tile(I0{}, I0{});
+                else if (wave == 1) a_tile(I1{}, I1{});
+                else if (wave == 2) a_tile(IC<2>{}, IC<2>{});
+                else if (wave == 3) a_tile(IC<3>{}, IC<3>{});
+                else if (wave == 4) {
+                    a_tile(I1{}, I0{});
+                    a_tile(IC<2>{}, I0{});
+                } else if (wave == 5) {
+                    a_tile(IC<2>{}, I1{});
+                    a_tile(IC<3>{}, I0{});
+                } else if (wave == 6) {
+                    a_tile(IC<3>{}, I1{});
+                    a_tile(IC<3>{}, IC<2>{});
+                } else if (wave == 7) {
+                    if constexpr (!MAP) {
+                        pa = p_pair(I0{}, I0{});
+                        pb = p_pair(IC<2>{}, I1{});
+                    }
+                }
+            } else if constexpr (G::CT == 4) {
                 // (3,1) goes to wavefront 0 where wavefront 2 also forms a P tile
                 if (wave == 0) {
                     a_tile(I0{}, I0{});
@@ -568,7 +594,7 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV>))
                     a_tile(I1{}, I1{});
                 }
             }
-            if constexpr (!MAP) {
+            if constexpr (!MAP && !kSplitKey) {
                 if constexpr (G::CT == 4) {
                     if (wave == 2) pa = p_pair(IC<0>{}, IC<0>{});
                     else if (wave == 3) pa = p_pair(IC<2>{}, IC<1>{});
@@ -651,7 +677,16 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV>))
                     store_acc(ts, 16, 0, t10);
                 }
             }
-            if constexpr (!MAP && G::CT == 4) {
+            if constexpr (!MAP && kSplitKey) {
+                if (wave == 4) {
+                    pa = p_pair(IC<3>{}, IC<0>{});
+                } else if (wave == 5) {
+                    pa = p_pair(IC<1>{}, IC<0>{});
+                    pb = p_pair(IC<2>{}, IC<0>{});
+                } else if (wave == 6) {
+                    pa = p_pair(IC<3>{}, IC<1>{});
+                }
+            } else if constexpr (!MAP && G::CT == 4) {
                 if (wave == 0) {
                     pb = p_pair(IC<3>{}, IC<0>{});
                 } else if (wave == 1) {
@@ -671,7 +706,19 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV>))
         if constexpr (DELTA) {
             // ---- F: P fragments and V^T into LDS (A and K are dead); W A-fragments = W^T tiles
             // (2 s2, ct) and (2 s2 + 1, ct), W = T diag(b exp G) K
-            if constexpr (!MAP) {
+            if constexpr (!MAP && kSplitKey) {
+                if (wave == 4) {
+                    p_store(IC<3>{}, IC<0>{}, pa);
+                } else if (wave == 5) {
+                    p_store(IC<1>{}, IC<0>{}, pa);
+                    p_store(IC<2>{}, IC<0>{}, pb);
+                } else if (wave == 6) {
+                    p_store(IC<3>{}, IC<1>{}, pa);
+                } else if (wave == 7) {
+                    p_store(IC<0>{}, IC<0>{}, pa);
+                    p_store(IC<2>{}, IC<1>{}, pb);
+                }
+            } else if constexpr (!MAP) {
                 if constexpr (G::CT == 4) {
                     if (wave == 0) {
                         p_store(IC<3>{}, IC<0>{}, pb);
