@@ -18,13 +18,14 @@
 // same chunk recurrence run on the identity with no values.  Three launches:
 //   MAP   (one workgroup per head and piece but the last) runs the recurrence
 //         on [values | identity] columns and stores [N_p | M_p];
-//   chain (one wavefront per head and 16 value columns) composes the maps
+//   chain (one workgroup per head and 16 value columns) composes the maps
 //         serially over pieces and stores every piece's true start state;
 //   OUT   (one workgroup per head and piece) reruns each piece from its
 //         start state and writes the outputs (and the final state).
 // With a single piece only OUT runs, from the caller's start state.
 //
-// Inside a workgroup (4 wavefronts) all per-chunk operands live in LDS:
+// Inside a workgroup (4 wavefronts; 8 for 128 x 128 heads, the keyside still on
+// four of them) all per-chunk operands live in LDS:
 // K K^T and A, T by blocked substitution (16x16 diagonal blocks one column
 // per lane, then 16x16 block products on MFMA with hi/lo bf16 splits), the
 // W and K^T fragments of the scan, and P = Q K^T .* decay.  Each wavefront
