@@ -100,9 +100,12 @@ def test_chunk_sizes_agree(orc):
 
 
 @pytest.mark.parametrize("T", [1, 2, 63, 65])
-def test_short_and_ragged_lengths(orc, T):
-    d = inputs(2, T, 2, 64, 64, torch.bfloat16)
-    check(orc, d, 64, TOL["bf16"], f"T={T}")
+@pytest.mark.parametrize("d_head", [64, 128])
+def test_short_and_ragged_lengths(orc, T, d_head):
+    """Sequences shorter than a chunk or one token past it (128-wide heads run eight-wavefront
+    workgroups)."""
+    d = inputs(2, T, 2, d_head, d_head, torch.bfloat16)
+    check(orc, d, 64, TOL["bf16"], f"T={T} d={d_head}")
 
 
 def test_zero_length_copies_the_state():
