@@ -104,8 +104,9 @@ def main():
                          "used to calibrate the HBM byte counters; the JSON line needs 'all'")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build measures one GPU only; the GDN path shards over heads and "
-              "sequences with no exchange, so multi-GPU runs are not part of it.", file=sys.stderr)
+        print("bench.py measures one GPU only (--gpus 1): heads and the sequences of a batch shard "
+              "over GPUs with no exchange inside the mixer, so a multi-GPU run would repeat the "
+              "one-GPU kernels on smaller shares.", file=sys.stderr)
         sys.exit(2)
 
     import torch
