@@ -121,12 +121,15 @@ def test_decode_error_leaves_buffers_untouched():
 
 
 @pytest.mark.parametrize("rule", [gdn.GDN_RULE_GATED_DELTA, gdn.GDN_RULE_GATED_DECAY])
-def test_decode_with_state_slots(orc, rule):
+@pytest.mark.parametrize("d_head", [64, 128])
+def test_decode_with_state_slots(orc, rule, d_head):
     """States in a pool of 10 slots; six sequences use slots 3, 7, 0, 9 and two padding entries
     (-1 and 12, out of range): valid slots follow the oracle, padding outputs are zero, every
-    other slot is left bit for bit as it was."""
+    other slot is left bit for bit as it was (64-wide states take two wavefronts each, 128-wide
+    eight, every one of which handles the padding entries on its own)."""
     import oracle
-    N, H, dk, dv, P = 6, 4, 64, 64, 10
+    print(f"[case] decode slots d={d_head} rule={rule}", flush=True)
+    N, H, dk, dv, P = 6, 4, d_head, d_head, 10
     slots = torch.tensor([3, 7, -1, 0, 12, 9], dtype=torch.int32, device=DEV)
     pool = gi.decode_state(P, H, dk, dv, device=DEV)
     pool0 = pool.clone()
