@@ -58,9 +58,12 @@ constexpr int kWave = 64;
 template <int DK, int DV>
 constexpr int kWavesOf = (DK == 128 && DV == 128) ? 8 : 4;
 constexpr int kKeyWaves = 4;  // wavefronts that build the keyside
-// bf16 row padding in LDS: row strides of 2 * odd dwords, so the 8-byte fragment
-// reads of 16 consecutive rows (one per lane) cover all 32 banks once
+// bf16 row padding in LDS.  Natural column order: row strides of 2 * odd dwords, so the
+// 8-byte fragment reads of 16 consecutive rows (one per lane) cover all 32 banks once.
+// Permuted order (below): strides of 4 * odd dwords, so the 16-byte fragment reads of 8
+// consecutive rows cover the 32 banks once.
 constexpr int kPad = 4;
+constexpr int kPadPerm = 8;
 constexpr int kXcds = 8;  // accelerator dies (each with its own L2) of an MI355X
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -172,6 +175,21 @@ struct ChunkArgs {
 };
 
 // Eight bf16 to an 8-byte aligned LDS address (padded rows are not 16-byte aligned).
+// Four-wavefront workgroups store the rows of K, Q, K^T and V^T with their columns permuted
+// inside each 32-column block, so that the eight k-slots a lane feeds an MFMA lie next to
+// each other: logical column 16 h + 4 g + e (h < 2, g < 4, e < 4) sits at 8 g + 4 h + e, and
+// a fragment is one 16-byte read instead of two 8-byte ones (64K prefill 0.79 -> 0.78 ms;
+// the eight-wavefront 128 x 128 kernel spills with it and keeps the natural order).
+__device__ __forceinline__ int perm_col(int c) { return (c & ~31) + 8 * ((c >> 2) & 3) + 4 * ((c >> 4) & 1) + (c & 3); }
+__device__ __forceinline__ bf16x8 lds_frag_perm(const uint16_t *rowp, int s, int gq) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8 *>(rowp + 32 * s + 8 * gq));
+}
+// logical columns [8 c8, 8 c8 + 8) of a permuted row: two runs of four
+__device__ __forceinline__ void lds_store8_perm(uint16_t *row, int c8, u16x8 x) {
+    const int m = c8 & 3, off = 32 * (c8 >> 2) + 16 * (m & 1) + 4 * (m >> 1);
+    reinterpret_cast<u16x4 *>(row + off)[0] = u16x4{x[0], x[1], x[2], x[3]};
+    reinterpret_cast<u16x4 *>(row + off + 8)[0] = u16x4{x[4], x[5], x[6], x[7]};
+}
 __device__ __forceinline__ void lds_store8(uint16_t *p, u16x8 x) {
     reinterpret_cast<u16x4 *>(p)[0] = u16x4{x[0], x[1], x[2], x[3]};
     reinterpret_cast<u16x4 *>(p)[1] = u16x4{x[4], x[5], x[6], x[7]};
@@ -263,11 +281,13 @@ template <int DK, int DV, int C, bool MAP, bool DELTA, bool STATES = false>
 __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV>)) void chunk_kernel(ChunkArgs a) {
     using G = Cfg<DK, DV, C, MAP>;
     using R = ChunkRegs<DK, DV, C, MAP>;
-    constexpr int KSTR = DK + kPad;   // K and Q rows
-    constexpr int VSTR = C + kPad;    // V^T rows
+    constexpr bool kPerm = G::WAVES == 4;  // permuted bf16 rows (see perm_col)
+    constexpr int kRowPad = kPerm ? kPadPerm : kPad;
+    constexpr int KSTR = DK + kRowPad;   // K and Q rows
+    constexpr int VSTR = C + kRowPad;    // V^T rows
     constexpr int CSTR = C + 4;       // A and T rows (fp32)
     constexpr int KV_ELEMS = C * KSTR > DV * VSTR ? C * KSTR : DV * VSTR;
-    constexpr int KTSTR = C + kPad;   // K^T rows
+    constexpr int KTSTR = C + kRowPad;   // K^T rows
     constexpr int CSTR16 = 20;        // rows of the 16x16 scratch tile (conflict-free f32x4 reads)
     static_assert(2 * G::CT * G::CS * kWave * 16 <= C * CSTR * 4, "P fragments fit in A's buffer");
     // With one 16-row tile of T per wavefront (chunk 64), F builds the hi/lo fragments of
@@ -370,7 +390,17 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV>))
     uint16_t(*qs)[KSTR] = reinterpret_cast<uint16_t(*)[KSTR]>(q_s);
     uint16_t(*kt)[KTSTR] = reinterpret_cast<uint16_t(*)[KTSTR]>(kt_s);
     // K^T A-fragment (d tile mt, chunk-row step s): K^T[16 mt + li][kmap(s, gq, e)]
-    auto kfrag = [&](int mt, int s) { return lds_frag_bf16(&kt[16 * mt + li][0], s, gq); };
+    // fragment reads, row stores and column positions in the chosen column order
+    auto frag = [&](const uint16_t *rowp, int s) {
+        if constexpr (kPerm) return lds_frag_perm(rowp, s, gq);
+        else return lds_frag_bf16(rowp, s, gq);
+    };
+    auto store8 = [&](uint16_t *row, int c8, u16x8 x) {
+        if constexpr (kPerm) lds_store8_perm(row, c8, x);
+        else lds_store8(row + 8 * c8, x);
+    };
+    auto col_of = [&](int c) { return kPerm ? perm_col(c) : c; };
+    auto kfrag = [&](int mt, int s) { return frag(&kt[16 * mt + li][0], s); };
     float(*as)[CSTR] = reinterpret_cast<float(*)[CSTR]>(a_s);
     float(*ts)[CSTR] = reinterpret_cast<float(*)[CSTR]>(t_s);
     bf16x8 *pf_s = reinterpret_cast<bf16x8 *>(a_s);  // P fragments: ((mt * CS + s) * 2 + hi/lo) * 64 + lane
@@ -414,12 +444,13 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV>))
         for (int i = 0; i < R::NK; ++i) {
             const int e = tid + i * G::BLOCK;
             const int rr = e % C, c8 = e / C;
-            lds_store8(&ks[rr][8 * c8], cur.k[i]);
+            store8(&ks[rr][0], c8, cur.k[i]);
+            const int rc = col_of(rr);
 #pragma unroll
-            for (int q8 = 0; q8 < 8; ++q8) kt[8 * c8 + q8][rr] = cur.k[i][q8];
+            for (int q8 = 0; q8 < 8; ++q8) kt[8 * c8 + q8][rc] = cur.k[i][q8];
             if (!MAP) {
                 const int rq = e / (DK / 8), cq = e % (DK / 8);
-                lds_store8(&qs[rq][8 * cq], cur.q[i]);
+                store8(&qs[rq][0], cq, cur.q[i]);
             }
         }
         if (wave == 0) {
@@ -443,7 +474,7 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV>))
                 for (int i = 0; i < R::NV; ++i) {
                     const int e = tid + i * R::VTHREADS, rr = e % C, c8 = e / C;
 #pragma unroll
-                    for (int q8 = 0; q8 < 8; ++q8) vt[8 * c8 + q8][rr] = cur.v[i][q8];
+                    for (int q8 = 0; q8 < 8; ++q8) vt[8 * c8 + q8][col_of(rr)] = cur.v[i][q8];
                 }
             }
         }
@@ -464,7 +495,7 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV>))
             f32x4 acc = zero4;
 #pragma unroll
             for (int s = 0; s < G::KS; ++s)
-                acc = mfma_bf16(lds_frag_bf16(&ks[16 * mt + li][0], s, gq), lds_frag_bf16(&ks[16 * nt + li][0], s, gq),
+                acc = mfma_bf16(frag(&ks[16 * mt + li][0], s), frag(&ks[16 * nt + li][0], s),
                                 acc);
             const f32x4 grow = *reinterpret_cast<const f32x4 *>(&g_s[16 * mt + 4 * gq]);
             const f32x4 brow = *reinterpret_cast<const f32x4 *>(&b_s[16 * mt + 4 * gq]);
@@ -526,8 +557,8 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV>))
                 if (jt > mt) continue;
 #pragma unroll
                 for (int ss = 0; ss < G::KS; ++ss)
-                    acc[half] = mfma_bf16(lds_frag_bf16(&ks[16 * jt + li][0], ss, gq),
-                                          lds_frag_bf16(&qs[16 * mt + li][0], ss, gq), acc[half]);
+                    acc[half] = mfma_bf16(frag(&ks[16 * jt + li][0], ss), frag(&qs[16 * mt + li][0], ss),
+                                          acc[half]);
             }
             // lane holds P[r][j] for r = 16 mt + li and j = kmap(s, gq, e)
             const int r = 16 * mt + li;
@@ -749,7 +780,7 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV>))
                 for (int i = 0; i < R::NV; ++i) {
                     const int e = tid + i * R::VTHREADS, rr = e % C, c8 = e / C;
     #pragma unroll
-                    for (int q8 = 0; q8 < 8; ++q8) vt[8 * c8 + q8][rr] = cur.v[i][q8];
+                    for (int q8 = 0; q8 < 8; ++q8) vt[8 * c8 + q8][col_of(rr)] = cur.v[i][q8];
                 }
             }
             if (kTbFrags && (kSplitF || wave < G::CT)) {
@@ -852,7 +883,7 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV>))
                 // no erase term: Delta = diag(b) V, four consecutive chunk rows per lane from V^T
 #pragma unroll
                 for (int ct = 0; ct < G::CT; ++ct) {
-                    const u16x4 v4 = *reinterpret_cast<const u16x4 *>(&vt[16 * sl + li][16 * ct + 4 * gq]);
+                    const u16x4 v4 = *reinterpret_cast<const u16x4 *>(&vt[16 * sl + li][col_of(16 * ct + 4 * gq)]);
                     const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&b_s[16 * ct + 4 * gq]);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) D[ct][r] = b4[r] * from_bf16(v4[r]);
@@ -860,7 +891,7 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV>))
             } else if (value_slice) {
 #pragma unroll
                 for (int s = 0; s < G::CS; ++s) {
-                    const bf16x8 vb = lds_frag_bf16(&vt[16 * sl + li][0], s, gq);
+                    const bf16x8 vb = frag(&vt[16 * sl + li][0], s);
 #pragma unroll
                     for (int ct = 0; ct < G::CT; ++ct) {
                         if (32 * s > 16 * ct + 15) continue;  // T is lower triangular
@@ -921,7 +952,7 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV>))
                     f32x4 qsa = zero4, pd = zero4;
 #pragma unroll
                     for (int s = 0; s < G::KS; ++s) {
-                        const bf16x8 qa = lds_frag_bf16(&qs[16 * mt + li][0], s, gq);
+                        const bf16x8 qa = frag(&qs[16 * mt + li][0], s);
                         qsa = mfma_bf16(Sh[s], qa, qsa);
                         qsa = mfma_bf16(Sl[s], qa, qsa);
                     }
