@@ -537,11 +537,22 @@ def main():
         t1 = time.perf_counter()
         oracle.prefill(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], s0)
         cpu_s = time.perf_counter() - t1
+        cores = oracle.num_threads()
+        # the same on one thread and one head, so the scaling over the host cores is visible
+        one = {k: x[:, :, :1].contiguous() for k, x in sl.items()}
+        oracle.set_num_threads(1)
+        t1 = time.perf_counter()
+        oracle.prefill(one["q"], one["k"], one["v"], one["g"], one["beta"], s0[:, :1].contiguous())
+        one_s = time.perf_counter() - t1
+        oracle.set_num_threads(cores)
         result["cpu_baseline"] = {
-            "value": round(w.B * T / cpu_s, 1), "unit": "tokens/s", "cores": oracle.num_threads(),
+            "value": round(w.B * T / cpu_s, 1), "unit": "tokens/s", "cores": cores,
             "kind": "oracle",
             "sample": f"fp64 token-by-token oracle on the first {T} tokens of the 1b_64k workload, "
                       f"all {w.H} heads and value rows ({cpu_s:.2f} s)",
+            "token_heads_per_s": round(w.B * T * w.H / cpu_s, 1),
+            "single_thread_token_heads_per_s": round(w.B * T / one_s, 1),
+            "single_thread_sample": f"one head of the same tokens on one thread ({one_s:.2f} s)",
         }
 
     print(json.dumps(result), flush=True)

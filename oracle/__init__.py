@@ -92,12 +92,18 @@ class Oracle:
         lib.gdn_oracle_backward_rule.restype = i32
         lib.gdn_oracle_num_threads.argtypes = []
         lib.gdn_oracle_num_threads.restype = i32
+        lib.gdn_oracle_set_num_threads.argtypes = [i32]
+        lib.gdn_oracle_set_num_threads.restype = None
         self.lib = lib
         self.brute_force = brute_force
         self.closed_form_decay = closed_form_decay
 
     def num_threads(self) -> int:
         return int(self.lib.gdn_oracle_num_threads())
+
+    def set_num_threads(self, n: int) -> None:
+        """Threads of the following calls (timing only; results do not depend on it)."""
+        self.lib.gdn_oracle_set_num_threads(int(n))
 
     def prefill(self, q, k, v, g, beta, s0=None, rows=None, rule=GATED_DELTA):
         """Token-by-token fp64 evaluation of ``rule`` (GATED_DELTA or GATED_DECAY).
@@ -237,5 +243,9 @@ def num_threads() -> int:
     return default().num_threads()
 
 
+def set_num_threads(n: int) -> None:
+    default().set_num_threads(n)
+
+
 __all__ = ["Oracle", "default", "prefill", "decode_step", "backward", "brute_force", "closed_form_decay", "prep",
-           "num_threads", "build", "GATED_DELTA", "GATED_DECAY"]
+           "num_threads", "set_num_threads", "build", "GATED_DELTA", "GATED_DECAY"]

@@ -415,3 +415,9 @@ int gdn_oracle_num_threads(void)
 {
     return omp_get_max_threads();
 }
+
+/* Threads the next calls use (n >= 1), for timing the oracle on fewer cores. */
+void gdn_oracle_set_num_threads(int n)
+{
+    if (n >= 1) omp_set_num_threads(n);
+}

@@ -250,3 +250,19 @@ def test_rejects_bad_arguments(orc):
         orc.prefill(d["q"], d["k"], d["v"][:, :3], d["g"], d["beta"])
     with pytest.raises(ValueError):
         run(orc, d, rows=[4])
+
+
+def test_thread_count_does_not_change_results(orc):
+    """The oracle's work is split over (batch, head, value row) items that never share a
+    result, so one thread and all threads give bit-identical outputs (the CPU baseline times
+    both)."""
+    d = gi.prefill_inputs(1, 300, 3, 16, 16, wid=902, qkv_dtype=torch.bfloat16, s0=True)
+    n = orc.num_threads()
+    o_all, s_all = run(orc, d)
+    orc.set_num_threads(1)
+    try:
+        o_one, s_one = run(orc, d)
+    finally:
+        orc.set_num_threads(n)
+    assert orc.num_threads() == n
+    assert np.array_equal(o_all, o_one) and np.array_equal(s_all, s_one)
