@@ -336,7 +336,37 @@ def main():
     p3_ms = sum(a.elapsed_time(b) for a, b in p3_ev) / len(p3_ev)
     p3_th = w3.B * w3.T * w3.H
     p3_bytes = p3_th * BYTES_PER_TOKEN_HEAD_128 + 2 * w3.B * w3.H * w3.dk * w3.dv * 4
-    del p3, o3, ws3
+    del p3
+
+    # the whole 3B-shaped 2M-token prefill: 32 chained 64K calls, each on its own inputs (all
+    # resident before timing, 39 GB), the state carried from zeros through every call in place
+    chain_in = [gi.workload_inputs("3b_2m", call=c, device=dev) for c in range(w3.calls)]
+    s_chain = torch.zeros((w3.B, w3.H, w3.dk, w3.dv), device=dev, dtype=torch.float32)
+
+    def chain_2m(ev=None):
+        for c, d in enumerate(chain_in):
+            if ev is not None:
+                ev[c][0].record(stream)
+            gdn.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], s_chain, chunk=w3.chunk, out=o3,
+                              final_state=s_chain, workspace=ws3)
+            if ev is not None:
+                ev[c][1].record(stream)
+    chain_2m()
+    chain_ev, chain_call_ev = [], []
+    for _ in range(3):
+        s_chain.zero_()
+        a, b = mk(), mk()
+        calls_ev = [(mk(), mk()) for _ in chain_in]
+        a.record(stream)
+        chain_2m(calls_ev)
+        b.record(stream)
+        chain_ev.append((a, b))
+        chain_call_ev += calls_ev
+    torch.cuda.synchronize()
+    chain_ms = sorted(a.elapsed_time(b) for a, b in chain_ev)
+    chain_call_ms = sorted(a.elapsed_time(b) for a, b in chain_call_ev)
+    chain_tokens = w3.B * w3.T * w3.calls
+    del chain_in, s_chain, o3, ws3
 
     # preparation: alone (64K shape and decode batch), and followed by the 64K prefill
     for _ in range(args.warmup):
@@ -511,6 +541,17 @@ def main():
             "GBps_algorithmic": round(p3_bytes / (p3_ms * 1e-3) / 1e9, 1),
             "hbm_frac": round(p3_bytes / (p3_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
             "useful_TFLOPs": round(p3_th * FLOPS_PER_TOKEN_HEAD_128 / (p3_ms * 1e-3) / 1e12, 2),
+        },
+        "prefill_3b_2m_chain": {
+            "workload": "3B-shaped 2M-token prefill: 32 chained calls of B=1 H=24 T=65536 d_k=d_v=128 chunk 64, "
+                        "each on its own inputs, state carried from zeros through every call in place",
+            "calls": w3.calls, "tokens": chain_tokens,
+            "ms_median": round(chain_ms[len(chain_ms) // 2], 3), "ms_min": round(chain_ms[0], 3),
+            "ms_per_call_median": round(chain_call_ms[len(chain_call_ms) // 2], 4),
+            "tokens_per_s": round(chain_tokens / (chain_ms[len(chain_ms) // 2] * 1e-3), 1),
+            "GBps_algorithmic": round((chain_tokens * w3.H * BYTES_PER_TOKEN_HEAD_128
+                                       + w3.calls * 2 * w3.B * w3.H * w3.dk * w3.dv * 4)
+                                      / (chain_ms[len(chain_ms) // 2] * 1e-3) / 1e9, 1),
         },
         "gated_decay_rule": {
             "prefill_ms_avg": round(decay_pre_ms, 4),
