@@ -312,6 +312,31 @@ def main():
     torch.cuda.synchronize()
     varlen_ms = sum(a.elapsed_time(b) for a, b in vl_ev) / len(vl_ev)
 
+    # the 1B-shaped 8K batch (B=4 H=32 T=8192 d=64, zero start state); reported beside the main figures
+    w8 = gi.WORKLOADS["1b_8k"]
+    p8 = gi.workload_inputs("1b_8k", device=dev)
+    o8 = torch.empty((w8.B, w8.T, w8.H, w8.dv), device=dev, dtype=torch.float32)
+    f8 = torch.empty((w8.B, w8.H, w8.dk, w8.dv), device=dev, dtype=torch.float32)
+    ws8 = torch.empty(max(gdn.workspace_bytes(w8.B, w8.T, w8.H, w8.dk, w8.dv, w8.chunk, gdn.GDN_BF16), 1),
+                      device=dev, dtype=torch.uint8)
+
+    def prefill_8k():
+        gdn.chunk_prefill(p8["q"], p8["k"], p8["v"], p8["g"], p8["beta"], None, chunk=w8.chunk, out=o8,
+                          final_state=f8, workspace=ws8)
+    for _ in range(args.warmup):
+        prefill_8k()
+    p8_ev = [(mk(), mk()) for _ in range(args.steps)]
+    for a, b in p8_ev:
+        a.record(stream)
+        prefill_8k()
+        b.record(stream)
+    torch.cuda.synchronize()
+    p8_ms = sorted(a.elapsed_time(b) for a, b in p8_ev)
+    p8_avg = sum(p8_ms) / len(p8_ms)
+    p8_th = w8.B * w8.T * w8.H
+    p8_bytes = p8_th * BYTES_PER_TOKEN_HEAD + w8.B * w8.H * w8.dk * w8.dv * 4  # final state out; no start state
+    del p8, o8, f8, ws8
+
     # one 64K call of the 3B-shaped chain (B=1 H=24 T=65536 d=128), state carried in and out;
     # reported beside the main figures
     w3 = gi.WORKLOADS["3b_2m"]
@@ -533,6 +558,14 @@ def main():
             "note": "forward recompute (keeps chunk start states) + per-chunk maps + reverse scan + per-chunk "
                     "gradients, fp32 on the matrix cores; FLOPs are the gradient kernels' multiply-adds x 2, "
                     "alu_frac against the fp32 peak",
+        },
+        "prefill_1b_8k": {
+            "workload": "1b_8k: B=4 H=32 T=8192 d_k=d_v=64 chunk 64, bf16 q/k/v, zero start state, final state out",
+            "ms_avg": round(p8_avg, 4), "ms_median": round(p8_ms[len(p8_ms) // 2], 4),
+            "tokens_per_s": round(w8.B * w8.T / (p8_avg * 1e-3), 1),
+            "GBps_algorithmic": round(p8_bytes / (p8_avg * 1e-3) / 1e9, 1),
+            "hbm_frac": round(p8_bytes / (p8_avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "useful_TFLOPs": round(p8_th * FLOPS_PER_TOKEN_HEAD / (p8_avg * 1e-3) / 1e12, 2),
         },
         "prefill_3b_64k": {
             "workload": "one 64K call of the 3B-shaped chain: B=1 H=24 T=65536 d_k=d_v=128 chunk 64, bf16 q/k/v, "
