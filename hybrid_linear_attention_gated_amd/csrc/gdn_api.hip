@@ -261,8 +261,9 @@ gdn_status decode_impl(gdn_rule rule, const void *q, const void *k, const void *
     if (N < 0 || H <= 0 || d_k <= 0 || d_v <= 0 || pool < 0) return GDN_ERR_SHAPE;
     if (qkv_dtype != GDN_F32 && qkv_dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
     if (!supported_dim(d_k) || !supported_dim(d_v)) return GDN_ERR_UNSUPPORTED;
+    // the decode grid has up to 8 wavefronts per (sequence, head) (128-wide states)
     if (prod({N, H, d_k, d_v}) == SIZE_MAX || prod({pool, H, d_k, d_v}) == SIZE_MAX ||
-        prod({N, H, 4}) > 0x7fffffffULL)
+        prod({N, H, 8}) > 0x7fffffffULL)
         return GDN_ERR_SHAPE;
     if (N == 0) return GDN_OK;
     if (!q || !k || !v || !g || !beta || !o) return GDN_ERR_NULL;

@@ -156,7 +156,7 @@ GDN_API size_t gdn_chunk_prefill_workspace_size(int B, int T, int H, int d_k, in
  *   g, beta   [N, H]       fp32
  *   state     [N, H, d_k, d_v] fp32, read and updated in place
  *   o         [N, H, d_v]  fp32, written
- * N may be 0 (nothing is done).
+ * N may be 0 (nothing is done); N * H * 8 must stay below 2^31 (GDN_ERR_SHAPE).
  * Errors: GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_UNSUPPORTED, GDN_ERR_ALIGN,
  * GDN_ERR_ALIAS (o or state overlapping an input or each other), GDN_ERR_HIP.
  */

@@ -88,6 +88,11 @@ def test_decode_rejects(kw, code):
     assert decode(**kw) == code
 
 
+def test_decode_rejects_a_grid_past_the_launch_limit():
+    """128-wide states take eight wavefronts per (sequence, head): N H 8 must stay below 2^31."""
+    assert decode(N=1 << 26, H=5, dk=128, dv=128) == SHAPE
+
+
 def test_decode_zero_sequences_is_a_no_op():
     assert decode(N=0, q=None, k=None) == OK
 
