@@ -271,6 +271,9 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<DK, DV, C, MAP> &r, const C
 // workgroup's barrier waits are filled by the other's work.
 template <int DK, int DV>
 constexpr int kBlocksPerCU = (DK == 64 && DV == 64) ? 2 : 1;
+// workgroups the chip holds at once (256 compute units), the target of the piece plan
+template <int DK, int DV>
+constexpr int kPlanSlots = 256 * kBlocksPerCU<DK, DV>;
 
 // DELTA selects the rule: the gated delta rule (true) or the same recurrence without the
 // erase term (false), S_t = a_t S_{t-1} + b_t v_t k_t^T, whose chunk form has A = 0 and T = I:
@@ -1257,16 +1260,17 @@ __global__ __launch_bounds__(kWave) void chain_varlen_kernel(SeqTable sq, const 
         gq, li, col);
 }
 
-// Piece plan: at most 512 workgroups (two per compute unit), at least eight
-// chunks per piece, and no empty pieces.  Rounding the piece count down keeps
-// the grid within 512: one workgroup over it would run alone in a further round
-// (64-wide heads run two workgroups per compute unit, so 512 is one round;
-// 128-wide heads run one, so 512 is two full rounds).
+// Piece plan: one round of workgroups (slots = 256 compute units x the workgroups
+// one unit holds: 512 for 64 x 64 heads, 256 otherwise), at least eight chunks per
+// piece, and no empty pieces.  Rounding the piece count down keeps the grid within
+// the slots: a workgroup over them would run alone in a further round.  (128 x 128,
+// 24 heads: 10 pieces in one round 1.49 ms against 21 pieces in two rounds 1.52 ms;
+// rounding up to 22 pieces and a third round of 16 workgroups took 2.57 ms.)
 struct PiecePlan {
     int P, piece_chunks;
 };
-PiecePlan piece_plan(int BH, int N) {
-    int P = 512 / BH;
+PiecePlan piece_plan(int BH, int N, int slots) {
+    int P = slots / BH;
     P = max(1, min(P, N / 8));
     const int pc = (N + P - 1) / P;
     return {(N + pc - 1) / pc, pc};
@@ -1276,7 +1280,7 @@ template <int DK, int DV, int C>
 size_t chunk_ws_bytes(int B, int T, int H) {
     const int N = (T + C - 1) / C;
     const int BH = B * H;
-    const int P = piece_plan(BH, N).P;
+    const int P = piece_plan(BH, N, kPlanSlots<DK, DV>).P;
     if (P == 1) return 0;
     const size_t maps = static_cast<size_t>(BH) * (P - 1) * DK * (DV + DK) * 4;
     const size_t starts = static_cast<size_t>(BH) * P * DK * DV * 4;
@@ -1289,7 +1293,7 @@ hipError_t run_chunk(const uint16_t *q, const uint16_t *k, const uint16_t *v, co
                      void *ws, hipStream_t stream, float *chunk_states = nullptr) {
     const int N = (T + C - 1) / C;
     const int BH = B * H;
-    const PiecePlan plan = piece_plan(BH, N);
+    const PiecePlan plan = piece_plan(BH, N, kPlanSlots<DK, DV>);
     const int P = plan.P;
     ChunkArgs a{};
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.o = o; a.s_final = s_out;
