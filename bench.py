@@ -440,6 +440,25 @@ def main():
     bwd_ms = sum(a.elapsed_time(b) for a, b in bw_ev) / len(bw_ev)
     bwd_flops = bw.B * bw.T * bw.H * BWD_FLOPS_PER_TOKEN_HEAD
 
+    # decode on 3B-shaped states (256 sequences, H=24, 128 x 128 fp32 states, 402 MB): each state
+    # takes eight wavefronts of 32 floats per lane; reported beside the main figures
+    s128 = gi.decode_state(dw.B, 24, 128, 128, wid=95, device=dev)
+    in128 = [gi.decode_inputs(dw.B, 24, 128, 128, t, wid=95, device=dev) for t in range(dw.calls)]
+    o128 = torch.empty((dw.B, 24, 128), device=dev, dtype=torch.float32)
+    for d in in128:
+        gdn.decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], s128, out=o128)
+    d128_ev = [(mk(), mk()) for _ in range(max(3, args.steps // 2))]
+    for a, b in d128_ev:
+        a.record(stream)
+        for d in in128:
+            gdn.decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], s128, out=o128)
+        b.record(stream)
+    torch.cuda.synchronize()
+    d128_ms = sorted(a.elapsed_time(b) / len(in128) for a, b in d128_ev)
+    d128_avg = sum(d128_ms) / len(d128_ms)
+    d128_bytes = dw.B * 24 * (2 * 4 * 128 * 128 + 3 * 128 * 2 + 8 + 128 * 4)
+    del s128, in128, o128
+
     # decode with a cold last-level cache: read a 1 GiB buffer before each step, outside the
     # events (a read leaves only clean lines behind, so no write-back competes with the step)
     flush = torch.ones(FLUSH_BYTES // 4, device=dev, dtype=torch.float32)
@@ -527,6 +546,12 @@ def main():
                     "launch gaps included), the 128 MiB state can stay in the 256 MB last-level cache; cold: a "
                     "1 GiB buffer is read before every step; graph: the 16 steps replayed from one HIP graph, "
                     "time / 16",
+        },
+        "decode_3b_shape": {
+            "workload": "256 sequences, H=24, d_k=d_v=128 fp32 states (402 MB), 16 steps launched back to back",
+            "us_per_step_avg": round(d128_avg * 1e3, 2), "bytes_per_step": d128_bytes,
+            "GBps": round(d128_bytes / (d128_avg * 1e-3) / 1e9, 1),
+            "hbm_frac": round(d128_bytes / (d128_avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         },
         "varlen_prefill": {
             "sequences": 64, "tokens": Tv, "ms_avg": round(varlen_ms, 4),
