@@ -43,13 +43,21 @@ constexpr int kWavesPerBlock = 2;
 
 template <int DK, int DV>
 struct DecodeShape {
+    // 128-wide keys: the two wavefronts of a workgroup split a slice's key rows (64 each) and
+    // add their partial sums through LDS, so a slice can be 32 columns wide (128-byte row
+    // segments, whole cache lines) with 32 state floats per lane.  16-column slices of whole
+    // 128-row columns read and wrote half lines (61% of HBM peak on 256 x 24 states of
+    // 128 x 128; 32-column slices with 64 floats per lane 66%).
+    static constexpr int KSPLIT = DK == 128 ? kWavesPerBlock : 1;
+    static constexpr int KR = DK / KSPLIT;  // key rows per wavefront
     // columns per wavefront: keep at most 32 state floats per lane
-    static constexpr int WC = (2048 / DK < DV) ? 2048 / DK : DV;
+    static constexpr int WC = KSPLIT > 1 ? (DV < 32 ? DV : 32) : ((2048 / DK < DV) ? 2048 / DK : DV);
     static constexpr int SLICES = DV / WC;
     static constexpr int LPR = WC / 4;       // lanes per key row (one float4 each)
     static constexpr int RG = kWave / LPR;   // key-row groups per wavefront
-    static constexpr int ROWS = DK / RG;     // key rows per lane
-    static_assert(WC % 4 == 0 && kWave % LPR == 0 && DK % RG == 0, "decode tiling");
+    static constexpr int ROWS = KR / RG;     // key rows per lane
+    static_assert(WC % 4 == 0 && kWave % LPR == 0 && KR % RG == 0, "decode tiling");
+    static_assert(KSPLIT == 1 || KSPLIT == kWavesPerBlock, "a split spans one workgroup");
 };
 
 template <int DK, int DV, typename TIn, bool DELTA>
@@ -59,22 +67,26 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void decode_kernel(
     float *__restrict__ o, int items, float scale, const int *__restrict__ slots, int H, int pool) {
     using S = DecodeShape<DK, DV>;
     const int lane = threadIdx.x % kWave;
-    const int item = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
-    if (item >= items) return;  // whole wavefront exits together
+    // work item: one (sequence, head, column slice); with split key rows a workgroup's two
+    // wavefronts share one item (half = which key rows), else each wavefront has its own
+    const int half = S::KSPLIT > 1 ? static_cast<int>(threadIdx.x) / kWave : 0;
+    const int item = S::KSPLIT > 1 ? static_cast<int>(blockIdx.x)
+                                   : static_cast<int>(blockIdx.x) * kWavesPerBlock + static_cast<int>(threadIdx.x) / kWave;
+    if (item >= items) return;  // the whole wavefront (with split rows: the whole workgroup) exits together
     const int slice = item % S::SLICES;
     const size_t nh = static_cast<size_t>(item / S::SLICES);  // n * H + h
 
     const int c = lane % S::LPR;   // float4 column index inside the slice
     const int rg = lane / S::LPR;  // key-row group
     const int col = slice * S::WC + 4 * c;
-    const int row0 = rg * S::ROWS;
+    const int row0 = half * S::KR + rg * S::ROWS;
 
     size_t sh = nh;  // state index: (slot * H + h) when states live in a pool
     if (slots) {
         const int n = static_cast<int>(nh / H), h = static_cast<int>(nh % H);
         const int slot = slots[n];  // the same for the whole wavefront
-        if (slot < 0 || slot >= pool) {
-            if (rg == 0) *reinterpret_cast<f32x4 *>(o + nh * DV + col) = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (slot < 0 || slot >= pool) {  // uniform over the workgroup's item
+            if (half == 0 && rg == 0) *reinterpret_cast<f32x4 *>(o + nh * DV + col) = f32x4{0.f, 0.f, 0.f, 0.f};
             return;
         }
         sh = static_cast<size_t>(slot) * H + h;
@@ -114,13 +126,34 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void decode_kernel(
         }
         kq += __shfl_xor(kq, off, kWave);
     }
+    if constexpr (S::KSPLIT > 1) {
+        // the other key rows' partial sums, through LDS; both wavefronts add them in the same
+        // order, so they hold the same totals
+        __shared__ f32x4 xu[S::KSPLIT][S::LPR], xp[S::KSPLIT][S::LPR];
+        __shared__ float xkq[S::KSPLIT];
+        if (rg == 0) {
+            xu[half][c] = u;
+            xp[half][c] = p;
+            if (c == 0) xkq[half] = kq;
+        }
+        __syncthreads();
+        u = xu[0][c];
+        p = xp[0][c];
+        kq = xkq[0];
+#pragma unroll
+        for (int hh = 1; hh < S::KSPLIT; ++hh) {
+            u += xu[hh][c];
+            p += xp[hh][c];
+            kq += xkq[hh];
+        }
+    }
 
     f32x4 vv;
 #pragma unroll
     for (int e = 0; e < 4; ++e) vv[e] = load_in(v, nh * DV + col + e);
     const f32x4 delta = DELTA ? b * (vv - a * u) : b * vv;
 
-    if (rg == 0) {
+    if (half == 0 && rg == 0) {
         const f32x4 out = scale * (a * p + delta * kq);
         *reinterpret_cast<f32x4 *>(o + nh * DV + col) = out;
     }
@@ -136,7 +169,7 @@ hipError_t launch_decode_t(const void *q, const void *k, const void *v, const fl
                            const int *slots, int pool, hipStream_t stream) {
     using S = DecodeShape<DK, DV>;
     const long long items = static_cast<long long>(N) * H * S::SLICES;
-    const int blocks = static_cast<int>((items + kWavesPerBlock - 1) / kWavesPerBlock);
+    const int blocks = static_cast<int>(S::KSPLIT > 1 ? items : (items + kWavesPerBlock - 1) / kWavesPerBlock);
     const float scale = 1.0f / sqrtf(static_cast<float>(DK));
     if (delta)
         hipLaunchKernelGGL((decode_kernel<DK, DV, TIn, true>), dim3(blocks), dim3(kWave * kWavesPerBlock),
