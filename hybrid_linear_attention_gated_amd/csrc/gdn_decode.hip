@@ -40,38 +40,41 @@ namespace {
 
 constexpr int kWave = 64;
 constexpr int kWavesPerBlock = 2;
+// wavefronts per workgroup: 128-wide keys split a slice's key rows over four of them
+template <int DK> constexpr int kWPB = DK == 128 ? 4 : kWavesPerBlock;
 
 template <int DK, int DV>
 struct DecodeShape {
-    // 128-wide keys: the two wavefronts of a workgroup split a slice's key rows (64 each) and
-    // add their partial sums through LDS, so a slice can be 32 columns wide (128-byte row
-    // segments, whole cache lines) with 32 state floats per lane.  16-column slices of whole
-    // 128-row columns read and wrote half lines (61% of HBM peak on 256 x 24 states of
-    // 128 x 128; 32-column slices with 64 floats per lane 66%).
-    static constexpr int KSPLIT = DK == 128 ? kWavesPerBlock : 1;
+    // 128-wide keys: the four wavefronts of a workgroup split a slice's key rows (32 each) and
+    // add their partial sums through LDS, so a slice can be 64 columns wide (256-byte row
+    // segments) with 32 state floats per lane.  16-column slices of whole 128-row columns read
+    // and wrote half cache lines (61% of HBM peak on 256 x 24 states of 128 x 128; 32-column
+    // slices split over two wavefronts 65%; this 66%).
+    static constexpr int KSPLIT = DK == 128 ? 4 : 1;
     static constexpr int KR = DK / KSPLIT;  // key rows per wavefront
     // columns per wavefront: keep at most 32 state floats per lane
-    static constexpr int WC = KSPLIT > 1 ? (DV < 32 ? DV : 32) : ((2048 / DK < DV) ? 2048 / DK : DV);
+    static constexpr int WC = KSPLIT > 1 ? (DV < 64 ? DV : 64) : ((2048 / DK < DV) ? 2048 / DK : DV);
     static constexpr int SLICES = DV / WC;
     static constexpr int LPR = WC / 4;       // lanes per key row (one float4 each)
     static constexpr int RG = kWave / LPR;   // key-row groups per wavefront
     static constexpr int ROWS = KR / RG;     // key rows per lane
     static_assert(WC % 4 == 0 && kWave % LPR == 0 && KR % RG == 0, "decode tiling");
-    static_assert(KSPLIT == 1 || KSPLIT == kWavesPerBlock, "a split spans one workgroup");
+    static_assert(KSPLIT == 1 || KSPLIT == kWPB<DK>, "a split spans one workgroup");
+
 };
 
 template <int DK, int DV, typename TIn, bool DELTA>
-__global__ __launch_bounds__(kWave * kWavesPerBlock) void decode_kernel(
+__global__ __launch_bounds__(kWave * kWPB<DK>) void decode_kernel(
     const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, float *__restrict__ state,
     float *__restrict__ o, int items, float scale, const int *__restrict__ slots, int H, int pool) {
     using S = DecodeShape<DK, DV>;
     const int lane = threadIdx.x % kWave;
-    // work item: one (sequence, head, column slice); with split key rows a workgroup's two
+    // work item: one (sequence, head, column slice); with split key rows a workgroup's
     // wavefronts share one item (half = which key rows), else each wavefront has its own
     const int half = S::KSPLIT > 1 ? static_cast<int>(threadIdx.x) / kWave : 0;
     const int item = S::KSPLIT > 1 ? static_cast<int>(blockIdx.x)
-                                   : static_cast<int>(blockIdx.x) * kWavesPerBlock + static_cast<int>(threadIdx.x) / kWave;
+                                   : static_cast<int>(blockIdx.x) * kWPB<DK> + static_cast<int>(threadIdx.x) / kWave;
     if (item >= items) return;  // the whole wavefront (with split rows: the whole workgroup) exits together
     const int slice = item % S::SLICES;
     const size_t nh = static_cast<size_t>(item / S::SLICES);  // n * H + h
@@ -169,15 +172,15 @@ hipError_t launch_decode_t(const void *q, const void *k, const void *v, const fl
                            const int *slots, int pool, hipStream_t stream) {
     using S = DecodeShape<DK, DV>;
     const long long items = static_cast<long long>(N) * H * S::SLICES;
-    const int blocks = static_cast<int>(S::KSPLIT > 1 ? items : (items + kWavesPerBlock - 1) / kWavesPerBlock);
+    const int blocks = static_cast<int>(S::KSPLIT > 1 ? items : (items + kWPB<DK> - 1) / kWPB<DK>);
     const float scale = 1.0f / sqrtf(static_cast<float>(DK));
     if (delta)
-        hipLaunchKernelGGL((decode_kernel<DK, DV, TIn, true>), dim3(blocks), dim3(kWave * kWavesPerBlock),
+        hipLaunchKernelGGL((decode_kernel<DK, DV, TIn, true>), dim3(blocks), dim3(kWave * kWPB<DK>),
                            0, stream, static_cast<const TIn *>(q), static_cast<const TIn *>(k),
                            static_cast<const TIn *>(v), g, beta, state, o, static_cast<int>(items),
                            scale, slots, H, pool);
     else
-        hipLaunchKernelGGL((decode_kernel<DK, DV, TIn, false>), dim3(blocks), dim3(kWave * kWavesPerBlock),
+        hipLaunchKernelGGL((decode_kernel<DK, DV, TIn, false>), dim3(blocks), dim3(kWave * kWPB<DK>),
                            0, stream, static_cast<const TIn *>(q), static_cast<const TIn *>(k),
                            static_cast<const TIn *>(v), g, beta, state, o, static_cast<int>(items),
                            scale, slots, H, pool);
