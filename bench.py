@@ -173,6 +173,23 @@ def main():
                            pcu, ppool, slots=pslots, decay_rate=din["decay_rate"], gate_bias=din["gate_bias"],
                            outs=pool_outs, workspace=pws)
 
+    # the same decode step (preparation + state update) fused into one launch, and as two launches
+    fstate = gi.decode_state(dw.B, dw.H, dw.dk, dw.dv, wid=202, device=dev)
+    fconv = din["conv_state"].clone()
+    fout = torch.empty((dw.B, dw.H, dw.dv), device=dev, dtype=torch.float32)
+    souts = tuple(torch.empty((dw.B, 1) + tuple(t.shape[1:]), device=dev, dtype=t.dtype) for t in pool_outs)
+
+    def decode_fused():
+        gdn.prepare_decode_step(pflat["xq"], pflat["xk"], pflat["xv"], din["conv_weight"], pflat["a_raw"],
+                                pflat["b_raw"], fconv, fstate, decay_rate=din["decay_rate"],
+                                gate_bias=din["gate_bias"], out=fout)
+
+    def decode_separate():
+        q, k, v, g, b = gdn.prepare(din["xq"], din["xk"], din["xv"], din["conv_weight"], din["a_raw"], din["b_raw"],
+                                    decay_rate=din["decay_rate"], gate_bias=din["gate_bias"], conv_state=fconv,
+                                    conv_state_out=fconv, outs=souts)
+        gdn.decode_step(q[:, 0], k[:, 0], v[:, 0], g[:, 0], b[:, 0], fstate, out=fout)
+
     def prepare():
         gdn.prepare(pin["xq"], pin["xk"], pin["xv"], pin["conv_weight"], pin["a_raw"], pin["b_raw"],
                     decay_rate=pin["decay_rate"], gate_bias=pin["gate_bias"], conv_state=pin["conv_state"],
@@ -398,7 +415,11 @@ def main():
         prepare()
         prepare_decode()
         prepare_decode_pool()
+        decode_fused()
+        decode_separate()
     pp_ev = [(mk(), mk()) for _ in range(args.steps)]
+    fu_ev = [(mk(), mk()) for _ in range(args.steps)]
+    se_ev = [(mk(), mk()) for _ in range(args.steps)]
     pd_ev = [(mk(), mk()) for _ in range(args.steps)]
     pv_ev = [(mk(), mk()) for _ in range(args.steps)]
     pc_ev = [(mk(), mk()) for _ in range(args.steps)]
@@ -412,6 +433,12 @@ def main():
         pv_ev[i][0].record(stream)
         prepare_decode_pool()
         pv_ev[i][1].record(stream)
+        fu_ev[i][0].record(stream)
+        decode_fused()
+        fu_ev[i][1].record(stream)
+        se_ev[i][0].record(stream)
+        decode_separate()
+        se_ev[i][1].record(stream)
     for i in range(args.steps):
         pc_ev[i][0].record(stream)
         prepare()
@@ -424,9 +451,15 @@ def main():
     prep_dec_ms = sum(a.elapsed_time(b) for a, b in pd_ev) / len(pd_ev)
     prep_pool_ms = sum(a.elapsed_time(b) for a, b in pv_ev) / len(pv_ev)
     prep_chain_ms = sum(a.elapsed_time(b) for a, b in pc_ev) / len(pc_ev)
+    fused_ms = sum(a.elapsed_time(b) for a, b in fu_ev) / len(fu_ev)
+    separate_ms = sum(a.elapsed_time(b) for a, b in se_ev) / len(se_ev)
+    del fstate, fconv
     conv_ch = w.H * (2 * w.dk + w.dv)
     prep_bytes = w.B * w.T * w.H * PREP_BYTES_PER_TOKEN_HEAD + conv_ch * (16 + 24 * w.B)
     prep_dec_bytes = dw.B * dw.H * PREP_BYTES_PER_TOKEN_HEAD + conv_ch * (16 + 24 * dw.B)
+    # fused step: raw q, k, v (bf16) + two logits in, the state read and written, o out, windows
+    fused_bytes = (dw.B * dw.H * (3 * 64 * 2 + 2 * 4 + 2 * dw.dk * dw.dv * 4 + dw.dv * 4)
+                   + conv_ch * (16 + 24 * dw.B))
 
     # backward on the training shape
     for _ in range(args.warmup):
@@ -567,12 +600,17 @@ def main():
             "decode_us_avg": round(prep_dec_ms * 1e3, 2),
             "decode_GBps_algorithmic": round(prep_dec_bytes / (prep_dec_ms * 1e-3) / 1e9, 1),
             "decode_pool_us_avg": round(prep_pool_ms * 1e3, 2),
+            "decode_step_fused_us_avg": round(fused_ms * 1e3, 2),
+            "decode_step_fused_hbm_frac": round(fused_bytes / (fused_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "decode_step_separate_us_avg": round(separate_ms * 1e3, 2),
             "traffic_bytes_per_call": recorded_traffic("prepare"),
             "prepare_then_prefill_ms_avg": round(prep_chain_ms, 4),
             "prepare_then_prefill_tokens_per_s": round(w.B * w.T / (prep_chain_ms * 1e-3), 1),
             "note": "short causal convolution + SiLU + q/k L2 norm + gate activations on the 64K shape "
                     "(bf16 in and out) and on the 256-sequence decode batch (state in place; decode_pool: the "
-                    "same step as 256 one-token packed sequences with states in a 512-slot pool)",
+                    "same step as 256 one-token packed sequences with states in a 512-slot pool; decode_step_fused: "
+                    "preparation and state update of that batch in one launch, decode_step_separate: the same as "
+                    "gdn_prepare + gdn_decode_step)",
         },
         "backward": {
             "workload": "1b_8k: B=4 H=32 T=8192 d_k=d_v=64, bf16 q/k/v, gated delta rule, zero start state",

@@ -8,8 +8,8 @@ pointers passed as integers):
 
     gdn_chunk_prefill, gdn_chunk_prefill_rule, gdn_chunk_prefill_workspace_size,
     gdn_chunk_prefill_varlen, gdn_chunk_prefill_varlen_workspace_size, gdn_decode_step,
-    gdn_decode_step_rule, gdn_decode_step_slots, gdn_prepare, gdn_chunk_backward,
-    gdn_chunk_backward_workspace_size, gdn_status_string, gdn_version
+    gdn_decode_step_rule, gdn_decode_step_slots, gdn_prepare, gdn_prepare_decode_step,
+    gdn_chunk_backward, gdn_chunk_backward_workspace_size, gdn_status_string, gdn_version
 
 Tensor helpers that allocate outputs with torch and call the above on the
 current stream:
@@ -18,6 +18,7 @@ current stream:
     decode_step(q, k, v, g, beta, state) -> o        (state updated in place)
     decode_step_slots / chunk_prefill_varlen          (states in a pool, packed sequences)
     prepare(xq, xk, xv, conv_weight, a_raw, b_raw) -> (q, k, v, g, beta)
+    prepare_decode_step(xq, xk, xv, conv_weight, a_raw, b_raw, conv_state, state) -> o
     chunk_backward(q, k, v, g, beta, d_o, ...) -> (dq, dk, dv, dg, dbeta, d_initial_state)
 
 The rule computed (a gated delta rule; the pages describe the GDN layer in
@@ -43,7 +44,7 @@ EXPORTS = ("gdn_chunk_prefill", "gdn_chunk_prefill_rule", "gdn_chunk_prefill_wor
            "gdn_chunk_prefill_varlen", "gdn_chunk_prefill_varlen_workspace_size",
            "gdn_decode_step", "gdn_decode_step_rule", "gdn_decode_step_slots", "gdn_prepare",
            "gdn_chunk_backward", "gdn_chunk_backward_workspace_size", "gdn_prepare_varlen",
-           "gdn_prepare_varlen_workspace_size", "gdn_status_string", "gdn_version")
+           "gdn_prepare_varlen_workspace_size", "gdn_prepare_decode_step", "gdn_status_string", "gdn_version")
 
 
 class GdnError(RuntimeError):
@@ -85,6 +86,8 @@ def lib():
         L.gdn_chunk_prefill_varlen_workspace_size.restype = sz
         L.gdn_prepare.argtypes = [vp] * 15 + [i32] * 6 + [vp]
         L.gdn_prepare.restype = i32
+        L.gdn_prepare_decode_step.argtypes = [i32] + [vp] * 11 + [i32] * 5 + [vp]
+        L.gdn_prepare_decode_step.restype = i32
         L.gdn_chunk_backward.argtypes = [i32] + [vp] * 14 + [i32] * 6 + [vp, sz, vp]
         L.gdn_chunk_backward.restype = i32
         L.gdn_chunk_backward_workspace_size.argtypes = [i32] * 6
@@ -144,6 +147,12 @@ def gdn_chunk_prefill_varlen(rule, q, k, v, g, beta, cu_seqlens, S, T_total, sta
 
 def gdn_chunk_prefill_varlen_workspace_size(cu_seqlens, S, H, d_k, d_v, chunk, qkv_dtype) -> int:
     return lib().gdn_chunk_prefill_varlen_workspace_size(cu_seqlens, S, H, d_k, d_v, chunk, qkv_dtype)
+
+
+def gdn_prepare_decode_step(rule, xq, xk, xv, conv_weight, a_raw, b_raw, decay_rate, gate_bias, conv_state,
+                            state, o, N, H, d_k, d_v, x_dtype, stream) -> int:
+    return lib().gdn_prepare_decode_step(rule, xq, xk, xv, conv_weight, a_raw, b_raw, decay_rate, gate_bias,
+                                         conv_state, state, o, N, H, d_k, d_v, x_dtype, stream)
 
 
 def gdn_prepare(xq, xk, xv, conv_weight, a_raw, b_raw, decay_rate, gate_bias, conv_state_in,
@@ -307,6 +316,37 @@ def decode_step_slots(q, k, v, g, beta, state_pool, slots, *, out=None, stream=N
                                _ptr(slots), state_pool.shape[0], _ptr(out), N, H, d_k, d_v, dt, stream)
     if st != 0:
         raise GdnError(st, "gdn_decode_step_slots")
+    return out
+
+
+def prepare_decode_step(xq, xk, xv, conv_weight, a_raw, b_raw, conv_state, state, *, decay_rate=None,
+                        gate_bias=None, out=None, stream=None, rule=GDN_RULE_GATED_DELTA):
+    """One token per sequence from the raw projections: xq, xk [N,H,d_k], xv [N,H,d_v] (bf16 or fp32);
+    conv_weight [H*(2 d_k + d_v), 4] fp32; a_raw, b_raw [N,H] fp32; conv_state [N, H*(2 d_k + d_v), 3]
+    fp32 and state [N,H,d_k,d_v] fp32, both updated in place; decay_rate, gate_bias [H] fp32 or None.
+    Returns o fp32 [N,H,d_v] (prepare with T = 1, then decode_step, in one launch)."""
+    import torch
+    N, H, d_k = xq.shape
+    d_v = xv.shape[-1]
+    dt = _dtype_code(xq)
+    C = H * (2 * d_k + d_v)
+    _check(xq, "xq", xq.dtype)
+    _check(xk, "xk", xq.dtype, (N, H, d_k))
+    _check(xv, "xv", xq.dtype, (N, H, d_v))
+    for t, n, shp in ((conv_weight, "conv_weight", (C, 4)), (a_raw, "a_raw", (N, H)), (b_raw, "b_raw", (N, H)),
+                      (decay_rate, "decay_rate", (H,)), (gate_bias, "gate_bias", (H,)),
+                      (conv_state, "conv_state", (N, C, 3)), (state, "state", (N, H, d_k, d_v))):
+        _check(t, n, torch.float32, shp)
+    if out is None:
+        out = torch.empty((N, H, d_v), device=xq.device, dtype=torch.float32)
+    _check(out, "out", torch.float32, (N, H, d_v))
+    if stream is None:
+        stream = torch.cuda.current_stream(xq.device).cuda_stream
+    st = gdn_prepare_decode_step(rule, _ptr(xq), _ptr(xk), _ptr(xv), _ptr(conv_weight), _ptr(a_raw), _ptr(b_raw),
+                                 _ptr(decay_rate), _ptr(gate_bias), _ptr(conv_state), _ptr(state), _ptr(out),
+                                 N, H, d_k, d_v, dt, stream)
+    if st != 0:
+        raise GdnError(st, "gdn_prepare_decode_step")
     return out
 
 
@@ -510,4 +550,4 @@ __all__ = ["EXPORTS", "GDN_F32", "GDN_BF16", "GDN_RULE_GATED_DELTA", "GDN_RULE_G
            "chunk_prefill", "chunk_prefill_varlen", "decode_step", "decode_step_slots", "workspace_bytes",
            "varlen_workspace_bytes", "gdn_prepare", "prepare", "gdn_chunk_backward",
            "gdn_chunk_backward_workspace_size", "chunk_backward", "backward_workspace_bytes", "gdn_prepare_varlen",
-           "gdn_prepare_varlen_workspace_size", "prepare_varlen"]
+           "gdn_prepare_varlen_workspace_size", "prepare_varlen", "gdn_prepare_decode_step", "prepare_decode_step"]

@@ -65,6 +65,13 @@ hipError_t launch_state_copy(const float *s0, float *s_out, size_t n, hipStream_
     return hipGetLastError();
 }
 
+// the fused decode step from raw projections (gdn_decode_prep.hip)
+bool prepare_decode_supported(int dk, int dv);
+hipError_t launch_prepare_decode(const void *xq, const void *xk, const void *xv, const float *w,
+                                 const float *a_raw, const float *b_raw, const float *rate,
+                                 const float *bias, float *conv_state, float *state, float *o, int N,
+                                 int H, gdn_dtype dt, bool delta, hipStream_t stream);
+
 }  // namespace gdn
 
 using namespace gdn;
@@ -312,6 +319,44 @@ gdn_status gdn_decode_step(const void *q, const void *k, const void *v, const fl
                            int d_v, gdn_dtype qkv_dtype, void *stream) {
     return gdn_decode_step_rule(GDN_RULE_GATED_DELTA, q, k, v, g, beta, state, o, N, H, d_k, d_v,
                                 qkv_dtype, stream);
+}
+
+gdn_status gdn_prepare_decode_step(gdn_rule rule, const void *xq, const void *xk, const void *xv,
+                                   const float *conv_weight, const float *a_raw, const float *b_raw,
+                                   const float *decay_rate, const float *gate_bias, float *conv_state,
+                                   float *state, float *o, int N, int H, int d_k, int d_v,
+                                   gdn_dtype x_dtype, void *stream) {
+    if (rule != GDN_RULE_GATED_DELTA && rule != GDN_RULE_GATED_DECAY) return GDN_ERR_UNSUPPORTED;
+    if (N < 0 || H <= 0 || d_k <= 0 || d_v <= 0) return GDN_ERR_SHAPE;
+    if (x_dtype != GDN_F32 && x_dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+    if (!prepare_decode_supported(d_k, d_v)) return GDN_ERR_UNSUPPORTED;
+    const long long C = static_cast<long long>(H) * (2 * d_k + d_v);
+    if (prod({N, H, d_k, d_v}) == SIZE_MAX || prod({N, C, 3}) == SIZE_MAX || prod({N, H}) > 0x7fffffffULL)
+        return GDN_ERR_SHAPE;
+    if (N == 0) return GDN_OK;
+    if (!xq || !xk || !xv || !conv_weight || !a_raw || !b_raw || !conv_state || !state || !o)
+        return GDN_ERR_NULL;
+    const void *ptrs[] = {xq, xk, xv, conv_weight, a_raw, b_raw, decay_rate, gate_bias, conv_state, state, o};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return GDN_ERR_ALIGN;
+    const size_t es = elem_bytes(x_dtype);
+    const Span in[] = {span(xq, prod({N, H, d_k}) * es), span(xk, prod({N, H, d_k}) * es),
+                       span(xv, prod({N, H, d_v}) * es), span(conv_weight, static_cast<size_t>(C) * 16),
+                       span(a_raw, prod({N, H}) * 4), span(b_raw, prod({N, H}) * 4),
+                       span(decay_rate, decay_rate ? static_cast<size_t>(H) * 4 : 0),
+                       span(gate_bias, gate_bias ? static_cast<size_t>(H) * 4 : 0)};
+    const Span out[] = {span(conv_state, prod({N, C, 3}) * 4), span(state, prod({N, H, d_k, d_v}) * 4),
+                        span(o, prod({N, H, d_v}) * 4)};
+    for (int i = 0; i < 3; ++i) {
+        for (int j = i + 1; j < 3; ++j)
+            if (overlap(out[i], out[j])) return GDN_ERR_ALIAS;
+        for (const Span &x : in)
+            if (overlap(out[i], x)) return GDN_ERR_ALIAS;
+    }
+    const hipError_t err = launch_prepare_decode(xq, xk, xv, conv_weight, a_raw, b_raw, decay_rate, gate_bias,
+                                                 conv_state, state, o, N, H, x_dtype,
+                                                 rule == GDN_RULE_GATED_DELTA, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
 gdn_status gdn_prepare(const void *xq, const void *xk, const void *xv, const float *conv_weight,

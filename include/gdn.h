@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 5
+#define GDN_ABI_VERSION 6
 
 #if defined(__GNUC__) || defined(__clang__)
 #define GDN_API __attribute__((visibility("default")))
@@ -302,6 +302,43 @@ GDN_API gdn_status gdn_prepare(const void *xq, const void *xk, const void *xv,
                                void *q, void *k, void *v, float *g, float *beta,
                                int B, int T, int H, int d_k, int d_v,
                                gdn_dtype x_dtype, void *stream);
+
+/*
+ * gdn_prepare_decode_step -- one generated token for each of N sequences, from
+ * the raw projections: gdn_prepare with T = 1 and the convolution window
+ * updated in place, then gdn_decode_step_rule on the prepared q, k, v, g, beta,
+ * in one launch (the prepared values stay on chip, in fp32: unlike gdn_prepare's
+ * outputs they are not rounded to bf16 for GDN_BF16).  The per-token loop of a serving
+ * engine (the pages' hybrids decode with a fixed-size state per request;
+ * ftxj.github.io digest of arXiv 2604.24715, Method: the converted GDN block keeps
+ * a short convolution and gate/decay parameters of its own).
+ *
+ *   rule            GDN_RULE_GATED_DELTA or GDN_RULE_GATED_DECAY
+ *   xq, xk          [N, H, d_k] x_dtype (raw projections of this token)
+ *   xv              [N, H, d_v] x_dtype
+ *   conv_weight     [H*(2 d_k + d_v), 4] fp32, as for gdn_prepare
+ *   a_raw, b_raw    [N, H] fp32 gate and write-strength logits
+ *   decay_rate      [H] fp32 or NULL (1);  gate_bias [H] fp32 or NULL (0)
+ *   conv_state      [N, H*(2 d_k + d_v), 3] fp32, the three raw inputs before
+ *                   this token (oldest first), read and updated in place
+ *   state           [N, H, d_k, d_v] fp32, read and updated in place
+ *   o               [N, H, d_v] fp32, written
+ * Supported: d_k = d_v = 64.  N may be 0 (nothing is done).  For GDN_F32 the
+ * result equals gdn_prepare followed by gdn_decode_step_rule up to the summation
+ * order of each head's squared q and k norms; for GDN_BF16 it is that of the
+ * separate steps without the bf16 rounding of the prepared q, k, v.
+ * Errors: GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_UNSUPPORTED (rule, dtype, or
+ * d_k, d_v other than 64), GDN_ERR_ALIGN, GDN_ERR_ALIAS (conv_state, state or
+ * o overlapping an input or each other), GDN_ERR_HIP.
+ */
+GDN_API gdn_status gdn_prepare_decode_step(gdn_rule rule,
+                                           const void *xq, const void *xk, const void *xv,
+                                           const float *conv_weight,
+                                           const float *a_raw, const float *b_raw,
+                                           const float *decay_rate, const float *gate_bias,
+                                           float *conv_state, float *state, float *o,
+                                           int N, int H, int d_k, int d_v,
+                                           gdn_dtype x_dtype, void *stream);
 
 /*
  * gdn_prepare_varlen -- gdn_prepare over S packed sequences of different

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     L = gdn.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert gdn.gdn_version() == 5
+    assert gdn.gdn_version() == 6
 
 
 def test_status_strings():
@@ -282,3 +282,29 @@ def test_prepare_varlen_validation():
     assert gdn.gdn_prepare_varlen_workspace_size(3) >= 40
     # no sequences: nothing to do
     assert prepare_varlen_call(cu=np.array([0], dtype=np.int32), S=0, T=0) == OK
+
+
+def prepare_decode_call(**kw):
+    args = dict(rule=0, xq=addr(0), xk=addr(1), xv=addr(2), w=addr(3), a=addr(4), b=addr(5), rate=None, bias=None,
+                conv=addr(6), state=addr(7), o=addr(8), N=256, H=32, dk=64, dv=64, dt=BF16, stream=None)
+    args.update(kw)
+    return gdn.gdn_prepare_decode_step(*[args[n] for n in ("rule", "xq", "xk", "xv", "w", "a", "b", "rate", "bias",
+                                                           "conv", "state", "o", "N", "H", "dk", "dv", "dt",
+                                                           "stream")])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(rule=2), UNSUP), (dict(H=0), SHAPE), (dict(N=-1), SHAPE), (dict(dk=128, dv=128), UNSUP),
+    (dict(dk=64, dv=128), UNSUP), (dict(dt=5), UNSUP), (dict(N=1 << 30, H=4), SHAPE),
+    (dict(xq=None), NULL), (dict(conv=None), NULL), (dict(state=None), NULL), (dict(o=None), NULL),
+    (dict(w=None), NULL), (dict(b=None), NULL),
+    (dict(xk=addr(1) + 8), ALIGN), (dict(state=addr(7) + 4), ALIGN), (dict(bias=addr(9) + 2), ALIGN),
+    (dict(o=addr(7) + 256), ALIAS), (dict(conv=addr(0)), ALIAS), (dict(state=addr(6) + 64), ALIAS),
+    (dict(o=addr(4)), ALIAS), (dict(rate=addr(8)), ALIAS),
+])
+def test_prepare_decode_rejects(kw, code):
+    assert prepare_decode_call(**kw) == code
+
+
+def test_prepare_decode_no_sequences_is_a_no_op():
+    assert prepare_decode_call(N=0, xq=None, xk=None, xv=None, conv=None, state=None, o=None) == OK
