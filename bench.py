@@ -72,7 +72,7 @@ TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_prefill_1b_64k_dec
 
 def recorded_traffic(kind):
     """Counter-measured HBM bytes for `kind` ('prefill' and 'prepare' per 64K call, 'decode' per
-    step) from the committed summary, or None when the kernel sources no longer match the recorded
+    step, 'fused' per one-launch decode step of the 256-sequence batch) from the committed summary, or None when the kernel sources no longer match the recorded
     digest."""
     try:
         with open(TRAFFIC_SUMMARY) as f:
@@ -603,6 +603,7 @@ def main():
             "decode_step_fused_us_avg": round(fused_ms * 1e3, 2),
             "decode_step_fused_hbm_frac": round(fused_bytes / (fused_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
             "decode_step_separate_us_avg": round(separate_ms * 1e3, 2),
+            "decode_step_fused_traffic_bytes": recorded_traffic("fused"),
             "traffic_bytes_per_call": recorded_traffic("prepare"),
             "prepare_then_prefill_ms_avg": round(prep_chain_ms, 4),
             "prepare_then_prefill_tokens_per_s": round(w.B * w.T / (prep_chain_ms * 1e-3), 1),
