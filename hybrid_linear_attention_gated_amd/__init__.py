@@ -39,7 +39,8 @@ LIB_PATH = os.path.join(PKG, "libgdn.so")
 GDN_F32, GDN_BF16 = 0, 1
 GDN_RULE_GATED_DELTA, GDN_RULE_GATED_DECAY = 0, 1
 STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_UNSUPPORTED",
-          4: "GDN_ERR_ALIGN", 5: "GDN_ERR_ALIAS", 6: "GDN_ERR_WORKSPACE", 7: "GDN_ERR_HIP"}
+          4: "GDN_ERR_ALIGN", 5: "GDN_ERR_ALIAS", 6: "GDN_ERR_WORKSPACE", 7: "GDN_ERR_HIP",
+          8: "GDN_ERR_CAPTURE"}
 EXPORTS = ("gdn_chunk_prefill", "gdn_chunk_prefill_rule", "gdn_chunk_prefill_workspace_size",
            "gdn_chunk_prefill_varlen", "gdn_chunk_prefill_varlen_workspace_size",
            "gdn_decode_step", "gdn_decode_step_rule", "gdn_decode_step_slots", "gdn_prepare",
@@ -223,6 +224,27 @@ def _check(t, name, dtype=None, shape=None):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
 
 
+def _stream_of(stream, dev):
+    """(raw stream handle, whether it was given by the caller)."""
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream(dev).cuda_stream, False
+    return stream, True
+
+
+def _keep_until_done(tensors, stream, given):
+    """Scratch allocated here is freed when the call returns; when the kernels run on a stream
+    the caller named (not torch's current stream), tell torch's caching allocator that the
+    memory is in use on that stream, so it is not handed out again before the kernels end."""
+    if not given:
+        return
+    import torch
+    ext = torch.cuda.ExternalStream(stream)
+    for t in tensors:
+        if t is not None:
+            t.record_stream(ext)
+
+
 def workspace_bytes(B, T, H, d_k, d_v, chunk, qkv_dtype) -> int:
     return int(gdn_chunk_prefill_workspace_size(B, T, H, d_k, d_v, chunk, qkv_dtype))
 
@@ -251,16 +273,17 @@ def chunk_prefill(q, k, v, g, beta, initial_state=None, chunk=64, *, out=None, f
     _check(out, "out", torch.float32, (B, T, H, d_v))
     _check(final_state, "final_state", torch.float32, (B, H, d_k, d_v))
     need = workspace_bytes(B, T, H, d_k, d_v, chunk, dt)
-    if workspace is None and need > 0:
+    own_ws = workspace is None and need > 0
+    if own_ws:
         workspace = torch.empty(need, device=dev, dtype=torch.uint8)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    if stream is None:
-        stream = torch.cuda.current_stream(dev).cuda_stream
+    stream, given = _stream_of(stream, dev)
     st = gdn_chunk_prefill_rule(rule, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                 _ptr(initial_state), _ptr(out), _ptr(final_state), B, T, H, d_k, d_v,
                                 chunk, dt, _ptr(workspace), ws_bytes, stream)
     if st != 0:
         raise GdnError(st, "gdn_chunk_prefill_rule")
+    _keep_until_done([workspace] if own_ws else [], stream, given)
     return out, final_state
 
 
@@ -416,16 +439,17 @@ def chunk_backward(q, k, v, g, beta, d_o, initial_state=None, d_final_state=None
     for t, n, shp in zip(outs, ("dq", "dk", "dv", "dg", "dbeta", "d_initial_state"), shapes):
         _check(t, n, torch.float32, shp)
     need = int(gdn_chunk_backward_workspace_size(B, T, H, d_k, d_v, dt))
-    if workspace is None and need > 0:
+    own_ws = workspace is None and need > 0
+    if own_ws:
         workspace = torch.empty(need, device=dev, dtype=torch.uint8)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    if stream is None:
-        stream = torch.cuda.current_stream(dev).cuda_stream
+    stream, given = _stream_of(stream, dev)
     st = gdn_chunk_backward(rule, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(d_o),
                             _ptr(d_final_state), *[_ptr(t) for t in outs], B, T, H, d_k, d_v, dt,
                             _ptr(workspace), ws_bytes, stream)
     if st != 0:
         raise GdnError(st, "gdn_chunk_backward")
+    _keep_until_done([workspace] if own_ws else [], stream, given)
     return outs
 
 
@@ -490,11 +514,11 @@ def prepare_varlen(xq, xk, xv, conv_weight, a_raw, b_raw, cu_seqlens, conv_pool,
                               ((T, H, d_k), (T, H, d_k), (T, H, d_v), (T, H), (T, H))):
         _check(t, n, dtp, shp)
     need = int(gdn_prepare_varlen_workspace_size(S))
-    if workspace is None and need > 0:
+    own_ws = workspace is None and need > 0
+    if own_ws:
         workspace = torch.empty(need, device=dev, dtype=torch.uint8)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    if stream is None:
-        stream = torch.cuda.current_stream(dev).cuda_stream
+    stream, given = _stream_of(stream, dev)
     pool_size = 0 if conv_pool is None else conv_pool.shape[0]
     st = gdn_prepare_varlen(_ptr(xq), _ptr(xk), _ptr(xv), _ptr(conv_weight), _ptr(a_raw), _ptr(b_raw),
                             _ptr(decay_rate), _ptr(gate_bias), _np_ptr(cu), S, T, _ptr(conv_pool), pool_size,
@@ -502,6 +526,7 @@ def prepare_varlen(xq, xk, xv, conv_weight, a_raw, b_raw, cu_seqlens, conv_pool,
                             ws_bytes, stream)
     if st != 0:
         raise GdnError(st, "gdn_prepare_varlen")
+    _keep_until_done([workspace] if own_ws else [], stream, given)
     return outs
 
 
@@ -529,17 +554,18 @@ def chunk_prefill_varlen(q, k, v, g, beta, cu_seqlens, state_pool, slots=None, h
         out = torch.empty((T, H, d_v), device=q.device, dtype=torch.float32)
     _check(out, "out", torch.float32, (T, H, d_v))
     need = int(gdn_chunk_prefill_varlen_workspace_size(_np_ptr(cu), S, H, d_k, d_v, chunk, dt))
-    if workspace is None and need > 0:
+    own_ws = workspace is None and need > 0
+    if own_ws:
         workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream
+    stream, given = _stream_of(stream, q.device)
     pool_size = 0 if state_pool is None else state_pool.shape[0]
     st = gdn_chunk_prefill_varlen(rule, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _np_ptr(cu), S, T,
                                   _ptr(state_pool), pool_size, _np_ptr(sl), _np_ptr(hi), _ptr(out), H, d_k, d_v,
                                   chunk, dt, _ptr(workspace), ws_bytes, stream)
     if st != 0:
         raise GdnError(st, "gdn_chunk_prefill_varlen")
+    _keep_until_done([workspace] if own_ws else [], stream, given)
     return out
 
 

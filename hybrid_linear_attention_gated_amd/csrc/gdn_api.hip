@@ -92,6 +92,9 @@ const char *gdn_status_string(gdn_status status) {
     case GDN_ERR_ALIAS: return "GDN_ERR_ALIAS: an output buffer overlaps another buffer";
     case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE: workspace missing or too small";
     case GDN_ERR_HIP: return "GDN_ERR_HIP: the HIP runtime failed to queue work";
+    case GDN_ERR_CAPTURE:
+        return "GDN_ERR_CAPTURE: the stream is capturing a graph; packed-sequence calls copy host data "
+               "and run eagerly only";
     }
     return "unknown gdn_status";
 }
@@ -195,6 +198,15 @@ gdn_status check_varlen_batch(const int32_t *cu, int S, int T_total, const int32
     return GDN_OK;
 }
 
+// The packed-sequence calls copy a host table into the workspace.  Recorded into a graph,
+// that copy would keep a pointer to the table, which dies when the call returns: refuse a
+// stream that is capturing, before anything is queued.
+gdn_status check_not_capturing(hipStream_t stream) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return GDN_ERR_HIP;
+    return cs == hipStreamCaptureStatusNone ? GDN_OK : GDN_ERR_CAPTURE;
+}
+
 bool varlen_supported(int d_k, int d_v, int chunk, gdn_dtype dt) {
     return dt == GDN_BF16 && prefill_bf16_uses_mfma(d_k, d_v, chunk);
 }
@@ -250,6 +262,8 @@ gdn_status gdn_chunk_prefill_varlen(gdn_rule rule, const void *q, const void *k,
     const Span all[] = {s_q, s_k, s_v, s_g, s_b, s_o, s_p};
     for (const Span &x : all)
         if (overlap(s_ws, x)) return GDN_ERR_ALIAS;
+    st = check_not_capturing(static_cast<hipStream_t>(stream));
+    if (st != GDN_OK) return st;
 
     const hipError_t err = launch_prefill_chunk_varlen(
         static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k), static_cast<const uint16_t *>(v), g,
@@ -516,6 +530,9 @@ gdn_status gdn_prepare_varlen(const void *xq, const void *xk, const void *xv, co
         for (const Span &x : in)
             if (overlap(out[i], x)) return GDN_ERR_ALIAS;
     }
+
+    st = check_not_capturing(static_cast<hipStream_t>(stream));
+    if (st != GDN_OK) return st;
 
     // the batch table (offsets, slots, start flags) into the workspace, then the kernels
     std::vector<int32_t> table(static_cast<size_t>(3) * S + 1);

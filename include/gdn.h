@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 6
+#define GDN_ABI_VERSION 7
 
 #if defined(__GNUC__) || defined(__clang__)
 #define GDN_API __attribute__((visibility("default")))
@@ -72,7 +72,9 @@ typedef enum gdn_status {
     GDN_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
     GDN_ERR_ALIAS = 5,       /* an output overlaps an input (other than the allowed in-place state) */
     GDN_ERR_WORKSPACE = 6,   /* workspace missing or smaller than gdn_chunk_prefill_workspace_size() */
-    GDN_ERR_HIP = 7          /* the HIP runtime reported an error while queuing work */
+    GDN_ERR_HIP = 7,         /* the HIP runtime reported an error while queuing work */
+    GDN_ERR_CAPTURE = 8      /* the stream is capturing a graph, and this call copies host
+                                data that must not outlive it (packed-sequence calls) */
 } gdn_status;
 
 typedef enum gdn_dtype {
@@ -226,11 +228,16 @@ GDN_API gdn_status gdn_decode_step_slots(gdn_rule rule,
  *   o              [T_total, H, d_v] fp32, written
  *   workspace      at least gdn_chunk_prefill_varlen_workspace_size(...) bytes
  * Supported: qkv_dtype GDN_BF16, d_k and d_v in {64, 128}, chunk in {32, 64};
- * both rules.  The host arrays are read during the call only.
+ * both rules.  The host arrays are read during the call only: the call turns
+ * them into a table that one host-to-device copy on `stream` puts into the
+ * workspace.  A graph recorded from that copy would keep a pointer to host
+ * memory that is gone once the call returns, so the call refuses a stream that
+ * is capturing (GDN_ERR_CAPTURE, before anything is queued); capture the
+ * dense calls instead, or run this one eagerly between graph launches.
  * Errors: GDN_ERR_UNSUPPORTED (rule, dtype or sizes), GDN_ERR_SHAPE (bad
  * offsets, slots out of range, pool_size < S without slots), GDN_ERR_NULL,
  * GDN_ERR_ALIGN, GDN_ERR_ALIAS (repeated slot, overlapping buffers),
- * GDN_ERR_WORKSPACE, GDN_ERR_HIP.
+ * GDN_ERR_WORKSPACE, GDN_ERR_CAPTURE, GDN_ERR_HIP.
  */
 GDN_API gdn_status gdn_chunk_prefill_varlen(gdn_rule rule,
                              const void *q, const void *k, const void *v,
@@ -361,9 +368,12 @@ GDN_API gdn_status gdn_prepare_decode_step(gdn_rule rule,
  *   q, k, v, g, beta   written, packed like the inputs
  *   workspace      device scratch of gdn_prepare_varlen_workspace_size(S) bytes
  * Other arguments and the computation as gdn_prepare.  The host arrays are
- * read during the call only.
+ * read during the call only, through one host-to-device copy into the
+ * workspace; as for gdn_chunk_prefill_varlen, a stream that is capturing a
+ * graph is refused with GDN_ERR_CAPTURE before anything is queued (a decode
+ * loop that is captured uses gdn_prepare or gdn_prepare_decode_step).
  * Errors: as gdn_prepare, plus GDN_ERR_SHAPE (bad offsets or slots),
- * GDN_ERR_ALIAS (a repeated slot), GDN_ERR_WORKSPACE.
+ * GDN_ERR_ALIAS (a repeated slot), GDN_ERR_WORKSPACE, GDN_ERR_CAPTURE.
  */
 GDN_API gdn_status gdn_prepare_varlen(const void *xq, const void *xk, const void *xv,
                                const float *conv_weight,

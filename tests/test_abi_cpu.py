@@ -26,11 +26,11 @@ def test_library_exports_every_declared_symbol():
     L = gdn.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert gdn.gdn_version() == 6
+    assert gdn.gdn_version() == 7
 
 
 def test_status_strings():
-    for code in range(8):
+    for code in range(9):
         assert gdn.gdn_status_string(code).startswith(gdn.STATUS[code])
     assert "rule" in gdn.gdn_status_string(3)
     assert gdn.gdn_status_string(99) == "unknown gdn_status"

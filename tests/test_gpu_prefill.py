@@ -251,7 +251,8 @@ def test_prefill_error_has_no_side_effect():
 
 # --- full-size workloads, as the benchmark runs them ---------------------------------------
 
-ROWS = [0, 13, 37, 63]
+# one value row in every 16-column slice of the state (each slice is a wavefront's share)
+ROWS = [0, 21, 38, 63]
 
 
 def test_workload_1b_8k(orc):
@@ -275,7 +276,7 @@ def test_workload_3b_2m_chain(orc):
     """H=24, d=128: 32 chained calls of T=65536 through the carried state (2M tokens),
     compared after every call on sampled value rows against an oracle chaining its own state."""
     w = gi.WORKLOADS["3b_2m"]
-    rows = [3, 77]
+    rows = [3, 17, 34, 50, 77, 85, 102, 127]  # one per 16-column slice (eight wavefronts)
     state = torch.zeros(1, w.H, w.dk, w.dv, device=DEV)
     ws = torch.empty(gdn.workspace_bytes(1, w.T, w.H, w.dk, w.dv, 64, gdn.GDN_BF16), dtype=torch.uint8,
                      device=DEV)
@@ -293,3 +294,14 @@ def test_workload_3b_2m_chain(orc):
                            f"3b_2m call {call} state")
         worst = max(worst, e1, e2)
     print(f"[parity] 3b_2m worst over 32 calls: {worst:.3e}", flush=True)
+
+
+def test_ragged_64k_plus_one(orc):
+    """T = 65537 (a partial last chunk of one token) with a start state, as one call at the
+    64K layer shape (B=1, H=32, d=64): every 16-column slice sampled."""
+    d = inputs(1, 65537, 32, 64, 64, torch.bfloat16, s0=True, wid=57)
+    print("[case] ragged B=1 H=32 T=65537", flush=True)
+    o, sf = run_gpu(d, 64)
+    ro, rs = run_oracle(orc, d, rows=ROWS)
+    assert_parity(o[..., ROWS], ro[..., ROWS], TOL["bf16"], f"T=65537 outputs (rows {ROWS})")
+    assert_parity(sf[..., ROWS], rs[..., ROWS], TOL["bf16"], f"T=65537 state (rows {ROWS})")
