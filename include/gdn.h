@@ -64,7 +64,16 @@ extern "C" {
 #define GDN_API
 #endif
 
-typedef enum gdn_status {
+/* In C++ the enums below get int as their underlying type, so every int a C
+ * caller passes is a value of the type (unknown codes are then rejected, not
+ * undefined). */
+#ifdef __cplusplus
+#define GDN_ENUM_INT : int
+#else
+#define GDN_ENUM_INT
+#endif
+
+typedef enum gdn_status GDN_ENUM_INT {
     GDN_OK = 0,
     GDN_ERR_NULL = 1,        /* a required pointer is NULL */
     GDN_ERR_SHAPE = 2,       /* a size is negative / zero where not allowed, or too large */
@@ -77,12 +86,12 @@ typedef enum gdn_status {
                                 data that must not outlive it (packed-sequence calls) */
 } gdn_status;
 
-typedef enum gdn_dtype {
+typedef enum gdn_dtype GDN_ENUM_INT {
     GDN_F32 = 0,  /* IEEE binary32 */
     GDN_BF16 = 1  /* bfloat16 (upper half of a binary32) */
 } gdn_dtype;
 
-typedef enum gdn_rule {
+typedef enum gdn_rule GDN_ENUM_INT {
     GDN_RULE_GATED_DELTA = 0, /* S_t = a_t S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T */
     GDN_RULE_GATED_DECAY = 1  /* S_t = a_t S_{t-1} + b_t v_t k_t^T (no erase term) */
 } gdn_rule;

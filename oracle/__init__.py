@@ -219,11 +219,16 @@ _default = None
 
 
 def default() -> Oracle:
+    """The oracle library the tests use: the default build, or the one GDN_ORACLE_LIB names (a
+    sanitizer build of the same source, loaded by the sanitizer test)."""
     global _default
     if _default is None:
-        if not os.path.exists(LIB):
-            build()
-        _default = Oracle(LIB)
+        path = os.environ.get("GDN_ORACLE_LIB", "")
+        if not path:
+            path = LIB
+            if not os.path.exists(LIB):
+                build()
+        _default = Oracle(path)
     return _default
 
 
