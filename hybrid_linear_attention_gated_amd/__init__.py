@@ -6,7 +6,7 @@ kernels of ``libgdn.so``.  PyTorch supplies device memory and the stream.
 Raw C-ABI entry points (same names and arguments as ``include/gdn.h``, with
 pointers passed as integers):
 
-    gdn_chunk_prefill, gdn_chunk_prefill_rule, gdn_chunk_prefill_workspace_size,
+    gdn_chunk_prefill, gdn_chunk_prefill_rule, gdn_chunk_prefill_workspace_size, gdn_chunk_prefill_noalloc,
     gdn_chunk_prefill_varlen, gdn_chunk_prefill_varlen_workspace_size, gdn_decode_step,
     gdn_decode_step_rule, gdn_decode_step_slots, gdn_prepare, gdn_prepare_decode_step,
     gdn_chunk_backward, gdn_chunk_backward_workspace_size, gdn_status_string, gdn_version
@@ -42,6 +42,7 @@ STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_UNSUPP
           4: "GDN_ERR_ALIGN", 5: "GDN_ERR_ALIAS", 6: "GDN_ERR_WORKSPACE", 7: "GDN_ERR_HIP",
           8: "GDN_ERR_CAPTURE"}
 EXPORTS = ("gdn_chunk_prefill", "gdn_chunk_prefill_rule", "gdn_chunk_prefill_workspace_size",
+           "gdn_chunk_prefill_noalloc",
            "gdn_chunk_prefill_varlen", "gdn_chunk_prefill_varlen_workspace_size",
            "gdn_decode_step", "gdn_decode_step_rule", "gdn_decode_step_slots", "gdn_prepare",
            "gdn_chunk_backward", "gdn_chunk_backward_workspace_size", "gdn_prepare_varlen",
@@ -71,6 +72,9 @@ def lib():
         L.gdn_chunk_prefill.restype = i32
         L.gdn_chunk_prefill_rule.argtypes = [i32] + L.gdn_chunk_prefill.argtypes
         L.gdn_chunk_prefill_rule.restype = i32
+        L.gdn_chunk_prefill_noalloc.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                                i32, i32, vp]
+        L.gdn_chunk_prefill_noalloc.restype = i32
         L.gdn_chunk_prefill_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
         L.gdn_chunk_prefill_workspace_size.restype = sz
         L.gdn_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
@@ -117,6 +121,12 @@ def gdn_chunk_prefill_rule(rule, q, k, v, g, beta, initial_state, o, final_state
                            chunk, qkv_dtype, workspace, workspace_bytes, stream) -> int:
     return lib().gdn_chunk_prefill_rule(rule, q, k, v, g, beta, initial_state, o, final_state, B, T, H,
                                         d_k, d_v, chunk, qkv_dtype, workspace, workspace_bytes, stream)
+
+
+def gdn_chunk_prefill_noalloc(rule, q, k, v, g, beta, initial_state, o, final_state, B, T, H, d_k, d_v, chunk,
+                              qkv_dtype, stream) -> int:
+    return lib().gdn_chunk_prefill_noalloc(rule, q, k, v, g, beta, initial_state, o, final_state, B, T, H, d_k,
+                                           d_v, chunk, qkv_dtype, stream)
 
 
 def gdn_chunk_prefill_workspace_size(B, T, H, d_k, d_v, chunk, qkv_dtype) -> int:
@@ -571,6 +581,7 @@ def chunk_prefill_varlen(q, k, v, g, beta, cu_seqlens, state_pool, slots=None, h
 
 __all__ = ["EXPORTS", "GDN_F32", "GDN_BF16", "GDN_RULE_GATED_DELTA", "GDN_RULE_GATED_DECAY", "GdnError",
            "lib", "gdn_chunk_prefill", "gdn_chunk_prefill_rule", "gdn_chunk_prefill_workspace_size",
+           "gdn_chunk_prefill_noalloc",
            "gdn_decode_step", "gdn_decode_step_rule", "gdn_status_string", "gdn_version",
            "gdn_decode_step_slots", "gdn_chunk_prefill_varlen", "gdn_chunk_prefill_varlen_workspace_size",
            "chunk_prefill", "chunk_prefill_varlen", "decode_step", "decode_step_slots", "workspace_bytes",

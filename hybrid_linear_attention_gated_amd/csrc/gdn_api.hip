@@ -6,6 +6,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "gdn_internal.h"
@@ -75,6 +76,34 @@ hipError_t launch_prepare_decode(const void *xq, const void *xk, const void *xv,
 }  // namespace gdn
 
 using namespace gdn;
+
+// Scratch of gdn_chunk_prefill_noalloc: the piece maps and start states the prefill otherwise
+// keeps in the caller's workspace, in one array per GPU that the library holds until the
+// process ends.  In host code `scratch` names a host-side stand-in, not device memory: host code
+// only ever passes the address hipGetSymbolAddress gives for the current device.
+static __device__ __align__(256) unsigned char scratch[GDN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_dev[kMaxScratchDevices];  // device address of `scratch`, per device id
+
+// The current device's copy of `scratch`, looked up once per device (with that device current).
+gdn_status scratch_of_current_device(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return GDN_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return GDN_ERR_HIP;
+        g_scratch_dev[dev] = ptr;
+    }
+    *out = g_scratch_dev[dev];
+    return GDN_OK;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -162,6 +191,27 @@ gdn_status gdn_chunk_prefill_rule(gdn_rule rule, const void *q, const void *k, c
         err = launch_prefill_valu(q, k, v, g, beta, initial_state, o, final_state, B, T, H, d_k,
                                   d_v, chunk, GDN_F32, delta, hs);
     return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+gdn_status gdn_chunk_prefill_noalloc(gdn_rule rule, const void *q, const void *k, const void *v,
+                                     const float *g, const float *beta, const float *initial_state,
+                                     float *o, float *final_state, int B, int T, int H, int d_k,
+                                     int d_v, int chunk, gdn_dtype qkv_dtype, void *stream) {
+    // the checks of gdn_chunk_prefill_rule that do not involve the workspace come first, so a
+    // bad call reports what the allocating call would report
+    if (rule != GDN_RULE_GATED_DELTA && rule != GDN_RULE_GATED_DECAY) return GDN_ERR_UNSUPPORTED;
+    const gdn_status st = check_prefill_shape(B, T, H, d_k, d_v, chunk, qkv_dtype);
+    if (st != GDN_OK) return st;
+    const size_t need = gdn_chunk_prefill_workspace_size(B, T, H, d_k, d_v, chunk, qkv_dtype);
+    if (need > GDN_NOALLOC_SCRATCH_BYTES) return GDN_ERR_WORKSPACE;
+    void *ws = nullptr;
+    if (need > 0) {
+        const gdn_status s2 = scratch_of_current_device(&ws);
+        if (s2 != GDN_OK) return s2;
+    }
+    return gdn_chunk_prefill_rule(rule, q, k, v, g, beta, initial_state, o, final_state, B, T, H, d_k,
+                                  d_v, chunk, qkv_dtype, ws, need > 0 ? GDN_NOALLOC_SCRATCH_BYTES : 0,
+                                  stream);
 }
 
 gdn_status gdn_chunk_prefill(const void *q, const void *k, const void *v, const float *g,

@@ -159,6 +159,34 @@ GDN_API size_t gdn_chunk_prefill_workspace_size(int B, int T, int H, int d_k, in
                                         gdn_dtype qkv_dtype);
 
 /*
+ * gdn_chunk_prefill_noalloc -- gdn_chunk_prefill_rule that allocates nothing
+ * and takes no workspace, for callers that cannot allocate device memory:
+ * code under HIP graph capture, serving loops that must not call hipMalloc,
+ * harnesses that forbid allocation.  The scratch the call needs comes from
+ * one static device array of GDN_NOALLOC_SCRATCH_BYTES per GPU, which the
+ * library holds from the first call on that GPU until the process ends.
+ *
+ * Arguments, layouts, results and errors are those of gdn_chunk_prefill_rule
+ * without the workspace; GDN_ERR_WORKSPACE means that
+ * gdn_chunk_prefill_workspace_size(...) exceeds GDN_NOALLOC_SCRATCH_BYTES
+ * (no dense call does today: the piece plan bounds that size by the chip's
+ * workgroup slots, not by T; the largest, 128-wide heads, need about 50 MiB).
+ * Every call on one GPU uses that GPU's single array: calls that may overlap
+ * in time on one GPU (different streams, or threads) race on it and must be
+ * ordered by the caller.  Nothing in the array needs clearing between calls
+ * (each call writes every scratch byte it reads).
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+GDN_API gdn_status gdn_chunk_prefill_noalloc(gdn_rule rule,
+                             const void *q, const void *k, const void *v,
+                             const float *g, const float *beta,
+                             const float *initial_state,
+                             float *o, float *final_state,
+                             int B, int T, int H, int d_k, int d_v, int chunk,
+                             gdn_dtype qkv_dtype, void *stream);
+
+/*
  * gdn_decode_step -- one token for each of N independent sequences: the rule
  * with T = 1, applied to a batch of per-sequence states in place.
  *

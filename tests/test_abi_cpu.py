@@ -308,3 +308,16 @@ def test_prepare_decode_rejects(kw, code):
 
 def test_prepare_decode_no_sequences_is_a_no_op():
     assert prepare_decode_call(N=0, xq=None, xk=None, xv=None, conv=None, state=None, o=None) == OK
+
+
+def test_noalloc_validates_like_the_workspace_call():
+    """gdn_chunk_prefill_noalloc rejects what gdn_chunk_prefill_rule rejects, before it looks up its
+    scratch on the device (so these run without a GPU)."""
+    def call(rule=0, dk=64, B=1, T=1000, q=addr(0), o=addr(5), dt=BF16):
+        return gdn.gdn_chunk_prefill_noalloc(rule, q, addr(1), addr(2), addr(3), addr(4), None, o, addr(6), B, T, 2,
+                                             dk, 64, 64, dt, None)
+    assert call(rule=9) == UNSUP
+    assert call(dk=32) == UNSUP
+    assert call(dt=5) == UNSUP
+    assert call(B=0) == SHAPE
+    assert call(T=-1) == SHAPE
