@@ -267,9 +267,14 @@ size_t gdn_chunk_prefill_varlen_workspace_size(const int32_t *cu_seqlens, int S,
                                                int chunk, gdn_dtype qkv_dtype) {
     if (S <= 0 || H <= 0 || !cu_seqlens || !varlen_supported(d_k, d_v, chunk, qkv_dtype)) return 0;
     if (check_varlen_batch(cu_seqlens, S, cu_seqlens[S], nullptr, S) != GDN_OK) return 0;
-    VarlenLayout L;
-    if (!varlen_layout(cu_seqlens, S, H, d_k, d_v, chunk, &L)) return 0;
-    return L.bytes;
+    // either rule (the size query takes no rule): the larger of the two plans
+    size_t bytes = 0;
+    for (bool delta : {true, false}) {
+        VarlenLayout L;
+        if (!varlen_layout(cu_seqlens, S, H, d_k, d_v, prefill_kernel_chunk(d_k, d_v, chunk, delta), &L)) return 0;
+        bytes = L.bytes > bytes ? L.bytes : bytes;
+    }
+    return bytes;
 }
 
 gdn_status gdn_chunk_prefill_varlen(gdn_rule rule, const void *q, const void *k, const void *v,
@@ -305,8 +310,9 @@ gdn_status gdn_chunk_prefill_varlen(gdn_rule rule, const void *q, const void *k,
         if (overlap(s_o, in) || overlap(s_p, in)) return GDN_ERR_ALIAS;
     if (overlap(s_o, s_p)) return GDN_ERR_ALIAS;
 
+    const int kchunk = prefill_kernel_chunk(d_k, d_v, chunk, rule == GDN_RULE_GATED_DELTA);
     VarlenLayout L;
-    if (!varlen_layout(cu_seqlens, S, H, d_k, d_v, chunk, &L)) return GDN_ERR_SHAPE;
+    if (!varlen_layout(cu_seqlens, S, H, d_k, d_v, kchunk, &L)) return GDN_ERR_SHAPE;
     if (!workspace || workspace_bytes < L.bytes) return GDN_ERR_WORKSPACE;
     const Span s_ws = span(workspace, L.bytes);
     const Span all[] = {s_q, s_k, s_v, s_g, s_b, s_o, s_p};
@@ -317,7 +323,7 @@ gdn_status gdn_chunk_prefill_varlen(gdn_rule rule, const void *q, const void *k,
 
     const hipError_t err = launch_prefill_chunk_varlen(
         static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k), static_cast<const uint16_t *>(v), g,
-        beta, cu_seqlens, S, slots, has_initial, state_pool, o, H, d_k, d_v, chunk,
+        beta, cu_seqlens, S, slots, has_initial, state_pool, o, H, d_k, d_v, kchunk,
         rule == GDN_RULE_GATED_DELTA, workspace, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }

@@ -54,6 +54,7 @@ hipError_t launch_prefill_valu(const void *q, const void *k, const void *v, cons
 
 // bf16 inputs: chunked prefill with bf16 MFMA contractions.
 bool prefill_bf16_uses_mfma(int dk, int dv, int chunk);
+int prefill_kernel_chunk(int dk, int dv, int chunk, bool delta);
 hipError_t launch_prefill_bf16(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                const float *g, const float *beta, const float *s0, float *o,
                                float *s_out, int B, int T, int H, int dk, int dv, int chunk,

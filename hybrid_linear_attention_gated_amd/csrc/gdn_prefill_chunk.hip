@@ -267,13 +267,17 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<DK, DV, C, MAP> &r, const C
     }
 }
 
-// Two workgroups per compute unit where LDS allows it (64-wide heads), so one
-// workgroup's barrier waits are filled by the other's work.
-template <int DK, int DV>
-constexpr int kBlocksPerCU = (DK == 64 && DV == 64) ? 2 : 1;
+// Several workgroups per compute unit where registers and LDS allow it (64-wide heads), so
+// one workgroup's dependent latencies and barrier waits are filled by the others' work: two
+// with chunk 64 (73 KB of LDS each), three with chunk 32 (29 KB; at most 168 registers per
+// lane, the occupancy bound of three wavefronts per SIMD).  64K prefill, 64-wide heads: chunk
+// 32 with three workgroups per compute unit 0.72 ms, with two 0.81 ms; chunk 64 with two 0.81 ms.
+template <int DK, int DV, int C>
+constexpr int kBlocksPerCU = (DK == 64 && DV == 64) ? (C == 32 ? 3 : 2) : 1;
 // workgroups the chip holds at once (256 compute units), the target of the piece plan
-template <int DK, int DV>
-constexpr int kPlanSlots = 256 * kBlocksPerCU<DK, DV>;
+template <int DK, int DV, int C>
+constexpr int kPlanSlots = 256 * kBlocksPerCU<DK, DV, C>;
+int plan_slots(int dk, int dv, int chunk) { return 256 * ((dk == 64 && dv == 64) ? (chunk == 32 ? 3 : 2) : 1); }
 
 // DELTA selects the rule: the gated delta rule (true) or the same recurrence without the
 // erase term (false), S_t = a_t S_{t-1} + b_t v_t k_t^T, whose chunk form has A = 0 and T = I:
@@ -281,7 +285,7 @@ constexpr int kPlanSlots = 256 * kBlocksPerCU<DK, DV>;
 // STATES (OUT only): write the state every chunk starts from (for the gradients) instead of the
 // outputs, which the gradients do not use.
 template <int DK, int DV, int C, bool MAP, bool DELTA, bool STATES = false>
-__global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV>)) void chunk_kernel(ChunkArgs a) {
+__global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C>)) void chunk_kernel(ChunkArgs a) {
     using G = Cfg<DK, DV, C, MAP>;
     using R = ChunkRegs<DK, DV, C, MAP>;
     constexpr bool kPerm = G::WAVES == 4;  // permuted bf16 rows (see perm_col)
@@ -516,34 +520,50 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV>))
                 }
             }
         };
-        // Diagonal block w of T = (I + A)^{-1} by forward substitution, t_r = delta_rj -
-        // sum_{m<r} A[r][m] t_m down column j.  Lane (j, q) = (lane / 4, lane % 4) sums the terms
-        // m in [4q, 4q + 4); two quad-lane adds complete each row.  A is strictly lower and t_m
-        // is zero until its row is reached, so nothing needs masking.  Reads only this
-        // wavefront's own A tile (LDS keeps a wavefront's accesses in order).
+        // Diagonal block w of T = (I + A)^{-1} by forward substitution down each column j,
+        // t_r = delta_rj - sum_{m<r} A[r][m] t_m, four rows at a time.  Lane (j, q) = (lane / 4,
+        // lane % 4) keeps t_m for m in [4q, 4q + 4).  For the rows of group g (4g .. 4g + 3) the
+        // sums over the earlier groups are independent of each other: each lane adds its four
+        // terms and two quad-lane adds complete them, four rows side by side.  The 4 x 4
+        // triangle inside the group is then solved on the lane that holds those columns of A
+        // (q = g), which also keeps the results.  Per group the chain is one reduction and
+        // three dependent fused multiply-adds, instead of one reduction per row.  A is strictly
+        // lower and t_m is zero until its group is reached, so nothing needs masking.  Reads
+        // only this wavefront's own A tile (LDS keeps a wavefront's accesses in order).
         auto inv_diag = [&]() {
             const int bb = 16 * wave, j = lane >> 2, q = lane & 3;
-            f32x4 arow[16];
-#pragma unroll
-            for (int r = 1; r < 16; ++r) arow[r] = *reinterpret_cast<const f32x4 *>(&as[bb + r][bb + 4 * q]);
             float tq[4] = {0.f, 0.f, 0.f, 0.f};  // t_m for m = 4q + i
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float t;
-                if (r == 0) {
-                    t = (j == 0) ? 1.f : 0.f;
-                } else {
-                    const int k = (r - 1) & 3;  // slot of the newest t (added last)
-                    float p = 0.f;
+            for (int g = 0; g < 4; ++g) {
+                f32x4 arow[4];  // this lane's four columns of the group's rows (loaded when reached)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (i != k) p = fmaf(arow[r][i], tq[i], p);
-                    p = fmaf(arow[r][k], tq[k], p);
-                    p += quad_xor1(p);
-                    p += quad_xor2(p);
-                    t = (r == j) ? 1.f : -p;
+                for (int a = 0; a < 4; ++a)
+                    arow[a] = *reinterpret_cast<const f32x4 *>(&as[bb + 4 * g + a][bb + 4 * q]);
+                float p[4] = {0.f, 0.f, 0.f, 0.f};
+                if (g > 0) {
+#pragma unroll
+                    for (int a = 0; a < 4; ++a) {
+                        float x = arow[a][0] * tq[0];
+#pragma unroll
+                        for (int i = 1; i < 4; ++i) x = fmaf(arow[a][i], tq[i], x);
+                        p[a] = x;
+                    }
+#pragma unroll
+                    for (int a = 0; a < 4; ++a) p[a] += quad_xor1(p[a]);
+#pragma unroll
+                    for (int a = 0; a < 4; ++a) p[a] += quad_xor2(p[a]);
                 }
-                tq[r & 3] = (q == (r >> 2)) ? t : tq[r & 3];
+                float t[4];
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    const int r = 4 * g + a;
+                    float v = ((r == j) ? 1.f : 0.f) - p[a];
+#pragma unroll
+                    for (int b = 0; b < a; ++b) v = fmaf(-arow[a][b], t[b], v);
+                    t[a] = v;
+                }
+#pragma unroll
+                for (int a = 0; a < 4; ++a) tq[a] = (q == g) ? t[a] : tq[a];
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) ts[bb + 4 * q + i][bb + j] = tq[i];
@@ -1280,7 +1300,7 @@ template <int DK, int DV, int C>
 size_t chunk_ws_bytes(int B, int T, int H) {
     const int N = (T + C - 1) / C;
     const int BH = B * H;
-    const int P = piece_plan(BH, N, kPlanSlots<DK, DV>).P;
+    const int P = piece_plan(BH, N, kPlanSlots<DK, DV, C>).P;
     if (P == 1) return 0;
     const size_t maps = static_cast<size_t>(BH) * (P - 1) * DK * (DV + DK) * 4;
     const size_t starts = static_cast<size_t>(BH) * P * DK * DV * 4;
@@ -1293,7 +1313,7 @@ hipError_t run_chunk(const uint16_t *q, const uint16_t *k, const uint16_t *v, co
                      void *ws, hipStream_t stream, float *chunk_states = nullptr) {
     const int N = (T + C - 1) / C;
     const int BH = B * H;
-    const PiecePlan plan = piece_plan(BH, N, kPlanSlots<DK, DV>);
+    const PiecePlan plan = piece_plan(BH, N, kPlanSlots<DK, DV, C>);
     const int P = plan.P;
     ChunkArgs a{};
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.o = o; a.s_final = s_out;
@@ -1381,11 +1401,12 @@ hipError_t run_chunk_varlen(const uint16_t *q, const uint16_t *k, const uint16_t
 }  // namespace
 
 // Plan for packed sequences: pieces of pc chunks (at least 8, and enough to give about
-// two workgroups per compute unit over all heads), the host table and the workspace layout.
+// one round of workgroups over all heads), the host table and the workspace layout.
 bool varlen_layout(const int *cu, int S, int H, int dk, int dv, int chunk, VarlenLayout *L) {
     long long chunk_heads = 0;
     for (int s = 0; s < S; ++s) chunk_heads += static_cast<long long>((cu[s + 1] - cu[s] + chunk - 1) / chunk) * H;
-    long long pc = (chunk_heads + 511) / 512;
+    const long long slots = plan_slots(dk, dv, chunk);
+    long long pc = (chunk_heads + slots - 1) / slots;
     if (pc < 8) pc = 8;
     long long NP = 0, NM = 0;
     for (int s = 0; s < S; ++s) {

@@ -99,8 +99,13 @@ typedef enum gdn_rule GDN_ENUM_INT {
 /*
  * gdn_chunk_prefill -- run the rule over T tokens of B sequences at once.
  *
- * The sequence is processed in chunks of `chunk` tokens (the last chunk may be
- * partial).  Inside a chunk the per-token updates are folded into dense
+ * The sequence is processed in chunks of at most `chunk` tokens (the last chunk
+ * may be partial): `chunk` is the longest chunk the kernels may use, and they
+ * pick their chunk length within it (bf16 inputs with 64- or 128-wide heads
+ * run the gated delta rule in 32-token chunks when 64 is allowed, which is
+ * faster on gfx950; the rule without the erase term keeps 64).  Any chunk
+ * length gives the same recurrence up to rounding.  Inside a chunk the
+ * per-token updates are folded into dense
  * products: a cumulative log-gate, the lower-triangular system
  * (I + tril(diag(b) K K^T * decay)) solved by forward substitution, the
  * W/U products, a scan of the fp32 state from chunk to chunk, and outputs as
