@@ -45,6 +45,9 @@ BF16_PEAK_TFLOPS = 2500.0
 #   forward substitution)
 BYTES_PER_TOKEN_HEAD = 648
 FLOPS_PER_TOKEN_HEAD = 64 * (6 * 64 + 4 * 64) + 6 * 64 * 64 + 64 * 64 // 3
+# the most useful MFMA work per second the HBM floor allows, as a fraction of the bf16 peak:
+# (FLOPs / bytes) x 8 TB/s / 2.5 PFLOP/s = 103.2 x 8e12 / 2.5e15 = 0.330
+CEILING_MFMA_FRAC = FLOPS_PER_TOKEN_HEAD / BYTES_PER_TOKEN_HEAD * HBM_PEAK_GBPS * 1e9 / (BF16_PEAK_TFLOPS * 1e12)
 # the same at d_k = d_v = 128 (one 64K call of the 3B-shaped chain): 3 * 128 * 2 + 8 + 128 * 4 bytes,
 # C (6 d_k + 4 d_v) + 6 d_k d_v + C^2 / 3 FLOPs
 BYTES_PER_TOKEN_HEAD_128 = 3 * 128 * 2 + 8 + 128 * 4
@@ -492,6 +495,36 @@ def main():
     d128_bytes = dw.B * 24 * (2 * 4 * 128 * 128 + 3 * 128 * 2 + 8 + 128 * 4)
     del s128, in128, o128
 
+    # decode over eight distinct states in rotation, one per GDN layer of an 8-GDN-layer hybrid: each
+    # step updates layer 0's 128 MiB state, then layer 1's, ... (8 x 128 MiB = 1 GiB, four times the
+    # 256 MB last-level cache), so every state read and every write-back of the previous layers'
+    # dirty lines falls on DRAM inside the timed window; eager launches back to back, and the same
+    # 8 x 16 launches replayed from one HIP graph
+    n_layers = 8
+    layer_states = [state0.clone() for _ in range(n_layers)]
+    rot_launch = lambda: [gdn.decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], st, out=dout)
+                          for d in steps_in for st in layer_states]
+    rot_launch()
+    rot_ev = [(mk(), mk()) for _ in range(max(2, args.steps // 4))]
+    for a, b in rot_ev:
+        a.record(stream)
+        rot_launch()
+        b.record(stream)
+    rot_graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(rot_graph):
+        rot_launch()
+    rot_graph.replay()
+    rotg_ev = [(mk(), mk()) for _ in range(max(2, args.steps // 4))]
+    for a, b in rotg_ev:
+        a.record(stream)
+        rot_graph.replay()
+        b.record(stream)
+    torch.cuda.synchronize()
+    n_rot = n_layers * len(steps_in)
+    rot_us = sorted(a.elapsed_time(b) * 1e3 / n_rot for a, b in rot_ev)
+    rotg_us = sorted(a.elapsed_time(b) * 1e3 / n_rot for a, b in rotg_ev)
+    del layer_states, rot_graph
+
     # decode with a cold last-level cache: read a 1 GiB buffer before each step, outside the
     # events (a read leaves only clean lines behind, so no write-back competes with the step)
     flush = torch.ones(FLUSH_BYTES // 4, device=dev, dtype=torch.float32)
@@ -563,7 +596,12 @@ def main():
             "ms_avg": round(pre_avg, 4), "ms_median": round(med(pre_ms), 4), "ms_min": round(pre_ms[0], 4),
             "GBps_algorithmic": round(pre_gbps, 1), "hbm_frac": round(pre_gbps / HBM_PEAK_GBPS, 4),
             "useful_TFLOPs": round(pre_tflops, 2), "mfma_frac": round(pre_tflops / BF16_PEAK_TFLOPS, 4),
+            "ceiling_mfma_frac": round(CEILING_MFMA_FRAC, 4),
+            "frac_of_ceiling": round(pre_tflops / BF16_PEAK_TFLOPS / CEILING_MFMA_FRAC, 4),
             "bytes_per_call": pre_bytes, "useful_flops_per_call": pre_flops,
+            "note": "ceiling_mfma_frac: the useful-MFMA fraction the HBM floor allows (algorithmic bytes at 8 TB/s), "
+                    "frac_of_ceiling: mfma_frac over it (= hbm_frac); the kernels run the chunk form in 32-token "
+                    "chunks (chunk=64 is the longest the call allows)",
         },
         "decode": {
             "us_per_step_avg": round(dec_avg * 1e3, 2), "us_per_step_median": round(med(dec_ms) * 1e3, 2),
@@ -579,6 +617,16 @@ def main():
                     "launch gaps included), the 128 MiB state can stay in the 256 MB last-level cache; cold: a "
                     "1 GiB buffer is read before every step; graph: the 16 steps replayed from one HIP graph, "
                     "time / 16",
+        },
+        "decode_8_layers": {
+            "workload": "the 256 x 32 x 64 decode step over 8 distinct 128 MiB states in rotation (one per GDN "
+                        "layer; 1 GiB of states, 4x the last-level cache), 16 steps x 8 layers",
+            "us_per_layer_step_avg": round(sum(rot_us) / len(rot_us), 2),
+            "GBps": round(dec_bytes / (sum(rot_us) / len(rot_us) * 1e-6) / 1e9, 1),
+            "hbm_frac": round(dec_bytes / (sum(rot_us) / len(rot_us) * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "graph_us_per_layer_step_avg": round(sum(rotg_us) / len(rotg_us), 2),
+            "graph_GBps": round(dec_bytes / (sum(rotg_us) / len(rotg_us) * 1e-6) / 1e9, 1),
+            "graph_hbm_frac": round(dec_bytes / (sum(rotg_us) / len(rotg_us) * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
         },
         "decode_3b_shape": {
             "workload": "256 sequences, H=24, d_k=d_v=128 fp32 states (402 MB), 16 steps launched back to back",

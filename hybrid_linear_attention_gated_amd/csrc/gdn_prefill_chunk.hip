@@ -317,6 +317,9 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
     // wavefronts 4-7, so 0-3 compute only their diagonal tile and its inverse in B, and the
     // blocks of T in C.
     constexpr bool kSplitKey = kSplitF;
+    // Chunk 32 with four wavefronts: the whole inversion (both diagonal blocks and T10) on
+    // wavefront 0 in B, and no phase C (four barriers per chunk instead of five).
+    constexpr bool kMergeBC = DELTA && C == 32 && G::WAVES == 4;
     __shared__ __align__(16) bf16x8 tbf_s[kSplitF ? G::CT * G::CS * 2 * kWave : 1];
     __shared__ float g_s[C], b_s[C], bg_s[C], dec_s[C], gam_s[C];  // g_s: G * log2(e)
 
@@ -530,15 +533,23 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
         // three dependent fused multiply-adds, instead of one reduction per row.  A is strictly
         // lower and t_m is zero until its group is reached, so nothing needs masking.  Reads
         // only this wavefront's own A tile (LDS keeps a wavefront's accesses in order).
-        auto inv_diag = [&]() {
-            const int bb = 16 * wave, j = lane >> 2, q = lane & 3;
+        auto inv_diag = [&](int bb) {
+            const int j = lane >> 2, q = lane & 3;
             float tq[4] = {0.f, 0.f, 0.f, 0.f};  // t_m for m = 4q + i
+            // this lane's four columns of a group's rows; the next group's are loaded while this one
+            // is solved
+            f32x4 arow[4], nrow[4];
+#pragma unroll
+            for (int a = 0; a < 4; ++a) nrow[a] = *reinterpret_cast<const f32x4 *>(&as[bb + a][bb + 4 * q]);
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                f32x4 arow[4];  // this lane's four columns of the group's rows (loaded when reached)
 #pragma unroll
-                for (int a = 0; a < 4; ++a)
-                    arow[a] = *reinterpret_cast<const f32x4 *>(&as[bb + 4 * g + a][bb + 4 * q]);
+                for (int a = 0; a < 4; ++a) arow[a] = nrow[a];
+                if (g + 1 < 4) {
+#pragma unroll
+                    for (int a = 0; a < 4; ++a)
+                        nrow[a] = *reinterpret_cast<const f32x4 *>(&as[bb + 4 * (g + 1) + a][bb + 4 * q]);
+                }
                 float p[4] = {0.f, 0.f, 0.f, 0.f};
                 if (g > 0) {
 #pragma unroll
@@ -646,12 +657,21 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
                     a_tile(IC<3>{}, IC<3>{});
                     a_tile(IC<3>{}, IC<2>{});
                 }
-            } else {
+            } else if constexpr (kMergeBC) {
                 if (wave == 0) {
                     a_tile(I0{}, I0{});
+                    a_tile(I1{}, I1{});
                     a_tile(I1{}, I0{});
+                }
+            } else {
+                // chunk 32: wavefronts 0 and 1 compute their diagonal tile and go straight on to its
+                // inverse; the tile below the diagonal (needed only in C) goes to wavefront 2
+                if (wave == 0) {
+                    a_tile(I0{}, I0{});
                 } else if (wave == 1) {
                     a_tile(I1{}, I1{});
+                } else if (wave == 2) {
+                    a_tile(I1{}, I0{});
                 }
             }
             if constexpr (!MAP && !kSplitKey) {
@@ -663,7 +683,20 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
                     else if (wave == 3) pa = p_pair(IC<1>{}, IC<0>{});
                 }
             }
-            if (wave < G::NB) inv_diag();
+            if constexpr (kMergeBC) {
+                // chunk 32, four wavefronts: wavefront 0 inverts both diagonal blocks (two independent
+                // chains the compiler interleaves) and forms T10 = -T11 A10 T00 right after, so no
+                // barrier separates the inversion from the block below it
+                if (wave == 0) {
+                    inv_diag(0);
+                    inv_diag(16);
+                    const f32x4 t10 =
+                        -mm16(rowfrag(ts, 16, 16), mm16(rowfrag(as, 16, 0), accfrag(ts, 0, 0), zero4), zero4);
+                    store_acc(ts, 16, 0, t10);
+                }
+            } else if (wave < G::NB) {
+                inv_diag(16 * wave);
+            }
             if constexpr (kTbFrags) {
                 // T's blocks (0,1) and (2,3) are read as zeros by F; last chunk's T diag(b)
                 // fragments (written over T's rows) are dead, so clear them again
@@ -693,7 +726,7 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
         }
         if constexpr (DELTA || !MAP) __syncthreads();
 
-        if constexpr (DELTA) {
+        if constexpr (DELTA && !kMergeBC) {
             if constexpr (G::WAVES == 4) __builtin_amdgcn_s_setprio(1);
             // ---- C: the blocks of T below the diagonal (chunk 64: T10, T32 and the lower-left
             // quarter T_BL = -T_BR A_BL T_TL), one output tile per wavefront:
