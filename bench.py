@@ -448,7 +448,25 @@ def main():
         gdn.chunk_prefill(pouts[0], pouts[1], pouts[2], pouts[3], pouts[4], pre["s0"], chunk=w.chunk,
                           out=out, final_state=fin, workspace=ws)
         pc_ev[i][1].record(stream)
+    # the same in one pass: the preparation inside the chunk kernels' loads
+    fws = torch.empty(max(gdn.gdn_prepare_chunk_prefill_workspace_size(w.B, w.T, w.H, w.dk, w.dv, w.chunk, gdn.GDN_BF16),
+                          1), device=dev, dtype=torch.uint8)
+
+    def prepared_prefill():
+        gdn.prepare_chunk_prefill(pin["xq"], pin["xk"], pin["xv"], pin["conv_weight"], pin["a_raw"], pin["b_raw"],
+                                  pre["s0"], decay_rate=pin["decay_rate"], gate_bias=pin["gate_bias"],
+                                  conv_state=pin["conv_state"], conv_state_out=pstate, chunk=w.chunk, out=out,
+                                  final_state=fin, workspace=fws)
+    for _ in range(args.warmup):
+        prepared_prefill()
+    pf_ev = [(mk(), mk()) for _ in range(args.steps)]
+    for a, b in pf_ev:
+        a.record(stream)
+        prepared_prefill()
+        b.record(stream)
     torch.cuda.synchronize()
+    fused_prefill_ms = sum(a.elapsed_time(b) for a, b in pf_ev) / len(pf_ev)
+    del fws
     din["conv_state"].copy_(dstate0)
     prep_ms = sum(a.elapsed_time(b) for a, b in pp_ev) / len(pp_ev)
     prep_dec_ms = sum(a.elapsed_time(b) for a, b in pd_ev) / len(pd_ev)
@@ -655,11 +673,14 @@ def main():
             "traffic_bytes_per_call": recorded_traffic("prepare"),
             "prepare_then_prefill_ms_avg": round(prep_chain_ms, 4),
             "prepare_then_prefill_tokens_per_s": round(w.B * w.T / (prep_chain_ms * 1e-3), 1),
+            "prepared_prefill_ms_avg": round(fused_prefill_ms, 4),
+            "prepared_prefill_tokens_per_s": round(w.B * w.T / (fused_prefill_ms * 1e-3), 1),
             "note": "short causal convolution + SiLU + q/k L2 norm + gate activations on the 64K shape "
                     "(bf16 in and out) and on the 256-sequence decode batch (state in place; decode_pool: the "
                     "same step as 256 one-token packed sequences with states in a 512-slot pool; decode_step_fused: "
                     "preparation and state update of that batch in one launch, decode_step_separate: the same as "
-                    "gdn_prepare + gdn_decode_step)",
+                    "gdn_prepare + gdn_decode_step; prepared_prefill: gdn_prepare_chunk_prefill, the preparation done "
+                    "in the prefill kernels' loads, against prepare_then_prefill, the two calls)",
         },
         "backward": {
             "workload": "1b_8k: B=4 H=32 T=8192 d_k=d_v=64, bf16 q/k/v, gated delta rule, zero start state",

@@ -19,6 +19,7 @@ current stream:
     decode_step_slots / chunk_prefill_varlen          (states in a pool, packed sequences)
     prepare(xq, xk, xv, conv_weight, a_raw, b_raw) -> (q, k, v, g, beta)
     prepare_decode_step(xq, xk, xv, conv_weight, a_raw, b_raw, conv_state, state) -> o
+    prepare_chunk_prefill(xq, xk, xv, conv_weight, a_raw, b_raw, initial_state) -> (o, final_state)
     chunk_backward(q, k, v, g, beta, d_o, ...) -> (dq, dk, dv, dg, dbeta, d_initial_state)
 
 The rule computed (a gated delta rule; the pages describe the GDN layer in
@@ -46,7 +47,8 @@ EXPORTS = ("gdn_chunk_prefill", "gdn_chunk_prefill_rule", "gdn_chunk_prefill_wor
            "gdn_chunk_prefill_varlen", "gdn_chunk_prefill_varlen_workspace_size",
            "gdn_decode_step", "gdn_decode_step_rule", "gdn_decode_step_slots", "gdn_prepare",
            "gdn_chunk_backward", "gdn_chunk_backward_workspace_size", "gdn_prepare_varlen",
-           "gdn_prepare_varlen_workspace_size", "gdn_prepare_decode_step", "gdn_status_string", "gdn_version")
+           "gdn_prepare_varlen_workspace_size", "gdn_prepare_decode_step", "gdn_prepare_chunk_prefill",
+           "gdn_prepare_chunk_prefill_workspace_size", "gdn_status_string", "gdn_version")
 
 
 class GdnError(RuntimeError):
@@ -101,6 +103,10 @@ def lib():
         L.gdn_prepare_varlen.restype = i32
         L.gdn_prepare_varlen_workspace_size.argtypes = [i32]
         L.gdn_prepare_varlen_workspace_size.restype = sz
+        L.gdn_prepare_chunk_prefill.argtypes = [i32] + [vp] * 13 + [i32] * 7 + [vp, sz, vp]
+        L.gdn_prepare_chunk_prefill.restype = i32
+        L.gdn_prepare_chunk_prefill_workspace_size.argtypes = [i32] * 7
+        L.gdn_prepare_chunk_prefill_workspace_size.restype = sz
         L.gdn_status_string.argtypes = [i32]
         L.gdn_status_string.restype = ctypes.c_char_p
         L.gdn_version.argtypes = []
@@ -193,6 +199,18 @@ def gdn_prepare_varlen(xq, xk, xv, conv_weight, a_raw, b_raw, decay_rate, gate_b
 
 def gdn_prepare_varlen_workspace_size(S) -> int:
     return lib().gdn_prepare_varlen_workspace_size(S)
+
+
+def gdn_prepare_chunk_prefill(rule, xq, xk, xv, conv_weight, a_raw, b_raw, decay_rate, gate_bias, conv_state_in,
+                              conv_state_out, initial_state, o, final_state, B, T, H, d_k, d_v, chunk, x_dtype,
+                              workspace, workspace_bytes, stream) -> int:
+    return lib().gdn_prepare_chunk_prefill(rule, xq, xk, xv, conv_weight, a_raw, b_raw, decay_rate, gate_bias,
+                                           conv_state_in, conv_state_out, initial_state, o, final_state, B, T, H,
+                                           d_k, d_v, chunk, x_dtype, workspace, workspace_bytes, stream)
+
+
+def gdn_prepare_chunk_prefill_workspace_size(B, T, H, d_k, d_v, chunk, x_dtype) -> int:
+    return lib().gdn_prepare_chunk_prefill_workspace_size(B, T, H, d_k, d_v, chunk, x_dtype)
 
 
 def gdn_status_string(status: int) -> str:
@@ -423,6 +441,50 @@ def prepare(xq, xk, xv, conv_weight, a_raw, b_raw, *, decay_rate=None, gate_bias
     return q, k, v, g, beta
 
 
+def prepare_chunk_prefill(xq, xk, xv, conv_weight, a_raw, b_raw, initial_state=None, *, decay_rate=None,
+                          gate_bias=None, conv_state=None, conv_state_out=None, chunk=64, out=None, final_state=None,
+                          workspace=None, stream=None, rule=GDN_RULE_GATED_DELTA):
+    """The preparation ahead of the mixer and the prefill in one pass (prepare() then chunk_prefill(),
+    without the prepared q, k, v, g, beta in device memory).  xq, xk [B,T,H,d_k], xv [B,T,H,d_v] bf16;
+    conv_weight [H*(2 d_k + d_v), 4]; a_raw, b_raw [B,T,H]; decay_rate, gate_bias [H] or None; conv_state
+    [B, H*(2 d_k + d_v), 3] or None (zeros); conv_state_out receives the carried window (pass conv_state
+    itself to update it in place); initial_state [B,H,d_k,d_v] or None.  Returns (o, final_state)."""
+    import torch
+    B, T, H, d_k = xq.shape
+    d_v = xv.shape[-1]
+    dt = _dtype_code(xq)
+    C = H * (2 * d_k + d_v)
+    _check(xq, "xq", xq.dtype)
+    _check(xk, "xk", xq.dtype, (B, T, H, d_k))
+    _check(xv, "xv", xq.dtype, (B, T, H, d_v))
+    for t, n, shp in ((conv_weight, "conv_weight", (C, 4)), (a_raw, "a_raw", (B, T, H)), (b_raw, "b_raw", (B, T, H)),
+                      (decay_rate, "decay_rate", (H,)), (gate_bias, "gate_bias", (H,)),
+                      (conv_state, "conv_state", (B, C, 3)), (conv_state_out, "conv_state_out", (B, C, 3)),
+                      (initial_state, "initial_state", (B, H, d_k, d_v))):
+        _check(t, n, torch.float32, shp)
+    dev = xq.device
+    if out is None:
+        out = torch.empty((B, T, H, d_v), device=dev, dtype=torch.float32)
+    if final_state is None:
+        final_state = torch.empty((B, H, d_k, d_v), device=dev, dtype=torch.float32)
+    _check(out, "out", torch.float32, (B, T, H, d_v))
+    _check(final_state, "final_state", torch.float32, (B, H, d_k, d_v))
+    need = int(gdn_prepare_chunk_prefill_workspace_size(B, T, H, d_k, d_v, chunk, dt))
+    own_ws = workspace is None and need > 0
+    if own_ws:
+        workspace = torch.empty(need, device=dev, dtype=torch.uint8)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    stream, given = _stream_of(stream, dev)
+    st = gdn_prepare_chunk_prefill(rule, _ptr(xq), _ptr(xk), _ptr(xv), _ptr(conv_weight), _ptr(a_raw), _ptr(b_raw),
+                                   _ptr(decay_rate), _ptr(gate_bias), _ptr(conv_state), _ptr(conv_state_out),
+                                   _ptr(initial_state), _ptr(out), _ptr(final_state), B, T, H, d_k, d_v, chunk, dt,
+                                   _ptr(workspace), ws_bytes, stream)
+    if st != 0:
+        raise GdnError(st, "gdn_prepare_chunk_prefill")
+    _keep_until_done([workspace] if own_ws else [], stream, given)
+    return out, final_state
+
+
 def chunk_backward(q, k, v, g, beta, d_o, initial_state=None, d_final_state=None, *, want_d_initial=True,
                    outs=None, workspace=None, stream=None, rule=GDN_RULE_GATED_DELTA):
     """Gradients of one prefill call for L = <d_o, o> + <d_final_state, S_T>.  Inputs as for
@@ -587,4 +649,5 @@ __all__ = ["EXPORTS", "GDN_F32", "GDN_BF16", "GDN_RULE_GATED_DELTA", "GDN_RULE_G
            "chunk_prefill", "chunk_prefill_varlen", "decode_step", "decode_step_slots", "workspace_bytes",
            "varlen_workspace_bytes", "gdn_prepare", "prepare", "gdn_chunk_backward",
            "gdn_chunk_backward_workspace_size", "chunk_backward", "backward_workspace_bytes", "gdn_prepare_varlen",
-           "gdn_prepare_varlen_workspace_size", "prepare_varlen", "gdn_prepare_decode_step", "prepare_decode_step"]
+           "gdn_prepare_varlen_workspace_size", "prepare_varlen", "gdn_prepare_decode_step", "prepare_decode_step",
+           "gdn_prepare_chunk_prefill", "gdn_prepare_chunk_prefill_workspace_size", "prepare_chunk_prefill"]

@@ -478,6 +478,68 @@ gdn_status gdn_prepare(const void *xq, const void *xk, const void *xv, const flo
     return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
+size_t gdn_prepare_chunk_prefill_workspace_size(int B, int T, int H, int d_k, int d_v, int chunk,
+                                                gdn_dtype x_dtype) {
+    if (B <= 0 || H <= 0 || T <= 0 || x_dtype != GDN_BF16 || !prepare_prefill_supported(d_k, d_v)) return 0;
+    if (chunk != 32 && chunk != 64) return 0;
+    if (prod({B, T, H, d_k}) == SIZE_MAX || prod({B, H, 16}) > 0x7fffffffULL) return 0;
+    return prepare_prefill_workspace(B, T, H, d_k, d_v);
+}
+
+gdn_status gdn_prepare_chunk_prefill(gdn_rule rule, const void *xq, const void *xk, const void *xv,
+                                     const float *conv_weight, const float *a_raw, const float *b_raw,
+                                     const float *decay_rate, const float *gate_bias, const float *conv_state_in,
+                                     float *conv_state_out, const float *initial_state, float *o,
+                                     float *final_state, int B, int T, int H, int d_k, int d_v, int chunk,
+                                     gdn_dtype x_dtype, void *workspace, size_t workspace_bytes, void *stream) {
+    if (rule != GDN_RULE_GATED_DELTA && rule != GDN_RULE_GATED_DECAY) return GDN_ERR_UNSUPPORTED;
+    if (B <= 0 || H <= 0 || T < 0 || d_k <= 0 || d_v <= 0 || chunk <= 0) return GDN_ERR_SHAPE;
+    if (x_dtype != GDN_BF16 || !prepare_prefill_supported(d_k, d_v) || (chunk != 32 && chunk != 64))
+        return GDN_ERR_UNSUPPORTED;
+    const long long C = static_cast<long long>(H) * (2 * d_k + d_v);
+    if (prod({B, T, H, d_k}) == SIZE_MAX || prod({B, H, 16}) > 0x7fffffffULL || prod({B, C, 3}) == SIZE_MAX ||
+        C > (1LL << 28))
+        return GDN_ERR_SHAPE;
+    if (!final_state || !conv_weight) return GDN_ERR_NULL;
+    if (T > 0 && (!xq || !xk || !xv || !a_raw || !b_raw || !o)) return GDN_ERR_NULL;
+    const void *ptrs[] = {xq, xk, xv, conv_weight, a_raw, b_raw, decay_rate, gate_bias, conv_state_in,
+                          conv_state_out, initial_state, o, final_state, workspace};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return GDN_ERR_ALIGN;
+
+    const size_t nk = prod({B, T, H, d_k}) * 2, nv = prod({B, T, H, d_v}) * 2, ng = prod({B, T, H}) * 4;
+    const size_t ns = prod({B, H, d_k, d_v}) * 4, nw = prod({B, C, 3}) * 4;
+    const Span s_init = initial_state ? span(initial_state, ns) : Span{0, 0};
+    const Span s_cin = conv_state_in ? span(conv_state_in, nw) : Span{0, 0};
+    const Span in[] = {span(xq, xq ? nk : 0), span(xk, xk ? nk : 0), span(xv, xv ? nv : 0),
+                       span(conv_weight, static_cast<size_t>(C) * 16), span(a_raw, a_raw ? ng : 0),
+                       span(b_raw, b_raw ? ng : 0), span(decay_rate, decay_rate ? static_cast<size_t>(H) * 4 : 0),
+                       span(gate_bias, gate_bias ? static_cast<size_t>(H) * 4 : 0), s_cin, s_init};
+    const size_t need = gdn_prepare_chunk_prefill_workspace_size(B, T, H, d_k, d_v, chunk, x_dtype);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return GDN_ERR_WORKSPACE;
+    const Span out[] = {span(o, o && T > 0 ? prod({B, T, H, d_v}) * 4 : 0), span(final_state, ns),
+                        conv_state_out ? span(conv_state_out, nw) : Span{0, 0},
+                        span(workspace, workspace ? need : 0)};
+    const int n_out = sizeof(out) / sizeof(out[0]);
+    for (int i = 0; i < n_out; ++i) {
+        for (int j = i + 1; j < n_out; ++j)
+            if (overlap(out[i], out[j])) return GDN_ERR_ALIAS;
+        for (const Span &x : in) {
+            // the allowed in-place updates: final state over the start state, window over window
+            const bool same = (i == 1 && initial_state == final_state && x.lo == s_init.lo && x.hi == s_init.hi) ||
+                              (i == 2 && conv_state_in == conv_state_out && x.lo == s_cin.lo && x.hi == s_cin.hi);
+            if (!same && overlap(out[i], x)) return GDN_ERR_ALIAS;
+        }
+    }
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (T == 0 && launch_state_copy(initial_state, final_state, ns / 4, hs) != hipSuccess) return GDN_ERR_HIP;
+    const hipError_t err = launch_prepare_prefill(
+        static_cast<const uint16_t *>(xq), static_cast<const uint16_t *>(xk), static_cast<const uint16_t *>(xv),
+        conv_weight, a_raw, b_raw, decay_rate, gate_bias, conv_state_in, conv_state_out, initial_state, o,
+        final_state, B, T, H, d_k, d_v, rule == GDN_RULE_GATED_DELTA, workspace, hs);
+    return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
 size_t gdn_chunk_backward_workspace_size(int B, int T, int H, int d_k, int d_v, gdn_dtype qkv_dtype) {
     if (B <= 0 || H <= 0 || T < 0 || !backward_supported(d_k, d_v, qkv_dtype)) return 0;
     if (prod({B, T, H, d_k}) == SIZE_MAX) return 0;

@@ -55,6 +55,13 @@ hipError_t launch_prefill_valu(const void *q, const void *k, const void *v, cons
 // bf16 inputs: chunked prefill with bf16 MFMA contractions.
 bool prefill_bf16_uses_mfma(int dk, int dv, int chunk);
 int prefill_kernel_chunk(int dk, int dv, int chunk, bool delta);
+// the input preparation fused into the MFMA chunk kernels' loads (bf16 raw projections)
+bool prepare_prefill_supported(int dk, int dv);
+size_t prepare_prefill_workspace(int B, int T, int H, int dk, int dv);
+hipError_t launch_prepare_prefill(const uint16_t *xq, const uint16_t *xk, const uint16_t *xv, const float *conv_w,
+                                  const float *a_raw, const float *b_raw, const float *rate, const float *bias,
+                                  const float *conv_in, float *conv_out, const float *s0, float *o, float *s_out,
+                                  int B, int T, int H, int dk, int dv, bool delta, void *ws, hipStream_t stream);
 hipError_t launch_prefill_bf16(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                const float *g, const float *beta, const float *s0, float *o,
                                float *s_out, int B, int T, int H, int dk, int dv, int chunk,

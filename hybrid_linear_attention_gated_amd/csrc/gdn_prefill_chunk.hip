@@ -34,9 +34,11 @@
 // so the serial path never leaves the wavefront.
 //
 // Precision: K K^T and Q K^T are exact bf16 products with fp32 accumulation.
-// W and the state in W St are single bf16; T diag(b) in U, the state in
-// Q St, P and Delta in P Delta, the decayed Delta in the state update and
-// both factors of the inversion's block products are hi + lo bf16 pairs.
+// Every other MFMA operand that is not an input is a hi + lo bf16 pair: T diag(b exp G)
+// in W, W and the state in W St (Delta = U - W St cancels where a slowly decaying state
+// already holds what the chunk writes), T diag(b) in U, the state in Q St, P and Delta
+// in P Delta, the decayed Delta in the state update, and both factors of the
+// inversion's block products.
 #include <type_traits>
 #include <vector>
 
@@ -172,6 +174,16 @@ struct ChunkArgs {
     SeqTable sq;           // packed sequences when sq.tok0 != NULL (then work items = pieces * H)
     float *pool;           // packed: state pool [slot][H][DK][DV] receiving final states
     int items;             // work items of this launch
+    // PREP (the input preparation in the loads): q, k, v, g, beta above then point at the raw
+    // projections and the raw gate / write-strength logits
+    const float *conv_w;   // [H (2 DK + DV)][4]: q channels, then k, then v (head-major)
+    const float *rate, *bias;  // [H] or NULL (1, 0)
+    const float *conv_in;  // [B][H (2 DK + DV)][3]: the three raw inputs before t = 0, or NULL
+};
+
+// Inputs of the preparation done in the chunk loads (PREP), beside the raw projections.
+struct PrepIn {
+    const float *conv_w, *rate, *bias, *conv_in;
 };
 
 // Eight bf16 to an 8-byte aligned LDS address (padded rows are not 16-byte aligned).
@@ -206,6 +218,15 @@ struct ChunkRegs {
     static_assert(C * DK % (8 * BLOCK) == 0 && C * DV % (8 * VTHREADS) == 0, "rows divide among threads");
     u16x8 k[NK], q[MAP ? 1 : NK], v[NV];
     float g, beta;
+    u16x8 halo;  // PREP: one raw vector of the three rows before the chunk (halo threads only)
+};
+
+// PREP: the raw rows before a chunk (the convolution's window) are loaded by the first
+// threads, one 8-channel vector each: three rows of K, of Q (not in MAP) and of V.
+template <int DK, int DV, bool MAP>
+struct Halo {
+    static constexpr int NKH = 3 * DK / 8, NQH = MAP ? 0 : 3 * DK / 8, NVH = 3 * DV / 8;
+    static constexpr int N = NKH + NQH + NVH;
 };
 
 // K and V are loaded one chunk row per lane (so their transposed copies can be
@@ -226,7 +247,7 @@ __device__ __forceinline__ float buf_load4(__amdgpu_buffer_rsrc_t r, unsigned by
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(byte_off), 0, 0));
 }
 
-template <int DK, int DV, int C, bool MAP>
+template <int DK, int DV, int C, bool MAP, bool PREP>
 __device__ __forceinline__ void load_chunk(ChunkRegs<DK, DV, C, MAP> &r, const ChunkArgs &a, size_t tok_base,
                                            int seq_len, int h, int n, int tid) {
     using R = ChunkRegs<DK, DV, C, MAP>;
@@ -265,6 +286,31 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<DK, DV, C, MAP> &r, const C
         r.g = buf_load4(chunk_rsrc(a.g + row0, rows_g), off);
         r.beta = buf_load4(chunk_rsrc(a.beta + row0, rows_g), off);
     }
+    if constexpr (PREP) {
+        using HL = Halo<DK, DV, MAP>;
+        if (tid < HL::N) {
+            // element: tensor (K, Q, V), halo row i (token t0 - 3 + i), 8-channel group c8
+            const bool isk = tid < HL::NKH, isq = !isk && tid < HL::NKH + HL::NQH;
+            const int e = isk ? tid : isq ? tid - HL::NKH : tid - HL::NKH - HL::NQH;
+            const int W = (isk || isq) ? DK : DV;
+            const int i = e / (W / 8), c8 = e % (W / 8);
+            const uint16_t *x = isk ? a.k : isq ? a.q : a.v;
+            if (t0 > 0) {  // chunks start at multiples of C >= 32: three earlier rows exist
+                r.halo = *reinterpret_cast<const u16x8 *>(x + ((tok_base + t0 - 3 + i) * a.H + h) * W + 8 * c8);
+            } else {
+                // the carried window [b][channel][3] (oldest first), read through bf16 (it holds
+                // raw inputs); zeros when absent
+                const int chan = (isq ? 0 : isk ? a.H * DK : 2 * a.H * DK) + h * W + 8 * c8;
+                const int nch = a.H * (2 * DK + DV);
+                u16x8 hv;
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    hv[j] = a.conv_in ? f32_to_bf16_bits(a.conv_in[(static_cast<size_t>(tok_base / a.T) * nch + chan + j) * 3 + i])
+                                      : static_cast<uint16_t>(0);
+                r.halo = hv;
+            }
+        }
+    }
 }
 
 // Several workgroups per compute unit where registers and LDS allow it (64-wide heads), so
@@ -284,7 +330,28 @@ int plan_slots(int dk, int dv, int chunk) { return 256 * ((dk == 64 && dv == 64)
 // Delta = diag(b) V with no W St term, and a piece map M_p that is a multiple of I.
 // STATES (OUT only): write the state every chunk starts from (for the gradients) instead of the
 // outputs, which the gradients do not use.
-template <int DK, int DV, int C, bool MAP, bool DELTA, bool STATES = false>
+// Sum over aligned groups of N adjacent lanes (N = 8 or 16), left in every lane of the group.
+template <int N>
+__device__ __forceinline__ float lane_group_sum(float x) {
+    x = dpp_add<0xB1>(x);                  // quad_perm [1,0,3,2]: lane ^ 1
+    x = dpp_add<0x4E>(x);                  // quad_perm [2,3,0,1]: lane ^ 2
+    x = dpp_add<0x141>(x);                 // row_half_mirror: the other quad of the eight
+    if constexpr (N == 16) x = dpp_add<0x140>(x);  // row_mirror: the other eight of the row
+    static_assert(N == 8 || N == 16, "group");
+    return x;
+}
+
+// SiLU as the preparation kernel evaluates it: c / (1 + e^-c)
+__device__ __forceinline__ float silu_f(float c) {
+    return c * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-c * kLog2e));
+}
+
+// PREP: the input preparation ahead of the mixer done in the chunk loads (the rows loaded are
+// the raw projections and logits): causal depthwise convolution of width 4, SiLU, the L2 norm
+// of each head's q and k rows (eps 1e-6 under the root), g = -A_h softplus(a + bias_h) and
+// beta = sigmoid(b); the prepared q, k, v are rounded once to bf16 (as the preparation kernel
+// stores them) and go on exactly like loaded rows.
+template <int DK, int DV, int C, bool MAP, bool DELTA, bool STATES = false, bool PREP = false>
 __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C>)) void chunk_kernel(ChunkArgs a) {
     using G = Cfg<DK, DV, C, MAP>;
     using R = ChunkRegs<DK, DV, C, MAP>;
@@ -307,7 +374,10 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
     // T = (I + A)^{-1}; without the erase term (no T) the same buffer holds V^T
     constexpr int TS_FLOATS = (DELTA || C * CSTR * 2 >= DV * VSTR) ? C * CSTR : (DV * VSTR + 1) / 2;
     __shared__ __align__(16) float t_s[TS_FLOATS];
-    __shared__ __align__(16) bf16x8 wf_s[DELTA ? G::CT * G::KS * kWave : 1];   // W A-fragments
+    // W A-fragments as hi + lo bf16 pairs: Delta = U - W St cancels where a slowly decaying state
+    // already holds what the chunk writes, so W St needs both factors split
+    __shared__ __align__(16) bf16x8 wf_s[DELTA ? G::CT * G::KS * kWave : 1];   // W, hi parts
+    __shared__ __align__(16) bf16x8 wfl_s[DELTA ? G::CT * G::KS * kWave : 1];  // W, lo parts
     __shared__ __align__(16) uint16_t kt_s[DK * KTSTR];            // K^T
     __shared__ __align__(16) float x_s[DELTA ? 16 * CSTR16 : 4];   // one 16x16 fp32 tile (C)
     // Eight wavefronts: two per T row tile build W in F (each half of its tiles), so the
@@ -322,6 +392,14 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
     constexpr bool kMergeBC = DELTA && C == 32 && G::WAVES == 4;
     __shared__ __align__(16) bf16x8 tbf_s[kSplitF ? G::CT * G::CS * 2 * kWave : 1];
     __shared__ float g_s[C], b_s[C], bg_s[C], dec_s[C], gam_s[C];  // g_s: G * log2(e)
+    // PREP: raw rows of the chunk after the three rows before it (row 3 + r holds chunk row r),
+    // the per-row partial squares of k, and this head's convolution weights (q, k, v channels)
+    constexpr int RKS = DK + 8, RVS = DV + 8;  // raw row strides (16-byte multiples)
+    __shared__ __align__(16) uint16_t kraw_s[PREP ? (C + 3) * RKS : 8];
+    __shared__ __align__(16) uint16_t qraw_s[(PREP && !MAP) ? (C + 3) * RKS : 8];
+    __shared__ __align__(16) uint16_t vraw_s[PREP ? (C + 3) * RVS : 8];
+    __shared__ __align__(16) float ksq_s[PREP ? C * (DK / 8) : 4];
+    __shared__ __align__(16) float wconv_s[PREP ? (2 * DK + DV) * 4 : 4];
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform
     const int tid = threadIdx.x, lane = tid % kWave;
@@ -393,6 +471,16 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
     }
     // T's blocks above the diagonal stay zero for the whole kernel
     for (int e = tid; e < TS_FLOATS; e += G::BLOCK) t_s[e] = 0.f;
+    float rate_h = 1.f, bias_h = 0.f;
+    if constexpr (PREP) {
+        for (int c = tid; c < 2 * DK + DV; c += G::BLOCK) {
+            const int chan = c < DK ? h * DK + c : c < 2 * DK ? a.H * DK + h * DK + (c - DK)
+                                                             : 2 * a.H * DK + h * DV + (c - 2 * DK);
+            *reinterpret_cast<f32x4 *>(&wconv_s[4 * c]) = *reinterpret_cast<const f32x4 *>(a.conv_w + 4 * static_cast<size_t>(chan));
+        }
+        if (a.rate) rate_h = a.rate[h];
+        if (a.bias) bias_h = a.bias[h];
+    }
 
     uint16_t(*ks)[KSTR] = reinterpret_cast<uint16_t(*)[KSTR]>(kv_s);
     uint16_t(*vt)[VSTR] = reinterpret_cast<uint16_t(*)[VSTR]>(DELTA ? static_cast<void *>(kv_s)
@@ -433,7 +521,7 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
     R cur;
-    if (n0 < n1) load_chunk<DK, DV, C, MAP>(cur, a, tok_base, seq_len, h, n0, tid);
+    if (n0 < n1) load_chunk<DK, DV, C, MAP, PREP>(cur, a, tok_base, seq_len, h, n0, tid);
 
     for (int n = n0; n < n1; ++n) {
         const int t0 = n * C;
@@ -447,6 +535,103 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
                         cs[(16 * mt + 4 * gq + r) * DV + 16 * (wave + G::WAVES * j) + li] = St[j][mt][r];
+        }
+
+        if constexpr (PREP) {
+            // ---- the input preparation: raw rows (and the window before the chunk) to LDS
+            using HL = Halo<DK, DV, MAP>;
+#pragma unroll
+            for (int i = 0; i < R::NK; ++i) {
+                const int e = tid + i * G::BLOCK;
+                *reinterpret_cast<u16x8 *>(&kraw_s[(3 + e % C) * RKS + 8 * (e / C)]) = cur.k[i];
+                if constexpr (!MAP)
+                    *reinterpret_cast<u16x8 *>(&qraw_s[(3 + e / (DK / 8)) * RKS + 8 * (e % (DK / 8))]) = cur.q[i];
+            }
+            if (tid < R::VTHREADS) {
+#pragma unroll
+                for (int i = 0; i < R::NV; ++i) {
+                    const int e = tid + i * R::VTHREADS;
+                    *reinterpret_cast<u16x8 *>(&vraw_s[(3 + e % C) * RVS + 8 * (e / C)]) = cur.v[i];
+                }
+            }
+            if (tid < HL::N) {
+                const bool isk = tid < HL::NKH, isq = !isk && tid < HL::NKH + HL::NQH;
+                const int e = isk ? tid : isq ? tid - HL::NKH : tid - HL::NKH - HL::NQH;
+                const int W = (isk || isq) ? DK : DV;
+                uint16_t *dst = isk ? kraw_s : isq ? qraw_s : vraw_s;
+                *reinterpret_cast<u16x8 *>(&dst[(e / (W / 8)) * (W + 8) + 8 * (e % (W / 8))]) = cur.halo;
+            }
+            if (wave == 0) {
+                // gates from the raw logits; rows past the sequence end stay inert (g = beta = 0)
+                const float z = cur.g + bias_h;
+                const float sp = fmaxf(z, 0.f) + log1pf(expf(-fabsf(z)));
+                cur.g = lane < L ? -rate_h * sp : 0.f;
+                cur.beta = lane < L ? 1.f / (1.f + expf(-cur.beta)) : 0.f;
+            }
+            __syncthreads();
+            // convolution over the four rows ending at the lane's row, then SiLU; rows past the
+            // sequence end give zeros
+            auto conv8 = [&](const uint16_t *raw, int stride, int r, int c0, const float *w, float (&y)[8]) {
+                u16x8 x[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) x[j] = *reinterpret_cast<const u16x8 *>(&raw[(r + j) * stride + c0]);
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    const f32x4 wc = *reinterpret_cast<const f32x4 *>(&w[4 * (c0 + c)]);
+                    const float cv = fmaf(wc[3], from_bf16(x[3][c]), fmaf(wc[2], from_bf16(x[2][c]),
+                                     fmaf(wc[1], from_bf16(x[1][c]), wc[0] * from_bf16(x[0][c]))));
+                    y[c] = r < L ? silu_f(cv) : 0.f;
+                }
+            };
+            // q first (finished here: its row's eight or sixteen lanes sum the squares), then k,
+            // whose sums cross wavefronts and wait for the next barrier
+            if constexpr (!MAP) {
+#pragma unroll
+                for (int i = 0; i < R::NK; ++i) {
+                    const int e = tid + i * G::BLOCK, rq = e / (DK / 8), cq = e % (DK / 8);
+                    float qy[8];
+                    conv8(qraw_s, RKS, rq, 8 * cq, wconv_s, qy);
+                    float qs2 = 0.f;
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) qs2 = fmaf(qy[c], qy[c], qs2);
+                    const float rn = __builtin_amdgcn_rsqf(lane_group_sum<DK / 8>(qs2) + 1e-6f);
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) qy[c] *= rn;
+                    cur.q[i] = __builtin_bit_cast(u16x8, pack_bf16(qy));
+                }
+            }
+            float ky[R::NK][8];
+#pragma unroll
+            for (int i = 0; i < R::NK; ++i) {
+                const int e = tid + i * G::BLOCK, rr = e % C, c8 = e / C;
+                conv8(kraw_s, RKS, rr, 8 * c8, wconv_s + 4 * DK, ky[i]);
+                float ss = 0.f;
+#pragma unroll
+                for (int c = 0; c < 8; ++c) ss = fmaf(ky[i][c], ky[i][c], ss);
+                ksq_s[rr * (DK / 8) + c8] = ss;
+            }
+            if (tid < R::VTHREADS) {
+#pragma unroll
+                for (int i = 0; i < R::NV; ++i) {
+                    const int e = tid + i * R::VTHREADS;
+                    float vy[8];
+                    conv8(vraw_s, RVS, e % C, 8 * (e / C), wconv_s + 8 * DK, vy);
+                    cur.v[i] = __builtin_bit_cast(u16x8, pack_bf16(vy));
+                }
+            }
+            __syncthreads();
+            // k's norm from the partial squares of its row
+#pragma unroll
+            for (int i = 0; i < R::NK; ++i) {
+                const int e = tid + i * G::BLOCK, rr = e % C;
+                float ss = 0.f;
+#pragma unroll
+                for (int c8 = 0; c8 < DK / 8; ++c8) ss += ksq_s[rr * (DK / 8) + c8];
+                const float rn = __builtin_amdgcn_rsqf(ss + 1e-6f);
+#pragma unroll
+                for (int c = 0; c < 8; ++c) ky[i][c] *= rn;
+                cur.k[i] = __builtin_bit_cast(u16x8, pack_bf16(ky[i]));
+            }
         }
 
         // ---- A: this chunk's rows into LDS (K both row-major and transposed); gates
@@ -866,17 +1051,21 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
                         xb[e] = x[e] * b0[e];
                         xb[4 + e] = x[4 + e] * b1[e];
                     }
-                    const bf16x8 bfr = pack_bf16(xg);
+                    bf16x8 bgh, bgl;
+                    split_bf16(xg, bgh, bgl);
                     split_bf16(xb, tbh[s], tbl[s]);
     #pragma unroll
-                    for (int mt = 0; mt < MTN; ++mt)
-                        accw[mt] = mfma_bf16(kfrag(half * MTN + mt, s), bfr, accw[mt]);
+                    for (int mt = 0; mt < MTN; ++mt) {
+                        accw[mt] = mfma_bf16(kfrag(half * MTN + mt, s), bgh, accw[mt]);
+                        accw[mt] = mfma_bf16(kfrag(half * MTN + mt, s), bgl, accw[mt]);
+                    }
                 }
     #pragma unroll
                 for (int s2 = 0; s2 < MTN / 2; ++s2) {
                     float x[8];
                     acc_pair_to_slots(accw[2 * s2], accw[2 * s2 + 1], x);
-                    wf_s[(ct * G::KS + half * (MTN / 2) + s2) * kWave + lane] = pack_bf16(x);
+                    const int wi = (ct * G::KS + half * (MTN / 2) + s2) * kWave + lane;
+                    split_bf16(x, wf_s[wi], wfl_s[wi]);
                 }
                 // this wavefront's T rows have all been read (LDS keeps a wavefront's accesses in
                 // order); keep the compiler from moving the stores above the loads
@@ -902,20 +1091,24 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
                         lds_slots_f32(&ts[16 * ct + li][0], s, gq, x);
     #pragma unroll
                         for (int e = 0; e < 8; ++e) x[e] *= bg_s[kmap(s, gq, e)];
-                        const bf16x8 bfr = pack_bf16(x);
-                        acc0 = mfma_bf16(kfrag(2 * s2, s), bfr, acc0);
-                        acc1 = mfma_bf16(kfrag(2 * s2 + 1, s), bfr, acc1);
+                        bf16x8 bgh, bgl;
+                        split_bf16(x, bgh, bgl);
+                        acc0 = mfma_bf16(kfrag(2 * s2, s), bgh, acc0);
+                        acc0 = mfma_bf16(kfrag(2 * s2, s), bgl, acc0);
+                        acc1 = mfma_bf16(kfrag(2 * s2 + 1, s), bgh, acc1);
+                        acc1 = mfma_bf16(kfrag(2 * s2 + 1, s), bgl, acc1);
                     }
                     float x[8];
                     acc_pair_to_slots(acc0, acc1, x);
-                    wf_s[(ct * G::KS + s2) * kWave + lane] = pack_bf16(x);
+                    const int wi = (ct * G::KS + s2) * kWave + lane;
+                    split_bf16(x, wf_s[wi], wfl_s[wi]);
                 }
             }
             __syncthreads();
         }
 
         // next chunk's rows: loads in flight during this chunk's slice work
-        if (n + 1 < n1) load_chunk<DK, DV, C, MAP>(cur, a, tok_base, seq_len, h, n + 1, tid);
+        if (n + 1 < n1) load_chunk<DK, DV, C, MAP, PREP>(cur, a, tok_base, seq_len, h, n + 1, tid);
 
         // ---- G: per slice: U = (T diag b) V, Delta = U - W St, outputs, state update
         if constexpr (G::WAVES == 4) __builtin_amdgcn_s_setprio(2);
@@ -967,33 +1160,33 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
                     }
                 }
             }
-            if constexpr (DELTA) {
-                bf16x8 Sb[G::KS];
-#pragma unroll
-                for (int s = 0; s < G::KS; ++s) {
-                    float x[8];
-                    acc_pair_to_slots(St[j][2 * s], St[j][2 * s + 1], x);
-                    Sb[s] = pack_bf16(x);
-                }
-#pragma unroll
-                for (int ct = 0; ct < G::CT; ++ct) {
-                    f32x4 acc = zero4;
-#pragma unroll
-                    for (int s = 0; s < G::KS; ++s)
-                        acc = mfma_bf16(wf_s[(ct * G::KS + s) * kWave + lane], Sb[s], acc);
-                    D[ct] -= acc;  // Delta = U - W St
-                }
-            }
-
-            if (!MAP && !STATES && value_slice) {
-                // O = scale (diag(exp G) Q St + P Delta) with the chunk's start state
-                bf16x8 Sh[G::KS], Sl[G::KS], Dh[G::CS], Dl[G::CS];
+            bf16x8 Sh[G::KS], Sl[G::KS];  // the chunk's start state as hi + lo pairs
+            if constexpr (DELTA || !MAP) {
 #pragma unroll
                 for (int s = 0; s < G::KS; ++s) {
                     float x[8];
                     acc_pair_to_slots(St[j][2 * s], St[j][2 * s + 1], x);
                     split_bf16(x, Sh[s], Sl[s]);
                 }
+            }
+            if constexpr (DELTA) {
+#pragma unroll
+                for (int ct = 0; ct < G::CT; ++ct) {
+                    f32x4 acc = zero4;
+#pragma unroll
+                    for (int s = 0; s < G::KS; ++s) {
+                        const bf16x8 wh = wf_s[(ct * G::KS + s) * kWave + lane];
+                        acc = mfma_bf16(wh, Sh[s], acc);
+                        acc = mfma_bf16(wh, Sl[s], acc);
+                        acc = mfma_bf16(wfl_s[(ct * G::KS + s) * kWave + lane], Sh[s], acc);
+                    }
+                    D[ct] -= acc;  // Delta = U - W St
+                }
+            }
+
+            if (!MAP && !STATES && value_slice) {
+                // O = scale (diag(exp G) Q St + P Delta) with the chunk's start state
+                bf16x8 Dh[G::CS], Dl[G::CS];
 #pragma unroll
                 for (int s = 0; s < G::CS; ++s) {
                     float x[8];
@@ -1057,7 +1250,9 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
             // products need twice the temporaries and spill (85 registers; MAP 0.90 -> 0.68 ms on
             // a 24-head 64K call with this barrier).  The 64 x 64 maps interleave them in
             // registers they have, and are faster that way (0.36 vs 0.38 ms).
-            if constexpr (G::SPW > 1 && G::WAVES == 8) __builtin_amdgcn_sched_barrier(0);
+            // Chunk 32 (three workgroups per compute unit, 168 registers): the same, else the two
+            // slices' hi/lo state pairs spill.
+            if constexpr (G::SPW > 1 && (G::WAVES == 8 || C == 32)) __builtin_amdgcn_sched_barrier(0);
         }
         if constexpr (G::WAVES == 4) __builtin_amdgcn_s_setprio(0);
         __syncthreads();
@@ -1340,10 +1535,10 @@ size_t chunk_ws_bytes(int B, int T, int H) {
     return ((maps + 255) & ~static_cast<size_t>(255)) + starts;
 }
 
-template <int DK, int DV, int C, bool DELTA>
+template <int DK, int DV, int C, bool DELTA, bool PREP = false>
 hipError_t run_chunk(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,
                      const float *beta, const float *s0, float *o, float *s_out, int B, int T, int H,
-                     void *ws, hipStream_t stream, float *chunk_states = nullptr) {
+                     void *ws, hipStream_t stream, float *chunk_states = nullptr, const PrepIn *pin = nullptr) {
     const int N = (T + C - 1) / C;
     const int BH = B * H;
     const PiecePlan plan = piece_plan(BH, N, kPlanSlots<DK, DV, C>);
@@ -1351,6 +1546,12 @@ hipError_t run_chunk(const uint16_t *q, const uint16_t *k, const uint16_t *v, co
     ChunkArgs a{};
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.o = o; a.s_final = s_out;
     a.chunk_states = chunk_states;
+    if constexpr (PREP) {
+        a.conv_w = pin->conv_w;
+        a.rate = pin->rate;
+        a.bias = pin->bias;
+        a.conv_in = pin->conv_in;
+    }
     a.T = T; a.H = H; a.BH = BH; a.P = P; a.N = N;
     a.sq = SeqTable{};
     auto grid = [](int items) { return dim3((items + kXcds - 1) / kXcds * kXcds); };
@@ -1365,7 +1566,7 @@ hipError_t run_chunk(const uint16_t *q, const uint16_t *k, const uint16_t *v, co
             }
         }
         if (chunk_states) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((chunk_kernel<DK, DV, C, false, DELTA>), grid(items), dim3(kWave * kWavesOf<DK, DV>), 0, stream, a);
+        hipLaunchKernelGGL((chunk_kernel<DK, DV, C, false, DELTA, false, PREP>), grid(items), dim3(kWave * kWavesOf<DK, DV>), 0, stream, a);
         return hipGetLastError();
     };
     if (P == 1) {
@@ -1379,7 +1580,7 @@ hipError_t run_chunk(const uint16_t *q, const uint16_t *k, const uint16_t *v, co
                                               ((maps_bytes + 255) & ~static_cast<size_t>(255)));
     a.maps = maps;
     a.items = BH * (P - 1);
-    hipLaunchKernelGGL((chunk_kernel<DK, DV, C, true, DELTA>), grid(BH * (P - 1)), dim3(kWave * kWavesOf<DK, DV>), 0, stream, a);
+    hipLaunchKernelGGL((chunk_kernel<DK, DV, C, true, DELTA, false, PREP>), grid(BH * (P - 1)), dim3(kWave * kWavesOf<DK, DV>), 0, stream, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL((chain_kernel<DK, DV>), dim3(BH * (DV / 16)), dim3(kWave * (DK / 32)), 0, stream,
@@ -1507,6 +1708,74 @@ hipError_t launch_prefill_chunk_varlen(const uint16_t *q, const uint16_t *k, con
 namespace {
 }  // namespace
 
+
+namespace {
+
+// The carried convolution window after a call: the last three raw inputs of [window before the
+// call, the call's tokens], oldest first, one thread per (sequence, channel).  Each thread reads
+// its three old entries before writing any, so the window may be updated in place; it runs
+// after the chunk kernels, which read the old window at the first chunk.
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void conv_window_kernel(const uint16_t *__restrict__ xq, const uint16_t *__restrict__ xk,
+                                                          const uint16_t *__restrict__ xv, const float *cin, float *cout,
+                                                          int B, int T, int H) {
+    const int nch = H * (2 * DK + DV);
+    const long long idx = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+    if (idx >= static_cast<long long>(B) * nch) return;
+    const int b = static_cast<int>(idx / nch), c = static_cast<int>(idx % nch);
+    const uint16_t *x;
+    int W, cc;  // the channel's tensor, its row width and the channel inside it
+    if (c < H * DK) { x = xq; W = H * DK; cc = c; }
+    else if (c < 2 * H * DK) { x = xk; W = H * DK; cc = c - H * DK; }
+    else { x = xv; W = H * DV; cc = c - 2 * H * DK; }
+    float w[3];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        const int p = T - 3 + i;  // the token at window entry i (negative: an entry of the old window)
+        w[i] = p >= 0 ? from_bf16(x[(static_cast<size_t>(b) * T + p) * W + cc])
+                      : (cin ? cin[static_cast<size_t>(idx) * 3 + 3 + p] : 0.f);
+    }
+#pragma unroll
+    for (int i = 0; i < 3; ++i) cout[static_cast<size_t>(idx) * 3 + i] = w[i];
+}
+
+}  // namespace
+
+bool prepare_prefill_supported(int dk, int dv) { return dk == dv && (dk == 64 || dk == 128); }
+
+// Fused preparation + prefill: always 32-token chunks (the preparation's raw rows must fit
+// beside three workgroups' LDS per compute unit for 64-wide heads)
+size_t prepare_prefill_workspace(int B, int T, int H, int dk, int dv) {
+    return prefill_chunk_workspace(B, T, H, dk, dv, 32);
+}
+
+hipError_t launch_prepare_prefill(const uint16_t *xq, const uint16_t *xk, const uint16_t *xv, const float *conv_w,
+                                  const float *a_raw, const float *b_raw, const float *rate, const float *bias,
+                                  const float *conv_in, float *conv_out, const float *s0, float *o, float *s_out,
+                                  int B, int T, int H, int dk, int dv, bool delta, void *ws, hipStream_t stream) {
+    if (!prepare_prefill_supported(dk, dv)) return hipErrorInvalidValue;
+    const PrepIn pin{conv_w, rate, bias, conv_in};
+    hipError_t err = hipSuccess;
+    if (T > 0) {
+        if (dk == 64)
+            err = delta ? run_chunk<64, 64, 32, true, true>(xq, xk, xv, a_raw, b_raw, s0, o, s_out, B, T, H, ws, stream, nullptr, &pin)
+                        : run_chunk<64, 64, 32, false, true>(xq, xk, xv, a_raw, b_raw, s0, o, s_out, B, T, H, ws, stream, nullptr, &pin);
+        else
+            err = delta ? run_chunk<128, 128, 32, true, true>(xq, xk, xv, a_raw, b_raw, s0, o, s_out, B, T, H, ws, stream, nullptr, &pin)
+                        : run_chunk<128, 128, 32, false, true>(xq, xk, xv, a_raw, b_raw, s0, o, s_out, B, T, H, ws, stream, nullptr, &pin);
+        if (err != hipSuccess) return err;
+    }
+    if (conv_out) {
+        const long long n = static_cast<long long>(B) * H * (2 * dk + dv);
+        const unsigned blocks = static_cast<unsigned>((n + 255) / 256);
+        if (dk == 64)
+            hipLaunchKernelGGL((conv_window_kernel<64, 64>), dim3(blocks), dim3(256), 0, stream, xq, xk, xv, conv_in, conv_out, B, T, H);
+        else
+            hipLaunchKernelGGL((conv_window_kernel<128, 128>), dim3(blocks), dim3(256), 0, stream, xq, xk, xv, conv_in, conv_out, B, T, H);
+        err = hipGetLastError();
+    }
+    return err;
+}
 
 size_t prefill_chunk_workspace(int B, int T, int H, int dk, int dv, int chunk) {
 #define GDN_WS(DK_, DV_, C_) \

@@ -353,6 +353,51 @@ GDN_API gdn_status gdn_prepare(const void *xq, const void *xk, const void *xv,
                                gdn_dtype x_dtype, void *stream);
 
 /*
+ * gdn_prepare_chunk_prefill -- gdn_prepare followed by gdn_chunk_prefill_rule in
+ * one pass: the chunk kernels read the raw projections and logits and apply
+ * the short convolution, SiLU, the q/k L2 norm and the gate activations as
+ * they load each chunk, so the prepared q, k, v, g, beta never go to device
+ * memory (the GDN block's own convolution and gates sit right before the
+ * mixer: ftxj.github.io digest of arXiv 2604.24715, Method).  The prepared
+ * q, k, v are rounded once to bf16, as gdn_prepare stores them for GDN_BF16,
+ * so the call computes what the two calls compute, up to the summation order
+ * of each head's squared q and k norms.
+ *
+ *   rule                      GDN_RULE_GATED_DELTA or GDN_RULE_GATED_DECAY
+ *   xq, xk, xv, conv_weight, a_raw, b_raw, decay_rate, gate_bias
+ *                             as for gdn_prepare (x_dtype must be GDN_BF16)
+ *   conv_state_in             [B, H*(2 d_k + d_v), 3] fp32 or NULL (zeros); it
+ *                             holds raw inputs and is read through bf16
+ *   conv_state_out            same shape or NULL; may be conv_state_in itself
+ *   initial_state, o, final_state, chunk, workspace
+ *                             as for gdn_chunk_prefill_rule (workspace of
+ *                             gdn_prepare_chunk_prefill_workspace_size bytes;
+ *                             chunk 32 or 64 = the longest chunk allowed, the
+ *                             kernels run 32-token chunks)
+ * Supported: GDN_BF16, d_k = d_v in {64, 128}.  T may be 0 (the states are
+ * copied).
+ * Errors: GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_UNSUPPORTED, GDN_ERR_ALIGN,
+ * GDN_ERR_ALIAS (an output overlapping an input or another output, other than
+ * final_state == initial_state and conv_state_out == conv_state_in),
+ * GDN_ERR_WORKSPACE, GDN_ERR_HIP.
+ */
+GDN_API gdn_status gdn_prepare_chunk_prefill(gdn_rule rule,
+                             const void *xq, const void *xk, const void *xv,
+                             const float *conv_weight,
+                             const float *a_raw, const float *b_raw,
+                             const float *decay_rate, const float *gate_bias,
+                             const float *conv_state_in, float *conv_state_out,
+                             const float *initial_state, float *o, float *final_state,
+                             int B, int T, int H, int d_k, int d_v, int chunk,
+                             gdn_dtype x_dtype,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes gdn_prepare_chunk_prefill needs (0 if none or when the
+ * arguments would be rejected). */
+GDN_API size_t gdn_prepare_chunk_prefill_workspace_size(int B, int T, int H, int d_k, int d_v, int chunk,
+                                                        gdn_dtype x_dtype);
+
+/*
  * gdn_prepare_decode_step -- one generated token for each of N sequences, from
  * the raw projections: gdn_prepare with T = 1 and the convolution window
  * updated in place, then gdn_decode_step_rule on the prepared q, k, v, g, beta,

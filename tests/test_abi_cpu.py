@@ -321,3 +321,33 @@ def test_noalloc_validates_like_the_workspace_call():
     assert call(dt=5) == UNSUP
     assert call(B=0) == SHAPE
     assert call(T=-1) == SHAPE
+
+
+def prepare_prefill_call(**kw):
+    args = dict(rule=0, xq=addr(0), xk=addr(1), xv=addr(2), w=addr(3), a=addr(4), b=addr(5), rate=None, bias=None,
+                cin=None, cout=None, s0=None, o=addr(6), sf=addr(7), B=1, T=4096, H=4, dk=64, dv=64, chunk=64,
+                dt=BF16, ws=addr(8), ws_bytes=1 << 30, stream=None)
+    args.update(kw)
+    return gdn.gdn_prepare_chunk_prefill(*[args[n] for n in ("rule", "xq", "xk", "xv", "w", "a", "b", "rate", "bias",
+                                                             "cin", "cout", "s0", "o", "sf", "B", "T", "H", "dk", "dv",
+                                                             "chunk", "dt", "ws", "ws_bytes", "stream")])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(rule=2), UNSUP), (dict(dt=F32), UNSUP), (dict(dk=64, dv=128), UNSUP), (dict(dk=16, dv=16), UNSUP),
+    (dict(chunk=16), UNSUP), (dict(B=0), SHAPE), (dict(T=-1), SHAPE), (dict(H=0), SHAPE),
+    (dict(xq=None), NULL), (dict(w=None), NULL), (dict(sf=None), NULL), (dict(o=None), NULL), (dict(b=None), NULL),
+    (dict(xk=addr(1) + 8), ALIGN), (dict(cin=addr(9) + 4), ALIGN), (dict(sf=addr(7) + 4), ALIGN),
+    (dict(o=addr(0)), ALIAS), (dict(sf=addr(3)), ALIAS), (dict(cout=addr(2) + 64), ALIAS),
+    (dict(cin=addr(9), cout=addr(9) + 16), ALIAS), (dict(s0=addr(10), sf=addr(10) + 256), ALIAS),
+    (dict(ws=addr(0)), ALIAS), (dict(ws=None), WS), (dict(ws_bytes=64), WS),
+])
+def test_prepare_prefill_rejects(kw, code):
+    assert prepare_prefill_call(**kw) == code
+
+
+def test_prepare_prefill_workspace_size():
+    n = gdn.gdn_prepare_chunk_prefill_workspace_size(1, 65536, 32, 64, 64, 64, BF16)
+    assert n == gdn.gdn_chunk_prefill_workspace_size(1, 65536, 32, 64, 64, 32, BF16) > 0
+    assert gdn.gdn_prepare_chunk_prefill_workspace_size(1, 65536, 32, 64, 64, 64, F32) == 0
+    assert gdn.gdn_prepare_chunk_prefill_workspace_size(1, 100, 2, 64, 64, 64, BF16) == 0
