@@ -360,7 +360,11 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
     constexpr int KSTR = DK + kRowPad;   // K and Q rows
     constexpr int VSTR = C + kRowPad;    // V^T rows
     constexpr int CSTR = C + 4;       // A and T rows (fp32)
-    constexpr int KV_ELEMS = C * KSTR > DV * VSTR ? C * KSTR : DV * VSTR;
+    // Chunk 32 with the erase term: no W.  Delta = U - W St = T diag(b) (V - diag(exp G) K St),
+    // formed per slice in G from K's rows, V^T and T, so there is no phase F; V^T and the P
+    // fragments get buffers of their own (K's rows stay live through G).
+    constexpr bool kNoW = DELTA && C == 32;
+    constexpr int KV_ELEMS = (kNoW || C * KSTR > DV * VSTR) ? C * KSTR : DV * VSTR;
     constexpr int KTSTR = C + kRowPad;   // K^T rows
     constexpr int CSTR16 = 20;        // rows of the 16x16 scratch tile (conflict-free f32x4 reads)
     static_assert(2 * G::CT * G::CS * kWave * 16 <= C * CSTR * 4, "P fragments fit in A's buffer");
@@ -368,7 +372,9 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
     // T diag(b) once and parks them over that wavefront's own (then dead) T rows.
     constexpr bool kTbFrags = G::CT == kKeyWaves;
     static_assert(!kTbFrags || 2 * G::CS * kWave * 16 <= 16 * CSTR * 4, "T diag(b) fragments fit in 16 T rows");
-    __shared__ __align__(16) uint16_t kv_s[KV_ELEMS];              // K rows, then V^T
+    __shared__ __align__(16) uint16_t kv_s[KV_ELEMS];              // K rows (then V^T, with W)
+    __shared__ __align__(16) uint16_t vt_s[kNoW ? DV * VSTR : 8];  // V^T (no W)
+    __shared__ __align__(16) bf16x8 pf2_s[kNoW ? 2 * G::CT * G::CS * kWave : 1];  // P fragments (no W)
     __shared__ __align__(16) uint16_t q_s[MAP ? 8 : C * KSTR];     // Q rows
     __shared__ __align__(16) float a_s[C * CSTR];                  // A, then P fragments
     // T = (I + A)^{-1}; without the erase term (no T) the same buffer holds V^T
@@ -376,8 +382,8 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
     __shared__ __align__(16) float t_s[TS_FLOATS];
     // W A-fragments as hi + lo bf16 pairs: Delta = U - W St cancels where a slowly decaying state
     // already holds what the chunk writes, so W St needs both factors split
-    __shared__ __align__(16) bf16x8 wf_s[DELTA ? G::CT * G::KS * kWave : 1];   // W, hi parts
-    __shared__ __align__(16) bf16x8 wfl_s[DELTA ? G::CT * G::KS * kWave : 1];  // W, lo parts
+    __shared__ __align__(16) bf16x8 wf_s[(DELTA && !kNoW) ? G::CT * G::KS * kWave : 1];   // W, hi parts
+    __shared__ __align__(16) bf16x8 wfl_s[(DELTA && !kNoW) ? G::CT * G::KS * kWave : 1];  // W, lo parts
     __shared__ __align__(16) uint16_t kt_s[DK * KTSTR];            // K^T
     __shared__ __align__(16) float x_s[DELTA ? 16 * CSTR16 : 4];   // one 16x16 fp32 tile (C)
     // Eight wavefronts: two per T row tile build W in F (each half of its tiles), so the
@@ -483,8 +489,9 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
     }
 
     uint16_t(*ks)[KSTR] = reinterpret_cast<uint16_t(*)[KSTR]>(kv_s);
-    uint16_t(*vt)[VSTR] = reinterpret_cast<uint16_t(*)[VSTR]>(DELTA ? static_cast<void *>(kv_s)
-                                                                     : static_cast<void *>(t_s));
+    uint16_t(*vt)[VSTR] = reinterpret_cast<uint16_t(*)[VSTR]>(kNoW ? static_cast<void *>(vt_s)
+                                                              : DELTA ? static_cast<void *>(kv_s)
+                                                                      : static_cast<void *>(t_s));
     uint16_t(*qs)[KSTR] = reinterpret_cast<uint16_t(*)[KSTR]>(q_s);
     uint16_t(*kt)[KTSTR] = reinterpret_cast<uint16_t(*)[KTSTR]>(kt_s);
     // K^T A-fragment (d tile mt, chunk-row step s): K^T[16 mt + li][kmap(s, gq, e)]
@@ -501,7 +508,8 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
     auto kfrag = [&](int mt, int s) { return frag(&kt[16 * mt + li][0], s); };
     float(*as)[CSTR] = reinterpret_cast<float(*)[CSTR]>(a_s);
     float(*ts)[CSTR] = reinterpret_cast<float(*)[CSTR]>(t_s);
-    bf16x8 *pf_s = reinterpret_cast<bf16x8 *>(a_s);  // P fragments: ((mt * CS + s) * 2 + hi/lo) * 64 + lane
+    // P fragments: ((mt * CS + s) * 2 + hi/lo) * 64 + lane
+    bf16x8 *pf_s = kNoW ? pf2_s : reinterpret_cast<bf16x8 *>(a_s);
 
     float(*xs)[CSTR16] = reinterpret_cast<float(*)[CSTR16]>(x_s);
     // 16x16 fp32 blocks of a row-major LDS matrix as MFMA operands
@@ -662,8 +670,8 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
                 dec_s[lane] = exp2_fast(glast - x);
             }
         }
-        if constexpr (!DELTA) {
-            // V^T goes to its own buffer at once: without the inversion no later phase frees one
+        if constexpr (!DELTA || kNoW) {
+            // V^T goes to its own buffer at once (no phase F to stage it in)
             if (tid < R::VTHREADS) {
 #pragma unroll
                 for (int i = 0; i < R::NV; ++i) {
@@ -863,6 +871,10 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
                 if constexpr (G::CT == 4) {
                     if (wave == 2) pa = p_pair(IC<0>{}, IC<0>{});
                     else if (wave == 3) pa = p_pair(IC<2>{}, IC<1>{});
+                } else if constexpr (kNoW) {
+                    // P has its own buffer: stored at once, read in G after B's barrier
+                    if (wave == 2) p_store(IC<0>{}, IC<0>{}, p_pair(IC<0>{}, IC<0>{}));
+                    else if (wave == 3) p_store(IC<1>{}, IC<0>{}, p_pair(IC<1>{}, IC<0>{}));
                 } else {
                     if (wave == 2) pa = p_pair(IC<0>{}, IC<0>{});
                     else if (wave == 3) pa = p_pair(IC<1>{}, IC<0>{});
@@ -982,7 +994,7 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
             if constexpr (kSplitF) return &tbf_s[((ct * G::CS + s) * 2 + hl) * kWave + lane];
             return reinterpret_cast<bf16x8 *>(&ts[16 * ct][0]) + (s * 2 + hl) * kWave + lane;
         };
-        if constexpr (DELTA) {
+        if constexpr (DELTA && !kNoW) {
             if constexpr (G::WAVES == 4) __builtin_amdgcn_s_setprio(0);
             // ---- F: P fragments and V^T into LDS (A and K are dead); W A-fragments = W^T tiles
             // (2 s2, ct) and (2 s2 + 1, ct), W = T diag(b exp G) K
@@ -1110,7 +1122,8 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
         // next chunk's rows: loads in flight during this chunk's slice work
         if (n + 1 < n1) load_chunk<DK, DV, C, MAP, PREP>(cur, a, tok_base, seq_len, h, n + 1, tid);
 
-        // ---- G: per slice: U = (T diag b) V, Delta = U - W St, outputs, state update
+        // ---- G: per slice: U = (T diag b) V, Delta = U - W St (chunk 32: Delta = T diag(b) R,
+        // R = V - diag(exp G) K St), outputs, state update
         if constexpr (G::WAVES == 4) __builtin_amdgcn_s_setprio(2);
 #pragma unroll
         for (int j = 0; j < G::SPW; ++j) {
@@ -1128,7 +1141,62 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
             f32x4 D[G::CT];
 #pragma unroll
             for (int ct = 0; ct < G::CT; ++ct) D[ct] = zero4;
-            if (!DELTA) {
+            bf16x8 Sh[G::KS], Sl[G::KS];  // the chunk's start state as hi + lo pairs
+            if constexpr (DELTA || !MAP) {
+#pragma unroll
+                for (int s = 0; s < G::KS; ++s) {
+                    float x[8];
+                    acc_pair_to_slots(St[j][2 * s], St[j][2 * s + 1], x);
+                    split_bf16(x, Sh[s], Sl[s]);
+                }
+            }
+            if constexpr (kNoW) {
+                // R = V - diag(exp G) K St in fp32 (V = 0 on a map's identity columns): where the
+                // state already holds what the chunk writes the two nearly cancel, so K St takes
+                // the state as hi + lo and R is split again before Delta = T diag(b) R
+                f32x4 Rr[G::CT];
+#pragma unroll
+                for (int ct = 0; ct < G::CT; ++ct) {
+                    f32x4 acc = zero4;
+#pragma unroll
+                    for (int s = 0; s < G::KS; ++s) {
+                        const bf16x8 kr = frag(&ks[16 * ct + li][0], s);
+                        acc = mfma_bf16(kr, Sh[s], acc);
+                        acc = mfma_bf16(kr, Sl[s], acc);
+                    }
+                    const f32x4 g4 = *reinterpret_cast<const f32x4 *>(&gam_s[16 * ct + 4 * gq]);
+                    if (value_slice) {
+                        const u16x4 v4 = *reinterpret_cast<const u16x4 *>(&vt[16 * sl + li][col_of(16 * ct + 4 * gq)]);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) Rr[ct][r] = fmaf(-g4[r], acc[r], from_bf16(v4[r]));
+                    } else {
+                        Rr[ct] = -(g4 * acc);
+                    }
+                }
+                bf16x8 Rh[G::CS], Rl[G::CS];
+#pragma unroll
+                for (int s = 0; s < G::CS; ++s) {
+                    float x[8];
+                    acc_pair_to_slots(Rr[2 * s], Rr[2 * s + 1], x);
+                    split_bf16(x, Rh[s], Rl[s]);
+                }
+#pragma unroll
+                for (int ct = 0; ct < G::CT; ++ct) {
+#pragma unroll
+                    for (int s = 0; s < G::CS; ++s) {
+                        if (32 * s > 16 * ct + 15) continue;  // T is lower triangular
+                        float x[8];
+                        lds_slots_f32(&ts[16 * ct + li][0], s, gq, x);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) x[e] *= b_s[kmap(s, gq, e)];
+                        bf16x8 th, tl;
+                        split_bf16(x, th, tl);
+                        D[ct] = mfma_bf16(th, Rh[s], D[ct]);
+                        D[ct] = mfma_bf16(th, Rl[s], D[ct]);
+                        D[ct] = mfma_bf16(tl, Rh[s], D[ct]);
+                    }
+                }
+            } else if (!DELTA) {
                 // no erase term: Delta = diag(b) V, four consecutive chunk rows per lane from V^T
 #pragma unroll
                 for (int ct = 0; ct < G::CT; ++ct) {
@@ -1160,16 +1228,7 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
                     }
                 }
             }
-            bf16x8 Sh[G::KS], Sl[G::KS];  // the chunk's start state as hi + lo pairs
-            if constexpr (DELTA || !MAP) {
-#pragma unroll
-                for (int s = 0; s < G::KS; ++s) {
-                    float x[8];
-                    acc_pair_to_slots(St[j][2 * s], St[j][2 * s + 1], x);
-                    split_bf16(x, Sh[s], Sl[s]);
-                }
-            }
-            if constexpr (DELTA) {
+            if constexpr (DELTA && !kNoW) {
 #pragma unroll
                 for (int ct = 0; ct < G::CT; ++ct) {
                     f32x4 acc = zero4;
