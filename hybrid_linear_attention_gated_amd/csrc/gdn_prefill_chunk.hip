@@ -247,6 +247,13 @@ __device__ __forceinline__ float buf_load4(__amdgpu_buffer_rsrc_t r, unsigned by
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(byte_off), 0, 0));
 }
 
+// A value every lane holds alike, moved to scalar registers (lane 0's copy)
+__device__ __forceinline__ size_t uniform_u64(size_t x) {
+    const unsigned lo = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(x));
+    const unsigned hi = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(x >> 32));
+    return (static_cast<size_t>(hi) << 32) | lo;
+}
+
 template <int DK, int DV, int C, bool MAP, bool PREP>
 __device__ __forceinline__ void load_chunk(ChunkRegs<DK, DV, C, MAP> &r, const ChunkArgs &a, size_t tok_base,
                                            int seq_len, int h, int n, int tid) {
@@ -280,11 +287,13 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<DK, DV, C, MAP> &r, const C
             r.v[i] = buf_load16(rv, static_cast<unsigned>(rr * a.H * DV + 8 * c8) * 2u);
         }
     }
+    const unsigned rows_g = __builtin_amdgcn_readfirstlane(static_cast<unsigned>((L - 1) * a.H + 1) * 4u);
+    const auto rg = chunk_rsrc(a.g + row0, rows_g);
+    const auto rb = chunk_rsrc(a.beta + row0, rows_g);
     if (tid < kWave) {
-        const unsigned rows_g = static_cast<unsigned>((L - 1) * a.H + 1) * 4u;
         const unsigned off = static_cast<unsigned>(tid * a.H) * 4u;
-        r.g = buf_load4(chunk_rsrc(a.g + row0, rows_g), off);
-        r.beta = buf_load4(chunk_rsrc(a.beta + row0, rows_g), off);
+        r.g = buf_load4(rg, off);
+        r.beta = buf_load4(rb, off);
     }
     if constexpr (PREP) {
         using HL = Halo<DK, DV, MAP>;
@@ -455,6 +464,15 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
             if (n1 == nchunks && slot >= 0) final_out = a.pool + (static_cast<size_t>(slot) * a.H + h) * DK * DV;
         }
     }
+
+    // The work item's indices are the same on every lane, but on the packed-sequence
+    // path they come from a table load the compiler cannot prove uniform: without this each
+    // chunk's buffer loads would run as a loop over distinct descriptors.
+    h = __builtin_amdgcn_readfirstlane(h);
+    n0 = __builtin_amdgcn_readfirstlane(n0);
+    n1 = __builtin_amdgcn_readfirstlane(n1);
+    seq_len = __builtin_amdgcn_readfirstlane(seq_len);
+    tok_base = uniform_u64(tok_base);
 
     // ---- carried state: St[j][mt] holds rows 16 mt + 4 gq + r, column 16 sl + li, sl = wave + 4 j
     f32x4 St[G::SPW][G::KT];
