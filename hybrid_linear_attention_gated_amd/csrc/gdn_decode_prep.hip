@@ -104,9 +104,10 @@ __global__ __launch_bounds__(2 * kWave) void prep_decode_kernel(PrepDecodeArgs a
     const float ga = gb[0], b = gb[1];
     const float av = __expf(ga);
     float *st = a.state + nh * kD * kD;
+    // the state streams through with non-temporal hints, as in the plain decode step
     f32x4 s[kRows];
 #pragma unroll
-    for (int m = 0; m < kRows; ++m) s[m] = *reinterpret_cast<const f32x4 *>(st + (row0 + m) * kD + col);
+    for (int m = 0; m < kRows; ++m) s[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(st + (row0 + m) * kD + col));
     f32x4 u = {0.f, 0.f, 0.f, 0.f}, p = {0.f, 0.f, 0.f, 0.f};
     float kq = 0.f;
 #pragma unroll
@@ -130,7 +131,7 @@ __global__ __launch_bounds__(2 * kWave) void prep_decode_kernel(PrepDecodeArgs a
     if (rg == 0) *reinterpret_cast<f32x4 *>(a.o + nh * kD + col) = a.scale * (av * p + delta * kq);
 #pragma unroll
     for (int m = 0; m < kRows; ++m)
-        *reinterpret_cast<f32x4 *>(st + (row0 + m) * kD + col) = av * s[m] + delta * ks[row0 + m];
+        __builtin_nontemporal_store(av * s[m] + delta * ks[row0 + m], reinterpret_cast<f32x4 *>(st + (row0 + m) * kD + col));
 }
 
 }  // namespace

@@ -1146,7 +1146,9 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
 #pragma unroll
         for (int j = 0; j < G::SPW; ++j) {
             const int sl = wave + G::WAVES * j;
-            const bool value_slice = sl < G::VT;
+            // sl < VT, known per j: VT is a multiple of the wavefront count
+            static_assert(G::VT % G::WAVES == 0, "value slices");
+            const bool value_slice = j < G::VT / G::WAVES;
             if constexpr (!DELTA) {
                 if (!value_slice) {
                     // identity columns of a piece map: with no erase term only the decay acts
