@@ -74,9 +74,10 @@ TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_prefill_1b_64k_dec
 
 
 def recorded_traffic(kind):
-    """Counter-measured HBM bytes for `kind` ('prefill' and 'prepare' per 64K call, 'decode' per
-    step, 'fused' per one-launch decode step of the 256-sequence batch) from the committed summary, or None when the kernel sources no longer match the recorded
-    digest."""
+    """Counter-measured HBM bytes for `kind` ('prefill', 'prepare' and 'prepared' -- the prefill
+    from the raw projections in one pass -- per 64K call, 'decode' per step, 'fused' per one-launch
+    decode step of the 256-sequence batch) from the committed summary, or None when the kernel
+    sources no longer match the recorded digest."""
     try:
         with open(TRAFFIC_SUMMARY) as f:
             fields = dict(line.strip().split(": ", 1) for line in f if line.strip().startswith(kind + "-"))
@@ -203,6 +204,17 @@ def main():
                     decay_rate=din["decay_rate"], gate_bias=din["gate_bias"], conv_state=din["conv_state"],
                     conv_state_out=din["conv_state"])
 
+    # the 64K prefill from the raw projections in one pass: the preparation inside the chunk
+    # kernels' loads
+    fws = torch.empty(max(gdn.gdn_prepare_chunk_prefill_workspace_size(w.B, w.T, w.H, w.dk, w.dv, w.chunk, gdn.GDN_BF16),
+                          1), device=dev, dtype=torch.uint8)
+
+    def prepared_prefill():
+        gdn.prepare_chunk_prefill(pin["xq"], pin["xk"], pin["xv"], pin["conv_weight"], pin["a_raw"], pin["b_raw"],
+                                  pre["s0"], decay_rate=pin["decay_rate"], gate_bias=pin["gate_bias"],
+                                  conv_state=pin["conv_state"], conv_state_out=pstate, chunk=w.chunk, out=out,
+                                  final_state=fin, workspace=fws)
+
     # gradients of one prefill call on the training shape 1b_8k (B=4 H=32 T=8192 d=64)
     bw = gi.WORKLOADS[args.backward_workload]
     bin_ = gi.workload_inputs(args.backward_workload, device=dev)
@@ -231,14 +243,20 @@ def main():
         return
 
     if args.only == "prepare":
+        # the preparation on both shapes, the prefill with the preparation in its loads, and the
+        # one-launch decode step from the raw projections
         for _ in range(args.warmup):
             prepare()
             prepare_decode()
+            prepared_prefill()
+            decode_fused()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for _ in range(args.steps):
             prepare()
             prepare_decode()
+            prepared_prefill()
+            decode_fused()
         torch.cuda.synchronize()
         print(json.dumps({"only": "prepare", "steps": args.steps,
                           "wall_ms": (time.perf_counter() - t0) * 1e3}), flush=True)
@@ -448,15 +466,6 @@ def main():
         gdn.chunk_prefill(pouts[0], pouts[1], pouts[2], pouts[3], pouts[4], pre["s0"], chunk=w.chunk,
                           out=out, final_state=fin, workspace=ws)
         pc_ev[i][1].record(stream)
-    # the same in one pass: the preparation inside the chunk kernels' loads
-    fws = torch.empty(max(gdn.gdn_prepare_chunk_prefill_workspace_size(w.B, w.T, w.H, w.dk, w.dv, w.chunk, gdn.GDN_BF16),
-                          1), device=dev, dtype=torch.uint8)
-
-    def prepared_prefill():
-        gdn.prepare_chunk_prefill(pin["xq"], pin["xk"], pin["xv"], pin["conv_weight"], pin["a_raw"], pin["b_raw"],
-                                  pre["s0"], decay_rate=pin["decay_rate"], gate_bias=pin["gate_bias"],
-                                  conv_state=pin["conv_state"], conv_state_out=pstate, chunk=w.chunk, out=out,
-                                  final_state=fin, workspace=fws)
     for _ in range(args.warmup):
         prepared_prefill()
     pf_ev = [(mk(), mk()) for _ in range(args.steps)]
@@ -675,6 +684,7 @@ def main():
             "prepare_then_prefill_tokens_per_s": round(w.B * w.T / (prep_chain_ms * 1e-3), 1),
             "prepared_prefill_ms_avg": round(fused_prefill_ms, 4),
             "prepared_prefill_tokens_per_s": round(w.B * w.T / (fused_prefill_ms * 1e-3), 1),
+            "prepared_prefill_traffic_bytes": recorded_traffic("prepared"),
             "note": "short causal convolution + SiLU + q/k L2 norm + gate activations on the 64K shape "
                     "(bf16 in and out) and on the 256-sequence decode batch (state in place; decode_pool: the "
                     "same step as 256 one-token packed sequences with states in a 512-slot pool; decode_step_fused: "
