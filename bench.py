@@ -640,10 +640,12 @@ def main():
             "graph_GBps": round(dec_bytes / (graph_avg * 1e-3) / 1e9, 1),
             "graph_hbm_frac": round(dec_bytes / (graph_avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
             "traffic_bytes_per_step": recorded_traffic("decode"),
+            "dram_bound_hbm_frac": round(dec_bytes / (sum(rot_us) / len(rot_us) * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
             "note": "warm: 16 back-to-back steps launched from Python, each between its own events (host "
                     "launch gaps included), the 128 MiB state can stay in the 256 MB last-level cache; cold: a "
                     "1 GiB buffer is read before every step; graph: the 16 steps replayed from one HIP graph, "
-                    "time / 16",
+                    "time / 16; dram_bound_hbm_frac: the headline decode figure, the same step over eight "
+                    "distinct states in rotation (decode_8_layers), every state access from DRAM",
         },
         "decode_8_layers": {
             "workload": "the 256 x 32 x 64 decode step over 8 distinct 128 MiB states in rotation (one per GDN "
