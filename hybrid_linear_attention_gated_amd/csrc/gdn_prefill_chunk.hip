@@ -402,11 +402,18 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
     // wavefronts 4-7, so 0-3 compute only their diagonal tile and its inverse in B, and the
     // blocks of T in C.
     constexpr bool kSplitKey = kSplitF;
-    // Chunk 32 with four wavefronts: the whole inversion (both diagonal blocks and T10) on
-    // wavefront 0 in B, and no phase C (four barriers per chunk instead of five).
+    // Chunk 32 with four wavefronts: the whole keyside in B, no phase C.  Wavefront 0 forms A's first
+    // diagonal tile and inverts it; wavefront 1 the second tile and its inverse, then A10, and after
+    // wavefront 0 has published T00 (an LDS flag holding the chunk index), T10 = -T11 A10 T00.
     constexpr bool kMergeBC = DELTA && C == 32 && G::WAVES == 4;
     __shared__ __align__(16) bf16x8 tbf_s[kSplitF ? G::CT * G::CS * 2 * kWave : 1];
     __shared__ float g_s[C], b_s[C], bg_s[C], dec_s[C], gam_s[C];  // g_s: G * log2(e)
+    __shared__ int t00_ready;  // the last chunk whose T00 wavefront 0 has stored (kMergeBC)
+    // The hi/lo A-fragments of T diag(b) for G, built once per chunk by wavefronts 0 and 1 at the end
+    // of B instead of by every slice wavefront (not in the preparation kernels, whose registers are
+    // at the occupancy limit already)
+    constexpr bool kShareTB = kMergeBC && !PREP;
+    __shared__ __align__(16) bf16x8 tbs_s[kShareTB ? 2 * G::CT * kWave : 1];  // (ct * 2 + hi/lo) * 64 + lane
     // PREP: raw rows of the chunk after the three rows before it (row 3 + r holds chunk row r),
     // the per-row partial squares of k, and this head's convolution weights (q, k, v channels)
     constexpr int RKS = DK + 8, RVS = DV + 8;  // raw row strides (16-byte multiples)
@@ -495,6 +502,7 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
     }
     // T's blocks above the diagonal stay zero for the whole kernel
     for (int e = tid; e < TS_FLOATS; e += G::BLOCK) t_s[e] = 0.f;
+    if (tid == 0) t00_ready = -1;
     float rate_h = 1.f, bias_h = 0.f;
     if constexpr (PREP) {
         for (int c = tid; c < 2 * DK + DV; c += G::BLOCK) {
@@ -871,8 +879,8 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
             } else if constexpr (kMergeBC) {
                 if (wave == 0) {
                     a_tile(I0{}, I0{});
+                } else if (wave == 1) {
                     a_tile(I1{}, I1{});
-                    a_tile(I1{}, I0{});
                 }
             } else {
                 // chunk 32: wavefronts 0 and 1 compute their diagonal tile and go straight on to its
@@ -899,15 +907,34 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
                 }
             }
             if constexpr (kMergeBC) {
-                // chunk 32, four wavefronts: wavefront 0 inverts both diagonal blocks (two independent
-                // chains the compiler interleaves) and forms T10 = -T11 A10 T00 right after, so no
-                // barrier separates the inversion from the block below it
+                // chunk 32, four wavefronts: the two diagonal inverses run side by side on wavefronts 0
+                // and 1; T10 waits for T00 on wavefront 1 through the flag instead of a barrier.  The
+                // wait ends: wavefront 0 publishes every chunk without waiting on anything of wavefront
+                // 1, and the chunk's barriers keep the two within one chunk of each other.  64K prefill
+                // 0.80 -> 0.78 ms against both inverses and T10 on wavefront 0; with the fragments of
+                // T diag(b) built here too, 0.75 ms.
+                auto tb_build = [&](int ct) {
+                    float x[8];
+                    lds_slots_f32(&ts[16 * ct + li][0], 0, gq, x);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) x[e] *= b_s[kmap(0, gq, e)];
+                    split_bf16(x, tbs_s[(2 * ct) * kWave + lane], tbs_s[(2 * ct + 1) * kWave + lane]);
+                };
                 if (wave == 0) {
                     inv_diag(0);
+                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+                    __hip_atomic_store(&t00_ready, n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                    if constexpr (kShareTB) tb_build(0);
+                } else if (wave == 1) {
                     inv_diag(16);
+                    a_tile(I1{}, I0{});
+                    while (__hip_atomic_load(&t00_ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < n)
+                        __builtin_amdgcn_s_sleep(1);
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
                     const f32x4 t10 =
                         -mm16(rowfrag(ts, 16, 16), mm16(rowfrag(as, 16, 0), accfrag(ts, 0, 0), zero4), zero4);
                     store_acc(ts, 16, 0, t10);
+                    if constexpr (kShareTB) tb_build(1);
                 }
             } else if (wave < G::NB) {
                 inv_diag(16 * wave);
@@ -1205,12 +1232,17 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
 #pragma unroll
                     for (int s = 0; s < G::CS; ++s) {
                         if (32 * s > 16 * ct + 15) continue;  // T is lower triangular
-                        float x[8];
-                        lds_slots_f32(&ts[16 * ct + li][0], s, gq, x);
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) x[e] *= b_s[kmap(s, gq, e)];
                         bf16x8 th, tl;
-                        split_bf16(x, th, tl);
+                        if constexpr (kShareTB) {
+                            th = tbs_s[(2 * ct) * kWave + lane];
+                            tl = tbs_s[(2 * ct + 1) * kWave + lane];
+                        } else {
+                            float x[8];
+                            lds_slots_f32(&ts[16 * ct + li][0], s, gq, x);
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) x[e] *= b_s[kmap(s, gq, e)];
+                            split_bf16(x, th, tl);
+                        }
                         D[ct] = mfma_bf16(th, Rh[s], D[ct]);
                         D[ct] = mfma_bf16(th, Rl[s], D[ct]);
                         D[ct] = mfma_bf16(tl, Rh[s], D[ct]);
