@@ -402,10 +402,12 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
     // wavefronts 4-7, so 0-3 compute only their diagonal tile and its inverse in B, and the
     // blocks of T in C.
     constexpr bool kSplitKey = kSplitF;
-    // Chunk 32 with four wavefronts: the whole keyside in B, no phase C.  Wavefront 0 forms A's first
-    // diagonal tile and inverts it; wavefront 1 the second tile and its inverse, then A10, and after
-    // wavefront 0 has published T00 (an LDS flag holding the chunk index), T10 = -T11 A10 T00.
-    constexpr bool kMergeBC = DELTA && C == 32 && G::WAVES == 4;
+    // Chunk 32: the whole keyside in B, no phase C.  Wavefront 0 forms A's first diagonal tile and
+    // inverts it; wavefront 1 the second tile and its inverse, then A10, and after wavefront 0 has
+    // published T00 (an LDS flag holding the chunk index), T10 = -T11 A10 T00.  (With eight
+    // wavefronts, 128 x 128 heads, wavefronts 4-7 wait in B: 3B-shaped 64K call 1.59 -> 1.56 ms
+    // against the A tiles on three wavefronts and T10 after a barrier of its own.)
+    constexpr bool kMergeBC = DELTA && C == 32 && (G::WAVES == 4 || G::WAVES == 8);
     __shared__ __align__(16) bf16x8 tbf_s[kSplitF ? G::CT * G::CS * 2 * kWave : 1];
     __shared__ float g_s[C], b_s[C], bg_s[C], dec_s[C], gam_s[C];  // g_s: G * log2(e)
     __shared__ int t00_ready;  // the last chunk whose T00 wavefront 0 has stored (kMergeBC)
@@ -907,7 +909,7 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
                 }
             }
             if constexpr (kMergeBC) {
-                // chunk 32, four wavefronts: the two diagonal inverses run side by side on wavefronts 0
+                // chunk 32: the two diagonal inverses run side by side on wavefronts 0
                 // and 1; T10 waits for T00 on wavefront 1 through the flag instead of a barrier.  The
                 // wait ends: wavefront 0 publishes every chunk without waiting on anything of wavefront
                 // 1, and the chunk's barriers keep the two within one chunk of each other.  64K prefill
