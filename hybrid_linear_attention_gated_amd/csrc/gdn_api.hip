@@ -135,11 +135,15 @@ size_t gdn_chunk_prefill_workspace_size(int B, int T, int H, int d_k, int d_v, i
     return 0;  // the fp32 path keeps everything on chip
 }
 
-gdn_status gdn_chunk_prefill_rule(gdn_rule rule, const void *q, const void *k, const void *v,
-                                  const float *g, const float *beta, const float *initial_state,
-                                  float *o, float *final_state, int B, int T, int H, int d_k,
-                                  int d_v, int chunk, gdn_dtype qkv_dtype, void *workspace,
-                                  size_t workspace_bytes, void *stream) {
+namespace {
+
+// The dense prefill.  tfrag: the workspace has room for the per-chunk T diag(b) fragments of
+// 128 x 128 heads (the size gdn_chunk_prefill_workspace_size reports); the call without allocation
+// runs from its smaller static scratch without them (same results).
+gdn_status prefill_rule(gdn_rule rule, const void *q, const void *k, const void *v, const float *g,
+                        const float *beta, const float *initial_state, float *o, float *final_state,
+                        int B, int T, int H, int d_k, int d_v, int chunk, gdn_dtype qkv_dtype,
+                        void *workspace, size_t workspace_bytes, void *stream, bool tfrag) {
     if (rule != GDN_RULE_GATED_DELTA && rule != GDN_RULE_GATED_DECAY) return GDN_ERR_UNSUPPORTED;
     const bool delta = rule == GDN_RULE_GATED_DELTA;
     gdn_status st = check_prefill_shape(B, T, H, d_k, d_v, chunk, qkv_dtype);
@@ -173,7 +177,7 @@ gdn_status gdn_chunk_prefill_rule(gdn_rule rule, const void *q, const void *k, c
         if (overlap(s_o, in) || overlap(s_fin, in)) return GDN_ERR_ALIAS;
     if (overlap(s_o, s_init) || overlap(s_o, s_fin)) return GDN_ERR_ALIAS;
 
-    const size_t need = gdn_chunk_prefill_workspace_size(B, T, H, d_k, d_v, chunk, qkv_dtype);
+    const size_t need = qkv_dtype == GDN_BF16 ? prefill_bf16_workspace(B, T, H, d_k, d_v, chunk, tfrag) : 0;
     if (need > 0) {
         if (!workspace || workspace_bytes < need) return GDN_ERR_WORKSPACE;
         const Span s_ws = span(workspace, need);
@@ -186,11 +190,22 @@ gdn_status gdn_chunk_prefill_rule(gdn_rule rule, const void *q, const void *k, c
     if (qkv_dtype == GDN_BF16)
         err = launch_prefill_bf16(static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
                                   static_cast<const uint16_t *>(v), g, beta, initial_state, o,
-                                  final_state, B, T, H, d_k, d_v, chunk, delta, workspace, hs);
+                                  final_state, B, T, H, d_k, d_v, chunk, delta, workspace, hs, tfrag);
     else
         err = launch_prefill_valu(q, k, v, g, beta, initial_state, o, final_state, B, T, H, d_k,
                                   d_v, chunk, GDN_F32, delta, hs);
     return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+}  // namespace
+
+gdn_status gdn_chunk_prefill_rule(gdn_rule rule, const void *q, const void *k, const void *v,
+                                  const float *g, const float *beta, const float *initial_state,
+                                  float *o, float *final_state, int B, int T, int H, int d_k,
+                                  int d_v, int chunk, gdn_dtype qkv_dtype, void *workspace,
+                                  size_t workspace_bytes, void *stream) {
+    return prefill_rule(rule, q, k, v, g, beta, initial_state, o, final_state, B, T, H, d_k, d_v,
+                        chunk, qkv_dtype, workspace, workspace_bytes, stream, true);
 }
 
 gdn_status gdn_chunk_prefill_noalloc(gdn_rule rule, const void *q, const void *k, const void *v,
@@ -202,16 +217,15 @@ gdn_status gdn_chunk_prefill_noalloc(gdn_rule rule, const void *q, const void *k
     if (rule != GDN_RULE_GATED_DELTA && rule != GDN_RULE_GATED_DECAY) return GDN_ERR_UNSUPPORTED;
     const gdn_status st = check_prefill_shape(B, T, H, d_k, d_v, chunk, qkv_dtype);
     if (st != GDN_OK) return st;
-    const size_t need = gdn_chunk_prefill_workspace_size(B, T, H, d_k, d_v, chunk, qkv_dtype);
+    const size_t need = (qkv_dtype == GDN_BF16 && T > 0) ? prefill_bf16_workspace(B, T, H, d_k, d_v, chunk, false) : 0;
     if (need > GDN_NOALLOC_SCRATCH_BYTES) return GDN_ERR_WORKSPACE;
     void *ws = nullptr;
     if (need > 0) {
         const gdn_status s2 = scratch_of_current_device(&ws);
         if (s2 != GDN_OK) return s2;
     }
-    return gdn_chunk_prefill_rule(rule, q, k, v, g, beta, initial_state, o, final_state, B, T, H, d_k,
-                                  d_v, chunk, qkv_dtype, ws, need > 0 ? GDN_NOALLOC_SCRATCH_BYTES : 0,
-                                  stream);
+    return prefill_rule(rule, q, k, v, g, beta, initial_state, o, final_state, B, T, H, d_k, d_v, chunk,
+                        qkv_dtype, ws, need > 0 ? GDN_NOALLOC_SCRATCH_BYTES : 0, stream, false);
 }
 
 gdn_status gdn_chunk_prefill(const void *q, const void *k, const void *v, const float *g,

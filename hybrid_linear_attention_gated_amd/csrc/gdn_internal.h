@@ -65,18 +65,21 @@ hipError_t launch_prepare_prefill(const uint16_t *xq, const uint16_t *xk, const 
 hipError_t launch_prefill_bf16(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                const float *g, const float *beta, const float *s0, float *o,
                                float *s_out, int B, int T, int H, int dk, int dv, int chunk,
-                               bool delta, void *ws, hipStream_t stream);
-size_t prefill_bf16_workspace(int B, int T, int H, int dk, int dv, int chunk);
+                               bool delta, void *ws, hipStream_t stream, bool tfrag = true);
+size_t prefill_bf16_workspace(int B, int T, int H, int dk, int dv, int chunk, bool tfrag = true);
 
 // bf16 inputs, fused chunk kernel with sequence pieces (gdn_prefill_chunk.hip).
 // chunk_states (optional): receives the state every chunk starts from, [B*H][N][dk][dv]; o is
 // then not written (the gradients need the states, not the outputs).
+// tfrag: 128 x 128 heads under the gated delta rule keep every chunk's T diag(b) fragments in the
+// workspace (MAP writes them, OUT reads them); the workspace must then be the size
+// prefill_chunk_workspace(..., true) gives.  Same results either way.
 hipError_t launch_prefill_chunk(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                 const float *g, const float *beta, const float *s0, float *o,
                                 float *s_out, int B, int T, int H, int dk, int dv, int chunk,
                                 bool delta, void *ws, hipStream_t stream,
-                                float *chunk_states = nullptr);
-size_t prefill_chunk_workspace(int B, int T, int H, int dk, int dv, int chunk);
+                                float *chunk_states = nullptr, bool tfrag = false);
+size_t prefill_chunk_workspace(int B, int T, int H, int dk, int dv, int chunk, bool tfrag = false);
 
 // Packed variable-length sequences (bf16, MFMA shapes).  cu, slots and init are host
 // arrays (cu[S + 1] token offsets; slots[S] pool slots, NULL = slot s, -1 = none;

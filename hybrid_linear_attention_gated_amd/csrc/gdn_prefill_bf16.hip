@@ -23,9 +23,10 @@ int prefill_kernel_chunk(int dk, int dv, int chunk, bool delta) {
 }
 
 // Workspace for either rule (the size query takes no rule): the larger of the two plans.
-size_t prefill_bf16_workspace(int B, int T, int H, int dk, int dv, int chunk) {
+// tfrag: with room for the gated delta rule's per-chunk T diag(b) fragments (128 x 128 heads).
+size_t prefill_bf16_workspace(int B, int T, int H, int dk, int dv, int chunk, bool tfrag) {
     if (!prefill_bf16_uses_mfma(dk, dv, chunk)) return 0;
-    const size_t a = prefill_chunk_workspace(B, T, H, dk, dv, prefill_kernel_chunk(dk, dv, chunk, true));
+    const size_t a = prefill_chunk_workspace(B, T, H, dk, dv, prefill_kernel_chunk(dk, dv, chunk, true), tfrag);
     const size_t b = prefill_chunk_workspace(B, T, H, dk, dv, prefill_kernel_chunk(dk, dv, chunk, false));
     return a > b ? a : b;
 }
@@ -33,12 +34,13 @@ size_t prefill_bf16_workspace(int B, int T, int H, int dk, int dv, int chunk) {
 hipError_t launch_prefill_bf16(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                const float *g, const float *beta, const float *s0, float *o,
                                float *s_out, int B, int T, int H, int dk, int dv, int chunk,
-                               bool delta, void *ws, hipStream_t stream) {
+                               bool delta, void *ws, hipStream_t stream, bool tfrag) {
     if (!prefill_bf16_uses_mfma(dk, dv, chunk))
         return launch_prefill_valu(q, k, v, g, beta, s0, o, s_out, B, T, H, dk, dv, chunk, GDN_BF16,
                                    delta, stream);
     return launch_prefill_chunk(q, k, v, g, beta, s0, o, s_out, B, T, H, dk, dv,
-                                prefill_kernel_chunk(dk, dv, chunk, delta), delta, ws, stream);
+                                prefill_kernel_chunk(dk, dv, chunk, delta), delta, ws, stream, nullptr,
+                                tfrag);
 }
 
 }  // namespace gdn

@@ -179,6 +179,10 @@ struct ChunkArgs {
     const float *conv_w;   // [H (2 DK + DV)][4]: q channels, then k, then v (head-major)
     const float *rate, *bias;  // [H] or NULL (1, 0)
     const float *conv_in;  // [B][H (2 DK + DV)][3]: the three raw inputs before t = 0, or NULL
+    // 128 x 128 heads, gated delta rule, dense: the hi/lo A-fragments of T diag(b) of every chunk,
+    // [BH][N][hi/lo x 2 row tiles][64 lanes], written by MAP (whose grid then also covers the
+    // last piece, keyside only) and read by OUT in place of its own keyside; NULL: OUT forms them
+    u16x8 *tfrag;
 };
 
 // Inputs of the preparation done in the chunk loads (PREP), beside the raw projections.
@@ -217,6 +221,10 @@ struct ChunkRegs {
     static constexpr int NK = C * DK / 8 / BLOCK, NV = C * DV / 8 / VTHREADS;
     static_assert(C * DK % (8 * BLOCK) == 0 && C * DV % (8 * VTHREADS) == 0, "rows divide among threads");
     u16x8 k[NK], q[MAP ? 1 : NK], v[NV];
+    // OUT, 128 x 128 heads: the chunk's T diag(b) fragments from MAP (wavefronts 0 and 1: hi, lo
+    // of row tile tid / 64)
+    static constexpr bool TB = !MAP && DK == 128 && C == 32;
+    u16x8 tb[TB ? 2 : 1];
     float g, beta;
     u16x8 halo;  // PREP: one raw vector of the three rows before the chunk (halo threads only)
 };
@@ -256,7 +264,7 @@ __device__ __forceinline__ size_t uniform_u64(size_t x) {
 
 template <int DK, int DV, int C, bool MAP, bool PREP>
 __device__ __forceinline__ void load_chunk(ChunkRegs<DK, DV, C, MAP> &r, const ChunkArgs &a, size_t tok_base,
-                                           int seq_len, int h, int n, int tid) {
+                                           int seq_len, int h, int n, int tid, const u16x8 *tb_src = nullptr) {
     using R = ChunkRegs<DK, DV, C, MAP>;
     // the lane offsets below are cheap to rebuild per chunk; hoisted out of the chunk loop
     // they would hold a dozen registers for its whole length
@@ -285,6 +293,13 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<DK, DV, C, MAP> &r, const C
             const int e = tid + i * R::VTHREADS;
             const int rr = e % C, c8 = e / C;
             r.v[i] = buf_load16(rv, static_cast<unsigned>(rr * a.H * DV + 8 * c8) * 2u);
+        }
+    }
+    if constexpr (R::TB) {
+        if (tb_src != nullptr && tid < 2 * kWave) {
+            const u16x8 *p = tb_src + static_cast<size_t>(n) * (4 * kWave) + 2 * (tid & ~(kWave - 1)) + tid % kWave;
+            r.tb[0] = p[0];
+            r.tb[1] = p[kWave];
         }
     }
     const unsigned rows_g = __builtin_amdgcn_readfirstlane(static_cast<unsigned>((L - 1) * a.H + 1) * 4u);
@@ -416,6 +431,12 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
     // at the occupancy limit already)
     constexpr bool kShareTB = kMergeBC && !PREP;
     __shared__ __align__(16) bf16x8 tbs_s[kShareTB ? 2 * G::CT * kWave : 1];  // (ct * 2 + hi/lo) * 64 + lane
+    // 128 x 128 heads (one workgroup per compute unit, so no other workgroup's work hides OUT's
+    // keyside): MAP stores those fragments and OUT loads them (3B-shaped 64K call 1.56 -> 1.45 ms).
+    // With three workgroups per compute unit the 64 x 64 kernels gain nothing from it (MAP +17 us
+    // for the stores, OUT -20 us).
+    constexpr bool kTfrag = kShareTB && DK == 128 && C == 32;
+    static_assert(!kTfrag || G::CT == 2, "two row tiles of T");
     // PREP: raw rows of the chunk after the three rows before it (row 3 + r holds chunk row r),
     // the per-row partial squares of k, and this head's convolution weights (q, k, v channels)
     constexpr int RKS = DK + 8, RVS = DV + 8;  // raw row strides (16-byte multiples)
@@ -442,6 +463,8 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
     float *map_out = nullptr;         // MAP: piece map [DK][DV + DK]
     float *final_out = nullptr;       // OUT: final state [DK][DV] of the sequence's last piece
     float *states_out = nullptr;      // OUT, dense: this head's chunk start states [N][DK][DV]
+    u16x8 *tb_ptr = nullptr;          // kTfrag: this head's T diag(b) fragments, chunk n at n * 4 * 64
+    bool key_only = false;            // MAP over the last piece (kTfrag): the fragments, no map
     if (a.sq.tok0 == nullptr) {
         const int piece = w / a.BH;
         const size_t bh = w % a.BH;
@@ -451,7 +474,11 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
         seq_len = a.T;
         n0 = piece * a.piece_chunks;
         n1 = min(n0 + a.piece_chunks, a.N);
-        if (MAP) map_out = a.maps + (bh * (a.P - 1) + piece) * DK * G::MAPW;
+        if constexpr (kTfrag) {
+            if (a.tfrag) tb_ptr = a.tfrag + bh * a.N * (4 * kWave);
+        }
+        key_only = MAP && piece >= a.P - 1;
+        if (MAP && !key_only) map_out = a.maps + (bh * (a.P - 1) + piece) * DK * G::MAPW;
         else if (a.s_start) start = a.s_start + (bh * a.P + piece) * DK * DV;
         if (!MAP && piece == a.P - 1) final_out = a.s_final + bh * DK * DV;
         if (!MAP && STATES) states_out = a.chunk_states + bh * a.N * DK * DV;
@@ -557,7 +584,7 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
     R cur;
-    if (n0 < n1) load_chunk<DK, DV, C, MAP, PREP>(cur, a, tok_base, seq_len, h, n0, tid);
+    if (n0 < n1) load_chunk<DK, DV, C, MAP, PREP>(cur, a, tok_base, seq_len, h, n0, tid, tb_ptr);
 
     for (int n = n0; n < n1; ++n) {
         const int t0 = n * C;
@@ -879,10 +906,12 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
                     a_tile(IC<3>{}, IC<2>{});
                 }
             } else if constexpr (kMergeBC) {
-                if (wave == 0) {
-                    a_tile(I0{}, I0{});
-                } else if (wave == 1) {
-                    a_tile(I1{}, I1{});
+                if (!(kTfrag && !MAP && tb_ptr)) {
+                    if (wave == 0) {
+                        a_tile(I0{}, I0{});
+                    } else if (wave == 1) {
+                        a_tile(I1{}, I1{});
+                    }
                 }
             } else {
                 // chunk 32: wavefronts 0 and 1 compute their diagonal tile and go straight on to its
@@ -920,9 +949,27 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
                     lds_slots_f32(&ts[16 * ct + li][0], 0, gq, x);
 #pragma unroll
                     for (int e = 0; e < 8; ++e) x[e] *= b_s[kmap(0, gq, e)];
-                    split_bf16(x, tbs_s[(2 * ct) * kWave + lane], tbs_s[(2 * ct + 1) * kWave + lane]);
+                    bf16x8 hi, lo;
+                    split_bf16(x, hi, lo);
+                    tbs_s[(2 * ct) * kWave + lane] = hi;
+                    tbs_s[(2 * ct + 1) * kWave + lane] = lo;
+                    if constexpr (kTfrag && MAP) {
+                        if (tb_ptr) {
+                            u16x8 *d = tb_ptr + static_cast<size_t>(n) * (4 * kWave) + (2 * ct) * kWave + lane;
+                            d[0] = __builtin_bit_cast(u16x8, hi);
+                            d[kWave] = __builtin_bit_cast(u16x8, lo);
+                        }
+                    }
                 };
-                if (wave == 0) {
+                if (kTfrag && !MAP && tb_ptr) {
+                    // the fragments MAP stored for this chunk, loaded with its rows
+                    if constexpr (ChunkRegs<DK, DV, C, MAP>::TB) {
+                        if (wave < 2) {
+                            tbs_s[(2 * wave) * kWave + lane] = __builtin_bit_cast(bf16x8, cur.tb[0]);
+                            tbs_s[(2 * wave + 1) * kWave + lane] = __builtin_bit_cast(bf16x8, cur.tb[1]);
+                        }
+                    }
+                } else if (wave == 0) {
                     inv_diag(0);
                     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
                     __hip_atomic_store(&t00_ready, n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -1167,7 +1214,8 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
         }
 
         // next chunk's rows: loads in flight during this chunk's slice work
-        if (n + 1 < n1) load_chunk<DK, DV, C, MAP, PREP>(cur, a, tok_base, seq_len, h, n + 1, tid);
+        if (n + 1 < n1) load_chunk<DK, DV, C, MAP, PREP>(cur, a, tok_base, seq_len, h, n + 1, tid, tb_ptr);
+        if (MAP && key_only) continue;
 
         // ---- G: per slice: U = (T diag b) V, Delta = U - W St (chunk 32: Delta = T diag(b) R,
         // R = V - diag(exp G) K St), outputs, state update
@@ -1372,6 +1420,7 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
     }
 
     // ---- results
+    if (MAP && key_only) return;
 #pragma unroll
     for (int j = 0; j < G::SPW; ++j) {
         const int sl = wave + G::WAVES * j;
@@ -1637,21 +1686,28 @@ PiecePlan piece_plan(int BH, int N, int slots) {
     return {(N + pc - 1) / pc, pc};
 }
 
+// Workspace of a dense call: the piece maps, the piece start states and (tfrag: 128 x 128 heads,
+// gated delta rule) the T diag(b) fragments of every chunk, 4 KiB each.
 template <int DK, int DV, int C>
-size_t chunk_ws_bytes(int B, int T, int H) {
+constexpr bool kTfragPlan = DK == 128 && DV == 128 && C == 32;
+inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+template <int DK, int DV, int C>
+size_t chunk_ws_bytes(int B, int T, int H, bool tfrag) {
     const int N = (T + C - 1) / C;
     const int BH = B * H;
     const int P = piece_plan(BH, N, kPlanSlots<DK, DV, C>).P;
     if (P == 1) return 0;
     const size_t maps = static_cast<size_t>(BH) * (P - 1) * DK * (DV + DK) * 4;
     const size_t starts = static_cast<size_t>(BH) * P * DK * DV * 4;
-    return ((maps + 255) & ~static_cast<size_t>(255)) + starts;
+    if (tfrag && kTfragPlan<DK, DV, C>) return align256(maps) + align256(starts) + static_cast<size_t>(BH) * N * 4096;
+    return align256(maps) + starts;
 }
 
 template <int DK, int DV, int C, bool DELTA, bool PREP = false>
 hipError_t run_chunk(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,
                      const float *beta, const float *s0, float *o, float *s_out, int B, int T, int H,
-                     void *ws, hipStream_t stream, float *chunk_states = nullptr, const PrepIn *pin = nullptr) {
+                     void *ws, hipStream_t stream, float *chunk_states = nullptr, const PrepIn *pin = nullptr,
+                     bool tfrag = false) {
     const int N = (T + C - 1) / C;
     const int BH = B * H;
     const PiecePlan plan = piece_plan(BH, N, kPlanSlots<DK, DV, C>);
@@ -1688,12 +1744,17 @@ hipError_t run_chunk(const uint16_t *q, const uint16_t *k, const uint16_t *v, co
         return launch_out(BH);
     }
     const size_t maps_bytes = static_cast<size_t>(BH) * (P - 1) * DK * (DV + DK) * 4;
+    const size_t starts_bytes = static_cast<size_t>(BH) * P * DK * DV * 4;
     float *maps = static_cast<float *>(ws);
-    float *starts = reinterpret_cast<float *>(static_cast<char *>(ws) +
-                                              ((maps_bytes + 255) & ~static_cast<size_t>(255)));
+    float *starts = reinterpret_cast<float *>(static_cast<char *>(ws) + align256(maps_bytes));
     a.maps = maps;
     a.items = BH * (P - 1);
-    hipLaunchKernelGGL((chunk_kernel<DK, DV, C, true, DELTA, false, PREP>), grid(BH * (P - 1)), dim3(kWave * kWavesOf<DK, DV>), 0, stream, a);
+    if (tfrag && DELTA && !PREP && kTfragPlan<DK, DV, C> && !chunk_states) {
+        // MAP also covers the last piece, keyside only, so OUT finds every chunk's fragments
+        a.tfrag = reinterpret_cast<u16x8 *>(static_cast<char *>(ws) + align256(maps_bytes) + align256(starts_bytes));
+        a.items = BH * P;
+    }
+    hipLaunchKernelGGL((chunk_kernel<DK, DV, C, true, DELTA, false, PREP>), grid(a.items), dim3(kWave * kWavesOf<DK, DV>), 0, stream, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL((chain_kernel<DK, DV>), dim3(BH * (DV / 16)), dim3(kWave * (DK / 32)), 0, stream,
@@ -1890,9 +1951,9 @@ hipError_t launch_prepare_prefill(const uint16_t *xq, const uint16_t *xk, const 
     return err;
 }
 
-size_t prefill_chunk_workspace(int B, int T, int H, int dk, int dv, int chunk) {
+size_t prefill_chunk_workspace(int B, int T, int H, int dk, int dv, int chunk, bool tfrag) {
 #define GDN_WS(DK_, DV_, C_) \
-    if (dk == DK_ && dv == DV_ && chunk == C_) return chunk_ws_bytes<DK_, DV_, C_>(B, T, H);
+    if (dk == DK_ && dv == DV_ && chunk == C_) return chunk_ws_bytes<DK_, DV_, C_>(B, T, H, tfrag);
     GDN_CHUNK_CASES(GDN_WS)
 #undef GDN_WS
     return 0;
@@ -1901,11 +1962,11 @@ size_t prefill_chunk_workspace(int B, int T, int H, int dk, int dv, int chunk) {
 hipError_t launch_prefill_chunk(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                 const float *g, const float *beta, const float *s0, float *o,
                                 float *s_out, int B, int T, int H, int dk, int dv, int chunk,
-                                bool delta, void *ws, hipStream_t stream, float *chunk_states) {
+                                bool delta, void *ws, hipStream_t stream, float *chunk_states, bool tfrag) {
 #define GDN_RUN(DK_, DV_, C_)                                                                      \
     if (dk == DK_ && dv == DV_ && chunk == C_)                                                     \
         return delta ? run_chunk<DK_, DV_, C_, true>(q, k, v, g, beta, s0, o, s_out, B, T, H, ws, stream,  \
-                                                     chunk_states)                                         \
+                                                     chunk_states, nullptr, tfrag)                         \
                      : run_chunk<DK_, DV_, C_, false>(q, k, v, g, beta, s0, o, s_out, B, T, H, ws, stream, \
                                                       chunk_states);
     GDN_CHUNK_CASES(GDN_RUN)

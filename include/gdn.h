@@ -158,7 +158,13 @@ GDN_API gdn_status gdn_chunk_prefill_rule(gdn_rule rule,
 /*
  * Bytes of device scratch gdn_chunk_prefill needs for these sizes (0 if
  * none); the same size serves gdn_chunk_prefill_rule with either rule.
- * Returns 0 as well for arguments gdn_chunk_prefill would reject.
+ * Returns 0 as well for arguments gdn_chunk_prefill would reject.  It holds
+ * the maps and start states of the sequence pieces (bounded by the chip's
+ * workgroup slots, not by T) and, for d_k = d_v = 128, every chunk's
+ * T diag(b) (T the inverse of the chunk's unit lower-triangular system of
+ * the chunked rule, kept as hi/lo bf16 operand fragments: 4 KiB per 32-token
+ * chunk and head), formed once in the pieces' first pass and read in the
+ * second.
  */
 GDN_API size_t gdn_chunk_prefill_workspace_size(int B, int T, int H, int d_k, int d_v, int chunk,
                                         gdn_dtype qkv_dtype);
@@ -172,10 +178,13 @@ GDN_API size_t gdn_chunk_prefill_workspace_size(int B, int T, int H, int d_k, in
  * library holds from the first call on that GPU until the process ends.
  *
  * Arguments, layouts, results and errors are those of gdn_chunk_prefill_rule
- * without the workspace; GDN_ERR_WORKSPACE means that
- * gdn_chunk_prefill_workspace_size(...) exceeds GDN_NOALLOC_SCRATCH_BYTES
- * (no dense call does today: the piece plan bounds that size by the chip's
- * workgroup slots, not by T; the largest, 128-wide heads, need about 50 MiB).
+ * without the workspace; GDN_ERR_WORKSPACE means that the pieces' maps and
+ * start states exceed GDN_NOALLOC_SCRATCH_BYTES (no dense call does today: the
+ * piece plan bounds them by the chip's workgroup slots, not by T; the largest,
+ * 128-wide heads, need about 50 MiB).  The per-chunk T diag(b) fragments that
+ * gdn_chunk_prefill_workspace_size also counts for 128-wide heads are not
+ * kept here: this call forms them again in the second pass, with the same
+ * results.
  * Every call on one GPU uses that GPU's single array: calls that may overlap
  * in time on one GPU (different streams, or threads) race on it and must be
  * ordered by the caller.  Nothing in the array needs clearing between calls

@@ -104,7 +104,10 @@ def test_workspace_size():
     # [DK][DV+DK] and start states [DK][DV], fp32, a few tens of MB at most
     w = gdn.gdn_chunk_prefill_workspace_size(1, 65536, 32, 64, 64, 64, BF16)
     assert 0 < w < 64 << 20
-    assert gdn.gdn_chunk_prefill_workspace_size(1, 65536, 24, 128, 128, 64, BF16) < 256 << 20
+    # 128-wide heads also keep every chunk's T diag(b) fragments: 4 KiB per 32-token chunk and head
+    # (10 pieces of 205 chunks for 24 heads)
+    maps, starts = 24 * 9 * 128 * 256 * 4, 24 * 10 * 128 * 128 * 4
+    assert gdn.gdn_chunk_prefill_workspace_size(1, 65536, 24, 128, 128, 64, BF16) == maps + starts + 24 * 2048 * 4096
     # fp32 inputs and the VALU shapes need none
     assert gdn.gdn_chunk_prefill_workspace_size(1, 64, 2, 16, 16, 16, F32) == 0
     assert gdn.gdn_chunk_prefill_workspace_size(1, 65536, 2, 64, 64, 16, BF16) == 0

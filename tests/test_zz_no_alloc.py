@@ -3,7 +3,10 @@
 Called through the C ABI, it must give what gdn_chunk_prefill_rule gives with a
 workspace of the caller's: the same kernels run on the same piece plan, so the
 outputs and final states agree bit for bit (and so within the bf16 bar of the
-oracle parity tests).  Two calls in a row share the one static scratch array;
+oracle parity tests).  For 128-wide heads under the gated delta rule the call
+with a workspace keeps every chunk's T diag(b) fragments there and its second
+pass reads them, where this call forms them again: the same arithmetic, so
+still bit for bit.  Two calls in a row share the one static scratch array;
 the second is smaller than the first, so it runs over the first call's leftover
 maps and start states."""
 import pytest
