@@ -272,6 +272,12 @@ gdn_status check_not_capturing(hipStream_t stream) {
 }
 
 bool varlen_supported(int d_k, int d_v, int chunk, gdn_dtype dt) {
+    return (dt == GDN_BF16 || dt == GDN_F32) && supported_dim(d_k) && supported_dim(d_v) && supported_chunk(chunk);
+}
+
+// bf16 inputs at the MFMA shapes run the chunk kernels with sequence pieces; fp32 inputs and the
+// 16-wide shapes the fp32 VALU kernel, one workgroup per sequence, head and 16 value columns
+bool varlen_mfma(int d_k, int d_v, int chunk, gdn_dtype dt) {
     return dt == GDN_BF16 && prefill_bf16_uses_mfma(d_k, d_v, chunk);
 }
 
@@ -281,6 +287,7 @@ size_t gdn_chunk_prefill_varlen_workspace_size(const int32_t *cu_seqlens, int S,
                                                int chunk, gdn_dtype qkv_dtype) {
     if (S <= 0 || H <= 0 || !cu_seqlens || !varlen_supported(d_k, d_v, chunk, qkv_dtype)) return 0;
     if (check_varlen_batch(cu_seqlens, S, cu_seqlens[S], nullptr, S) != GDN_OK) return 0;
+    if (!varlen_mfma(d_k, d_v, chunk, qkv_dtype)) return prefill_valu_varlen_workspace(S);
     // either rule (the size query takes no rule): the larger of the two plans
     size_t bytes = 0;
     for (bool delta : {true, false}) {
@@ -324,9 +331,15 @@ gdn_status gdn_chunk_prefill_varlen(gdn_rule rule, const void *q, const void *k,
         if (overlap(s_o, in) || overlap(s_p, in)) return GDN_ERR_ALIAS;
     if (overlap(s_o, s_p)) return GDN_ERR_ALIAS;
 
-    const int kchunk = prefill_kernel_chunk(d_k, d_v, chunk, rule == GDN_RULE_GATED_DELTA);
-    VarlenLayout L;
-    if (!varlen_layout(cu_seqlens, S, H, d_k, d_v, kchunk, &L)) return GDN_ERR_SHAPE;
+    if (prod({S, H, 16}) > 0x7fffffffULL) return GDN_ERR_SHAPE;  // the VALU kernel's grid
+    const bool mfma = varlen_mfma(d_k, d_v, chunk, qkv_dtype);
+    const int kchunk = mfma ? prefill_kernel_chunk(d_k, d_v, chunk, rule == GDN_RULE_GATED_DELTA) : chunk;
+    VarlenLayout L{};
+    if (mfma) {
+        if (!varlen_layout(cu_seqlens, S, H, d_k, d_v, kchunk, &L)) return GDN_ERR_SHAPE;
+    } else {
+        L.bytes = prefill_valu_varlen_workspace(S);
+    }
     if (!workspace || workspace_bytes < L.bytes) return GDN_ERR_WORKSPACE;
     const Span s_ws = span(workspace, L.bytes);
     const Span all[] = {s_q, s_k, s_v, s_g, s_b, s_o, s_p};
@@ -335,10 +348,14 @@ gdn_status gdn_chunk_prefill_varlen(gdn_rule rule, const void *q, const void *k,
     st = check_not_capturing(static_cast<hipStream_t>(stream));
     if (st != GDN_OK) return st;
 
-    const hipError_t err = launch_prefill_chunk_varlen(
-        static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k), static_cast<const uint16_t *>(v), g,
-        beta, cu_seqlens, S, slots, has_initial, state_pool, o, H, d_k, d_v, kchunk,
-        rule == GDN_RULE_GATED_DELTA, workspace, static_cast<hipStream_t>(stream));
+    const hipError_t err =
+        mfma ? launch_prefill_chunk_varlen(static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
+                                           static_cast<const uint16_t *>(v), g, beta, cu_seqlens, S, slots,
+                                           has_initial, state_pool, o, H, d_k, d_v, kchunk,
+                                           rule == GDN_RULE_GATED_DELTA, workspace, static_cast<hipStream_t>(stream))
+             : launch_prefill_valu_varlen(q, k, v, g, beta, cu_seqlens, S, slots, has_initial, state_pool, o, H,
+                                          d_k, d_v, chunk, qkv_dtype, rule == GDN_RULE_GATED_DELTA, workspace,
+                                          static_cast<hipStream_t>(stream));
     return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 

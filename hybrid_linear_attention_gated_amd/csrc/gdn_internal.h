@@ -51,6 +51,13 @@ hipError_t launch_prefill_valu(const void *q, const void *k, const void *v, cons
                                const float *beta, const float *s0, float *o, float *s_out, int B,
                                int T, int H, int dk, int dv, int chunk, gdn_dtype dt,
                                bool delta, hipStream_t stream, float *chunk_states = nullptr);
+// The same for packed sequences (cu, slots, init: host arrays as for the MFMA packed path); the
+// workspace holds a table of prefill_valu_varlen_workspace(S) bytes built from them.
+size_t prefill_valu_varlen_workspace(int S);
+hipError_t launch_prefill_valu_varlen(const void *q, const void *k, const void *v, const float *g,
+                                      const float *beta, const int *cu, int S, const int *slots,
+                                      const int *init, float *pool, float *o, int H, int dk, int dv, int chunk,
+                                      gdn_dtype dt, bool delta, void *ws, hipStream_t stream);
 
 // bf16 inputs: chunked prefill with bf16 MFMA contractions.
 bool prefill_bf16_uses_mfma(int dk, int dv, int chunk);

@@ -25,6 +25,10 @@
 // Work layout: one workgroup per (sequence, head, 16-wide value slice);
 // value columns of the state evolve independently, so slices never talk.
 // Chunks run in order inside the workgroup with the state slice in LDS.
+// Packed sequences (seqs != NULL) take the same layout with each sequence's
+// token range and pool slot from a device table.
+#include <vector>
+
 #include "gdn_internal.h"
 
 namespace gdn {
@@ -33,12 +37,20 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kSW = 16;  // value columns per workgroup
 
+// Packed sequences for this kernel: S sequences, table [4][S] of ints (first token, length, pool
+// slot or -1, start from the stored state), states in pool [slots][H][DK][DV].
+struct ValuSeqs {
+    const int *table;
+    int S;
+    float *pool;
+};
+
 template <int DK, int C, typename TIn, bool DELTA>
 __global__ __launch_bounds__(kThreads) void prefill_valu_kernel(
     const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, const float *__restrict__ s0,
-    float *__restrict__ o, float *__restrict__ s_out, float *__restrict__ chunk_states, int T, int H,
-    int DV, float scale) {
+    float *__restrict__ o, float *__restrict__ s_out, float *__restrict__ chunk_states, int T_dense, int H,
+    int DV, float scale, ValuSeqs sq) {
     __shared__ float A[C][C + 1];   // A, then the intra-chunk output weights P
     __shared__ float Tm[C][C + 1];  // (I + A)^{-1}
     __shared__ float St[DK][kSW];
@@ -51,13 +63,27 @@ __global__ __launch_bounds__(kThreads) void prefill_valu_kernel(
     const int nslices = DV / kSW;
     const int slice = blockIdx.x % nslices;
     const int h = (blockIdx.x / nslices) % H;
-    const int b = blockIdx.x / (nslices * H);
+    const int b = blockIdx.x / (nslices * H);  // sequence
     const int col0 = slice * kSW;
     const size_t bh = static_cast<size_t>(b) * H + h;
+    // the sequence's first token in the [tokens, H, d] layout, its length, and the state it starts
+    // from (NULL = zeros) and ends in (NULL = dropped)
+    size_t tok_base = static_cast<size_t>(b) * T_dense;
+    int T = T_dense;
+    const float *start = s0 ? s0 + bh * DK * DV : nullptr;
+    float *fin = s_out ? s_out + bh * DK * DV : nullptr;
+    if (sq.table) {
+        tok_base = static_cast<size_t>(sq.table[b]);
+        T = sq.table[sq.S + b];
+        const int slot = sq.table[2 * sq.S + b];
+        float *st = slot >= 0 ? sq.pool + (static_cast<size_t>(slot) * H + h) * DK * DV : nullptr;
+        start = sq.table[3 * sq.S + b] ? st : nullptr;
+        fin = st;
+    }
 
     for (int e = tid; e < DK * kSW; e += kThreads) {
         const int m = e / kSW, c = e % kSW;
-        St[m][c] = s0 ? s0[(bh * DK + m) * DV + col0 + c] : 0.f;
+        St[m][c] = start ? start[m * DV + col0 + c] : 0.f;
     }
 
     for (int t0 = 0; t0 < T; t0 += C) {
@@ -66,8 +92,8 @@ __global__ __launch_bounds__(kThreads) void prefill_valu_kernel(
             float *cs = chunk_states + (bh * ((T + C - 1) / C) + t0 / C) * DK * DV;
             for (int e = tid; e < DK * kSW; e += kThreads) cs[(e / kSW) * DV + col0 + e % kSW] = St[e / kSW][e % kSW];
         }
-        // rows of token t of this (b, h): index (b*T + t)*H + h
-        auto row = [&](int r) { return (static_cast<size_t>(b) * T + t0 + r) * H + h; };
+        // rows of token t of this (sequence, h): index (first token + t)*H + h
+        auto row = [&](int r) { return (tok_base + t0 + r) * H + h; };
 
         if (tid < L) bet[tid] = beta[row(tid)];
         if (tid == 0) {
@@ -161,37 +187,42 @@ __global__ __launch_bounds__(kThreads) void prefill_valu_kernel(
         __syncthreads();
     }
 
-    for (int e = tid; e < DK * kSW; e += kThreads) {
-        const int m = e / kSW, c = e % kSW;
-        s_out[(bh * DK + m) * DV + col0 + c] = St[m][c];
+    if (fin) {
+        // every thread reads only its own columns of the start state above (and that before the
+        // chunk loop's barriers), so writing the final state over it in place is safe
+        for (int e = tid; e < DK * kSW; e += kThreads) {
+            const int m = e / kSW, c = e % kSW;
+            fin[m * DV + col0 + c] = St[m][c];
+        }
     }
 }
 
 template <int DK, int C, typename TIn>
 hipError_t launch_valu_t(const void *q, const void *k, const void *v, const float *g,
                          const float *beta, const float *s0, float *o, float *s_out, float *chunk_states,
-                         int B, int T, int H, int dv, bool delta, hipStream_t stream) {
-    const int blocks = B * H * (dv / kSW);
+                         int B, int T, int H, int dv, bool delta, hipStream_t stream, ValuSeqs sq) {
+    const int blocks = B * H * (dv / kSW);  // B: sequences
     const float scale = 1.0f / sqrtf(static_cast<float>(DK));
     if (delta)
         hipLaunchKernelGGL((prefill_valu_kernel<DK, C, TIn, true>), dim3(blocks), dim3(kThreads), 0,
                            stream, static_cast<const TIn *>(q), static_cast<const TIn *>(k),
-                           static_cast<const TIn *>(v), g, beta, s0, o, s_out, chunk_states, T, H, dv, scale);
+                           static_cast<const TIn *>(v), g, beta, s0, o, s_out, chunk_states, T, H, dv, scale, sq);
     else
         hipLaunchKernelGGL((prefill_valu_kernel<DK, C, TIn, false>), dim3(blocks), dim3(kThreads), 0,
                            stream, static_cast<const TIn *>(q), static_cast<const TIn *>(k),
-                           static_cast<const TIn *>(v), g, beta, s0, o, s_out, chunk_states, T, H, dv, scale);
+                           static_cast<const TIn *>(v), g, beta, s0, o, s_out, chunk_states, T, H, dv, scale, sq);
     return hipGetLastError();
 }
 
 template <typename TIn>
 hipError_t dispatch_valu(const void *q, const void *k, const void *v, const float *g,
                          const float *beta, const float *s0, float *o, float *s_out, float *chunk_states,
-                         int B, int T, int H, int dk, int dv, int chunk, bool delta, hipStream_t stream) {
+                         int B, int T, int H, int dk, int dv, int chunk, bool delta, hipStream_t stream,
+                         ValuSeqs sq = ValuSeqs{}) {
 #define GDN_VALU(DK_, C_)                                                                         \
     if (dk == DK_ && chunk == C_)                                                                 \
         return launch_valu_t<DK_, C_, TIn>(q, k, v, g, beta, s0, o, s_out, chunk_states, B, T, H, dv, delta, \
-                                           stream);
+                                           stream, sq);
     GDN_VALU(16, 16) GDN_VALU(16, 32) GDN_VALU(16, 64)
     GDN_VALU(64, 16) GDN_VALU(64, 32) GDN_VALU(64, 64)
     GDN_VALU(128, 16) GDN_VALU(128, 32) GDN_VALU(128, 64)
@@ -210,6 +241,31 @@ hipError_t launch_prefill_valu(const void *q, const void *k, const void *v, cons
                                        delta, stream);
     return dispatch_valu<float>(q, k, v, g, beta, s0, o, s_out, chunk_states, B, T, H, dk, dv, chunk, delta,
                                 stream);
+}
+
+size_t prefill_valu_varlen_workspace(int S) { return S > 0 ? (static_cast<size_t>(4) * S * 4 + 255) & ~static_cast<size_t>(255) : 0; }
+
+hipError_t launch_prefill_valu_varlen(const void *q, const void *k, const void *v, const float *g,
+                                      const float *beta, const int *cu, int S, const int *slots,
+                                      const int *init, float *pool, float *o, int H, int dk, int dv, int chunk,
+                                      gdn_dtype dt, bool delta, void *ws, hipStream_t stream) {
+    if (S <= 0) return hipSuccess;
+    // the table [4][S]: first token, length, slot (-1: none), start from the stored state
+    std::vector<int> t(static_cast<size_t>(4) * S);
+    for (int s = 0; s < S; ++s) {
+        t[s] = cu[s];
+        t[S + s] = cu[s + 1] - cu[s];
+        t[2 * S + s] = slots ? slots[s] : s;
+        t[3 * S + s] = init ? (init[s] != 0) : 1;
+    }
+    hipError_t err = hipMemcpyAsync(ws, t.data(), t.size() * sizeof(int), hipMemcpyHostToDevice, stream);
+    if (err != hipSuccess) return err;
+    const ValuSeqs sq{static_cast<const int *>(ws), S, pool};
+    if (dt == GDN_BF16)
+        return dispatch_valu<uint16_t>(q, k, v, g, beta, nullptr, o, nullptr, nullptr, S, 0, H, dk, dv, chunk,
+                                       delta, stream, sq);
+    return dispatch_valu<float>(q, k, v, g, beta, nullptr, o, nullptr, nullptr, S, 0, H, dk, dv, chunk, delta,
+                                stream, sq);
 }
 
 }  // namespace gdn

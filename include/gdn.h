@@ -262,9 +262,9 @@ GDN_API gdn_status gdn_decode_step_slots(gdn_rule rule,
  * runtime keeps a fixed-size state per request, ftxj.github.io digest of
  * arXiv 2604.24715, Key Ideas).
  *
- *   q, k           [T_total, H, d_k] bf16 (sequence s = tokens cu_seqlens[s] ..
+ *   q, k           [T_total, H, d_k] qkv_dtype (sequence s = tokens cu_seqlens[s] ..
  *                  cu_seqlens[s+1]-1)
- *   v              [T_total, H, d_v] bf16
+ *   v              [T_total, H, d_v] qkv_dtype
  *   g, beta        [T_total, H] fp32
  *   cu_seqlens     HOST array [S + 1]: 0 = cu[0] <= cu[1] <= ... <= cu[S] = T_total
  *                  (empty sequences allowed)
@@ -278,8 +278,11 @@ GDN_API gdn_status gdn_decode_step_slots(gdn_rule rule,
  *                  0 = start from zeros (a new request)
  *   o              [T_total, H, d_v] fp32, written
  *   workspace      at least gdn_chunk_prefill_varlen_workspace_size(...) bytes
- * Supported: qkv_dtype GDN_BF16, d_k and d_v in {64, 128}, chunk in {32, 64};
- * both rules.  The host arrays are read during the call only: the call turns
+ * Supported: the sizes and types of gdn_chunk_prefill, both rules.  bf16 q/k/v
+ * with d_k, d_v in {64, 128} and chunk in {32, 64} run the MFMA chunk kernels,
+ * long sequences split into pieces; fp32 q/k/v and the 16-wide shapes run the
+ * fp32 VALU chunk kernel, one workgroup per sequence, head and 16 value
+ * columns (as the dense call does for them).  The host arrays are read during the call only: the call turns
  * them into a table that one host-to-device copy on `stream` puts into the
  * workspace.  A graph recorded from that copy would keep a pointer to host
  * memory that is gone once the call returns, so the call refuses a stream that

@@ -168,7 +168,9 @@ def test_varlen_validation():
                                             None if init is None else init.ctypes.data, o, 2, dk, dv, chunk, dt,
                                             ws, ws_bytes, None)
     assert call(rule=4) == UNSUP
-    assert call(dt=F32) == UNSUP and call(dk=16) == UNSUP and call(chunk=16) == UNSUP
+    assert call(dt=7) == UNSUP and call(dk=32) == UNSUP and call(chunk=8) == UNSUP
+    # fp32 q/k/v and the 16-wide shapes go to the VALU kernel, whose workspace is a 4 x S int table
+    assert call(dt=F32, ws_bytes=255) == WS and call(dk=16, chunk=16, ws=None) == WS
     assert call(T=351) == SHAPE                                   # offsets must end at T_total
     assert call(cu=np.array([0, 100, 90, 350], dtype=np.int32)) == SHAPE  # decreasing offsets
     assert call(cu=np.array([5, 100, 350], dtype=np.int32)) == SHAPE      # must start at 0
@@ -181,7 +183,9 @@ def test_varlen_validation():
     assert call(o=addr(0)) == ALIAS and call(pool=addr(4)) == ALIAS
     need = gdn.gdn_chunk_prefill_varlen_workspace_size(cu.ctypes.data, 3, 2, 64, 64, 64, BF16)
     assert 0 < need < 1 << 20
-    assert gdn.gdn_chunk_prefill_varlen_workspace_size(cu.ctypes.data, 3, 2, 16, 64, 64, BF16) == 0
+    assert gdn.gdn_chunk_prefill_varlen_workspace_size(cu.ctypes.data, 3, 2, 16, 64, 64, BF16) == 256
+    assert gdn.gdn_chunk_prefill_varlen_workspace_size(cu.ctypes.data, 3, 2, 64, 64, 64, F32) == 256
+    assert gdn.gdn_chunk_prefill_varlen_workspace_size(cu.ctypes.data, 3, 2, 32, 64, 64, F32) == 0
     assert call(cu=np.array([0], dtype=np.int32), T=0) == OK      # no sequences: nothing to do
 
 
