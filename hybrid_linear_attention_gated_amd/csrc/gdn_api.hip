@@ -71,7 +71,7 @@ bool prepare_decode_supported(int dk, int dv);
 hipError_t launch_prepare_decode(const void *xq, const void *xk, const void *xv, const float *w,
                                  const float *a_raw, const float *b_raw, const float *rate,
                                  const float *bias, float *conv_state, float *state, float *o, int N,
-                                 int H, gdn_dtype dt, bool delta, hipStream_t stream);
+                                 int H, int d, gdn_dtype dt, bool delta, hipStream_t stream);
 
 }  // namespace gdn
 
@@ -455,7 +455,7 @@ gdn_status gdn_prepare_decode_step(gdn_rule rule, const void *xq, const void *xk
             if (overlap(out[i], x)) return GDN_ERR_ALIAS;
     }
     const hipError_t err = launch_prepare_decode(xq, xk, xv, conv_weight, a_raw, b_raw, decay_rate, gate_bias,
-                                                 conv_state, state, o, N, H, x_dtype,
+                                                 conv_state, state, o, N, H, d_k, x_dtype,
                                                  rule == GDN_RULE_GATED_DELTA, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }

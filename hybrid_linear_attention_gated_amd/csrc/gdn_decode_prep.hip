@@ -18,10 +18,15 @@
 // 2604.24715, Method); the update is the decode step of the gated delta rule
 // (or the gated-decay rule without the erase term).
 //
-// Layout: d_k = d_v = 64.  Workgroup = 2 wavefronts = one (sequence, head).
+// Layout, d_k = d_v = 64: workgroup = 2 wavefronts = one (sequence, head).
 // Wavefront 0 prepares the q and v channels, wavefront 1 the two gates and the
 // k channels (one channel per lane); then each wavefront updates one 32-column
 // half of the state (32 state floats per lane, as the decode kernel).
+// d_k = d_v = 128: workgroup = 4 wavefronts.  Wavefronts 0-1 prepare the q and
+// v channels, 2-3 the k channels and the gates (each head's q and k norm adds
+// two wavefronts' partial sums through LDS); then, as the decode kernel does
+// for these states, each wavefront takes 32 key rows of whole 128-column rows
+// (64 state floats per lane) and the four add their partial u, p through LDS.
 #include "gdn_internal.h"
 
 namespace gdn {
@@ -134,17 +139,125 @@ __global__ __launch_bounds__(2 * kWave) void prep_decode_kernel(PrepDecodeArgs a
         __builtin_nontemporal_store(av * s[m] + delta * ks[row0 + m], reinterpret_cast<f32x4 *>(st + (row0 + m) * kD + col));
 }
 
+// d_k = d_v = 128 (layout above)
+constexpr int kD2 = 128;
+constexpr int kLPR2 = kD2 / 4;          // lanes per key row: whole 128-column rows
+constexpr int kRG2 = kWave / kLPR2;     // 2 key-row groups per wavefront
+constexpr int kRows2 = 32 / kRG2;       // 16 key rows per lane (32 per wavefront)
+
+template <typename TIn, bool DELTA>
+__global__ __launch_bounds__(4 * kWave) void prep_decode_kernel128(PrepDecodeArgs a) {
+    __shared__ float qs[kD2], ks[kD2], vs[kD2], gb[2], nrm[4];
+    __shared__ f32x4 xu[4][kLPR2], xp[4][kLPR2];
+    __shared__ float xkq[4];
+    const size_t nh = blockIdx.x;  // n * H + h
+    const int n = static_cast<int>(nh / a.H), h = static_cast<int>(nh % a.H);
+    const int tid = static_cast<int>(threadIdx.x);
+    const int wave = tid / kWave, lane = tid % kWave;
+    const int HK = a.H * kD2, C = 3 * HK;
+    float *cs = a.conv_state + static_cast<size_t>(n) * C * 3;
+
+    // ---- preparation: threads 0-127 a q and a v channel, 128-255 a k channel
+    const int ch = tid % kD2;
+    float y;  // q (threads < 128) or k, before the norm
+    if (tid < kD2) {
+        const int cq = h * kD2 + ch, cv = 2 * HK + h * kD2 + ch;
+        y = conv_silu(a.w + static_cast<size_t>(cq) * 4, cs + static_cast<size_t>(cq) * 3,
+                      load_in(static_cast<const TIn *>(a.xq), nh * kD2 + ch));
+        vs[ch] = conv_silu(a.w + static_cast<size_t>(cv) * 4, cs + static_cast<size_t>(cv) * 3,
+                           load_in(static_cast<const TIn *>(a.xv), nh * kD2 + ch));
+    } else {
+        if (tid == kD2) {
+            const float z = a.a_raw[nh] + (a.bias ? a.bias[h] : 0.f);
+            const float sp = fmaxf(z, 0.f) + log1pf(expf(-fabsf(z)));
+            gb[0] = -(a.rate ? a.rate[h] : 1.f) * sp;
+            gb[1] = 1.f / (1.f + expf(-a.b_raw[nh]));
+        }
+        const int ck = HK + h * kD2 + ch;
+        y = conv_silu(a.w + static_cast<size_t>(ck) * 4, cs + static_cast<size_t>(ck) * 3,
+                      load_in(static_cast<const TIn *>(a.xk), nh * kD2 + ch));
+    }
+    const float part = wave_sum(y * y);
+    if (lane == 0) nrm[wave] = part;
+    __syncthreads();
+    const int w0 = wave & ~1;  // the two wavefronts of this tensor, added in one order
+    const float rn = __builtin_amdgcn_rsqf(nrm[w0] + nrm[w0 + 1] + kEps);
+    if (tid < kD2) qs[ch] = y * rn;
+    else ks[ch] = y * rn;
+    __syncthreads();
+
+    // ---- the decode step: this wavefront's 32 key rows of whole 128-column rows
+    const int c = lane % kLPR2, rg = lane / kLPR2;
+    const int col = 4 * c, row0 = wave * 32 + rg * kRows2;
+    const float ga = gb[0], b = gb[1];
+    const float av = __expf(ga);
+    float *st = a.state + nh * kD2 * kD2;
+    f32x4 s[kRows2];
+#pragma unroll
+    for (int m = 0; m < kRows2; ++m)
+        s[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(st + (row0 + m) * kD2 + col));
+    f32x4 u = {0.f, 0.f, 0.f, 0.f}, p = {0.f, 0.f, 0.f, 0.f};
+    float kq = 0.f;
+#pragma unroll
+    for (int m = 0; m < kRows2; ++m) {
+        const float kr = ks[row0 + m], qr = qs[row0 + m];
+        u += s[m] * kr;
+        p += s[m] * qr;
+        kq += kr * qr;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        u[e] += __shfl_xor(u[e], kLPR2, kWave);
+        p[e] += __shfl_xor(p[e], kLPR2, kWave);
+    }
+    kq += __shfl_xor(kq, kLPR2, kWave);
+    // the other wavefronts' key rows, through LDS; every wavefront adds them in one order
+    if (rg == 0) {
+        xu[wave][c] = u;
+        xp[wave][c] = p;
+        if (c == 0) xkq[wave] = kq;
+    }
+    __syncthreads();
+    u = xu[0][c];
+    p = xp[0][c];
+    kq = xkq[0];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) {
+        u += xu[w][c];
+        p += xp[w][c];
+        kq += xkq[w];
+    }
+    const f32x4 vv = {vs[col], vs[col + 1], vs[col + 2], vs[col + 3]};
+    const f32x4 delta = DELTA ? b * (vv - av * u) : b * vv;
+    if (wave == 0 && rg == 0) *reinterpret_cast<f32x4 *>(a.o + nh * kD2 + col) = a.scale * (av * p + delta * kq);
+#pragma unroll
+    for (int m = 0; m < kRows2; ++m)
+        __builtin_nontemporal_store(av * s[m] + delta * ks[row0 + m],
+                                    reinterpret_cast<f32x4 *>(st + (row0 + m) * kD2 + col));
+}
+
 }  // namespace
 
-bool prepare_decode_supported(int dk, int dv) { return dk == kD && dv == kD; }
+bool prepare_decode_supported(int dk, int dv) { return dk == dv && (dk == kD || dk == kD2); }
 
 hipError_t launch_prepare_decode(const void *xq, const void *xk, const void *xv, const float *w,
                                  const float *a_raw, const float *b_raw, const float *rate,
                                  const float *bias, float *conv_state, float *state, float *o, int N,
-                                 int H, gdn_dtype dt, bool delta, hipStream_t stream) {
+                                 int H, int d, gdn_dtype dt, bool delta, hipStream_t stream) {
     PrepDecodeArgs a{xq, xk, xv, w, a_raw, b_raw, rate, bias, conv_state, state, o, H,
-                     1.0f / sqrtf(static_cast<float>(kD))};
+                     1.0f / sqrtf(static_cast<float>(d))};
     const dim3 grid(static_cast<unsigned>(static_cast<long long>(N) * H)), block(2 * kWave);
+    if (d == kD2) {
+        const dim3 block4(4 * kWave);
+        if (dt == GDN_BF16) {
+            if (delta) hipLaunchKernelGGL((prep_decode_kernel128<uint16_t, true>), grid, block4, 0, stream, a);
+            else hipLaunchKernelGGL((prep_decode_kernel128<uint16_t, false>), grid, block4, 0, stream, a);
+        } else {
+            if (delta) hipLaunchKernelGGL((prep_decode_kernel128<float, true>), grid, block4, 0, stream, a);
+            else hipLaunchKernelGGL((prep_decode_kernel128<float, false>), grid, block4, 0, stream, a);
+        }
+        return hipGetLastError();
+    }
     if (dt == GDN_BF16) {
         if (delta) hipLaunchKernelGGL((prep_decode_kernel<uint16_t, true>), grid, block, 0, stream, a);
         else hipLaunchKernelGGL((prep_decode_kernel<uint16_t, false>), grid, block, 0, stream, a);

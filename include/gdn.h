@@ -429,12 +429,12 @@ GDN_API size_t gdn_prepare_chunk_prefill_workspace_size(int B, int T, int H, int
  *                   this token (oldest first), read and updated in place
  *   state           [N, H, d_k, d_v] fp32, read and updated in place
  *   o               [N, H, d_v] fp32, written
- * Supported: d_k = d_v = 64.  N may be 0 (nothing is done).  For GDN_F32 the
- * result equals gdn_prepare followed by gdn_decode_step_rule up to the summation
- * order of each head's squared q and k norms; for GDN_BF16 it is that of the
+ * Supported: d_k = d_v in {64, 128}.  N may be 0 (nothing is done).  For GDN_F32
+ * the result equals gdn_prepare followed by gdn_decode_step_rule up to the
+ * summation order of each head's squared q and k norms; for GDN_BF16 it is that of the
  * separate steps without the bf16 rounding of the prepared q, k, v.
  * Errors: GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_UNSUPPORTED (rule, dtype, or
- * d_k, d_v other than 64), GDN_ERR_ALIGN, GDN_ERR_ALIAS (conv_state, state or
+ * d_k, d_v unequal or not 64 or 128), GDN_ERR_ALIGN, GDN_ERR_ALIAS (conv_state, state or
  * o overlapping an input or each other), GDN_ERR_HIP.
  */
 GDN_API gdn_status gdn_prepare_decode_step(gdn_rule rule,

@@ -301,7 +301,7 @@ def prepare_decode_call(**kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(rule=2), UNSUP), (dict(H=0), SHAPE), (dict(N=-1), SHAPE), (dict(dk=128, dv=128), UNSUP),
+    (dict(rule=2), UNSUP), (dict(H=0), SHAPE), (dict(N=-1), SHAPE), (dict(dk=16, dv=16), UNSUP),
     (dict(dk=64, dv=128), UNSUP), (dict(dt=5), UNSUP), (dict(N=1 << 30, H=4), SHAPE),
     (dict(xq=None), NULL), (dict(conv=None), NULL), (dict(state=None), NULL), (dict(o=None), NULL),
     (dict(w=None), NULL), (dict(b=None), NULL),

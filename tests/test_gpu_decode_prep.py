@@ -35,10 +35,10 @@ def step_inputs(N, H, d, t, dtype, wid):
 
 @pytest.mark.parametrize("rule", [gdn.GDN_RULE_GATED_DELTA, gdn.GDN_RULE_GATED_DECAY])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
-@pytest.mark.parametrize("N,H", [(5, 3), (256, 32)])
-def test_fused_step_matches_oracles_and_separate_launches(orc, rule, dtype, N, H):
-    d, steps, wid = 64, 3, 400 + N
-    print(f"[case] prepare+decode fused N={N} H={H} {dtype} rule={rule}", flush=True)
+@pytest.mark.parametrize("N,H,d", [(5, 3, 64), (256, 32, 64), (5, 3, 128), (256, 24, 128)])
+def test_fused_step_matches_oracles_and_separate_launches(orc, rule, dtype, N, H, d):
+    steps, wid = 3, 400 + N + d
+    print(f"[case] prepare+decode fused N={N} H={H} d={d} {dtype} rule={rule}", flush=True)
     first = step_inputs(N, H, d, 0, dtype, wid)
     conv0 = first["conv_state"].clone()
     state0 = gi.decode_state(N, H, d, d, wid=wid, device=DEV)
@@ -96,9 +96,9 @@ def test_fused_step_without_rate_or_bias(orc):
 
 def test_fused_step_rejects_unsupported_heads():
     N, H = 2, 2
-    x = gi.prep_inputs(N, 1, H, 128, 128, wid=421, device=DEV)
+    x = gi.prep_inputs(N, 1, H, 16, 16, wid=421, device=DEV)
     x = {k: (v[:, 0] if k in ("xq", "xk", "xv", "a_raw", "b_raw") else v) for k, v in x.items()}
-    state = torch.zeros((N, H, 128, 128), device=DEV)
+    state = torch.zeros((N, H, 16, 16), device=DEV)
     with pytest.raises(gdn.GdnError):
         gdn.prepare_decode_step(x["xq"], x["xk"], x["xv"], x["conv_weight"], x["a_raw"], x["b_raw"],
                                 x["conv_state"], state)
