@@ -504,7 +504,7 @@ def main():
     bwd_flops = bw.B * bw.T * bw.H * BWD_FLOPS_PER_TOKEN_HEAD
 
     # decode on 3B-shaped states (256 sequences, H=24, 128 x 128 fp32 states, 402 MB): each state
-    # takes eight wavefronts of 32 floats per lane; reported beside the main figures
+    # takes four wavefronts of 32 key rows of whole 128-column rows; reported beside the main figures
     s128 = gi.decode_state(dw.B, 24, 128, 128, wid=95, device=dev)
     in128 = [gi.decode_inputs(dw.B, 24, 128, 128, t, wid=95, device=dev) for t in range(dw.calls)]
     o128 = torch.empty((dw.B, 24, 128), device=dev, dtype=torch.float32)
@@ -520,7 +520,27 @@ def main():
     d128_ms = sorted(a.elapsed_time(b) / len(in128) for a, b in d128_ev)
     d128_avg = sum(d128_ms) / len(d128_ms)
     d128_bytes = dw.B * 24 * (2 * 4 * 128 * 128 + 3 * 128 * 2 + 8 + 128 * 4)
-    del s128, in128, o128
+    # the same states stepped from the raw projections, preparation and update in one launch
+    f128 = gi.prep_inputs(dw.B, 1, 24, 128, 128, wid=203, device=dev)
+    f128f = {kk: f128[kk][:, 0].contiguous() for kk in ("xq", "xk", "xv", "a_raw", "b_raw")}
+    fconv128 = f128["conv_state"].clone()
+
+    def decode_fused_128():
+        gdn.prepare_decode_step(f128f["xq"], f128f["xk"], f128f["xv"], f128["conv_weight"], f128f["a_raw"],
+                                f128f["b_raw"], fconv128, s128, decay_rate=f128["decay_rate"],
+                                gate_bias=f128["gate_bias"], out=o128)
+    for _ in range(args.warmup):
+        decode_fused_128()
+    f128_ev = [(mk(), mk()) for _ in range(args.steps)]
+    for a, b in f128_ev:
+        a.record(stream)
+        decode_fused_128()
+        b.record(stream)
+    torch.cuda.synchronize()
+    f128_ms = sum(a.elapsed_time(b) for a, b in f128_ev) / len(f128_ev)
+    conv128 = 24 * 3 * 128
+    f128_bytes = dw.B * 24 * (3 * 128 * 2 + 2 * 4 + 2 * 128 * 128 * 4 + 128 * 4) + conv128 * (16 + 24 * dw.B)
+    del s128, in128, o128, f128, f128f, fconv128
 
     # decode over eight distinct states in rotation, one per GDN layer of an 8-GDN-layer hybrid: each
     # step updates layer 0's 128 MiB state, then layer 1's, ... (8 x 128 MiB = 1 GiB, four times the
@@ -662,6 +682,10 @@ def main():
             "us_per_step_avg": round(d128_avg * 1e3, 2), "bytes_per_step": d128_bytes,
             "GBps": round(d128_bytes / (d128_avg * 1e-3) / 1e9, 1),
             "hbm_frac": round(d128_bytes / (d128_avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "fused_step_us_avg": round(f128_ms * 1e3, 2), "fused_step_bytes": f128_bytes,
+            "fused_step_hbm_frac": round(f128_bytes / (f128_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "note": "fused_step: gdn_prepare_decode_step on the same states, the preparation from raw bf16 "
+                    "projections and the state update in one launch",
         },
         "varlen_prefill": {
             "sequences": 64, "tokens": Tv, "ms_avg": round(varlen_ms, 4),
