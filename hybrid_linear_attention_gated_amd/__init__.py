@@ -488,7 +488,7 @@ def prepare_chunk_prefill(xq, xk, xv, conv_weight, a_raw, b_raw, initial_state=N
 def chunk_backward(q, k, v, g, beta, d_o, initial_state=None, d_final_state=None, *, want_d_initial=True,
                    outs=None, workspace=None, stream=None, rule=GDN_RULE_GATED_DELTA):
     """Gradients of one prefill call for L = <d_o, o> + <d_final_state, S_T>.  Inputs as for
-    chunk_prefill (bf16 or fp32 q/k/v, d_k = d_v = 64); d_o [B,T,H,d_v] fp32; d_final_state [B,H,d_k,d_v]
+    chunk_prefill (bf16 or fp32 q/k/v, d_k = d_v = 64 or 128); d_o [B,T,H,d_v] fp32; d_final_state [B,H,d_k,d_v]
     fp32 or None.  Returns (dq, dk, dv, dg, dbeta, d_initial_state or None), all fp32."""
     import torch
     B, T, H, d_k = q.shape

@@ -27,7 +27,9 @@
 // (gdn_prefill_chunk.hip): bwd_map_kernel (F and R of every chunk, chunks in
 // parallel), bwd_scan_kernel (Y of every chunk, chunks in reverse order; long
 // sequences in two levels of pieces) and bwd_grad_kernel (all gradients, chunks in
-// parallel).  fp32 arithmetic (matrix cores for the products) on LDS-resident chunk matrices.
+// parallel).  fp32 arithmetic (matrix cores for the products) on LDS-resident chunk matrices;
+// 128-wide heads keep the gradient pass's larger matrices (the state and its gradient alone are
+// 128 KB) in a global scratch slot per workgroup instead (bwd_grad_gs_kernel).
 #include "gdn_internal.h"
 
 namespace gdn {
@@ -47,7 +49,7 @@ namespace {
 #define GDN_BWD_PAD_C 4
 #endif
 constexpr int kC = 32;                     // tokens per chunk
-constexpr int kBT = 256;                   // threads per scan workgroup
+template <int DK> constexpr int kBT = 4 * DK;  // threads per scan workgroup: one 16-row tile per wavefront
 constexpr int kBTM = GDN_BWD_MAP_THREADS;  // threads per map workgroup
 constexpr int kBTG = GDN_BWD_THREADS;      // threads per gradient workgroup
 constexpr int kPD = GDN_BWD_PAD_D;         // row padding of d-wide LDS matrices (floats)
@@ -67,6 +69,7 @@ struct BwdArgs {
     float *dq, *dk, *dv, *dg, *dbeta, *ds0;
     int T, H, N, BH;
     float scale;
+    void *gscratch;       // 128-wide heads: the gradient pass's global scratch slots
 };
 
 // out(i, j) = sum_kk A(i, kk) B(kk, j) for i < M, j < N, on the fp32 matrix cores:
@@ -82,17 +85,24 @@ __device__ __forceinline__ void mm(FA A, FB Bm, FS store, int w0 = 0, int nw = 0
     const int li = lane % 16, lk = lane / 16;
     const int waves = nw > 0 ? nw : static_cast<int>(blockDim.x) / 64;
     if (wave < 0 || wave >= waves) return;
+    // operands read before the products, a block of at most 64 along K at a time (128-wide
+    // contractions would otherwise hold 64 operand registers per lane)
+    constexpr int KB = K > 64 ? 64 : K;
+    static_assert(K % KB == 0, "K blocks");
     for (int t = wave; t < TILES; t += waves) {
         const int i0 = (t / TN) * 16, j0 = (t % TN) * 16;
-        float av[K / 4], bv[K / 4];  // the tile's operands, read before the first product
-#pragma unroll
-        for (int s = 0; s < K / 4; ++s) {
-            av[s] = A(i0 + li, 4 * s + lk);
-            bv[s] = Bm(4 * s + lk, j0 + li);
-        }
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+        for (int k0 = 0; k0 < K; k0 += KB) {
+            float av[KB / 4], bv[KB / 4];
 #pragma unroll
-        for (int s = 0; s < K / 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s], bv[s], acc, 0, 0, 0);
+            for (int s = 0; s < KB / 4; ++s) {
+                av[s] = A(i0 + li, k0 + 4 * s + lk);
+                bv[s] = Bm(k0 + 4 * s + lk, j0 + li);
+            }
+#pragma unroll
+            for (int s = 0; s < KB / 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s], bv[s], acc, 0, 0, 0);
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) store(i0 + 4 * lk + r, j0 + li, acc[r]);
     }
@@ -126,7 +136,8 @@ template <int DK, int DV> struct alignas(16) ChunkLds {
 // takes v and the chunk's start state and end-state gradient.
 template <int NT, int DK, int DV, bool GRAD> struct ChunkRows {
     static constexpr int NQ = kC * DK / NT, NV = kC * DV / NT, NS = GRAD ? DK * DV / NT : 1;
-    static_assert(NQ >= 2 && NQ <= 4 && NV >= 2 && NV <= 4 && (!GRAD || NS == 4 || NS == 8), "runs per thread");
+    static_assert((NQ == 2 || NQ == 4 || NQ == 8) && (NV == 2 || NV == 4 || NV == 8) && (!GRAD || NS == 4 || NS == 8),
+                  "runs per thread");
     float q[NQ], k[NQ], dO[NV], v[GRAD ? NV : 1], S[NS], Y[NS], g, b;
 };
 
@@ -143,14 +154,17 @@ __device__ __forceinline__ ChunkPos chunk_pos(const BwdArgs &a, int w) {
     return p;
 }
 
-// n consecutive stored values (n = 2 or 4) widened to fp32, or zeros
+// n consecutive stored values (n = 2, 4 or 8) widened to fp32, or zeros
 template <int n> __device__ __forceinline__ void load_run(const uint16_t *p, bool in, float (&x)[n]) {
     uint32_t u[n / 2];
     if (n == 2) u[0] = in ? *reinterpret_cast<const uint32_t *>(p) : 0u;
     else {
-        const uint2 w = in ? *reinterpret_cast<const uint2 *>(p) : make_uint2(0u, 0u);
-        u[0] = w.x;
-        u[n / 2 - 1] = w.y;
+#pragma unroll
+        for (int i = 0; i < n / 4; ++i) {
+            const uint2 w = in ? reinterpret_cast<const uint2 *>(p)[i] : make_uint2(0u, 0u);
+            u[2 * i] = w.x;
+            u[2 * i + 1] = w.y;
+        }
     }
 #pragma unroll
     for (int i = 0; i < n / 2; ++i) {
@@ -421,8 +435,9 @@ struct ScanArgs {
 };
 
 template <int DK, int DV, int MODE>
-__global__ __launch_bounds__(kBT) void bwd_scan_kernel(ScanArgs a) {
-    static_assert(DK == 64 && DV % kSW == 0, "one 16-row tile of Y per wavefront");
+__global__ __launch_bounds__(kBT<DK>) void bwd_scan_kernel(ScanArgs a) {
+    static_assert(DK % 16 == 0 && DV % kSW == 0, "one 16-row tile of Y per wavefront");
+    constexpr int BT = kBT<DK>;
     constexpr int SW = kSW, YP = SW + 4, NCOL = MODE == kScanMap ? DV + DK : DV;
     constexpr int SLICES = NCOL / SW;
     __shared__ float Yb[2][DK][YP];
@@ -441,7 +456,7 @@ __global__ __launch_bounds__(kBT) void bwd_scan_kernel(ScanArgs a) {
     const int n1 = MODE == kScanAll ? a.steps : min(n0 + a.m, a.steps);
     const size_t head = static_cast<size_t>(bh) * a.steps;
     const size_t hp = static_cast<size_t>(bh) * a.P + piece;
-    for (int e = tid; e < DK * SW; e += kBT) {
+    for (int e = tid; e < DK * SW; e += BT) {
         const int j = e / SW, c = e % SW;
         float y = 0.f;
         if (MODE == kScanAll) y = a.y_end ? a.y_end[static_cast<size_t>(bh) * DK * DV + j * DV + c0 + c] : 0.f;
@@ -507,11 +522,11 @@ __global__ __launch_bounds__(kBT) void bwd_scan_kernel(ScanArgs a) {
     }
     const int fin = (n1 - n0) & 1;
     if (MODE == kScanAll && a.y_start) {
-        for (int e = tid; e < DK * SW; e += kBT)
+        for (int e = tid; e < DK * SW; e += BT)
             a.y_start[static_cast<size_t>(bh) * DK * DV + (e / SW) * DV + c0 + e % SW] = Yb[fin][e / SW][e % SW];
     }
     if (MODE == kScanMap) {
-        for (int e = tid; e < DK * SW; e += kBT) {
+        for (int e = tid; e < DK * SW; e += BT) {
             const int j = e / SW, c = e % SW;
             if (has_r) a.cp[hp * DK * DV + j * DV + c0 + c] = Yb[fin][j][c];
             else a.Gp[hp * DK * DK + j * DK + c0 - DV + c] = Yb[fin][j][c];
@@ -539,30 +554,15 @@ template <int DK, int DV> struct alignas(16) GradLds {
 
 // Independent products of a phase run side by side on disjoint wavefronts of the 16
 // (ranges in the calls' last two arguments).
-template <int DK, int DV, typename TIn, bool DELTA>
-__global__ __launch_bounds__(kBTG) void bwd_grad_kernel(BwdArgs a) {
+// The gradient phases of one chunk, from its staged rows, start state S, end-state gradient Y and
+// keyside (the caller has synchronised after staging and zeroed u.red).  s and u are LDS, or (u, for
+// 128-wide heads) a global scratch slot of the workgroup's; the products are the same.
+template <int DK, int DV, bool DELTA>
+__device__ __forceinline__ void grad_phases(const BwdArgs &a, ChunkLds<DK, DV> &s, GradLds<DK, DV> &u,
+                                            size_t tok, int h, int L) {
     static_assert(DK == DV, "the dW buffer reuses K Y's");
     static_assert(kBTG == 1024, "the phases below are laid out for 16 wavefronts");
-    __shared__ ChunkLds<DK, DV> s;
-    __shared__ GradLds<DK, DV> u;
     const int tid = threadIdx.x;
-    const int w = blockIdx.x;
-    const ChunkPos pos = chunk_pos(a, w);
-    const size_t tok = pos.tok;
-    const int h = pos.h, L = pos.L;
-    {
-        // the chunk's rows and the keyside its map pass stored
-        ChunkRows<kBTG, DK, DV, true> rows;
-        KsRows ks{};
-        chunk_load<kBTG, DK, DV, TIn, true>(a, w, rows);
-        keyside_load<DK, DELTA>(a, w, ks);
-        chunk_stage<kBTG, DK, DV, true>(rows, s, u.v, u.S, u.Yv);
-        keyside_stage<DK, DV, DELTA>(ks, s);
-    }
-    if (tid < kC)
-        for (int m = 0; m < 9; ++m) u.red[m][tid] = 0.f;
-    __syncthreads();
-
     // Delta = T diag(b) V - W S  (decay rule: diag(b) V);  K Y
     if (DELTA) {
         mm<kC, DV, kC>([&](int i, int j) { return s.T[i][j]; }, [&](int j, int c) { return s.b[j] * u.v[j][c]; },
@@ -654,7 +654,9 @@ __global__ __launch_bounds__(kBTG) void bwd_grad_kernel(BwdArgs a) {
     __syncthreads();
     // combine: dG per position, db, and the last position's end-state terms (one wavefront)
     if (tid < 64) {
-        float last = s.gam[kC - 1] * u.red64[tid];
+        float ys = 0.f;
+        for (int j = tid; j < DK; j += 64) ys += u.red64[j];
+        float last = s.gam[kC - 1] * ys;
         if (tid < kC) {
             const int r = tid;
             const float e = s.eps[r] * u.red[2][r];
@@ -698,6 +700,81 @@ __global__ __launch_bounds__(kBTG) void bwd_grad_kernel(BwdArgs a) {
     }
 }
 
+template <int DK, int DV, typename TIn, bool DELTA>
+__global__ __launch_bounds__(kBTG) void bwd_grad_kernel(BwdArgs a) {
+    __shared__ ChunkLds<DK, DV> s;
+    __shared__ GradLds<DK, DV> u;
+    const int tid = threadIdx.x;
+    const int w = blockIdx.x;
+    const ChunkPos pos = chunk_pos(a, w);
+    {
+        // the chunk's rows and the keyside its map pass stored
+        ChunkRows<kBTG, DK, DV, true> rows;
+        KsRows ks{};
+        chunk_load<kBTG, DK, DV, TIn, true>(a, w, rows);
+        keyside_load<DK, DELTA>(a, w, ks);
+        chunk_stage<kBTG, DK, DV, true>(rows, s, u.v, u.S, u.Yv);
+        keyside_stage<DK, DV, DELTA>(ks, s);
+    }
+    if (tid < kC)
+        for (int m = 0; m < 9; ++m) u.red[m][tid] = 0.f;
+    __syncthreads();
+    grad_phases<DK, DV, DELTA>(a, s, u, pos.tok, pos.h, pos.L);
+}
+
+// 128-wide heads: the chunk rows and keyside in LDS (81 KB), the rest of the gradient pass's
+// matrices (270 KB) in the workgroup's global scratch slot; the workgroups loop over the chunks.
+template <int DK, int DV, typename TIn, bool DELTA>
+__global__ __launch_bounds__(kBTG) void bwd_grad_gs_kernel(BwdArgs a, GradLds<DK, DV> *scratch) {
+    __shared__ ChunkLds<DK, DV> s;
+    GradLds<DK, DV> &u = scratch[blockIdx.x];
+    const int tid = threadIdx.x;
+    const TIn *q = static_cast<const TIn *>(a.q), *k = static_cast<const TIn *>(a.k), *v = static_cast<const TIn *>(a.v);
+    for (int w = blockIdx.x; w < a.BH * a.N; w += gridDim.x) {
+        const ChunkPos p = chunk_pos(a, w);
+        for (int e = tid; e < kC * DK; e += kBTG) {
+            const int r = e / DK, c = e % DK;
+            const size_t x = ((p.tok + r) * a.H + p.h) * DK + c;
+            s.q[r][c] = r < p.L ? load_in(q, x) : 0.f;
+            s.k[r][c] = r < p.L ? load_in(k, x) : 0.f;
+        }
+        for (int e = tid; e < kC * DV; e += kBTG) {
+            const int r = e / DV, c = e % DV;
+            const size_t x = ((p.tok + r) * a.H + p.h) * DV + c;
+            s.dO[r][c] = r < p.L ? a.d_o[x] : 0.f;
+            u.v[r][c] = r < p.L ? load_in(v, x) : 0.f;
+        }
+        const size_t sx = static_cast<size_t>(w) * DK * DV;
+        for (int e = tid; e < DK * DV; e += kBTG) {
+            u.S[e / DV][e % DV] = a.states[sx + e];
+            u.Yv[e / DV][e % DV] = a.Y[sx + e];
+        }
+        // the keyside its map pass stored: T, KG, P (C x C each), W (C x DK), G, gam, eps
+        const float *ks = a.KS + static_cast<size_t>(w) * ks_floats<DK>();
+        for (int e = tid; e < kC * kC; e += kBTG) {
+            const int r = e / kC, c = e % kC;
+            if (DELTA) {
+                s.T[r][c] = ks[e];
+                s.KG[r][c] = ks[kC * kC + e];
+            }
+            s.P[r][c] = ks[2 * kC * kC + e];
+        }
+        if (DELTA)
+            for (int e = tid; e < kC * DK; e += kBTG) s.W[e / DK][e % DK] = ks[3 * kC * kC + e];
+        if (tid < kC) {
+            const float *gates = ks + 3 * kC * kC + kC * DK;
+            s.G[tid] = gates[tid];
+            s.gam[tid] = gates[kC + tid];
+            s.eps[tid] = gates[2 * kC + tid];
+            s.b[tid] = tid < p.L ? a.beta[(p.tok + tid) * a.H + p.h] : 0.f;
+            for (int m = 0; m < 9; ++m) u.red[m][tid] = 0.f;
+        }
+        __syncthreads();
+        grad_phases<DK, DV, DELTA>(a, s, u, p.tok, p.h, p.L);
+        __syncthreads();  // the next chunk restages s and u
+    }
+}
+
 // Pieces for the reverse scan: none when the heads alone give enough workgroups or the
 // sequence is short (the pieces triple the work: their maps run on twice the columns); else
 // about sqrt(N) chunks per piece (three short sequential passes).
@@ -710,6 +787,11 @@ ScanPlan scan_plan(int BH, int N) {
     while (m * m < N) m *= 2;
     return {m, (N + m - 1) / m};
 }
+
+// 128-wide heads: the gradient pass keeps its larger matrices in global scratch, one slot per
+// workgroup (one workgroup per compute unit: 81 KB of LDS)
+template <int DK, int DV> constexpr bool kGradGlobal = DK == 128;
+constexpr int kGradSlots = 256;
 
 template <int DK, int DV, bool DELTA>
 hipError_t run_backward(BwdArgs &a, gdn_dtype dt, const ScanPlan &plan, float *Gp, float *cp, float *yend,
@@ -728,33 +810,40 @@ hipError_t run_backward(BwdArgs &a, gdn_dtype dt, const ScanPlan &plan, float *G
     if (plan.P == 1) {
         sa.y_end = a.ds_final; sa.y_start = a.ds0; sa.m = a.N; sa.P = 1;
         sa.items = a.BH * (DV / kSW);
-        hipLaunchKernelGGL((bwd_scan_kernel<DK, DV, kScanAll>), grid8(sa.items), dim3(kBT), 0, stream, sa);
+        hipLaunchKernelGGL((bwd_scan_kernel<DK, DV, kScanAll>), grid8(sa.items), dim3(kBT<DK>), 0, stream, sa);
     } else {
         // piece maps, then the chain over pieces (the same scan with piece maps as its steps), then
         // every chunk's Y inside each piece from the piece's end value
         sa.m = plan.m; sa.P = plan.P; sa.Gp = Gp; sa.cp = cp;
         sa.items = a.BH * plan.P * ((DV + DK) / kSW);
-        hipLaunchKernelGGL((bwd_scan_kernel<DK, DV, kScanMap>), grid8(sa.items), dim3(kBT), 0, stream, sa);
+        hipLaunchKernelGGL((bwd_scan_kernel<DK, DV, kScanMap>), grid8(sa.items), dim3(kBT<DK>), 0, stream, sa);
         ScanArgs ch{};
         ch.F = Gp; ch.R = cp; ch.Y = yend; ch.y_end = a.ds_final; ch.y_start = a.ds0;
         ch.steps = plan.P; ch.m = plan.P; ch.P = 1;
         ch.items = a.BH * (DV / kSW);
-        hipLaunchKernelGGL((bwd_scan_kernel<DK, DV, kScanAll>), grid8(ch.items), dim3(kBT), 0, stream, ch);
+        hipLaunchKernelGGL((bwd_scan_kernel<DK, DV, kScanAll>), grid8(ch.items), dim3(kBT<DK>), 0, stream, ch);
         sa.y_end = yend;
         sa.items = a.BH * plan.P * (DV / kSW);
-        hipLaunchKernelGGL((bwd_scan_kernel<DK, DV, kScanPiece>), grid8(sa.items), dim3(kBT), 0, stream, sa);
+        hipLaunchKernelGGL((bwd_scan_kernel<DK, DV, kScanPiece>), grid8(sa.items), dim3(kBT<DK>), 0, stream, sa);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || items == 0) return e;
-    if (bf) hipLaunchKernelGGL((bwd_grad_kernel<DK, DV, uint16_t, DELTA>), dim3(items), dim3(kBTG), 0, stream, a);
-    else hipLaunchKernelGGL((bwd_grad_kernel<DK, DV, float, DELTA>), dim3(items), dim3(kBTG), 0, stream, a);
+    if constexpr (kGradGlobal<DK, DV>) {
+        auto *slots = static_cast<GradLds<DK, DV> *>(a.gscratch);
+        const dim3 grid(items < kGradSlots ? items : kGradSlots);
+        if (bf) hipLaunchKernelGGL((bwd_grad_gs_kernel<DK, DV, uint16_t, DELTA>), grid, dim3(kBTG), 0, stream, a, slots);
+        else hipLaunchKernelGGL((bwd_grad_gs_kernel<DK, DV, float, DELTA>), grid, dim3(kBTG), 0, stream, a, slots);
+    } else {
+        if (bf) hipLaunchKernelGGL((bwd_grad_kernel<DK, DV, uint16_t, DELTA>), dim3(items), dim3(kBTG), 0, stream, a);
+        else hipLaunchKernelGGL((bwd_grad_kernel<DK, DV, float, DELTA>), dim3(items), dim3(kBTG), 0, stream, a);
+    }
     return hipGetLastError();
 }
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 struct BwdLayout {
-    size_t fwd, o, sfin, states, F, R, Y, KS, Gp, cp, yend, total;
+    size_t fwd, o, sfin, states, F, R, Y, KS, Gp, cp, yend, gs, total;
 };
 BwdLayout bwd_layout(int B, int T, int H, int dk, int dv) {
     const size_t BH = static_cast<size_t>(B) * H, N = (static_cast<size_t>(T) + kC - 1) / kC;
@@ -767,12 +856,13 @@ BwdLayout bwd_layout(int B, int T, int H, int dk, int dv) {
     L.F = off; off += align256(BH * N * dk * dk * 4);
     L.R = off; off += align256(BH * N * dk * dv * 4);
     L.Y = off; off += align256(BH * N * dk * dv * 4);
-    L.KS = off; off += align256(BH * N * ks_floats<64>() * 4);
+    L.KS = off; off += align256(BH * N * (dk == 128 ? ks_floats<128>() : ks_floats<64>()) * 4);
     const ScanPlan plan = scan_plan(static_cast<int>(BH), static_cast<int>(N));
     const size_t PP = plan.P > 1 ? static_cast<size_t>(plan.P) : 0;
     L.Gp = off; off += align256(BH * PP * dk * dk * 4);
     L.cp = off; off += align256(BH * PP * dk * dv * 4);
     L.yend = off; off += align256(BH * PP * dk * dv * 4);
+    L.gs = off; off += dk == 128 ? align256(kGradSlots * sizeof(GradLds<128, 128>)) : 0;
     L.total = off;
     return L;
 }
@@ -780,7 +870,7 @@ BwdLayout bwd_layout(int B, int T, int H, int dk, int dv) {
 }  // namespace
 
 bool backward_supported(int dk, int dv, gdn_dtype dt) {
-    return dk == 64 && dv == 64 && (dt == GDN_BF16 || dt == GDN_F32);
+    return dk == dv && (dk == 64 || dk == 128) && (dt == GDN_BF16 || dt == GDN_F32);
 }
 
 int backward_chunk() { return kC; }
@@ -805,6 +895,7 @@ hipError_t launch_backward(const void *q, const void *k, const void *v, const fl
     a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.ds0 = ds0;
     a.T = T; a.H = H; a.BH = B * H; a.N = (T + kC - 1) / kC;
     a.scale = 1.0f / sqrtf(static_cast<float>(d_k));
+    a.gscratch = w + L.gs;
     if (T > 0 && dt == GDN_F32) {
         // fp32 q/k/v: the fp32 chunk kernel, again keeping every chunk's start state
         hipError_t e = launch_prefill_valu(q, k, v, g, beta, s0, reinterpret_cast<float *>(w + L.o),
@@ -823,6 +914,9 @@ hipError_t launch_backward(const void *q, const void *k, const void *v, const fl
     const ScanPlan plan = scan_plan(a.BH, a.N);
     float *Gp = reinterpret_cast<float *>(w + L.Gp), *cp = reinterpret_cast<float *>(w + L.cp);
     float *yend = reinterpret_cast<float *>(w + L.yend);
+    if (d_k == 128)
+        return delta ? run_backward<128, 128, true>(a, dt, plan, Gp, cp, yend, stream)
+                     : run_backward<128, 128, false>(a, dt, plan, Gp, cp, yend, stream);
     return delta ? run_backward<64, 64, true>(a, dt, plan, Gp, cp, yend, stream)
                  : run_backward<64, 64, false>(a, dt, plan, Gp, cp, yend, stream);
 }

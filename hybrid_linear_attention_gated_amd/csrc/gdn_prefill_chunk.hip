@@ -1728,7 +1728,7 @@ hipError_t run_chunk(const uint16_t *q, const uint16_t *k, const uint16_t *v, co
     a.scale = 1.0f / sqrtf(static_cast<float>(DK));
     // the OUT pass, with chunk start states written only where the gradients need them
     auto launch_out = [&](int items) {
-        if constexpr (DK == 64 && DV == 64 && C == 32) {
+        if constexpr (DK == DV && (DK == 64 || DK == 128) && C == 32 && !PREP) {
             if (chunk_states) {
                 hipLaunchKernelGGL((chunk_kernel<DK, DV, C, false, DELTA, true>), grid(items), dim3(kWave * kWavesOf<DK, DV>), 0, stream, a);
                 return hipGetLastError();

@@ -241,7 +241,9 @@ def test_backward_rejects(kw, code):
 
 def test_backward_workspace_size():
     assert gdn.gdn_chunk_backward_workspace_size(1, 8192, 4, 64, 64, BF16) > 4 * 256 * 64 * 64 * 4 * 4
-    assert gdn.gdn_chunk_backward_workspace_size(1, 8192, 4, 128, 128, BF16) == 0
+    assert gdn.gdn_chunk_backward_workspace_size(1, 8192, 4, 128, 128, BF16) > 4 * 256 * 128 * 128 * 4 * 4
+    assert gdn.gdn_chunk_backward_workspace_size(1, 8192, 4, 16, 16, BF16) == 0
+    assert gdn.gdn_chunk_backward_workspace_size(1, 8192, 4, 64, 128, BF16) == 0
     assert gdn.gdn_chunk_backward_workspace_size(0, 8192, 4, 64, 64, BF16) == 0
     # nothing to compute: T = 0 without an initial-state gradient is accepted without a GPU
     assert backward_call(T=0, q=None, k=None, v=None, g=None, beta=None, do=None, dq=None, dk=None, dv=None,

@@ -4,8 +4,9 @@ Every gradient (dq, dk, dv, dg, dbeta, d_initial_state) of the HIP path is compa
 element with the fp64 token-by-token adjoint of the oracle on the same seeded inputs (q, k, v
 stored as bf16, so both sides see the same values), within the bf16-input tolerance of the
 forward (max |err| <= 2e-2 RMS of the oracle's tensor; 1e-4 for fp32 q/k/v).  Cases: ragged lengths, several forward
-pieces, both rules, with and without start state and final-state gradient, T = 0 and 1, and the
-full 1b_8k training shape."""
+pieces, both rules, with and without start state and final-state gradient, T = 0 and 1, the
+full 1b_8k training shape, and 128-wide heads (the 3B-shaped layers) on ragged, multi-piece and
+two-level-scan sequences and on sampled heads of a 24-head 8K call."""
 import numpy as np
 import pytest
 import torch
@@ -27,9 +28,9 @@ def grad_inputs(B, T, H, d, wid, s0=True, dsf=True, dtype=torch.bfloat16):
     return x, d_o, ds
 
 
-def run_case(B, T, H, rule, wid, s0=True, dsf=True, want_d_initial=True, dtype=torch.bfloat16):
-    print(f"[case] backward B={B} T={T} H={H} rule={rule} s0={s0} dsf={dsf} {dtype}", flush=True)
-    x, d_o, ds = grad_inputs(B, T, H, 64, wid, s0, dsf, dtype)
+def run_case(B, T, H, rule, wid, s0=True, dsf=True, want_d_initial=True, dtype=torch.bfloat16, d=64):
+    print(f"[case] backward B={B} T={T} H={H} d={d} rule={rule} s0={s0} dsf={dsf} {dtype}", flush=True)
+    x, d_o, ds = grad_inputs(B, T, H, d, wid, s0, dsf, dtype)
     got = gdn.chunk_backward(x["q"], x["k"], x["v"], x["g"], x["beta"], d_o, x["s0"], ds,
                              want_d_initial=want_d_initial, rule=rule)
     torch.cuda.synchronize()
@@ -105,3 +106,38 @@ def test_backward_two_level_scan_1b_64k_sampled():
                           sub(d_o), sub(ds))
     for name, t in zip(("dq", "dk", "dv", "dg", "dbeta", "ds0"), got):
         assert_parity(sub(t).numpy(), ref[name], TOL["bf16"], f"{name} 1b_64k heads {heads}")
+
+
+@pytest.mark.parametrize("rule", [gdn.GDN_RULE_GATED_DELTA, gdn.GDN_RULE_GATED_DECAY])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_backward_d128_ragged(rule, dtype):
+    # 128-wide heads: the gradient pass keeps its larger matrices in global scratch
+    run_case(2, 100, 3, rule, 240, dtype=dtype, d=128)
+
+
+@pytest.mark.parametrize("rule", [gdn.GDN_RULE_GATED_DELTA, gdn.GDN_RULE_GATED_DECAY])
+def test_backward_d128_pieces_and_two_level_scan(rule):
+    # 150 chunks on 2 heads: the forward recompute runs in pieces and the reverse scan in pieces of
+    # 16 chunks (the last chunk 4 tokens short)
+    run_case(1, 150 * 32 - 4, 2, rule, 241, d=128)
+
+
+def test_backward_d128_short_and_no_state():
+    run_case(2, 33, 2, gdn.GDN_RULE_GATED_DELTA, 242, s0=False, dsf=False, d=128)
+    run_case(1, 1, 2, gdn.GDN_RULE_GATED_DELTA, 243, d=128)
+
+
+def test_backward_3b_shaped_8k_sampled_heads():
+    # a 3B-shaped layer's 8K training call (B=1 H=24 T=8192 d=128); the oracle runs on 2 of the
+    # 24 heads (heads are independent: the same inputs restricted to those heads)
+    B, T, H, d = 1, 8192, 24, 128
+    print(f"[case] backward 3b-shaped T={T} H={H} d={d}", flush=True)
+    x, d_o, ds = grad_inputs(B, T, H, d, 244)
+    got = gdn.chunk_backward(x["q"], x["k"], x["v"], x["g"], x["beta"], d_o, x["s0"], ds)
+    torch.cuda.synchronize()
+    heads = [0, 17]
+    sub = lambda t: t[:, :, heads].contiguous().cpu() if t.dim() >= 3 and t.shape[1] == T else t[:, heads].contiguous().cpu()
+    ref = oracle.backward(sub(x["q"]), sub(x["k"]), sub(x["v"]), sub(x["g"]), sub(x["beta"]), sub(x["s0"]),
+                          sub(d_o), sub(ds))
+    for name, t in zip(("dq", "dk", "dv", "dg", "dbeta", "ds0"), got):
+        assert_parity(sub(t).numpy(), ref[name], TOL["bf16"], f"{name} 3b-shaped heads {heads}")
