@@ -502,6 +502,30 @@ def main():
     torch.cuda.synchronize()
     bwd_ms = sum(a.elapsed_time(b) for a, b in bw_ev) / len(bw_ev)
     bwd_flops = bw.B * bw.T * bw.H * BWD_FLOPS_PER_TOKEN_HEAD
+    del bin_, bdo, bouts, bws
+
+    # the gradients of a 3B-shaped layer's 8K training call (B=1 H=24 T=8192 d=128); reported
+    # beside the main figures
+    b3 = gi.prefill_inputs(1, 8192, 24, 128, 128, wid=244, device=dev)
+    b3do = gi.draw_v((1, 8192, 24, 128), gi.seed_of(244, 1, "v"), torch.float32, dev)
+    b3outs = (torch.empty((1, 8192, 24, 128), **f32), torch.empty((1, 8192, 24, 128), **f32),
+              torch.empty((1, 8192, 24, 128), **f32), torch.empty((1, 8192, 24), **f32),
+              torch.empty((1, 8192, 24), **f32), torch.empty((1, 24, 128, 128), **f32))
+    b3ws = torch.empty(gdn.backward_workspace_bytes(1, 8192, 24, 128, 128, gdn.GDN_BF16), device=dev, dtype=torch.uint8)
+
+    def backward_3b():
+        gdn.chunk_backward(b3["q"], b3["k"], b3["v"], b3["g"], b3["beta"], b3do, None, None, outs=b3outs,
+                           workspace=b3ws)
+    for _ in range(args.warmup):
+        backward_3b()
+    b3_ev = [(mk(), mk()) for _ in range(max(2, args.steps // 4))]
+    for a, b in b3_ev:
+        a.record(stream)
+        backward_3b()
+        b.record(stream)
+    torch.cuda.synchronize()
+    bwd3_ms = sum(a.elapsed_time(b) for a, b in b3_ev) / len(b3_ev)
+    del b3, b3do, b3outs, b3ws
 
     # decode on 3B-shaped states (256 sequences, H=24, 128 x 128 fp32 states, 402 MB): each state
     # takes four wavefronts of 32 key rows of whole 128-column rows; reported beside the main figures
@@ -727,6 +751,12 @@ def main():
             "note": "forward recompute (keeps chunk start states) + per-chunk maps + reverse scan + per-chunk "
                     "gradients, fp32 on the matrix cores; FLOPs are the gradient kernels' multiply-adds x 2, "
                     "alu_frac against the fp32 peak",
+        },
+        "backward_3b_shape": {
+            "workload": "one 3B-shaped layer's 8K training call: B=1 H=24 T=8192 d_k=d_v=128, bf16 q/k/v, gated "
+                        "delta rule, zero start state",
+            "ms_avg": round(bwd3_ms, 4), "tokens_per_s": round(8192 / (bwd3_ms * 1e-3), 1),
+            "note": "the gradient pass keeps its larger matrices in global scratch (they do not fit on chip)",
         },
         "prefill_1b_8k": {
             "workload": "1b_8k: B=4 H=32 T=8192 d_k=d_v=64 chunk 64, bf16 q/k/v, zero start state, final state out",
