@@ -777,12 +777,15 @@ __global__ __launch_bounds__(kBTG) void bwd_grad_gs_kernel(BwdArgs a, GradLds<DK
 
 // Pieces for the reverse scan: none when the heads alone give enough workgroups or the
 // sequence is short (the pieces triple the work: their maps run on twice the columns); else
-// about sqrt(N) chunks per piece (three short sequential passes).
+// about sqrt(N) chunks per piece (three short sequential passes).  128-wide heads have twice
+// the columns per head and four times the work per step, so the pieces pay later: a 3B-shaped
+// 8K call (24 heads, 256 chunks) takes 4.86 ms with one level against 5.39 ms with two.
 struct ScanPlan {
     int m, P;  // chunks per piece, pieces per head (P = 1: one range per head)
 };
-ScanPlan scan_plan(int BH, int N) {
+ScanPlan scan_plan(int BH, int N, int dk) {
     if (N < 128 || BH * (64 / kSW) >= 256) return {N, 1};  // heads alone fill the 256 CUs
+    if (dk == 128 && N < 1024) return {N, 1};
     int m = 16;
     while (m * m < N) m *= 2;
     return {m, (N + m - 1) / m};
@@ -857,7 +860,7 @@ BwdLayout bwd_layout(int B, int T, int H, int dk, int dv) {
     L.R = off; off += align256(BH * N * dk * dv * 4);
     L.Y = off; off += align256(BH * N * dk * dv * 4);
     L.KS = off; off += align256(BH * N * (dk == 128 ? ks_floats<128>() : ks_floats<64>()) * 4);
-    const ScanPlan plan = scan_plan(static_cast<int>(BH), static_cast<int>(N));
+    const ScanPlan plan = scan_plan(static_cast<int>(BH), static_cast<int>(N), dk);
     const size_t PP = plan.P > 1 ? static_cast<size_t>(plan.P) : 0;
     L.Gp = off; off += align256(BH * PP * dk * dk * 4);
     L.cp = off; off += align256(BH * PP * dk * dv * 4);
@@ -911,7 +914,7 @@ hipError_t launch_backward(const void *q, const void *k, const void *v, const fl
                                             reinterpret_cast<float *>(w + L.states));
         if (e != hipSuccess) return e;
     }
-    const ScanPlan plan = scan_plan(a.BH, a.N);
+    const ScanPlan plan = scan_plan(a.BH, a.N, d_k);
     float *Gp = reinterpret_cast<float *>(w + L.Gp), *cp = reinterpret_cast<float *>(w + L.cp);
     float *yend = reinterpret_cast<float *>(w + L.yend);
     if (d_k == 128)

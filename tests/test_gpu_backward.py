@@ -116,10 +116,16 @@ def test_backward_d128_ragged(rule, dtype):
 
 
 @pytest.mark.parametrize("rule", [gdn.GDN_RULE_GATED_DELTA, gdn.GDN_RULE_GATED_DECAY])
-def test_backward_d128_pieces_and_two_level_scan(rule):
-    # 150 chunks on 2 heads: the forward recompute runs in pieces and the reverse scan in pieces of
-    # 16 chunks (the last chunk 4 tokens short)
+def test_backward_d128_forward_pieces(rule):
+    # 150 chunks on 2 heads: the forward recompute runs in pieces; one-level reverse scan (the last
+    # chunk 4 tokens short)
     run_case(1, 150 * 32 - 4, 2, rule, 241, d=128)
+
+
+def test_backward_d128_two_level_scan():
+    # 1,100 chunks on 2 heads: the reverse scan runs in pieces of 64 chunks (the last piece 12
+    # chunks, its last chunk 4 tokens short)
+    run_case(1, 1100 * 32 - 4, 2, gdn.GDN_RULE_GATED_DELTA, 245, d=128)
 
 
 def test_backward_d128_short_and_no_state():
