@@ -749,8 +749,9 @@ def main():
             "alu_frac": round(bwd_flops / (bwd_ms * 1e-3) / 1e12 / FP32_VALU_PEAK_TFLOPS, 4),
             "flops_per_call": bwd_flops,
             "note": "forward recompute (keeps chunk start states) + per-chunk maps + reverse scan + per-chunk "
-                    "gradients, fp32 on the matrix cores; FLOPs are the gradient kernels' multiply-adds x 2, "
-                    "alu_frac against the fp32 peak",
+                    "gradients; products as three-pass hi/lo bf16 MFMA (fp32-class results) except the gate "
+                    "prefix sums, the 16x16 inverse blocks and the scan (fp32 MFMA); FLOPs are the gradient "
+                    "kernels' useful multiply-adds x 2, alu_frac against the fp32 peak (the precision delivered)",
         },
         "backward_3b_shape": {
             "workload": "one 3B-shaped layer's 8K training call: B=1 H=24 T=8192 d_k=d_v=128, bf16 q/k/v, gated "

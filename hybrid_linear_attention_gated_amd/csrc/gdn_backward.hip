@@ -30,7 +30,7 @@
 // parallel).  fp32 arithmetic (matrix cores for the products) on LDS-resident chunk matrices;
 // 128-wide heads keep the gradient pass's larger matrices (the state and its gradient alone are
 // 128 KB) in a global scratch slot per workgroup instead (bwd_grad_gs_kernel).
-#include "gdn_internal.h"
+#include "gdn_mfma.h"
 
 namespace gdn {
 namespace {
@@ -77,7 +77,12 @@ struct BwdArgs {
 // the workgroup's), so independent products can run side by side; each tile accumulated by
 // v_mfma_f32_16x16x4_f32 over K in steps of 4.  Lane l feeds A(i0 + l % 16, k0 + l / 16)
 // and B(k0 + l / 16, j0 + l % 16) and receives out(i0 + 4 (l / 16) + r, j0 + l % 16), r < 4.
-template <int M, int N, int K, class FA, class FB, class FS>
+//
+// HL (bf16 inputs, K a multiple of 32): the same tiles on v_mfma_f32_16x16x32_bf16 instead, both
+// operands split into hi + lo bf16 and three passes (hi.hi + hi.lo + lo.hi): about 16 significant
+// bits per operand, fp32 accumulation.  Lane (lk, li) feeds the k-slots kmap(s, lk, e) of row
+// i0 + li of A and of column j0 + li of B; the output layout is the same.
+template <int M, int N, int K, bool HL = false, class FA, class FB, class FS>
 __device__ __forceinline__ void mm(FA A, FB Bm, FS store, int w0 = 0, int nw = 0) {
     static_assert(M % 16 == 0 && N % 16 == 0 && K % 4 == 0, "tile");
     constexpr int TN = N / 16, TILES = (M / 16) * TN;
@@ -85,6 +90,31 @@ __device__ __forceinline__ void mm(FA A, FB Bm, FS store, int w0 = 0, int nw = 0
     const int li = lane % 16, lk = lane / 16;
     const int waves = nw > 0 ? nw : static_cast<int>(blockDim.x) / 64;
     if (wave < 0 || wave >= waves) return;
+    if constexpr (HL && K % 32 == 0) {
+        for (int t = wave; t < TILES; t += waves) {
+            const int i0 = (t / TN) * 16, j0 = (t % TN) * 16;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < K / 32; ++s) {
+                float xa[8], xb[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int kk = kmap(s, lk, e);
+                    xa[e] = A(i0 + li, kk);
+                    xb[e] = Bm(kk, j0 + li);
+                }
+                bf16x8 ah, al, bh, bl;
+                split_bf16(xa, ah, al);
+                split_bf16(xb, bh, bl);
+                acc = mfma_bf16(ah, bh, acc);
+                acc = mfma_bf16(ah, bl, acc);
+                acc = mfma_bf16(al, bh, acc);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) store(i0 + 4 * lk + r, j0 + li, acc[r]);
+        }
+        return;
+    }
     // operands read before the products, a block of at most 64 along K at a time (128-wide
     // contractions would otherwise hold 64 operand registers per lane)
     constexpr int KB = K > 64 ? 64 : K;
@@ -109,9 +139,9 @@ __device__ __forceinline__ void mm(FA A, FB Bm, FS store, int w0 = 0, int nw = 0
 }
 
 // sum_kk A(i, kk) for i < M, by a product with a block of ones; store(i, x).
-template <int M, int K, class FA, class FS>
+template <int M, int K, bool HL = false, class FA, class FS>
 __device__ __forceinline__ void rowsum(FA A, FS store, int w0 = 0, int nw = 0) {
-    mm<M, 16, K>(A, [](int, int) { return 1.f; }, [&](int i, int j, float x) { if (j == 0) store(i, x); }, w0, nw);
+    mm<M, 16, K, HL>(A, [](int, int) { return 1.f; }, [&](int i, int j, float x) { if (j == 0) store(i, x); }, w0, nw);
 }
 
 // x as held by lane l of the wavefront (l a constant; a uniform value)
@@ -246,7 +276,7 @@ __device__ __forceinline__ void chunk_stage(const ChunkRows<NT, DK, DV, GRAD> &R
 
 // The chunk's keyside from its staged rows (the caller has synchronised after staging):
 // G, gam, eps, P, KG and, for the delta rule, T and W.
-template <int DK, int DV, bool DELTA>
+template <int DK, int DV, bool DELTA, bool HL>
 __device__ void chunk_keyside(ChunkLds<DK, DV> &s) {
     const int tid = threadIdx.x;
     // G = (lower-triangular ones) g
@@ -259,10 +289,10 @@ __device__ void chunk_keyside(ChunkLds<DK, DV> &s) {
     }
     // P and K K^T with the decay of every pair (exponents are <= 0 below the diagonal)
     const int half = static_cast<int>(blockDim.x) / 128;  // wavefronts in each half of the workgroup
-    mm<kC, kC, DK>([&](int i, int kk) { return s.q[i][kk]; }, [&](int kk, int j) { return s.k[j][kk]; },
+    mm<kC, kC, DK, HL>([&](int i, int kk) { return s.q[i][kk]; }, [&](int kk, int j) { return s.k[j][kk]; },
                    [&](int i, int j, float x) { s.P[i][j] = j <= i ? x * expf(s.G[i] - s.G[j]) : 0.f; }, 0, half);
     if (DELTA)
-        mm<kC, kC, DK>([&](int i, int kk) { return s.k[i][kk]; }, [&](int kk, int j) { return s.k[j][kk]; },
+        mm<kC, kC, DK, HL>([&](int i, int kk) { return s.k[i][kk]; }, [&](int kk, int j) { return s.k[j][kk]; },
                        [&](int i, int j, float x) { s.KG[i][j] = j < i ? x * expf(s.G[i] - s.G[j]) : 0.f; },
                        half, half);
     __syncthreads();
@@ -309,7 +339,7 @@ __device__ void chunk_keyside(ChunkLds<DK, DV> &s) {
                    [&](int i, int c, float x) { s.T[16 + i][c] = -x; }, 0, 1);
     __syncthreads();
     // W = T diag(b gam) K
-    mm<kC, DK, kC>([&](int i, int j) { return s.T[i][j]; },
+    mm<kC, DK, kC, HL>([&](int i, int j) { return s.T[i][j]; },
                    [&](int j, int c) { return s.b[j] * s.gam[j] * s.k[j][c]; },
                    [&](int i, int c, float x) { s.W[i][c] = x; });
     __syncthreads();
@@ -356,6 +386,7 @@ __device__ __forceinline__ void keyside_stage(const KsRows &R, ChunkLds<DK, DV> 
 template <int DK, int DV, typename TIn, bool DELTA>
 __global__ __launch_bounds__(kBTM) void bwd_map_kernel(BwdArgs a) {
     __shared__ ChunkLds<DK, DV> s;  // (its q rows become diag(gam) Q - P W)
+    constexpr bool kHL = sizeof(TIn) == 2;  // bf16 inputs: hi/lo bf16 products
     const int w = blockIdx.x;
     {
         ChunkRows<kBTM, DK, DV, false> rows;
@@ -363,7 +394,7 @@ __global__ __launch_bounds__(kBTM) void bwd_map_kernel(BwdArgs a) {
         chunk_stage<kBTM, DK, DV, false>(rows, s, nullptr, nullptr, nullptr);
     }
     __syncthreads();
-    chunk_keyside<DK, DV, DELTA>(s);
+    chunk_keyside<DK, DV, DELTA, kHL>(s);
     {
         // the keyside, for the gradient kernel
         float *ks = a.KS + static_cast<size_t>(w) * ks_floats<DK>();
@@ -386,7 +417,7 @@ __global__ __launch_bounds__(kBTM) void bwd_map_kernel(BwdArgs a) {
     if (DELTA) {
         // in place: each element is read and rewritten by the thread that computes it, and the
         // product reads P and W only
-        mm<kC, DK, kC>([&](int i, int j) { return s.P[i][j]; }, [&](int j, int c) { return s.W[j][c]; },
+        mm<kC, DK, kC, kHL>([&](int i, int j) { return s.P[i][j]; }, [&](int j, int c) { return s.W[j][c]; },
                        [&](int i, int c, float x) { s.q[i][c] = s.gam[i] * s.q[i][c] - x; });
     } else {
         for (int e = threadIdx.x; e < kC * DK; e += kBTM) s.q[e / DK][e % DK] *= s.gam[e / DK];
@@ -395,12 +426,12 @@ __global__ __launch_bounds__(kBTM) void bwd_map_kernel(BwdArgs a) {
     const size_t base = static_cast<size_t>(w);
     float *R = a.R + base * DK * DV;
     const int half = static_cast<int>(blockDim.x) / 128;
-    mm<DK, DV, kC>([&](int j, int r) { return s.q[r][j]; }, [&](int r, int i) { return s.dO[r][i]; },
+    mm<DK, DV, kC, kHL>([&](int j, int r) { return s.q[r][j]; }, [&](int r, int i) { return s.dO[r][i]; },
                    [&](int j, int i, float x) { R[j * DV + i] = a.scale * x; }, 0, half);
     float *F = a.F + base * DK * DK;
     const float gl = s.gam[kC - 1];
     if (DELTA) {
-        mm<DK, DK, kC>([&](int j, int r) { return s.W[r][j]; }, [&](int r, int m) { return s.eps[r] * s.k[r][m]; },
+        mm<DK, DK, kC, kHL>([&](int j, int r) { return s.W[r][j]; }, [&](int r, int m) { return s.eps[r] * s.k[r][m]; },
                        [&](int j, int m, float x) { F[j * DK + m] = (j == m ? gl : 0.f) - x; }, half, half);
     } else {
         for (int e = threadIdx.x; e < DK * DK; e += kBTM) F[e] = (e / DK == e % DK) ? gl : 0.f;
@@ -557,7 +588,7 @@ template <int DK, int DV> struct alignas(16) GradLds {
 // The gradient phases of one chunk, from its staged rows, start state S, end-state gradient Y and
 // keyside (the caller has synchronised after staging and zeroed u.red).  s and u are LDS, or (u, for
 // 128-wide heads) a global scratch slot of the workgroup's; the products are the same.
-template <int DK, int DV, bool DELTA>
+template <int DK, int DV, bool DELTA, bool HL>
 __device__ __forceinline__ void grad_phases(const BwdArgs &a, ChunkLds<DK, DV> &s, GradLds<DK, DV> &u,
                                             size_t tok, int h, int L) {
     static_assert(DK == DV, "the dW buffer reuses K Y's");
@@ -565,25 +596,25 @@ __device__ __forceinline__ void grad_phases(const BwdArgs &a, ChunkLds<DK, DV> &
     const int tid = threadIdx.x;
     // Delta = T diag(b) V - W S  (decay rule: diag(b) V);  K Y
     if (DELTA) {
-        mm<kC, DV, kC>([&](int i, int j) { return s.T[i][j]; }, [&](int j, int c) { return s.b[j] * u.v[j][c]; },
+        mm<kC, DV, kC, HL>([&](int i, int j) { return s.T[i][j]; }, [&](int j, int c) { return s.b[j] * u.v[j][c]; },
                        [&](int i, int c, float x) { u.D[i][c] = x; }, 0, 8);
     } else {
         for (int e = tid; e < kC * DV; e += kBTG) u.D[e / DV][e % DV] = s.b[e / DV] * u.v[e / DV][e % DV];
     }
-    mm<kC, DV, DK>([&](int i, int j) { return s.k[i][j]; }, [&](int j, int c) { return u.Yv[j][c]; },
+    mm<kC, DV, DK, HL>([&](int i, int j) { return s.k[i][j]; }, [&](int j, int c) { return u.Yv[j][c]; },
                    [&](int i, int c, float x) { u.KY[i][c] = x; }, 8, 8);
     __syncthreads();
     if (DELTA) {
-        mm<kC, DV, DK>([&](int i, int j) { return s.W[i][j]; }, [&](int j, int c) { return u.S[j][c]; },
+        mm<kC, DV, DK, HL>([&](int i, int j) { return s.W[i][j]; }, [&](int j, int c) { return u.S[j][c]; },
                        [&](int i, int c, float x) { u.D[i][c] -= x; }, 0, 8);
-        rowsum<DK, DV>([&](int j, int i) { return u.Yv[j][i] * u.S[j][i]; }, [&](int j, float x) { u.red64[j] = x; },
+        rowsum<DK, DV, HL>([&](int j, int i) { return u.Yv[j][i] * u.S[j][i]; }, [&](int j, float x) { u.red64[j] = x; },
                        8, 4);
         __syncthreads();
     }
     // dDelta = scale P^T dO + diag(eps) K Y;  dP = scale tril(dO Delta^T)
-    mm<kC, DV, kC>([&](int i, int r) { return s.P[r][i]; }, [&](int r, int c) { return s.dO[r][c]; },
+    mm<kC, DV, kC, HL>([&](int i, int r) { return s.P[r][i]; }, [&](int r, int c) { return s.dO[r][c]; },
                    [&](int i, int c, float x) { u.dD[i][c] = a.scale * x + s.eps[i] * u.KY[i][c]; }, 0, 8);
-    mm<kC, kC, DV>([&](int r, int c) { return s.dO[r][c]; }, [&](int c, int j) { return u.D[j][c]; },
+    mm<kC, kC, DV, HL>([&](int r, int c) { return s.dO[r][c]; }, [&](int c, int j) { return u.D[j][c]; },
                    [&](int r, int j, float x) {
                        const float dp = j <= r ? a.scale * x : 0.f;
                        u.dPg[r][j] = dp * (j <= r ? expf(s.G[r] - s.G[j]) : 0.f);
@@ -591,20 +622,20 @@ __device__ __forceinline__ void grad_phases(const BwdArgs &a, ChunkLds<DK, DV> &
                    },
                    8, 4);
     if (!DELTA)
-        rowsum<DK, DV>([&](int j, int i) { return u.Yv[j][i] * u.S[j][i]; }, [&](int j, float x) { u.red64[j] = x; },
+        rowsum<DK, DV, HL>([&](int j, int i) { return u.Yv[j][i] * u.S[j][i]; }, [&](int j, float x) { u.red64[j] = x; },
                        12, 4);
     __syncthreads();
     // row reductions for the gate and write-strength gradients: P, the end-state decay
-    rowsum<kC, kC>([&](int i, int k) { return u.X1[i][k]; }, [&](int i, float x) { u.red[0][i] = x; }, 8, 2);
-    rowsum<kC, kC>([&](int i, int k) { return u.X1[k][i]; }, [&](int i, float x) { u.red[1][i] = x; }, 10, 2);
-    rowsum<kC, DV>([&](int i, int c) { return u.KY[i][c] * u.D[i][c]; }, [&](int i, float x) { u.red[2][i] = x; }, 12, 2);
+    rowsum<kC, kC, HL>([&](int i, int k) { return u.X1[i][k]; }, [&](int i, float x) { u.red[0][i] = x; }, 8, 2);
+    rowsum<kC, kC, HL>([&](int i, int k) { return u.X1[k][i]; }, [&](int i, float x) { u.red[1][i] = x; }, 10, 2);
+    rowsum<kC, DV, HL>([&](int i, int c) { return u.KY[i][c] * u.D[i][c]; }, [&](int i, float x) { u.red[2][i] = x; }, 12, 2);
 
     // dQ = scale diag(gam) dO S^T (+ its gate term) + (dP .* Gam) K, into W's buffer
-    mm<kC, DK, DV>([&](int r, int i) { return s.dO[r][i]; }, [&](int i, int c) { return u.S[c][i]; },
+    mm<kC, DK, DV, HL>([&](int r, int i) { return s.dO[r][i]; }, [&](int i, int c) { return u.S[c][i]; },
                    [&](int r, int c, float x) { s.W[r][c] = a.scale * s.gam[r] * x; }, 0, 8);
     __syncthreads();
-    rowsum<kC, DK>([&](int i, int c) { return s.q[i][c] * s.W[i][c]; }, [&](int i, float x) { u.red[3][i] = x; }, 8, 2);
-    mm<kC, DK, kC>([&](int r, int j) { return u.dPg[r][j]; }, [&](int j, int c) { return s.k[j][c]; },
+    rowsum<kC, DK, HL>([&](int i, int c) { return s.q[i][c] * s.W[i][c]; }, [&](int i, float x) { u.red[3][i] = x; }, 8, 2);
+    mm<kC, DK, kC, HL>([&](int r, int j) { return u.dPg[r][j]; }, [&](int j, int c) { return s.k[j][c]; },
                    [&](int r, int c, float x) {
                        if (r < L) a.dq[((tok + r) * a.H + h) * DK + c] = s.W[r][c] + x;
                    },
@@ -612,44 +643,44 @@ __device__ __forceinline__ void grad_phases(const BwdArgs &a, ChunkLds<DK, DV> &
     // dW = -dDelta S^T (into K Y's buffer), T^T dDelta
     __syncthreads();
     if (DELTA) {
-        mm<kC, DK, DV>([&](int i, int l) { return u.dD[i][l]; }, [&](int l, int c) { return u.S[c][l]; },
+        mm<kC, DK, DV, HL>([&](int i, int l) { return u.dD[i][l]; }, [&](int l, int c) { return u.S[c][l]; },
                        [&](int i, int c, float x) { u.KY[i][c] = -x; }, 0, 8);
-        mm<kC, DV, kC>([&](int j, int i) { return s.T[i][j]; }, [&](int i, int c) { return u.dD[i][c]; },
+        mm<kC, DV, kC, HL>([&](int j, int i) { return s.T[i][j]; }, [&](int i, int c) { return u.dD[i][c]; },
                        [&](int j, int c, float x) { u.TdU[j][c] = x; }, 8, 8);
         __syncthreads();
-        mm<kC, DK, kC>([&](int j, int i) { return s.T[i][j]; }, [&](int i, int c) { return u.KY[i][c]; },
+        mm<kC, DK, kC, HL>([&](int j, int i) { return s.T[i][j]; }, [&](int i, int c) { return u.KY[i][c]; },
                        [&](int j, int c, float x) { u.TdW[j][c] = x; }, 0, 8);
         // dT = dW (diag(b gam) K)^T + dDelta (diag(b) V)^T
-        mm<kC, kC, DK>([&](int i, int c) { return u.KY[i][c]; },
+        mm<kC, kC, DK, HL>([&](int i, int c) { return u.KY[i][c]; },
                        [&](int c, int j) { return s.b[j] * s.gam[j] * s.k[j][c]; },
                        [&](int i, int j, float x) { u.dT[i][j] = x; }, 8, 4);
         __syncthreads();
-        mm<kC, kC, DV>([&](int i, int c) { return u.dD[i][c]; }, [&](int c, int j) { return s.b[j] * u.v[j][c]; },
+        mm<kC, kC, DV, HL>([&](int i, int c) { return u.dD[i][c]; }, [&](int c, int j) { return s.b[j] * u.v[j][c]; },
                        [&](int i, int j, float x) { u.dT[i][j] += x; }, 0, 4);
-        rowsum<kC, DK>([&](int i, int c) { return u.TdW[i][c] * s.k[i][c]; }, [&](int i, float x) { u.red[7][i] = x; }, 4, 2);
-        rowsum<kC, DV>([&](int i, int c) { return u.TdU[i][c] * u.v[i][c]; }, [&](int i, float x) { u.red[8][i] = x; }, 6, 2);
+        rowsum<kC, DK, HL>([&](int i, int c) { return u.TdW[i][c] * s.k[i][c]; }, [&](int i, float x) { u.red[7][i] = x; }, 4, 2);
+        rowsum<kC, DV, HL>([&](int i, int c) { return u.TdU[i][c] * u.v[i][c]; }, [&](int i, float x) { u.red[8][i] = x; }, 6, 2);
         __syncthreads();
         // dA = -T^T (dT T^T), strictly lower
-        mm<kC, kC, kC>([&](int i, int l) { return u.dT[i][l]; }, [&](int l, int j) { return s.T[j][l]; },
+        mm<kC, kC, kC, HL>([&](int i, int l) { return u.dT[i][l]; }, [&](int l, int j) { return s.T[j][l]; },
                        [&](int i, int j, float x) { u.Z[i][j] = x; });
         __syncthreads();
-        mm<kC, kC, kC>([&](int i, int l) { return s.T[l][i]; }, [&](int l, int j) { return u.Z[l][j]; },
+        mm<kC, kC, kC, HL>([&](int i, int l) { return s.T[l][i]; }, [&](int l, int j) { return u.Z[l][j]; },
                        [&](int i, int j, float x) {
                            const float da = j < i ? -x : 0.f;
                            u.dT[i][j] = da;                        // dA
                            u.X1[i][j] = da * s.b[i] * s.KG[i][j];  // dA .* A
                        });
         __syncthreads();
-        rowsum<kC, kC>([&](int i, int k) { return u.X1[i][k]; }, [&](int i, float x) { u.red[4][i] = x; }, 0, 2);
-        rowsum<kC, kC>([&](int i, int k) { return u.X1[k][i]; }, [&](int i, float x) { u.red[5][i] = x; }, 2, 2);
-        rowsum<kC, kC>([&](int i, int k) { return u.dT[i][k] * s.KG[i][k]; }, [&](int i, float x) { u.red[6][i] = x; }, 4, 2);
+        rowsum<kC, kC, HL>([&](int i, int k) { return u.X1[i][k]; }, [&](int i, float x) { u.red[4][i] = x; }, 0, 2);
+        rowsum<kC, kC, HL>([&](int i, int k) { return u.X1[k][i]; }, [&](int i, float x) { u.red[5][i] = x; }, 2, 2);
+        rowsum<kC, kC, HL>([&](int i, int k) { return u.dT[i][k] * s.KG[i][k]; }, [&](int i, float x) { u.red[6][i] = x; }, 4, 2);
         // E = diag(b) dA .* Gam, kept in Z
         for (int e = tid; e < kC * kC; e += kBTG) {
             const int i = e / kC, j = e % kC;
             u.Z[i][j] = j < i ? s.b[i] * u.dT[i][j] * expf(s.G[i] - s.G[j]) : 0.f;
         }
     } else {
-        rowsum<kC, DV>([&](int i, int c) { return u.dD[i][c] * u.v[i][c]; }, [&](int i, float x) { u.red[8][i] = x; }, 6, 2);
+        rowsum<kC, DV, HL>([&](int i, int c) { return u.dD[i][c] * u.v[i][c]; }, [&](int i, float x) { u.red[8][i] = x; }, 6, 2);
     }
     __syncthreads();
     // combine: dG per position, db, and the last position's end-state terms (one wavefront)
@@ -679,18 +710,18 @@ __device__ __forceinline__ void grad_phases(const BwdArgs &a, ChunkLds<DK, DV> &
         if (r < L) a.dv[((tok + r) * a.H + h) * DV + c] = s.b[r] * (DELTA ? u.TdU[r][c] : u.dD[r][c]);
     }
     // dK = (dP .* Gam)^T Q + diag(eps) Delta Y^T [+ diag(b gam) T^T dW + E K + E^T K]
-    mm<kC, DK, kC>([&](int j, int r) { return u.dPg[r][j]; }, [&](int r, int c) { return s.q[r][c]; },
+    mm<kC, DK, kC, HL>([&](int j, int r) { return u.dPg[r][j]; }, [&](int r, int c) { return s.q[r][c]; },
                    [&](int j, int c, float x) { s.W[j][c] = x; }, 8, 8);
     __syncthreads();
     // dg: reverse cumulative sum of dG inside the chunk (upper-triangular ones); dbeta
     mm<kC, 16, kC>([](int i, int j) { return j >= i ? 1.f : 0.f; }, [&](int j, int) { return u.dG[j]; },
                    [&](int i, int c, float x) { if (c == 0 && i < L) a.dg[(tok + i) * a.H + h] = x; }, 0, 2);
     if (tid < L) a.dbeta[(tok + tid) * a.H + h] = u.dbv[tid];
-    mm<kC, DK, DV>([&](int j, int i) { return u.D[j][i]; }, [&](int i, int c) { return u.Yv[c][i]; },
+    mm<kC, DK, DV, HL>([&](int j, int i) { return u.D[j][i]; }, [&](int i, int c) { return u.Yv[c][i]; },
                    [&](int j, int c, float x) { s.W[j][c] += s.eps[j] * x; }, 8, 8);
     __syncthreads();
     if (DELTA) {
-        mm<kC, DK, kC>([&](int i, int j) { return u.Z[i][j] + u.Z[j][i]; }, [&](int j, int c) { return s.k[j][c]; },
+        mm<kC, DK, kC, HL>([&](int i, int j) { return u.Z[i][j] + u.Z[j][i]; }, [&](int j, int c) { return s.k[j][c]; },
                        [&](int i, int c, float x) { s.W[i][c] += x + s.b[i] * s.gam[i] * u.TdW[i][c]; }, 8, 8);
         __syncthreads();
     }
@@ -719,7 +750,7 @@ __global__ __launch_bounds__(kBTG) void bwd_grad_kernel(BwdArgs a) {
     if (tid < kC)
         for (int m = 0; m < 9; ++m) u.red[m][tid] = 0.f;
     __syncthreads();
-    grad_phases<DK, DV, DELTA>(a, s, u, pos.tok, pos.h, pos.L);
+    grad_phases<DK, DV, DELTA, sizeof(TIn) == 2>(a, s, u, pos.tok, pos.h, pos.L);
 }
 
 // 128-wide heads: the chunk rows and keyside in LDS (81 KB), the rest of the gradient pass's
@@ -770,7 +801,7 @@ __global__ __launch_bounds__(kBTG) void bwd_grad_gs_kernel(BwdArgs a, GradLds<DK
             for (int m = 0; m < 9; ++m) u.red[m][tid] = 0.f;
         }
         __syncthreads();
-        grad_phases<DK, DV, DELTA>(a, s, u, p.tok, p.h, p.L);
+        grad_phases<DK, DV, DELTA, sizeof(TIn) == 2>(a, s, u, p.tok, p.h, p.L);
         __syncthreads();  // the next chunk restages s and u
     }
 }
