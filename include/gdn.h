@@ -110,7 +110,11 @@ typedef enum gdn_rule GDN_ENUM_INT {
  * (I + tril(diag(b) K K^T * decay)) solved by forward substitution, the
  * W/U products, a scan of the fp32 state from chunk to chunk, and outputs as
  * the intra-chunk term plus Q times the chunk's start state.  The result
- * equals the token-by-token rule up to rounding.
+ * equals the token-by-token rule up to rounding.  The final state is the
+ * fixed-size hidden state a GDN layer keeps per request in place of a KV
+ * cache, so a long prompt can be fed in successive calls with the state
+ * carried between them (ftxj.github.io digest of arXiv 2604.24715, Key Ideas;
+ * Figure 5 runs such hybrids to 2M-token contexts).
  *
  *   q, k           [B, T, H, d_k]  qkv_dtype
  *   v              [B, T, H, d_v]  qkv_dtype
@@ -202,7 +206,11 @@ GDN_API gdn_status gdn_chunk_prefill_noalloc(gdn_rule rule,
 
 /*
  * gdn_decode_step -- one token for each of N independent sequences: the rule
- * with T = 1, applied to a batch of per-sequence states in place.
+ * with T = 1, applied to a batch of per-sequence states in place.  The state
+ * has a fixed size, so a step costs the same at any context length (we0.ai
+ * article on Priming: attention layers converted into fixed-state SSM layers;
+ * ftxj.github.io digest of arXiv 2604.24715, Figure 5: with the recurrent
+ * layers' fixed state, time per output token stays about level from 8K to 64K).
  *
  *   q, k      [N, H, d_k]  qkv_dtype
  *   v         [N, H, d_v]  qkv_dtype
