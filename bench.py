@@ -750,7 +750,7 @@ def main():
             "flops_per_call": bwd_flops,
             "note": "forward recompute (keeps chunk start states) + per-chunk maps + reverse scan + per-chunk "
                     "gradients; products as three-pass hi/lo bf16 MFMA (fp32-class results) except the gate "
-                    "prefix sums, the 16x16 inverse blocks and the scan (fp32 MFMA); FLOPs are the gradient "
+                    "prefix sums and the 16x16 inverse blocks (fp32 MFMA); FLOPs are the gradient "
                     "kernels' useful multiply-adds x 2, alu_frac against the fp32 peak (the precision delivered)",
         },
         "backward_3b_shape": {

@@ -465,7 +465,9 @@ struct ScanArgs {
     int items;               // workgroups with work (the grid is rounded up to a multiple of 8)
 };
 
-template <int DK, int DV, int MODE>
+// HL (bf16 inputs): the products F_n Y_n as three-pass hi/lo bf16 MFMA (F's rows already sit in
+// the k-slot order kmap gives: slots 0-3 and 4-7 of step s are F's float4s 2 s and 2 s + 1)
+template <int DK, int DV, int MODE, bool HL = false>
 __global__ __launch_bounds__(kBT<DK>) void bwd_scan_kernel(ScanArgs a) {
     static_assert(DK % 16 == 0 && DV % kSW == 0, "one 16-row tile of Y per wavefront");
     constexpr int BT = kBT<DK>;
@@ -531,15 +533,36 @@ __global__ __launch_bounds__(kBT<DK>) void bwd_scan_kernel(ScanArgs a) {
         f32x4 acc[SW / 16];
 #pragma unroll
         for (int t = 0; t < SW / 16; ++t) acc[t] = Rc[t];
+        if constexpr (HL) {
 #pragma unroll
-        for (int blk = 0; blk < DK / 16; ++blk) {
-            const float fa[4] = {Fc[blk].x, Fc[blk].y, Fc[blk].z, Fc[blk].w};
+            for (int s2 = 0; s2 < DK / 32; ++s2) {
+                const float4 f0 = Fc[2 * s2], f1 = Fc[2 * s2 + 1];
+                const float xa[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+                bf16x8 fh, fl;
+                split_bf16(xa, fh, fl);
 #pragma unroll
-            for (int mm = 0; mm < 4; ++mm)
+                for (int t = 0; t < SW / 16; ++t) {
+                    float xb[8];
 #pragma unroll
-                for (int t = 0; t < SW / 16; ++t)
-                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[mm], Yb[cur][16 * blk + 4 * lk + mm][16 * t + li],
-                                                                  acc[t], 0, 0, 0);
+                    for (int e = 0; e < 8; ++e) xb[e] = Yb[cur][kmap(s2, lk, e)][16 * t + li];
+                    bf16x8 yh, yl;
+                    split_bf16(xb, yh, yl);
+                    acc[t] = mfma_bf16(fh, yh, acc[t]);
+                    acc[t] = mfma_bf16(fh, yl, acc[t]);
+                    acc[t] = mfma_bf16(fl, yh, acc[t]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int blk = 0; blk < DK / 16; ++blk) {
+                const float fa[4] = {Fc[blk].x, Fc[blk].y, Fc[blk].z, Fc[blk].w};
+#pragma unroll
+                for (int mm = 0; mm < 4; ++mm)
+#pragma unroll
+                    for (int t = 0; t < SW / 16; ++t)
+                        acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[mm], Yb[cur][16 * blk + 4 * lk + mm][16 * t + li],
+                                                                      acc[t], 0, 0, 0);
+            }
         }
 #pragma unroll
         for (int t = 0; t < SW / 16; ++t)
@@ -844,21 +867,25 @@ hipError_t run_backward(BwdArgs &a, gdn_dtype dt, const ScanPlan &plan, float *G
     if (plan.P == 1) {
         sa.y_end = a.ds_final; sa.y_start = a.ds0; sa.m = a.N; sa.P = 1;
         sa.items = a.BH * (DV / kSW);
-        hipLaunchKernelGGL((bwd_scan_kernel<DK, DV, kScanAll>), grid8(sa.items), dim3(kBT<DK>), 0, stream, sa);
+        if (bf) hipLaunchKernelGGL((bwd_scan_kernel<DK, DV, kScanAll, true>), grid8(sa.items), dim3(kBT<DK>), 0, stream, sa);
+        else hipLaunchKernelGGL((bwd_scan_kernel<DK, DV, kScanAll, false>), grid8(sa.items), dim3(kBT<DK>), 0, stream, sa);
     } else {
         // piece maps, then the chain over pieces (the same scan with piece maps as its steps), then
         // every chunk's Y inside each piece from the piece's end value
         sa.m = plan.m; sa.P = plan.P; sa.Gp = Gp; sa.cp = cp;
         sa.items = a.BH * plan.P * ((DV + DK) / kSW);
-        hipLaunchKernelGGL((bwd_scan_kernel<DK, DV, kScanMap>), grid8(sa.items), dim3(kBT<DK>), 0, stream, sa);
+        if (bf) hipLaunchKernelGGL((bwd_scan_kernel<DK, DV, kScanMap, true>), grid8(sa.items), dim3(kBT<DK>), 0, stream, sa);
+        else hipLaunchKernelGGL((bwd_scan_kernel<DK, DV, kScanMap, false>), grid8(sa.items), dim3(kBT<DK>), 0, stream, sa);
         ScanArgs ch{};
         ch.F = Gp; ch.R = cp; ch.Y = yend; ch.y_end = a.ds_final; ch.y_start = a.ds0;
         ch.steps = plan.P; ch.m = plan.P; ch.P = 1;
         ch.items = a.BH * (DV / kSW);
-        hipLaunchKernelGGL((bwd_scan_kernel<DK, DV, kScanAll>), grid8(ch.items), dim3(kBT<DK>), 0, stream, ch);
+        if (bf) hipLaunchKernelGGL((bwd_scan_kernel<DK, DV, kScanAll, true>), grid8(ch.items), dim3(kBT<DK>), 0, stream, ch);
+        else hipLaunchKernelGGL((bwd_scan_kernel<DK, DV, kScanAll, false>), grid8(ch.items), dim3(kBT<DK>), 0, stream, ch);
         sa.y_end = yend;
         sa.items = a.BH * plan.P * (DV / kSW);
-        hipLaunchKernelGGL((bwd_scan_kernel<DK, DV, kScanPiece>), grid8(sa.items), dim3(kBT<DK>), 0, stream, sa);
+        if (bf) hipLaunchKernelGGL((bwd_scan_kernel<DK, DV, kScanPiece, true>), grid8(sa.items), dim3(kBT<DK>), 0, stream, sa);
+        else hipLaunchKernelGGL((bwd_scan_kernel<DK, DV, kScanPiece, false>), grid8(sa.items), dim3(kBT<DK>), 0, stream, sa);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || items == 0) return e;
