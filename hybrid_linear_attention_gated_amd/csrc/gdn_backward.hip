@@ -589,14 +589,13 @@ __global__ __launch_bounds__(kBT<DK>) void bwd_scan_kernel(ScanArgs a) {
 }
 
 // ---- all gradients of one chunk -----------------------------------------------
+// The gradient pass's matrices in two parts: GradLds always in LDS, GradBig in LDS for 64-wide
+// heads and in a global scratch slot for 128-wide ones (the start state and its gradient alone are
+// 128 KB there).
 template <int DK, int DV> struct alignas(16) GradLds {
-    float v[kC][DV + kPD];
-    float S[DK][DV + kPD], Yv[DK][DV + kPD];
     float D[kC][DV + kPD];     // Delta
     float dD[kC][DV + kPD];    // dDelta
     float KY[kC][DV + kPD];    // K Y, later dW (DV == DK)
-    float TdW[kC][DK + kPD];   // T^T dW
-    float TdU[kC][DV + kPD];   // T^T dDelta
     float dPg[kC][kCP];      // dP .* Gam
     float X1[kC][kCP];       // dP .* P, later dA .* A
     float dT[kC][kCP];       // dT, later dA
@@ -605,6 +604,12 @@ template <int DK, int DV> struct alignas(16) GradLds {
     float red64[DK];         // row sums of Y .* S
     float dG[kC], dbv[kC];
 };
+template <int DK, int DV> struct alignas(16) GradBig {
+    float v[kC][DV + kPD];
+    float S[DK][DV + kPD], Yv[DK][DV + kPD];
+    float TdW[kC][DK + kPD];   // T^T dW
+    float TdU[kC][DV + kPD];   // T^T dDelta
+};
 
 // Independent products of a phase run side by side on disjoint wavefronts of the 16
 // (ranges in the calls' last two arguments).
@@ -612,25 +617,25 @@ template <int DK, int DV> struct alignas(16) GradLds {
 // keyside (the caller has synchronised after staging and zeroed u.red).  s and u are LDS, or (u, for
 // 128-wide heads) a global scratch slot of the workgroup's; the products are the same.
 template <int DK, int DV, bool DELTA, bool HL>
-__device__ __forceinline__ void grad_phases(const BwdArgs &a, ChunkLds<DK, DV> &s, GradLds<DK, DV> &u,
+__device__ __forceinline__ void grad_phases(const BwdArgs &a, ChunkLds<DK, DV> &s, GradLds<DK, DV> &u, GradBig<DK, DV> &g,
                                             size_t tok, int h, int L) {
     static_assert(DK == DV, "the dW buffer reuses K Y's");
     static_assert(kBTG == 1024, "the phases below are laid out for 16 wavefronts");
     const int tid = threadIdx.x;
     // Delta = T diag(b) V - W S  (decay rule: diag(b) V);  K Y
     if (DELTA) {
-        mm<kC, DV, kC, HL>([&](int i, int j) { return s.T[i][j]; }, [&](int j, int c) { return s.b[j] * u.v[j][c]; },
+        mm<kC, DV, kC, HL>([&](int i, int j) { return s.T[i][j]; }, [&](int j, int c) { return s.b[j] * g.v[j][c]; },
                        [&](int i, int c, float x) { u.D[i][c] = x; }, 0, 8);
     } else {
-        for (int e = tid; e < kC * DV; e += kBTG) u.D[e / DV][e % DV] = s.b[e / DV] * u.v[e / DV][e % DV];
+        for (int e = tid; e < kC * DV; e += kBTG) u.D[e / DV][e % DV] = s.b[e / DV] * g.v[e / DV][e % DV];
     }
-    mm<kC, DV, DK, HL>([&](int i, int j) { return s.k[i][j]; }, [&](int j, int c) { return u.Yv[j][c]; },
+    mm<kC, DV, DK, HL>([&](int i, int j) { return s.k[i][j]; }, [&](int j, int c) { return g.Yv[j][c]; },
                    [&](int i, int c, float x) { u.KY[i][c] = x; }, 8, 8);
     __syncthreads();
     if (DELTA) {
-        mm<kC, DV, DK, HL>([&](int i, int j) { return s.W[i][j]; }, [&](int j, int c) { return u.S[j][c]; },
+        mm<kC, DV, DK, HL>([&](int i, int j) { return s.W[i][j]; }, [&](int j, int c) { return g.S[j][c]; },
                        [&](int i, int c, float x) { u.D[i][c] -= x; }, 0, 8);
-        rowsum<DK, DV, HL>([&](int j, int i) { return u.Yv[j][i] * u.S[j][i]; }, [&](int j, float x) { u.red64[j] = x; },
+        rowsum<DK, DV, HL>([&](int j, int i) { return g.Yv[j][i] * g.S[j][i]; }, [&](int j, float x) { u.red64[j] = x; },
                        8, 4);
         __syncthreads();
     }
@@ -645,7 +650,7 @@ __device__ __forceinline__ void grad_phases(const BwdArgs &a, ChunkLds<DK, DV> &
                    },
                    8, 4);
     if (!DELTA)
-        rowsum<DK, DV, HL>([&](int j, int i) { return u.Yv[j][i] * u.S[j][i]; }, [&](int j, float x) { u.red64[j] = x; },
+        rowsum<DK, DV, HL>([&](int j, int i) { return g.Yv[j][i] * g.S[j][i]; }, [&](int j, float x) { u.red64[j] = x; },
                        12, 4);
     __syncthreads();
     // row reductions for the gate and write-strength gradients: P, the end-state decay
@@ -654,7 +659,7 @@ __device__ __forceinline__ void grad_phases(const BwdArgs &a, ChunkLds<DK, DV> &
     rowsum<kC, DV, HL>([&](int i, int c) { return u.KY[i][c] * u.D[i][c]; }, [&](int i, float x) { u.red[2][i] = x; }, 12, 2);
 
     // dQ = scale diag(gam) dO S^T (+ its gate term) + (dP .* Gam) K, into W's buffer
-    mm<kC, DK, DV, HL>([&](int r, int i) { return s.dO[r][i]; }, [&](int i, int c) { return u.S[c][i]; },
+    mm<kC, DK, DV, HL>([&](int r, int i) { return s.dO[r][i]; }, [&](int i, int c) { return g.S[c][i]; },
                    [&](int r, int c, float x) { s.W[r][c] = a.scale * s.gam[r] * x; }, 0, 8);
     __syncthreads();
     rowsum<kC, DK, HL>([&](int i, int c) { return s.q[i][c] * s.W[i][c]; }, [&](int i, float x) { u.red[3][i] = x; }, 8, 2);
@@ -666,22 +671,22 @@ __device__ __forceinline__ void grad_phases(const BwdArgs &a, ChunkLds<DK, DV> &
     // dW = -dDelta S^T (into K Y's buffer), T^T dDelta
     __syncthreads();
     if (DELTA) {
-        mm<kC, DK, DV, HL>([&](int i, int l) { return u.dD[i][l]; }, [&](int l, int c) { return u.S[c][l]; },
+        mm<kC, DK, DV, HL>([&](int i, int l) { return u.dD[i][l]; }, [&](int l, int c) { return g.S[c][l]; },
                        [&](int i, int c, float x) { u.KY[i][c] = -x; }, 0, 8);
         mm<kC, DV, kC, HL>([&](int j, int i) { return s.T[i][j]; }, [&](int i, int c) { return u.dD[i][c]; },
-                       [&](int j, int c, float x) { u.TdU[j][c] = x; }, 8, 8);
+                       [&](int j, int c, float x) { g.TdU[j][c] = x; }, 8, 8);
         __syncthreads();
         mm<kC, DK, kC, HL>([&](int j, int i) { return s.T[i][j]; }, [&](int i, int c) { return u.KY[i][c]; },
-                       [&](int j, int c, float x) { u.TdW[j][c] = x; }, 0, 8);
+                       [&](int j, int c, float x) { g.TdW[j][c] = x; }, 0, 8);
         // dT = dW (diag(b gam) K)^T + dDelta (diag(b) V)^T
         mm<kC, kC, DK, HL>([&](int i, int c) { return u.KY[i][c]; },
                        [&](int c, int j) { return s.b[j] * s.gam[j] * s.k[j][c]; },
                        [&](int i, int j, float x) { u.dT[i][j] = x; }, 8, 4);
         __syncthreads();
-        mm<kC, kC, DV, HL>([&](int i, int c) { return u.dD[i][c]; }, [&](int c, int j) { return s.b[j] * u.v[j][c]; },
+        mm<kC, kC, DV, HL>([&](int i, int c) { return u.dD[i][c]; }, [&](int c, int j) { return s.b[j] * g.v[j][c]; },
                        [&](int i, int j, float x) { u.dT[i][j] += x; }, 0, 4);
-        rowsum<kC, DK, HL>([&](int i, int c) { return u.TdW[i][c] * s.k[i][c]; }, [&](int i, float x) { u.red[7][i] = x; }, 4, 2);
-        rowsum<kC, DV, HL>([&](int i, int c) { return u.TdU[i][c] * u.v[i][c]; }, [&](int i, float x) { u.red[8][i] = x; }, 6, 2);
+        rowsum<kC, DK, HL>([&](int i, int c) { return g.TdW[i][c] * s.k[i][c]; }, [&](int i, float x) { u.red[7][i] = x; }, 4, 2);
+        rowsum<kC, DV, HL>([&](int i, int c) { return g.TdU[i][c] * g.v[i][c]; }, [&](int i, float x) { u.red[8][i] = x; }, 6, 2);
         __syncthreads();
         // dA = -T^T (dT T^T), strictly lower
         mm<kC, kC, kC, HL>([&](int i, int l) { return u.dT[i][l]; }, [&](int l, int j) { return s.T[j][l]; },
@@ -703,7 +708,7 @@ __device__ __forceinline__ void grad_phases(const BwdArgs &a, ChunkLds<DK, DV> &
             u.Z[i][j] = j < i ? s.b[i] * u.dT[i][j] * expf(s.G[i] - s.G[j]) : 0.f;
         }
     } else {
-        rowsum<kC, DV, HL>([&](int i, int c) { return u.dD[i][c] * u.v[i][c]; }, [&](int i, float x) { u.red[8][i] = x; }, 6, 2);
+        rowsum<kC, DV, HL>([&](int i, int c) { return u.dD[i][c] * g.v[i][c]; }, [&](int i, float x) { u.red[8][i] = x; }, 6, 2);
     }
     __syncthreads();
     // combine: dG per position, db, and the last position's end-state terms (one wavefront)
@@ -730,7 +735,7 @@ __device__ __forceinline__ void grad_phases(const BwdArgs &a, ChunkLds<DK, DV> &
     // dV = diag(b) T^T dDelta (decay rule: diag(b) dDelta)
     for (int e = tid; e < kC * DV; e += kBTG) {
         const int r = e / DV, c = e % DV;
-        if (r < L) a.dv[((tok + r) * a.H + h) * DV + c] = s.b[r] * (DELTA ? u.TdU[r][c] : u.dD[r][c]);
+        if (r < L) a.dv[((tok + r) * a.H + h) * DV + c] = s.b[r] * (DELTA ? g.TdU[r][c] : u.dD[r][c]);
     }
     // dK = (dP .* Gam)^T Q + diag(eps) Delta Y^T [+ diag(b gam) T^T dW + E K + E^T K]
     mm<kC, DK, kC, HL>([&](int j, int r) { return u.dPg[r][j]; }, [&](int r, int c) { return s.q[r][c]; },
@@ -740,12 +745,12 @@ __device__ __forceinline__ void grad_phases(const BwdArgs &a, ChunkLds<DK, DV> &
     mm<kC, 16, kC>([](int i, int j) { return j >= i ? 1.f : 0.f; }, [&](int j, int) { return u.dG[j]; },
                    [&](int i, int c, float x) { if (c == 0 && i < L) a.dg[(tok + i) * a.H + h] = x; }, 0, 2);
     if (tid < L) a.dbeta[(tok + tid) * a.H + h] = u.dbv[tid];
-    mm<kC, DK, DV, HL>([&](int j, int i) { return u.D[j][i]; }, [&](int i, int c) { return u.Yv[c][i]; },
+    mm<kC, DK, DV, HL>([&](int j, int i) { return u.D[j][i]; }, [&](int i, int c) { return g.Yv[c][i]; },
                    [&](int j, int c, float x) { s.W[j][c] += s.eps[j] * x; }, 8, 8);
     __syncthreads();
     if (DELTA) {
         mm<kC, DK, kC, HL>([&](int i, int j) { return u.Z[i][j] + u.Z[j][i]; }, [&](int j, int c) { return s.k[j][c]; },
-                       [&](int i, int c, float x) { s.W[i][c] += x + s.b[i] * s.gam[i] * u.TdW[i][c]; }, 8, 8);
+                       [&](int i, int c, float x) { s.W[i][c] += x + s.b[i] * s.gam[i] * g.TdW[i][c]; }, 8, 8);
         __syncthreads();
     }
     for (int e = tid; e < kC * DK; e += kBTG) {
@@ -758,6 +763,7 @@ template <int DK, int DV, typename TIn, bool DELTA>
 __global__ __launch_bounds__(kBTG) void bwd_grad_kernel(BwdArgs a) {
     __shared__ ChunkLds<DK, DV> s;
     __shared__ GradLds<DK, DV> u;
+    __shared__ GradBig<DK, DV> g;
     const int tid = threadIdx.x;
     const int w = blockIdx.x;
     const ChunkPos pos = chunk_pos(a, w);
@@ -767,21 +773,23 @@ __global__ __launch_bounds__(kBTG) void bwd_grad_kernel(BwdArgs a) {
         KsRows ks{};
         chunk_load<kBTG, DK, DV, TIn, true>(a, w, rows);
         keyside_load<DK, DELTA>(a, w, ks);
-        chunk_stage<kBTG, DK, DV, true>(rows, s, u.v, u.S, u.Yv);
+        chunk_stage<kBTG, DK, DV, true>(rows, s, g.v, g.S, g.Yv);
         keyside_stage<DK, DV, DELTA>(ks, s);
     }
     if (tid < kC)
         for (int m = 0; m < 9; ++m) u.red[m][tid] = 0.f;
     __syncthreads();
-    grad_phases<DK, DV, DELTA, sizeof(TIn) == 2>(a, s, u, pos.tok, pos.h, pos.L);
+    grad_phases<DK, DV, DELTA, sizeof(TIn) == 2>(a, s, u, g, pos.tok, pos.h, pos.L);
 }
 
-// 128-wide heads: the chunk rows and keyside in LDS (81 KB), the rest of the gradient pass's
-// matrices (270 KB) in the workgroup's global scratch slot; the workgroups loop over the chunks.
+// 128-wide heads: the chunk rows, keyside and the chunk-sized intermediates in LDS (151 KB), the
+// start state, its gradient, V and the two T^T products (183 KB) in the workgroup's global scratch
+// slot; the workgroups loop over the chunks.
 template <int DK, int DV, typename TIn, bool DELTA>
-__global__ __launch_bounds__(kBTG) void bwd_grad_gs_kernel(BwdArgs a, GradLds<DK, DV> *scratch) {
+__global__ __launch_bounds__(kBTG) void bwd_grad_gs_kernel(BwdArgs a, GradBig<DK, DV> *scratch) {
     __shared__ ChunkLds<DK, DV> s;
-    GradLds<DK, DV> &u = scratch[blockIdx.x];
+    __shared__ GradLds<DK, DV> u;
+    GradBig<DK, DV> &g = scratch[blockIdx.x];
     const int tid = threadIdx.x;
     const TIn *q = static_cast<const TIn *>(a.q), *k = static_cast<const TIn *>(a.k), *v = static_cast<const TIn *>(a.v);
     for (int w = blockIdx.x; w < a.BH * a.N; w += gridDim.x) {
@@ -796,12 +804,12 @@ __global__ __launch_bounds__(kBTG) void bwd_grad_gs_kernel(BwdArgs a, GradLds<DK
             const int r = e / DV, c = e % DV;
             const size_t x = ((p.tok + r) * a.H + p.h) * DV + c;
             s.dO[r][c] = r < p.L ? a.d_o[x] : 0.f;
-            u.v[r][c] = r < p.L ? load_in(v, x) : 0.f;
+            g.v[r][c] = r < p.L ? load_in(v, x) : 0.f;
         }
         const size_t sx = static_cast<size_t>(w) * DK * DV;
         for (int e = tid; e < DK * DV; e += kBTG) {
-            u.S[e / DV][e % DV] = a.states[sx + e];
-            u.Yv[e / DV][e % DV] = a.Y[sx + e];
+            g.S[e / DV][e % DV] = a.states[sx + e];
+            g.Yv[e / DV][e % DV] = a.Y[sx + e];
         }
         // the keyside its map pass stored: T, KG, P (C x C each), W (C x DK), G, gam, eps
         const float *ks = a.KS + static_cast<size_t>(w) * ks_floats<DK>();
@@ -824,7 +832,7 @@ __global__ __launch_bounds__(kBTG) void bwd_grad_gs_kernel(BwdArgs a, GradLds<DK
             for (int m = 0; m < 9; ++m) u.red[m][tid] = 0.f;
         }
         __syncthreads();
-        grad_phases<DK, DV, DELTA, sizeof(TIn) == 2>(a, s, u, p.tok, p.h, p.L);
+        grad_phases<DK, DV, DELTA, sizeof(TIn) == 2>(a, s, u, g, p.tok, p.h, p.L);
         __syncthreads();  // the next chunk restages s and u
     }
 }
@@ -890,7 +898,7 @@ hipError_t run_backward(BwdArgs &a, gdn_dtype dt, const ScanPlan &plan, float *G
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || items == 0) return e;
     if constexpr (kGradGlobal<DK, DV>) {
-        auto *slots = static_cast<GradLds<DK, DV> *>(a.gscratch);
+        auto *slots = static_cast<GradBig<DK, DV> *>(a.gscratch);
         const dim3 grid(items < kGradSlots ? items : kGradSlots);
         if (bf) hipLaunchKernelGGL((bwd_grad_gs_kernel<DK, DV, uint16_t, DELTA>), grid, dim3(kBTG), 0, stream, a, slots);
         else hipLaunchKernelGGL((bwd_grad_gs_kernel<DK, DV, float, DELTA>), grid, dim3(kBTG), 0, stream, a, slots);
@@ -923,7 +931,7 @@ BwdLayout bwd_layout(int B, int T, int H, int dk, int dv) {
     L.Gp = off; off += align256(BH * PP * dk * dk * 4);
     L.cp = off; off += align256(BH * PP * dk * dv * 4);
     L.yend = off; off += align256(BH * PP * dk * dv * 4);
-    L.gs = off; off += dk == 128 ? align256(kGradSlots * sizeof(GradLds<128, 128>)) : 0;
+    L.gs = off; off += dk == 128 ? align256(kGradSlots * sizeof(GradBig<128, 128>)) : 0;
     L.total = off;
     return L;
 }

@@ -519,7 +519,7 @@ GDN_API size_t gdn_prepare_varlen_workspace_size(int S);
  * Supported: qkv_dtype GDN_BF16 or GDN_F32, d_k = d_v in {64, 128}; both
  * rules.  T may be 0 (then d_initial_state = d_final_state, or zeros).  For
  * 128-wide heads the workspace also holds 256 slots of the gradient pass's
- * per-chunk matrices (about 69 MB), which do not fit on chip.
+ * larger per-chunk matrices (about 47 MB), which do not fit on chip.
  * Errors: GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_UNSUPPORTED, GDN_ERR_ALIGN,
  * GDN_ERR_ALIAS (an output overlapping an input, another output or the
  * workspace), GDN_ERR_WORKSPACE, GDN_ERR_HIP.
