@@ -27,9 +27,12 @@
 // (gdn_prefill_chunk.hip): bwd_map_kernel (F and R of every chunk, chunks in
 // parallel), bwd_scan_kernel (Y of every chunk, chunks in reverse order; long
 // sequences in two levels of pieces) and bwd_grad_kernel (all gradients, chunks in
-// parallel).  fp32 arithmetic (matrix cores for the products) on LDS-resident chunk matrices;
-// 128-wide heads keep the gradient pass's larger matrices (the state and its gradient alone are
-// 128 KB) in a global scratch slot per workgroup instead (bwd_grad_gs_kernel).
+// parallel), on LDS-resident chunk matrices; 128-wide heads keep the gradient pass's largest
+// matrices (the state and its gradient alone are 128 KB) in a global scratch slot per workgroup
+// instead (bwd_grad_gs_kernel).  Products run on the matrix cores: for bf16 inputs as three-pass
+// hi/lo bf16 MFMA (fp32-class results; one or two passes measured over the error bar), except the
+// gate prefix sums and the 16 x 16 blocks of the inverse, which stay fp32; fp32 inputs keep every
+// product in fp32.
 #include "gdn_mfma.h"
 
 namespace gdn {

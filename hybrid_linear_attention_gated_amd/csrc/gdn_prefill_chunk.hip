@@ -432,7 +432,7 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
     constexpr bool kShareTB = kMergeBC && !PREP;
     __shared__ __align__(16) bf16x8 tbs_s[kShareTB ? 2 * G::CT * kWave : 1];  // (ct * 2 + hi/lo) * 64 + lane
     // 128 x 128 heads (one workgroup per compute unit, so no other workgroup's work hides OUT's
-    // keyside): MAP stores those fragments and OUT loads them (3B-shaped 64K call 1.56 -> 1.45 ms).
+    // keyside): MAP stores those fragments and OUT loads them (3B-shaped 64K call 1.56 -> 1.48 ms).
     // With three workgroups per compute unit the 64 x 64 kernels gain nothing from it (MAP +17 us
     // for the stores, OUT -20 us).
     constexpr bool kTfrag = kShareTB && DK == 128 && C == 32;
