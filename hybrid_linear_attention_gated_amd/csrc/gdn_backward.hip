@@ -85,7 +85,10 @@ struct BwdArgs {
 // operands split into hi + lo bf16 and three passes (hi.hi + hi.lo + lo.hi): about 16 significant
 // bits per operand, fp32 accumulation.  Lane (lk, li) feeds the k-slots kmap(s, lk, e) of row
 // i0 + li of A and of column j0 + li of B; the output layout is the same.
-template <int M, int N, int K, bool HL = false, class FA, class FB, class FS>
+// NP (with HL): the passes taken, a mask of 1 = hi.hi, 2 = hi(A).lo(B), 4 = lo(A).hi(B).  Where an
+// operand is exact in bf16 (the q and k inputs, the ones of a row sum) its lo part is zero, and the
+// pass that would multiply it is left out (and the part not computed): the same results.
+template <int M, int N, int K, bool HL = false, int NP = 7, class FA, class FB, class FS>
 __device__ __forceinline__ void mm(FA A, FB Bm, FS store, int w0 = 0, int nw = 0) {
     static_assert(M % 16 == 0 && N % 16 == 0 && K % 4 == 0, "tile");
     constexpr int TN = N / 16, TILES = (M / 16) * TN;
@@ -107,11 +110,13 @@ __device__ __forceinline__ void mm(FA A, FB Bm, FS store, int w0 = 0, int nw = 0
                     xb[e] = Bm(kk, j0 + li);
                 }
                 bf16x8 ah, al, bh, bl;
-                split_bf16(xa, ah, al);
-                split_bf16(xb, bh, bl);
+                if constexpr ((NP & 4) != 0) split_bf16(xa, ah, al);
+                else ah = pack_bf16(xa);
+                if constexpr ((NP & 2) != 0) split_bf16(xb, bh, bl);
+                else bh = pack_bf16(xb);
                 acc = mfma_bf16(ah, bh, acc);
-                acc = mfma_bf16(ah, bl, acc);
-                acc = mfma_bf16(al, bh, acc);
+                if constexpr ((NP & 2) != 0) acc = mfma_bf16(ah, bl, acc);
+                if constexpr ((NP & 4) != 0) acc = mfma_bf16(al, bh, acc);
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) store(i0 + 4 * lk + r, j0 + li, acc[r]);
@@ -144,7 +149,7 @@ __device__ __forceinline__ void mm(FA A, FB Bm, FS store, int w0 = 0, int nw = 0
 // sum_kk A(i, kk) for i < M, by a product with a block of ones; store(i, x).
 template <int M, int K, bool HL = false, class FA, class FS>
 __device__ __forceinline__ void rowsum(FA A, FS store, int w0 = 0, int nw = 0) {
-    mm<M, 16, K, HL>(A, [](int, int) { return 1.f; }, [&](int i, int j, float x) { if (j == 0) store(i, x); }, w0, nw);
+    mm<M, 16, K, HL, 5>(A, [](int, int) { return 1.f; }, [&](int i, int j, float x) { if (j == 0) store(i, x); }, w0, nw);
 }
 
 // x as held by lane l of the wavefront (l a constant; a uniform value)
@@ -292,10 +297,10 @@ __device__ void chunk_keyside(ChunkLds<DK, DV> &s) {
     }
     // P and K K^T with the decay of every pair (exponents are <= 0 below the diagonal)
     const int half = static_cast<int>(blockDim.x) / 128;  // wavefronts in each half of the workgroup
-    mm<kC, kC, DK, HL>([&](int i, int kk) { return s.q[i][kk]; }, [&](int kk, int j) { return s.k[j][kk]; },
+    mm<kC, kC, DK, HL, 1>([&](int i, int kk) { return s.q[i][kk]; }, [&](int kk, int j) { return s.k[j][kk]; },
                    [&](int i, int j, float x) { s.P[i][j] = j <= i ? x * expf(s.G[i] - s.G[j]) : 0.f; }, 0, half);
     if (DELTA)
-        mm<kC, kC, DK, HL>([&](int i, int kk) { return s.k[i][kk]; }, [&](int kk, int j) { return s.k[j][kk]; },
+        mm<kC, kC, DK, HL, 1>([&](int i, int kk) { return s.k[i][kk]; }, [&](int kk, int j) { return s.k[j][kk]; },
                        [&](int i, int j, float x) { s.KG[i][j] = j < i ? x * expf(s.G[i] - s.G[j]) : 0.f; },
                        half, half);
     __syncthreads();
@@ -632,7 +637,7 @@ __device__ __forceinline__ void grad_phases(const BwdArgs &a, ChunkLds<DK, DV> &
     } else {
         for (int e = tid; e < kC * DV; e += kBTG) u.D[e / DV][e % DV] = s.b[e / DV] * g.v[e / DV][e % DV];
     }
-    mm<kC, DV, DK, HL>([&](int i, int j) { return s.k[i][j]; }, [&](int j, int c) { return g.Yv[j][c]; },
+    mm<kC, DV, DK, HL, 3>([&](int i, int j) { return s.k[i][j]; }, [&](int j, int c) { return g.Yv[j][c]; },
                    [&](int i, int c, float x) { u.KY[i][c] = x; }, 8, 8);
     __syncthreads();
     if (DELTA) {
@@ -666,7 +671,7 @@ __device__ __forceinline__ void grad_phases(const BwdArgs &a, ChunkLds<DK, DV> &
                    [&](int r, int c, float x) { s.W[r][c] = a.scale * s.gam[r] * x; }, 0, 8);
     __syncthreads();
     rowsum<kC, DK, HL>([&](int i, int c) { return s.q[i][c] * s.W[i][c]; }, [&](int i, float x) { u.red[3][i] = x; }, 8, 2);
-    mm<kC, DK, kC, HL>([&](int r, int j) { return u.dPg[r][j]; }, [&](int j, int c) { return s.k[j][c]; },
+    mm<kC, DK, kC, HL, 5>([&](int r, int j) { return u.dPg[r][j]; }, [&](int j, int c) { return s.k[j][c]; },
                    [&](int r, int c, float x) {
                        if (r < L) a.dq[((tok + r) * a.H + h) * DK + c] = s.W[r][c] + x;
                    },
@@ -741,7 +746,7 @@ __device__ __forceinline__ void grad_phases(const BwdArgs &a, ChunkLds<DK, DV> &
         if (r < L) a.dv[((tok + r) * a.H + h) * DV + c] = s.b[r] * (DELTA ? g.TdU[r][c] : u.dD[r][c]);
     }
     // dK = (dP .* Gam)^T Q + diag(eps) Delta Y^T [+ diag(b gam) T^T dW + E K + E^T K]
-    mm<kC, DK, kC, HL>([&](int j, int r) { return u.dPg[r][j]; }, [&](int r, int c) { return s.q[r][c]; },
+    mm<kC, DK, kC, HL, 5>([&](int j, int r) { return u.dPg[r][j]; }, [&](int r, int c) { return s.q[r][c]; },
                    [&](int j, int c, float x) { s.W[j][c] = x; }, 8, 8);
     __syncthreads();
     // dg: reverse cumulative sum of dG inside the chunk (upper-triangular ones); dbeta
@@ -752,7 +757,7 @@ __device__ __forceinline__ void grad_phases(const BwdArgs &a, ChunkLds<DK, DV> &
                    [&](int j, int c, float x) { s.W[j][c] += s.eps[j] * x; }, 8, 8);
     __syncthreads();
     if (DELTA) {
-        mm<kC, DK, kC, HL>([&](int i, int j) { return u.Z[i][j] + u.Z[j][i]; }, [&](int j, int c) { return s.k[j][c]; },
+        mm<kC, DK, kC, HL, 5>([&](int i, int j) { return u.Z[i][j] + u.Z[j][i]; }, [&](int j, int c) { return s.k[j][c]; },
                        [&](int i, int c, float x) { s.W[i][c] += x + s.b[i] * s.gam[i] * g.TdW[i][c]; }, 8, 8);
         __syncthreads();
     }
