@@ -94,6 +94,7 @@ size_t prefill_chunk_workspace(int B, int T, int H, int dk, int dv, int chunk, b
 // built from them, the piece maps and the piece start states.
 struct VarlenLayout {
     int pc, NP, NM, chunk;   // chunks per piece, global pieces, global maps, chunk size
+    int out_per_xcd;         // OUT's piece slots per XCD (ceil(NP / 8))
     size_t table_ints, maps_off, starts_off, bytes;
 };
 bool varlen_layout(const int *cu, int S, int H, int dk, int dv, int chunk, VarlenLayout *L);

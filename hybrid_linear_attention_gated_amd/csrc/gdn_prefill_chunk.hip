@@ -39,6 +39,7 @@
 // already holds what the chunk writes), T diag(b) in U, the state in Q St, P and Delta
 // in P Delta, the decayed Delta in the state update, and both factors of the
 // inversion's block products.
+#include <algorithm>
 #include <type_traits>
 #include <vector>
 
@@ -159,6 +160,9 @@ struct Cfg {
 struct SeqTable {
     const int *piece_seq, *map_seq;
     const int *tok0, *len, *pstart, *mstart, *slot, *init;
+    // OUT: the global piece of each work-item slot (kXcds x out_per_xcd slots, -1 = none): the
+    // pieces dealt to the XCDs in balanced bins, each bin longest first
+    const int *out_order;
 };
 
 struct ChunkArgs {
@@ -483,7 +487,8 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
         if (!MAP && piece == a.P - 1) final_out = a.s_final + bh * DK * DV;
         if (!MAP && STATES) states_out = a.chunk_states + bh * a.N * DK * DV;
     } else {
-        const int gp = w / a.H;  // global piece (OUT) or global map (MAP)
+        const int gp = MAP ? w / a.H : a.sq.out_order[w / a.H];  // global map (MAP) or piece (OUT)
+        if (gp < 0) return;  // an empty slot of the dealing (uniform over the workgroup)
         h = w % a.H;
         const int s = MAP ? a.sq.map_seq[gp] : a.sq.piece_seq[gp];
         const int piece = gp - (MAP ? a.sq.mstart[s] : a.sq.pstart[s]);
@@ -1780,6 +1785,7 @@ hipError_t run_chunk_varlen(const uint16_t *q, const uint16_t *k, const uint16_t
     sq.mstart = sq.pstart + S + 1;
     sq.slot = sq.mstart + S + 1;
     sq.init = sq.slot + S;
+    sq.out_order = sq.init + S;
     float *maps = reinterpret_cast<float *>(static_cast<char *>(ws) + L.maps_off);
     float *starts = reinterpret_cast<float *>(static_cast<char *>(ws) + L.starts_off);
     ChunkArgs a{};
@@ -1801,7 +1807,7 @@ hipError_t run_chunk_varlen(const uint16_t *q, const uint16_t *k, const uint16_t
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || L.NP == 0) return err;
     a.s_start = starts;
-    a.items = L.NP * H;
+    a.items = kXcds * L.out_per_xcd * H;  // a multiple of kXcds: each XCD's range holds whole piece slots
     hipLaunchKernelGGL((chunk_kernel<DK, DV, C, false, DELTA>), grid(a.items), dim3(kWave * kWavesOf<DK, DV>), 0, stream, a);
     return hipGetLastError();
 }
@@ -1823,12 +1829,14 @@ bool varlen_layout(const int *cu, int S, int H, int dk, int dv, int chunk, Varle
         NP += P;
         NM += P > 1 ? P - 1 : 0;
     }
-    if (NP * H > 0x7fffffffLL || static_cast<long long>(S) * H * (dv / 16) > 0x7fffffffLL) return false;
+    if ((NP + kXcds) * H > 0x7fffffffLL || static_cast<long long>(S) * H * (dv / 16) > 0x7fffffffLL) return false;
     L->chunk = chunk;
     L->pc = static_cast<int>(pc);
     L->NP = static_cast<int>(NP);
     L->NM = static_cast<int>(NM);
-    L->table_ints = static_cast<size_t>(NP + NM) + 6 * static_cast<size_t>(S) + 2;
+    L->out_per_xcd = static_cast<int>((NP + kXcds - 1) / kXcds);
+    L->table_ints = static_cast<size_t>(NP + NM) + 6 * static_cast<size_t>(S) + 2 +
+                    static_cast<size_t>(kXcds) * L->out_per_xcd;
     auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
     L->maps_off = up(L->table_ints * 4);
     L->starts_off = L->maps_off + up(static_cast<size_t>(NM) * H * dk * (dv + dk) * 4);
@@ -1855,6 +1863,32 @@ void varlen_table(const int *cu, int S, const int *slots, const int *init, const
     }
     pstart[S] = gp;
     mstart[S] = gm;
+    // OUT's dealing: work items go to the XCDs in contiguous ranges of out_per_xcd piece slots, and
+    // the dispatcher starts them in index order.  Pieces by length (chunks), longest first, each to
+    // the XCD with the least work so far that has a free slot; inside an XCD longest first, so no long
+    // prompt starts last and no XCD gets all the long ones.
+    int *order = ini + S;
+    const int ppx = L.out_per_xcd;
+    std::vector<int> chunks(static_cast<size_t>(L.NP)), byLen(static_cast<size_t>(L.NP));
+    for (int s = 0; s < S; ++s) {
+        const int nchunks = (len[s] + L.chunk - 1) / L.chunk;
+        for (int p = pstart[s]; p < pstart[s + 1]; ++p) {
+            const int left = nchunks - (p - pstart[s]) * L.pc;
+            chunks[p] = left < L.pc ? left : L.pc;
+        }
+    }
+    for (int p = 0; p < L.NP; ++p) byLen[p] = p;
+    std::stable_sort(byLen.begin(), byLen.end(), [&](int x, int y) { return chunks[x] > chunks[y]; });
+    long long load[kXcds] = {};
+    int used[kXcds] = {};
+    for (int i = 0; i < kXcds * ppx; ++i) order[i] = -1;
+    for (int p : byLen) {
+        int best = -1;
+        for (int x = 0; x < kXcds; ++x)
+            if (used[x] < ppx && (best < 0 || load[x] < load[best])) best = x;
+        order[best * ppx + used[best]++] = p;
+        load[best] += chunks[p];
+    }
 }
 
 hipError_t launch_prefill_chunk_varlen(const uint16_t *q, const uint16_t *k, const uint16_t *v,
