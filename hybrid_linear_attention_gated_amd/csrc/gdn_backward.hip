@@ -75,6 +75,16 @@ struct BwdArgs {
     void *gscratch;       // 128-wide heads: the gradient pass's global scratch slots
 };
 
+// threadIdx.x, read so that the compiler takes it as a new value: a kernel that loops over chunks
+// reads it once per chunk and passes it to the chunk's products, which then derive their per-lane
+// LDS addresses inside the iteration instead of holding them all in registers across the loop
+// (which spills).
+__device__ __forceinline__ int thread_id() {
+    int t = static_cast<int>(threadIdx.x);
+    asm volatile("" : "+v"(t));
+    return t;
+}
+
 // out(i, j) = sum_kk A(i, kk) B(kk, j) for i < M, j < N, on the fp32 matrix cores:
 // 16 x 16 output tiles dealt round-robin to wavefronts w0 .. w0 + nw - 1 (nw = 0: all of
 // the workgroup's), so independent products can run side by side; each tile accumulated by
@@ -88,11 +98,12 @@ struct BwdArgs {
 // NP (with HL): the passes taken, a mask of 1 = hi.hi, 2 = hi(A).lo(B), 4 = lo(A).hi(B).  Where an
 // operand is exact in bf16 (the q and k inputs, the ones of a row sum) its lo part is zero, and the
 // pass that would multiply it is left out (and the part not computed): the same results.
+// tid: threadIdx.x, passed in (see thread_id).
 template <int M, int N, int K, bool HL = false, int NP = 7, class FA, class FB, class FS>
-__device__ __forceinline__ void mm(FA A, FB Bm, FS store, int w0 = 0, int nw = 0) {
+__device__ __forceinline__ void mm_t(int tid, FA A, FB Bm, FS store, int w0 = 0, int nw = 0) {
     static_assert(M % 16 == 0 && N % 16 == 0 && K % 4 == 0, "tile");
     constexpr int TN = N / 16, TILES = (M / 16) * TN;
-    const int lane = threadIdx.x % 64, wave = static_cast<int>(threadIdx.x / 64) - w0;
+    const int lane = tid % 64, wave = __builtin_amdgcn_readfirstlane(tid / 64) - w0;
     const int li = lane % 16, lk = lane / 16;
     const int waves = nw > 0 ? nw : static_cast<int>(blockDim.x) / 64;
     if (wave < 0 || wave >= waves) return;
@@ -146,10 +157,16 @@ __device__ __forceinline__ void mm(FA A, FB Bm, FS store, int w0 = 0, int nw = 0
     }
 }
 
+template <int M, int N, int K, bool HL = false, int NP = 7, class FA, class FB, class FS>
+__device__ __forceinline__ void mm(FA A, FB Bm, FS store, int w0 = 0, int nw = 0) {
+    mm_t<M, N, K, HL, NP>(static_cast<int>(threadIdx.x), A, Bm, store, w0, nw);
+}
+
 // sum_kk A(i, kk) for i < M, by a product with a block of ones; store(i, x).
 template <int M, int K, bool HL = false, class FA, class FS>
-__device__ __forceinline__ void rowsum(FA A, FS store, int w0 = 0, int nw = 0) {
-    mm<M, 16, K, HL, 5>(A, [](int, int) { return 1.f; }, [&](int i, int j, float x) { if (j == 0) store(i, x); }, w0, nw);
+__device__ __forceinline__ void rowsum_t(int tid, FA A, FS store, int w0 = 0, int nw = 0) {
+    mm_t<M, 16, K, HL, 5>(tid, A, [](int, int) { return 1.f; }, [&](int i, int j, float x) { if (j == 0) store(i, x); },
+                          w0, nw);
 }
 
 // x as held by lane l of the wavefront (l a constant; a uniform value)
@@ -622,35 +639,35 @@ template <int DK, int DV> struct alignas(16) GradBig {
 // Independent products of a phase run side by side on disjoint wavefronts of the 16
 // (ranges in the calls' last two arguments).
 // The gradient phases of one chunk, from its staged rows, start state S, end-state gradient Y and
-// keyside (the caller has synchronised after staging and zeroed u.red).  s and u are LDS, or (u, for
-// 128-wide heads) a global scratch slot of the workgroup's; the products are the same.
+// keyside (the caller has synchronised after staging and zeroed u.red); tid = threadIdx.x.  s and u
+// are LDS, or (u, for 128-wide heads) a global scratch slot of the workgroup's; the products are the
+// same.
 template <int DK, int DV, bool DELTA, bool HL>
 __device__ __forceinline__ void grad_phases(const BwdArgs &a, ChunkLds<DK, DV> &s, GradLds<DK, DV> &u, GradBig<DK, DV> &g,
-                                            size_t tok, int h, int L) {
+                                            size_t tok, int h, int L, int tid) {
     static_assert(DK == DV, "the dW buffer reuses K Y's");
     static_assert(kBTG == 1024, "the phases below are laid out for 16 wavefronts");
-    const int tid = threadIdx.x;
     // Delta = T diag(b) V - W S  (decay rule: diag(b) V);  K Y
     if (DELTA) {
-        mm<kC, DV, kC, HL>([&](int i, int j) { return s.T[i][j]; }, [&](int j, int c) { return s.b[j] * g.v[j][c]; },
+        mm_t<kC, DV, kC, HL>(tid, [&](int i, int j) { return s.T[i][j]; }, [&](int j, int c) { return s.b[j] * g.v[j][c]; },
                        [&](int i, int c, float x) { u.D[i][c] = x; }, 0, 8);
     } else {
         for (int e = tid; e < kC * DV; e += kBTG) u.D[e / DV][e % DV] = s.b[e / DV] * g.v[e / DV][e % DV];
     }
-    mm<kC, DV, DK, HL, 3>([&](int i, int j) { return s.k[i][j]; }, [&](int j, int c) { return g.Yv[j][c]; },
+    mm_t<kC, DV, DK, HL, 3>(tid, [&](int i, int j) { return s.k[i][j]; }, [&](int j, int c) { return g.Yv[j][c]; },
                    [&](int i, int c, float x) { u.KY[i][c] = x; }, 8, 8);
     __syncthreads();
     if (DELTA) {
-        mm<kC, DV, DK, HL>([&](int i, int j) { return s.W[i][j]; }, [&](int j, int c) { return g.S[j][c]; },
+        mm_t<kC, DV, DK, HL>(tid, [&](int i, int j) { return s.W[i][j]; }, [&](int j, int c) { return g.S[j][c]; },
                        [&](int i, int c, float x) { u.D[i][c] -= x; }, 0, 8);
-        rowsum<DK, DV, HL>([&](int j, int i) { return g.Yv[j][i] * g.S[j][i]; }, [&](int j, float x) { u.red64[j] = x; },
+        rowsum_t<DK, DV, HL>(tid, [&](int j, int i) { return g.Yv[j][i] * g.S[j][i]; }, [&](int j, float x) { u.red64[j] = x; },
                        8, 4);
         __syncthreads();
     }
     // dDelta = scale P^T dO + diag(eps) K Y;  dP = scale tril(dO Delta^T)
-    mm<kC, DV, kC, HL>([&](int i, int r) { return s.P[r][i]; }, [&](int r, int c) { return s.dO[r][c]; },
+    mm_t<kC, DV, kC, HL>(tid, [&](int i, int r) { return s.P[r][i]; }, [&](int r, int c) { return s.dO[r][c]; },
                    [&](int i, int c, float x) { u.dD[i][c] = a.scale * x + s.eps[i] * u.KY[i][c]; }, 0, 8);
-    mm<kC, kC, DV, HL>([&](int r, int c) { return s.dO[r][c]; }, [&](int c, int j) { return u.D[j][c]; },
+    mm_t<kC, kC, DV, HL>(tid, [&](int r, int c) { return s.dO[r][c]; }, [&](int c, int j) { return u.D[j][c]; },
                    [&](int r, int j, float x) {
                        const float dp = j <= r ? a.scale * x : 0.f;
                        u.dPg[r][j] = dp * (j <= r ? expf(s.G[r] - s.G[j]) : 0.f);
@@ -658,20 +675,20 @@ __device__ __forceinline__ void grad_phases(const BwdArgs &a, ChunkLds<DK, DV> &
                    },
                    8, 4);
     if (!DELTA)
-        rowsum<DK, DV, HL>([&](int j, int i) { return g.Yv[j][i] * g.S[j][i]; }, [&](int j, float x) { u.red64[j] = x; },
+        rowsum_t<DK, DV, HL>(tid, [&](int j, int i) { return g.Yv[j][i] * g.S[j][i]; }, [&](int j, float x) { u.red64[j] = x; },
                        12, 4);
     __syncthreads();
     // row reductions for the gate and write-strength gradients: P, the end-state decay
-    rowsum<kC, kC, HL>([&](int i, int k) { return u.X1[i][k]; }, [&](int i, float x) { u.red[0][i] = x; }, 8, 2);
-    rowsum<kC, kC, HL>([&](int i, int k) { return u.X1[k][i]; }, [&](int i, float x) { u.red[1][i] = x; }, 10, 2);
-    rowsum<kC, DV, HL>([&](int i, int c) { return u.KY[i][c] * u.D[i][c]; }, [&](int i, float x) { u.red[2][i] = x; }, 12, 2);
+    rowsum_t<kC, kC, HL>(tid, [&](int i, int k) { return u.X1[i][k]; }, [&](int i, float x) { u.red[0][i] = x; }, 8, 2);
+    rowsum_t<kC, kC, HL>(tid, [&](int i, int k) { return u.X1[k][i]; }, [&](int i, float x) { u.red[1][i] = x; }, 10, 2);
+    rowsum_t<kC, DV, HL>(tid, [&](int i, int c) { return u.KY[i][c] * u.D[i][c]; }, [&](int i, float x) { u.red[2][i] = x; }, 12, 2);
 
     // dQ = scale diag(gam) dO S^T (+ its gate term) + (dP .* Gam) K, into W's buffer
-    mm<kC, DK, DV, HL>([&](int r, int i) { return s.dO[r][i]; }, [&](int i, int c) { return g.S[c][i]; },
+    mm_t<kC, DK, DV, HL>(tid, [&](int r, int i) { return s.dO[r][i]; }, [&](int i, int c) { return g.S[c][i]; },
                    [&](int r, int c, float x) { s.W[r][c] = a.scale * s.gam[r] * x; }, 0, 8);
     __syncthreads();
-    rowsum<kC, DK, HL>([&](int i, int c) { return s.q[i][c] * s.W[i][c]; }, [&](int i, float x) { u.red[3][i] = x; }, 8, 2);
-    mm<kC, DK, kC, HL, 5>([&](int r, int j) { return u.dPg[r][j]; }, [&](int j, int c) { return s.k[j][c]; },
+    rowsum_t<kC, DK, HL>(tid, [&](int i, int c) { return s.q[i][c] * s.W[i][c]; }, [&](int i, float x) { u.red[3][i] = x; }, 8, 2);
+    mm_t<kC, DK, kC, HL, 5>(tid, [&](int r, int j) { return u.dPg[r][j]; }, [&](int j, int c) { return s.k[j][c]; },
                    [&](int r, int c, float x) {
                        if (r < L) a.dq[((tok + r) * a.H + h) * DK + c] = s.W[r][c] + x;
                    },
@@ -679,44 +696,44 @@ __device__ __forceinline__ void grad_phases(const BwdArgs &a, ChunkLds<DK, DV> &
     // dW = -dDelta S^T (into K Y's buffer), T^T dDelta
     __syncthreads();
     if (DELTA) {
-        mm<kC, DK, DV, HL>([&](int i, int l) { return u.dD[i][l]; }, [&](int l, int c) { return g.S[c][l]; },
+        mm_t<kC, DK, DV, HL>(tid, [&](int i, int l) { return u.dD[i][l]; }, [&](int l, int c) { return g.S[c][l]; },
                        [&](int i, int c, float x) { u.KY[i][c] = -x; }, 0, 8);
-        mm<kC, DV, kC, HL>([&](int j, int i) { return s.T[i][j]; }, [&](int i, int c) { return u.dD[i][c]; },
+        mm_t<kC, DV, kC, HL>(tid, [&](int j, int i) { return s.T[i][j]; }, [&](int i, int c) { return u.dD[i][c]; },
                        [&](int j, int c, float x) { g.TdU[j][c] = x; }, 8, 8);
         __syncthreads();
-        mm<kC, DK, kC, HL>([&](int j, int i) { return s.T[i][j]; }, [&](int i, int c) { return u.KY[i][c]; },
+        mm_t<kC, DK, kC, HL>(tid, [&](int j, int i) { return s.T[i][j]; }, [&](int i, int c) { return u.KY[i][c]; },
                        [&](int j, int c, float x) { g.TdW[j][c] = x; }, 0, 8);
         // dT = dW (diag(b gam) K)^T + dDelta (diag(b) V)^T
-        mm<kC, kC, DK, HL>([&](int i, int c) { return u.KY[i][c]; },
+        mm_t<kC, kC, DK, HL>(tid, [&](int i, int c) { return u.KY[i][c]; },
                        [&](int c, int j) { return s.b[j] * s.gam[j] * s.k[j][c]; },
                        [&](int i, int j, float x) { u.dT[i][j] = x; }, 8, 4);
         __syncthreads();
-        mm<kC, kC, DV, HL>([&](int i, int c) { return u.dD[i][c]; }, [&](int c, int j) { return s.b[j] * g.v[j][c]; },
+        mm_t<kC, kC, DV, HL>(tid, [&](int i, int c) { return u.dD[i][c]; }, [&](int c, int j) { return s.b[j] * g.v[j][c]; },
                        [&](int i, int j, float x) { u.dT[i][j] += x; }, 0, 4);
-        rowsum<kC, DK, HL>([&](int i, int c) { return g.TdW[i][c] * s.k[i][c]; }, [&](int i, float x) { u.red[7][i] = x; }, 4, 2);
-        rowsum<kC, DV, HL>([&](int i, int c) { return g.TdU[i][c] * g.v[i][c]; }, [&](int i, float x) { u.red[8][i] = x; }, 6, 2);
+        rowsum_t<kC, DK, HL>(tid, [&](int i, int c) { return g.TdW[i][c] * s.k[i][c]; }, [&](int i, float x) { u.red[7][i] = x; }, 4, 2);
+        rowsum_t<kC, DV, HL>(tid, [&](int i, int c) { return g.TdU[i][c] * g.v[i][c]; }, [&](int i, float x) { u.red[8][i] = x; }, 6, 2);
         __syncthreads();
         // dA = -T^T (dT T^T), strictly lower
-        mm<kC, kC, kC, HL>([&](int i, int l) { return u.dT[i][l]; }, [&](int l, int j) { return s.T[j][l]; },
+        mm_t<kC, kC, kC, HL>(tid, [&](int i, int l) { return u.dT[i][l]; }, [&](int l, int j) { return s.T[j][l]; },
                        [&](int i, int j, float x) { u.Z[i][j] = x; });
         __syncthreads();
-        mm<kC, kC, kC, HL>([&](int i, int l) { return s.T[l][i]; }, [&](int l, int j) { return u.Z[l][j]; },
+        mm_t<kC, kC, kC, HL>(tid, [&](int i, int l) { return s.T[l][i]; }, [&](int l, int j) { return u.Z[l][j]; },
                        [&](int i, int j, float x) {
                            const float da = j < i ? -x : 0.f;
                            u.dT[i][j] = da;                        // dA
                            u.X1[i][j] = da * s.b[i] * s.KG[i][j];  // dA .* A
                        });
         __syncthreads();
-        rowsum<kC, kC, HL>([&](int i, int k) { return u.X1[i][k]; }, [&](int i, float x) { u.red[4][i] = x; }, 0, 2);
-        rowsum<kC, kC, HL>([&](int i, int k) { return u.X1[k][i]; }, [&](int i, float x) { u.red[5][i] = x; }, 2, 2);
-        rowsum<kC, kC, HL>([&](int i, int k) { return u.dT[i][k] * s.KG[i][k]; }, [&](int i, float x) { u.red[6][i] = x; }, 4, 2);
+        rowsum_t<kC, kC, HL>(tid, [&](int i, int k) { return u.X1[i][k]; }, [&](int i, float x) { u.red[4][i] = x; }, 0, 2);
+        rowsum_t<kC, kC, HL>(tid, [&](int i, int k) { return u.X1[k][i]; }, [&](int i, float x) { u.red[5][i] = x; }, 2, 2);
+        rowsum_t<kC, kC, HL>(tid, [&](int i, int k) { return u.dT[i][k] * s.KG[i][k]; }, [&](int i, float x) { u.red[6][i] = x; }, 4, 2);
         // E = diag(b) dA .* Gam, kept in Z
         for (int e = tid; e < kC * kC; e += kBTG) {
             const int i = e / kC, j = e % kC;
             u.Z[i][j] = j < i ? s.b[i] * u.dT[i][j] * expf(s.G[i] - s.G[j]) : 0.f;
         }
     } else {
-        rowsum<kC, DV, HL>([&](int i, int c) { return u.dD[i][c] * g.v[i][c]; }, [&](int i, float x) { u.red[8][i] = x; }, 6, 2);
+        rowsum_t<kC, DV, HL>(tid, [&](int i, int c) { return u.dD[i][c] * g.v[i][c]; }, [&](int i, float x) { u.red[8][i] = x; }, 6, 2);
     }
     __syncthreads();
     // combine: dG per position, db, and the last position's end-state terms (one wavefront)
@@ -746,18 +763,18 @@ __device__ __forceinline__ void grad_phases(const BwdArgs &a, ChunkLds<DK, DV> &
         if (r < L) a.dv[((tok + r) * a.H + h) * DV + c] = s.b[r] * (DELTA ? g.TdU[r][c] : u.dD[r][c]);
     }
     // dK = (dP .* Gam)^T Q + diag(eps) Delta Y^T [+ diag(b gam) T^T dW + E K + E^T K]
-    mm<kC, DK, kC, HL, 5>([&](int j, int r) { return u.dPg[r][j]; }, [&](int r, int c) { return s.q[r][c]; },
+    mm_t<kC, DK, kC, HL, 5>(tid, [&](int j, int r) { return u.dPg[r][j]; }, [&](int r, int c) { return s.q[r][c]; },
                    [&](int j, int c, float x) { s.W[j][c] = x; }, 8, 8);
     __syncthreads();
     // dg: reverse cumulative sum of dG inside the chunk (upper-triangular ones); dbeta
-    mm<kC, 16, kC>([](int i, int j) { return j >= i ? 1.f : 0.f; }, [&](int j, int) { return u.dG[j]; },
+    mm_t<kC, 16, kC>(tid, [](int i, int j) { return j >= i ? 1.f : 0.f; }, [&](int j, int) { return u.dG[j]; },
                    [&](int i, int c, float x) { if (c == 0 && i < L) a.dg[(tok + i) * a.H + h] = x; }, 0, 2);
     if (tid < L) a.dbeta[(tok + tid) * a.H + h] = u.dbv[tid];
-    mm<kC, DK, DV, HL>([&](int j, int i) { return u.D[j][i]; }, [&](int i, int c) { return g.Yv[c][i]; },
+    mm_t<kC, DK, DV, HL>(tid, [&](int j, int i) { return u.D[j][i]; }, [&](int i, int c) { return g.Yv[c][i]; },
                    [&](int j, int c, float x) { s.W[j][c] += s.eps[j] * x; }, 8, 8);
     __syncthreads();
     if (DELTA) {
-        mm<kC, DK, kC, HL, 5>([&](int i, int j) { return u.Z[i][j] + u.Z[j][i]; }, [&](int j, int c) { return s.k[j][c]; },
+        mm_t<kC, DK, kC, HL, 5>(tid, [&](int i, int j) { return u.Z[i][j] + u.Z[j][i]; }, [&](int j, int c) { return s.k[j][c]; },
                        [&](int i, int c, float x) { s.W[i][c] += x + s.b[i] * s.gam[i] * g.TdW[i][c]; }, 8, 8);
         __syncthreads();
     }
@@ -787,12 +804,14 @@ __global__ __launch_bounds__(kBTG) void bwd_grad_kernel(BwdArgs a) {
     if (tid < kC)
         for (int m = 0; m < 9; ++m) u.red[m][tid] = 0.f;
     __syncthreads();
-    grad_phases<DK, DV, DELTA, sizeof(TIn) == 2>(a, s, u, g, pos.tok, pos.h, pos.L);
+    grad_phases<DK, DV, DELTA, sizeof(TIn) == 2>(a, s, u, g, pos.tok, pos.h, pos.L, tid);
 }
 
 // 128-wide heads: the chunk rows, keyside and the chunk-sized intermediates in LDS (151 KB), the
 // start state, its gradient, V and the two T^T products (183 KB) in the workgroup's global scratch
-// slot; the workgroups loop over the chunks.
+// slot; the workgroups loop over the chunks.  Each chunk's products take a thread id read anew for
+// that chunk: with threadIdx.x itself the compiler keeps their addresses live across the loop and
+// spills 107 registers (3B-shaped 8K call 3.04 -> 2.75 ms).
 template <int DK, int DV, typename TIn, bool DELTA>
 __global__ __launch_bounds__(kBTG) void bwd_grad_gs_kernel(BwdArgs a, GradBig<DK, DV> *scratch) {
     __shared__ ChunkLds<DK, DV> s;
@@ -840,7 +859,7 @@ __global__ __launch_bounds__(kBTG) void bwd_grad_gs_kernel(BwdArgs a, GradBig<DK
             for (int m = 0; m < 9; ++m) u.red[m][tid] = 0.f;
         }
         __syncthreads();
-        grad_phases<DK, DV, DELTA, sizeof(TIn) == 2>(a, s, u, g, p.tok, p.h, p.L);
+        grad_phases<DK, DV, DELTA, sizeof(TIn) == 2>(a, s, u, g, p.tok, p.h, p.L, thread_id());
         __syncthreads();  // the next chunk restages s and u
     }
 }
