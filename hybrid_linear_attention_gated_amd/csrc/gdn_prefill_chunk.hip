@@ -85,6 +85,8 @@ template <int N>
 using IC = std::integral_constant<int, N>;
 
 constexpr float kLog2e = 1.4426950408889634f;
+// MAP: the largest element of a piece map's identity slice that may be dropped (2^-32)
+constexpr float kFlush = 0x1p-32f;
 // 2^x by the hardware instruction (the decays here are 2^(non-positive) in log2 units)
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -430,6 +432,10 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
     __shared__ __align__(16) bf16x8 tbf_s[kSplitF ? G::CT * G::CS * 2 * kWave : 1];
     __shared__ float g_s[C], b_s[C], bg_s[C], dec_s[C], gam_s[C];  // g_s: G * log2(e)
     __shared__ int t00_ready;  // the last chunk whose T00 wavefront 0 has stored (kMergeBC)
+    // MAP, gated delta rule (the identity slices dropped below kFlush, in G): grow_s, some chunk of
+    // the piece so far can expand the map (a log gate above 0, or b |k|^2 > 2); flush_s[n & 1], a
+    // wavefront dropped a slice at the end of chunk n (read in chunk n + 1)
+    __shared__ int grow_s, flush_s[2];
     // The hi/lo A-fragments of T diag(b) for G, built once per chunk by wavefronts 0 and 1 at the end
     // of B instead of by every slice wavefront (not in the preparation kernels, whose registers are
     // at the occupancy limit already)
@@ -517,26 +523,32 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
 
     // ---- carried state: St[j][mt] holds rows 16 mt + 4 gq + r, column 16 sl + li, sl = wave + 4 j
     f32x4 St[G::SPW][G::KT];
+    auto init_state = [&]() {
 #pragma unroll
-    for (int j = 0; j < G::SPW; ++j) {
-        const int sl = wave + G::WAVES * j;
+        for (int j = 0; j < G::SPW; ++j) {
+            const int sl = wave + G::WAVES * j;
 #pragma unroll
-        for (int mt = 0; mt < G::KT; ++mt)
+            for (int mt = 0; mt < G::KT; ++mt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = 16 * mt + 4 * gq + r;
-                float x = 0.f;
-                if (MAP) {
-                    if (sl >= G::VT) x = (row == 16 * (sl - G::VT) + li) ? 1.f : 0.f;
-                } else if (start) {
-                    x = start[row * DV + 16 * sl + li];
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * mt + 4 * gq + r;
+                    float x = 0.f;
+                    if (MAP) {
+                        if (sl >= G::VT) x = (row == 16 * (sl - G::VT) + li) ? 1.f : 0.f;
+                    } else if (start) {
+                        x = start[row * DV + 16 * sl + li];
+                    }
+                    St[j][mt][r] = x;
                 }
-                St[j][mt][r] = x;
-            }
-    }
+        }
+    };
+    init_state();
     // T's blocks above the diagonal stay zero for the whole kernel
     for (int e = tid; e < TS_FLOATS; e += G::BLOCK) t_s[e] = 0.f;
-    if (tid == 0) t00_ready = -1;
+    if (tid == 0) {
+        t00_ready = -1;
+        grow_s = flush_s[0] = flush_s[1] = 0;
+    }
     float rate_h = 1.f, bias_h = 0.f;
     if constexpr (PREP) {
         for (int c = tid; c < 2 * DK + DV; c += G::BLOCK) {
@@ -590,13 +602,20 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
 
     R cur;
     if (n0 < n1) load_chunk<DK, DV, C, MAP, PREP>(cur, a, tok_base, seq_len, h, n0, tid, tb_ptr);
-    // MAP, gated delta rule: identity slice j of this wavefront is exactly zero.  Its columns of the piece
-    // map carry no values, so once the decays have taken them below fp32's range they stay zero
-    // (R = -diag(exp G) K 0 = 0, Delta = 0, St' = 0) and the slice is skipped for the rest of the
-    // piece: the same map, computed for less.  What it saves depends on the gates: 64K workload
-    // 0.745 -> 0.727 ms, its literal-gate reading 0.73 -> 0.67 ms, 3B-shaped call 1.49 -> 1.40 ms;
-    // a head whose decays keep the map above fp32's range gains nothing.
+    // MAP, gated delta rule: identity slice j of this wavefront is zero and skipped for the rest of
+    // the piece.  Its columns of the piece map carry no values, so a zero slice stays zero
+    // (R = -diag(exp G) K 0 = 0, Delta = 0, St' = 0).  A slice is zero once the decays have taken it
+    // below fp32's range, or is set to zero once every element is at most kFlush while every token
+    // of the piece so far has a map of norm at most 1 (log gate <= 0 and b |k|^2 <= 2: then each
+    // later token can only shrink what was dropped).  Dropping at most kFlush per element over the
+    // d_k identity columns changes the map by at most d_k kFlush = 2^-25 in norm (d_k <= 128), under
+    // half a unit in the last place of fp32: the piece's end state S_p M_p + N_p moves by less than
+    // its own rounding relative to |S_p|.  A chunk that can expand the map turns the drops off for
+    // the rest of the piece, and if a slice was already dropped, the piece's map is recomputed
+    // from its first chunk without drops.  Gains: 64K workload 0.745 -> 0.705 ms (exact zeros
+    // alone: 0.727), literal-gate reading 0.73 -> 0.67 ms, 3B-shaped call 1.49 -> 1.31 ms.
     bool id_zero[G::SPW] = {};
+    bool flush_ok = true, any_flush = false;
 
     for (int n = n0; n < n1; ++n) {
         const int t0 = n * C;
@@ -729,6 +748,7 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
             const float x = wave_prefix_sum(cur.g) * kLog2e;
             const float glast = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), C - 1));
             if (lane < C) {
+                if (MAP && DELTA && !(cur.g <= 0.f)) grow_s = 1;
                 const float ex = exp2_fast(x);
                 g_s[lane] = x;
                 b_s[lane] = cur.beta;
@@ -780,6 +800,8 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
                     // diagonal tile: exp of a clamped exponent times a 0/1 mask (no branch)
                     const float ex = exp2_fast(fminf(grow[r] - gcol, 0.f));
                     as[row][col] = ((row > col) ? 1.f : 0.f) * (brow[r] * acc[r] * ex);
+                    // the diagonal holds |k_row|^2: the token's map (I - b k k^T) has norm above 1
+                    if (MAP && row == col && !(brow[r] * acc[r] <= 2.f)) grow_s = 1;
                 }
             }
         };
@@ -1226,7 +1248,19 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
         }
 
         // next chunk's rows: loads in flight during this chunk's slice work
-        if (n + 1 < n1) load_chunk<DK, DV, C, MAP, PREP>(cur, a, tok_base, seq_len, h, n + 1, tid, tb_ptr);
+        // MAP: drops in earlier chunks, and whether this chunk ends them (uniform: neither flag is
+        // written again before the barrier that ends the chunk).  A restart loads the piece's first
+        // chunk next instead of chunk n + 1.
+        bool restart = false;
+        if constexpr (MAP && DELTA) {
+            any_flush = any_flush || __builtin_amdgcn_readfirstlane(flush_s[(n - 1) & 1]) != 0;
+            if (flush_ok && __builtin_amdgcn_readfirstlane(grow_s) != 0) {
+                flush_ok = false;
+                restart = any_flush;
+            }
+        }
+        const int next = restart ? n0 : n + 1;
+        if (next < n1) load_chunk<DK, DV, C, MAP, PREP>(cur, a, tok_base, seq_len, h, next, tid, tb_ptr);
         if (MAP && key_only) continue;
 
         // ---- G: per slice: U = (T diag b) V, Delta = U - W St (chunk 32: Delta = T diag(b) R,
@@ -1239,7 +1273,7 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
             static_assert(G::VT % G::WAVES == 0, "value slices");
             const bool value_slice = j < G::VT / G::WAVES;
             if constexpr (MAP && DELTA) {
-                if (!value_slice && id_zero[j]) continue;
+                if (restart || (!value_slice && id_zero[j])) continue;
             }
             if constexpr (!DELTA) {
                 if (!value_slice) {
@@ -1424,12 +1458,19 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
             }
             if constexpr (MAP && DELTA) {
                 if (!value_slice) {
-                    bool nz = false;
+                    // (a NaN counts as large)
+                    const float lim = flush_ok ? kFlush : 0.f;
+                    bool big = false;
 #pragma unroll
                     for (int mt = 0; mt < G::KT; ++mt)
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) nz = nz || St[j][mt][r] != 0.f;
-                    id_zero[j] = __builtin_amdgcn_ballot_w64(nz) == 0;  // uniform over the wavefront
+                        for (int r = 0; r < 4; ++r) big = big || !(fabsf(St[j][mt][r]) <= lim);
+                    id_zero[j] = __builtin_amdgcn_ballot_w64(big) == 0;  // uniform over the wavefront
+                    if (id_zero[j] && flush_ok) {
+#pragma unroll
+                        for (int mt = 0; mt < G::KT; ++mt) St[j][mt] = zero4;
+                        if (lane == 0) flush_s[n & 1] = 1;
+                    }
                 }
             }
             // 128 x 128 maps: two slices per wavefront, one after the other.  Interleaved, their
@@ -1442,6 +1483,17 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
         }
         if constexpr (G::WAVES == 4) __builtin_amdgcn_s_setprio(0);
         __syncthreads();
+        if constexpr (MAP && DELTA) {
+            if (restart) {
+                // the piece's map again from its first chunk (its rows loaded above), with no
+                // drops; wavefront 1 waits for T00 of chunk n0 again
+                init_state();
+#pragma unroll
+                for (int j = 0; j < G::SPW; ++j) id_zero[j] = false;
+                if (tid == 0) t00_ready = n0 - 1;
+                n = n0 - 1;
+            }
+        }
     }
 
     // ---- results

@@ -76,6 +76,23 @@ def test_bf16_sequence_pieces(orc, gate, dk, dv, chunk, T, s0):
     check(orc, d, chunk, TOL["bf16"], f"pieces T={T} dk={dk} dv={dv} gate={gate}")
 
 
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128), (128, 64), (64, 128)])
+def test_map_drops_then_expanding_chunk(orc, dk, dv):
+    """The map pass drops an identity slice once it is below 2^-32 only while no token of the
+    piece so far can expand the map; a later chunk that can (b |k|^2 > 2) makes it recompute the
+    piece's map from its first chunk with no drops.  Even 32-token chunks decay hard (g = -1.1:
+    their maps fall far below 2^-32); odd ones have b = 1 and |k|^2 near 2.2 (the token's map
+    I - b k k^T has an eigenvalue near -1.2).  Pieces of nine chunks start on even and odd chunks
+    in turn: the first drop and then restart, the others stop dropping before any drop.  Every
+    element against the oracle."""
+    d = inputs(1, 4096 + 19, 2, dk, dv, torch.bfloat16)
+    odd = ((torch.arange(d["g"].shape[1], device=DEV) // 32) % 2 == 1)[None, :, None]
+    d["g"] = torch.where(odd, d["g"], torch.full_like(d["g"], -1.1))
+    d["beta"] = torch.where(odd, torch.ones_like(d["beta"]), d["beta"])
+    d["k"] = torch.where(odd[..., None], (d["k"].float() * 2.2 ** 0.5).to(torch.bfloat16), d["k"])
+    check(orc, d, 64, TOL["bf16"], f"map drops then expanding keys dk={dk} dv={dv}")
+
+
 @pytest.mark.parametrize("dk,dv", [(16, 16), (16, 64), (64, 16), (64, 64)])
 def test_bf16_chunk16_and_small_heads(orc, dk, dv):
     d = inputs(1, 70, 2, dk, dv, torch.bfloat16)
