@@ -522,8 +522,11 @@ __global__ __launch_bounds__(kBT<DK>) void bwd_scan_kernel(ScanArgs a) {
         if (MODE == kScanMap && !has_r) y = (j == c0 - DV + c) ? 1.f : 0.f;
         Yb[0][j][c] = y;
     }
-    float4 Fc[DK / 16], Fn[DK / 16];
-    f32x4 Rc[SW / 16], Rn[SW / 16];
+    // F and R of three steps in registers: step s reads the ones loaded two steps earlier, and
+    // issues the loads of step s + 2 into the buffer step s - 1 read, so a load has two steps to
+    // arrive (with one, every step waited on the memory latency: 3B-shaped 8K scan 795 us)
+    float4 F0[DK / 16], F1[DK / 16], F2[DK / 16];
+    f32x4 R0[SW / 16], R1[SW / 16], R2[SW / 16];
     auto load_f = [&](int n, float4 (&f)[DK / 16]) {
         const float *F = a.F + (head + n) * DK * DK + (i0 + li) * DK + 4 * lk;
 #pragma unroll
@@ -536,16 +539,22 @@ __global__ __launch_bounds__(kBT<DK>) void bwd_scan_kernel(ScanArgs a) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) r[t][q] = has_r ? R[(i0 + 4 * lk + q) * DV + 16 * t + li] : 0.f;
     };
-    if (n1 > n0) {
-        load_f(n1 - 1, Fc);
-        load_r(n1 - 1, Rc);
+    const int S = n1 - n0;
+    if (S > 0) {
+        load_f(n1 - 1, F0);
+        load_r(n1 - 1, R0);
+    }
+    if (S > 1) {
+        load_f(n1 - 2, F1);
+        load_r(n1 - 2, R1);
     }
     __syncthreads();
-    for (int s = 0; s < n1 - n0; ++s) {
+    auto step = [&](int s, const float4 (&Fc)[DK / 16], const f32x4 (&Rc)[SW / 16], float4 (&Fl)[DK / 16],
+                    f32x4 (&Rl)[SW / 16]) {
         const int n = n1 - 1 - s, cur = s & 1;
-        if (n > n0) {
-            load_f(n - 1, Fn);
-            load_r(n - 1, Rn);
+        if (n - 2 >= n0) {
+            load_f(n - 2, Fl);
+            load_r(n - 2, Rl);
         }
         if (MODE != kScanMap) {  // this step's Y, before the update
             float *Yo = a.Y + (head + n) * DK * DV + c0;
@@ -593,11 +602,12 @@ __global__ __launch_bounds__(kBT<DK>) void bwd_scan_kernel(ScanArgs a) {
         for (int t = 0; t < SW / 16; ++t)
 #pragma unroll
             for (int q = 0; q < 4; ++q) Yb[cur ^ 1][i0 + 4 * lk + q][16 * t + li] = acc[t][q];
-#pragma unroll
-        for (int blk = 0; blk < DK / 16; ++blk) Fc[blk] = Fn[blk];
-#pragma unroll
-        for (int t = 0; t < SW / 16; ++t) Rc[t] = Rn[t];
         __syncthreads();
+    };
+    for (int s = 0; s < S; s += 3) {
+        step(s, F0, R0, F2, R2);
+        if (s + 1 < S) step(s + 1, F1, R1, F0, R0);
+        if (s + 2 < S) step(s + 2, F2, R2, F1, R1);
     }
     const int fin = (n1 - n0) & 1;
     if (MODE == kScanAll && a.y_start) {

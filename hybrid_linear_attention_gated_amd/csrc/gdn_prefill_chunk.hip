@@ -614,8 +614,11 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
     // the rest of the piece, and if a slice was already dropped, the piece's map is recomputed
     // from its first chunk without drops.  Gains: 64K workload 0.745 -> 0.705 ms (exact zeros
     // alone: 0.727), literal-gate reading 0.73 -> 0.67 ms, 3B-shaped call 1.49 -> 1.31 ms.
+    // (not with the preparation in the loads, whose kernels are at their register limit: there a
+    // slice is skipped only once it is exactly zero)
+    constexpr bool kDrop = MAP && DELTA && !PREP;
     bool id_zero[G::SPW] = {};
-    bool flush_ok = true, any_flush = false;
+    bool flush_ok = kDrop, any_flush = false;
 
     for (int n = n0; n < n1; ++n) {
         const int t0 = n * C;
@@ -1252,7 +1255,7 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
         // written again before the barrier that ends the chunk).  A restart loads the piece's first
         // chunk next instead of chunk n + 1.
         bool restart = false;
-        if constexpr (MAP && DELTA) {
+        if constexpr (kDrop) {
             any_flush = any_flush || __builtin_amdgcn_readfirstlane(flush_s[(n - 1) & 1]) != 0;
             if (flush_ok && __builtin_amdgcn_readfirstlane(grow_s) != 0) {
                 flush_ok = false;
@@ -1459,14 +1462,14 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
             if constexpr (MAP && DELTA) {
                 if (!value_slice) {
                     // (a NaN counts as large)
-                    const float lim = flush_ok ? kFlush : 0.f;
+                    const float lim = (kDrop && flush_ok) ? kFlush : 0.f;
                     bool big = false;
 #pragma unroll
                     for (int mt = 0; mt < G::KT; ++mt)
 #pragma unroll
                         for (int r = 0; r < 4; ++r) big = big || !(fabsf(St[j][mt][r]) <= lim);
                     id_zero[j] = __builtin_amdgcn_ballot_w64(big) == 0;  // uniform over the wavefront
-                    if (id_zero[j] && flush_ok) {
+                    if (kDrop && id_zero[j] && flush_ok) {
 #pragma unroll
                         for (int mt = 0; mt < G::KT; ++mt) St[j][mt] = zero4;
                         if (lane == 0) flush_s[n & 1] = 1;
@@ -1483,7 +1486,7 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
         }
         if constexpr (G::WAVES == 4) __builtin_amdgcn_s_setprio(0);
         __syncthreads();
-        if constexpr (MAP && DELTA) {
+        if constexpr (kDrop) {
             if (restart) {
                 // the piece's map again from its first chunk (its rows loaded above), with no
                 // drops; wavefront 1 waits for T00 of chunk n0 again
