@@ -131,3 +131,49 @@ def test_chunk_form_catches_a_wrong_readout():
         o_wrong[c0:c0 + 16] = scale * (np.exp(G)[:, None] * (Q @ st) + P @ delta)
         st = np.exp(G[-1]) * st + K.T @ (np.exp(G[-1] - G)[:, None] * delta)
     assert rel(o_wrong, o) > 1e-3
+
+
+def _piece_map(k, g, b):
+    """M_p by the oracle: one head's run on the identity with no values (q and v zero), key-major,
+    so that St_out = M_p St_in for a value-free piece."""
+    import oracle
+    T, dk = k.shape
+    z = np.zeros((1, T, 1, dk))
+    _, sf = oracle.prefill(z, k[None, :, None, :], z, g[None, :, None], b[None, :, None], np.eye(dk)[None, None])
+    return sf[0, 0]
+
+
+def test_piece_map_drop_bound():
+    """The map pass may set a piece map's identity columns to zero once every element is at most
+    2^-32, provided every later token's map a (I - b k k^T) has norm at most 1 (g <= 0 and
+    b |k|^2 <= 2).  Then what was dropped is only shrunk by the rest of the piece: the piece's end
+    state moves by at most d_k max|M| |S| in Frobenius norm.  Pinned here on the oracle: a hard-
+    decaying chunk takes the map below 2^-32, a non-expanding chunk after it keeps the dropped
+    part within that bound, and a chunk with b |k|^2 = 4 (eigenvalue -3 along k) breaks it, which
+    is why such a chunk turns the drops off (and recomputes a map that already dropped)."""
+    rng = np.random.default_rng(11)
+    dk = dv = 16
+
+    def keys(n, norm2):
+        k = rng.standard_normal((n, dk))
+        return k / np.linalg.norm(k, axis=1, keepdims=True) * np.sqrt(norm2)
+
+    k1, g1, b1 = keys(32, 1.0), np.full(32, -1.1), rng.uniform(0.2, 1.0, 32)
+    m1 = _piece_map(k1, g1, b1)
+    tiny = np.max(np.abs(m1))
+    assert 0 < tiny <= 2.0 ** -32
+    s = rng.standard_normal((dk, dv))
+    bound = dk * tiny * np.linalg.norm(s)
+
+    # a chunk that cannot expand the map: the dropped part stays within the bound
+    k2, g2, b2 = keys(32, 1.0), np.full(32, -0.03), rng.uniform(0.2, 1.0, 32)
+    m2 = _piece_map(k2, g2, b2)
+    m = _piece_map(np.concatenate([k1, k2]), np.concatenate([g1, g2]), np.concatenate([b1, b2]))
+    assert np.allclose(m, m2 @ m1, rtol=1e-9, atol=1e-12 * tiny)  # maps compose by products
+    assert np.linalg.norm(m2, 2) <= 1 + 1e-12
+    assert np.linalg.norm(m @ s) <= bound
+
+    # a chunk that can (b = 1, |k|^2 = 4, no decay): the same drop would move the state past it
+    k3, g3, b3 = keys(32, 4.0), np.zeros(32), np.ones(32)
+    me = _piece_map(np.concatenate([k1, k3]), np.concatenate([g1, g3]), np.concatenate([b1, b3]))
+    assert np.linalg.norm(me @ s) > 10 * bound
