@@ -19,12 +19,15 @@ DEV = "cuda:0"
 ORULE = {gdn.GDN_RULE_GATED_DELTA: oracle.GATED_DELTA, gdn.GDN_RULE_GATED_DECAY: oracle.GATED_DECAY}
 
 
-def run_case(orc, lens, H, dk, dv, chunk, slots, init, pool_size, rule, rows=None, wid=80, dtype=torch.bfloat16):
+def run_case(orc, lens, H, dk, dv, chunk, slots, init, pool_size, rule, rows=None, wid=80, dtype=torch.bfloat16,
+             mutate=None):
     S, T = len(lens), int(sum(lens))
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     tol = TOL["bf16"] if dtype == torch.bfloat16 else TOL["f32"]
     d = gi.prefill_inputs(1, T, H, dk, dv, wid=wid, qkv_dtype=dtype, device=DEV)
     d = {k: x[0] for k, x in d.items() if x is not None}
+    if mutate is not None:
+        mutate(d, cu)
     pool = gi.decode_state(pool_size, H, dk, dv, wid=wid + 1, device=DEV)
     pool0 = pool.clone()
     print(f"[case] varlen S={S} T={T} H={H} dk={dk} dv={dv} chunk={chunk} rule={rule} dtype={dtype}", flush=True)
@@ -65,6 +68,26 @@ def test_varlen_matches_each_sequence(orc, rule, dk, dv, chunk):
     slots = np.array([2, 5, -1, 0, 7, 4], dtype=np.int32)
     init = np.array([1, 0, 1, 1, 0, 1], dtype=np.int32)
     run_case(orc, lens, 3, dk, dv, chunk, slots, init, 8, rule)
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128)])
+def test_varlen_map_drops_then_expanding_chunk(orc, dk, dv):
+    """Packed sequences through the map pass's identity-slice drops and their restart: inside each
+    sequence, even 32-token chunks decay hard (g = -1.1, the map falls far below 2^-32) and odd ones
+    have b = 1 and |k|^2 near 2.2 (a token map with an eigenvalue near -1.2), so every piece that
+    drops a slice restarts its map.  Each sequence against the oracle run on it alone."""
+    def mutate(d, cu):
+        pos = torch.zeros(d["g"].shape[0], dtype=torch.long, device=DEV)
+        for s in range(len(cu) - 1):
+            pos[cu[s]:cu[s + 1]] = torch.arange(cu[s + 1] - cu[s], device=DEV)
+        odd = ((pos // 32) % 2 == 1)[:, None]
+        d["g"] = torch.where(odd, d["g"], torch.full_like(d["g"], -1.1))
+        d["beta"] = torch.where(odd, torch.ones_like(d["beta"]), d["beta"])
+        d["k"] = torch.where(odd[..., None], (d["k"].float() * 2.2 ** 0.5).to(torch.bfloat16), d["k"])
+    lens = [2500, 700, 3100, 40]
+    slots = np.array([1, 3, 0, 2], dtype=np.int32)
+    init = np.array([1, 1, 0, 1], dtype=np.int32)
+    run_case(orc, lens, 2, dk, dv, 64, slots, init, 4, gdn.GDN_RULE_GATED_DELTA, mutate=mutate)
 
 
 def test_varlen_default_slots_and_many_sequences(orc):
