@@ -1547,6 +1547,19 @@ __device__ __forceinline__ void chain_load(ChainMap<DK, DV> &c, const float *mp,
 template <int DK, int DV>
 __device__ __forceinline__ void chain_step(f32x4 (&St)[DK / 16], const ChainMap<DK, DV> &c) {
     constexpr int KT = DK / 16, KS = DK / 32;
+    // M_p = 0 (every identity slice of the map dropped or decayed to zero): St = N_p, no product
+    bool nz = false;
+#pragma unroll
+    for (int mt = 0; mt < KT; ++mt)
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) nz = nz || c.m[mt][s][e] != 0.f;
+    if (__builtin_amdgcn_ballot_w64(nz) == 0) {
+#pragma unroll
+        for (int mt = 0; mt < KT; ++mt) St[mt] = f32x4{c.n[mt][0], c.n[mt][1], c.n[mt][2], c.n[mt][3]};
+        return;
+    }
     bf16x8 Sh[KS], Sl[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -1661,8 +1674,22 @@ __global__ __launch_bounds__(kWave * (DK / 32)) void chain_kernel(const float *_
                 starts[((bh * P + p) * DK + 16 * (mt0 + rt) + 4 * gq + r) * DV + col] = own[rt][r];
         }
     };
-    // own rows of piece p + 1's start state from piece p's: M_p St + N_p
+    // own rows of piece p + 1's start state from piece p's: M_p St + N_p (just N_p where this
+    // wavefront's rows of M_p are all zero, as the map pass leaves them once every identity slice is
+    // dropped or has decayed to zero: then no product and no read of the slice)
     auto step = [&](int p, const ChainRows<DK> &c) {
+        bool nz = false;
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int ss = 0; ss < KS; ++ss)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) nz = nz || c.m[rt][ss][e] != 0.f;
+        if (__builtin_amdgcn_ballot_w64(nz) == 0) {
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) own[rt] = f32x4{c.n[rt][0], c.n[rt][1], c.n[rt][2], c.n[rt][3]};
+            return;
+        }
         bf16x8 Sh[KS], Sl[KS];
 #pragma unroll
         for (int ss = 0; ss < KS; ++ss) {
