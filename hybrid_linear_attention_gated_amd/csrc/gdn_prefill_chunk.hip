@@ -432,6 +432,7 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
     __shared__ __align__(16) bf16x8 tbf_s[kSplitF ? G::CT * G::CS * 2 * kWave : 1];
     __shared__ float g_s[C], b_s[C], bg_s[C], dec_s[C], gam_s[C];  // g_s: G * log2(e)
     __shared__ int t00_ready;  // the last chunk whose T00 wavefront 0 has stored (kMergeBC)
+    __shared__ int a10_ready;  // the last chunk whose A10 wavefront 2 has stored (kMergeBC)
     // MAP, gated delta rule (the identity slices dropped below kFlush, in G): grow_s, some chunk of
     // the piece so far can expand the map (a log gate above 0, or b |k|^2 > 2); flush_s[n & 1], a
     // wavefront dropped a slice at the end of chunk n (read in chunk n + 1)
@@ -546,7 +547,7 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
     // T's blocks above the diagonal stay zero for the whole kernel
     for (int e = tid; e < TS_FLOATS; e += G::BLOCK) t_s[e] = 0.f;
     if (tid == 0) {
-        t00_ready = -1;
+        t00_ready = a10_ready = -1;
         grow_s = flush_s[0] = flush_s[1] = 0;
     }
     float rate_h = 1.f, bias_h = 0.f;
@@ -948,6 +949,11 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
                         a_tile(I0{}, I0{});
                     } else if (wave == 1) {
                         a_tile(I1{}, I1{});
+                    } else if (wave == 2) {
+                        // the tile below the diagonal, for wavefront 1's T10, published like T00
+                        a_tile(I1{}, I0{});
+                        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+                        __hip_atomic_store(&a10_ready, n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
                     }
                 }
             } else {
@@ -1013,8 +1019,8 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
                     if constexpr (kShareTB) tb_build(0);
                 } else if (wave == 1) {
                     inv_diag(16);
-                    a_tile(I1{}, I0{});
-                    while (__hip_atomic_load(&t00_ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < n)
+                    while (__hip_atomic_load(&a10_ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < n ||
+                           __hip_atomic_load(&t00_ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < n)
                         __builtin_amdgcn_s_sleep(1);
                     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
                     const f32x4 t10 =
@@ -1493,7 +1499,7 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
                 init_state();
 #pragma unroll
                 for (int j = 0; j < G::SPW; ++j) id_zero[j] = false;
-                if (tid == 0) t00_ready = n0 - 1;
+                if (tid == 0) t00_ready = a10_ready = n0 - 1;
                 n = n0 - 1;
             }
         }
