@@ -110,7 +110,14 @@ typedef enum gdn_rule GDN_ENUM_INT {
  * (I + tril(diag(b) K K^T * decay)) solved by forward substitution, the
  * W/U products, a scan of the fp32 state from chunk to chunk, and outputs as
  * the intra-chunk term plus Q times the chunk's start state.  The result
- * equals the token-by-token rule up to rounding.  The final state is the
+ * equals the token-by-token rule up to rounding.  A long sequence on few heads
+ * is split into pieces run side by side, each piece's affine map from its
+ * start state to its end state chained afterwards; the map's part that
+ * multiplies the start state is set to zero once every element is at most
+ * 2^-32 while no token of the piece so far could enlarge it (log-gate <= 0
+ * and b |k|^2 <= 2), which moves a piece's end state by at most 2^-25 of the
+ * start state's norm, below fp32 rounding (inputs outside that range get the
+ * map without this).  The final state is the
  * fixed-size hidden state a GDN layer keeps per request in place of a KV
  * cache, so a long prompt can be fed in successive calls with the state
  * carried between them (ftxj.github.io digest of arXiv 2604.24715, Key Ideas;
