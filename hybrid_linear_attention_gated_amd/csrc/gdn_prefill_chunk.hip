@@ -610,7 +610,7 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
     // of the piece so far has a map of norm at most 1 (log gate <= 0 and b |k|^2 <= 2: then each
     // later token can only shrink what was dropped).  Dropping at most kFlush per element over the
     // d_k identity columns changes the map by at most d_k kFlush = 2^-25 in norm (d_k <= 128), under
-    // half a unit in the last place of fp32: the piece's end state S_p M_p + N_p moves by less than
+    // half a unit in the last place of fp32: the piece's end state M_p S_p + N_p moves by less than
     // its own rounding relative to |S_p|.  A chunk that can expand the map turns the drops off for
     // the rest of the piece, and if a slice was already dropped, the piece's map is recomputed
     // from its first chunk without drops.  Gains: 64K workload 0.745 -> 0.705 ms (exact zeros
@@ -1495,7 +1495,7 @@ __global__ __launch_bounds__((kWave * kWavesOf<DK, DV>), (kBlocksPerCU<DK, DV, C
         if constexpr (kDrop) {
             if (restart) {
                 // the piece's map again from its first chunk (its rows loaded above), with no
-                // drops; wavefront 1 waits for T00 of chunk n0 again
+                // drops; wavefront 1 waits for T00 and A10 of chunk n0 again
                 init_state();
 #pragma unroll
                 for (int j = 0; j < G::SPW; ++j) id_zero[j] = false;
