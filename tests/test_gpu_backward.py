@@ -28,9 +28,11 @@ def grad_inputs(B, T, H, d, wid, s0=True, dsf=True, dtype=torch.bfloat16):
     return x, d_o, ds
 
 
-def run_case(B, T, H, rule, wid, s0=True, dsf=True, want_d_initial=True, dtype=torch.bfloat16, d=64):
+def run_case(B, T, H, rule, wid, s0=True, dsf=True, want_d_initial=True, dtype=torch.bfloat16, d=64, mutate=None):
     print(f"[case] backward B={B} T={T} H={H} d={d} rule={rule} s0={s0} dsf={dsf} {dtype}", flush=True)
     x, d_o, ds = grad_inputs(B, T, H, d, wid, s0, dsf, dtype)
+    if mutate is not None:
+        mutate(x)
     got = gdn.chunk_backward(x["q"], x["k"], x["v"], x["g"], x["beta"], d_o, x["s0"], ds,
                              want_d_initial=want_d_initial, rule=rule)
     torch.cuda.synchronize()
@@ -57,6 +59,20 @@ def test_backward_ragged(rule):
 def test_backward_several_forward_pieces(rule):
     # 64 chunks of 32 tokens per head over 2 heads: the forward recompute runs in 8 pieces
     run_case(1, 2048, 2, rule, 211)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_forward_map_restart(d):
+    """The forward recompute's map pass through its identity-slice drops and their restart: even
+    32-token chunks decay hard (g = -1.1), odd ones have b = 1 and |k|^2 near 2.2 (a token map with
+    an eigenvalue near -1.2), over 16 forward pieces per head, so every piece that drops a slice
+    recomputes its map.  Every gradient against the oracle's adjoint."""
+    def mutate(x):
+        odd = ((torch.arange(x["g"].shape[1], device=DEV) // 32) % 2 == 1)[None, :, None]
+        x["g"] = torch.where(odd, x["g"], torch.full_like(x["g"], -1.1))
+        x["beta"] = torch.where(odd, torch.ones_like(x["beta"]), x["beta"])
+        x["k"] = torch.where(odd[..., None], (x["k"].float() * 2.2 ** 0.5).to(torch.bfloat16), x["k"])
+    run_case(1, 4096 + 19, 2, gdn.GDN_RULE_GATED_DELTA, 219, d=d, mutate=mutate)
 
 
 def test_backward_without_state_or_final_gradient():
