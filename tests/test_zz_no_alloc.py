@@ -68,3 +68,21 @@ def test_noalloc_in_place_and_short_call():
     torch.cuda.synchronize()
     assert torch.equal(o, o_ref) and torch.equal(st, s_ref)
     assert torch.equal(oy, oy_ref) and torch.equal(sy, sy_ref)
+
+
+@pytest.mark.parametrize("dk", [64, 128])
+def test_noalloc_map_restart_matches_workspace_call(dk):
+    """Inputs that make the map pass drop identity slices and then restart a piece's map (even 32-token
+    chunks decay hard, odd ones have b = 1 and |k|^2 near 2.2): the allocation-free call still equals
+    the call with a workspace bit for bit."""
+    B, T, H = 1, 4096 + 19, 2
+    d = gi.prefill_inputs(B, T, H, dk, dk, wid=133, qkv_dtype=torch.bfloat16, s0=True, device=DEV)
+    odd = ((torch.arange(T, device=DEV) // 32) % 2 == 1)[None, :, None]
+    d["g"] = torch.where(odd, d["g"], torch.full_like(d["g"], -1.1))
+    d["beta"] = torch.where(odd, torch.ones_like(d["beta"]), d["beta"])
+    d["k"] = torch.where(odd[..., None], (d["k"].float() * 2.2 ** 0.5).to(torch.bfloat16), d["k"])
+    print(f"[case] noalloc restart: B={B} T={T} H={H} d={dk}", flush=True)
+    o_ref, s_ref = gdn.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], chunk=64)
+    o, sf = call_noalloc(d, B, T, H, dk, dk, gdn.GDN_RULE_GATED_DELTA)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(sf, s_ref)
